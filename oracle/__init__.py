@@ -1,0 +1,159 @@
+"""Sequential CPU oracle for scan, compaction and packing (ctypes over oracle.c).
+
+TEST INFRASTRUCTURE ONLY: tests/, the smoke check in __graft_entry__.py and the
+cpu_baseline leg of bench.py may import this package; the library under
+stream_compaction_wave64_amd/ never does, and this package never imports it.
+
+Every function takes and returns numpy arrays.  Scans work on a dense
+row-major (outer, len, inner) array and scan along the middle axis, following
+the exclusive / inclusive prefix-sum definitions on Merry's "Prefix sums on
+GPUs" slides; floating-point results are returned in fp64 (fp32 inputs are
+accumulated in fp64, fp64 inputs in double-double).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+OPS = {"sum": 0, "prod": 1, "max": 2, "min": 3}
+CMPS = {"gt": 0, "ge": 1, "lt": 2, "le": 3, "eq": 4, "ne": 5}
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c with gcc -O2 (no fast-math) into liboracle.so."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-std=c99", "-fPIC", "-shared",
+                               "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=False)
+        lib = ctypes.CDLL(_LIB)
+        vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        for name in ("oracle_scan_i32", "oracle_scan_u32", "oracle_scan_i64",
+                     "oracle_scan_f32", "oracle_scan_f64"):
+            f = getattr(lib, name)
+            f.argtypes = [vp, vp, i64, i64, i64, i32, i32]
+            f.restype = i32
+        for name in ("oracle_abs_prefix_f32", "oracle_abs_prefix_f64"):
+            f = getattr(lib, name)
+            f.argtypes = [vp, vp, i64, i64, i64, i32]
+            f.restype = i32
+        lib.oracle_compact_f32.argtypes = [vp, i64, i32, ctypes.c_float, vp]
+        lib.oracle_compact_f32.restype = i64
+        lib.oracle_compact_i32.argtypes = [vp, i64, i32, ctypes.c_int32, vp]
+        lib.oracle_compact_i32.restype = i64
+        lib.oracle_pack_offsets.argtypes = [vp, i64, vp]
+        lib.oracle_pack_offsets.restype = i64
+        lib.oracle_pack_emit.argtypes = [vp, i64, vp]
+        lib.oracle_pack_emit.restype = i32
+        lib.oracle_block_size.argtypes = [i64, i64, i64, i64]
+        lib.oracle_block_size.restype = i64
+        _lib = lib
+    return _lib
+
+
+def _ptr(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+def _dims(x: np.ndarray, dims):
+    if dims is None:
+        return 1, x.size, 1
+    outer, length, inner = (int(d) for d in dims)
+    if outer * length * inner != x.size:
+        raise ValueError(f"dims {dims} do not match size {x.size}")
+    return outer, length, inner
+
+
+_SCAN = {
+    np.dtype(np.int32): ("oracle_scan_i32", np.int32),
+    np.dtype(np.uint32): ("oracle_scan_u32", np.uint32),
+    np.dtype(np.int64): ("oracle_scan_i64", np.int64),
+    np.dtype(np.float32): ("oracle_scan_f32", np.float64),
+    np.dtype(np.float64): ("oracle_scan_f64", np.float64),
+}
+
+
+def scan(x: np.ndarray, op: str = "sum", exclusive: bool = False, dims=None) -> np.ndarray:
+    """Scan of x along the middle axis of (outer, len, inner).
+
+    Integers: same dtype, wrapping arithmetic.  fp32 / fp64: fp64 result.
+    """
+    lib = _load()
+    x = np.ascontiguousarray(x)
+    name, out_t = _SCAN[x.dtype]
+    outer, length, inner = _dims(x, dims)
+    y = np.empty(x.size, dtype=out_t)
+    if x.size:
+        rc = getattr(lib, name)(_ptr(x), _ptr(y), outer, length, inner, OPS[op], int(exclusive))
+        if rc != 0:
+            raise ValueError("oracle scan rejected its arguments")
+    return y.reshape(x.shape)
+
+
+def abs_prefix(x: np.ndarray, exclusive: bool = False, dims=None) -> np.ndarray:
+    """P_i: sum of |x_j| over the inputs output i depends on, in fp64."""
+    lib = _load()
+    x = np.ascontiguousarray(x)
+    outer, length, inner = _dims(x, dims)
+    p = np.empty(x.size, dtype=np.float64)
+    if x.size:
+        fn = {np.dtype(np.float32): lib.oracle_abs_prefix_f32,
+              np.dtype(np.float64): lib.oracle_abs_prefix_f64}[x.dtype]
+        fn(_ptr(x), _ptr(p), outer, length, inner, int(exclusive))
+    return p.reshape(x.shape)
+
+
+def compact(x: np.ndarray, cmp: str = "gt", threshold=0.5) -> np.ndarray:
+    """Ascending int32 indices i with x[i] <cmp> threshold (in x's precision)."""
+    lib = _load()
+    x = np.ascontiguousarray(x)
+    idx = np.empty(max(x.size, 1), dtype=np.int32)
+    if x.dtype == np.float32:
+        cnt = lib.oracle_compact_f32(_ptr(x), x.size, CMPS[cmp], float(np.float32(threshold)), _ptr(idx))
+    elif x.dtype == np.int32:
+        cnt = lib.oracle_compact_i32(_ptr(x), x.size, CMPS[cmp], int(threshold), _ptr(idx))
+    else:
+        raise TypeError(x.dtype)
+    return idx[:cnt].copy()
+
+
+def pack_offsets(counts: np.ndarray):
+    """(offsets[n+1] int32, total as a Python int computed in 64 bits)."""
+    lib = _load()
+    c = np.ascontiguousarray(counts, dtype=np.int32)
+    off = np.empty(c.size + 1, dtype=np.int32)
+    total = lib.oracle_pack_offsets(_ptr(c), c.size, _ptr(off))
+    return off, int(total)
+
+
+def pack_emit(offsets: np.ndarray) -> np.ndarray:
+    """Records of every object packed at its offset: object i, record j -> (i+1+j) mod n."""
+    lib = _load()
+    off = np.ascontiguousarray(offsets, dtype=np.int32)
+    n = off.size - 1
+    out = np.empty(max(int(off[-1]), 1), dtype=np.int32)
+    if n > 0:
+        lib.oracle_pack_emit(_ptr(off), n, _ptr(out))
+    return out[: int(off[-1])].copy()
+
+
+def block_size(esize: int, budget: int, explicit: int = 0, default: int = 256) -> int:
+    """Block size for elements of esize bytes under a local-memory budget."""
+    return int(_load().oracle_block_size(esize, budget, explicit, default))

@@ -1,0 +1,97 @@
+"""Plant plausible mistakes in a copy of the oracle (CPU only) and check that the
+pins in test_oracle.py catch each one.  This shows the pins are sensitive to a
+dropped term, a wrong index, a swapped comparison or an off-by-one anywhere in
+the oracle, rather than merely agreeing with it."""
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+import test_oracle as T
+
+SRC = open(os.path.join(os.path.dirname(oracle.__file__), "oracle.c")).read()
+
+MUTANTS = {
+    "i32 exclusive written after combining": (
+        "y[at] = (int32_t)acc;\n                    acc = i32_combine(op, acc, a);",
+        "acc = i32_combine(op, acc, a);\n                    y[at] = (int32_t)acc;"),
+    "scan index with len and inner swapped": (
+        "int64_t at = (o * len + i) * inner + k;", "int64_t at = (o * inner + i) * len + k;"),
+    "i32 max identity 0": ("case O_MAX: return (uint32_t)INT32_MIN;", "case O_MAX: return 0u;"),
+    "u32 max compares the wrong way": ("case O_MAX: return (a > b) ? a : b;",
+                                       "case O_MAX: return (a < b) ? a : b;"),
+    "i64 prod adds": ("case O_PROD: return a * b;\n    case O_MAX: return ((int64_t)a",
+                      "case O_PROD: return a + b;\n    case O_MAX: return ((int64_t)a"),
+    "fp32 accumulated in fp32": ("acc = f64_combine(op, acc, a);\n                    y[at] = acc;",
+                                 "acc = (float)f64_combine(op, acc, a);\n                    y[at] = acc;"),
+    "fp64 TwoSum error term dropped": ("return dd_renorm(s, err + a.lo);", "return dd_renorm(s, a.lo);"),
+    "fp64 prod ignores low word": ("return dd_renorm(p, err + a.lo * b);", "return dd_renorm(p, err);"),
+    "abs prefix exclusive/inclusive swapped": (
+        "if (exclusive) { p[at] = acc; acc += fabs((double)x[at]); }",
+        "if (!exclusive) { p[at] = acc; acc += fabs((double)x[at]); }"),
+    "compaction off by one": ("idx[count++] = (int32_t)i;", "idx[count++] = (int32_t)(i + 1);"),
+    "compaction > taken as >=": ("case O_GT: return v > t;", "case O_GT: return v >= t;"),
+    "pack offsets shifted": ("offsets[i + 1] = (int32_t)run;", "offsets[i] = (int32_t)run;"),
+    "emit record drops the +1": ("(int32_t)((i + 1 + j) % n)", "(int32_t)((i + j) % n)"),
+    "block rule without the per-thread totals": ("2 * b * esize > budget", "b * esize > budget"),
+    "block rule floor 1": [("while (b > 2 &&", "while (b > 1 &&"), ("if (b < 2) b = 2;", "")],
+}
+
+PINS = [
+    lambda o: [T.test_merry_prefix_sum_example(o, dt) for dt in T.ALL_TYPES],
+    lambda o: [T.test_merry_kogge_stone_states(o, dt) for dt in T.ALL_TYPES],
+    lambda o: [T.test_merry_brent_kung_example(o, dt) for dt in T.ALL_TYPES],
+    lambda o: [T.test_merry_radix4_example(o, dt) for dt in T.ALL_TYPES],
+    lambda o: T.test_merry_output_packing_example(o),
+    lambda o: T.test_pr208_block_size_rule(o),
+    lambda o: [T.test_constant_and_extrema_closed_forms(o, dt) for dt in T.ALL_TYPES],
+    lambda o: T.test_prod_powers_of_two_wrap(o),
+    lambda o: [T.test_brute_force_small(o, dt, op, 65) for dt in T.ALL_TYPES for op in T.OPS],
+    lambda o: T.test_matches_numpy_accumulate_u32_i64(o),
+    lambda o: T.test_scan_invariants_float(o),
+    lambda o: T.test_fp64_exact_integer_shadow(o),
+    lambda o: [T.test_dims_layouts_agree(o, dt) for dt in (np.int32, np.float32)],
+    lambda o: T.test_compaction_brute_and_numpy(o),
+    lambda o: T.test_compaction_closed_forms(o),
+    lambda o: T.test_pack_offsets_and_emit(o),
+]
+
+
+def _caught(lib_path):
+    saved = oracle._lib
+    oracle._lib = None
+    real = oracle._LIB
+    try:
+        oracle._LIB = lib_path
+        oracle._load()
+        for pin in PINS:
+            try:
+                pin(oracle)
+            except Exception:
+                return True
+        return False
+    finally:
+        oracle._lib = saved
+        oracle._LIB = real
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(tmp_path, name):
+    edits = MUTANTS[name]
+    if isinstance(edits, tuple):
+        edits = [edits]
+    text = SRC
+    for old, new in edits:
+        assert old in text, f"mutation anchor for {name!r} not found"
+        text = text.replace(old, new)
+    src = tmp_path / "mut.c"
+    src.write_text(text)
+    lib = tmp_path / "libmut.so"
+    subprocess.check_call(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-w", "-o", str(lib), str(src), "-lm"])
+    assert _caught(str(lib)), f"no pin caught the mutant: {name}"
+
+
+def test_unmutated_oracle_passes_all_pins(oracle_lib):
+    assert not _caught(oracle._LIB)
