@@ -1,0 +1,254 @@
+// api.hip -- the C ABI (include/scan_wave64.h): argument checks, the tile
+// planner and kernel selection.  Everything here runs on the host; every
+// arithmetic step of a scan runs in the kernels.
+#include <stdint.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "launch.hpp"
+#include "scan_wave64.h"
+
+namespace sw64 {
+
+LbLaunch find_lookback_i32(scan_op_t, int, int, int);
+LbLaunch find_lookback_u32(scan_op_t, int, int, int);
+LbLaunch find_lookback_i64(scan_op_t, int, int, int);
+LbLaunch find_lookback_f32(scan_op_t, int, int, int);
+LbLaunch find_lookback_f64(scan_op_t, int, int, int);
+
+LbLaunch find_lookback(scan_dtype_t dt, scan_op_t op, int block, int rows, int vec) {
+    switch (dt) {
+    case SCAN_I32: return find_lookback_i32(op, block, rows, vec);
+    case SCAN_U32: return find_lookback_u32(op, block, rows, vec);
+    case SCAN_I64: return find_lookback_i64(op, block, rows, vec);
+    case SCAN_F32: return find_lookback_f32(op, block, rows, vec);
+    case SCAN_F64: return find_lookback_f64(op, block, rows, vec);
+    }
+    return nullptr;
+}
+
+namespace {
+
+constexpr size_t kHeader = 256;
+constexpr uint32_t kDefaultSpinLimit = 1u << 22;
+
+bool valid_dtype(int dt) { return dt >= SCAN_I32 && dt <= SCAN_F64; }
+bool valid_op(int op) { return op >= SCAN_OP_SUM && op <= SCAN_OP_MIN; }
+
+int dtype_bytes(scan_dtype_t dt) { return (dt == SCAN_I64 || dt == SCAN_F64) ? 8 : 4; }
+
+// Bytes of the value a tile hands to its successors (see Carry in device.hpp).
+int carry_bytes(scan_dtype_t dt, scan_op_t op) {
+    if (dt == SCAN_F32 && (op == SCAN_OP_SUM || op == SCAN_OP_PROD)) return 8;
+    return dtype_bytes(dt);
+}
+
+size_t round_up(size_t x, size_t m) { return (x + m - 1) / m * m; }
+
+scan_tuning_t tuning_or_default(const scan_tuning_t *t) {
+    scan_tuning_t d;
+    memset(&d, 0, sizeof(d));
+    if (t) d = *t;
+    return d;
+}
+
+// Plan of the look-back / reduce-then-scan launch for scalar elements.
+struct LbPlan {
+    int block, rows, vec;
+    int64_t tile;
+    int64_t tiles_per_seg, num_tiles;
+    int carry_words;
+    size_t ws_bytes;
+};
+
+int plan_lookback(scan_dtype_t dt, scan_op_t op, int64_t outer, int64_t len, bool aligned,
+                  const scan_tuning_t &tu, LbPlan &p) {
+    const int vmax = 16 / dtype_bytes(dt);
+    p.vec = (aligned && len % vmax == 0) ? vmax : 1;
+    p.block = tu.block_size > 0 ? tu.block_size : 256;
+    int ipt = tu.items_per_thread > 0 ? tu.items_per_thread : 8 * vmax;
+    if (p.vec == 1 && tu.items_per_thread <= 0) ipt = 8;  // element-wide fallback: 8 rows of 1
+    if (ipt % p.vec != 0) return SCAN_ERR_UNSUPPORTED;
+    p.rows = ipt / p.vec;
+    // The element-wide fallback (misaligned data or a length that breaks the
+    // vector alignment) is built for 1 and 8 rows only: snap to the nearer.
+    if (p.vec == 1 && !find_lookback(dt, op, p.block, p.rows, 1)) p.rows = p.rows >= 8 ? 8 : 1;
+    if (!find_lookback(dt, op, p.block, p.rows, p.vec)) return SCAN_ERR_UNSUPPORTED;
+    p.tile = int64_t(p.block) * p.rows * p.vec;
+    p.tiles_per_seg = (len + p.tile - 1) / p.tile;
+    p.num_tiles = outer * p.tiles_per_seg;
+    if (p.num_tiles > int64_t(INT32_MAX)) return SCAN_ERR_OVERFLOW;  // grid x limit
+    p.carry_words = carry_bytes(dt, op) / 4;
+    p.ws_bytes = kHeader + round_up(size_t(p.num_tiles) * p.carry_words * 8, 256);
+    return SCAN_OK;
+}
+
+bool aligned16(const void *a, const void *b) {
+    return ((reinterpret_cast<uintptr_t>(a) | reinterpret_cast<uintptr_t>(b)) & 15u) == 0;
+}
+
+int check_ws(const void *ws, size_t ws_bytes, size_t need) {
+    if (ws == nullptr || ws_bytes < need) return SCAN_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(ws) & 255u) return SCAN_ERR_WORKSPACE;  // header + descriptors aligned
+    return SCAN_OK;
+}
+
+int scan_common(const void *in, void *out, int64_t outer, int64_t len, int64_t inner,
+                scan_dtype_t dt, scan_op_t op, int exclusive, void *total_out, void *ws,
+                size_t ws_bytes, const scan_tuning_t *tuning, hipStream_t stream) {
+    if (!valid_dtype(dt) || !valid_op(op)) return SCAN_ERR_INVALID_ARG;
+    if (outer < 0 || len < 0 || inner < 1) return SCAN_ERR_INVALID_ARG;
+    if (outer == 0 || len == 0) return SCAN_OK;
+    if (in == nullptr || out == nullptr) return SCAN_ERR_INVALID_ARG;
+    const scan_tuning_t tu = tuning_or_default(tuning);
+    if (tu.algo < SCAN_ALGO_AUTO || tu.algo > SCAN_ALGO_REDUCE_THEN_SCAN) return SCAN_ERR_INVALID_ARG;
+    if (inner != 1) return SCAN_ERR_UNSUPPORTED;
+    if (tu.algo == SCAN_ALGO_REDUCE_THEN_SCAN) return SCAN_ERR_UNSUPPORTED;
+
+    LbPlan p;
+    int rc = plan_lookback(dt, op, outer, len, aligned16(in, out), tu, p);
+    if (rc != SCAN_OK) return rc;
+    rc = check_ws(ws, ws_bytes, p.ws_bytes);
+    if (rc != SCAN_OK) return rc;
+    LbArgs a;
+    a.in = in;
+    a.out = out;
+    a.seg_len = len;
+    a.tiles_per_seg = uint32_t(p.tiles_per_seg);
+    a.num_tiles = uint32_t(p.num_tiles);
+    a.exclusive = exclusive ? 1 : 0;
+    a.total_out = total_out;
+    a.ws = ws;
+    a.ws_words = (ws_bytes - kHeader) / 8;
+    a.words_used = p.tiles_per_seg > 1 ? uint64_t(p.num_tiles) * p.carry_words : 0;
+    a.spin_limit = tu.spin_limit > 0 ? uint32_t(tu.spin_limit) : kDefaultSpinLimit;
+    a.grid_blocks = tu.grid_blocks > 0 ? uint32_t(tu.grid_blocks) : 0u;
+    return find_lookback(dt, op, p.block, p.rows, p.vec)(a, stream);
+}
+
+}  // namespace
+}  // namespace sw64
+
+using namespace sw64;
+
+extern "C" {
+
+int scan_plan(scan_call_t call, scan_dtype_t dtype, scan_op_t op, int64_t outer, int64_t len,
+              int64_t inner, const scan_tuning_t *tuning, scan_plan_t *plan) {
+    if (plan == nullptr) return SCAN_ERR_INVALID_ARG;
+    memset(plan, 0, sizeof(*plan));
+    if (!valid_dtype(dtype) || !valid_op(op)) return SCAN_ERR_INVALID_ARG;
+    if (outer < 0 || len < 0 || inner < 1) return SCAN_ERR_INVALID_ARG;
+    const scan_tuning_t tu = tuning_or_default(tuning);
+    if (call != SCAN_CALL_SCAN) return SCAN_ERR_UNSUPPORTED;
+    if (inner != 1 || tu.algo == SCAN_ALGO_REDUCE_THEN_SCAN) return SCAN_ERR_UNSUPPORTED;
+    if (outer == 0 || len == 0) {
+        plan->kernel = SCAN_KERNEL_NONE;
+        return SCAN_OK;
+    }
+    LbPlan p;
+    int rc = plan_lookback(dtype, op, outer, len, true, tu, p);
+    if (rc != SCAN_OK) return rc;
+    plan->kernel = SCAN_KERNEL_LOOKBACK;
+    plan->block_size = p.block;
+    plan->items_per_thread = p.rows * p.vec;
+    plan->vec = p.vec;
+    plan->tile_elems = p.tile;
+    plan->num_tiles = p.num_tiles;
+    plan->lds_bytes = int64_t(p.rows) * (p.block / 64) * dtype_bytes(dtype) + carry_bytes(dtype, op) + 16;
+    plan->workspace_bytes = int64_t(p.ws_bytes);
+    plan->launches = 1;
+    plan->carry_words = p.carry_words;
+    return SCAN_OK;
+}
+
+size_t scan_workspace_bytes(scan_dtype_t dtype, int64_t count) {
+    (void)dtype;
+    if (count < 0) count = 0;
+    // <= 0.5 byte of descriptors or partials per value for any kernel and
+    // tuning (smallest tiles: 16 values per 8-byte word), plus the header and
+    // room for reduce-then-scan partials.
+    return kHeader + round_up(size_t(count + 15) / 16 * 8, 256) + 65536;
+}
+
+int scan_workspace_init(void *ws, size_t ws_bytes, void *stream) {
+    if (ws_bytes == 0) return SCAN_OK;
+    if (ws == nullptr || (reinterpret_cast<uintptr_t>(ws) & 7u)) return SCAN_ERR_INVALID_ARG;
+    return launch_fill_u64(ws, ws_bytes / 8, 0, reinterpret_cast<hipStream_t>(stream));
+}
+
+int scan_workspace_error(const void *ws, int32_t *error, void *stream) {
+    if (ws == nullptr || error == nullptr) return SCAN_ERR_INVALID_ARG;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    // the error word sits after counter, epoch and the 64-bit high-water mark
+    const char *p = reinterpret_cast<const char *>(ws) + 16;
+    if (hipMemcpyAsync(error, p, sizeof(int32_t), hipMemcpyDeviceToHost, s) != hipSuccess) return SCAN_ERR_HIP;
+    return hipStreamSynchronize(s) == hipSuccess ? SCAN_OK : SCAN_ERR_HIP;
+}
+
+int scan_inclusive(const void *in, void *out, int64_t n, scan_dtype_t dtype, scan_op_t op, int32_t width,
+                   void *ws, size_t ws_bytes, const scan_tuning_t *tuning, void *stream) {
+    if (width < 1 || n < 0) return SCAN_ERR_INVALID_ARG;
+    return scan_common(in, out, 1, n, width, dtype, op, 0, nullptr, ws, ws_bytes, tuning,
+                       reinterpret_cast<hipStream_t>(stream));
+}
+
+int scan_exclusive(const void *in, void *out, int64_t n, scan_dtype_t dtype, scan_op_t op, int32_t width,
+                   void *ws, size_t ws_bytes, const scan_tuning_t *tuning, void *stream) {
+    if (width < 1 || n < 0) return SCAN_ERR_INVALID_ARG;
+    return scan_common(in, out, 1, n, width, dtype, op, 1, nullptr, ws, ws_bytes, tuning,
+                       reinterpret_cast<hipStream_t>(stream));
+}
+
+int scan_dim(const void *in, void *out, int64_t outer, int64_t len, int64_t inner, scan_dtype_t dtype,
+             scan_op_t op, int exclusive, void *ws, size_t ws_bytes, const scan_tuning_t *tuning,
+             void *stream) {
+    return scan_common(in, out, outer, len, inner, dtype, op, exclusive, nullptr, ws, ws_bytes, tuning,
+                       reinterpret_cast<hipStream_t>(stream));
+}
+
+int compact_if(const void *x, int64_t n, scan_dtype_t x_dtype, scan_cmp_t cmp, double threshold,
+               int32_t *out_idx, int32_t *d_count, void *ws, size_t ws_bytes, const scan_tuning_t *tuning,
+               void *stream) {
+    (void)x; (void)n; (void)x_dtype; (void)cmp; (void)threshold; (void)out_idx; (void)d_count;
+    (void)ws; (void)ws_bytes; (void)tuning; (void)stream;
+    return SCAN_ERR_UNSUPPORTED;
+}
+
+int pack_offsets(const int32_t *counts, int64_t n, int32_t *offsets, void *ws, size_t ws_bytes,
+                 const scan_tuning_t *tuning, void *stream) {
+    if (n < 0 || offsets == nullptr) return SCAN_ERR_INVALID_ARG;
+    if (n > INT32_MAX) return SCAN_ERR_OVERFLOW;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (n == 0) return launch_fill_i32(offsets, 1, 0, s);
+    if (counts == nullptr) return SCAN_ERR_INVALID_ARG;
+    return scan_common(counts, offsets, 1, n, 1, SCAN_I32, SCAN_OP_SUM, 1, offsets + n, ws, ws_bytes, tuning, s);
+}
+
+int pack_emit_neighbors(const int32_t *offsets, int64_t n, int32_t *out, void *stream) {
+    (void)offsets; (void)n; (void)out; (void)stream;
+    return SCAN_ERR_UNSUPPORTED;
+}
+
+int scan_copy(const void *in, void *out, size_t bytes, void *stream) {
+    if (bytes == 0) return SCAN_OK;
+    if (in == nullptr || out == nullptr || bytes % 16 != 0 || !aligned16(in, out)) return SCAN_ERR_INVALID_ARG;
+    return launch_copy(in, out, bytes, reinterpret_cast<hipStream_t>(stream));
+}
+
+const char *scan_status_string(int status) {
+    switch (status) {
+    case SCAN_OK: return "ok";
+    case SCAN_ERR_INVALID_ARG: return "invalid argument";
+    case SCAN_ERR_UNSUPPORTED: return "unsupported dtype/op/shape/tuning combination";
+    case SCAN_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case SCAN_ERR_HIP: return "HIP runtime or launch error";
+    case SCAN_ERR_OVERFLOW: return "size exceeds an index type";
+    }
+    return "unknown status";
+}
+
+const char *scan_version(void) { return "scan_wave64 0.1 (gfx950)"; }
+
+}  // extern "C"

@@ -1,0 +1,370 @@
+// device.hpp -- device primitives for the gfx950 scan kernels.
+//
+//  * operators with identities and wrap-around integer arithmetic;
+//  * the wavefront scan: Kogge-Stone doubling over the 64 lanes of a wave
+//    with DPP row shifts and row broadcasts (Merry, "Prefix sums on GPUs",
+//    slide "Kogge-Stone"; The CUDA Handbook ch. 13, section 13.3.1, where the
+//    warp scan is the innermost step of every scan);
+//  * the workgroup scan of per-wave totals through one LDS slot per wave
+//    (AcceleratedKernels.jl PR #208, second bullet: one slot per sub-group);
+//  * tile descriptors and the decoupled look-back (The CUDA Handbook ch. 13,
+//    decoupled look-back section, Figure 13-11 and Listing 13-13).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include <type_traits>
+
+namespace sw64 {
+
+constexpr int kWave = 64;
+
+// ------------------------------------------------------------- operators --
+
+template <class T>
+struct Limits;
+template <> struct Limits<int32_t> {
+    __device__ static int32_t lowest() { return INT32_MIN; }
+    __device__ static int32_t highest() { return INT32_MAX; }
+};
+template <> struct Limits<uint32_t> {
+    __device__ static uint32_t lowest() { return 0u; }
+    __device__ static uint32_t highest() { return UINT32_MAX; }
+};
+template <> struct Limits<int64_t> {
+    __device__ static int64_t lowest() { return INT64_MIN; }
+    __device__ static int64_t highest() { return INT64_MAX; }
+};
+template <> struct Limits<float> {
+    __device__ static float lowest() { return -__builtin_huge_valf(); }
+    __device__ static float highest() { return __builtin_huge_valf(); }
+};
+template <> struct Limits<double> {
+    __device__ static double lowest() { return -__builtin_huge_val(); }
+    __device__ static double highest() { return __builtin_huge_val(); }
+};
+
+// Integer sum and product wrap modulo 2^bits: computed in the unsigned type
+// of the same width (signed overflow is undefined in C++).
+struct OpSum {
+    static constexpr int id = 0;
+    template <class T> __device__ __forceinline__ static T identity() { return T(0); }
+    template <class T> __device__ __forceinline__ static T apply(T a, T b) {
+        if constexpr (std::is_integral_v<T>) {
+            using U = std::make_unsigned_t<T>;
+            return T(U(a) + U(b));
+        } else {
+            return a + b;
+        }
+    }
+};
+
+struct OpProd {
+    static constexpr int id = 1;
+    template <class T> __device__ __forceinline__ static T identity() { return T(1); }
+    template <class T> __device__ __forceinline__ static T apply(T a, T b) {
+        if constexpr (std::is_integral_v<T>) {
+            using U = std::make_unsigned_t<T>;
+            return T(U(a) * U(b));
+        } else {
+            return a * b;
+        }
+    }
+};
+
+struct OpMax {
+    static constexpr int id = 2;
+    template <class T> __device__ __forceinline__ static T identity() { return Limits<T>::lowest(); }
+    template <class T> __device__ __forceinline__ static T apply(T a, T b) { return a > b ? a : b; }
+};
+
+struct OpMin {
+    static constexpr int id = 3;
+    template <class T> __device__ __forceinline__ static T identity() { return Limits<T>::highest(); }
+    template <class T> __device__ __forceinline__ static T apply(T a, T b) { return a < b ? a : b; }
+};
+
+// Type in which a tile's aggregate and prefix travel between workgroups.
+// fp32 sums and products carry in fp64: a prefix that crosses ~1e5 tiles in
+// fp32 would spend a large share of the fp32 tolerance on that chain alone.
+template <class T, class Op> struct Carry { using type = T; };
+template <> struct Carry<float, OpSum> { using type = double; };
+template <> struct Carry<float, OpProd> { using type = double; };
+
+// -------------------------------------------------------------- cross-lane --
+
+// DPP move of a 32-bit-multiple value.  Lanes whose source is outside the
+// row (or that the row mask disables) receive `old`, the operator identity.
+template <int CTRL, int ROW_MASK = 0xf, int BANK_MASK = 0xf, class T>
+__device__ __forceinline__ T dpp_mov(T old, T src) {
+    static_assert(sizeof(T) % 4 == 0, "DPP moves 32-bit words");
+    if constexpr (sizeof(T) == 4) {
+        return __builtin_bit_cast(
+            T, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old), __builtin_bit_cast(int, src),
+                                           CTRL, ROW_MASK, BANK_MASK, false));
+    } else {
+        struct W { int w[sizeof(T) / 4]; };
+        W o = __builtin_bit_cast(W, old), s = __builtin_bit_cast(W, src), r;
+#pragma unroll
+        for (int i = 0; i < int(sizeof(T) / 4); i++)
+            r.w[i] = __builtin_amdgcn_update_dpp(o.w[i], s.w[i], CTRL, ROW_MASK, BANK_MASK, false);
+        return __builtin_bit_cast(T, r);
+    }
+}
+
+// DPP control codes (GFX9 family, valid on gfx950).
+constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
+constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143, kWaveShr1 = 0x138;
+
+// Inclusive scan over the 64 lanes: four Kogge-Stone doubling rounds inside
+// each 16-lane row (shift 1, 2, 4, 8), then lane 15 of rows 0/2 feeds rows
+// 1/3 and lane 31 feeds rows 2/3.  Earlier lanes are the left operand.
+template <class Op, class T>
+__device__ __forceinline__ T wave_scan_incl(T x) {
+    const T id = Op::template identity<T>();
+    x = Op::apply(dpp_mov<kRowShr1>(id, x), x);
+    x = Op::apply(dpp_mov<kRowShr2>(id, x), x);
+    x = Op::apply(dpp_mov<kRowShr4>(id, x), x);
+    x = Op::apply(dpp_mov<kRowShr8>(id, x), x);
+    x = Op::apply(dpp_mov<kRowBcast15, 0xa>(id, x), x);
+    x = Op::apply(dpp_mov<kRowBcast31, 0xc>(id, x), x);
+    return x;
+}
+
+// Shift every lane's value to the next lane; lane 0 receives `id`.
+template <class T>
+__device__ __forceinline__ T wave_shr1(T id, T x) {
+    return dpp_mov<kWaveShr1>(id, x);
+}
+
+// Value of lane `lane` broadcast to the whole wave (a scalar register).
+template <class T>
+__device__ __forceinline__ T wave_read(T x, int lane) {
+    static_assert(sizeof(T) % 4 == 0, "readlane moves 32-bit words");
+    struct W { int w[sizeof(T) / 4]; };
+    W s = __builtin_bit_cast(W, x), r;
+#pragma unroll
+    for (int i = 0; i < int(sizeof(T) / 4); i++) r.w[i] = __builtin_amdgcn_readlane(s.w[i], lane);
+    return __builtin_bit_cast(T, r);
+}
+
+template <class Op, class T>
+__device__ __forceinline__ T wave_reduce(T x) {
+    return wave_read(wave_scan_incl<Op>(x), kWave - 1);
+}
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// --------------------------------------------------------- tile descriptors --
+//
+// A tile publishes its aggregate (state A) and later its inclusive prefix
+// (state P) in `words` 64-bit descriptor words.  Each word carries one 32-bit
+// chunk of the carry value in its low half and, in its high half, the tag
+// (epoch << 2 | state).  Any word whose tag is not the current epoch reads as
+// X (nothing published), so a stale workspace needs no clearing.  A value
+// wider than 32 bits spans several words written one after another; a
+// reader accepts it only when every word carries the same tag, which is
+// unambiguous because each state is written exactly once per call.  Plain
+// agent-scope atomic loads and stores suffice: no fence is needed, since a
+// reader never combines a tag with a value from another write.
+
+constexpr uint32_t kStateA = 1u, kStateP = 2u;
+constexpr uint32_t kEpochMask = 0x3fffffffu;
+
+template <class C>
+struct Desc {
+    static constexpr int kWords = int(sizeof(C) / 4);
+    struct Chunks { uint32_t w[kWords]; };
+
+    __device__ __forceinline__ static void publish(uint64_t *d, uint32_t tag, C value) {
+        Chunks c = __builtin_bit_cast(Chunks, value);
+#pragma unroll
+        for (int i = 0; i < kWords; i++)
+            __hip_atomic_store(d + i, (uint64_t(tag) << 32) | c.w[i], __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    }
+
+    // Returns kStateA / kStateP when all words carry that state of `epoch`,
+    // 0 otherwise (not yet published, or caught between two word writes).
+    __device__ __forceinline__ static uint32_t read(const uint64_t *d, uint32_t epoch, C &value) {
+        uint64_t w[kWords];
+#pragma unroll
+        for (int i = 0; i < kWords; i++)
+            w[i] = __hip_atomic_load(d + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t tag = uint32_t(w[0] >> 32);
+        bool ok = (tag >> 2) == epoch && (tag & 3u) != 0u;
+        Chunks c;
+#pragma unroll
+        for (int i = 0; i < kWords; i++) {
+            ok = ok && uint32_t(w[i] >> 32) == tag;
+            c.w[i] = uint32_t(w[i]);
+        }
+        value = __builtin_bit_cast(C, c);
+        return ok ? (tag & 3u) : 0u;
+    }
+};
+
+// Workspace header (first 256 bytes of the workspace).
+struct WsHeader {
+    uint32_t started;     // workgroups of the running call that have read the epoch; 0 between calls
+    uint32_t epoch;       // tag of the running call's descriptors
+    uint64_t high_water;  // descriptor words written since the last full clear
+    uint32_t error;       // nonzero: a wait gave up (see kErr*)
+};
+constexpr size_t kWsHeaderBytes = 256;
+constexpr uint32_t kErrSpin = 1u, kErrStart = 2u;
+
+__device__ __forceinline__ void flag_error(WsHeader *hdr, uint32_t code) {
+    __hip_atomic_fetch_or(&hdr->error, code, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Start of a call that publishes descriptors: thread 0 reads the epoch and
+// then counts this workgroup in `started` with a fire-and-forget atomic whose
+// operand depends on the loaded epoch, so the read has returned before the
+// count is made.  Whoever later sees every workgroup counted therefore knows
+// that no workgroup will read the epoch again.  Call with the whole
+// workgroup; contains a barrier; returns the epoch.
+__device__ __forceinline__ uint32_t begin_call(WsHeader *hdr, uint32_t &s_epoch) {
+    if (threadIdx.x == 0) {
+        const uint32_t e = __hip_atomic_load(&hdr->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(&hdr->started, 1u + (e >> 30), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_epoch = e;
+    }
+    __syncthreads();
+    return s_epoch;
+}
+
+// End of such a call, run by one workgroup after its last descriptor write:
+// wait until all `participants` workgroups are counted, then reset the count
+// and advance the epoch for the next call on this workspace.  When the
+// 30-bit epoch wraps, words beyond this call's (up to the high-water mark,
+// within the workspace) that older calls tagged could alias the new epoch,
+// so they are cleared; words below `words_used` were rewritten by this call
+// with a different tag.  Bounded like every wait here.  Whole workgroup.
+__device__ __forceinline__ void end_call(WsHeader *hdr, uint32_t participants, uint32_t epoch,
+                                         uint64_t words_used, uint64_t ws_words, uint64_t *desc,
+                                         uint32_t spin_limit, uint64_t &s_clear_end) {
+    if (threadIdx.x == 0) {
+        uint64_t clear_end = 0;
+        uint32_t polls = 0;
+        while (__hip_atomic_load(&hdr->started, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < participants) {
+            if (++polls > spin_limit) {
+                flag_error(hdr, kErrStart);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
+        const uint32_t next = (epoch + 1u) & kEpochMask;
+        const uint64_t hw = __hip_atomic_load(&hdr->high_water, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (next == 0u) {
+            clear_end = hw < ws_words ? hw : ws_words;
+            __hip_atomic_store(&hdr->high_water, words_used, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else if (words_used > hw) {
+            __hip_atomic_store(&hdr->high_water, words_used, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __hip_atomic_store(&hdr->started, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&hdr->epoch, next, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_clear_end = clear_end;
+    }
+    __syncthreads();
+    const uint64_t clear_end = s_clear_end;
+    if (clear_end > words_used) {  // uniform over the workgroup; once per 2^30 calls
+        for (uint64_t i = words_used + threadIdx.x; i < clear_end; i += blockDim.x)
+            __hip_atomic_store(desc + i, uint64_t(0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// Decoupled look-back by one wave (The CUDA Handbook ch. 13, Figure 13-11):
+// lane L inspects the descriptor of tile `frontier - L`, nearest first.  The
+// window is re-read until no lane sees X; the nearest lane in state P ends
+// the walk, and the values of lanes 0..that lane (aggregates, then that
+// prefix) are combined.  With no P in the window, all 64 aggregates are
+// combined and the window moves 64 tiles back.  Tiles before `first` (the
+// start of the segment) count as P with the identity.  Returns the exclusive
+// prefix of tile `tile`, the same value in every lane.  Operators must be
+// commutative: the window is combined in lane order, not tile order.
+//
+// Every wait is bounded: after `spin_limit` polls of one window the wave
+// flags kErrSpin in the header and takes the unpublished lanes as P with the
+// identity, so the kernel always finishes (with a wrong result that the
+// flag reports) instead of spinning forever on a tile that never runs.
+template <class Op, class C>
+__device__ __forceinline__ C lookback(const uint64_t *desc, uint32_t epoch, int64_t tile, int64_t first,
+                                      WsHeader *hdr, uint32_t spin_limit) {
+    const int lane = lane_id();
+    const C id = Op::template identity<C>();
+    C excl = id;
+    int64_t frontier = tile - 1;
+    for (;;) {
+        const int64_t p = frontier - lane;
+        uint32_t st;
+        C v;
+        for (uint32_t polls = 0;; polls++) {
+            if (p >= first) {
+                st = Desc<C>::read(desc + p * Desc<C>::kWords, epoch, v);
+            } else {
+                st = kStateP;
+                v = id;
+            }
+            if (!__any(st == 0u)) break;
+            if (polls >= spin_limit) {
+                if (lane == 0) flag_error(hdr, kErrSpin);
+                if (st == 0u) {
+                    st = kStateP;
+                    v = id;
+                }
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+        const uint64_t pmask = __ballot(st == kStateP);
+        const int first_p = pmask ? __builtin_ctzll(pmask) : kWave;
+        const C contrib = (lane <= first_p) ? v : id;
+        excl = Op::apply(wave_reduce<Op>(contrib), excl);
+        if (pmask) break;
+        frontier -= kWave;
+    }
+    return excl;
+}
+
+// ---------------------------------------------------------- vector access --
+
+template <class T, int V>
+struct alignas(sizeof(T) * V) Vec {
+    T v[V];
+};
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// 128-bit (or element-wide) accesses that bypass cache allocation: every
+// input is read once and every output written once, so streaming through
+// the caches only evicts data others could use.
+template <class T, int V>
+__device__ __forceinline__ Vec<T, V> load_vec(const T *p) {
+    constexpr int B = int(sizeof(T)) * V;
+    if constexpr (B == 16) {
+        return __builtin_bit_cast(Vec<T, V>, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p)));
+    } else if constexpr (B == 8) {
+        return __builtin_bit_cast(Vec<T, V>, __builtin_nontemporal_load(reinterpret_cast<const uint64_t *>(p)));
+    } else {
+        static_assert(B == 4, "vector access of 4, 8 or 16 bytes");
+        return __builtin_bit_cast(Vec<T, V>, __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(p)));
+    }
+}
+
+template <class T, int V>
+__device__ __forceinline__ void store_vec(T *p, const Vec<T, V> &x) {
+    constexpr int B = int(sizeof(T)) * V;
+    if constexpr (B == 16) {
+        __builtin_nontemporal_store(__builtin_bit_cast(u32x4_t, x), reinterpret_cast<u32x4_t *>(p));
+    } else if constexpr (B == 8) {
+        __builtin_nontemporal_store(__builtin_bit_cast(uint64_t, x), reinterpret_cast<uint64_t *>(p));
+    } else {
+        static_assert(B == 4, "vector access of 4, 8 or 16 bytes");
+        __builtin_nontemporal_store(__builtin_bit_cast(uint32_t, x), reinterpret_cast<uint32_t *>(p));
+    }
+}
+
+}  // namespace sw64

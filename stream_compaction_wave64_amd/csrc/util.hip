@@ -1,0 +1,65 @@
+// util.hip -- fill kernels (workspace initialisation, empty outputs) and the
+// copy kernel that measures the attainable read+write bandwidth with the same
+// 128-bit access pattern and tile shape as the fp32 scan.
+#include "device.hpp"
+#include "launch.hpp"
+
+namespace sw64 {
+
+__global__ __launch_bounds__(256) void k_fill_u64(uint64_t *p, uint64_t words, uint64_t value) {
+    for (uint64_t i = uint64_t(blockIdx.x) * 256 + threadIdx.x; i < words; i += uint64_t(gridDim.x) * 256)
+        p[i] = value;
+}
+
+__global__ __launch_bounds__(256) void k_fill_i32(int32_t *p, int64_t count, int32_t value) {
+    for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < count; i += int64_t(gridDim.x) * 256)
+        p[i] = value;
+}
+
+int launch_fill_u64(void *p, uint64_t words, uint64_t value, hipStream_t s) {
+    if (words == 0) return SCAN_OK;
+    const uint64_t blocks = (words + 255) / 256;
+    hipLaunchKernelGGL(k_fill_u64, dim3(unsigned(blocks < 4096 ? blocks : 4096)), dim3(256), 0, s,
+                       reinterpret_cast<uint64_t *>(p), words, value);
+    return hipGetLastError() == hipSuccess ? SCAN_OK : SCAN_ERR_HIP;
+}
+
+int launch_fill_i32(int32_t *p, int64_t count, int32_t value, hipStream_t s) {
+    if (count <= 0) return SCAN_OK;
+    const int64_t blocks = (count + 255) / 256;
+    hipLaunchKernelGGL(k_fill_i32, dim3(unsigned(blocks < 4096 ? blocks : 4096)), dim3(256), 0, s, p, count,
+                       value);
+    return hipGetLastError() == hipSuccess ? SCAN_OK : SCAN_ERR_HIP;
+}
+
+// Copy ceiling: tiles of 256 threads x 8 rows x 16 bytes, one tile per
+// workgroup, each row one 1 KiB-per-wave 128-bit nontemporal access (the
+// access the scan tiles use).
+constexpr int kCopyBlock = 256, kCopyRows = 8;
+
+__global__ __launch_bounds__(kCopyBlock) void k_copy16(const uint32_t *in, uint32_t *out, int64_t vecs) {
+    const int64_t base = int64_t(blockIdx.x) * kCopyBlock * kCopyRows;
+    Vec<uint32_t, 4> x[kCopyRows];
+#pragma unroll
+    for (int r = 0; r < kCopyRows; r++) {
+        const int64_t i = base + int64_t(r) * kCopyBlock + threadIdx.x;
+        x[r] = load_vec<uint32_t, 4>(in + 4 * (i < vecs ? i : base));
+    }
+#pragma unroll
+    for (int r = 0; r < kCopyRows; r++) {
+        const int64_t i = base + int64_t(r) * kCopyBlock + threadIdx.x;
+        if (i < vecs) store_vec<uint32_t, 4>(out + 4 * i, x[r]);
+    }
+}
+
+int launch_copy(const void *in, void *out, size_t bytes, hipStream_t s) {
+    const int64_t vecs = int64_t(bytes / 16);
+    if (vecs == 0) return SCAN_OK;
+    const int64_t per = int64_t(kCopyBlock) * kCopyRows;
+    const int64_t blocks = (vecs + per - 1) / per;
+    hipLaunchKernelGGL(k_copy16, dim3(unsigned(blocks)), dim3(kCopyBlock), 0, s,
+                       reinterpret_cast<const uint32_t *>(in), reinterpret_cast<uint32_t *>(out), vecs);
+    return hipGetLastError() == hipSuccess ? SCAN_OK : SCAN_ERR_HIP;
+}
+
+}  // namespace sw64

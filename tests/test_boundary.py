@@ -1,0 +1,123 @@
+"""Host-side checks of the C ABI (no GPU): the library builds and loads, it
+exports every function include/scan_wave64.h declares, the planner's tile
+arithmetic, and argument errors that are rejected before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "scan_wave64.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from stream_compaction_wave64_amd import binding
+    if not os.path.exists(binding.LIB_PATH):
+        from stream_compaction_wave64_amd import build
+        build.build()
+    return binding.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("scan_inclusive", "scan_exclusive", "scan_dim", "compact_if", "pack_offsets",
+                     "pack_emit_neighbors", "scan_plan", "scan_workspace_bytes", "scan_workspace_init",
+                     "scan_status_string"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    from stream_compaction_wave64_amd import binding
+    assert set(binding.EXPORTS) == set(declared_functions())
+
+
+def test_header_compiles_as_c():
+    import subprocess
+    import tempfile
+    with tempfile.TemporaryDirectory() as d:
+        src = os.path.join(d, "t.c")
+        open(src, "w").write('#include "scan_wave64.h"\nint main(void){scan_plan_t p; (void)p; return 0;}\n')
+        subprocess.check_call(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.dirname(HEADER), "-c", src,
+                               "-o", os.path.join(d, "t.o")])
+
+
+def test_status_strings(lib):
+    for code in (0, -1, -2, -3, -4, -5):
+        assert lib.scan_status_string(code)
+    assert b"unknown" in lib.scan_status_string(-99)
+    assert b"gfx950" in lib.scan_version()
+
+
+def test_plan_fp32_metric_shape():
+    from stream_compaction_wave64_amd import binding
+    import torch
+    p = binding.plan("scan", torch.float32, "sum", 1, 10 ** 8)
+    assert p["kernel"] == "lookback" and p["vec"] == 4
+    assert p["tile_elems"] == p["block_size"] * p["items_per_thread"]
+    assert p["num_tiles"] == -(-10 ** 8 // p["tile_elems"])
+    assert p["carry_words"] == 2  # fp32 sums carry in fp64 between tiles
+    assert p["launches"] == 1
+    assert p["workspace_bytes"] >= 256 + p["num_tiles"] * 16
+
+
+def test_plan_segments_and_types():
+    from stream_compaction_wave64_amd import binding
+    import torch
+    p = binding.plan("scan", torch.int32, "sum", 4096, 4096)
+    assert p["num_tiles"] == 4096 * -(-4096 // p["tile_elems"])
+    assert p["carry_words"] == 1
+    p = binding.plan("scan", torch.float64, "max", 1, 10 ** 7)
+    assert p["carry_words"] == 2 and p["vec"] == 2
+    p = binding.plan("scan", torch.float32, "max", 1, 1000)
+    assert p["carry_words"] == 1
+    p = binding.plan("scan", torch.float32, "sum", 1, 1000, tuning={"block_size": 256, "items_per_thread": 4})
+    assert p["tile_elems"] == 1024
+    with pytest.raises(binding.ScanError):
+        binding.plan("scan", torch.float32, "sum", 1, 1000, tuning={"block_size": 192, "items_per_thread": 4})
+
+
+def _call_scan(lib, fn, inp, out, n, dt=3, op=0, width=1, ws=None, wsb=0):
+    return getattr(lib, fn)(inp, out, n, dt, op, width, ws, wsb, None, None)
+
+
+def test_argument_errors_before_launch(lib):
+    fake = ctypes.c_void_p(1 << 20)
+    ws = ctypes.c_void_p(1 << 24)
+    for fn in ("scan_inclusive", "scan_exclusive"):
+        assert _call_scan(lib, fn, None, None, 0) == 0           # n == 0: no-op
+        assert _call_scan(lib, fn, None, fake, 10) == -1         # NULL input
+        assert _call_scan(lib, fn, fake, None, 10) == -1         # NULL output
+        assert _call_scan(lib, fn, fake, fake, -1) == -1         # negative size
+        assert _call_scan(lib, fn, fake, fake, 10, dt=9) == -1   # bad dtype
+        assert _call_scan(lib, fn, fake, fake, 10, op=7) == -1   # bad op
+        assert _call_scan(lib, fn, fake, fake, 10, width=0) == -1
+        assert _call_scan(lib, fn, fake, fake, 10, ws=None, wsb=0) == -3        # no workspace
+        assert _call_scan(lib, fn, fake, fake, 10 ** 6, ws=ws, wsb=300) == -3   # too small
+        assert _call_scan(lib, fn, fake, fake, 10, ws=ctypes.c_void_p((1 << 24) + 8), wsb=1 << 20) == -3
+    assert lib.scan_dim(fake, fake, 2, 3, 0, 3, 0, 0, ws, 1 << 20, None, None) == -1  # inner < 1
+    assert lib.scan_dim(fake, fake, 0, 3, 1, 3, 0, 0, None, 0, None, None) == 0       # empty
+    assert lib.pack_offsets(fake, -1, fake, ws, 1 << 20, None, None) == -1
+    assert lib.pack_offsets(fake, 1 << 31, fake, ws, 1 << 20, None, None) == -5     # int32 overflow
+    assert lib.scan_copy(fake, fake, 17, None) == -1
+
+
+def test_workspace_bound_covers_plans():
+    from stream_compaction_wave64_amd import binding
+    import torch
+    for dt in (torch.int32, torch.float32, torch.float64, torch.int64):
+        for n in (4, 1000, 10 ** 6, 10 ** 8):
+            for tuning in (None, {"block_size": 256, "items_per_thread": 16 // torch.empty(0, dtype=dt).element_size()}):
+                p = binding.plan("scan", dt, "sum", 1, n, tuning=tuning)
+                assert p["workspace_bytes"] <= binding.scan_workspace_bytes(dt, n)

@@ -1,0 +1,230 @@
+"""GPU parity of the single-pass look-back scan against the CPU oracle.
+
+Sizes span one partial tile, exact tile multiples, several tiles with a
+ragged tail, and many tiles forced by a small explicit tile shape; every
+dtype x op x inclusive/exclusive; aligned (128-bit) and misaligned
+(element-wide) access; in-place; the full-size metric and fp64 configs."""
+import numpy as np
+import pytest
+import torch
+
+import stream_compaction_wave64_amd as sw
+from stream_compaction_wave64_amd import inputs
+from gpu_util import DEV, TORCH, assert_scan_matches, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+DTYPES = [np.int32, np.uint32, np.int64, np.float32, np.float64]
+OPS = ["sum", "prod", "max", "min"]
+
+
+def _input(dt, n, seed, op):
+    kind = "near1" if op == "prod" and np.issubdtype(dt, np.floating) else "wide"
+    if op == "sum" and np.issubdtype(dt, np.floating):
+        kind = "default"
+    return inputs.generic(dt, n, seed, kind)
+
+
+def _run(x, op, exclusive, tuning=None, offset=0):
+    """Scan x on the device; offset > 0 shifts the data off 16-byte alignment."""
+    if offset:
+        buf = to_dev(np.concatenate([np.zeros(offset, x.dtype), x]))
+        xd = buf[offset:]
+        outbuf = torch.empty(x.size + offset, dtype=xd.dtype, device=DEV)
+        out = outbuf[offset:]
+    else:
+        xd = to_dev(x)
+        out = None
+    fn = sw.scan_exclusive if exclusive else sw.scan_inclusive
+    res = fn(xd, op=op, out=out, tuning=tuning)
+    torch.cuda.synchronize()
+    return to_host(res)
+
+
+@pytest.mark.parametrize("dt", DTYPES, ids=lambda d: np.dtype(d).name)
+@pytest.mark.parametrize("op", OPS)
+@pytest.mark.parametrize("exclusive", [False, True], ids=["incl", "excl"])
+def test_parity_default_tiles(dt, op, exclusive):
+    p = sw.plan("scan", TORCH[np.dtype(dt)], op, 1, 10 ** 6)
+    tile = p["tile_elems"]
+    for i, n in enumerate([1, 2, 3, 63, 64, 65, 1000, tile - 4, tile, tile + 4, 3 * tile + 12,
+                           64 * tile - 4, 65 * tile + 4, 200_003]):
+        x = _input(dt, n, 100 + i, op)
+        assert_scan_matches(x, _run(x, op, exclusive), op, exclusive, what=f"n={n}")
+
+
+@pytest.mark.parametrize("dt", DTYPES, ids=lambda d: np.dtype(d).name)
+@pytest.mark.parametrize("op", OPS)
+def test_parity_many_small_tiles(dt, op):
+    # one row per tile: tile = 256 x vec elements, so 1e5 elements make
+    # hundreds of tiles and the look-back walks windows of 64
+    vec = 16 // np.dtype(dt).itemsize
+    tuning = {"block_size": 256, "items_per_thread": vec}
+    for n, seed in ((100_000, 1), (256 * vec * 70 + 8, 2)):
+        x = _input(dt, n, seed, op)
+        for excl in (False, True):
+            assert_scan_matches(x, _run(x, op, excl, tuning), op, excl, what=f"n={n} excl={excl}")
+
+
+@pytest.mark.parametrize("dt", DTYPES, ids=lambda d: np.dtype(d).name)
+@pytest.mark.parametrize("grid", [1, 2, 3, 7, 64])
+def test_parity_small_persistent_grid(dt, grid):
+    # a grid of a few workgroups makes each one scan many tiles in turn,
+    # exercising the prefetch alternation and look-back across rounds
+    vec = 16 // np.dtype(dt).itemsize
+    tuning = {"block_size": 256, "items_per_thread": vec, "grid_blocks": grid}
+    for n, seed in ((256 * vec * 37 + 4 * vec, 3), (256 * vec * 2, 4), (5 * vec, 5)):
+        x = _input(dt, n, seed, "sum")
+        for excl in (False, True):
+            assert_scan_matches(x, _run(x, "sum", excl, tuning), "sum", excl, what=f"n={n} excl={excl}")
+
+
+@pytest.mark.parametrize("dt", DTYPES, ids=lambda d: np.dtype(d).name)
+def test_parity_misaligned_elementwise(dt):
+    for n in (1, 5, 3001, 100_001):
+        x = _input(dt, n, 7, "sum")
+        for excl in (False, True):
+            assert_scan_matches(x, _run(x, "sum", excl, offset=1), "sum", excl, what=f"n={n}")
+            assert_scan_matches(x, _run(x, "max", excl, offset=1), "max", excl, what=f"n={n}")
+
+
+@pytest.mark.parametrize("dt", [np.float32, np.float64], ids=["float32", "float64"])
+def test_prod_of_powers_of_two_bit_exact(dt):
+    # factors 2^d with d in {-1, 0, 1} steered to keep the exponent walk inside
+    # [-60, 60]: every partial product is exact, so any association must give
+    # the oracle's value bit for bit (a dropped or repeated factor shows).
+    rng = np.random.default_rng(31)
+    n = 300_001
+    d = rng.integers(-1, 2, n)
+    e = 0
+    for i in range(n):
+        if abs(e + d[i]) > 60:
+            d[i] = -d[i]
+        e += d[i]
+    x = np.ldexp(np.ones(n), d).astype(dt)
+    for excl in (False, True):
+        for tuning in (None, {"block_size": 256, "items_per_thread": 16 // np.dtype(dt).itemsize}):
+            got = _run(x, "prod", excl, tuning)
+            ref = __import__("oracle").scan(x, "prod", exclusive=excl).astype(dt)
+            assert np.array_equal(got, ref), f"excl={excl} tuning={tuning}"
+
+
+def test_in_place():
+    x = inputs.generic(np.int32, 300_001, 9, "wide")
+    xd = to_dev(x)
+    sw.scan_inclusive(xd, out=xd)
+    torch.cuda.synchronize()
+    assert_scan_matches(x, to_host(xd), "sum", False)
+    y = inputs.generic(np.float32, 123_457 * 4, 10)
+    yd = to_dev(y)
+    sw.scan_exclusive(yd, out=yd)
+    torch.cuda.synchronize()
+    assert_scan_matches(y, to_host(yd), "sum", True)
+
+
+def test_repeated_calls_reuse_workspace():
+    # descriptors are tagged with a per-workspace epoch: back-to-back calls of
+    # different sizes and types on one workspace must not see each other's
+    x = inputs.generic(np.int32, 500_000, 11, "wide")
+    xd = to_dev(x)
+    f = inputs.generic(np.float64, 77_777, 12)
+    fd = to_dev(f)
+    for k in range(20):
+        a = sw.scan_inclusive(xd if k % 2 == 0 else xd[: 100_000 + k])
+        b = sw.scan_exclusive(fd, op="sum")
+        torch.cuda.synchronize()
+        assert_scan_matches(x if k % 2 == 0 else x[: 100_000 + k], to_host(a), "sum", False, what=f"k={k}")
+        assert_scan_matches(f, to_host(b), "sum", True, what=f"k={k}")
+
+
+def test_epoch_wrap_clears_stale_descriptors():
+    # A large call at epoch 2 leaves descriptors tagged 2.  The header is then
+    # moved to just below the 30-bit wrap; small calls cross the wrap (the
+    # wrapping call must clear the words beyond its own up to the high-water
+    # mark) and reach epoch 2 again, where a large call on different data
+    # would otherwise accept the stale tag-2 descriptors as published.
+    from stream_compaction_wave64_amd import binding
+    ws = torch.zeros(1 << 22, dtype=torch.uint8, device=DEV)
+    hdr = ws[:16].view(torch.int32)
+    words = ws[256:].view(torch.int64)
+    big1 = inputs.generic(np.int32, 2_000_003, 13, "wide")
+    big2 = inputs.generic(np.int32, 2_000_003, 16, "wide")
+    small = inputs.generic(np.int32, 50_000, 14, "wide")
+    tiles_big = -(-big1.size // sw.plan("scan", torch.int32, "sum", 1, big1.size)["tile_elems"])
+    tiles_small = -(-small.size // sw.plan("scan", torch.int32, "sum", 1, small.size)["tile_elems"])
+    key = (torch.device(DEV).index, binding._stream(torch.device(DEV)))
+    saved = binding.workspaces._ws.get(key)
+    binding.workspaces._ws[key] = ws
+    try:
+        hdr[1] = 2
+        r = sw.scan_inclusive(to_dev(big1))
+        torch.cuda.synchronize()
+        assert_scan_matches(big1, to_host(r), "sum", False, what="big at epoch 2")
+        assert int(hdr[1].item()) == 3 and int(hdr[2].item()) == tiles_big
+        hdr[1] = (1 << 30) - 2
+        sd = to_dev(small)
+        for k in range(4):
+            r = sw.scan_inclusive(sd)
+            torch.cuda.synchronize()
+            assert_scan_matches(small, to_host(r), "sum", False, what=f"small call {k}")
+            if k == 1:  # this call wrapped the epoch to 0
+                assert int(hdr[1].item()) == 0
+                assert not words[tiles_small:tiles_big].any().item()
+        assert int(hdr[1].item()) == 2
+        r = sw.scan_inclusive(to_dev(big2))
+        torch.cuda.synchronize()
+        assert_scan_matches(big2, to_host(r), "sum", False, what="big at epoch 2 after the wrap")
+    finally:
+        if saved is None:
+            binding.workspaces._ws.pop(key, None)
+        else:
+            binding.workspaces._ws[key] = saved
+
+
+def test_empty_and_degenerate():
+    e = torch.empty(0, dtype=torch.float32, device=DEV)
+    assert sw.scan_inclusive(e).numel() == 0
+    one = to_dev(np.array([2.5], np.float32))
+    assert to_host(sw.scan_inclusive(one))[0] == 2.5
+    assert to_host(sw.scan_exclusive(one))[0] == 0.0
+    assert to_host(sw.scan_exclusive(one, op="max"))[0] == -np.inf
+    assert to_host(sw.scan_exclusive(to_dev(np.array([7], np.int32)), op="min"))[0] == np.iinfo(np.int32).max
+
+
+def test_config_int32_2pow20_bit_exact():
+    x = inputs.int32_uniform_0_100(2 ** 20, seed=0)
+    xd = to_dev(x)
+    for excl in (False, True):
+        fn = sw.scan_exclusive if excl else sw.scan_inclusive
+        r = fn(xd)
+        torch.cuda.synchronize()
+        assert_scan_matches(x, to_host(r), "sum", excl, what=f"C1 excl={excl}")
+
+
+def test_config_fp32_1e8_within_tolerance():
+    x = inputs.f32_uniform_01(10 ** 8, seed=1)
+    r = sw.scan_inclusive(to_dev(x))
+    torch.cuda.synchronize()
+    assert_scan_matches(x, to_host(r), "sum", False, what="fp32 1e8")
+
+
+def test_config_fp64_1e7_within_tolerance():
+    x = inputs.f64_uniform_pm1(10 ** 7, seed=1)
+    r = sw.scan_inclusive(to_dev(x))
+    torch.cuda.synchronize()
+    assert_scan_matches(x, to_host(r), "sum", False, what="fp64 1e7")
+
+
+def test_beyond_2pow31_elements_sampled():
+    # int32 all-ones over 2^31 + 1027 elements: element i is (i + 1) mod 2^32;
+    # exercises 64-bit element offsets; checked on samples and the tail.
+    n = 2 ** 31 + 1027
+    x = torch.ones(n, dtype=torch.int32, device=DEV)
+    out = sw.scan_inclusive(x)
+    torch.cuda.synchronize()
+    del x
+    rng = np.random.default_rng(15)
+    idx = np.concatenate([rng.integers(0, n, 200_000), np.arange(n - 5000, n), np.arange(2 ** 31 - 10, 2 ** 31 + 10)])
+    got = to_host(out[torch.from_numpy(idx).to(DEV)])
+    want = ((idx + 1) % (1 << 32)).astype(np.uint32).view(np.int32)
+    assert np.array_equal(got, want)
