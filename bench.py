@@ -24,10 +24,22 @@ import numpy as np
 METRIC = "GElem/s and % of HBM roofline, fp32 inclusive scan n=1e8 on 1 MI355X"
 HBM_PEAK_GBS = 8000.0
 N = 10 ** 8
-# HBM bytes per launch as measured with rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
-# on the current scan kernel, scaled by the plain-copy calibration factor
-# (null until counters exist for the kernel as built).
-TRAFFIC_BYTES = None
+# HBM bytes per launch measured with rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE on
+# the scan kernel, each scaled by what the counter reads for the copy kernel of
+# known size (profiles/lookback_scan_fp32_1e8_hbm_counters.md).  Valid only for
+# the kernel sources that were measured: reported as null once they change.
+TRAFFIC_BYTES = 8.044e8
+TRAFFIC_SOURCES_SHA = "42001f70c2cfdd68"
+
+
+def _kernel_sources_sha():
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "stream_compaction_wave64_amd", "csrc")
+    for f in ("lookback.hip", "tile.hpp", "device.hpp"):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def parse():
@@ -125,7 +137,10 @@ def main():
                    "items_per_thread": plan["items_per_thread"], "tile_elems": plan["tile_elems"],
                    "num_tiles": plan["num_tiles"]},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": TRAFFIC_BYTES},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": TRAFFIC_BYTES if (_kernel_sources_sha() == TRAFFIC_SOURCES_SHA
+                                                  and args.algo == "lookback" and not args.block
+                                                  and not args.ipt) else None},
         "copy_ceiling": {"achieved": round(copy_gbs, 1), "unit": "GB/s", "frac": round(copy_gbs / HBM_PEAK_GBS, 4),
                          "scan_vs_copy": round(achieved / copy_gbs, 4)},
     }

@@ -45,9 +45,10 @@
  * workspace epoch held in the workspace header and advance it at the end of
  * each call, so no clearing launch is needed between calls.  Calls that may
  * overlap in time (different streams) need distinct workspaces.  Layout
- * (informative): bytes [0, 256) header { uint32 count of started workgroups,
- * uint32 epoch, uint64 descriptor high-water mark in words, uint32 error },
- * then 64-bit descriptor words.
+ * (informative): bytes [0, 4096) header { uint32 epoch, uint32 error word,
+ * uint64 descriptor high-water mark, uint32 mode, uint32 claim counter, and
+ * sixteen counters of started workgroups, one per 128-byte line from byte
+ * 128 }, then 64-bit descriptor words.
  */
 #ifndef SCAN_WAVE64_H
 #define SCAN_WAVE64_H
@@ -118,6 +119,9 @@ typedef struct {
                                   a few seconds); tests force tiny values */
     int32_t grid_blocks;       /* cap on the persistent look-back grid (default:
                                   every workgroup that can be resident) */
+    int32_t mode_limit;        /* polls a call waits for all of its workgroups
+                                  to start before it claims tiles dynamically
+                                  instead (default 512); tests force tiny values */
 } scan_tuning_t;
 
 /* Kernel family a call runs (reported by scan_plan). */
@@ -164,11 +168,13 @@ size_t scan_workspace_bytes(scan_dtype_t dtype, int64_t count);
 int scan_workspace_init(void *ws, size_t ws_bytes, void *stream);
 
 /* Diagnostic (synchronizes `stream`): copy the workspace's error word to
- * *error.  Nonzero means a wait gave up after spin_limit polls: a look-back
- * window (bit 0) or the end-of-call count of started workgroups (bit 1),
- * e.g. because the workspace was not zeroed or was used by overlapping
- * calls.  The results of that call are invalid and the workspace must be
- * re-initialised.  Never set in normal operation. */
+ * *error.  Bits 0 and 1 mean a wait gave up after spin_limit polls (a
+ * look-back window, or the end-of-call count of started workgroups), e.g.
+ * because the workspace was not zeroed or was used by overlapping calls: the
+ * results of that call are invalid and the workspace must be re-initialised.
+ * Bit 2 means a call could not confirm that all of its workgroups were
+ * resident and claimed tiles one by one instead (results valid, slower).
+ * None is set in normal operation; the word stays set until re-init. */
 int scan_workspace_error(const void *ws, int32_t *error, void *stream);
 
 /* Inclusive scan of n elements of `width` components each (AoS structs;

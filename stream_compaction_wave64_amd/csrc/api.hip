@@ -30,8 +30,10 @@ LbLaunch find_lookback(scan_dtype_t dt, scan_op_t op, int block, int rows, int v
 
 namespace {
 
-constexpr size_t kHeader = 256;
+constexpr size_t kHeader = 4096;  // workspace header bytes (WsHeader)
 constexpr uint32_t kDefaultSpinLimit = 1u << 22;
+constexpr uint32_t kDefaultModeLimit = 512;
+constexpr int kDefaultBlock = 512, kDefaultRows = 8;  // look-back tile shape
 
 bool valid_dtype(int dt) { return dt >= SCAN_I32 && dt <= SCAN_F64; }
 bool valid_op(int op) { return op >= SCAN_OP_SUM && op <= SCAN_OP_MIN; }
@@ -66,14 +68,19 @@ int plan_lookback(scan_dtype_t dt, scan_op_t op, int64_t outer, int64_t len, boo
                   const scan_tuning_t &tu, LbPlan &p) {
     const int vmax = 16 / dtype_bytes(dt);
     p.vec = (aligned && len % vmax == 0) ? vmax : 1;
-    p.block = tu.block_size > 0 ? tu.block_size : 256;
-    int ipt = tu.items_per_thread > 0 ? tu.items_per_thread : 8 * vmax;
-    if (p.vec == 1 && tu.items_per_thread <= 0) ipt = 8;  // element-wide fallback: 8 rows of 1
+    const int rows_default = dtype_bytes(dt) == 8 ? kDefaultRows / 2 : kDefaultRows;
+    p.block = tu.block_size > 0 ? tu.block_size : kDefaultBlock;
+    int ipt = tu.items_per_thread > 0 ? tu.items_per_thread : rows_default * vmax;
+    if (p.vec == 1 && tu.items_per_thread <= 0) ipt = rows_default;  // element-wide fallback
     if (ipt % p.vec != 0) return SCAN_ERR_UNSUPPORTED;
     p.rows = ipt / p.vec;
     // The element-wide fallback (misaligned data or a length that breaks the
-    // vector alignment) is built for 1 and 8 rows only: snap to the nearer.
-    if (p.vec == 1 && !find_lookback(dt, op, p.block, p.rows, 1)) p.rows = p.rows >= 8 ? 8 : 1;
+    // vector alignment) is built for the default and one-row shapes only:
+    // snap to the nearer.
+    if (p.vec == 1 && !find_lookback(dt, op, p.block, p.rows, 1)) {
+        p.rows = p.rows >= rows_default ? rows_default : 1;
+        p.block = p.rows == 1 ? 256 : kDefaultBlock;
+    }
     if (!find_lookback(dt, op, p.block, p.rows, p.vec)) return SCAN_ERR_UNSUPPORTED;
     p.tile = int64_t(p.block) * p.rows * p.vec;
     p.tiles_per_seg = (len + p.tile - 1) / p.tile;
@@ -90,7 +97,7 @@ bool aligned16(const void *a, const void *b) {
 
 int check_ws(const void *ws, size_t ws_bytes, size_t need) {
     if (ws == nullptr || ws_bytes < need) return SCAN_ERR_WORKSPACE;
-    if (reinterpret_cast<uintptr_t>(ws) & 255u) return SCAN_ERR_WORKSPACE;  // header + descriptors aligned
+    if (reinterpret_cast<uintptr_t>(ws) & 255u) return SCAN_ERR_WORKSPACE;  // 256-byte aligned
     return SCAN_OK;
 }
 
@@ -124,6 +131,7 @@ int scan_common(const void *in, void *out, int64_t outer, int64_t len, int64_t i
     a.words_used = p.tiles_per_seg > 1 ? uint64_t(p.num_tiles) * p.carry_words : 0;
     a.spin_limit = tu.spin_limit > 0 ? uint32_t(tu.spin_limit) : kDefaultSpinLimit;
     a.grid_blocks = tu.grid_blocks > 0 ? uint32_t(tu.grid_blocks) : 0u;
+    a.mode_limit = tu.mode_limit > 0 ? uint32_t(tu.mode_limit) : kDefaultModeLimit;
     return find_lookback(dt, op, p.block, p.rows, p.vec)(a, stream);
 }
 
@@ -181,8 +189,8 @@ int scan_workspace_init(void *ws, size_t ws_bytes, void *stream) {
 int scan_workspace_error(const void *ws, int32_t *error, void *stream) {
     if (ws == nullptr || error == nullptr) return SCAN_ERR_INVALID_ARG;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    // the error word sits after counter, epoch and the 64-bit high-water mark
-    const char *p = reinterpret_cast<const char *>(ws) + 16;
+    // the error word follows the epoch
+    const char *p = reinterpret_cast<const char *>(ws) + 4;
     if (hipMemcpyAsync(error, p, sizeof(int32_t), hipMemcpyDeviceToHost, s) != hipSuccess) return SCAN_ERR_HIP;
     return hipStreamSynchronize(s) == hipSuccess ? SCAN_OK : SCAN_ERR_HIP;
 }

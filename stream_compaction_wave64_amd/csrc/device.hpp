@@ -206,125 +206,214 @@ struct Desc {
     }
 };
 
-// Workspace header (first 256 bytes of the workspace).
+// Workspace header.  Counters that many workgroups update at once sit in
+// separate 128-byte lines: same-address agent-scope atomics serialize at about
+// 11.5 ns each on MI355X, sixteen addresses give about 1 ns each.
 struct WsHeader {
-    uint32_t started;     // workgroups of the running call that have read the epoch; 0 between calls
     uint32_t epoch;       // tag of the running call's descriptors
+    uint32_t error;       // kErr* bits (see flag_error)
     uint64_t high_water;  // descriptor words written since the last full clear
-    uint32_t error;       // nonzero: a wait gave up (see kErr*)
+    uint32_t mode;        // 0 undecided, kModeStatic or kModeDynamic (running call)
+    uint32_t claim;       // next tile ticket in dynamic mode
+    uint32_t pad0[26];
+    struct {
+        uint32_t count;   // workgroups of the running call counted in this slot
+        uint32_t pad[31];
+    } started[16];
 };
-constexpr size_t kWsHeaderBytes = 256;
-constexpr uint32_t kErrSpin = 1u, kErrStart = 2u;
+constexpr size_t kWsHeaderBytes = 4096;
+static_assert(sizeof(WsHeader) <= kWsHeaderBytes, "header fits its reserved bytes");
+constexpr uint32_t kErrSpin = 1u, kErrStart = 2u, kErrFallback = 4u;
+constexpr uint32_t kModeStatic = 1u, kModeDynamic = 2u;
 
 __device__ __forceinline__ void flag_error(WsHeader *hdr, uint32_t code) {
     __hip_atomic_fetch_or(&hdr->error, code, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Start of a call that publishes descriptors: thread 0 reads the epoch and
-// then counts this workgroup in `started` with a fire-and-forget atomic whose
-// operand depends on the loaded epoch, so the read has returned before the
-// count is made.  Whoever later sees every workgroup counted therefore knows
-// that no workgroup will read the epoch again.  Call with the whole
-// workgroup; contains a barrier; returns the epoch.
-__device__ __forceinline__ uint32_t begin_call(WsHeader *hdr, uint32_t &s_epoch) {
-    if (threadIdx.x == 0) {
-        const uint32_t e = __hip_atomic_load(&hdr->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_fetch_add(&hdr->started, 1u + (e >> 30), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_epoch = e;
-    }
-    __syncthreads();
-    return s_epoch;
+template <class U>
+__device__ __forceinline__ U ld(const U *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <class U>
+__device__ __forceinline__ void st(U *p, U v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// End of such a call, run by one workgroup after its last descriptor write:
-// wait until all `participants` workgroups are counted, then reset the count
-// and advance the epoch for the next call on this workspace.  When the
-// 30-bit epoch wraps, words beyond this call's (up to the high-water mark,
-// within the workspace) that older calls tagged could alias the new epoch,
-// so they are cleared; words below `words_used` were rewritten by this call
-// with a different tag.  Bounded like every wait here.  Whole workgroup.
-__device__ __forceinline__ void end_call(WsHeader *hdr, uint32_t participants, uint32_t epoch,
-                                         uint64_t words_used, uint64_t ws_words, uint64_t *desc,
-                                         uint32_t spin_limit, uint64_t &s_clear_end) {
-    if (threadIdx.x == 0) {
-        uint64_t clear_end = 0;
-        uint32_t polls = 0;
-        while (__hip_atomic_load(&hdr->started, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < participants) {
-            if (++polls > spin_limit) {
-                flag_error(hdr, kErrStart);
-                break;
-            }
+// Start of a call that publishes descriptors (thread 0 only): read the epoch,
+// then count this workgroup with a fire-and-forget atomic whose operand
+// depends on the loaded epoch, so the read has returned before the count is
+// made.  Whoever later sees every workgroup counted knows that none will
+// read the epoch again.
+__device__ __forceinline__ uint32_t begin_call(WsHeader *hdr) {
+    const uint32_t e = ld(&hdr->epoch);
+    __hip_atomic_fetch_add(&hdr->started[blockIdx.x & 15].count, 1u + (e >> 30), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    return e;
+}
+
+__device__ __forceinline__ uint32_t started_sum(const WsHeader *hdr) {
+    uint32_t s = 0;
+#pragma unroll
+    for (int i = 0; i < 16; i++) s += ld(&hdr->started[i].count);
+    return s;
+}
+
+// Decide, once per call, how tiles are assigned (thread 0 only).  The static
+// round-robin (workgroup w takes tiles w, w+G, ...) needs all G workgroups
+// resident at once: a resident workgroup may wait on a tile of one that has
+// not started.  The occupancy the runtime reports is not a guarantee (other
+// work may hold compute units, and at full register occupancy it was measured
+// to overstate), so the first workgroup that sees all G counted selects
+// static mode; one that waits `limit` polls without seeing them selects
+// dynamic mode, where tiles are claimed in order from a counter -- slower
+// (one same-address atomic per tile), but deadlock-free with any number of
+// resident workgroups.  No descriptor is published before the decision.
+__device__ __forceinline__ uint32_t decide_mode(WsHeader *hdr, uint32_t G, uint32_t limit) {
+    uint32_t m = ld(&hdr->mode);
+    for (uint32_t polls = 0; m == 0u; polls++) {
+        uint32_t want = 0u;
+        if (started_sum(hdr) >= G) {
+            want = kModeStatic;
+        } else if (polls >= limit) {
+            want = kModeDynamic;
+        }
+        if (want != 0u) {
+            uint32_t expected = 0u;
+            __hip_atomic_compare_exchange_strong(&hdr->mode, &expected, want, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+            if (want == kModeDynamic && expected == 0u) flag_error(hdr, kErrFallback);
+        } else {
             __builtin_amdgcn_s_sleep(2);
         }
+        m = ld(&hdr->mode);
+    }
+    return m;
+}
+
+// End of a call, run by one workgroup once every workgroup is known to have
+// read the epoch: reset the per-call words and advance the epoch for the next
+// call on this workspace.  When the 30-bit epoch wraps, descriptor words
+// beyond this call's (up to the high-water mark, within the workspace) that
+// older calls tagged could alias the new epoch, so they are cleared; words
+// below `words_used` were rewritten by this call with a different tag.
+// Whole workgroup; one barrier.
+__device__ __forceinline__ void end_call(WsHeader *hdr, uint32_t epoch, uint64_t words_used, uint64_t ws_words,
+                                         uint64_t *desc, uint64_t &s_clear_end) {
+    if (threadIdx.x == 0) {
+        uint64_t clear_end = 0;
         const uint32_t next = (epoch + 1u) & kEpochMask;
-        const uint64_t hw = __hip_atomic_load(&hdr->high_water, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint64_t hw = ld(&hdr->high_water);
         if (next == 0u) {
             clear_end = hw < ws_words ? hw : ws_words;
-            __hip_atomic_store(&hdr->high_water, words_used, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            st(&hdr->high_water, words_used);
         } else if (words_used > hw) {
-            __hip_atomic_store(&hdr->high_water, words_used, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            st(&hdr->high_water, words_used);
         }
-        __hip_atomic_store(&hdr->started, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&hdr->epoch, next, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+        for (int i = 0; i < 16; i++) st(&hdr->started[i].count, 0u);
+        st(&hdr->claim, 0u);
+        st(&hdr->mode, 0u);
+        st(&hdr->epoch, next);
         s_clear_end = clear_end;
     }
     __syncthreads();
     const uint64_t clear_end = s_clear_end;
     if (clear_end > words_used) {  // uniform over the workgroup; once per 2^30 calls
-        for (uint64_t i = words_used + threadIdx.x; i < clear_end; i += blockDim.x)
-            __hip_atomic_store(desc + i, uint64_t(0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (uint64_t i = words_used + threadIdx.x; i < clear_end; i += blockDim.x) st(desc + i, uint64_t(0));
     }
 }
 
-// Decoupled look-back by one wave (The CUDA Handbook ch. 13, Figure 13-11):
-// lane L inspects the descriptor of tile `frontier - L`, nearest first.  The
-// window is re-read until no lane sees X; the nearest lane in state P ends
-// the walk, and the values of lanes 0..that lane (aggregates, then that
-// prefix) are combined.  With no P in the window, all 64 aggregates are
-// combined and the window moves 64 tiles back.  Tiles before `first` (the
-// start of the segment) count as P with the identity.  Returns the exclusive
-// prefix of tile `tile`, the same value in every lane.  Operators must be
-// commutative: the window is combined in lane order, not tile order.
+// Static mode's end: the workgroup that finished the last tile waits
+// (bounded) until all G workgroups are counted -- already true when static
+// mode was chosen -- then ends the call.
+__device__ __forceinline__ void end_call_static(WsHeader *hdr, uint32_t G, uint32_t epoch, uint64_t words_used,
+                                                uint64_t ws_words, uint64_t *desc, uint32_t spin_limit,
+                                                uint64_t &s_clear_end) {
+    if (threadIdx.x == 0) {
+        for (uint32_t polls = 0; started_sum(hdr) < G; polls++) {
+            if (polls >= spin_limit) {
+                flag_error(hdr, kErrStart);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
+    }
+    end_call(hdr, epoch, words_used, ws_words, desc, s_clear_end);
+}
+
+// Decoupled look-back by one wave (The CUDA Handbook ch. 13, Figure 13-11),
+// widened for MI355X.  The page's warp inspects the 32 nearest predecessors
+// per step; here every lane reads DEPTH descriptors at once, so one round
+// trip covers the 64*DEPTH nearest predecessors: slot (lane, k) holds tile
+// frontier - lane - 64*k, i.e. distance d = lane + 64*k.  A descriptor read
+// crosses XCDs (~1.3 us), and the frontier of published prefixes advances at
+// most one window per round trip, so the window must span more tiles than
+// the grid finishes per round trip; 64 does not at HBM rate.
+//
+// The window is re-read while any slot nearer than the nearest P is still X.
+// Then the values of slots 0..nearest P (aggregates, then that prefix) are
+// combined; with no P in the window, all of them are combined and the
+// window moves 64*DEPTH tiles back.  Tiles before `first` (the start of the
+// segment) count as P with the identity.  Returns the exclusive prefix of
+// `tile`, the same in every lane.  Operators must be commutative: the window
+// is combined in lane order, not tile order.
 //
 // Every wait is bounded: after `spin_limit` polls of one window the wave
-// flags kErrSpin in the header and takes the unpublished lanes as P with the
+// flags kErrSpin in the header and takes the unpublished slots as P with the
 // identity, so the kernel always finishes (with a wrong result that the
 // flag reports) instead of spinning forever on a tile that never runs.
-template <class Op, class C>
+template <class Op, class C, int DEPTH>
 __device__ __forceinline__ C lookback(const uint64_t *desc, uint32_t epoch, int64_t tile, int64_t first,
                                       WsHeader *hdr, uint32_t spin_limit) {
+    constexpr int kSpan = kWave * DEPTH;
     const int lane = lane_id();
     const C id = Op::template identity<C>();
     C excl = id;
     int64_t frontier = tile - 1;
     for (;;) {
-        const int64_t p = frontier - lane;
-        uint32_t st;
-        C v;
+        uint32_t st[DEPTH];
+        C v[DEPTH];
+        int near_p = kSpan;  // distance of the nearest P (kSpan: none)
         for (uint32_t polls = 0;; polls++) {
-            if (p >= first) {
-                st = Desc<C>::read(desc + p * Desc<C>::kWords, epoch, v);
-            } else {
-                st = kStateP;
-                v = id;
+#pragma unroll
+            for (int k = 0; k < DEPTH; k++) {
+                const int64_t p = frontier - lane - int64_t(kWave) * k;
+                if (p >= first) {
+                    st[k] = Desc<C>::read(desc + p * Desc<C>::kWords, epoch, v[k]);
+                } else {
+                    st[k] = kStateP;
+                    v[k] = id;
+                }
             }
-            if (!__any(st == 0u)) break;
+            int near_x = kSpan;
+            near_p = kSpan;
+#pragma unroll
+            for (int k = DEPTH - 1; k >= 0; k--) {
+                const uint64_t xm = __ballot(st[k] == 0u);
+                const uint64_t pm = __ballot(st[k] == kStateP);
+                if (xm) near_x = kWave * k + __builtin_ctzll(xm);
+                if (pm) near_p = kWave * k + __builtin_ctzll(pm);
+            }
+            if (near_x == kSpan || near_p < near_x) break;
             if (polls >= spin_limit) {
                 if (lane == 0) flag_error(hdr, kErrSpin);
-                if (st == 0u) {
-                    st = kStateP;
-                    v = id;
+#pragma unroll
+                for (int k = 0; k < DEPTH; k++) {
+                    if (st[k] == 0u) v[k] = id;
                 }
+                near_p = near_x;
                 break;
             }
             __builtin_amdgcn_s_sleep(1);
         }
-        const uint64_t pmask = __ballot(st == kStateP);
-        const int first_p = pmask ? __builtin_ctzll(pmask) : kWave;
-        const C contrib = (lane <= first_p) ? v : id;
+        C contrib = id;
+#pragma unroll
+        for (int k = 0; k < DEPTH; k++) {
+            if (lane + kWave * k <= near_p) contrib = Op::apply(v[k], contrib);
+        }
         excl = Op::apply(wave_reduce<Op>(contrib), excl);
-        if (pmask) break;
-        frontier -= kWave;
+        if (near_p < kSpan) break;
+        frontier -= kSpan;
     }
     return excl;
 }

@@ -31,6 +31,7 @@ struct LbArgs {
     uint64_t words_used;      // descriptor words this launch writes
     uint32_t spin_limit;      // polls of one look-back window before giving up
     uint32_t grid_blocks;     // cap on the persistent grid (0 = resident capacity)
+    uint32_t mode_limit;      // polls before a call falls back to dynamic claiming
 };
 using LbLaunch = int (*)(const LbArgs &, hipStream_t);
 LbLaunch find_lookback(scan_dtype_t dt, scan_op_t op, int block, int rows, int vec);

@@ -45,7 +45,7 @@ def test_garbage_epoch_times_out_lookback_and_reinit_recovers():
     x = inputs.generic(np.int32, 400_000, 21, "wide")
     xd = to_dev(x)
     ws = torch.zeros(1 << 20, dtype=torch.uint8, device=DEV)
-    ws[:16].view(torch.int32)[1] = 1 << 30  # an epoch no descriptor tag can carry
+    ws[:16].view(torch.int32)[0] = 1 << 30  # an epoch no descriptor tag can carry
     with _Installed(ws):
         sw.scan_inclusive(xd, tuning={"spin_limit": 32})
         torch.cuda.synchronize()
@@ -53,17 +53,27 @@ def test_garbage_epoch_times_out_lookback_and_reinit_recovers():
         _recovers(ws, x, xd)
 
 
-def test_wrapped_start_count_times_out_end_of_call():
-    x = inputs.generic(np.int32, 400_000, 23, "wide")
+@pytest.mark.parametrize("dt", [np.int32, np.float32, np.float64])
+def test_unconfirmed_residency_falls_back_to_dynamic_claiming(dt):
+    # A start count that wraps past the grid size never confirms that all
+    # workgroups are resident: the call must take the dynamic path (flag bit 2)
+    # and still produce the exact result, over many tiles and small grids.
+    x = inputs.generic(dt, 1_000_003, 23, "wide" if dt == np.int32 else "default")
     xd = to_dev(x)
-    ws = torch.zeros(1 << 20, dtype=torch.uint8, device=DEV)
-    ws[:16].view(torch.int32)[0] = -1  # count of started workgroups wraps past the grid size
-    with _Installed(ws):
-        r = sw.scan_inclusive(xd, tuning={"spin_limit": 32})
-        torch.cuda.synchronize()
-        assert sw.scan_workspace_error(ws) & 2
-        assert_scan_matches(x, to_host(r), "sum", False)  # the scan itself was unaffected
-        _recovers(ws, x, xd)
+    vec = 16 // np.dtype(dt).itemsize
+    for tuning in ({"mode_limit": 8}, {"mode_limit": 8, "block_size": 256, "items_per_thread": vec},
+                   {"mode_limit": 8, "grid_blocks": 5}):
+        ws = torch.zeros(1 << 22, dtype=torch.uint8, device=DEV)
+        ws[128:132].view(torch.int32)[0] = -1  # first started-count slot
+        with _Installed(ws):
+            for excl in (False, True):
+                fn = sw.scan_exclusive if excl else sw.scan_inclusive
+                r = fn(xd, tuning=tuning)
+                torch.cuda.synchronize()
+                assert sw.scan_workspace_error(ws) == 4, tuning
+                assert_scan_matches(x, to_host(r), "sum", excl, what=str(tuning))
+                ws[128:132].view(torch.int32)[0] = -1  # the call reset it; force the fallback again
+            _recovers(ws, x, xd)
 
 
 def test_errors_never_set_in_normal_operation():

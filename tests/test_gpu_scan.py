@@ -145,8 +145,8 @@ def test_epoch_wrap_clears_stale_descriptors():
     # would otherwise accept the stale tag-2 descriptors as published.
     from stream_compaction_wave64_amd import binding
     ws = torch.zeros(1 << 22, dtype=torch.uint8, device=DEV)
-    hdr = ws[:16].view(torch.int32)
-    words = ws[256:].view(torch.int64)
+    hdr = ws[:16].view(torch.int32)  # [0] epoch, [1] error, [2:4] high-water mark
+    words = ws[4096:].view(torch.int64)
     big1 = inputs.generic(np.int32, 2_000_003, 13, "wide")
     big2 = inputs.generic(np.int32, 2_000_003, 16, "wide")
     small = inputs.generic(np.int32, 50_000, 14, "wide")
@@ -156,21 +156,22 @@ def test_epoch_wrap_clears_stale_descriptors():
     saved = binding.workspaces._ws.get(key)
     binding.workspaces._ws[key] = ws
     try:
-        hdr[1] = 2
+        hdr[0] = 2
         r = sw.scan_inclusive(to_dev(big1))
         torch.cuda.synchronize()
         assert_scan_matches(big1, to_host(r), "sum", False, what="big at epoch 2")
-        assert int(hdr[1].item()) == 3 and int(hdr[2].item()) == tiles_big
-        hdr[1] = (1 << 30) - 2
+        assert int(hdr[0].item()) == 3 and int(hdr[2].item()) == tiles_big
+        hdr[0] = (1 << 30) - 2
         sd = to_dev(small)
         for k in range(4):
             r = sw.scan_inclusive(sd)
             torch.cuda.synchronize()
             assert_scan_matches(small, to_host(r), "sum", False, what=f"small call {k}")
             if k == 1:  # this call wrapped the epoch to 0
-                assert int(hdr[1].item()) == 0
+                assert int(hdr[0].item()) == 0
                 assert not words[tiles_small:tiles_big].any().item()
-        assert int(hdr[1].item()) == 2
+        assert int(hdr[0].item()) == 2
+        assert int(hdr[1].item()) == 0  # no error and no fallback along the way
         r = sw.scan_inclusive(to_dev(big2))
         torch.cuda.synchronize()
         assert_scan_matches(big2, to_host(r), "sum", False, what="big at epoch 2 after the wrap")
