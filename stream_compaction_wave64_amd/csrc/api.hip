@@ -4,18 +4,20 @@
 #include <stdint.h>
 #include <string.h>
 
-#include <algorithm>
-
 #include "launch.hpp"
 #include "scan_wave64.h"
 
 namespace sw64 {
 
-LbLaunch find_lookback_i32(scan_op_t, int, int, int);
-LbLaunch find_lookback_u32(scan_op_t, int, int, int);
-LbLaunch find_lookback_i64(scan_op_t, int, int, int);
-LbLaunch find_lookback_f32(scan_op_t, int, int, int);
-LbLaunch find_lookback_f64(scan_op_t, int, int, int);
+#define SW64_DECLARE_PER_TYPE(name, ret)              \
+    ret name##_i32(scan_op_t, int, int, int);       \
+    ret name##_u32(scan_op_t, int, int, int);       \
+    ret name##_i64(scan_op_t, int, int, int);       \
+    ret name##_f32(scan_op_t, int, int, int);       \
+    ret name##_f64(scan_op_t, int, int, int);
+SW64_DECLARE_PER_TYPE(find_lookback, LbLaunch)
+SW64_DECLARE_PER_TYPE(find_rts, RtsLaunch)
+#undef SW64_DECLARE_PER_TYPE
 
 LbLaunch find_lookback(scan_dtype_t dt, scan_op_t op, int block, int rows, int vec) {
     switch (dt) {
@@ -28,15 +30,28 @@ LbLaunch find_lookback(scan_dtype_t dt, scan_op_t op, int block, int rows, int v
     return nullptr;
 }
 
+RtsLaunch find_rts(scan_dtype_t dt, scan_op_t op, int block, int rows, int vec) {
+    switch (dt) {
+    case SCAN_I32: return find_rts_i32(op, block, rows, vec);
+    case SCAN_U32: return find_rts_u32(op, block, rows, vec);
+    case SCAN_I64: return find_rts_i64(op, block, rows, vec);
+    case SCAN_F32: return find_rts_f32(op, block, rows, vec);
+    case SCAN_F64: return find_rts_f64(op, block, rows, vec);
+    }
+    return nullptr;
+}
+
 namespace {
 
-constexpr size_t kHeader = 4096;  // workspace header bytes (WsHeader)
+constexpr size_t kHeader = kWsHeaderBytes;  // workspace header bytes (WsHeader)
 constexpr uint32_t kDefaultSpinLimit = 1u << 22;
 constexpr uint32_t kDefaultModeLimit = 512;
 constexpr int kDefaultBlock = 512, kDefaultRows = 8;  // look-back tile shape
+constexpr int kDefaultRtsBlocks = 1024;               // C of reduce-then-scan
 
 bool valid_dtype(int dt) { return dt >= SCAN_I32 && dt <= SCAN_F64; }
 bool valid_op(int op) { return op >= SCAN_OP_SUM && op <= SCAN_OP_MIN; }
+bool valid_cmp(int c) { return c >= SCAN_CMP_GT && c <= SCAN_CMP_NE; }
 
 int dtype_bytes(scan_dtype_t dt) { return (dt == SCAN_I64 || dt == SCAN_F64) ? 8 : 4; }
 
@@ -55,39 +70,86 @@ scan_tuning_t tuning_or_default(const scan_tuning_t *t) {
     return d;
 }
 
-// Plan of the look-back / reduce-then-scan launch for scalar elements.
-struct LbPlan {
+// Plan of a tiled launch over scalar elements (look-back, reduce-then-scan
+// or compaction).
+struct TilePlan {
+    int kernel;               // scan_kernel_t
     int block, rows, vec;
     int64_t tile;
     int64_t tiles_per_seg, num_tiles;
     int carry_words;
+    int64_t rts_blocks, rts_chunk;
     size_t ws_bytes;
+    int launches;
 };
 
-int plan_lookback(scan_dtype_t dt, scan_op_t op, int64_t outer, int64_t len, bool aligned,
-                  const scan_tuning_t &tu, LbPlan &p) {
-    const int vmax = 16 / dtype_bytes(dt);
-    p.vec = (aligned && len % vmax == 0) ? vmax : 1;
-    const int rows_default = dtype_bytes(dt) == 8 ? kDefaultRows / 2 : kDefaultRows;
+// Shape of a tile: the default (512 threads x 8 rows of 128-bit vectors, 4
+// rows for 8-byte elements), or block_size / items_per_thread from the
+// tuning.  The element-wide fallback (misaligned data or a length that
+// breaks the vector alignment) is built for the default and one-row shapes:
+// a tuned shape snaps to the nearer.
+template <class Find>
+int plan_shape(int esize, bool vec_ok, const scan_tuning_t &tu, TilePlan &p, Find find) {
+    const int vmax = 16 / esize;
+    const int rows_default = esize == 8 ? kDefaultRows / 2 : kDefaultRows;
+    p.vec = vec_ok ? vmax : 1;
     p.block = tu.block_size > 0 ? tu.block_size : kDefaultBlock;
     int ipt = tu.items_per_thread > 0 ? tu.items_per_thread : rows_default * vmax;
-    if (p.vec == 1 && tu.items_per_thread <= 0) ipt = rows_default;  // element-wide fallback
+    if (p.vec == 1 && tu.items_per_thread <= 0) ipt = rows_default;
     if (ipt % p.vec != 0) return SCAN_ERR_UNSUPPORTED;
     p.rows = ipt / p.vec;
-    // The element-wide fallback (misaligned data or a length that breaks the
-    // vector alignment) is built for the default and one-row shapes only:
-    // snap to the nearer.
-    if (p.vec == 1 && !find_lookback(dt, op, p.block, p.rows, 1)) {
+    if (p.vec == 1 && !find(p.block, p.rows, 1)) {
         p.rows = p.rows >= rows_default ? rows_default : 1;
         p.block = p.rows == 1 ? 256 : kDefaultBlock;
     }
-    if (!find_lookback(dt, op, p.block, p.rows, p.vec)) return SCAN_ERR_UNSUPPORTED;
+    if (!find(p.block, p.rows, p.vec)) return SCAN_ERR_UNSUPPORTED;
     p.tile = int64_t(p.block) * p.rows * p.vec;
+    return SCAN_OK;
+}
+
+int plan_scan(scan_dtype_t dt, scan_op_t op, int64_t outer, int64_t len, bool aligned, const scan_tuning_t &tu,
+              TilePlan &p) {
+    const int esize = dtype_bytes(dt);
+    const bool rts = tu.algo == SCAN_ALGO_REDUCE_THEN_SCAN;
+    if (rts && outer != 1) return SCAN_ERR_UNSUPPORTED;  // reduce-then-scan: whole arrays only
+    const bool vec_ok = aligned && len % (16 / esize) == 0;
+    int rc = rts ? plan_shape(esize, vec_ok, tu, p,
+                              [&](int b, int r, int v) { return find_rts(dt, op, b, r, v) != nullptr; })
+                 : plan_shape(esize, vec_ok, tu, p,
+                              [&](int b, int r, int v) { return find_lookback(dt, op, b, r, v) != nullptr; });
+    if (rc != SCAN_OK) return rc;
     p.tiles_per_seg = (len + p.tile - 1) / p.tile;
     p.num_tiles = outer * p.tiles_per_seg;
     if (p.num_tiles > int64_t(INT32_MAX)) return SCAN_ERR_OVERFLOW;  // grid x limit
     p.carry_words = carry_bytes(dt, op) / 4;
-    p.ws_bytes = kHeader + round_up(size_t(p.num_tiles) * p.carry_words * 8, 256);
+    if (rts) {
+        p.kernel = SCAN_KERNEL_RTS;
+        int64_t c = tu.rts_blocks > 0 ? tu.rts_blocks : kDefaultRtsBlocks;
+        if (c > p.num_tiles) c = p.num_tiles;
+        p.rts_chunk = (p.num_tiles + c - 1) / c;
+        p.rts_blocks = (p.num_tiles + p.rts_chunk - 1) / p.rts_chunk;
+        p.ws_bytes = kHeader + round_up(size_t(p.rts_blocks) * carry_bytes(dt, op), 256);
+        p.launches = 3;
+    } else {
+        p.kernel = SCAN_KERNEL_LOOKBACK;
+        p.rts_blocks = p.rts_chunk = 0;
+        p.ws_bytes = kHeader + round_up(size_t(p.num_tiles) * p.carry_words * 8, 256);
+        p.launches = 1;
+    }
+    return SCAN_OK;
+}
+
+int plan_compact(scan_dtype_t dt, int64_t n, bool aligned, const scan_tuning_t &tu, TilePlan &p) {
+    const int rc = plan_shape(4, aligned, tu, p, [&](int b, int r, int v) {
+        return find_compact(dt, SCAN_CMP_GT, b, r, v) != nullptr;
+    });
+    if (rc != SCAN_OK) return rc;
+    p.kernel = SCAN_KERNEL_COMPACT;
+    p.tiles_per_seg = p.num_tiles = (n + p.tile - 1) / p.tile;
+    p.carry_words = 1;
+    p.rts_blocks = p.rts_chunk = 0;
+    p.ws_bytes = kHeader + round_up(size_t(p.num_tiles) * 8, 256);
+    p.launches = 1;
     return SCAN_OK;
 }
 
@@ -101,9 +163,21 @@ int check_ws(const void *ws, size_t ws_bytes, size_t need) {
     return SCAN_OK;
 }
 
-int scan_common(const void *in, void *out, int64_t outer, int64_t len, int64_t inner,
-                scan_dtype_t dt, scan_op_t op, int exclusive, void *total_out, void *ws,
-                size_t ws_bytes, const scan_tuning_t *tuning, hipStream_t stream) {
+PipeArgs pipe_args(const TilePlan &p, void *ws, size_t ws_bytes, const scan_tuning_t &tu) {
+    PipeArgs a;
+    a.ws = ws;
+    a.ws_words = (ws_bytes - kHeader) / 8;
+    a.words_used = p.tiles_per_seg > 1 ? uint64_t(p.num_tiles) * p.carry_words : 0;
+    a.num_tiles = uint32_t(p.num_tiles);
+    a.tiles_per_seg = uint32_t(p.tiles_per_seg);
+    a.spin_limit = tu.spin_limit > 0 ? uint32_t(tu.spin_limit) : kDefaultSpinLimit;
+    a.mode_limit = tu.mode_limit > 0 ? uint32_t(tu.mode_limit) : kDefaultModeLimit;
+    return a;
+}
+
+int scan_common(const void *in, void *out, int64_t outer, int64_t len, int64_t inner, scan_dtype_t dt,
+                scan_op_t op, int exclusive, void *total_out, void *ws, size_t ws_bytes,
+                const scan_tuning_t *tuning, hipStream_t stream) {
     if (!valid_dtype(dt) || !valid_op(op)) return SCAN_ERR_INVALID_ARG;
     if (outer < 0 || len < 0 || inner < 1) return SCAN_ERR_INVALID_ARG;
     if (outer == 0 || len == 0) return SCAN_OK;
@@ -111,28 +185,47 @@ int scan_common(const void *in, void *out, int64_t outer, int64_t len, int64_t i
     const scan_tuning_t tu = tuning_or_default(tuning);
     if (tu.algo < SCAN_ALGO_AUTO || tu.algo > SCAN_ALGO_REDUCE_THEN_SCAN) return SCAN_ERR_INVALID_ARG;
     if (inner != 1) return SCAN_ERR_UNSUPPORTED;
-    if (tu.algo == SCAN_ALGO_REDUCE_THEN_SCAN) return SCAN_ERR_UNSUPPORTED;
 
-    LbPlan p;
-    int rc = plan_lookback(dt, op, outer, len, aligned16(in, out), tu, p);
+    TilePlan p;
+    int rc = plan_scan(dt, op, outer, len, aligned16(in, out), tu, p);
     if (rc != SCAN_OK) return rc;
     rc = check_ws(ws, ws_bytes, p.ws_bytes);
     if (rc != SCAN_OK) return rc;
-    LbArgs a;
+    if (p.kernel == SCAN_KERNEL_RTS) {
+        if (total_out != nullptr) return SCAN_ERR_UNSUPPORTED;
+        RtsArgs r;
+        r.in = in;
+        r.out = out;
+        r.n = len;
+        r.num_tiles = uint32_t(p.num_tiles);
+        r.chunk_tiles = uint32_t(p.rts_chunk);
+        r.blocks = uint32_t(p.rts_blocks);
+        r.exclusive = exclusive ? 1 : 0;
+        r.partials = reinterpret_cast<char *>(ws) + kHeader;
+        return find_rts(dt, op, p.block, p.rows, p.vec)(r, stream);
+    }
+    ScanArgs a;
+    a.pipe = pipe_args(p, ws, ws_bytes, tu);
     a.in = in;
     a.out = out;
     a.seg_len = len;
-    a.tiles_per_seg = uint32_t(p.tiles_per_seg);
-    a.num_tiles = uint32_t(p.num_tiles);
     a.exclusive = exclusive ? 1 : 0;
     a.total_out = total_out;
-    a.ws = ws;
-    a.ws_words = (ws_bytes - kHeader) / 8;
-    a.words_used = p.tiles_per_seg > 1 ? uint64_t(p.num_tiles) * p.carry_words : 0;
-    a.spin_limit = tu.spin_limit > 0 ? uint32_t(tu.spin_limit) : kDefaultSpinLimit;
-    a.grid_blocks = tu.grid_blocks > 0 ? uint32_t(tu.grid_blocks) : 0u;
-    a.mode_limit = tu.mode_limit > 0 ? uint32_t(tu.mode_limit) : kDefaultModeLimit;
-    return find_lookback(dt, op, p.block, p.rows, p.vec)(a, stream);
+    const uint32_t grid_cap = tu.grid_blocks > 0 ? uint32_t(tu.grid_blocks) : 0u;
+    return find_lookback(dt, op, p.block, p.rows, p.vec)(a, grid_cap, stream);
+}
+
+void fill_plan(const TilePlan &p, scan_dtype_t dt, scan_op_t op, scan_plan_t *plan) {
+    plan->kernel = p.kernel;
+    plan->block_size = p.block;
+    plan->items_per_thread = p.rows * p.vec;
+    plan->vec = p.vec;
+    plan->tile_elems = p.tile;
+    plan->num_tiles = p.kernel == SCAN_KERNEL_RTS ? p.rts_blocks : p.num_tiles;
+    plan->lds_bytes = int64_t(p.rows) * (p.block / 64) * dtype_bytes(dt) + carry_bytes(dt, op) + 32;
+    plan->workspace_bytes = int64_t(p.ws_bytes);
+    plan->launches = p.launches;
+    plan->carry_words = p.carry_words;
 }
 
 }  // namespace
@@ -142,32 +235,42 @@ using namespace sw64;
 
 extern "C" {
 
-int scan_plan(scan_call_t call, scan_dtype_t dtype, scan_op_t op, int64_t outer, int64_t len,
-              int64_t inner, const scan_tuning_t *tuning, scan_plan_t *plan) {
+int scan_plan(scan_call_t call, scan_dtype_t dtype, scan_op_t op, int64_t outer, int64_t len, int64_t inner,
+              const scan_tuning_t *tuning, scan_plan_t *plan) {
     if (plan == nullptr) return SCAN_ERR_INVALID_ARG;
     memset(plan, 0, sizeof(*plan));
     if (!valid_dtype(dtype) || !valid_op(op)) return SCAN_ERR_INVALID_ARG;
     if (outer < 0 || len < 0 || inner < 1) return SCAN_ERR_INVALID_ARG;
     const scan_tuning_t tu = tuning_or_default(tuning);
-    if (call != SCAN_CALL_SCAN) return SCAN_ERR_UNSUPPORTED;
-    if (inner != 1 || tu.algo == SCAN_ALGO_REDUCE_THEN_SCAN) return SCAN_ERR_UNSUPPORTED;
-    if (outer == 0 || len == 0) {
-        plan->kernel = SCAN_KERNEL_NONE;
-        return SCAN_OK;
+    TilePlan p;
+    int rc;
+    switch (call) {
+    case SCAN_CALL_SCAN:
+        if (inner != 1) return SCAN_ERR_UNSUPPORTED;
+        if (outer == 0 || len == 0) return SCAN_OK;
+        rc = plan_scan(dtype, op, outer, len, true, tu, p);
+        break;
+    case SCAN_CALL_COMPACT:
+        if (dtype != SCAN_F32 && dtype != SCAN_I32) return SCAN_ERR_UNSUPPORTED;
+        if (outer * len * inner > int64_t(INT32_MAX)) return SCAN_ERR_OVERFLOW;
+        if (outer * len * inner == 0) return SCAN_OK;
+        rc = plan_compact(dtype, outer * len * inner, true, tu, p);
+        break;
+    case SCAN_CALL_PACK: {
+        if (dtype != SCAN_I32 || outer != 1 || inner != 1) return SCAN_ERR_INVALID_ARG;
+        if (len > int64_t(INT32_MAX)) return SCAN_ERR_OVERFLOW;
+        if (len == 0) return SCAN_OK;
+        scan_tuning_t lb = tu;
+        lb.algo = SCAN_ALGO_LOOKBACK;
+        rc = plan_scan(SCAN_I32, SCAN_OP_SUM, 1, len, true, lb, p);
+        if (rc == SCAN_OK) p.kernel = SCAN_KERNEL_PACK;
+        break;
     }
-    LbPlan p;
-    int rc = plan_lookback(dtype, op, outer, len, true, tu, p);
+    default:
+        return SCAN_ERR_INVALID_ARG;
+    }
     if (rc != SCAN_OK) return rc;
-    plan->kernel = SCAN_KERNEL_LOOKBACK;
-    plan->block_size = p.block;
-    plan->items_per_thread = p.rows * p.vec;
-    plan->vec = p.vec;
-    plan->tile_elems = p.tile;
-    plan->num_tiles = p.num_tiles;
-    plan->lds_bytes = int64_t(p.rows) * (p.block / 64) * dtype_bytes(dtype) + carry_bytes(dtype, op) + 16;
-    plan->workspace_bytes = int64_t(p.ws_bytes);
-    plan->launches = 1;
-    plan->carry_words = p.carry_words;
+    fill_plan(p, dtype, op, plan);
     return SCAN_OK;
 }
 
@@ -210,18 +313,44 @@ int scan_exclusive(const void *in, void *out, int64_t n, scan_dtype_t dtype, sca
 }
 
 int scan_dim(const void *in, void *out, int64_t outer, int64_t len, int64_t inner, scan_dtype_t dtype,
-             scan_op_t op, int exclusive, void *ws, size_t ws_bytes, const scan_tuning_t *tuning,
-             void *stream) {
+             scan_op_t op, int exclusive, void *ws, size_t ws_bytes, const scan_tuning_t *tuning, void *stream) {
     return scan_common(in, out, outer, len, inner, dtype, op, exclusive, nullptr, ws, ws_bytes, tuning,
                        reinterpret_cast<hipStream_t>(stream));
 }
 
-int compact_if(const void *x, int64_t n, scan_dtype_t x_dtype, scan_cmp_t cmp, double threshold,
-               int32_t *out_idx, int32_t *d_count, void *ws, size_t ws_bytes, const scan_tuning_t *tuning,
-               void *stream) {
-    (void)x; (void)n; (void)x_dtype; (void)cmp; (void)threshold; (void)out_idx; (void)d_count;
-    (void)ws; (void)ws_bytes; (void)tuning; (void)stream;
-    return SCAN_ERR_UNSUPPORTED;
+int compact_if(const void *x, int64_t n, scan_dtype_t x_dtype, scan_cmp_t cmp, double threshold, int32_t *out_idx,
+               int32_t *d_count, void *ws, size_t ws_bytes, const scan_tuning_t *tuning, void *stream) {
+    if (n < 0 || !valid_cmp(cmp) || d_count == nullptr) return SCAN_ERR_INVALID_ARG;
+    if (!valid_dtype(x_dtype)) return SCAN_ERR_INVALID_ARG;
+    if (x_dtype != SCAN_F32 && x_dtype != SCAN_I32) return SCAN_ERR_UNSUPPORTED;
+    if (n > int64_t(INT32_MAX)) return SCAN_ERR_OVERFLOW;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (n == 0) return launch_fill_i32(d_count, 1, 0, s);
+    if (x == nullptr || out_idx == nullptr) return SCAN_ERR_INVALID_ARG;
+    const scan_tuning_t tu = tuning_or_default(tuning);
+    TilePlan p;
+    int rc = plan_compact(x_dtype, n, aligned16(x, x), tu, p);
+    if (rc != SCAN_OK) return rc;
+    rc = check_ws(ws, ws_bytes, p.ws_bytes);
+    if (rc != SCAN_OK) return rc;
+    CompactArgs a;
+    a.pipe = pipe_args(p, ws, ws_bytes, tu);
+    a.x = x;
+    a.n = n;
+    if (x_dtype == SCAN_F32) {
+        const float t = float(threshold);
+        memcpy(&a.threshold, &t, 4);
+    } else {
+        // clamp to the int32 range, then compare in int32
+        const double c = threshold < double(INT32_MIN) ? double(INT32_MIN)
+                         : threshold > double(INT32_MAX) ? double(INT32_MAX) : threshold;
+        const int32_t t = int32_t(c);
+        memcpy(&a.threshold, &t, 4);
+    }
+    a.out_idx = out_idx;
+    a.count = d_count;
+    const uint32_t grid_cap = tu.grid_blocks > 0 ? uint32_t(tu.grid_blocks) : 0u;
+    return find_compact(x_dtype, cmp, p.block, p.rows, p.vec)(a, grid_cap, s);
 }
 
 int pack_offsets(const int32_t *counts, int64_t n, int32_t *offsets, void *ws, size_t ws_bytes,
@@ -231,12 +360,17 @@ int pack_offsets(const int32_t *counts, int64_t n, int32_t *offsets, void *ws, s
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if (n == 0) return launch_fill_i32(offsets, 1, 0, s);
     if (counts == nullptr) return SCAN_ERR_INVALID_ARG;
-    return scan_common(counts, offsets, 1, n, 1, SCAN_I32, SCAN_OP_SUM, 1, offsets + n, ws, ws_bytes, tuning, s);
+    scan_tuning_t tu = tuning_or_default(tuning);
+    tu.algo = SCAN_ALGO_LOOKBACK;  // the total comes from the look-back's last tile
+    return scan_common(counts, offsets, 1, n, 1, SCAN_I32, SCAN_OP_SUM, 1, offsets + n, ws, ws_bytes, &tu, s);
 }
 
 int pack_emit_neighbors(const int32_t *offsets, int64_t n, int32_t *out, void *stream) {
-    (void)offsets; (void)n; (void)out; (void)stream;
-    return SCAN_ERR_UNSUPPORTED;
+    if (n < 0) return SCAN_ERR_INVALID_ARG;
+    if (n == 0) return SCAN_OK;
+    if (offsets == nullptr || out == nullptr) return SCAN_ERR_INVALID_ARG;
+    if (n > INT32_MAX) return SCAN_ERR_OVERFLOW;
+    return launch_emit_neighbors(offsets, n, out, reinterpret_cast<hipStream_t>(stream));
 }
 
 int scan_copy(const void *in, void *out, size_t bytes, void *stream) {
@@ -257,6 +391,6 @@ const char *scan_status_string(int status) {
     return "unknown status";
 }
 
-const char *scan_version(void) { return "scan_wave64 0.1 (gfx950)"; }
+const char *scan_version(void) { return "scan_wave64 0.2 (gfx950)"; }
 
 }  // extern "C"

@@ -8,52 +8,60 @@
 
 #include <stdint.h>
 
+#include "pipeline.hpp"
 #include "scan_wave64.h"
 
 namespace sw64 {
 
 // ---------------------------------------------------------------- look-back
-// One launch of a persistent grid of at most resident-capacity workgroups of
-// `block` threads; workgroup w scans tiles w, w+G, ... of block*rows*vec
-// elements.  Segments (rows of a (outer, len, 1)
-// array) are seg_len elements long and split into tiles_per_seg tiles; the
-// look-back never crosses a segment start.
-struct LbArgs {
+// One launch of the persistent pipeline (pipeline.hpp): at most the resident
+// capacity of workgroups of `block` threads; workgroup w scans tiles w, w+G,
+// ... of block*rows*vec elements.  Segments (rows of an (outer, len, 1)
+// array) are seg_len elements long; the look-back never crosses a segment
+// start.
+struct ScanArgs {
+    PipeArgs pipe;
     const void *in;
     void *out;
     int64_t seg_len;          // elements per segment
-    uint32_t tiles_per_seg;   // tiles per segment (>= 1)
-    uint32_t num_tiles;       // segments * tiles_per_seg (grid size)
     int32_t exclusive;        // 0 inclusive, 1 exclusive
     void *total_out;          // optional: per-segment total, written by its last tile
-    void *ws;                 // workspace (header + descriptors)
-    uint64_t ws_words;        // descriptor words the workspace holds
-    uint64_t words_used;      // descriptor words this launch writes
-    uint32_t spin_limit;      // polls of one look-back window before giving up
-    uint32_t grid_blocks;     // cap on the persistent grid (0 = resident capacity)
-    uint32_t mode_limit;      // polls before a call falls back to dynamic claiming
 };
-using LbLaunch = int (*)(const LbArgs &, hipStream_t);
+using LbLaunch = int (*)(const ScanArgs &, uint32_t grid_cap, hipStream_t);
 LbLaunch find_lookback(scan_dtype_t dt, scan_op_t op, int block, int rows, int vec);
 
 // ---------------------------------------------------------- reduce-then-scan
 // Three launches over `blocks` workgroups, each owning `chunk_tiles`
 // consecutive tiles of block*rows*vec elements: reduce each chunk into a
 // partial, scan the partials in one workgroup, rescan each chunk from its
-// base.  `partials` points at blocks carry values inside the workspace; the
-// last launch zeroes them again so the workspace stays clean for the
-// look-back descriptors.
+// base.  `partials` (blocks carry values) lives in the workspace's
+// descriptor area; the last launch zeroes it again, which leaves valid
+// (untagged) descriptor words behind.
 struct RtsArgs {
     const void *in;
     void *out;
     int64_t n;
-    uint32_t blocks;
+    uint32_t num_tiles;
     uint32_t chunk_tiles;
+    uint32_t blocks;
     int32_t exclusive;
     void *partials;
 };
 using RtsLaunch = int (*)(const RtsArgs &, hipStream_t);
 RtsLaunch find_rts(scan_dtype_t dt, scan_op_t op, int block, int rows, int vec);
+
+// ---------------------------------------------------------------- compaction
+struct CompactArgs {
+    PipeArgs pipe;
+    const void *x;
+    int64_t n;
+    uint32_t threshold;       // bit pattern of the threshold in x's type
+    int32_t *out_idx;
+    int32_t *count;
+};
+using CompactLaunch = int (*)(const CompactArgs &, uint32_t grid_cap, hipStream_t);
+CompactLaunch find_compact(scan_dtype_t x_dt, scan_cmp_t cmp, int block, int rows, int vec);
+int launch_emit_neighbors(const int32_t *offsets, int64_t n, int32_t *out, hipStream_t s);
 
 // -------------------------------------------------------------- utilities
 int launch_fill_u64(void *p, uint64_t words, uint64_t value, hipStream_t s);

@@ -98,6 +98,26 @@ struct TileScan {
         agg = run;
     }
 
+    // Tile aggregate only (the reduce pass of reduce-then-scan): per-thread
+    // reduction of all its elements, wave reduction, one LDS slot per wave.
+    // Contains one __syncthreads(); the caller separates reuses of `sh`.
+    __device__ __forceinline__ void reduce(Shared &sh) {
+        const T id = Op::template identity<T>();
+        T acc = id;
+#pragma unroll
+        for (int r = 0; r < ROWS; r++) {
+#pragma unroll
+            for (int c = 0; c < VEC; c++) acc = Op::apply(acc, v[r].v[c]);
+        }
+        const T w = wave_reduce<Op>(acc);
+        if (lane_id() == 0) sh.tot[0][threadIdx.x / kWave] = w;
+        __syncthreads();
+        T run = id;
+#pragma unroll
+        for (int k = 0; k < W; k++) run = Op::apply(run, sh.tot[0][k]);
+        agg = run;
+    }
+
     // Add the tile's exclusive prefix `pre` and store; inclusive or exclusive.
     __device__ __forceinline__ void store(T *dst, int64_t remaining, C pre, bool exclusive) const {
 #pragma unroll

@@ -1,10 +1,36 @@
 // util.hip -- fill kernels (workspace initialisation, empty outputs) and the
 // copy kernel that measures the attainable read+write bandwidth with the same
 // 128-bit access pattern and tile shape as the fp32 scan.
+#include <mutex>
+
 #include "device.hpp"
 #include "launch.hpp"
 
 namespace sw64 {
+
+int resident_blocks(const void *kernel, int waves_per_block) {
+    static std::mutex mu;
+    static const void *keys[512];
+    static int devs[512], vals[512], count = 0;
+    const int block = waves_per_block * kWave;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    std::lock_guard<std::mutex> lock(mu);
+    for (int i = 0; i < count; i++)
+        if (keys[i] == kernel && devs[i] == dev) return vals[i];
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, 0) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    if (per_cu * waves_per_block > 28) per_cu = 28 / waves_per_block > 0 ? 28 / waves_per_block : 1;
+    const int v = per_cu * cus;
+    if (count < 512) {
+        keys[count] = kernel;
+        devs[count] = dev;
+        vals[count] = v;
+        count++;
+    }
+    return v;
+}
 
 __global__ __launch_bounds__(256) void k_fill_u64(uint64_t *p, uint64_t words, uint64_t value) {
     for (uint64_t i = uint64_t(blockIdx.x) * 256 + threadIdx.x; i < words; i += uint64_t(gridDim.x) * 256)

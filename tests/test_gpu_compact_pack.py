@@ -1,0 +1,107 @@
+"""GPU parity of stream compaction and count-scan-emit packing against the
+oracle: bit-exact indices, counts, offsets, totals and emitted records, at the
+configuration sizes (n = 1e7) and on edge cases (empty, all/none selected,
+alternating, ties at the threshold, ragged and misaligned inputs, many tiles,
+zero and huge counts)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import stream_compaction_wave64_amd as sw
+from stream_compaction_wave64_amd import inputs
+from gpu_util import DEV, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+CMPS = ["gt", "ge", "lt", "le", "eq", "ne"]
+
+
+def _compact(x, cmp="gt", t=0.5, tuning=None, offset=0):
+    if offset:
+        buf = to_dev(np.concatenate([np.zeros(offset, x.dtype), x]))
+        xd = buf[offset:]
+    else:
+        xd = to_dev(x)
+    out, count = sw.compact_if(xd, cmp, t, tuning=tuning)
+    torch.cuda.synchronize()
+    c = int(count.item())
+    return to_host(out[:c]) if c else np.zeros(0, np.int32), c
+
+
+def _check_compact(x, cmp="gt", t=0.5, **kw):
+    ref = oracle.compact(x, cmp, t)
+    got, c = _compact(x, cmp, t, **kw)
+    assert c == ref.size, (c, ref.size)
+    assert np.array_equal(got, ref)
+
+
+def test_compaction_config_1e7():
+    x, _ = inputs.compaction_inputs(10 ** 7, seed=4)
+    _check_compact(x, "gt", 0.5)
+
+
+@pytest.mark.parametrize("cmp", CMPS)
+@pytest.mark.parametrize("dt", [np.float32, np.int32])
+def test_compaction_all_comparisons(cmp, dt):
+    rng = np.random.default_rng(40)
+    if dt == np.float32:
+        x = rng.random(300_001, dtype=np.float32)
+        x[::97] = np.float32(0.5)  # exact ties
+        t = 0.5
+    else:
+        x = rng.integers(-50, 51, 300_001, dtype=np.int32)
+        t = 3
+    _check_compact(x, cmp, t)
+    _check_compact(x, cmp, t, tuning={"block_size": 256, "items_per_thread": 4})
+
+
+def test_compaction_closed_forms_and_edges():
+    for n in (1, 3, 4, 5, 1000, 16384, 16385, 100_003):
+        _check_compact(np.ones(n, np.float32))                      # all selected -> iota
+        _check_compact(np.zeros(n, np.float32))                     # none selected
+        _check_compact(np.tile(np.array([0, 1], np.float32), n)[:n])  # alternating -> 2k+1
+    out, count = sw.compact_if(torch.empty(0, dtype=torch.float32, device=DEV))
+    torch.cuda.synchronize()
+    assert int(count.item()) == 0
+
+
+def test_compaction_ragged_misaligned_many_tiles():
+    x, _ = inputs.compaction_inputs(500_003, seed=41)
+    for tuning in (None, {"block_size": 256, "items_per_thread": 4},
+                   {"block_size": 256, "items_per_thread": 4, "grid_blocks": 3}):
+        _check_compact(x, tuning=tuning)
+        _check_compact(x, tuning=tuning, offset=1)  # element-wide loads
+
+
+def test_pack_config_1e7_offsets_and_emit():
+    _, counts = inputs.compaction_inputs(10 ** 7, seed=4)
+    ref_off, ref_total = oracle.pack_offsets(counts)
+    off = sw.pack_offsets(to_dev(counts))
+    torch.cuda.synchronize()
+    got_off = to_host(off)
+    assert np.array_equal(got_off, ref_off)
+    total = int(got_off[-1])
+    assert total == ref_total
+    rec = sw.pack_emit_neighbors(off, total)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(rec)[:total], oracle.pack_emit(ref_off))
+
+
+def test_pack_edges():
+    cases = [np.zeros(1000, np.int32), np.ones(4097, np.int32), np.array([0, 0, 1000, 0], np.int32),
+             np.array([5], np.int32), np.array([3, 2, 0, 1, 2], np.int32),
+             inputs.compaction_inputs(300_001, seed=42)[1]]
+    for counts in cases:
+        ref_off, ref_total = oracle.pack_offsets(counts)
+        for tuning in (None, {"block_size": 256, "items_per_thread": 4}):
+            off = sw.pack_offsets(to_dev(counts), tuning=tuning)
+            torch.cuda.synchronize()
+            assert np.array_equal(to_host(off), ref_off)
+        if ref_total:
+            rec = sw.pack_emit_neighbors(off, ref_total)
+            torch.cuda.synchronize()
+            assert np.array_equal(to_host(rec)[:ref_total], oracle.pack_emit(ref_off))
+    off = sw.pack_offsets(torch.empty(0, dtype=torch.int32, device=DEV))
+    torch.cuda.synchronize()
+    assert to_host(off).tolist() == [0]

@@ -109,6 +109,37 @@ def test_prod_of_powers_of_two_bit_exact(dt):
             assert np.array_equal(got, ref), f"excl={excl} tuning={tuning}"
 
 
+@pytest.mark.parametrize("dt", DTYPES, ids=lambda d: np.dtype(d).name)
+@pytest.mark.parametrize("op", OPS)
+def test_parity_reduce_then_scan(dt, op):
+    vec = 16 // np.dtype(dt).itemsize
+    for n, tuning in ((1, {}), (1000, {}), (3_000_001, {}), (1_000_003, {"rts_blocks": 7}),
+                      (256 * vec * 50 + 4, {"block_size": 256, "items_per_thread": vec, "rts_blocks": 3}),
+                      (123_457, {"block_size": 256, "items_per_thread": vec, "rts_blocks": 1000})):
+        x = _input(dt, n, 60, op)
+        tu = dict(tuning, algo="reduce_then_scan")
+        for excl in (False, True):
+            assert_scan_matches(x, _run(x, op, excl, tu), op, excl, what=f"n={n} {tuning} excl={excl}")
+
+
+def test_reduce_then_scan_leaves_workspace_clean():
+    # its partials share the descriptor area: a look-back call right after must
+    # see only untagged words
+    x = inputs.generic(np.float32, 2_000_000, 61)
+    for _ in range(3):
+        a = _run(x, "sum", False, {"algo": "reduce_then_scan"})
+        b = _run(x, "sum", False)
+        assert_scan_matches(x, a, "sum", False)
+        assert_scan_matches(x, b, "sum", False)
+
+
+def test_config_fp32_1e8_reduce_then_scan():
+    x = inputs.f32_uniform_01(10 ** 8, seed=1)
+    r = sw.scan_inclusive(to_dev(x), tuning={"algo": "reduce_then_scan"})
+    torch.cuda.synchronize()
+    assert_scan_matches(x, to_host(r), "sum", False, what="fp32 1e8 rts")
+
+
 def test_in_place():
     x = inputs.generic(np.int32, 300_001, 9, "wide")
     xd = to_dev(x)
