@@ -18,6 +18,22 @@ namespace sw64 {
 SW64_DECLARE_PER_TYPE(find_lookback, LbLaunch)
 SW64_DECLARE_PER_TYPE(find_rts, RtsLaunch)
 #undef SW64_DECLARE_PER_TYPE
+ElemLaunch find_element_i32(scan_op_t, int);
+ElemLaunch find_element_u32(scan_op_t, int);
+ElemLaunch find_element_i64(scan_op_t, int);
+ElemLaunch find_element_f32(scan_op_t, int);
+ElemLaunch find_element_f64(scan_op_t, int);
+
+ElemLaunch find_element(scan_dtype_t dt, scan_op_t op, int width) {
+    switch (dt) {
+    case SCAN_I32: return find_element_i32(op, width);
+    case SCAN_U32: return find_element_u32(op, width);
+    case SCAN_I64: return find_element_i64(op, width);
+    case SCAN_F32: return find_element_f32(op, width);
+    case SCAN_F64: return find_element_f64(op, width);
+    }
+    return nullptr;
+}
 
 LbLaunch find_lookback(scan_dtype_t dt, scan_op_t op, int block, int rows, int vec) {
     switch (dt) {
@@ -48,6 +64,19 @@ constexpr uint32_t kDefaultSpinLimit = 1u << 22;
 constexpr uint32_t kDefaultModeLimit = 512;
 constexpr int kDefaultBlock = 512, kDefaultRows = 8;  // look-back tile shape
 constexpr int kDefaultRtsBlocks = 1024;               // C of reduce-then-scan
+constexpr int64_t kDefaultLocalMem = 64 * 1024;       // LDS budget of the large-element rule
+constexpr int kElemDefaultBlock = 256;                // large elements: start of the rule
+
+// AcceleratedKernels.jl PR #208, first bullet: an explicit block size is kept
+// as given; an unset one starts at the default and is lowered to the largest
+// power of two B whose one-item-per-thread tile plus one per-thread total
+// (2 * B * esize bytes) fits the local-memory budget, never below 2.
+int64_t element_block(int64_t esize, int64_t budget, int64_t explicit_b, int64_t default_b) {
+    if (explicit_b > 0) return explicit_b;
+    int64_t b = default_b;
+    while (b > 2 && 2 * b * esize > budget) b /= 2;
+    return b < 2 ? 2 : b;
+}
 
 bool valid_dtype(int dt) { return dt >= SCAN_I32 && dt <= SCAN_F64; }
 bool valid_op(int op) { return op >= SCAN_OP_SUM && op <= SCAN_OP_MIN; }
@@ -81,6 +110,7 @@ struct TilePlan {
     int64_t rts_blocks, rts_chunk;
     size_t ws_bytes;
     int launches;
+    int width;                // components per element (element kernel)
 };
 
 // Shape of a tile: the default (512 threads x 8 rows of 128-bit vectors, 4
@@ -139,6 +169,33 @@ int plan_scan(scan_dtype_t dt, scan_op_t op, int64_t outer, int64_t len, bool al
     return SCAN_OK;
 }
 
+// Large elements (inner > 1): one element per thread, `block` elements per
+// tile from the PR's rule; the kernel's waves need block >= 64 (and the
+// launch bound allows 256).
+int plan_element(scan_dtype_t dt, scan_op_t op, int64_t outer, int64_t len, int64_t inner, bool aligned,
+                 const scan_tuning_t &tu, TilePlan &p) {
+    if (tu.algo == SCAN_ALGO_REDUCE_THEN_SCAN) return SCAN_ERR_UNSUPPORTED;
+    if (inner > 64 || !find_element(dt, op, int(inner))) return SCAN_ERR_UNSUPPORTED;
+    const int esize = dtype_bytes(dt);
+    const int64_t budget = tu.local_mem_bytes > 0 ? tu.local_mem_bytes : kDefaultLocalMem;
+    const int64_t b = element_block(inner * esize, budget, tu.block_size, kElemDefaultBlock);
+    if (b != 64 && b != 128 && b != 256) return SCAN_ERR_UNSUPPORTED;
+    p.kernel = SCAN_KERNEL_ELEMENT;
+    p.block = int(b);
+    p.rows = 1;
+    p.vec = (aligned && (inner * esize) % 16 == 0) ? 16 / esize : 1;
+    p.width = int(inner);
+    p.tile = b;
+    p.tiles_per_seg = (len + b - 1) / b;
+    p.num_tiles = outer * p.tiles_per_seg;
+    if (p.num_tiles > int64_t(INT32_MAX)) return SCAN_ERR_OVERFLOW;
+    p.carry_words = int(inner) * carry_bytes(dt, op) / 4;
+    p.rts_blocks = p.rts_chunk = 0;
+    p.ws_bytes = kHeader + round_up(size_t(p.num_tiles) * p.carry_words * 8, 256);
+    p.launches = 1;
+    return SCAN_OK;
+}
+
 int plan_compact(scan_dtype_t dt, int64_t n, bool aligned, const scan_tuning_t &tu, TilePlan &p) {
     const int rc = plan_shape(4, aligned, tu, p, [&](int b, int r, int v) {
         return find_compact(dt, SCAN_CMP_GT, b, r, v) != nullptr;
@@ -184,7 +241,23 @@ int scan_common(const void *in, void *out, int64_t outer, int64_t len, int64_t i
     if (in == nullptr || out == nullptr) return SCAN_ERR_INVALID_ARG;
     const scan_tuning_t tu = tuning_or_default(tuning);
     if (tu.algo < SCAN_ALGO_AUTO || tu.algo > SCAN_ALGO_REDUCE_THEN_SCAN) return SCAN_ERR_INVALID_ARG;
-    if (inner != 1) return SCAN_ERR_UNSUPPORTED;
+    if (inner != 1) {
+        if (total_out != nullptr) return SCAN_ERR_UNSUPPORTED;
+        TilePlan p;
+        int rc = plan_element(dt, op, outer, len, inner, aligned16(in, out), tu, p);
+        if (rc != SCAN_OK) return rc;
+        rc = check_ws(ws, ws_bytes, p.ws_bytes);
+        if (rc != SCAN_OK) return rc;
+        ElemArgs a;
+        a.pipe = pipe_args(p, ws, ws_bytes, tu);
+        a.in = in;
+        a.out = out;
+        a.seg_len = len;
+        a.exclusive = exclusive ? 1 : 0;
+        a.vec16 = p.vec > 1 ? 1 : 0;
+        const uint32_t grid_cap = tu.grid_blocks > 0 ? uint32_t(tu.grid_blocks) : 0u;
+        return find_element(dt, op, p.width)(a, p.block, grid_cap, stream);
+    }
 
     TilePlan p;
     int rc = plan_scan(dt, op, outer, len, aligned16(in, out), tu, p);
@@ -220,9 +293,12 @@ void fill_plan(const TilePlan &p, scan_dtype_t dt, scan_op_t op, scan_plan_t *pl
     plan->block_size = p.block;
     plan->items_per_thread = p.rows * p.vec;
     plan->vec = p.vec;
-    plan->tile_elems = p.tile;
+    plan->tile_elems = p.tile;  // elements (of `width` components for the element kernel)
     plan->num_tiles = p.kernel == SCAN_KERNEL_RTS ? p.rts_blocks : p.num_tiles;
-    plan->lds_bytes = int64_t(p.rows) * (p.block / 64) * dtype_bytes(dt) + carry_bytes(dt, op) + 32;
+    if (p.kernel == SCAN_KERNEL_ELEMENT)
+        plan->lds_bytes = int64_t(p.width) * (4 * dtype_bytes(dt) + 4 * carry_bytes(dt, op)) + 32;
+    else
+        plan->lds_bytes = int64_t(p.rows) * (p.block / 64) * dtype_bytes(dt) + carry_bytes(dt, op) + 32;
     plan->workspace_bytes = int64_t(p.ws_bytes);
     plan->launches = p.launches;
     plan->carry_words = p.carry_words;
@@ -246,9 +322,9 @@ int scan_plan(scan_call_t call, scan_dtype_t dtype, scan_op_t op, int64_t outer,
     int rc;
     switch (call) {
     case SCAN_CALL_SCAN:
-        if (inner != 1) return SCAN_ERR_UNSUPPORTED;
         if (outer == 0 || len == 0) return SCAN_OK;
-        rc = plan_scan(dtype, op, outer, len, true, tu, p);
+        rc = inner == 1 ? plan_scan(dtype, op, outer, len, true, tu, p)
+                        : plan_element(dtype, op, outer, len, inner, true, tu, p);
         break;
     case SCAN_CALL_COMPACT:
         if (dtype != SCAN_F32 && dtype != SCAN_I32) return SCAN_ERR_UNSUPPORTED;

@@ -43,6 +43,8 @@ struct CompactPolicy : ScalarCarry<OpSum, int32_t> {
         TS ts;
         uint32_t bits;  // bit r*VEC + c: element c of this thread's vector in row r is selected
 
+        __device__ __forceinline__ void set_slot(int) {}
+
         __device__ __forceinline__ void load(const Args &a, uint32_t tile) {
             const int64_t start = int64_t(tile) * TS::TILE;
             const int64_t remaining = a.n - start;

@@ -63,6 +63,20 @@ using CompactLaunch = int (*)(const CompactArgs &, uint32_t grid_cap, hipStream_
 CompactLaunch find_compact(scan_dtype_t x_dt, scan_cmp_t cmp, int block, int rows, int vec);
 int launch_emit_neighbors(const int32_t *offsets, int64_t n, int32_t *out, hipStream_t s);
 
+// ---------------------------------------------------------- large elements
+// Elements of W components scanned component-wise along the middle axis of
+// an (outer, len, W) array; `block` elements per tile (64, 128 or 256).
+struct ElemArgs {
+    PipeArgs pipe;
+    const void *in;
+    void *out;
+    int64_t seg_len;          // elements per segment (len)
+    int32_t exclusive;
+    int32_t vec16;            // 1: element rows are 16-byte aligned, use 128-bit accesses
+};
+using ElemLaunch = int (*)(const ElemArgs &, int block, uint32_t grid_cap, hipStream_t);
+ElemLaunch find_element(scan_dtype_t dt, scan_op_t op, int width);
+
 // -------------------------------------------------------------- utilities
 int launch_fill_u64(void *p, uint64_t words, uint64_t value, hipStream_t s);
 int launch_fill_i32(int32_t *p, int64_t count, int32_t value, hipStream_t s);

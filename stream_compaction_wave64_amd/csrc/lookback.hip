@@ -29,6 +29,8 @@ struct ScanPolicy : ScalarCarry<Op_, typename Carry<T_, Op_>::type> {
     struct Tile {
         TS ts;
 
+        __device__ __forceinline__ void set_slot(int) {}
+
         __device__ __forceinline__ static void geom(const Args &a, uint32_t tile, int64_t &start, int64_t &remaining,
                                                     uint32_t &seg, uint32_t &j) {
             seg = tile / a.pipe.tiles_per_seg;

@@ -26,13 +26,16 @@
 //   struct Args { PipeArgs pipe; ... }
 //   struct Shared;                 LDS the tile scan needs
 //   struct Tile {
+//     void set_slot(int);          which of the three pipeline buffers it is
 //     void load(const Args&, uint32_t tile);
 //     void scan(Shared&);          one barrier; afterwards aggregate() valid
 //     C aggregate() const;
 //     void emit(const Args&, uint32_t tile, const C* prefix);  prefix in LDS
 //   };
-//   static void publish(uint64_t*, uint32_t tag, const C&);   descriptor I/O
-//   static C lookback(...);
+//   static void publish_aggregate(Tile&, uint64_t* desc, uint32_t tag);  thread 0
+//   static void resolve(Tile&, ...);   wave 0: look back, publish P, write the
+//                                      exclusive prefix to LDS
+//   static void set_identity(C* prefix);   lane 0
 #pragma once
 
 #include "device.hpp"
@@ -73,7 +76,7 @@ struct Pipeline {
         ts.scan(sm.ps);
         if (a.pipe.tiles_per_seg > 1 && threadIdx.x == 0) {
             const uint32_t state = (tile % a.pipe.tiles_per_seg == 0) ? kStateP : kStateA;
-            P::publish(desc_of(desc, tile), (epoch << 2) | state, ts.aggregate());
+            P::publish_aggregate(ts, desc_of(desc, tile), (epoch << 2) | state);
         }
     }
 
@@ -83,13 +86,10 @@ struct Pipeline {
                                                   uint64_t *desc, uint32_t epoch) {
         const uint32_t j = tile % a.pipe.tiles_per_seg;
         if (threadIdx.x < kWave) {
-            C pre = P::identity();
-            if (a.pipe.tiles_per_seg > 1 && j != 0) {
-                const C agg = ts.aggregate();
-                pre = P::lookback(desc, epoch, tile, int64_t(tile - j), hdr, a.pipe.spin_limit);
-                if (lane_id() == 0) P::publish(desc_of(desc, tile), (epoch << 2) | kStateP, P::combine(pre, agg));
-            }
-            if (lane_id() == 0) sm.prefix = pre;
+            if (a.pipe.tiles_per_seg > 1 && j != 0)
+                P::resolve(ts, desc, epoch, tile, int64_t(tile - j), hdr, a.pipe.spin_limit, &sm.prefix);
+            else
+                P::set_identity(&sm.prefix);
         }
         __syncthreads();
         ts.emit(a, tile, &sm.prefix);
@@ -123,6 +123,9 @@ struct Pipeline {
         // in flight).  The first two loads are issued before the mode is
         // known; dynamic mode drops them.
         Tile b0, b1, b2;
+        b0.set_slot(0);
+        b1.set_slot(1);
+        b2.set_slot(2);
         uint32_t t = blockIdx.x;
         b0.load(a, t);
         if (t + G < n) b1.load(a, t + G);
@@ -170,18 +173,31 @@ struct Pipeline {
 };
 
 // Descriptor I/O and look-back for a policy whose carry is one value of type
-// C (scalar scans and compaction).
+// C (scalar scans and compaction); its Tile provides aggregate().
 template <class Op, class C>
 struct ScalarCarry {
     static constexpr int kDescWords = Desc<C>::kWords;
-    __device__ __forceinline__ static C identity() { return Op::template identity<C>(); }
-    __device__ __forceinline__ static C combine(const C &a, const C &b) { return Op::apply(a, b); }
-    __device__ __forceinline__ static void publish(uint64_t *d, uint32_t tag, const C &v) {
-        Desc<C>::publish(d, tag, v);
+
+    template <class Tile>
+    __device__ __forceinline__ static void publish_aggregate(const Tile &ts, uint64_t *d, uint32_t tag) {
+        Desc<C>::publish(d, tag, ts.aggregate());
     }
-    __device__ __forceinline__ static C lookback(const uint64_t *desc, uint32_t epoch, int64_t tile, int64_t first,
-                                                 WsHeader *hdr, uint32_t spin_limit) {
-        return sw64::lookback<Op, C, 1>(desc, epoch, tile, first, hdr, spin_limit);
+
+    template <class Tile>
+    __device__ __forceinline__ static void resolve(const Tile &ts, const uint64_t *desc, uint32_t epoch,
+                                                   uint32_t tile, int64_t first, WsHeader *hdr, uint32_t spin_limit,
+                                                   C *prefix) {
+        const C agg = ts.aggregate();
+        const C pre = sw64::lookback<Op, C, 1>(desc, epoch, tile, first, hdr, spin_limit);
+        if (lane_id() == 0) {
+            Desc<C>::publish(const_cast<uint64_t *>(desc) + uint64_t(tile) * kDescWords, (epoch << 2) | kStateP,
+                             Op::apply(pre, agg));
+            *prefix = pre;
+        }
+    }
+
+    __device__ __forceinline__ static void set_identity(C *prefix) {
+        if (lane_id() == 0) *prefix = Op::template identity<C>();
     }
 };
 

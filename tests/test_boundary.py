@@ -121,3 +121,30 @@ def test_workspace_bound_covers_plans():
             for tuning in (None, {"block_size": 256, "items_per_thread": 16 // torch.empty(0, dtype=dt).element_size()}):
                 p = binding.plan("scan", dt, "sum", 1, n, tuning=tuning)
                 assert p["workspace_bytes"] <= binding.scan_workspace_bytes(dt, n)
+
+
+def test_element_block_rule_matches_oracle():
+    # The planner applies the large-element block rule (AcceleratedKernels.jl
+    # PR #208) on the HIP side; the oracle implements the same rule
+    # independently.  Widths whose rule lands on 64..256 use the element kernel.
+    import oracle
+    from stream_compaction_wave64_amd import binding
+    import torch
+    oracle.build(force=False)
+    for dt, esz in ((torch.float32, 4), (torch.float64, 8)):
+        for w in (2, 3, 4, 8, 16, 17, 24):
+            for budget in (0, 32768, 65536, 49152):
+                tun = {"local_mem_bytes": budget} if budget else None
+                expect = oracle.block_size(w * esz, budget or 65536, 0, 256)
+                if expect < 64:
+                    continue
+                p = binding.plan("scan", dt, "sum", 1, 10 ** 6, w, tuning=tun)
+                assert p["kernel"] == "element" and p["block_size"] == expect, (dt, w, budget, p)
+    # explicit block size is kept
+    p = binding.plan("scan", torch.float64, "sum", 1, 10 ** 6, 17, tuning={"block_size": 64})
+    assert p["block_size"] == 64
+    # the two struct configs: 136-byte duals and 96-byte structs at the 64 KiB default
+    assert binding.plan("scan", torch.float64, "sum", 1, 10 ** 6, 17)["block_size"] == 128
+    assert binding.plan("scan", torch.float32, "sum", 1, 10 ** 6, 24)["block_size"] == 256
+    assert binding.plan("scan", torch.float64, "sum", 1, 10 ** 6, 17)["carry_words"] == 34
+    assert binding.plan("scan", torch.float32, "sum", 1, 10 ** 6, 24)["carry_words"] == 48
