@@ -24,6 +24,23 @@ ElemLaunch find_element_i64(scan_op_t, int);
 ElemLaunch find_element_f32(scan_op_t, int);
 ElemLaunch find_element_f64(scan_op_t, int);
 
+ColLaunch find_columns_i32(scan_op_t, int);
+ColLaunch find_columns_u32(scan_op_t, int);
+ColLaunch find_columns_i64(scan_op_t, int);
+ColLaunch find_columns_f32(scan_op_t, int);
+ColLaunch find_columns_f64(scan_op_t, int);
+
+ColLaunch find_columns(scan_dtype_t dt, scan_op_t op, int vec) {
+    switch (dt) {
+    case SCAN_I32: return find_columns_i32(op, vec);
+    case SCAN_U32: return find_columns_u32(op, vec);
+    case SCAN_I64: return find_columns_i64(op, vec);
+    case SCAN_F32: return find_columns_f32(op, vec);
+    case SCAN_F64: return find_columns_f64(op, vec);
+    }
+    return nullptr;
+}
+
 ElemLaunch find_element(scan_dtype_t dt, scan_op_t op, int width) {
     switch (dt) {
     case SCAN_I32: return find_element_i32(op, width);
@@ -111,6 +128,7 @@ struct TilePlan {
     size_t ws_bytes;
     int launches;
     int width;                // components per element (element kernel)
+    int64_t col_rows, col_chunks, col_strips;  // column kernel
 };
 
 // Shape of a tile: the default (512 threads x 8 rows of 128-bit vectors, 4
@@ -196,6 +214,39 @@ int plan_element(scan_dtype_t dt, scan_op_t op, int64_t outer, int64_t len, int6
     return SCAN_OK;
 }
 
+// Wide inner extents: reduce-then-scan over row chunks.  About 2048
+// workgroups over (outer, chunk, strip), at least 16 rows per chunk (so the
+// partials stay within 0.5 byte per value) and at most 1024 chunks (one
+// workgroup scans a column's partials).
+int plan_columns(scan_dtype_t dt, scan_op_t op, int64_t outer, int64_t len, int64_t inner, bool aligned,
+                 TilePlan &p) {
+    const int esize = dtype_bytes(dt);
+    const int vmax = 16 / esize;
+    p.kernel = SCAN_KERNEL_COLUMNS;
+    p.vec = (aligned && inner % vmax == 0) ? vmax : 1;
+    if (!find_columns(dt, op, p.vec)) return SCAN_ERR_UNSUPPORTED;
+    p.block = 256;
+    p.rows = 1;
+    p.width = 1;
+    p.col_strips = (inner + 256 * p.vec - 1) / (256 * p.vec);
+    int64_t chunks = (2048 + p.col_strips * outer - 1) / (p.col_strips * outer);
+    int64_t rows = (len + chunks - 1) / chunks;
+    if (rows < 16) rows = 16;
+    if (rows * 1024 < len) rows = (len + 1023) / 1024;
+    p.col_rows = rows;
+    p.col_chunks = (len + rows - 1) / rows;
+    const int64_t wgs = outer * p.col_chunks * p.col_strips;
+    if (wgs > int64_t(INT32_MAX) || outer > int64_t(UINT32_MAX)) return SCAN_ERR_OVERFLOW;
+    p.tile = rows * inner;
+    p.tiles_per_seg = p.col_chunks;
+    p.num_tiles = wgs;
+    p.carry_words = carry_bytes(dt, op) / 4;
+    p.rts_blocks = p.rts_chunk = 0;
+    p.ws_bytes = kHeader + round_up(size_t(outer * p.col_chunks * inner) * carry_bytes(dt, op), 256);
+    p.launches = 3;
+    return SCAN_OK;
+}
+
 int plan_compact(scan_dtype_t dt, int64_t n, bool aligned, const scan_tuning_t &tu, TilePlan &p) {
     const int rc = plan_shape(4, aligned, tu, p, [&](int b, int r, int v) {
         return find_compact(dt, SCAN_CMP_GT, b, r, v) != nullptr;
@@ -245,6 +296,24 @@ int scan_common(const void *in, void *out, int64_t outer, int64_t len, int64_t i
         if (total_out != nullptr) return SCAN_ERR_UNSUPPORTED;
         TilePlan p;
         int rc = plan_element(dt, op, outer, len, inner, aligned16(in, out), tu, p);
+        if (rc == SCAN_ERR_UNSUPPORTED) {
+            rc = plan_columns(dt, op, outer, len, inner, aligned16(in, out), p);
+            if (rc != SCAN_OK) return rc;
+            rc = check_ws(ws, ws_bytes, p.ws_bytes);
+            if (rc != SCAN_OK) return rc;
+            ColArgs c;
+            c.in = in;
+            c.out = out;
+            c.outer = uint32_t(outer);
+            c.len = len;
+            c.inner = inner;
+            c.rows = p.col_rows;
+            c.chunks = uint32_t(p.col_chunks);
+            c.strips = uint32_t(p.col_strips);
+            c.exclusive = exclusive ? 1 : 0;
+            c.partials = reinterpret_cast<char *>(ws) + kHeader;
+            return find_columns(dt, op, p.vec)(c, stream);
+        }
         if (rc != SCAN_OK) return rc;
         rc = check_ws(ws, ws_bytes, p.ws_bytes);
         if (rc != SCAN_OK) return rc;
@@ -323,8 +392,12 @@ int scan_plan(scan_call_t call, scan_dtype_t dtype, scan_op_t op, int64_t outer,
     switch (call) {
     case SCAN_CALL_SCAN:
         if (outer == 0 || len == 0) return SCAN_OK;
-        rc = inner == 1 ? plan_scan(dtype, op, outer, len, true, tu, p)
-                        : plan_element(dtype, op, outer, len, inner, true, tu, p);
+        if (inner == 1) {
+            rc = plan_scan(dtype, op, outer, len, true, tu, p);
+        } else {
+            rc = plan_element(dtype, op, outer, len, inner, true, tu, p);
+            if (rc == SCAN_ERR_UNSUPPORTED) rc = plan_columns(dtype, op, outer, len, inner, true, p);
+        }
         break;
     case SCAN_CALL_COMPACT:
         if (dtype != SCAN_F32 && dtype != SCAN_I32) return SCAN_ERR_UNSUPPORTED;

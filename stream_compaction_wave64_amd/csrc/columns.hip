@@ -1,0 +1,187 @@
+// columns.hip -- scan along the middle axis of an (outer, len, inner) array
+// whose inner extent is too wide for one element per thread: every column
+// (o, :, k) is an independent scan of stride `inner` (AcceleratedKernels.jl
+// PR #208: SliceScan along dims; a 4096 x 4096 row-major matrix scanned down
+// its columns is (1, 4096, 4096)).
+//
+// Reduce-then-scan over row chunks, with threads across columns (The CUDA
+// Handbook ch. 13 section 13.3.3; Merry, "Prefix sums on GPUs", slides
+// "Reduce-then-Scan strategy" and "Prefix-Summing a Block": each workgroup
+// scans its block serially).  A workgroup owns a strip of 256 x VEC columns
+// and a chunk of R rows; every thread owns VEC adjacent columns, so each row
+// of a strip is one coalesced 128-bit access per thread.
+//   1. reduce: each thread folds its columns over the chunk's R rows into one
+//      partial per column (carry type);
+//   2. partials: for every column, an exclusive scan over the chunks (one
+//      thread per chunk, a workgroup scan across them);
+//   3. rescan: each thread runs down its columns again from the chunk's base
+//      and writes the outputs, then zeroes its partials (the workspace's
+//      descriptor area must be left zeroed).
+// Traffic is two reads and one write of the array; the second read of a
+// chunk often hits the 256 MB Infinity Cache when the array is small.
+//
+// Compiled once per element type (SW64_DT).
+#include "launch.hpp"
+#include "tile.hpp"
+
+namespace sw64 {
+
+constexpr int kColThreads = 256;
+
+// Workgroup index -> (outer slice, row chunk, column strip).
+__device__ __forceinline__ static void col_decode(const ColArgs &a, uint32_t wg, uint32_t &o, uint32_t &c,
+                                                  uint32_t &s) {
+    s = wg % a.strips;
+    const uint32_t rest = wg / a.strips;
+    c = rest % a.chunks;
+    o = rest / a.chunks;
+}
+
+template <class T, class Op, int V>
+__global__ __launch_bounds__(kColThreads) void k_col_reduce(ColArgs a) {
+    using C = typename Carry<T, Op>::type;
+    uint32_t o, c, s;
+    col_decode(a, blockIdx.x, o, c, s);
+    const int64_t col = (int64_t(s) * kColThreads + threadIdx.x) * V;
+    if (col >= a.inner) return;
+    const int64_t r0 = int64_t(c) * a.rows, r1 = r0 + a.rows < a.len ? r0 + a.rows : a.len;
+    const T *src = reinterpret_cast<const T *>(a.in) + (int64_t(o) * a.len) * a.inner + col;
+    C acc[V];
+#pragma unroll
+    for (int v = 0; v < V; v++) acc[v] = Op::template identity<C>();
+    // V > 1 only when inner is a multiple of V with 16-byte aligned rows, so
+    // a thread's V columns are one aligned 128-bit access per row.
+    for (int64_t r = r0; r < r1; r++) {
+        const T *p = src + r * a.inner;
+        if constexpr (V > 1) {
+            const Vec<T, V> x = *reinterpret_cast<const Vec<T, V> *>(p);
+#pragma unroll
+            for (int v = 0; v < V; v++) acc[v] = Op::apply(acc[v], C(x.v[v]));
+        } else {
+            acc[0] = Op::apply(acc[0], C(p[0]));
+        }
+    }
+    C *part = reinterpret_cast<C *>(a.partials) + (int64_t(o) * a.chunks + c) * a.inner + col;
+#pragma unroll
+    for (int v = 0; v < V; v++) part[v] = acc[v];
+}
+
+// One workgroup per (outer, group of V columns); thread t is chunk t (the
+// host guarantees chunks <= blockDim.x <= 1024).  Exclusive scan over the
+// chunks with the wave scan and one LDS slot per wave.
+template <class T, class Op, int V>
+__global__ __launch_bounds__(1024) void k_col_partials(ColArgs a) {
+    using C = typename Carry<T, Op>::type;
+    __shared__ C tot[16][V];
+    const int64_t groups = (a.inner + V - 1) / V;
+    const uint32_t o = uint32_t(blockIdx.x / groups);
+    const int64_t col = int64_t(blockIdx.x % groups) * V;
+    const uint32_t c = threadIdx.x;
+    const C id = Op::template identity<C>();
+    C *part = reinterpret_cast<C *>(a.partials) + int64_t(o) * a.chunks * a.inner + col;
+    C x[V], inc[V];
+#pragma unroll
+    for (int v = 0; v < V; v++) x[v] = (c < a.chunks) ? part[int64_t(c) * a.inner + v] : id;
+    const int wave = threadIdx.x / kWave, waves = blockDim.x / kWave;
+#pragma unroll
+    for (int v = 0; v < V; v++) inc[v] = wave_scan_incl<Op>(x[v]);
+    if (lane_id() == kWave - 1) {
+#pragma unroll
+        for (int v = 0; v < V; v++) tot[wave][v] = inc[v];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int v = 0; v < V; v++) {
+        C base = id;
+        for (int w = 0; w < waves && w < wave; w++) base = Op::apply(base, tot[w][v]);
+        const C ex = Op::apply(base, wave_shr1(id, inc[v]));
+        if (c < a.chunks) part[int64_t(c) * a.inner + v] = ex;
+    }
+}
+
+template <class T, class Op, int V>
+__global__ __launch_bounds__(kColThreads) void k_col_rescan(ColArgs a) {
+    using C = typename Carry<T, Op>::type;
+    uint32_t o, c, s;
+    col_decode(a, blockIdx.x, o, c, s);
+    const int64_t col = (int64_t(s) * kColThreads + threadIdx.x) * V;
+    if (col >= a.inner) return;
+    const int64_t r0 = int64_t(c) * a.rows, r1 = r0 + a.rows < a.len ? r0 + a.rows : a.len;
+    const int64_t base_off = (int64_t(o) * a.len) * a.inner + col;
+    const T *src = reinterpret_cast<const T *>(a.in) + base_off;
+    T *dst = reinterpret_cast<T *>(a.out) + base_off;
+    C *part = reinterpret_cast<C *>(a.partials) + (int64_t(o) * a.chunks + c) * a.inner + col;
+    C run[V];
+#pragma unroll
+    for (int v = 0; v < V; v++) {
+        run[v] = part[v];
+        part[v] = C{};  // leave the workspace zeroed
+    }
+    for (int64_t r = r0; r < r1; r++) {
+        const T *p = src + r * a.inner;
+        T *q = dst + r * a.inner;
+        if constexpr (V > 1) {
+            const Vec<T, V> x = *reinterpret_cast<const Vec<T, V> *>(p);
+            Vec<T, V> y;
+#pragma unroll
+            for (int v = 0; v < V; v++) {
+                const C next = Op::apply(run[v], C(x.v[v]));
+                y.v[v] = T(a.exclusive ? run[v] : next);
+                run[v] = next;
+            }
+            *reinterpret_cast<Vec<T, V> *>(q) = y;
+        } else {
+            const C next = Op::apply(run[0], C(p[0]));
+            q[0] = T(a.exclusive ? run[0] : next);
+            run[0] = next;
+        }
+    }
+}
+
+template <class T, class Op, int V>
+static int launch_columns_impl(const ColArgs &a, hipStream_t s) {
+    const uint32_t wgs = a.outer * a.chunks * a.strips;
+    hipLaunchKernelGGL((k_col_reduce<T, Op, V>), dim3(wgs), dim3(kColThreads), 0, s, a);
+    if (hipGetLastError() != hipSuccess) return SCAN_ERR_HIP;
+    const int64_t groups = (a.inner + V - 1) / V;
+    const uint32_t pthreads = ((a.chunks + kWave - 1) / kWave) * kWave;
+    hipLaunchKernelGGL((k_col_partials<T, Op, V>), dim3(uint32_t(a.outer * groups)), dim3(pthreads), 0, s, a);
+    if (hipGetLastError() != hipSuccess) return SCAN_ERR_HIP;
+    hipLaunchKernelGGL((k_col_rescan<T, Op, V>), dim3(wgs), dim3(kColThreads), 0, s, a);
+    return hipGetLastError() == hipSuccess ? SCAN_OK : SCAN_ERR_HIP;
+}
+
+template <class T, class Op>
+static ColLaunch pick_col_vec(int vec) {
+    constexpr int VMAX = 16 / int(sizeof(T));
+    if (vec == VMAX) return &launch_columns_impl<T, Op, VMAX>;
+    if (vec == 1) return &launch_columns_impl<T, Op, 1>;
+    return nullptr;
+}
+
+template <class T>
+static ColLaunch pick_col_op(scan_op_t op, int vec) {
+    switch (op) {
+    case SCAN_OP_SUM: return pick_col_vec<T, OpSum>(vec);
+    case SCAN_OP_PROD: return pick_col_vec<T, OpProd>(vec);
+    case SCAN_OP_MAX: return pick_col_vec<T, OpMax>(vec);
+    case SCAN_OP_MIN: return pick_col_vec<T, OpMin>(vec);
+    }
+    return nullptr;
+}
+
+#if SW64_DT == 0
+ColLaunch find_columns_i32(scan_op_t op, int v) { return pick_col_op<int32_t>(op, v); }
+#elif SW64_DT == 1
+ColLaunch find_columns_u32(scan_op_t op, int v) { return pick_col_op<uint32_t>(op, v); }
+#elif SW64_DT == 2
+ColLaunch find_columns_i64(scan_op_t op, int v) { return pick_col_op<int64_t>(op, v); }
+#elif SW64_DT == 3
+ColLaunch find_columns_f32(scan_op_t op, int v) { return pick_col_op<float>(op, v); }
+#elif SW64_DT == 4
+ColLaunch find_columns_f64(scan_op_t op, int v) { return pick_col_op<double>(op, v); }
+#else
+#error "SW64_DT must select an element type (0..4)"
+#endif
+
+}  // namespace sw64

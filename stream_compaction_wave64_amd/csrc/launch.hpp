@@ -77,6 +77,24 @@ struct ElemArgs {
 using ElemLaunch = int (*)(const ElemArgs &, int block, uint32_t grid_cap, hipStream_t);
 ElemLaunch find_element(scan_dtype_t dt, scan_op_t op, int width);
 
+// ------------------------------------------------------------ wide columns
+// (outer, len, inner) with a wide inner extent: reduce-then-scan over chunks
+// of `rows` rows, workgroups of 256 threads over strips of 256 x vec columns.
+struct ColArgs {
+    const void *in;
+    void *out;
+    uint32_t outer;
+    int64_t len;
+    int64_t inner;
+    int64_t rows;             // rows per chunk (R)
+    uint32_t chunks;          // chunks per column (<= 1024)
+    uint32_t strips;          // column strips
+    int32_t exclusive;
+    void *partials;           // outer * chunks * inner carry values, in the workspace
+};
+using ColLaunch = int (*)(const ColArgs &, hipStream_t);
+ColLaunch find_columns(scan_dtype_t dt, scan_op_t op, int vec);
+
 // -------------------------------------------------------------- utilities
 int launch_fill_u64(void *p, uint64_t words, uint64_t value, hipStream_t s);
 int launch_fill_i32(int32_t *p, int64_t count, int32_t value, hipStream_t s);
