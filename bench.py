@@ -10,6 +10,17 @@ Prints one JSON line with the throughput (GElem/s), the roofline of the scan
 kernel (algorithmic bytes = one read + one write of n fp32 values per launch,
 over the measured average launch duration, against 8 TB/s HBM), the copy
 ceiling measured the same way, and the CPU oracle timed on this host.
+
+Beside the headline figure, "rows" times every other workload of the path
+once each: int32 2^20 inclusive and exclusive, fp64 1e7, the reduce-then-scan
+comparison on the fp32 1e8 array, the four 2-D scans (4096 x 4096 along rows
+and along columns, 1e6 x 8 along its long axis, 2 x 1e7 along rows),
+compaction of 1e7 fp32 with x > 0.5, count-scan-emit packing of 1e7 Poisson(3)
+counts, and the 136-byte and 96-byte struct scans of 1e6 elements.  Each row
+rotates over enough copies of its buffers (> 512 MB in all) that no call
+finds its data in the 256 MB Infinity Cache, replays the calls from a HIP
+graph (so small launches are not timed against the Python host), and reports
+the algorithmic bytes of one call over its average duration.
 """
 from __future__ import annotations
 
@@ -29,14 +40,14 @@ N = 10 ** 8
 # known size (profiles/lookback_scan_fp32_1e8_hbm_counters.md).  Valid only for
 # the kernel sources that were measured: reported as null once they change.
 TRAFFIC_BYTES = 8.044e8
-TRAFFIC_SOURCES_SHA = "42001f70c2cfdd68"
+TRAFFIC_SOURCES_SHA = "f2411b1868591862"
 
 
 def _kernel_sources_sha():
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "stream_compaction_wave64_amd", "csrc")
-    for f in ("lookback.hip", "tile.hpp", "device.hpp"):
+    for f in ("lookback.hip", "pipeline.hpp", "tile.hpp", "device.hpp"):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -52,6 +63,8 @@ def parse():
     ap.add_argument("--ipt", type=int, default=0, help="tuning: items per thread")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle leg (profiling runs)")
     ap.add_argument("--no-verify", action="store_true")
+    ap.add_argument("--no-rows", action="store_true", help="time only the headline fp32 1e8 scan")
+    ap.add_argument("--row-steps", type=int, default=20, help="calls timed per row")
     return ap.parse_args()
 
 
@@ -86,6 +99,184 @@ def cpu_baseline(x: np.ndarray):
     return {"value": round(x.size / best / 1e9, 4), "unit": "GElem/s", "cores": 1, "kind": "oracle",
             "sample": f"full {x.size:.0e}-element fp32 array, sequential fp64 accumulation, best of {runs} runs",
             "host_cpus": os.cpu_count()}, ref
+
+
+# ------------------------------------------------------------------ rows
+COLD_BYTES = 512 << 20  # buffers touched per rotation: twice the Infinity Cache
+
+
+class _Row:
+    """One workload: `sets` copies of its buffers and a call per copy."""
+
+    def __init__(self, name, workload, elems, alg_bytes, set_bytes, make, check=None):
+        self.name, self.workload, self.elems, self.alg_bytes = name, workload, elems, alg_bytes
+        self.sets = max(1, -(-COLD_BYTES // max(set_bytes, 1)))
+        self.make, self.check = make, check
+
+
+def _rows(dev, lib, binding, inputs):
+    """Row definitions; each make(k) returns (call(stream), outputs) for buffer set k."""
+    import torch
+    vp = lambda t: t.data_ptr()  # noqa: E731
+    null = binding._tuning(None)
+    rows = []
+
+    def ws_for(call, dtype, op, outer, length, inner, tuning=None):
+        p = binding.plan(call, dtype, op, outer, length, inner, tuning)
+        return torch.zeros(max(int(p["workspace_bytes"]), 1 << 16), dtype=torch.uint8, device=dev)
+
+    def scan_row(name, workload, host, width=1, excl=False, algo=None, elems=None):
+        x0 = torch.from_numpy(host).to(dev)
+        n = x0.numel() // width
+        tun = {"algo": algo} if algo else None
+        ws = ws_for("scan", x0.dtype, "sum", 1, n, width, tun)
+        fn = lib.scan_exclusive if excl else lib.scan_inclusive
+        t = binding._tuning(tun)
+        dt = binding._dtype(x0)
+
+        def make(k):
+            x = x0 if k == 0 else x0.clone()
+            y = torch.empty_like(x)
+            return (lambda s: fn(vp(x), vp(y), n, dt, 0, width, vp(ws), ws.numel(), t, s)), [y]
+        b = x0.numel() * x0.element_size()
+        rows.append(_Row(name, workload, elems or n, 2 * b, 2 * b, make))
+
+    def dim_row(name, workload, host, dim):
+        x0 = torch.from_numpy(np.ascontiguousarray(host)).to(dev)
+        shape = list(x0.shape)
+        outer = int(np.prod(shape[:dim], dtype=np.int64))
+        length = shape[dim]
+        inner = int(np.prod(shape[dim + 1:], dtype=np.int64))
+        ws = ws_for("scan", x0.dtype, "sum", outer, length, inner)
+        dt = binding._dtype(x0)
+
+        def make(k):
+            x = x0 if k == 0 else x0.clone()
+            y = torch.empty_like(x)
+            return (lambda s: lib.scan_dim(vp(x), vp(y), outer, length, inner, dt, 0, 0, vp(ws), ws.numel(),
+                                           null, s)), [y]
+        b = x0.numel() * x0.element_size()
+        rows.append(_Row(name, workload, x0.numel(), 2 * b, 2 * b, make))
+
+    scan_row("int32_incl_2p20", "int32 inclusive sum scan, n=2^20, uniform 0..100, seed 0",
+             inputs.int32_uniform_0_100(2 ** 20, 0))
+    scan_row("int32_excl_2p20", "int32 exclusive sum scan, n=2^20, uniform 0..100, seed 0",
+             inputs.int32_uniform_0_100(2 ** 20, 0), excl=True)
+    scan_row("fp64_incl_1e7", "fp64 inclusive sum scan, n=1e7, uniform [-1,1), seed 1",
+             inputs.f64_uniform_pm1(10 ** 7, 1))
+    scan_row("fp32_incl_1e8_reduce_then_scan", "fp32 inclusive sum scan, n=1e8, reduce-then-scan (3 launches)",
+             inputs.f32_uniform_01(N, 1), algo="reduce_then_scan")
+    sq, tall, wide = inputs.dims_arrays(3)
+    dim_row("fp32_4096x4096_along_rows", "4096 x 4096 fp32 row-major, scan along rows (dim 1), seed 3", sq, 1)
+    dim_row("fp32_4096x4096_along_cols", "4096 x 4096 fp32 row-major, scan along columns (dim 0), seed 3", sq, 0)
+    dim_row("fp32_1e6x8_along_dim0", "1e6 x 8 fp32, scan along the 1e6 axis (dim 0), seed 3", tall, 0)
+    dim_row("fp32_2x1e7_along_rows", "2 x 1e7 fp32, scan along rows (dim 1), seed 3", wide, 1)
+    del sq, tall, wide
+
+    xc, counts = inputs.compaction_inputs(10 ** 7, 4)
+    x0 = torch.from_numpy(xc).to(dev)
+    n = x0.numel()
+    kept = int(np.count_nonzero(xc > np.float32(0.5)))
+    ws_c = ws_for("compact", torch.float32, "sum", 1, n, 1)
+
+    def make_compact(k):
+        x = x0 if k == 0 else x0.clone()
+        idx = torch.empty(n, dtype=torch.int32, device=dev)
+        cnt = torch.empty(1, dtype=torch.int32, device=dev)
+        return (lambda s: lib.compact_if(vp(x), n, 3, 0, 0.5, vp(idx), vp(cnt), vp(ws_c), ws_c.numel(), null,
+                                         s)), [idx, cnt]
+    rows.append(_Row("compact_fp32_gt_half_1e7", "compaction of 1e7 fp32 uniform [0,1) with x > 0.5, seed 4",
+                     n, 4 * n + 4 * kept + 4, 4 * n + 4 * kept, make_compact))
+
+    c0 = torch.from_numpy(counts).to(dev)
+    total = int(counts.sum(dtype=np.int64))
+    ws_p = ws_for("pack", torch.int32, "sum", 1, n, 1)
+
+    def make_pack(k):
+        c = c0 if k == 0 else c0.clone()
+        off = torch.empty(n + 1, dtype=torch.int32, device=dev)
+        rec = torch.empty(total, dtype=torch.int32, device=dev)
+
+        def call(s):
+            st = lib.pack_offsets(vp(c), n, vp(off), vp(ws_p), ws_p.numel(), null, s)
+            return st or lib.pack_emit_neighbors(vp(off), n, vp(rec), s)
+        return call, [off, rec]
+    rows.append(_Row("pack_offsets_emit_1e7", "count-scan-emit: offsets of 1e7 Poisson(3) int32 counts, then "
+                     "emit of every record (2 launches), seed 4", n, 4 * n + 4 * (n + 1) + 4 * total,
+                     4 * n + 8 * (n + 1) + 4 * total, make_pack))
+    del xc, counts
+
+    s64, s32 = inputs.struct_inputs(10 ** 6, 5)
+    scan_row("struct136_fp64x17_1e6", "1e6 elements of 17 fp64 (136 B), elementwise sum, seed 5", s64.reshape(-1),
+             width=17)
+    scan_row("struct96_fp32x24_1e6", "1e6 elements of 24 fp32 (96 B), elementwise sum, seed 5", s32.reshape(-1),
+             width=24)
+    return rows
+
+
+def time_row(row, lib, steps, warmup, use_graph=True):
+    """Average duration of one call of the row, cycling through its buffer sets."""
+    import torch
+    calls, outs = [], []
+    for k in range(row.sets):
+        c, o = row.make(k)
+        calls.append(c)
+        outs.append(o)
+    stream = torch.cuda.current_stream()
+
+    def run_all(s):
+        for c in calls:
+            st = c(s)
+            if st != 0:
+                raise RuntimeError(f"{row.name}: {lib.scan_status_string(st).decode()} (status {st})")
+
+    for _ in range(max(warmup, 1)):
+        run_all(stream.cuda_stream)
+    torch.cuda.synchronize()
+    eager = [[t.clone() for t in o] for o in outs[:1]]
+    graph = None
+    if use_graph:
+        try:
+            g = torch.cuda.CUDAGraph()
+            side = torch.cuda.Stream()
+            side.wait_stream(stream)
+            with torch.cuda.stream(side):
+                g.capture_begin()
+                try:
+                    run_all(side.cuda_stream)
+                finally:
+                    g.capture_end()
+            stream.wait_stream(side)
+            torch.cuda.synchronize()
+            graph = g
+        except Exception as e:  # report and time eagerly
+            print(f"# {row.name}: graph capture failed ({e}); timing eager calls", file=sys.stderr)
+            graph = None
+    reps = max(2, -(-steps // row.sets))
+    fn = graph.replay if graph is not None else (lambda: run_all(stream.cuda_stream))
+    fn()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(reps):
+        fn()
+    end.record(stream)
+    torch.cuda.synchronize()
+    us = start.elapsed_time(end) * 1e3 / (reps * row.sets)
+    same = all(_same(a, b) for a, b in zip(eager[0], outs[0]))
+    gbs = row.alg_bytes / (us * 1e-6) / 1e9
+    return {"workload": row.workload, "us_per_call": round(us, 3), "gelem_s": round(row.elems / us / 1e3, 3),
+            "alg_bytes": int(row.alg_bytes), "achieved_gbs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "buffer_sets": row.sets, "hip_graph": graph is not None, "replay_matches_eager": same}
+
+
+def _same(a, b):
+    import torch
+    if a.dtype.is_floating_point:
+        # look-back combines predecessors in an order that depends on timing
+        return bool(torch.allclose(a, b, rtol=1e-5, atol=1e-3))
+    return bool(torch.equal(a, b))
 
 
 def main():
@@ -144,6 +335,15 @@ def main():
         "copy_ceiling": {"achieved": round(copy_gbs, 1), "unit": "GB/s", "frac": round(copy_gbs / HBM_PEAK_GBS, 4),
                          "scan_vs_copy": round(achieved / copy_gbs, 4)},
     }
+
+    if not args.no_rows:
+        from stream_compaction_wave64_amd import binding
+        lib = binding.load_library()
+        rows = {}
+        for row in _rows(dev, lib, binding, inputs):
+            rows[row.name] = time_row(row, lib, args.row_steps, 2)
+            torch.cuda.empty_cache()
+        result["rows"] = rows
 
     ref = None
     if not args.no_cpu_baseline:
