@@ -42,8 +42,9 @@
  * on arrays of up to `count` values).  Before its first use it must be zeroed
  * once (scan_workspace_init or any zero fill).  After that it is self-
  * resetting: the look-back kernels tag their tile descriptors with a per-
- * workspace epoch held in the workspace header and advance it at the end of
- * each call, so no clearing launch is needed between calls.  Calls that may
+ * workspace epoch held in the workspace header, advance it at the end of
+ * each call and clear the descriptor words a previous, larger call left
+ * above their own, so no clearing launch is needed between calls.  Calls that may
  * overlap in time (different streams) need distinct workspaces.  Layout
  * (informative): bytes [0, 4096) header { uint32 epoch, uint32 error word,
  * uint64 descriptor high-water mark, uint32 mode, uint32 claim counter, and
@@ -145,7 +146,8 @@ typedef struct {
     int64_t lds_bytes;         /* LDS per workgroup of the main launch */
     int64_t workspace_bytes;   /* workspace this call needs */
     int32_t launches;          /* kernel launches the call enqueues */
-    int32_t carry_words;       /* 64-bit descriptor words per tile */
+    int32_t carry_words;       /* 64-bit descriptor words per tile (look-back kernels; carry
+                                  values per partial for reduce-then-scan) */
 } scan_plan_t;
 
 /* Which call scan_plan describes. */

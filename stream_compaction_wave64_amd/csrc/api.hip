@@ -107,6 +107,14 @@ int carry_bytes(scan_dtype_t dt, scan_op_t op) {
     return dtype_bytes(dt);
 }
 
+// 64-bit descriptor words per tile of a scalar look-back scan: one 32-bit
+// chunk per word, except fp32 sums and products, whose fp64 carry packs into
+// one word (DescTrunc in device.hpp).
+int desc_words(scan_dtype_t dt, scan_op_t op) {
+    if (dt == SCAN_F32 && (op == SCAN_OP_SUM || op == SCAN_OP_PROD)) return 1;
+    return carry_bytes(dt, op) / 4;
+}
+
 size_t round_up(size_t x, size_t m) { return (x + m - 1) / m * m; }
 
 scan_tuning_t tuning_or_default(const scan_tuning_t *t) {
@@ -135,9 +143,10 @@ struct TilePlan {
 // rows for 8-byte elements), or block_size / items_per_thread from the
 // tuning.  The element-wide fallback (misaligned data or a length that
 // breaks the vector alignment) is built for the default and one-row shapes:
-// a tuned shape snaps to the nearer.
+// a tuned shape snaps to the nearer.  Kernels with a control wave (`ctrl`)
+// give the tile block - 64 threads.
 template <class Find>
-int plan_shape(int esize, bool vec_ok, const scan_tuning_t &tu, TilePlan &p, Find find) {
+int plan_shape(int esize, bool vec_ok, const scan_tuning_t &tu, TilePlan &p, Find find, bool ctrl = false) {
     const int vmax = 16 / esize;
     const int rows_default = esize == 8 ? kDefaultRows / 2 : kDefaultRows;
     p.vec = vec_ok ? vmax : 1;
@@ -151,7 +160,7 @@ int plan_shape(int esize, bool vec_ok, const scan_tuning_t &tu, TilePlan &p, Fin
         p.block = p.rows == 1 ? 256 : kDefaultBlock;
     }
     if (!find(p.block, p.rows, p.vec)) return SCAN_ERR_UNSUPPORTED;
-    p.tile = int64_t(p.block) * p.rows * p.vec;
+    p.tile = int64_t(ctrl ? p.block - 64 : p.block) * p.rows * p.vec;
     return SCAN_OK;
 }
 
@@ -163,13 +172,14 @@ int plan_scan(scan_dtype_t dt, scan_op_t op, int64_t outer, int64_t len, bool al
     const bool vec_ok = aligned && len % (16 / esize) == 0;
     int rc = rts ? plan_shape(esize, vec_ok, tu, p,
                               [&](int b, int r, int v) { return find_rts(dt, op, b, r, v) != nullptr; })
-                 : plan_shape(esize, vec_ok, tu, p,
-                              [&](int b, int r, int v) { return find_lookback(dt, op, b, r, v) != nullptr; });
+                 : plan_shape(
+                       esize, vec_ok, tu, p,
+                       [&](int b, int r, int v) { return find_lookback(dt, op, b, r, v) != nullptr; }, true);
     if (rc != SCAN_OK) return rc;
     p.tiles_per_seg = (len + p.tile - 1) / p.tile;
     p.num_tiles = outer * p.tiles_per_seg;
     if (p.num_tiles > int64_t(INT32_MAX)) return SCAN_ERR_OVERFLOW;  // grid x limit
-    p.carry_words = carry_bytes(dt, op) / 4;
+    p.carry_words = rts ? carry_bytes(dt, op) / 4 : desc_words(dt, op);
     if (rts) {
         p.kernel = SCAN_KERNEL_RTS;
         int64_t c = tu.rts_blocks > 0 ? tu.rts_blocks : kDefaultRtsBlocks;
@@ -248,9 +258,10 @@ int plan_columns(scan_dtype_t dt, scan_op_t op, int64_t outer, int64_t len, int6
 }
 
 int plan_compact(scan_dtype_t dt, int64_t n, bool aligned, const scan_tuning_t &tu, TilePlan &p) {
-    const int rc = plan_shape(4, aligned, tu, p, [&](int b, int r, int v) {
-        return find_compact(dt, SCAN_CMP_GT, b, r, v) != nullptr;
-    });
+    // 128-bit loads need 16-byte aligned x and whole vectors up to n
+    const int rc = plan_shape(
+        4, aligned && n % 4 == 0, tu, p,
+        [&](int b, int r, int v) { return find_compact(dt, SCAN_CMP_GT, b, r, v) != nullptr; }, true);
     if (rc != SCAN_OK) return rc;
     p.kernel = SCAN_KERNEL_COMPACT;
     p.tiles_per_seg = p.num_tiles = (n + p.tile - 1) / p.tile;

@@ -29,79 +29,109 @@ __device__ __forceinline__ bool keep(X v, X t) {
 }
 
 template <class X, int CMP, int BLOCK_, int ROWS, int VEC>
-struct CompactPolicy : ScalarCarry<OpSum, int32_t> {
+struct CompactPolicy {
     using T = int32_t;
     using Op = OpSum;
     using C = int32_t;
+    using D = Desc<C>;
+    static constexpr int kDescWords = D::kWords;
     static constexpr int BLOCK = BLOCK_;
     using TS = TileScan<int32_t, OpSum, BLOCK, ROWS, VEC>;
     using Args = CompactArgs;
     using Shared = typename TS::Shared;
     static_assert(ROWS * VEC <= 32, "selection bits fit one word");
 
+    __device__ __forceinline__ static C aggregate(const Shared &sh) { return TS::template aggregate_from<C>(sh); }
+
+    // A scanned tile waiting for its prefix: every thread's row offsets and
+    // selection bits.
+    struct Stash {
+        int32_t off[ROWS][BLOCK];
+        uint32_t bits[BLOCK];
+    };
+
+    // Each selected element's index at its position.
+    __device__ __forceinline__ static void emit(const Stash &st, const Args &a, uint32_t tile, C pre, bool valid) {
+        if (!valid) return;
+        const int64_t start = int64_t(tile) * TS::TILE;
+        const uint32_t bits = st.bits[threadIdx.x];
+#pragma unroll
+        for (int r = 0; r < ROWS; r++) {
+            const int64_t e = TS::elem(r);
+            int32_t pos = pre + st.off[r][threadIdx.x];
+#pragma unroll
+            for (int c = 0; c < VEC; c++) {
+                if (bits & (1u << (r * VEC + c))) {
+                    a.out_idx[pos] = int32_t(start + e + c);
+                    pos++;
+                }
+            }
+        }
+    }
+
+    // The count after the last tile.
+    __device__ __forceinline__ static void on_resolved(const Args &a, uint32_t tile, C pre, C agg) {
+        if (tile == a.pipe.num_tiles - 1) *a.count = pre + agg;
+    }
+
     struct Tile {
-        TS ts;
+        TS ts;          // raw element bits after load, 0/1 counts after scan
         uint32_t bits;  // bit r*VEC + c: element c of this thread's vector in row r is selected
+        uint32_t thr;   // threshold bits
+        int64_t rem;    // elements of the tile in range
 
-        __device__ __forceinline__ void set_slot(int) {}
-
+        // Issue the loads only (see TileScan::load): the predicate is
+        // evaluated in scan(), so pipelined loads stay in flight.  Every
+        // load is unconditional: rows past the end re-read the tile's first
+        // vector (n is a multiple of VEC), and a tile past the end (the
+        // pipeline's prefetch beyond the last tile) reads x's first vector.
         __device__ __forceinline__ void load(const Args &a, uint32_t tile) {
-            const int64_t start = int64_t(tile) * TS::TILE;
-            const int64_t remaining = a.n - start;
-            const X *x = reinterpret_cast<const X *>(a.x) + start;
-            const X t = __builtin_bit_cast(X, a.threshold);
+            const bool valid = tile < a.pipe.num_tiles;
+            const int64_t start = valid ? int64_t(tile) * TS::TILE : 0;
+            rem = valid ? uniform(a.n - start) : 0;
+            thr = a.threshold;
+            const int32_t *x = reinterpret_cast<const int32_t *>(a.x) + uniform(start);
+#pragma unroll
+            for (int r = 0; r < ROWS; r++) {
+                const int64_t e = TS::elem(r);
+                ts.v[r] = load_vec<int32_t, VEC>(x + (e < rem ? e : 0));
+            }
+        }
+
+        __device__ __forceinline__ void scan(Shared &sh) {
+            const X t = __builtin_bit_cast(X, thr);
             bits = 0;
 #pragma unroll
             for (int r = 0; r < ROWS; r++) {
                 const int64_t e = TS::elem(r);
-                Vec<X, VEC> v;
-                if (e + VEC <= remaining) {
-                    v = load_vec<X, VEC>(x + e);
-                } else {
-#pragma unroll
-                    for (int c = 0; c < VEC; c++) v.v[c] = (e + c < remaining) ? x[e + c] : t;
-                }
 #pragma unroll
                 for (int c = 0; c < VEC; c++) {
-                    const bool k = (e + c < remaining) && keep<X, CMP>(v.v[c], t);
+                    const bool k = (e + c < rem) && keep<X, CMP>(__builtin_bit_cast(X, ts.v[r].v[c]), t);
                     ts.v[r].v[c] = k ? 1 : 0;
                     bits |= uint32_t(k) << (r * VEC + c);
                 }
             }
+            ts.rem = TS::TILE;  // counts past the end are already 0
+            ts.scan(sh);
         }
 
-        __device__ __forceinline__ void scan(Shared &sh) { ts.scan(sh); }
-
-        __device__ __forceinline__ C aggregate() const { return ts.agg; }
-
-        __device__ __forceinline__ void emit(const Args &a, uint32_t tile, const C *prefix) const {
-            const int64_t start = int64_t(tile) * TS::TILE;
-            const int32_t pre = *prefix;
+        __device__ __forceinline__ void stash(Stash &st, const Args &) const {
 #pragma unroll
-            for (int r = 0; r < ROWS; r++) {
-                const int64_t e = TS::elem(r);
-                int32_t pos = pre + ts.off[r];
-#pragma unroll
-                for (int c = 0; c < VEC; c++) {
-                    if (bits & (1u << (r * VEC + c))) {
-                        a.out_idx[pos] = int32_t(start + e + c);
-                        pos++;
-                    }
-                }
-            }
-            if (threadIdx.x == 0 && tile == a.pipe.num_tiles - 1) *a.count = pre + ts.agg;
+            for (int r = 0; r < ROWS; r++) st.off[r][threadIdx.x] = ts.off[r];
+            st.bits[threadIdx.x] = bits;
         }
     };
 };
 
 template <class P>
-__global__ __launch_bounds__(P::BLOCK) void k_compact(typename P::Args a) {
-    Pipeline<P>::run(a);
+__global__ __launch_bounds__(CtrlPipeline<P>::THREADS) void k_compact(typename P::Args a) {
+    CtrlPipeline<P>::run(a);
 }
 
+// B threads per workgroup: B - 64 data threads and the control wave.
 template <class X, int CMP, int B, int R, int V>
 static int launch_compact_impl(const CompactArgs &a, uint32_t grid_cap, hipStream_t s) {
-    using P = CompactPolicy<X, CMP, B, R, V>;
+    using P = CompactPolicy<X, CMP, B - kWave, R, V>;
     const int g = pipeline_grid(reinterpret_cast<const void *>(&k_compact<P>), B, a.pipe.num_tiles, grid_cap);
     if (g <= 0) return SCAN_ERR_HIP;
     hipLaunchKernelGGL((k_compact<P>), dim3(g), dim3(B), 0, s, a);

@@ -157,54 +157,106 @@ __device__ __forceinline__ T wave_reduce(T x) {
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// A wave-uniform value moved to scalar registers, so that branches on it are
+// scalar branches rather than exec-mask regions.
+// (The builtin returns a signed int: each half is widened as unsigned.)
+__device__ __forceinline__ uint32_t uniform(uint32_t x) { return uint32_t(__builtin_amdgcn_readfirstlane(x)); }
+__device__ __forceinline__ int64_t uniform(int64_t x) {
+    const uint64_t u = uint64_t(x);
+    const uint64_t hi = uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(u >> 32)));
+    const uint64_t lo = uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(u)));
+    return int64_t((hi << 32) | lo);
+}
+
 // --------------------------------------------------------- tile descriptors --
 //
 // A tile publishes its aggregate (state A) and later its inclusive prefix
-// (state P) in `words` 64-bit descriptor words.  Each word carries one 32-bit
-// chunk of the carry value in its low half and, in its high half, the tag
-// (epoch << 2 | state).  Any word whose tag is not the current epoch reads as
-// X (nothing published), so a stale workspace needs no clearing.  A value
-// wider than 32 bits spans several words written one after another; a
-// reader accepts it only when every word carries the same tag, which is
-// unambiguous because each state is written exactly once per call.  Plain
-// agent-scope atomic loads and stores suffice: no fence is needed, since a
-// reader never combines a tag with a value from another write.
+// (state P) in 64-bit descriptor words written with agent-scope atomic
+// stores.  Every word carries in its top 10 bits the tag (epoch mod 256) << 2
+// | state and a payload in the low 54 bits.  A word whose tag is not the
+// running call's reads as X (nothing published yet).  Each call rewrites
+// every word it uses and, at its end, clears the words above its own up to
+// the previous high-water mark (end_call), so every word of the workspace
+// carries the last call's tag or none: consecutive calls need only distinct
+// tags.
+//
+// Desc<C>: C split into 32-bit chunks, one per word, written one after
+// another; a reader accepts the value only when every word carries the same
+// tag, which is unambiguous because each state is written exactly once per
+// call.  DescTrunc: a double in one word, its low 10 mantissa bits dropped
+// (42 of 52 kept, relative change below 2^-42) -- the inter-tile carry of
+// fp32 sums and products, which only needs to be far more precise than the
+// fp32 outputs.  Plain agent-scope atomic loads and stores suffice: no fence
+// is needed, since a reader never combines a tag with a value from another
+// write.
 
 constexpr uint32_t kStateA = 1u, kStateP = 2u;
-constexpr uint32_t kEpochMask = 0x3fffffffu;
+constexpr uint32_t kEpochMask = 0x3fffffffu;  // the header's epoch counter
+constexpr int kTagShift = 54;
+
+__device__ __forceinline__ uint64_t desc_tag(uint32_t epoch, uint32_t state) {
+    return uint64_t(((epoch & 0xffu) << 2) | state) << kTagShift;
+}
+
+// The state a word shows to a call at `epoch`: kStateA / kStateP, or 0 (X).
+// An epoch outside the counter's range (a corrupted header) matches no tag,
+// so every look-back times out and reports it.
+__device__ __forceinline__ uint32_t desc_state(uint64_t w, uint32_t epoch) {
+    const uint32_t tag = uint32_t(w >> kTagShift);
+    const uint32_t want = epoch <= kEpochMask ? (epoch & 0xffu) : 0x400u;
+    return (tag >> 2) == want ? (tag & 3u) : 0u;
+}
 
 template <class C>
 struct Desc {
     static constexpr int kWords = int(sizeof(C) / 4);
     struct Chunks { uint32_t w[kWords]; };
 
-    __device__ __forceinline__ static void publish(uint64_t *d, uint32_t tag, C value) {
-        Chunks c = __builtin_bit_cast(Chunks, value);
+    __device__ __forceinline__ static void publish(uint64_t *d, uint32_t epoch, uint32_t state, C value) {
+        const Chunks c = __builtin_bit_cast(Chunks, value);
+        const uint64_t tag = desc_tag(epoch, state);
 #pragma unroll
         for (int i = 0; i < kWords; i++)
-            __hip_atomic_store(d + i, (uint64_t(tag) << 32) | c.w[i], __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(d + i, tag | c.w[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 
-    // Returns kStateA / kStateP when all words carry that state of `epoch`,
-    // 0 otherwise (not yet published, or caught between two word writes).
+    // kStateA / kStateP when all words carry that state of `epoch`, 0
+    // otherwise (not yet published, or caught between two word writes).
     __device__ __forceinline__ static uint32_t read(const uint64_t *d, uint32_t epoch, C &value) {
         uint64_t w[kWords];
 #pragma unroll
         for (int i = 0; i < kWords; i++)
             w[i] = __hip_atomic_load(d + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const uint32_t tag = uint32_t(w[0] >> 32);
-        bool ok = (tag >> 2) == epoch && (tag & 3u) != 0u;
+        const uint32_t state = desc_state(w[0], epoch);
+        bool ok = state != 0u;
         Chunks c;
 #pragma unroll
         for (int i = 0; i < kWords; i++) {
-            ok = ok && uint32_t(w[i] >> 32) == tag;
+            ok = ok && (w[i] >> kTagShift) == (w[0] >> kTagShift);
             c.w[i] = uint32_t(w[i]);
         }
         value = __builtin_bit_cast(C, c);
-        return ok ? (tag & 3u) : 0u;
+        return ok ? state : 0u;
     }
 };
+
+struct DescTrunc {
+    static constexpr int kWords = 1;
+    __device__ __forceinline__ static void publish(uint64_t *d, uint32_t epoch, uint32_t state, double value) {
+        __hip_atomic_store(d, desc_tag(epoch, state) | (__builtin_bit_cast(uint64_t, value) >> (64 - kTagShift)),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __device__ __forceinline__ static uint32_t read(const uint64_t *d, uint32_t epoch, double &value) {
+        const uint64_t w = __hip_atomic_load(d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        value = __builtin_bit_cast(double, w << (64 - kTagShift));
+        return desc_state(w, epoch);
+    }
+};
+
+// The descriptor format of a scalar carry: fp32 data carried in fp64 packs
+// into one word; everything else is carried exactly.
+template <class T, class C>
+using DescFor = std::conditional_t<std::is_same_v<T, float> && std::is_same_v<C, double>, DescTrunc, Desc<C>>;
 
 // Workspace header.  Counters that many workgroups update at once sit in
 // separate 128-byte lines: same-address agent-scope atomics serialize at about
@@ -212,7 +264,7 @@ struct Desc {
 struct WsHeader {
     uint32_t epoch;       // tag of the running call's descriptors
     uint32_t error;       // kErr* bits (see flag_error)
-    uint64_t high_water;  // descriptor words written since the last full clear
+    uint64_t high_water;  // descriptor words the last call left tagged
     uint32_t mode;        // 0 undecided, kModeStatic or kModeDynamic (running call)
     uint32_t claim;       // next tile ticket in dynamic mode
     uint32_t pad0[26];
@@ -291,36 +343,26 @@ __device__ __forceinline__ uint32_t decide_mode(WsHeader *hdr, uint32_t G, uint3
 }
 
 // End of a call, run by one workgroup once every workgroup is known to have
-// read the epoch: reset the per-call words and advance the epoch for the next
-// call on this workspace.  When the 30-bit epoch wraps, descriptor words
-// beyond this call's (up to the high-water mark, within the workspace) that
-// older calls tagged could alias the new epoch, so they are cleared; words
-// below `words_used` were rewritten by this call with a different tag.
-// Whole workgroup; one barrier.
+// read the epoch: reset the per-call words, advance the epoch for the next
+// call on this workspace, and clear the descriptor words above this call's
+// up to the previous high-water mark (within the workspace): words below
+// `words_used` were all rewritten by this call, so afterwards every word
+// carries this call's tag or none.  Whole workgroup; one barrier.
 __device__ __forceinline__ void end_call(WsHeader *hdr, uint32_t epoch, uint64_t words_used, uint64_t ws_words,
                                          uint64_t *desc, uint64_t &s_clear_end) {
     if (threadIdx.x == 0) {
-        uint64_t clear_end = 0;
-        const uint32_t next = (epoch + 1u) & kEpochMask;
         const uint64_t hw = ld(&hdr->high_water);
-        if (next == 0u) {
-            clear_end = hw < ws_words ? hw : ws_words;
-            st(&hdr->high_water, words_used);
-        } else if (words_used > hw) {
-            st(&hdr->high_water, words_used);
-        }
+        st(&hdr->high_water, words_used);
 #pragma unroll
         for (int i = 0; i < 16; i++) st(&hdr->started[i].count, 0u);
         st(&hdr->claim, 0u);
         st(&hdr->mode, 0u);
-        st(&hdr->epoch, next);
-        s_clear_end = clear_end;
+        st(&hdr->epoch, (epoch + 1u) & kEpochMask);
+        s_clear_end = hw < ws_words ? hw : ws_words;
     }
     __syncthreads();
     const uint64_t clear_end = s_clear_end;
-    if (clear_end > words_used) {  // uniform over the workgroup; once per 2^30 calls
-        for (uint64_t i = words_used + threadIdx.x; i < clear_end; i += blockDim.x) st(desc + i, uint64_t(0));
-    }
+    for (uint64_t i = words_used + threadIdx.x; i < clear_end; i += blockDim.x) st(desc + i, uint64_t(0));
 }
 
 // Static mode's end: the workgroup that finished the last tile waits
@@ -362,7 +404,7 @@ __device__ __forceinline__ void end_call_static(WsHeader *hdr, uint32_t G, uint3
 // flags kErrSpin in the header and takes the unpublished slots as P with the
 // identity, so the kernel always finishes (with a wrong result that the
 // flag reports) instead of spinning forever on a tile that never runs.
-template <class Op, class C, int DEPTH>
+template <class Op, class C, int DEPTH, class D = Desc<C>>
 __device__ __forceinline__ C lookback(const uint64_t *desc, uint32_t epoch, int64_t tile, int64_t first,
                                       WsHeader *hdr, uint32_t spin_limit) {
     constexpr int kSpan = kWave * DEPTH;
@@ -379,7 +421,7 @@ __device__ __forceinline__ C lookback(const uint64_t *desc, uint32_t epoch, int6
             for (int k = 0; k < DEPTH; k++) {
                 const int64_t p = frontier - lane - int64_t(kWave) * k;
                 if (p >= first) {
-                    st[k] = Desc<C>::read(desc + p * Desc<C>::kWords, epoch, v[k]);
+                    st[k] = D::read(desc + p * D::kWords, epoch, v[k]);
                 } else {
                     st[k] = kStateP;
                     v[k] = id;
@@ -440,6 +482,37 @@ __device__ __forceinline__ Vec<T, V> load_vec(const T *p) {
     } else {
         static_assert(B == 4, "vector access of 4, 8 or 16 bytes");
         return __builtin_bit_cast(Vec<T, V>, __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(p)));
+    }
+}
+
+// Buffer resource over `count` elements at `base` (a wave-uniform pointer):
+// accesses at byte offsets past the range read 0 / are dropped by the
+// hardware, so a tile's ragged end needs no branch.  Word 3 is the gfx9
+// family's raw-buffer configuration (no swizzle, no format conversion).
+using BufRsrc = __amdgpu_buffer_rsrc_t;
+// The operands are moved to scalar registers explicitly: a resource the
+// compiler cannot prove uniform would be wrapped in a per-lane loop.
+template <class T>
+__device__ __forceinline__ BufRsrc make_rsrc(const T *base, int64_t count) {
+    T *b = reinterpret_cast<T *>(uniform(int64_t(reinterpret_cast<uintptr_t>(base))));
+    const uint32_t bytes = uniform(uint32_t(count * int64_t(sizeof(T))));
+    return __builtin_amdgcn_make_buffer_rsrc(b, 0, int(bytes), 0x00020000);
+}
+
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+
+// Nontemporal (streaming) store of one vector through a buffer resource.
+template <class T, int V>
+__device__ __forceinline__ void store_vec_bounded(BufRsrc rs, uint32_t byte_off, const Vec<T, V> &x) {
+    constexpr int B = int(sizeof(T)) * V;
+    constexpr int kNT = 2;  // cache policy: nontemporal
+    if constexpr (B == 16) {
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, x), rs, byte_off, 0, kNT);
+    } else if constexpr (B == 8) {
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, x), rs, byte_off, 0, kNT);
+    } else {
+        static_assert(B == 4, "vector access of 4, 8 or 16 bytes");
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x), rs, byte_off, 0, kNT);
     }
 }
 

@@ -71,9 +71,10 @@ struct ElemPolicy {
 
     // Component by component, so the registers in use do not grow with W.
     template <class TileT>
-    __device__ __forceinline__ static void publish_aggregate(const TileT &ts, uint64_t *d, uint32_t tag) {
+    __device__ __forceinline__ static void publish_aggregate(const TileT &ts, uint64_t *d, uint32_t epoch,
+                                                             uint32_t state) {
 #pragma unroll 1
-        for (int k = 0; k < W; k++) Desc<C1>::publish(d + k * kCW, tag, ts.aggp->c[k]);
+        for (int k = 0; k < W; k++) Desc<C1>::publish(d + k * kCW, epoch, state, ts.aggp->c[k]);
     }
 
     __device__ __forceinline__ static void set_identity(C *prefix) {
@@ -105,12 +106,14 @@ struct ElemPolicy {
         for (;;) {
             const int64_t p = frontier - lane;
             const uint64_t *dl = desc + p * kDescWords;
-            uint32_t tag = 0, st = kStateP;
+            uint64_t tag = 0;
+            uint32_t st = kStateP;
             int near_p = kWave, near_x = kWave;
             for (uint32_t polls = 0;; polls++) {
                 if (p >= first) {
-                    tag = uint32_t(ld(dl) >> 32);
-                    st = ((tag >> 2) == epoch) ? (tag & 3u) : 0u;
+                    const uint64_t w0 = ld(dl);
+                    tag = w0 >> kTagShift;
+                    st = desc_state(w0, epoch);
                 } else {
                     st = kStateP;
                 }
@@ -136,7 +139,7 @@ struct ElemPolicy {
 #pragma unroll
                     for (int i = 0; i < kCW; i++) {
                         const uint64_t word = ld(dl + k * kCW + i);
-                        bad = bad || uint32_t(word >> 32) != tag;
+                        bad = bad || (word >> kTagShift) != tag;
                         c.w[i] = uint32_t(word);
                     }
                     v = __builtin_bit_cast(C1, c);
@@ -160,7 +163,7 @@ struct ElemPolicy {
             uint64_t *d = const_cast<uint64_t *>(desc) + uint64_t(tile) * kDescWords;
 #pragma unroll 1
             for (int k = 0; k < W; k++)
-                Desc<C1>::publish(d + k * kCW, (epoch << 2) | kStateP, Op::apply(prefix->c[k], ts.aggp->c[k]));
+                Desc<C1>::publish(d + k * kCW, epoch, kStateP, Op::apply(prefix->c[k], ts.aggp->c[k]));
         }
     }
 

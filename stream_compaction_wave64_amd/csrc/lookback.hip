@@ -17,70 +17,98 @@
 namespace sw64 {
 
 template <class T_, class Op_, int BLOCK_, int ROWS, int VEC>
-struct ScanPolicy : ScalarCarry<Op_, typename Carry<T_, Op_>::type> {
+struct ScanPolicy {
     using T = T_;
     using Op = Op_;
     using C = typename Carry<T, Op>::type;
+    using D = DescFor<T, C>;
+    static constexpr int kDescWords = D::kWords;
     static constexpr int BLOCK = BLOCK_;
     using TS = TileScan<T, Op, BLOCK, ROWS, VEC>;
     using Args = ScanArgs;
     using Shared = typename TS::Shared;
 
+    __device__ __forceinline__ static C aggregate(const Shared &sh) { return TS::template aggregate_from<C>(sh); }
+
+    // A scanned tile waiting for its prefix: every thread's fold()ed rows.
+    struct Stash {
+        Vec<T, VEC> v[ROWS][BLOCK];
+    };
+
+    __device__ __forceinline__ static void geom(const Args &a, uint32_t tile, int64_t &start, int64_t &remaining,
+                                                uint32_t &seg, uint32_t &j) {
+        seg = tile / a.pipe.tiles_per_seg;
+        j = tile - seg * a.pipe.tiles_per_seg;
+        start = uniform(int64_t(seg) * a.seg_len + int64_t(j) * TS::TILE);
+        remaining = uniform(a.seg_len - int64_t(j) * TS::TILE);
+    }
+
+    // Store the stashed tile with its prefix.  An invalid call stores
+    // nothing (its buffer resource has no range) but issues the same
+    // instructions.
+    __device__ __forceinline__ static void emit(const Stash &st, const Args &a, uint32_t tile, C pre, bool valid) {
+        int64_t start, remaining;
+        uint32_t seg, j;
+        geom(a, tile, start, remaining, seg, j);
+        Vec<T, VEC> w[ROWS];
+#pragma unroll
+        for (int r = 0; r < ROWS; r++) w[r] = st.v[r][threadIdx.x];
+        TS::store_folded(w, reinterpret_cast<T *>(a.out) + (valid ? start : 0), valid ? remaining : 0, pre);
+    }
+
+    // The segment total after its last tile (count-scan-emit's offsets[n]).
+    __device__ __forceinline__ static void on_resolved(const Args &a, uint32_t tile, C pre, C agg) {
+        int64_t start, remaining;
+        uint32_t seg, j;
+        geom(a, tile, start, remaining, seg, j);
+        if (a.total_out != nullptr && j == a.pipe.tiles_per_seg - 1)
+            reinterpret_cast<T *>(a.total_out)[seg] = T(Op::apply(pre, agg));
+    }
+
     struct Tile {
         TS ts;
 
-        __device__ __forceinline__ void set_slot(int) {}
-
-        __device__ __forceinline__ static void geom(const Args &a, uint32_t tile, int64_t &start, int64_t &remaining,
-                                                    uint32_t &seg, uint32_t &j) {
-            seg = tile / a.pipe.tiles_per_seg;
-            j = tile - seg * a.pipe.tiles_per_seg;
-            start = int64_t(seg) * a.seg_len + int64_t(j) * TS::TILE;
-            remaining = a.seg_len - int64_t(j) * TS::TILE;
-        }
-
+        // A tile past the end (the pipeline's prefetch beyond the last tile)
+        // loads the array's first vector in every row and is never scanned.
         __device__ __forceinline__ void load(const Args &a, uint32_t tile) {
             int64_t start, remaining;
             uint32_t seg, j;
             geom(a, tile, start, remaining, seg, j);
-            ts.load(reinterpret_cast<const T *>(a.in) + start, remaining);
+            const bool valid = tile < a.pipe.num_tiles;
+            ts.load(reinterpret_cast<const T *>(a.in) + (valid ? start : 0), valid ? remaining : 0);
         }
 
         __device__ __forceinline__ void scan(Shared &sh) { ts.scan(sh); }
 
-        __device__ __forceinline__ C aggregate() const { return C(ts.agg); }
-
-        __device__ __forceinline__ void emit(const Args &a, uint32_t tile, const C *prefix) const {
-            int64_t start, remaining;
-            uint32_t seg, j;
-            geom(a, tile, start, remaining, seg, j);
-            const C pre = *prefix;
-            ts.store(reinterpret_cast<T *>(a.out) + start, remaining, pre, a.exclusive != 0);
-            if (a.total_out != nullptr && threadIdx.x == 0 && j == a.pipe.tiles_per_seg - 1)
-                reinterpret_cast<T *>(a.total_out)[seg] = T(Op::apply(pre, C(ts.agg)));
+        __device__ __forceinline__ void stash(Stash &st, const Args &a) {
+            ts.fold(a.exclusive != 0);
+#pragma unroll
+            for (int r = 0; r < ROWS; r++) st.v[r][threadIdx.x] = ts.v[r];
         }
     };
 };
 
 template <class P>
-__global__ __launch_bounds__(P::BLOCK) void k_lookback(typename P::Args a) {
-    Pipeline<P>::run(a);
+__global__ __launch_bounds__(CtrlPipeline<P>::THREADS) void k_lookback(typename P::Args a) {
+    CtrlPipeline<P>::run(a);
 }
 
+// B threads per workgroup: B - 64 data threads and the control wave.
 template <class T, class Op, int B, int R, int V>
 static int launch_lookback_impl(const ScanArgs &a, uint32_t grid_cap, hipStream_t s) {
-    using P = ScanPolicy<T, Op, B, R, V>;
+    using P = ScanPolicy<T, Op, B - kWave, R, V>;
+    static_assert(CtrlPipeline<P>::THREADS == B, "launch size");
     const int g = pipeline_grid(reinterpret_cast<const void *>(&k_lookback<P>), B, a.pipe.num_tiles, grid_cap);
     if (g <= 0) return SCAN_ERR_HIP;
     hipLaunchKernelGGL((k_lookback<P>), dim3(g), dim3(B), 0, s, a);
     return hipGetLastError() == hipSuccess ? SCAN_OK : SCAN_ERR_HIP;
 }
 
-// Instantiated (block, rows) shapes.  Every type gets the default shape
-// (512 threads x 8 rows of 128-bit vectors, 64 KiB per tile, the best
-// measured on MI355X; 4 rows for 8-byte elements) and a one-row shape
-// (small tiles, used to force many tiles at small n); fp32 sum also gets the
-// shapes the tuning sweep visits.
+// Instantiated (block, rows) shapes, block counting the control wave.
+// Every type gets the default shape (512 threads = 448 data threads x 8 rows
+// of 128-bit vectors, 56 KiB per tile; 4 rows for 8-byte elements) and a
+// one-row shape (small tiles, used to force many tiles at small n); fp32 sum
+// also gets the shapes the tuning sweep visits.
 template <class T, class Op, int V>
 static LbLaunch pick_shape(int block, int rows) {
 #define SW64_SHAPE(B, R) \

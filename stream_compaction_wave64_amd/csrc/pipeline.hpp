@@ -1,8 +1,6 @@
-// pipeline.hpp -- the persistent, software-pipelined single-pass look-back
-// driver shared by every look-back kernel (plain scans, compaction, element
-// scans).  A tile policy P says how one tile is loaded, scanned and emitted;
-// the driver owns tile ordering, descriptors, the look-back and the
-// workspace protocol.
+// pipeline.hpp -- the persistent single-pass look-back drivers.  A tile
+// policy P says how one tile is loaded, scanned and emitted; the driver owns
+// tile ordering, descriptors, the look-back and the workspace protocol.
 //
 // Method: The CUDA Handbook ch. 13, decoupled look-back section (Figure
 // 13-11): each tile publishes its aggregate (A), looks back over its
@@ -16,12 +14,15 @@
 //    at ~11.5 ns each on MI355X (12k of them exceed the HBM time of a
 //    1e8-element scan).  Residency is verified at run time (decide_mode);
 //    without it the call claims tiles in order from a counter instead.
-//  * Software pipeline: three register tiles per workgroup.  While tile t
-//    waits for its look-back, tile t + G is already scanned with its
-//    aggregate published and the loads of t + 2G are in flight, so one slow
-//    look-back does not hold back the next round's aggregates.
+//  * CtrlPipeline (scalar carries: scans and compaction): a control wave
+//    owns the descriptors and the look-back, and scanned tiles wait in LDS
+//    for their prefix (see its comment).
+//  * Pipeline (the element kernel): three register tiles per workgroup;
+//    while tile t waits for its look-back (wave 0), tile t + G is already
+//    scanned with its aggregate published and the loads of t + 2G are in
+//    flight.
 //
-// Policy interface (all __device__):
+// Pipeline's policy interface (all __device__):
 //   using T, C (carry type), Op;   static constexpr int BLOCK, kDescWords
 //   struct Args { PipeArgs pipe; ... }
 //   struct Shared;                 LDS the tile scan needs
@@ -32,7 +33,7 @@
 //     C aggregate() const;
 //     void emit(const Args&, uint32_t tile, const C* prefix);  prefix in LDS
 //   };
-//   static void publish_aggregate(Tile&, uint64_t* desc, uint32_t tag);  thread 0
+//   static void publish_aggregate(Tile&, uint64_t* desc, uint32_t epoch, uint32_t state);  thread 0
 //   static void resolve(Tile&, ...);   wave 0: look back, publish P, write the
 //                                      exclusive prefix to LDS
 //   static void set_identity(C* prefix);   lane 0
@@ -76,7 +77,7 @@ struct Pipeline {
         ts.scan(sm.ps);
         if (a.pipe.tiles_per_seg > 1 && threadIdx.x == 0) {
             const uint32_t state = (tile % a.pipe.tiles_per_seg == 0) ? kStateP : kStateA;
-            P::publish_aggregate(ts, desc_of(desc, tile), (epoch << 2) | state);
+            P::publish_aggregate(ts, desc_of(desc, tile), epoch, state);
         }
     }
 
@@ -172,32 +173,225 @@ struct Pipeline {
     }
 };
 
-// Descriptor I/O and look-back for a policy whose carry is one value of type
-// C (scalar scans and compaction); its Tile provides aggregate().
-template <class Op, class C>
-struct ScalarCarry {
-    static constexpr int kDescWords = Desc<C>::kWords;
+// The pipeline with a control wave and deferred emission, for policies whose
+// carry is one value of type C.
+//
+// The workgroup is P::BLOCK data threads plus one extra wave that owns every
+// descriptor access.  While HBM is saturated a descriptor round trip takes
+// about 2 us (the request waits in the same queues as the tile traffic), so
+// the look-back must not sit on the tile's critical path, and it must not
+// need several round trips.  Hence:
+//  * A scanned tile waits two steps in LDS before it is emitted (gfx950 has
+//    160 KB of LDS per workgroup; each data thread stashes and later reads
+//    back only its own slots, so no barrier guards the reuse).  By then the
+//    aggregates of the whole round have long been published, and the
+//    control wave's look-back for it completes in one round trip while the
+//    data waves stream the next tiles.
+//  * Descriptor reads are what the look-back costs: each poll reads one
+//    window of 64 predecessors (measured: four windows per round trip cost
+//    more HBM time than the extra round trips they save), and fp32 carries
+//    pack into one word per tile (DescTrunc).
+//  * On gfx950 a wave's vector memory counter retires loads and stores in
+//    issue order: the control wave holds no tile traffic, so its polls are
+//    never counted behind a tile.
+//
+// Tiles of workgroup w are T(k) = w + kG.  Step s (s = 0 .. K+1, K tiles):
+//   data waves:    issue T(s+1)'s loads (the other register tile); scan T(s)
+//                  (barrier 1); barrier 2; emit T(s-2) from its LDS stash
+//                  with the prefix the control wave left; stash T(s).
+//   control wave:  look back for T(s-2), publish its inclusive prefix, leave
+//                  the exclusive prefix in LDS; barrier 1; combine T(s)'s
+//                  per-wave totals into its aggregate and publish it (A, or
+//                  P at a segment start); barrier 2.
+// Every load a data wave issues is unconditional (a tile past the end loads
+// the array's first vector and discards it), and so is every store of the
+// scan policies (dropped past the end by the buffer resource), so the
+// compiler counts the accesses in flight exactly and waits only for the
+// tile it scans.
+//
+// Policy interface:
+//   using T, C, Op, Args, Shared, Stash;  static constexpr int BLOCK, kDescWords
+//   static C aggregate(const Shared&)     control wave, between the scan's
+//                                         barrier and the next
+//   static void emit(const Stash&, const Args&, uint32_t tile, C pre, bool valid)
+//                                         data threads; !valid: no effect
+//   static void on_resolved(const Args&, uint32_t tile, C pre, C agg)
+//                                         control lane 0, after the prefix
+//   struct Tile {
+//     void load(const Args&, uint32_t tile);   tile >= num_tiles: dummy loads
+//     void scan(Shared&);                      exactly one __syncthreads()
+//     void stash(Stash&, const Args&) const;   own slots only
+//   };
+template <class P>
+struct CtrlPipeline {
+    using Tile = typename P::Tile;
+    using C = typename P::C;
+    using Op = typename P::Op;
+    using Args = typename P::Args;
+    static constexpr int DATA = P::BLOCK;
+    static constexpr int THREADS = DATA + kWave;
+    static constexpr int kDepth = 1;  // look-back windows of 64 per round trip
+    static_assert(DATA % kWave == 0 && THREADS <= 1024, "whole waves");
 
-    template <class Tile>
-    __device__ __forceinline__ static void publish_aggregate(const Tile &ts, uint64_t *d, uint32_t tag) {
-        Desc<C>::publish(d, tag, ts.aggregate());
+    struct Smem {
+        typename P::Stash stash[2];  // scanned tiles waiting for their prefix
+        typename P::Shared ps;
+        C prefix[2];  // exclusive prefix of the tile emitted in this step
+        uint32_t epoch, mode, ticket;
+        uint64_t clear_end;
+    };
+
+    __device__ __forceinline__ static uint64_t *desc_of(uint64_t *desc, uint32_t tile) {
+        return desc + uint64_t(tile) * P::kDescWords;
     }
 
-    template <class Tile>
-    __device__ __forceinline__ static void resolve(const Tile &ts, const uint64_t *desc, uint32_t epoch,
-                                                   uint32_t tile, int64_t first, WsHeader *hdr, uint32_t spin_limit,
-                                                   C *prefix) {
-        const C agg = ts.aggregate();
-        const C pre = sw64::lookback<Op, C, 1>(desc, epoch, tile, first, hdr, spin_limit);
+    // Control wave, between the barrier of the data waves' scan of `tile`
+    // and the next barrier: the tile's aggregate, published.
+    __device__ __forceinline__ static C ctrl_publish(const Args &a, uint32_t tile, const Smem &sm, uint64_t *desc,
+                                                     uint32_t epoch) {
+        const C agg = P::aggregate(sm.ps);
+        if (a.pipe.tiles_per_seg > 1 && lane_id() == 0) {
+            const uint32_t state = (tile % a.pipe.tiles_per_seg == 0) ? kStateP : kStateA;
+            P::D::publish(desc_of(desc, tile), epoch, state, agg);
+        }
+        return agg;
+    }
+
+    // Control wave: the exclusive prefix of `tile` into `*prefix`.
+    __device__ __forceinline__ static void ctrl_resolve(const Args &a, uint32_t tile, C agg, C *prefix, WsHeader *hdr,
+                                                        uint64_t *desc, uint32_t epoch) {
+        const uint32_t j = tile % a.pipe.tiles_per_seg;
+        C pre = Op::template identity<C>();
+        if (a.pipe.tiles_per_seg > 1 && j != 0) {
+            pre = sw64::lookback<Op, C, kDepth, typename P::D>(desc, epoch, tile, int64_t(tile - j), hdr,
+                                                               a.pipe.spin_limit);
+            if (lane_id() == 0) P::D::publish(desc_of(desc, tile), epoch, kStateP, Op::apply(pre, agg));
+        }
         if (lane_id() == 0) {
-            Desc<C>::publish(const_cast<uint64_t *>(desc) + uint64_t(tile) * kDescWords, (epoch << 2) | kStateP,
-                             Op::apply(pre, agg));
             *prefix = pre;
+            P::on_resolved(a, tile, pre, agg);
         }
     }
 
-    __device__ __forceinline__ static void set_identity(C *prefix) {
-        if (lane_id() == 0) *prefix = Op::template identity<C>();
+    // One static-mode step of the data waves: `cur` holds T(s), `other`
+    // receives T(s+1).  Returns false after the last step.
+    __device__ __forceinline__ static bool data_step(Tile &cur, Tile &other, const Args &a, uint32_t s, uint32_t K,
+                                                     Smem &sm) {
+        const uint32_t w = blockIdx.x, G = gridDim.x;
+        other.load(a, s + 1 < K ? w + (s + 1) * G : a.pipe.num_tiles);
+        if (s < K)
+            cur.scan(sm.ps);
+        else
+            __syncthreads();
+        __syncthreads();
+        const bool emit = s >= 2;
+        P::emit(sm.stash[s & 1], a, emit ? w + (s - 2) * G : a.pipe.num_tiles, sm.prefix[s & 1], emit);
+        if (s < K) cur.stash(sm.stash[s & 1], a);
+        return s + 1 < K + 2;
+    }
+
+    // The kernel body.  The host launches THREADS threads per workgroup, at
+    // most as many workgroups as can be resident and no more than there are
+    // tiles.  The two roles run separate loops with the same sequence of
+    // barriers (two per step), so the control wave keeps no tile registers
+    // live.
+    __device__ __forceinline__ static void run(const Args &a) {
+        __shared__ Smem sm;
+        WsHeader *hdr = reinterpret_cast<WsHeader *>(a.pipe.ws);
+        uint64_t *desc = reinterpret_cast<uint64_t *>(reinterpret_cast<char *>(a.pipe.ws) + kWsHeaderBytes);
+        const uint32_t n = a.pipe.num_tiles, G = gridDim.x, w = blockIdx.x;
+        const uint32_t K = (n - w + G - 1) / G;  // tiles of this workgroup (>= 1)
+        const bool chained = a.pipe.tiles_per_seg > 1;
+        // Wave-uniform role (a scalar branch: no wave ever runs both sides).
+        const bool ctrl = uniform(uint32_t(threadIdx.x)) >= uint32_t(DATA);
+
+        if (ctrl) {
+            if (chained && lane_id() == 0) {
+                sm.epoch = begin_call(hdr);
+                sm.mode = decide_mode(hdr, G, a.pipe.mode_limit);
+            }
+            __syncthreads();
+            const uint32_t epoch = chained ? sm.epoch : 0u;
+            const uint32_t mode = chained ? sm.mode : kModeStatic;
+            if (mode == kModeStatic) {
+                C agg0 = Op::template identity<C>(), agg1 = agg0;  // aggregates of T(s-2), T(s-1)
+                for (uint32_t s = 0; s < K + 2; s++) {
+                    if (s >= 2) ctrl_resolve(a, w + (s - 2) * G, agg0, &sm.prefix[s & 1], hdr, desc, epoch);
+                    __syncthreads();
+                    agg0 = agg1;
+                    if (s < K) agg1 = ctrl_publish(a, w + s * G, sm, desc, epoch);
+                    __syncthreads();
+                }
+                end_static(a, sm, hdr, desc, epoch);
+            } else {
+                ctrl_dynamic(a, sm, hdr, desc, epoch);
+            }
+            return;
+        }
+
+        Tile b0, b1;
+        b0.load(a, w);
+        __syncthreads();
+        const uint32_t epoch = chained ? sm.epoch : 0u;
+        const uint32_t mode = chained ? sm.mode : kModeStatic;
+        if (mode == kModeStatic) {
+            for (uint32_t s = 0;; s += 2) {
+                if (!data_step(b0, b1, a, s, K, sm)) break;
+                if (!data_step(b1, b0, a, s + 1, K, sm)) break;
+            }
+            end_static(a, sm, hdr, desc, epoch);
+            return;
+        }
+
+        // Dynamic mode (data waves): one tile at a time, in claim order.
+        for (;;) {
+            __syncthreads();
+            const uint32_t tk = sm.ticket;
+            if (tk >= n) {
+                if (tk == n + G - 1) end_call(hdr, epoch, a.pipe.words_used, a.pipe.ws_words, desc, sm.clear_end);
+                break;
+            }
+            b0.load(a, tk);
+            b0.scan(sm.ps);
+            b0.stash(sm.stash[0], a);
+            __syncthreads();
+            __syncthreads();
+            P::emit(sm.stash[0], a, tk, sm.prefix[0], true);
+        }
+    }
+
+    // End of a static call: the workgroup that owns the last tile resets the
+    // workspace header (whole workgroup, both roles).
+    __device__ __forceinline__ static void end_static(const Args &a, Smem &sm, WsHeader *hdr, uint64_t *desc,
+                                                      uint32_t epoch) {
+        const uint32_t n = a.pipe.num_tiles, G = gridDim.x;
+        if (a.pipe.tiles_per_seg > 1 && blockIdx.x == (n - 1) % G)
+            end_call_static(hdr, G, epoch, a.pipe.words_used, a.pipe.ws_words, desc, a.pipe.spin_limit,
+                            sm.clear_end);
+    }
+
+    // Dynamic mode (control wave): claim a tile, then resolve it.  Every
+    // workgroup makes exactly one claim past the last tile, so the holder of
+    // ticket n + G - 1 knows all others are done with the header.  Barriers
+    // per tile match the data waves': claim; scan; aggregate; prefix.
+    __device__ __forceinline__ static void ctrl_dynamic(const Args &a, Smem &sm, WsHeader *hdr, uint64_t *desc,
+                                                        uint32_t epoch) {
+        const uint32_t n = a.pipe.num_tiles, G = gridDim.x;
+        for (;;) {
+            if (lane_id() == 0)
+                sm.ticket = __hip_atomic_fetch_add(&hdr->claim, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __syncthreads();
+            const uint32_t tk = sm.ticket;
+            if (tk >= n) {
+                if (tk == n + G - 1) end_call(hdr, epoch, a.pipe.words_used, a.pipe.ws_words, desc, sm.clear_end);
+                break;
+            }
+            __syncthreads();
+            const C agg = ctrl_publish(a, tk, sm, desc, epoch);
+            __syncthreads();
+            ctrl_resolve(a, tk, agg, &sm.prefix[0], hdr, desc, epoch);
+            __syncthreads();
+        }
     }
 };
 

@@ -37,29 +37,44 @@ struct TileScan {
     Vec<T, VEC> v[ROWS];  // loaded values, then their in-vector inclusive scan
     T off[ROWS];          // exclusive offset of this thread's vector in each row
     T agg;                // tile aggregate
+    int64_t rem;          // elements of the tile in range (>= TILE: all)
 
     __device__ __forceinline__ static int64_t elem(int r) {
         return (int64_t(r) * BLOCK + threadIdx.x) * VEC;
     }
 
-    // Load the tile; vectors at or past `remaining` hold the identity.  The
-    // caller guarantees remaining is a multiple of VEC.
+    // Issue the tile's loads.  No loaded value is read here: the registers
+    // are first touched by scan() or reduce(), so a pipelined caller keeps
+    // the loads in flight while it works on other tiles (a select applied at
+    // load time would make the compiler wait for the data right away).
+    // Out-of-range rows re-read the tile's first vector (always in range), so
+    // every load is unconditional.  The caller guarantees `remaining` is a
+    // multiple of VEC.
     __device__ __forceinline__ void load(const T *src, int64_t remaining) {
-        // Out-of-range rows re-read the tile's first vector (always in range)
-        // so every load is unconditional and all of them are in flight at once.
-        const T id = Op::template identity<T>();
+        rem = remaining;
 #pragma unroll
         for (int r = 0; r < ROWS; r++) {
             const int64_t e = elem(r);
-            const bool in = e < remaining;
-            const Vec<T, VEC> x = load_vec<T, VEC>(src + (in ? e : 0));
+            v[r] = load_vec<T, VEC>(src + (e < remaining ? e : 0));
+        }
+    }
+
+    // Identity in every vector at or past the end (only the last tile of a
+    // segment has any).
+    __device__ __forceinline__ void mask_tail() {
+        if (rem >= TILE) return;
+        const T id = Op::template identity<T>();
 #pragma unroll
-            for (int c = 0; c < VEC; c++) v[r].v[c] = in ? x.v[c] : id;
+        for (int r = 0; r < ROWS; r++) {
+            const bool in = elem(r) < rem;
+#pragma unroll
+            for (int c = 0; c < VEC; c++) v[r].v[c] = in ? v[r].v[c] : id;
         }
     }
 
     // Levels 1-3 above.  Contains one __syncthreads().
     __device__ __forceinline__ void scan(Shared &sh) {
+        mask_tail();
         const T id = Op::template identity<T>();
         const int lane = lane_id();
         const int wave = threadIdx.x / kWave;
@@ -98,10 +113,21 @@ struct TileScan {
         agg = run;
     }
 
+    // The tile aggregate from the per-wave totals scan() left in LDS, in the
+    // carry type, computed by any one whole wave after scan()'s barrier (the
+    // same value in every lane).  Operators are commutative.
+    template <class C2>
+    __device__ __forceinline__ static C2 aggregate_from(const Shared &sh) {
+        C2 acc = Op::template identity<C2>();
+        for (int i = lane_id(); i < ROWS * W; i += kWave) acc = Op::apply(acc, C2(sh.tot[i / W][i % W]));
+        return wave_reduce<Op>(acc);
+    }
+
     // Tile aggregate only (the reduce pass of reduce-then-scan): per-thread
     // reduction of all its elements, wave reduction, one LDS slot per wave.
     // Contains one __syncthreads(); the caller separates reuses of `sh`.
     __device__ __forceinline__ void reduce(Shared &sh) {
+        mask_tail();
         const T id = Op::template identity<T>();
         T acc = id;
 #pragma unroll
@@ -118,8 +144,41 @@ struct TileScan {
         agg = run;
     }
 
+    // After scan(): replace every value by its tile-local result (inclusive,
+    // or exclusive with the identity before the tile's first element), i.e.
+    // the output less the tile's prefix.
+    __device__ __forceinline__ void fold(bool exclusive) {
+#pragma unroll
+        for (int r = 0; r < ROWS; r++) {
+            T prev = off[r];
+#pragma unroll
+            for (int c = 0; c < VEC; c++) {
+                const T inc = Op::apply(off[r], v[r].v[c]);
+                v[r].v[c] = exclusive ? prev : inc;
+                prev = inc;
+            }
+        }
+    }
+
+    // Store fold()ed values with the tile's prefix `pre` applied (in the
+    // carry type, rounded once).  Rows at or past `remaining` are dropped.
+    __device__ __forceinline__ static void store_folded(const Vec<T, VEC> (&w)[ROWS], T *dst, int64_t remaining,
+                                                        C pre) {
+        const BufRsrc rs = make_rsrc(dst, remaining < TILE ? (remaining > 0 ? remaining : 0) : TILE);
+#pragma unroll
+        for (int r = 0; r < ROWS; r++) {
+            Vec<T, VEC> o;
+#pragma unroll
+            for (int c = 0; c < VEC; c++) o.v[c] = T(Op::apply(pre, C(w[r].v[c])));
+            store_vec_bounded<T, VEC>(rs, uint32_t(elem(r) * int64_t(sizeof(T))), o);
+        }
+    }
+
     // Add the tile's exclusive prefix `pre` and store; inclusive or exclusive.
+    // Every store is issued (no branch): rows at or past `remaining` fall
+    // outside the buffer resource's range and the hardware drops them.
     __device__ __forceinline__ void store(T *dst, int64_t remaining, C pre, bool exclusive) const {
+        const BufRsrc rs = make_rsrc(dst, remaining < TILE ? (remaining > 0 ? remaining : 0) : TILE);
 #pragma unroll
         for (int r = 0; r < ROWS; r++) {
             const T base = T(Op::apply(pre, C(off[r])));
@@ -131,8 +190,7 @@ struct TileScan {
                 o.v[c] = Op::apply(base, exclusive ? prev : cur);
                 prev = cur;
             }
-            const int64_t e = elem(r);
-            if (e < remaining) store_vec<T, VEC>(dst + e, o);
+            store_vec_bounded<T, VEC>(rs, uint32_t(elem(r) * int64_t(sizeof(T))), o);
         }
     }
 };

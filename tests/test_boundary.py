@@ -65,11 +65,12 @@ def test_plan_fp32_metric_shape():
     import torch
     p = binding.plan("scan", torch.float32, "sum", 1, 10 ** 8)
     assert p["kernel"] == "lookback" and p["vec"] == 4
-    assert p["tile_elems"] == p["block_size"] * p["items_per_thread"]
+    # the look-back kernels give one wave of each workgroup to the look-back
+    assert p["tile_elems"] == (p["block_size"] - 64) * p["items_per_thread"]
     assert p["num_tiles"] == -(-10 ** 8 // p["tile_elems"])
-    assert p["carry_words"] == 2  # fp32 sums carry in fp64 between tiles
+    assert p["carry_words"] == 1  # fp32 sums carry in fp64 between tiles, packed into one word
     assert p["launches"] == 1
-    assert p["workspace_bytes"] >= 256 + p["num_tiles"] * 16
+    assert p["workspace_bytes"] >= 4096 + p["num_tiles"] * 8 * p["carry_words"]
 
 
 def test_plan_segments_and_types():
@@ -83,7 +84,10 @@ def test_plan_segments_and_types():
     p = binding.plan("scan", torch.float32, "max", 1, 1000)
     assert p["carry_words"] == 1
     p = binding.plan("scan", torch.float32, "sum", 1, 1000, tuning={"block_size": 256, "items_per_thread": 4})
-    assert p["tile_elems"] == 1024
+    assert p["tile_elems"] == 192 * 4
+    p = binding.plan("scan", torch.float32, "sum", 1, 1000, tuning={"block_size": 256, "items_per_thread": 4,
+                                                                     "algo": "reduce_then_scan"})
+    assert p["tile_elems"] == 256 * 4
     with pytest.raises(binding.ScanError):
         binding.plan("scan", torch.float32, "sum", 1, 1000, tuning={"block_size": 192, "items_per_thread": 4})
 

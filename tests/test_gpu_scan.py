@@ -56,7 +56,8 @@ def test_parity_default_tiles(dt, op, exclusive):
 @pytest.mark.parametrize("dt", DTYPES, ids=lambda d: np.dtype(d).name)
 @pytest.mark.parametrize("op", OPS)
 def test_parity_many_small_tiles(dt, op):
-    # one row per tile: tile = 256 x vec elements, so 1e5 elements make
+    # one row per tile: tile = 192 x vec elements (256 threads less the
+    # look-back wave), so 1e5 elements make
     # hundreds of tiles and the look-back walks windows of 64
     vec = 16 // np.dtype(dt).itemsize
     tuning = {"block_size": 256, "items_per_thread": vec}
@@ -168,12 +169,12 @@ def test_repeated_calls_reuse_workspace():
         assert_scan_matches(f, to_host(b), "sum", True, what=f"k={k}")
 
 
-def test_epoch_wrap_clears_stale_descriptors():
-    # A large call at epoch 2 leaves descriptors tagged 2.  The header is then
-    # moved to just below the 30-bit wrap; small calls cross the wrap (the
-    # wrapping call must clear the words beyond its own up to the high-water
-    # mark) and reach epoch 2 again, where a large call on different data
-    # would otherwise accept the stale tag-2 descriptors as published.
+def test_shrinking_call_clears_stale_descriptors():
+    # Descriptor tags carry the epoch mod 256.  A large call at epoch 2 leaves
+    # its words tagged 2.  A small call at epoch 257 must clear the words above
+    # its own up to the high-water mark: the next call runs at epoch 258,
+    # which is 2 mod 256, and a large call there would otherwise accept the
+    # stale tag-2 words as published.
     from stream_compaction_wave64_amd import binding
     ws = torch.zeros(1 << 22, dtype=torch.uint8, device=DEV)
     hdr = ws[:16].view(torch.int32)  # [0] epoch, [1] error, [2:4] high-water mark
@@ -183,6 +184,7 @@ def test_epoch_wrap_clears_stale_descriptors():
     small = inputs.generic(np.int32, 50_000, 14, "wide")
     tiles_big = -(-big1.size // sw.plan("scan", torch.int32, "sum", 1, big1.size)["tile_elems"])
     tiles_small = -(-small.size // sw.plan("scan", torch.int32, "sum", 1, small.size)["tile_elems"])
+    assert tiles_small > 1 and tiles_big > 2 * tiles_small
     key = (torch.device(DEV).index, binding._stream(torch.device(DEV)))
     saved = binding.workspaces._ws.get(key)
     binding.workspaces._ws[key] = ws
@@ -192,20 +194,17 @@ def test_epoch_wrap_clears_stale_descriptors():
         torch.cuda.synchronize()
         assert_scan_matches(big1, to_host(r), "sum", False, what="big at epoch 2")
         assert int(hdr[0].item()) == 3 and int(hdr[2].item()) == tiles_big
-        hdr[0] = (1 << 30) - 2
-        sd = to_dev(small)
-        for k in range(4):
-            r = sw.scan_inclusive(sd)
-            torch.cuda.synchronize()
-            assert_scan_matches(small, to_host(r), "sum", False, what=f"small call {k}")
-            if k == 1:  # this call wrapped the epoch to 0
-                assert int(hdr[0].item()) == 0
-                assert not words[tiles_small:tiles_big].any().item()
-        assert int(hdr[0].item()) == 2
-        assert int(hdr[1].item()) == 0  # no error and no fallback along the way
+        assert words[tiles_small:tiles_big].ne(0).all().item()  # tagged words left behind
+        hdr[0] = 257
+        r = sw.scan_inclusive(to_dev(small))
+        torch.cuda.synchronize()
+        assert_scan_matches(small, to_host(r), "sum", False, what="small at epoch 257")
+        assert int(hdr[0].item()) == 258 and int(hdr[2].item()) == tiles_small
+        assert not words[tiles_small:tiles_big].any().item()
         r = sw.scan_inclusive(to_dev(big2))
         torch.cuda.synchronize()
-        assert_scan_matches(big2, to_host(r), "sum", False, what="big at epoch 2 after the wrap")
+        assert_scan_matches(big2, to_host(r), "sum", False, what="big at epoch 258")
+        assert int(hdr[1].item()) == 0  # no error and no fallback along the way
     finally:
         if saved is None:
             binding.workspaces._ws.pop(key, None)
