@@ -79,7 +79,7 @@ namespace {
 constexpr size_t kHeader = kWsHeaderBytes;  // workspace header bytes (WsHeader)
 constexpr uint32_t kDefaultSpinLimit = 1u << 22;
 constexpr uint32_t kDefaultModeLimit = 512;
-constexpr int kDefaultBlock = 512, kDefaultRows = 8;  // look-back tile shape
+constexpr int kDefaultBlock = 512;  // threads per workgroup of the tiled kernels
 constexpr int kDefaultRtsBlocks = 1024;               // C of reduce-then-scan
 constexpr int64_t kDefaultLocalMem = 64 * 1024;       // LDS budget of the large-element rule
 constexpr int kElemDefaultBlock = 256;                // large elements: start of the rule
@@ -146,9 +146,9 @@ struct TilePlan {
 // a tuned shape snaps to the nearer.  Kernels with a control wave (`ctrl`)
 // give the tile block - 64 threads.
 template <class Find>
-int plan_shape(int esize, bool vec_ok, const scan_tuning_t &tu, TilePlan &p, Find find, bool ctrl = false) {
+int plan_shape(int esize, bool vec_ok, const scan_tuning_t &tu, TilePlan &p, Find find, bool ctrl,
+               int rows_default) {
     const int vmax = 16 / esize;
-    const int rows_default = esize == 8 ? kDefaultRows / 2 : kDefaultRows;
     p.vec = vec_ok ? vmax : 1;
     p.block = tu.block_size > 0 ? tu.block_size : kDefaultBlock;
     int ipt = tu.items_per_thread > 0 ? tu.items_per_thread : rows_default * vmax;
@@ -170,12 +170,29 @@ int plan_scan(scan_dtype_t dt, scan_op_t op, int64_t outer, int64_t len, bool al
     const bool rts = tu.algo == SCAN_ALGO_REDUCE_THEN_SCAN;
     if (rts && outer != 1) return SCAN_ERR_UNSUPPORTED;  // reduce-then-scan: whole arrays only
     const bool vec_ok = aligned && len % (16 / esize) == 0;
-    int rc = rts ? plan_shape(esize, vec_ok, tu, p,
-                              [&](int b, int r, int v) { return find_rts(dt, op, b, r, v) != nullptr; })
+    // default rows: reduce-then-scan 8 (4 for 8-byte elements); look-back 10
+    // (8), its tiles bounded by the two LDS stashes of the pipeline
+    int rc = rts ? plan_shape(
+                       esize, vec_ok, tu, p,
+                       [&](int b, int r, int v) { return find_rts(dt, op, b, r, v) != nullptr; }, false,
+                       esize == 8 ? 4 : 8)
                  : plan_shape(
                        esize, vec_ok, tu, p,
-                       [&](int b, int r, int v) { return find_lookback(dt, op, b, r, v) != nullptr; }, true);
+                       [&](int b, int r, int v) { return find_lookback(dt, op, b, r, v) != nullptr; }, true,
+                       esize == 8 ? 8 : 10);
     if (rc != SCAN_OK) return rc;
+    if (!rts && tu.block_size <= 0 && tu.items_per_thread <= 0 && len < p.tile) {
+        // Short segments: the fewest rows whose tile holds a whole segment, so
+        // each segment is one tile (no look-back) with little of it idle.
+        for (int r : {1, 2, 3, 5}) {
+            const int64_t t = int64_t(p.block - 64) * r * p.vec;
+            if (r < p.rows && t >= len && find_lookback(dt, op, p.block, r, p.vec) != nullptr) {
+                p.rows = r;
+                p.tile = t;
+                break;
+            }
+        }
+    }
     p.tiles_per_seg = (len + p.tile - 1) / p.tile;
     p.num_tiles = outer * p.tiles_per_seg;
     if (p.num_tiles > int64_t(INT32_MAX)) return SCAN_ERR_OVERFLOW;  // grid x limit
@@ -261,7 +278,7 @@ int plan_compact(scan_dtype_t dt, int64_t n, bool aligned, const scan_tuning_t &
     // 128-bit loads need 16-byte aligned x and whole vectors up to n
     const int rc = plan_shape(
         4, aligned && n % 4 == 0, tu, p,
-        [&](int b, int r, int v) { return find_compact(dt, SCAN_CMP_GT, b, r, v) != nullptr; }, true);
+        [&](int b, int r, int v) { return find_compact(dt, SCAN_CMP_GT, b, r, v) != nullptr; }, true, 8);
     if (rc != SCAN_OK) return rc;
     p.kernel = SCAN_KERNEL_COMPACT;
     p.tiles_per_seg = p.num_tiles = (n + p.tile - 1) / p.tile;

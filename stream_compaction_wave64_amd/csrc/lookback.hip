@@ -105,26 +105,33 @@ static int launch_lookback_impl(const ScanArgs &a, uint32_t grid_cap, hipStream_
 }
 
 // Instantiated (block, rows) shapes, block counting the control wave.
-// Every type gets the default shape (512 threads = 448 data threads x 8 rows
-// of 128-bit vectors, 56 KiB per tile; 4 rows for 8-byte elements) and a
-// one-row shape (small tiles, used to force many tiles at small n); fp32 sum
+// Every type gets the default shape -- 512 threads (448 data threads) x 10
+// rows of 128-bit vectors for 4-byte elements (70 KiB per tile), x 8 rows for
+// 8-byte elements (56 KiB): the largest tiles whose two LDS stashes fit the
+// 160 KiB of LDS, measured fastest on MI355X -- and a one-row shape (small
+// tiles, used to force many tiles at small n), and 1, 2, 3 and 5 rows, which
+// the planner picks so that one tile holds a whole short segment.  fp32 sum
 // also gets the shapes the tuning sweep visits.
 template <class T, class Op, int V>
 static LbLaunch pick_shape(int block, int rows) {
 #define SW64_SHAPE(B, R) \
     if (block == B && rows == R) return &launch_lookback_impl<T, Op, B, R, V>;
     SW64_SHAPE(256, 1)
+    SW64_SHAPE(512, 1)
+    SW64_SHAPE(512, 2)
+    SW64_SHAPE(512, 3)
+    SW64_SHAPE(512, 5)
     if constexpr (sizeof(T) == 4) {
-        SW64_SHAPE(512, 8)
+        SW64_SHAPE(512, 10)
     } else {
-        SW64_SHAPE(512, 4)  // 8-byte elements: 8 rows would spill past 256 VGPRs
+        SW64_SHAPE(512, 8)
     }
     if constexpr (std::is_same_v<T, float> && std::is_same_v<Op, OpSum>) {
         SW64_SHAPE(256, 2)
         SW64_SHAPE(256, 4)
         SW64_SHAPE(256, 8)
-        SW64_SHAPE(512, 2)
         SW64_SHAPE(512, 4)
+        SW64_SHAPE(512, 8)
         SW64_SHAPE(1024, 2)
     }
 #undef SW64_SHAPE
