@@ -18,11 +18,11 @@ namespace sw64 {
 SW64_DECLARE_PER_TYPE(find_lookback, LbLaunch)
 SW64_DECLARE_PER_TYPE(find_rts, RtsLaunch)
 #undef SW64_DECLARE_PER_TYPE
-ElemLaunch find_element_i32(scan_op_t, int);
-ElemLaunch find_element_u32(scan_op_t, int);
-ElemLaunch find_element_i64(scan_op_t, int);
-ElemLaunch find_element_f32(scan_op_t, int);
-ElemLaunch find_element_f64(scan_op_t, int);
+ElemLaunch find_element_i32(scan_op_t, int, int, bool);
+ElemLaunch find_element_u32(scan_op_t, int, int, bool);
+ElemLaunch find_element_i64(scan_op_t, int, int, bool);
+ElemLaunch find_element_f32(scan_op_t, int, int, bool);
+ElemLaunch find_element_f64(scan_op_t, int, int, bool);
 
 ColLaunch find_columns_i32(scan_op_t, int);
 ColLaunch find_columns_u32(scan_op_t, int);
@@ -41,13 +41,13 @@ ColLaunch find_columns(scan_dtype_t dt, scan_op_t op, int vec) {
     return nullptr;
 }
 
-ElemLaunch find_element(scan_dtype_t dt, scan_op_t op, int width) {
+ElemLaunch find_element(scan_dtype_t dt, scan_op_t op, int width, int e, bool vec) {
     switch (dt) {
-    case SCAN_I32: return find_element_i32(op, width);
-    case SCAN_U32: return find_element_u32(op, width);
-    case SCAN_I64: return find_element_i64(op, width);
-    case SCAN_F32: return find_element_f32(op, width);
-    case SCAN_F64: return find_element_f64(op, width);
+    case SCAN_I32: return find_element_i32(op, width, e, vec);
+    case SCAN_U32: return find_element_u32(op, width, e, vec);
+    case SCAN_I64: return find_element_i64(op, width, e, vec);
+    case SCAN_F32: return find_element_f32(op, width, e, vec);
+    case SCAN_F64: return find_element_f64(op, width, e, vec);
     }
     return nullptr;
 }
@@ -83,6 +83,7 @@ constexpr int kDefaultBlock = 512;  // threads per workgroup of the tiled kernel
 constexpr int kDefaultRtsBlocks = 1024;               // C of reduce-then-scan
 constexpr int64_t kDefaultLocalMem = 64 * 1024;       // LDS budget of the large-element rule
 constexpr int kElemDefaultBlock = 256;                // large elements: start of the rule
+constexpr int64_t kElemChunks = 2048;                 // large elements: workgroups per launch
 
 // AcceleratedKernels.jl PR #208, first bullet: an explicit block size is kept
 // as given; an unset one starts at the default and is lowered to the largest
@@ -214,30 +215,40 @@ int plan_scan(scan_dtype_t dt, scan_op_t op, int64_t outer, int64_t len, bool al
     return SCAN_OK;
 }
 
-// Large elements (inner > 1): one element per thread, `block` elements per
-// tile from the PR's rule; the kernel's waves need block >= 64 (and the
-// launch bound allows 256).
+// Large elements (inner > 1): `block` threads per workgroup from the PR's
+// rule, each owning E elements of a tile: E = elem_e_max(inner) when that
+// tile still fits the rule's budget (2 * block * E * esize bytes), else 1.
+// Chunks of tiles give about kElemChunks workgroups per launch.
 int plan_element(scan_dtype_t dt, scan_op_t op, int64_t outer, int64_t len, int64_t inner, bool aligned,
                  const scan_tuning_t &tu, TilePlan &p) {
     if (tu.algo == SCAN_ALGO_REDUCE_THEN_SCAN) return SCAN_ERR_UNSUPPORTED;
-    if (inner > 64 || !find_element(dt, op, int(inner))) return SCAN_ERR_UNSUPPORTED;
+    if (inner > 64) return SCAN_ERR_UNSUPPORTED;
     const int esize = dtype_bytes(dt);
     const int64_t budget = tu.local_mem_bytes > 0 ? tu.local_mem_bytes : kDefaultLocalMem;
     const int64_t b = element_block(inner * esize, budget, tu.block_size, kElemDefaultBlock);
-    if (b != 64 && b != 128 && b != 256) return SCAN_ERR_UNSUPPORTED;
+    if (b < 64 || b > 512 || b % 64 != 0) return SCAN_ERR_UNSUPPORTED;
+    const bool vec = aligned && (inner * esize) % 16 == 0;
+    int e = elem_e_max(int(inner));
+    if (e > 1 && 2 * b * e * inner * esize > budget) e = 1;
+    if (!find_element(dt, op, int(inner), e, vec)) return SCAN_ERR_UNSUPPORTED;
     p.kernel = SCAN_KERNEL_ELEMENT;
     p.block = int(b);
-    p.rows = 1;
-    p.vec = (aligned && (inner * esize) % 16 == 0) ? 16 / esize : 1;
+    p.rows = e;
+    p.vec = vec ? 16 / esize : 1;
     p.width = int(inner);
-    p.tile = b;
-    p.tiles_per_seg = (len + b - 1) / b;
+    p.tile = b * e;
+    p.tiles_per_seg = (len + p.tile - 1) / p.tile;
     p.num_tiles = outer * p.tiles_per_seg;
     if (p.num_tiles > int64_t(INT32_MAX)) return SCAN_ERR_OVERFLOW;
+    int64_t chunks = (kElemChunks + outer - 1) / outer;
+    if (chunks > p.tiles_per_seg) chunks = p.tiles_per_seg;
+    if (chunks < 1) chunks = 1;
+    p.rts_chunk = (p.tiles_per_seg + chunks - 1) / chunks;      // tiles per chunk
+    p.rts_blocks = (p.tiles_per_seg + p.rts_chunk - 1) / p.rts_chunk;  // chunks per segment
+    if (outer * p.rts_blocks > int64_t(INT32_MAX) || outer * inner > int64_t(INT32_MAX)) return SCAN_ERR_OVERFLOW;
     p.carry_words = int(inner) * carry_bytes(dt, op) / 4;
-    p.rts_blocks = p.rts_chunk = 0;
-    p.ws_bytes = kHeader + round_up(size_t(p.num_tiles) * p.carry_words * 8, 256);
-    p.launches = 1;
+    p.ws_bytes = kHeader + round_up(size_t(outer * p.rts_blocks * inner) * carry_bytes(dt, op), 256);
+    p.launches = 3;
     return SCAN_OK;
 }
 
@@ -346,14 +357,15 @@ int scan_common(const void *in, void *out, int64_t outer, int64_t len, int64_t i
         rc = check_ws(ws, ws_bytes, p.ws_bytes);
         if (rc != SCAN_OK) return rc;
         ElemArgs a;
-        a.pipe = pipe_args(p, ws, ws_bytes, tu);
         a.in = in;
         a.out = out;
-        a.seg_len = len;
+        a.outer = uint32_t(outer);
+        a.len = len;
+        a.chunks = uint32_t(p.rts_blocks);
+        a.tiles_per_chunk = uint32_t(p.rts_chunk);
         a.exclusive = exclusive ? 1 : 0;
-        a.vec16 = p.vec > 1 ? 1 : 0;
-        const uint32_t grid_cap = tu.grid_blocks > 0 ? uint32_t(tu.grid_blocks) : 0u;
-        return find_element(dt, op, p.width)(a, p.block, grid_cap, stream);
+        a.partials = reinterpret_cast<char *>(ws) + kHeader;
+        return find_element(dt, op, p.width, p.rows, p.vec > 1)(a, p.block, stream);
     }
 
     TilePlan p;
@@ -385,15 +397,26 @@ int scan_common(const void *in, void *out, int64_t outer, int64_t len, int64_t i
     return find_lookback(dt, op, p.block, p.rows, p.vec)(a, grid_cap, stream);
 }
 
+// LDS of the element kernels (ElemTile::lds_bytes in element.hip): the tile
+// in the owner layout, each thread's slots padded to an odd number of
+// accesses, then one slot per wave (up to 8) and component.
+int64_t element_lds_bytes(scan_dtype_t dt, scan_op_t op, const TilePlan &p) {
+    const int64_t s = dtype_bytes(dt), lv = p.vec;  // values per access
+    const int64_t vpt = int64_t(p.rows) * p.width, upt = vpt / lv;
+    const int64_t stride = vpt + (upt % 2 == 0 ? lv : 0);
+    return int64_t(p.block) * stride * s + 8 * int64_t(p.width) * carry_bytes(dt, op);
+}
+
 void fill_plan(const TilePlan &p, scan_dtype_t dt, scan_op_t op, scan_plan_t *plan) {
     plan->kernel = p.kernel;
     plan->block_size = p.block;
-    plan->items_per_thread = p.rows * p.vec;
+    plan->items_per_thread = p.kernel == SCAN_KERNEL_ELEMENT ? p.rows : p.rows * p.vec;
     plan->vec = p.vec;
     plan->tile_elems = p.tile;  // elements (of `width` components for the element kernel)
     plan->num_tiles = p.kernel == SCAN_KERNEL_RTS ? p.rts_blocks : p.num_tiles;
+    if (p.kernel == SCAN_KERNEL_ELEMENT) plan->num_tiles = p.num_tiles / p.tiles_per_seg * p.rts_blocks;
     if (p.kernel == SCAN_KERNEL_ELEMENT)
-        plan->lds_bytes = int64_t(p.width) * (4 * dtype_bytes(dt) + 4 * carry_bytes(dt, op)) + 32;
+        plan->lds_bytes = element_lds_bytes(dt, op, p);
     else
         plan->lds_bytes = int64_t(p.rows) * (p.block / 64) * dtype_bytes(dt) + carry_bytes(dt, op) + 32;
     plan->workspace_bytes = int64_t(p.ws_bytes);

@@ -1,326 +1,364 @@
 // element.hip -- scans of large elements: each element is W consecutive
 // components combined component-wise (AcceleratedKernels.jl PR #208: scans
 // of structs and of ForwardDiff duals, value + 16 partials = 136 bytes).  The
-// same kernel scans along the long axis of an (outer, len, W) array, i.e.
+// same kernels scan along the long axis of an (outer, len, W) array, i.e.
 // scan_dim with a small inner extent (1e6 x 8 along dim 0 is 1e6 elements of
 // 8 components).
 //
-// Design: one element per thread, held in registers as W components; the W
-// component scans of a tile run side by side (W wave scans on DPP, one LDS
-// slot per wave and component), and the tile's carry is the W-component
-// aggregate, whose descriptor spans W x (carry bytes / 4) words.  Tiles are
-// `block` elements, chosen on the host by the PR's rule for large element
-// types (largest power of two whose one-item-per-thread tile plus per-thread
-// totals fits the local-memory budget); this kernel keeps less than that in
-// LDS (one slot per wave, the PR's second bullet), so the rule is a safe
-// bound here.  The loads of one element are consecutive 128-bit accesses
-// (lanes at a stride of one element): the cache lines a wave touches are
-// shared by its few consecutive accesses, so they go through the caches
-// (no nontemporal hint) and HBM sees each byte once.  Ordering, descriptors
-// and look-back come from the persistent pipeline (pipeline.hpp).
+// Reduce-then-scan over chunks of tiles (The CUDA Handbook ch. 13 section
+// 13.3.3; Merry, "Prefix sums on GPUs", slide "Reduce-then-Scan strategy"),
+// chosen over the single-pass look-back here because a carry of W components
+// makes every look-back window W times as expensive to read, while the second
+// read of a chunk mostly hits the 256 MB Infinity Cache at these sizes.
+//   1. reduce: each workgroup folds its chunk into W component partials;
+//   2. partials: per segment and component, an exclusive scan over chunks;
+//   3. rescan: each workgroup scans its chunk again from those prefixes,
+//      tile by tile with a running carry, and zeroes its partials (the
+//      workspace's descriptor area is left zeroed).
+//
+// A tile is `threads` x E elements.  It is moved between HBM and LDS with
+// coalesced accesses (consecutive lanes, consecutive 16-byte vectors, or
+// element-wide values when the data is not 16-byte aligned) and transposed
+// through LDS so that each thread owns E consecutive elements: the W
+// component scans are then thread-serial over E elements, W wave scans on
+// DPP, and one LDS slot per wave and component (the PR's second bullet).  A
+// thread's LDS slots are padded to an odd number of accesses so the
+// transposed reads are free of bank conflicts.  `threads` comes from the
+// PR's LDS-budget rule for large elements and E fills the rest of the budget
+// (see plan_element in api.hip).
 //
 // Compiled once per element type (SW64_DT).
 #include "launch.hpp"
-#include "tile.hpp"
 
 namespace sw64 {
 
-constexpr int kElemMaxWaves = 4;  // block <= 256 elements
+constexpr int kElemMaxThreads = 512;
+constexpr int kElemMaxWaves = kElemMaxThreads / kWave;
 
-template <class C1, int W>
-struct Agg {
-    C1 c[W];
-};
+template <class T, class Op, int W, int E, int LG>
+struct ElemTile {
+    using C = typename Carry<T, Op>::type;
+    static constexpr int S = int(sizeof(T));
+    static constexpr int LV = LG / S;       // values per global access
+    static constexpr int VPT = E * W;       // values a thread owns per tile
+    static_assert(LG % S == 0 && VPT % LV == 0, "whole accesses per thread");
+    static constexpr int UPT = VPT / LV;    // accesses per thread per tile
+    static constexpr int STRIDE = VPT + (UPT % 2 == 0 ? LV : 0);  // LDS values per thread
 
-template <class Op>
-struct ElemOp {
-    template <class A>
-    __device__ __forceinline__ static A identity() {
-        A r;
-#pragma unroll
-        for (int k = 0; k < int(sizeof(A::c) / sizeof(A::c[0])); k++)
-            r.c[k] = Op::template identity<std::remove_reference_t<decltype(r.c[0])>>();
-        return r;
+    static constexpr size_t lds_bytes(int threads) {
+        return size_t(threads) * STRIDE * S + size_t(kElemMaxWaves) * W * sizeof(C);
     }
-    template <class A>
-    __device__ __forceinline__ static A apply(const A &a, const A &b) {
-        A r;
-#pragma unroll
-        for (int k = 0; k < int(sizeof(A::c) / sizeof(A::c[0])); k++) r.c[k] = Op::apply(a.c[k], b.c[k]);
-        return r;
-    }
-};
 
-template <class T_, class Op_, int W>
-struct ElemPolicy {
-    using T = T_;
-    using Op = Op_;
-    using C1 = typename Carry<T, Op>::type;
-    using C = Agg<C1, W>;
-    static constexpr int BLOCK = 256;  // launch bound; blockDim.x is 64, 128 or 256
-    static constexpr int kDescWords = Desc<C>::kWords;
-    static constexpr int kBytes = W * int(sizeof(T));
-    using Args = ElemArgs;
+    using Acc = Vec<T, LV>;  // one global access
 
-    struct Shared {
-        T tot[W][kElemMaxWaves];
-        C agg[3];
+    // Geometry of tile `j` of segment `seg`.
+    struct Geo {
+        int64_t e0;     // first element of the tile within its segment
+        int64_t valid;  // elements of the tile in range (<= threads * E)
+        BufRsrc rs;     // the tile's bytes in the (input or output) array
     };
 
-    static constexpr int kCW = Desc<C1>::kWords;  // descriptor words per component
-
-    // Component by component, so the registers in use do not grow with W.
-    template <class TileT>
-    __device__ __forceinline__ static void publish_aggregate(const TileT &ts, uint64_t *d, uint32_t epoch,
-                                                             uint32_t state) {
-#pragma unroll 1
-        for (int k = 0; k < W; k++) Desc<C1>::publish(d + k * kCW, epoch, state, ts.aggp->c[k]);
+    __device__ __forceinline__ static Geo geo(const ElemArgs &a, const void *base, uint32_t seg, int64_t j) {
+        Geo g;
+        const int64_t tile = int64_t(blockDim.x) * E;
+        g.e0 = j * tile;
+        const int64_t rem = a.len - g.e0;
+        g.valid = uniform(rem < tile ? rem : tile);
+        const T *p = reinterpret_cast<const T *>(base) + (int64_t(seg) * a.len + g.e0) * W;
+        g.rs = make_rsrc(p, g.valid * W);
+        return g;
     }
 
-    __device__ __forceinline__ static void set_identity(C *prefix) {
-        if (lane_id() == 0) {
-#pragma unroll 1
-            for (int k = 0; k < W; k++) prefix->c[k] = Op::template identity<C1>();
-        }
-    }
-
-    // The decoupled look-back of the pipeline, component-serial (wave 0).
-    // Phase 1 polls word 0 of each window slot for its state, as in the
-    // scalar look-back.  Phase 2 reduces the slots up to the nearest P one
-    // component at a time into LDS; every word read must carry the tag seen
-    // in phase 1, otherwise that descriptor advanced from A to P between the
-    // reads and the window is read again (states only move forward, so this
-    // repeats at most once per slot).  The exclusive prefix accumulates in
-    // LDS; lane 0 then publishes P component-wise.
-    template <class TileT>
-    __device__ static void resolve(const TileT &ts, const uint64_t *desc, uint32_t epoch, uint32_t tile,
-                                   int64_t first, WsHeader *hdr, uint32_t spin_limit, C *prefix) {
-        __shared__ C1 win[W];
-        const int lane = lane_id();
-        const C1 id = Op::template identity<C1>();
-        if (lane == 0) {
-#pragma unroll 1
-            for (int k = 0; k < W; k++) prefix->c[k] = id;
-        }
-        int64_t frontier = int64_t(tile) - 1;
-        for (;;) {
-            const int64_t p = frontier - lane;
-            const uint64_t *dl = desc + p * kDescWords;
-            uint64_t tag = 0;
-            uint32_t st = kStateP;
-            int near_p = kWave, near_x = kWave;
-            for (uint32_t polls = 0;; polls++) {
-                if (p >= first) {
-                    const uint64_t w0 = ld(dl);
-                    tag = w0 >> kTagShift;
-                    st = desc_state(w0, epoch);
-                } else {
-                    st = kStateP;
-                }
-                const uint64_t xm = __ballot(st == 0u), pm = __ballot(st == kStateP);
-                near_x = xm ? __builtin_ctzll(xm) : kWave;
-                near_p = pm ? __builtin_ctzll(pm) : kWave;
-                if (near_x == kWave || near_p < near_x) break;
-                if (polls >= spin_limit) {
-                    if (lane == 0) flag_error(hdr, kErrSpin);
-                    near_p = near_x;  // unpublished slots count as P with the identity
-                    break;
-                }
-                __builtin_amdgcn_s_sleep(1);
-            }
-            const bool reads = p >= first && st != 0u && lane <= near_p;
-            bool torn = false;
-#pragma unroll 1
-            for (int k = 0; k < W; k++) {
-                C1 v = id;
-                bool bad = false;
-                if (reads) {
-                    struct Chunks { uint32_t w[kCW]; } c;
+    // Global -> LDS in the owner layout: access u of the tile (value u * LV)
+    // belongs to thread u / UPT at its slot (u % UPT) * LV.
+    __device__ __forceinline__ static void load_tile(const Geo &g, T *lds) {
 #pragma unroll
-                    for (int i = 0; i < kCW; i++) {
-                        const uint64_t word = ld(dl + k * kCW + i);
-                        bad = bad || (word >> kTagShift) != tag;
-                        c.w[i] = uint32_t(word);
-                    }
-                    v = __builtin_bit_cast(C1, c);
-                }
-                if (__any(bad)) {
-                    torn = true;
-                    break;
-                }
-                const C1 sum = wave_reduce<Op>(v);
-                if (lane == 0) win[k] = sum;
-            }
-            if (torn) continue;
-            if (lane == 0) {
-#pragma unroll 1
-                for (int k = 0; k < W; k++) prefix->c[k] = Op::apply(win[k], prefix->c[k]);
-            }
-            if (near_p < kWave) break;
-            frontier -= kWave;
-        }
-        if (lane == 0) {
-            uint64_t *d = const_cast<uint64_t *>(desc) + uint64_t(tile) * kDescWords;
-#pragma unroll 1
-            for (int k = 0; k < W; k++)
-                Desc<C1>::publish(d + k * kCW, epoch, kStateP, Op::apply(prefix->c[k], ts.aggp->c[k]));
+        for (int r = 0; r < UPT; r++) {
+            const uint32_t u = uint32_t(r) * blockDim.x + threadIdx.x;
+            Acc x;
+            if constexpr (LG == 16)
+                x = __builtin_bit_cast(Acc, __builtin_amdgcn_raw_buffer_load_b128(g.rs, u * 16u, 0, 2));
+            else if constexpr (LG == 8)
+                x = __builtin_bit_cast(Acc, __builtin_amdgcn_raw_buffer_load_b64(g.rs, u * 8u, 0, 2));
+            else
+                x = __builtin_bit_cast(Acc, __builtin_amdgcn_raw_buffer_load_b32(g.rs, u * 4u, 0, 2));
+            *reinterpret_cast<Acc *>(lds + (u / UPT) * STRIDE + (u % UPT) * LV) = x;
         }
     }
 
-    struct Tile {
-        T x[W];          // the element; after scan(), its tile-local scan
-        int slot;
-        bool excl;
-        const C *aggp;   // this buffer's aggregate slot in LDS
-
-        __device__ __forceinline__ void set_slot(int s) { slot = s; }
-
-        __device__ __forceinline__ static void geom(const Args &a, uint32_t tile, int64_t &start,
-                                                    int64_t &remaining) {
-            const uint32_t seg = tile / a.pipe.tiles_per_seg;
-            const uint32_t j = tile - seg * a.pipe.tiles_per_seg;
-            start = int64_t(seg) * a.seg_len + int64_t(j) * blockDim.x;
-            remaining = a.seg_len - int64_t(j) * blockDim.x;
+    // LDS (owner layout) -> global, dropping values past the tile's range.
+    __device__ __forceinline__ static void store_tile(const Geo &g, const T *lds) {
+#pragma unroll
+        for (int r = 0; r < UPT; r++) {
+            const uint32_t u = uint32_t(r) * blockDim.x + threadIdx.x;
+            const Acc x = *reinterpret_cast<const Acc *>(lds + (u / UPT) * STRIDE + (u % UPT) * LV);
+            store_vec_bounded<T, LV>(g.rs, u * uint32_t(LG), x);
         }
+    }
 
-        __device__ __forceinline__ void load(const Args &a, uint32_t tile) {
-            int64_t start, remaining;
-            geom(a, tile, start, remaining);
-            excl = a.exclusive != 0;
-            const int64_t e = start + threadIdx.x;
-            const T *src = reinterpret_cast<const T *>(a.in) + e * W;
-            if (threadIdx.x < remaining) {
-                if constexpr (kBytes % 16 == 0) {
-                    if (a.vec16) {
+    // This thread's E elements from LDS; elements past the range hold the
+    // identity.
+    __device__ __forceinline__ static void read_own(const Geo &g, const T *lds, T (&v)[VPT]) {
+        const T *src = lds + threadIdx.x * STRIDE;
 #pragma unroll
-                        for (int q = 0; q < kBytes / 16; q++) {
-                            const u32x4_t w = reinterpret_cast<const u32x4_t *>(src)[q];
-                            struct Q { T t[16 / sizeof(T)]; };
-                            const Q qq = __builtin_bit_cast(Q, w);
+        for (int q = 0; q < UPT; q++) {
+            const Acc x = *reinterpret_cast<const Acc *>(src + q * LV);
 #pragma unroll
-                            for (int i = 0; i < int(16 / sizeof(T)); i++) x[q * (16 / sizeof(T)) + i] = qq.t[i];
-                        }
-                        return;
-                    }
-                }
+            for (int i = 0; i < LV; i++) v[q * LV + i] = x.v[i];
+        }
+        const T id = Op::template identity<T>();
 #pragma unroll
-                for (int k = 0; k < W; k++) x[k] = src[k];
-            } else {
+        for (int e = 0; e < E; e++) {
+            const bool in = int64_t(threadIdx.x) * E + e < g.valid;
 #pragma unroll
-                for (int k = 0; k < W; k++) x[k] = Op::template identity<T>();
+            for (int c = 0; c < W; c++) v[e * W + c] = in ? v[e * W + c] : id;
+        }
+    }
+
+    __device__ __forceinline__ static void write_own(T *lds, const T (&v)[VPT]) {
+        T *dst = lds + threadIdx.x * STRIDE;
+#pragma unroll
+        for (int q = 0; q < UPT; q++) {
+            Acc x;
+#pragma unroll
+            for (int i = 0; i < LV; i++) x.v[i] = v[q * LV + i];
+            *reinterpret_cast<Acc *>(dst + q * LV) = x;
+        }
+    }
+
+    __device__ __forceinline__ static uint32_t tiles_of(const ElemArgs &a, uint32_t chunk, int64_t &j0) {
+        const int64_t tiles = (a.len + int64_t(blockDim.x) * E - 1) / (int64_t(blockDim.x) * E);
+        j0 = int64_t(chunk) * a.tiles_per_chunk;
+        const int64_t left = tiles - j0;
+        return uint32_t(left < int64_t(a.tiles_per_chunk) ? (left > 0 ? left : 0) : a.tiles_per_chunk);
+    }
+
+    // Pass 1: the W component partials of each chunk.
+    __device__ static void reduce(const ElemArgs &a) {
+        extern __shared__ __align__(16) char smem[];
+        T *lds = reinterpret_cast<T *>(smem);
+        C *red = reinterpret_cast<C *>(smem + size_t(blockDim.x) * STRIDE * S);
+        const uint32_t seg = blockIdx.x / a.chunks, chunk = blockIdx.x % a.chunks;
+        const C cid = Op::template identity<C>();
+        C acc[W];
+#pragma unroll
+        for (int c = 0; c < W; c++) acc[c] = cid;
+        int64_t j0;
+        const uint32_t nt = tiles_of(a, chunk, j0);
+        for (uint32_t k = 0; k < nt; k++) {
+            const Geo g = geo(a, a.in, seg, j0 + k);
+            if (k > 0) __syncthreads();  // previous tile's reads are done
+            load_tile(g, lds);
+            __syncthreads();
+            T v[VPT];
+            read_own(g, lds, v);
+#pragma unroll
+            for (int e = 0; e < E; e++) {
+#pragma unroll
+                for (int c = 0; c < W; c++) acc[c] = Op::apply(acc[c], C(v[e * W + c]));
             }
         }
+        const int wave = threadIdx.x / kWave, waves = blockDim.x / kWave;
+#pragma unroll
+        for (int c = 0; c < W; c++) {
+            const C r = wave_reduce<Op>(acc[c]);
+            if (lane_id() == 0) red[wave * W + c] = r;
+        }
+        __syncthreads();
+        if (threadIdx.x < W) {
+            C t = cid;
+            for (int w = 0; w < waves; w++) t = Op::apply(t, red[w * W + threadIdx.x]);
+            reinterpret_cast<C *>(a.partials)[(int64_t(seg) * a.chunks + chunk) * W + threadIdx.x] = t;
+        }
+    }
 
-        // W wave scans, one LDS slot per wave and component, then every
-        // thread combines the per-wave totals.  One barrier.
-        __device__ __forceinline__ void scan(Shared &sh) {
-            const T id = Op::template identity<T>();
-            const int lane = lane_id(), wave = threadIdx.x / kWave, waves = blockDim.x / kWave;
+    // Pass 3: scan each tile of the chunk from the chunk's prefix.
+    __device__ static void rescan(const ElemArgs &a) {
+        extern __shared__ __align__(16) char smem[];
+        T *lds = reinterpret_cast<T *>(smem);
+        T *wt = reinterpret_cast<T *>(smem + size_t(blockDim.x) * STRIDE * S);
+        const uint32_t seg = blockIdx.x / a.chunks, chunk = blockIdx.x % a.chunks;
+        const int lane = lane_id(), wave = threadIdx.x / kWave, waves = blockDim.x / kWave;
+        const T id = Op::template identity<T>();
+        C *part = reinterpret_cast<C *>(a.partials) + (int64_t(seg) * a.chunks + chunk) * W;
+        C carry[W];
 #pragma unroll
-            for (int k = 0; k < W; k++) x[k] = wave_scan_incl<Op>(x[k]);
-            if (lane == kWave - 1) {
+        for (int c = 0; c < W; c++) carry[c] = part[c];
+        __syncthreads();  // every thread has read the prefix
+        if (threadIdx.x < W) part[threadIdx.x] = C{};  // leave the workspace zeroed
+        int64_t j0;
+        const uint32_t nt = tiles_of(a, chunk, j0);
+        for (uint32_t k = 0; k < nt; k++) {
+            const Geo gi = geo(a, a.in, seg, j0 + k);
+            if (k > 0) __syncthreads();  // previous tile's stores have read LDS
+            load_tile(gi, lds);
+            __syncthreads();
+            T v[VPT];
+            read_own(gi, lds, v);
+            // thread-serial inclusive scans of the E elements, per component
+            T run[W];
 #pragma unroll
-                for (int k = 0; k < W; k++) sh.tot[k][wave] = x[k];
+            for (int c = 0; c < W; c++) run[c] = id;
+#pragma unroll
+            for (int e = 0; e < E; e++) {
+#pragma unroll
+                for (int c = 0; c < W; c++) {
+                    run[c] = Op::apply(run[c], v[e * W + c]);
+                    v[e * W + c] = run[c];
+                }
+            }
+            // wave scans of the thread totals; run[c] becomes the thread's
+            // exclusive offset within its wave
+#pragma unroll
+            for (int c = 0; c < W; c++) {
+                const T inc = wave_scan_incl<Op>(run[c]);
+                if (lane == kWave - 1) wt[wave * W + c] = inc;
+                run[c] = wave_shr1(id, inc);
             }
             __syncthreads();
-            C agg;
 #pragma unroll
-            for (int k = 0; k < W; k++) {
-                T base = id, run = id;
+            for (int c = 0; c < W; c++) {
+                T base = id, tot = id;
                 for (int w = 0; w < waves; w++) {
-                    const T t = sh.tot[k][w];
+                    const T t = wt[w * W + c];
                     if (w < wave) base = Op::apply(base, t);
-                    run = Op::apply(run, t);
+                    tot = Op::apply(tot, t);
                 }
-                const T mine = excl ? wave_shr1(id, x[k]) : x[k];
-                x[k] = Op::apply(base, mine);
-                agg.c[k] = C1(run);
-            }
-            if (threadIdx.x == 0) sh.agg[slot] = agg;
-            aggp = &sh.agg[slot];
-        }
-
-        __device__ __forceinline__ C aggregate() const { return *aggp; }
-
-        __device__ __forceinline__ void emit(const Args &a, uint32_t tile, const C *prefix) const {
-            int64_t start, remaining;
-            geom(a, tile, start, remaining);
-            if (threadIdx.x >= remaining) return;
-            const C pre = *prefix;
-            T *dst = reinterpret_cast<T *>(a.out) + (start + threadIdx.x) * W;
-            T y[W];
+                const T off = Op::apply(base, run[c]);
+                T prev = off;
 #pragma unroll
-            for (int k = 0; k < W; k++) y[k] = T(Op::apply(pre.c[k], C1(x[k])));
-            if constexpr (kBytes % 16 == 0) {
-                if (a.vec16) {
-#pragma unroll
-                    for (int q = 0; q < kBytes / 16; q++) {
-                        struct Q { T t[16 / sizeof(T)]; } qq;
-#pragma unroll
-                        for (int i = 0; i < int(16 / sizeof(T)); i++) qq.t[i] = y[q * (16 / sizeof(T)) + i];
-                        reinterpret_cast<u32x4_t *>(dst)[q] = __builtin_bit_cast(u32x4_t, qq);
-                    }
-                    return;
+                for (int e = 0; e < E; e++) {
+                    const T inc = Op::apply(off, v[e * W + c]);
+                    v[e * W + c] = T(Op::apply(carry[c], C(a.exclusive ? prev : inc)));
+                    prev = inc;
                 }
+                carry[c] = Op::apply(carry[c], C(tot));
             }
-#pragma unroll
-            for (int k = 0; k < W; k++) dst[k] = y[k];
+            write_own(lds, v);
+            __syncthreads();
+            store_tile(geo(a, a.out, seg, j0 + k), lds);
         }
-    };
+    }
 };
 
-template <class P>
-__global__ __launch_bounds__(P::BLOCK) void k_element(typename P::Args a) {
-    Pipeline<P>::run(a);
+template <class K>
+__global__ __launch_bounds__(kElemMaxThreads) void k_elem_reduce(ElemArgs a) {
+    K::reduce(a);
 }
 
+template <class K>
+__global__ __launch_bounds__(kElemMaxThreads) void k_elem_rescan(ElemArgs a) {
+    K::rescan(a);
+}
+
+// Pass 2: one workgroup per (segment, component) scans the chunk partials
+// into exclusive prefixes: each thread folds a run of consecutive chunks,
+// then a workgroup scan of the runs.
 template <class T, class Op, int W>
-static int launch_element_impl(const ElemArgs &a, int block, uint32_t grid_cap, hipStream_t s) {
-    using P = ElemPolicy<T, Op, W>;
-    const int g = pipeline_grid(reinterpret_cast<const void *>(&k_element<P>), block, a.pipe.num_tiles, grid_cap);
-    if (g <= 0) return SCAN_ERR_HIP;
-    hipLaunchKernelGGL((k_element<P>), dim3(g), dim3(block), 0, s, a);
+__global__ __launch_bounds__(256) void k_elem_partials(ElemArgs a) {
+    using C = typename Carry<T, Op>::type;
+    __shared__ C tot[256 / kWave];
+    const uint32_t seg = blockIdx.x / W, comp = blockIdx.x % W;
+    C *part = reinterpret_cast<C *>(a.partials) + int64_t(seg) * a.chunks * W + comp;
+    const C id = Op::template identity<C>();
+    const uint32_t per = (a.chunks + 255u) / 256u;
+    const uint32_t c0 = threadIdx.x * per;
+    C run = id;
+    for (uint32_t i = 0; i < per; i++)
+        if (c0 + i < a.chunks) run = Op::apply(run, part[int64_t(c0 + i) * W]);
+    const int wave = threadIdx.x / kWave;
+    const C inc = wave_scan_incl<Op>(run);
+    if (lane_id() == kWave - 1) tot[wave] = inc;
+    __syncthreads();
+    C base = id;
+    for (int w = 0; w < wave; w++) base = Op::apply(base, tot[w]);
+    C ex = Op::apply(base, wave_shr1(id, inc));
+    for (uint32_t i = 0; i < per; i++) {
+        if (c0 + i < a.chunks) {
+            const C x = part[int64_t(c0 + i) * W];
+            part[int64_t(c0 + i) * W] = ex;
+            ex = Op::apply(ex, x);
+        }
+    }
+}
+
+template <class T, class Op, int W, int E, int LG>
+static int launch_elem_impl(const ElemArgs &a, int threads, hipStream_t s) {
+    using K = ElemTile<T, Op, W, E, LG>;
+    if (threads < kWave || threads > kElemMaxThreads || threads % kWave) return SCAN_ERR_UNSUPPORTED;
+    const uint32_t blocks = a.outer * a.chunks;
+    const size_t lds = K::lds_bytes(threads);
+    if (lds > 65536) {  // above the default dynamic LDS limit (gfx950 has 160 KiB per workgroup)
+        if (hipFuncSetAttribute(reinterpret_cast<const void *>(&k_elem_reduce<K>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, int(lds)) != hipSuccess ||
+            hipFuncSetAttribute(reinterpret_cast<const void *>(&k_elem_rescan<K>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, int(lds)) != hipSuccess)
+            return SCAN_ERR_HIP;
+    }
+    hipLaunchKernelGGL((k_elem_reduce<K>), dim3(blocks), dim3(threads), lds, s, a);
+    if (hipGetLastError() != hipSuccess) return SCAN_ERR_HIP;
+    hipLaunchKernelGGL((k_elem_partials<T, Op, W>), dim3(a.outer * W), dim3(256), 0, s, a);
+    if (hipGetLastError() != hipSuccess) return SCAN_ERR_HIP;
+    hipLaunchKernelGGL((k_elem_rescan<K>), dim3(blocks), dim3(threads), lds, s, a);
     return hipGetLastError() == hipSuccess ? SCAN_OK : SCAN_ERR_HIP;
+}
+
+// Variants per width: E = elem_e_max(W) or 1, 16-byte accesses (when W
+// components span whole 16-byte vectors) or element-wide ones.
+template <class T, class Op, int W>
+static ElemLaunch pick_elem_variant(int e, bool vec) {
+    constexpr int EM = elem_e_max(W);
+    constexpr bool kVecOk = (W * int(sizeof(T))) % 16 == 0;
+    if (vec) {
+        if constexpr (kVecOk) {
+            if (e == EM) return &launch_elem_impl<T, Op, W, EM, 16>;
+            if (e == 1) return &launch_elem_impl<T, Op, W, 1, 16>;
+        }
+        return nullptr;
+    }
+    if (e == EM) return &launch_elem_impl<T, Op, W, EM, int(sizeof(T))>;
+    if (e == 1) return &launch_elem_impl<T, Op, W, 1, int(sizeof(T))>;
+    return nullptr;
 }
 
 // Built widths: small vectors and the struct shapes of the measured configs
 // (24 x fp32 = 96 B, 17 x fp64 = 136 B); any other width is scanned by the
 // column kernel.
 template <class T, class Op>
-static ElemLaunch pick_width(int w) {
+static ElemLaunch pick_width(int w, int e, bool vec) {
     switch (w) {
-    case 2: return &launch_element_impl<T, Op, 2>;
-    case 3: return &launch_element_impl<T, Op, 3>;
-    case 4: return &launch_element_impl<T, Op, 4>;
-    case 8: return &launch_element_impl<T, Op, 8>;
-    case 16: return &launch_element_impl<T, Op, 16>;
-    case 17: return &launch_element_impl<T, Op, 17>;
-    case 24: return &launch_element_impl<T, Op, 24>;
+    case 2: return pick_elem_variant<T, Op, 2>(e, vec);
+    case 3: return pick_elem_variant<T, Op, 3>(e, vec);
+    case 4: return pick_elem_variant<T, Op, 4>(e, vec);
+    case 8: return pick_elem_variant<T, Op, 8>(e, vec);
+    case 16: return pick_elem_variant<T, Op, 16>(e, vec);
+    case 17: return pick_elem_variant<T, Op, 17>(e, vec);
+    case 24: return pick_elem_variant<T, Op, 24>(e, vec);
     }
     return nullptr;
 }
 
 template <class T>
-static ElemLaunch pick_elem_op(scan_op_t op, int w) {
+static ElemLaunch pick_elem_op(scan_op_t op, int w, int e, bool vec) {
     switch (op) {
-    case SCAN_OP_SUM: return pick_width<T, OpSum>(w);
-    case SCAN_OP_PROD: return pick_width<T, OpProd>(w);
-    case SCAN_OP_MAX: return pick_width<T, OpMax>(w);
-    case SCAN_OP_MIN: return pick_width<T, OpMin>(w);
+    case SCAN_OP_SUM: return pick_width<T, OpSum>(w, e, vec);
+    case SCAN_OP_PROD: return pick_width<T, OpProd>(w, e, vec);
+    case SCAN_OP_MAX: return pick_width<T, OpMax>(w, e, vec);
+    case SCAN_OP_MIN: return pick_width<T, OpMin>(w, e, vec);
     }
     return nullptr;
 }
 
 #if SW64_DT == 0
-ElemLaunch find_element_i32(scan_op_t op, int w) { return pick_elem_op<int32_t>(op, w); }
+ElemLaunch find_element_i32(scan_op_t op, int w, int e, bool vec) { return pick_elem_op<int32_t>(op, w, e, vec); }
 #elif SW64_DT == 1
-ElemLaunch find_element_u32(scan_op_t op, int w) { return pick_elem_op<uint32_t>(op, w); }
+ElemLaunch find_element_u32(scan_op_t op, int w, int e, bool vec) { return pick_elem_op<uint32_t>(op, w, e, vec); }
 #elif SW64_DT == 2
-ElemLaunch find_element_i64(scan_op_t op, int w) { return pick_elem_op<int64_t>(op, w); }
+ElemLaunch find_element_i64(scan_op_t op, int w, int e, bool vec) { return pick_elem_op<int64_t>(op, w, e, vec); }
 #elif SW64_DT == 3
-ElemLaunch find_element_f32(scan_op_t op, int w) { return pick_elem_op<float>(op, w); }
+ElemLaunch find_element_f32(scan_op_t op, int w, int e, bool vec) { return pick_elem_op<float>(op, w, e, vec); }
 #elif SW64_DT == 4
-ElemLaunch find_element_f64(scan_op_t op, int w) { return pick_elem_op<double>(op, w); }
+ElemLaunch find_element_f64(scan_op_t op, int w, int e, bool vec) { return pick_elem_op<double>(op, w, e, vec); }
 #else
 #error "SW64_DT must select an element type (0..4)"
 #endif

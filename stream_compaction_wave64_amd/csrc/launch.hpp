@@ -65,17 +65,25 @@ int launch_emit_neighbors(const int32_t *offsets, int64_t n, int32_t *out, hipSt
 
 // ---------------------------------------------------------- large elements
 // Elements of W components scanned component-wise along the middle axis of
-// an (outer, len, W) array; `block` elements per tile (64, 128 or 256).
+// an (outer, len, W) array by reduce-then-scan over chunks of tiles; a tile
+// is `threads` x E elements staged through LDS (element.hip).
 struct ElemArgs {
-    PipeArgs pipe;
     const void *in;
     void *out;
-    int64_t seg_len;          // elements per segment (len)
+    uint32_t outer;            // segments
+    int64_t len;               // elements per segment
+    uint32_t chunks;           // chunks per segment (one workgroup each)
+    uint32_t tiles_per_chunk;
     int32_t exclusive;
-    int32_t vec16;            // 1: element rows are 16-byte aligned, use 128-bit accesses
+    void *partials;            // outer * chunks * W carry values, in the workspace
 };
-using ElemLaunch = int (*)(const ElemArgs &, int block, uint32_t grid_cap, hipStream_t);
-ElemLaunch find_element(scan_dtype_t dt, scan_op_t op, int width);
+using ElemLaunch = int (*)(const ElemArgs &, int threads, hipStream_t);
+// e: elements per thread (elem_e_max(width) or 1); vec: 16-byte accesses
+ElemLaunch find_element(scan_dtype_t dt, scan_op_t op, int width, int e, bool vec);
+
+// Elements per thread of an element kernel's wide variant: the largest power
+// of two that keeps at most 32 component values per thread.
+constexpr int elem_e_max(int w) { return w > 16 ? 1 : (w > 8 ? 2 : (w > 4 ? 4 : (w > 2 ? 8 : 16))); }
 
 // ------------------------------------------------------------ wide columns
 // (outer, len, inner) with a wide inner extent: reduce-then-scan over chunks

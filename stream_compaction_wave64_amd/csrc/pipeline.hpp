@@ -14,29 +14,8 @@
 //    at ~11.5 ns each on MI355X (12k of them exceed the HBM time of a
 //    1e8-element scan).  Residency is verified at run time (decide_mode);
 //    without it the call claims tiles in order from a counter instead.
-//  * CtrlPipeline (scalar carries: scans and compaction): a control wave
-//    owns the descriptors and the look-back, and scanned tiles wait in LDS
-//    for their prefix (see its comment).
-//  * Pipeline (the element kernel): three register tiles per workgroup;
-//    while tile t waits for its look-back (wave 0), tile t + G is already
-//    scanned with its aggregate published and the loads of t + 2G are in
-//    flight.
-//
-// Pipeline's policy interface (all __device__):
-//   using T, C (carry type), Op;   static constexpr int BLOCK, kDescWords
-//   struct Args { PipeArgs pipe; ... }
-//   struct Shared;                 LDS the tile scan needs
-//   struct Tile {
-//     void set_slot(int);          which of the three pipeline buffers it is
-//     void load(const Args&, uint32_t tile);
-//     void scan(Shared&);          one barrier; afterwards aggregate() valid
-//     C aggregate() const;
-//     void emit(const Args&, uint32_t tile, const C* prefix);  prefix in LDS
-//   };
-//   static void publish_aggregate(Tile&, uint64_t* desc, uint32_t epoch, uint32_t state);  thread 0
-//   static void resolve(Tile&, ...);   wave 0: look back, publish P, write the
-//                                      exclusive prefix to LDS
-//   static void set_identity(C* prefix);   lane 0
+//  * A control wave owns the descriptors and the look-back, and scanned
+//    tiles wait in LDS for their prefix (see CtrlPipeline's comment).
 #pragma once
 
 #include "device.hpp"
@@ -51,126 +30,6 @@ struct PipeArgs {
     uint32_t tiles_per_seg;   // tiles per segment (>= 1)
     uint32_t spin_limit;      // polls of one look-back window before giving up
     uint32_t mode_limit;      // polls before a call falls back to dynamic claiming
-};
-
-template <class P>
-struct Pipeline {
-    using Tile = typename P::Tile;
-    using C = typename P::C;
-    using Args = typename P::Args;
-
-    struct Smem {
-        typename P::Shared ps;
-        C prefix;
-        uint32_t epoch, mode, ticket;
-        uint64_t clear_end;
-    };
-
-    __device__ __forceinline__ static uint64_t *desc_of(uint64_t *desc, uint32_t tile) {
-        return desc + uint64_t(tile) * P::kDescWords;
-    }
-
-    // Stage 1: scan a loaded tile and publish its aggregate (A), or its
-    // inclusive prefix (P) if it opens its segment.  One barrier.
-    __device__ __forceinline__ static void scan_publish(Tile &ts, const Args &a, uint32_t tile, Smem &sm,
-                                                        uint64_t *desc, uint32_t epoch) {
-        ts.scan(sm.ps);
-        if (a.pipe.tiles_per_seg > 1 && threadIdx.x == 0) {
-            const uint32_t state = (tile % a.pipe.tiles_per_seg == 0) ? kStateP : kStateA;
-            P::publish_aggregate(ts, desc_of(desc, tile), epoch, state);
-        }
-    }
-
-    // Stage 2: look back for the tile's exclusive prefix (wave 0), publish
-    // P, then every thread emits the tile with the prefix.  One barrier.
-    __device__ __forceinline__ static void finish(Tile &ts, const Args &a, uint32_t tile, Smem &sm, WsHeader *hdr,
-                                                  uint64_t *desc, uint32_t epoch) {
-        const uint32_t j = tile % a.pipe.tiles_per_seg;
-        if (threadIdx.x < kWave) {
-            if (a.pipe.tiles_per_seg > 1 && j != 0)
-                P::resolve(ts, desc, epoch, tile, int64_t(tile - j), hdr, a.pipe.spin_limit, &sm.prefix);
-            else
-                P::set_identity(&sm.prefix);
-        }
-        __syncthreads();
-        ts.emit(a, tile, &sm.prefix);
-    }
-
-    // One pipeline step (see the header comment).  Returns false when tile
-    // t + G is past the end.
-    __device__ __forceinline__ static bool step(Tile &cur, Tile &nxt, Tile &fut, const Args &a, uint32_t t,
-                                                Smem &sm, WsHeader *hdr, uint64_t *desc, uint32_t epoch) {
-        const uint32_t n = a.pipe.num_tiles, G = gridDim.x;
-        const uint32_t tn = t + G, tf = tn + G;
-        if (tf < n) fut.load(a, tf);
-        if (tn < n) scan_publish(nxt, a, tn, sm, desc, epoch);
-        finish(cur, a, t, sm, hdr, desc, epoch);
-        return tn < n;
-    }
-
-    // The kernel body.  The host launches at most as many workgroups as can
-    // be resident and no more than there are tiles.
-    __device__ __forceinline__ static void run(const Args &a) {
-        __shared__ Smem sm;
-        WsHeader *hdr = reinterpret_cast<WsHeader *>(a.pipe.ws);
-        uint64_t *desc = reinterpret_cast<uint64_t *>(reinterpret_cast<char *>(a.pipe.ws) + kWsHeaderBytes);
-        const uint32_t n = a.pipe.num_tiles, G = gridDim.x;
-        // Segments of a single tile need no look-back: their tiles are
-        // independent and the header is not touched.
-        const bool chained = a.pipe.tiles_per_seg > 1;
-        if (chained && threadIdx.x == 0) sm.epoch = begin_call(hdr);
-
-        // Three register tiles in rotation (scanned and waiting / loaded /
-        // in flight).  The first two loads are issued before the mode is
-        // known; dynamic mode drops them.
-        Tile b0, b1, b2;
-        b0.set_slot(0);
-        b1.set_slot(1);
-        b2.set_slot(2);
-        uint32_t t = blockIdx.x;
-        b0.load(a, t);
-        if (t + G < n) b1.load(a, t + G);
-        uint32_t epoch = 0, mode = kModeStatic;
-        if (chained) {
-            if (threadIdx.x == 0) sm.mode = decide_mode(hdr, G, a.pipe.mode_limit);
-            __syncthreads();
-            epoch = sm.epoch;
-            mode = sm.mode;
-        }
-
-        if (mode == kModeStatic) {
-            scan_publish(b0, a, t, sm, desc, epoch);
-            for (;;) {
-                if (!step(b0, b1, b2, a, t, sm, hdr, desc, epoch)) break;
-                t += G;
-                if (!step(b1, b2, b0, a, t, sm, hdr, desc, epoch)) break;
-                t += G;
-                if (!step(b2, b0, b1, a, t, sm, hdr, desc, epoch)) break;
-                t += G;
-            }
-            if (chained && blockIdx.x == (n - 1) % G)
-                end_call_static(hdr, G, epoch, a.pipe.words_used, a.pipe.ws_words, desc, a.pipe.spin_limit,
-                                sm.clear_end);
-            return;
-        }
-
-        // Dynamic mode: one tile at a time, claimed in order.  Every
-        // workgroup makes exactly one claim past the last tile, so the holder
-        // of ticket n + G - 1 knows all others are done with the header.
-        for (;;) {
-            if (threadIdx.x == 0)
-                sm.ticket = __hip_atomic_fetch_add(&hdr->claim, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __syncthreads();
-            const uint32_t tk = sm.ticket;
-            if (tk >= n) {
-                if (tk == n + G - 1) end_call(hdr, epoch, a.pipe.words_used, a.pipe.ws_words, desc, sm.clear_end);
-                break;
-            }
-            b0.load(a, tk);
-            scan_publish(b0, a, tk, sm, desc, epoch);
-            finish(b0, a, tk, sm, hdr, desc, epoch);
-        }
-    }
 };
 
 // The pipeline with a control wave and deferred emission, for policies whose
