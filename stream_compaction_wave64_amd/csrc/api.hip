@@ -267,10 +267,12 @@ int plan_columns(scan_dtype_t dt, scan_op_t op, int64_t outer, int64_t len, int6
     p.rows = 1;
     p.width = 1;
     p.col_strips = (inner + 256 * p.vec - 1) / (256 * p.vec);
-    int64_t chunks = (2048 + p.col_strips * outer - 1) / (p.col_strips * outer);
+    // about 512 workgroups, chunks of at least 16 rows, at most 256 chunks
+    // (the partials kernel's LDS block)
+    int64_t chunks = (512 + p.col_strips * outer - 1) / (p.col_strips * outer);
     int64_t rows = (len + chunks - 1) / chunks;
     if (rows < 16) rows = 16;
-    if (rows * 1024 < len) rows = (len + 1023) / 1024;
+    if (rows * 256 < len) rows = (len + 255) / 256;
     p.col_rows = rows;
     p.col_chunks = (len + rows - 1) / rows;
     const int64_t wgs = outer * p.col_chunks * p.col_strips;

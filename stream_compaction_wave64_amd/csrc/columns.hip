@@ -12,8 +12,8 @@
 // of a strip is one coalesced 128-bit access per thread.
 //   1. reduce: each thread folds its columns over the chunk's R rows into one
 //      partial per column (carry type);
-//   2. partials: for every column, an exclusive scan over the chunks (one
-//      thread per chunk, a workgroup scan across them);
+//   2. partials: for every column, an exclusive scan over the chunks
+//      (columns in groups of 32, transposed through LDS);
 //   3. rescan: each thread runs down its columns again from the chunk's base
 //      and writes the outputs, then zeroes its partials (the workspace's
 //      descriptor area must be left zeroed).
@@ -51,6 +51,7 @@ __global__ __launch_bounds__(kColThreads) void k_col_reduce(ColArgs a) {
     for (int v = 0; v < V; v++) acc[v] = Op::template identity<C>();
     // V > 1 only when inner is a multiple of V with 16-byte aligned rows, so
     // a thread's V columns are one aligned 128-bit access per row.
+#pragma unroll 8
     for (int64_t r = r0; r < r1; r++) {
         const T *p = src + r * a.inner;
         if constexpr (V > 1) {
@@ -66,36 +67,50 @@ __global__ __launch_bounds__(kColThreads) void k_col_reduce(ColArgs a) {
     for (int v = 0; v < V; v++) part[v] = acc[v];
 }
 
-// One workgroup per (outer, group of V columns); thread t is chunk t (the
-// host guarantees chunks <= blockDim.x <= 1024).  Exclusive scan over the
-// chunks with the wave scan and one LDS slot per wave.
-template <class T, class Op, int V>
-__global__ __launch_bounds__(1024) void k_col_partials(ColArgs a) {
+// Partials: per (outer, column), an exclusive scan over the chunks.  A
+// workgroup takes kColGroup adjacent columns of one outer slice: it reads the
+// [chunks][kColGroup] block of partials with consecutive lanes on consecutive
+// columns (rows of the block are contiguous), scans each column in LDS with
+// kColSegs threads per column (each serial over a run of chunks, then the
+// run totals combined), and writes the exclusive prefixes back the same way.
+// The host keeps chunks <= kColMaxChunks.
+constexpr int kColGroup = 32, kColSegs = kColThreads / kColGroup, kColMaxChunks = 256;
+
+template <class T, class Op>
+__global__ __launch_bounds__(kColThreads) void k_col_partials(ColArgs a) {
     using C = typename Carry<T, Op>::type;
-    __shared__ C tot[16][V];
-    const int64_t groups = (a.inner + V - 1) / V;
+    __shared__ C blk[kColMaxChunks][kColGroup + 1];  // +1: column-wise walks hit distinct banks
+    __shared__ C seg[kColSegs][kColGroup];
+    const int64_t groups = (a.inner + kColGroup - 1) / kColGroup;
     const uint32_t o = uint32_t(blockIdx.x / groups);
-    const int64_t col = int64_t(blockIdx.x % groups) * V;
-    const uint32_t c = threadIdx.x;
+    const int64_t col0 = int64_t(blockIdx.x % groups) * kColGroup;
+    const int ncol = int(a.inner - col0 < kColGroup ? a.inner - col0 : kColGroup);
+    const int nch = int(a.chunks);
     const C id = Op::template identity<C>();
-    C *part = reinterpret_cast<C *>(a.partials) + int64_t(o) * a.chunks * a.inner + col;
-    C x[V], inc[V];
-#pragma unroll
-    for (int v = 0; v < V; v++) x[v] = (c < a.chunks) ? part[int64_t(c) * a.inner + v] : id;
-    const int wave = threadIdx.x / kWave, waves = blockDim.x / kWave;
-#pragma unroll
-    for (int v = 0; v < V; v++) inc[v] = wave_scan_incl<Op>(x[v]);
-    if (lane_id() == kWave - 1) {
-#pragma unroll
-        for (int v = 0; v < V; v++) tot[wave][v] = inc[v];
+    C *part = reinterpret_cast<C *>(a.partials) + int64_t(o) * a.chunks * a.inner + col0;
+    for (int i = threadIdx.x; i < nch * kColGroup; i += kColThreads) {
+        const int c = i / kColGroup, k = i % kColGroup;
+        blk[c][k] = k < ncol ? part[int64_t(c) * a.inner + k] : id;
     }
     __syncthreads();
-#pragma unroll
-    for (int v = 0; v < V; v++) {
-        C base = id;
-        for (int w = 0; w < waves && w < wave; w++) base = Op::apply(base, tot[w][v]);
-        const C ex = Op::apply(base, wave_shr1(id, inc[v]));
-        if (c < a.chunks) part[int64_t(c) * a.inner + v] = ex;
+    const int k = threadIdx.x % kColGroup, sgi = threadIdx.x / kColGroup;
+    const int per = (nch + kColSegs - 1) / kColSegs;
+    const int c0 = sgi * per, c1 = c0 + per < nch ? c0 + per : nch;
+    C run = id;
+    for (int c = c0; c < c1; c++) run = Op::apply(run, blk[c][k]);
+    seg[sgi][k] = run;
+    __syncthreads();
+    C ex = id;
+    for (int g = 0; g < sgi; g++) ex = Op::apply(ex, seg[g][k]);
+    for (int c = c0; c < c1; c++) {
+        const C x = blk[c][k];
+        blk[c][k] = ex;
+        ex = Op::apply(ex, x);
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < nch * kColGroup; i += kColThreads) {
+        const int c = i / kColGroup, kk = i % kColGroup;
+        if (kk < ncol) part[int64_t(c) * a.inner + kk] = blk[c][kk];
     }
 }
 
@@ -117,6 +132,7 @@ __global__ __launch_bounds__(kColThreads) void k_col_rescan(ColArgs a) {
         run[v] = part[v];
         part[v] = C{};  // leave the workspace zeroed
     }
+#pragma unroll 8
     for (int64_t r = r0; r < r1; r++) {
         const T *p = src + r * a.inner;
         T *q = dst + r * a.inner;
@@ -143,9 +159,9 @@ static int launch_columns_impl(const ColArgs &a, hipStream_t s) {
     const uint32_t wgs = a.outer * a.chunks * a.strips;
     hipLaunchKernelGGL((k_col_reduce<T, Op, V>), dim3(wgs), dim3(kColThreads), 0, s, a);
     if (hipGetLastError() != hipSuccess) return SCAN_ERR_HIP;
-    const int64_t groups = (a.inner + V - 1) / V;
-    const uint32_t pthreads = ((a.chunks + kWave - 1) / kWave) * kWave;
-    hipLaunchKernelGGL((k_col_partials<T, Op, V>), dim3(uint32_t(a.outer * groups)), dim3(pthreads), 0, s, a);
+    if (a.chunks > uint32_t(kColMaxChunks)) return SCAN_ERR_UNSUPPORTED;
+    const int64_t groups = (a.inner + kColGroup - 1) / kColGroup;
+    hipLaunchKernelGGL((k_col_partials<T, Op>), dim3(uint32_t(a.outer * groups)), dim3(kColThreads), 0, s, a);
     if (hipGetLastError() != hipSuccess) return SCAN_ERR_HIP;
     hipLaunchKernelGGL((k_col_rescan<T, Op, V>), dim3(wgs), dim3(kColThreads), 0, s, a);
     return hipGetLastError() == hipSuccess ? SCAN_OK : SCAN_ERR_HIP;

@@ -95,7 +95,7 @@ struct ColArgs {
     int64_t len;
     int64_t inner;
     int64_t rows;             // rows per chunk (R)
-    uint32_t chunks;          // chunks per column (<= 1024)
+    uint32_t chunks;          // chunks per column (<= 256)
     uint32_t strips;          // column strips
     int32_t exclusive;
     void *partials;           // outer * chunks * inner carry values, in the workspace
