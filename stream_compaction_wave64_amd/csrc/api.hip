@@ -140,25 +140,25 @@ struct TilePlan {
     int64_t col_rows, col_chunks, col_strips;  // column kernel
 };
 
-// Shape of a tile: the default (512 threads x 8 rows of 128-bit vectors, 4
-// rows for 8-byte elements), or block_size / items_per_thread from the
+// Shape of a tile: the caller's default (block_default threads x rows_default
+// rows of 128-bit vectors), or block_size / items_per_thread from the
 // tuning.  The element-wide fallback (misaligned data or a length that
 // breaks the vector alignment) is built for the default and one-row shapes:
 // a tuned shape snaps to the nearer.  Kernels with a control wave (`ctrl`)
 // give the tile block - 64 threads.
 template <class Find>
 int plan_shape(int esize, bool vec_ok, const scan_tuning_t &tu, TilePlan &p, Find find, bool ctrl,
-               int rows_default) {
+               int rows_default, int block_default) {
     const int vmax = 16 / esize;
     p.vec = vec_ok ? vmax : 1;
-    p.block = tu.block_size > 0 ? tu.block_size : kDefaultBlock;
+    p.block = tu.block_size > 0 ? tu.block_size : block_default;
     int ipt = tu.items_per_thread > 0 ? tu.items_per_thread : rows_default * vmax;
     if (p.vec == 1 && tu.items_per_thread <= 0) ipt = rows_default;
     if (ipt % p.vec != 0) return SCAN_ERR_UNSUPPORTED;
     p.rows = ipt / p.vec;
     if (p.vec == 1 && !find(p.block, p.rows, 1)) {
         p.rows = p.rows >= rows_default ? rows_default : 1;
-        p.block = p.rows == 1 ? 256 : kDefaultBlock;
+        p.block = p.rows == 1 ? 256 : block_default;
     }
     if (!find(p.block, p.rows, p.vec)) return SCAN_ERR_UNSUPPORTED;
     p.tile = int64_t(ctrl ? p.block - 64 : p.block) * p.rows * p.vec;
@@ -171,23 +171,26 @@ int plan_scan(scan_dtype_t dt, scan_op_t op, int64_t outer, int64_t len, bool al
     const bool rts = tu.algo == SCAN_ALGO_REDUCE_THEN_SCAN;
     if (rts && outer != 1) return SCAN_ERR_UNSUPPORTED;  // reduce-then-scan: whole arrays only
     const bool vec_ok = aligned && len % (16 / esize) == 0;
-    // default rows: reduce-then-scan 8 (4 for 8-byte elements); look-back 10
-    // (8), its tiles bounded by the two LDS stashes of the pipeline
+    // default shapes: reduce-then-scan 512 threads x 8 rows (4 for 8-byte
+    // elements); look-back 768 x 7 (512 x 8 for 8-byte elements), its tiles
+    // bounded by the two LDS stashes of the pipeline
     int rc = rts ? plan_shape(
                        esize, vec_ok, tu, p,
                        [&](int b, int r, int v) { return find_rts(dt, op, b, r, v) != nullptr; }, false,
-                       esize == 8 ? 4 : 8)
+                       esize == 8 ? 4 : 8, kDefaultBlock)
                  : plan_shape(
                        esize, vec_ok, tu, p,
                        [&](int b, int r, int v) { return find_lookback(dt, op, b, r, v) != nullptr; }, true,
-                       esize == 8 ? 8 : 10);
+                       esize == 8 ? 8 : 7, esize == 8 ? kDefaultBlock : 768);
     if (rc != SCAN_OK) return rc;
     if (!rts && tu.block_size <= 0 && tu.items_per_thread <= 0 && len < p.tile) {
-        // Short segments: the fewest rows whose tile holds a whole segment, so
-        // each segment is one tile (no look-back) with little of it idle.
+        // Short segments: the fewest rows of a 512-thread tile that hold a
+        // whole segment, so each segment is one tile (no look-back) with
+        // little of it idle.
         for (int r : {1, 2, 3, 5}) {
-            const int64_t t = int64_t(p.block - 64) * r * p.vec;
-            if (r < p.rows && t >= len && find_lookback(dt, op, p.block, r, p.vec) != nullptr) {
+            const int64_t t = int64_t(kDefaultBlock - 64) * r * p.vec;
+            if (t < p.tile && t >= len && find_lookback(dt, op, kDefaultBlock, r, p.vec) != nullptr) {
+                p.block = kDefaultBlock;
                 p.rows = r;
                 p.tile = t;
                 break;
@@ -291,7 +294,8 @@ int plan_compact(scan_dtype_t dt, int64_t n, bool aligned, const scan_tuning_t &
     // 128-bit loads need 16-byte aligned x and whole vectors up to n
     const int rc = plan_shape(
         4, aligned && n % 4 == 0, tu, p,
-        [&](int b, int r, int v) { return find_compact(dt, SCAN_CMP_GT, b, r, v) != nullptr; }, true, 8);
+        [&](int b, int r, int v) { return find_compact(dt, SCAN_CMP_GT, b, r, v) != nullptr; }, true, 8,
+        kDefaultBlock);
     if (rc != SCAN_OK) return rc;
     p.kernel = SCAN_KERNEL_COMPACT;
     p.tiles_per_seg = p.num_tiles = (n + p.tile - 1) / p.tile;

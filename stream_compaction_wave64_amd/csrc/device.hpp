@@ -220,13 +220,22 @@ struct Desc {
             __hip_atomic_store(d + i, tag | c.w[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 
+    // The words of one descriptor, loaded (decode() reads them later).
+    __device__ __forceinline__ static void fetch(const uint64_t *d, uint64_t (&w)[kWords]) {
+#pragma unroll
+        for (int i = 0; i < kWords; i++)
+            w[i] = __hip_atomic_load(d + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+
     // kStateA / kStateP when all words carry that state of `epoch`, 0
     // otherwise (not yet published, or caught between two word writes).
     __device__ __forceinline__ static uint32_t read(const uint64_t *d, uint32_t epoch, C &value) {
         uint64_t w[kWords];
-#pragma unroll
-        for (int i = 0; i < kWords; i++)
-            w[i] = __hip_atomic_load(d + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        fetch(d, w);
+        return decode(w, epoch, value);
+    }
+
+    __device__ __forceinline__ static uint32_t decode(const uint64_t (&w)[kWords], uint32_t epoch, C &value) {
         const uint32_t state = desc_state(w[0], epoch);
         bool ok = state != 0u;
         Chunks c;
@@ -246,10 +255,17 @@ struct DescTrunc {
         __hip_atomic_store(d, desc_tag(epoch, state) | (__builtin_bit_cast(uint64_t, value) >> (64 - kTagShift)),
                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+    __device__ __forceinline__ static void fetch(const uint64_t *d, uint64_t (&w)[1]) {
+        w[0] = __hip_atomic_load(d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __device__ __forceinline__ static uint32_t decode(const uint64_t (&w)[1], uint32_t epoch, double &value) {
+        value = __builtin_bit_cast(double, w[0] << (64 - kTagShift));
+        return desc_state(w[0], epoch);
+    }
     __device__ __forceinline__ static uint32_t read(const uint64_t *d, uint32_t epoch, double &value) {
-        const uint64_t w = __hip_atomic_load(d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        value = __builtin_bit_cast(double, w << (64 - kTagShift));
-        return desc_state(w, epoch);
+        uint64_t w[1];
+        fetch(d, w);
+        return decode(w, epoch, value);
     }
 };
 
@@ -459,6 +475,77 @@ __device__ __forceinline__ C lookback(const uint64_t *desc, uint32_t epoch, int6
     }
     return excl;
 }
+
+// Look-back of the static order by aggregates only (an MI355X design).  The
+// page's look-back finds a predecessor's inclusive prefix, so the prefixes
+// form a chain through the workgroups of a round: with 64 predecessors per
+// round trip, the last of G = 256 workgroups needs four dependent round
+// trips.  In the static order workgroup w owns tiles w, w + G, ..., so it
+// already knows the inclusive prefix of its own previous tile t - G; tile
+// t's exclusive prefix is that value combined with the aggregates of the
+// G - 1 tiles between them, which their owners published a step or more
+// earlier.  One round trip, which issue() starts and finish() completes
+// after the caller's other work, and no tile waits for another's prefix.
+// The G - 1 reads per tile (64 * NR at most) are the price.
+//
+// Slot (lane, k) reads tile lo + lane + 64k for tiles in [lo, hi).  A slot
+// still X at finish() is re-read until published; after `spin_limit` polls
+// the wave flags kErrSpin and counts it as the identity, so the wait always
+// ends.  Operators must be commutative (slots combine in lane order).
+template <class C, class D, int NR>
+struct GapRead {
+    uint64_t w[NR][D::kWords];
+    int64_t lo, hi;
+
+    __device__ __forceinline__ void issue(const uint64_t *desc, int64_t lo_, int64_t hi_) {
+        lo = lo_;
+        hi = hi_;
+#pragma unroll
+        for (int k = 0; k < NR; k++) {
+            const int64_t p = lo + lane_id() + int64_t(kWave) * k;
+            if (p < hi) D::fetch(desc + p * D::kWords, w[k]);
+        }
+    }
+
+    // The combination of the aggregates of [lo, hi), the same in every lane.
+    template <class Op>
+    __device__ __forceinline__ C finish(const uint64_t *desc, uint32_t epoch, WsHeader *hdr, uint32_t spin_limit) {
+        const C id = Op::template identity<C>();
+        C acc = id;
+        uint32_t pending = 0;  // bit k: slot k not yet published
+#pragma unroll
+        for (int k = 0; k < NR; k++) {
+            const int64_t p = lo + lane_id() + int64_t(kWave) * k;
+            C v;
+            if (p < hi) {
+                if (D::decode(w[k], epoch, v) != 0u)
+                    acc = Op::apply(v, acc);
+                else
+                    pending |= 1u << k;
+            }
+        }
+        for (uint32_t polls = 0; __ballot(pending != 0u) != 0ull; polls++) {
+            if (polls >= spin_limit) {
+                if (lane_id() == 0) flag_error(hdr, kErrSpin);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+            for (int k = 0; k < NR; k++) {
+                if (pending & (1u << k)) {
+                    const int64_t p = lo + lane_id() + int64_t(kWave) * k;
+                    C v;
+                    D::fetch(desc + p * D::kWords, w[k]);
+                    if (D::decode(w[k], epoch, v) != 0u) {
+                        acc = Op::apply(v, acc);
+                        pending &= ~(1u << k);
+                    }
+                }
+            }
+        }
+        return wave_reduce<Op>(acc);
+    }
+};
 
 // ---------------------------------------------------------- vector access --
 

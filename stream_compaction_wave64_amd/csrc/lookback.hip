@@ -105,13 +105,13 @@ static int launch_lookback_impl(const ScanArgs &a, uint32_t grid_cap, hipStream_
 }
 
 // Instantiated (block, rows) shapes, block counting the control wave.
-// Every type gets the default shape -- 512 threads (448 data threads) x 10
-// rows of 128-bit vectors for 4-byte elements (70 KiB per tile), x 8 rows for
-// 8-byte elements (56 KiB): the largest tiles whose two LDS stashes fit the
+// Every type gets a default shape -- 768 threads (704 data threads) x 7 rows
+// of 128-bit vectors for 4-byte elements (77 KiB per tile), 512 threads (448)
+// x 8 rows for 8-byte elements (56 KiB): tiles whose two LDS stashes fit the
 // 160 KiB of LDS, measured fastest on MI355X -- and a one-row shape (small
-// tiles, used to force many tiles at small n), and 1, 2, 3 and 5 rows, which
-// the planner picks so that one tile holds a whole short segment.  fp32 sum
-// also gets the shapes the tuning sweep visits.
+// tiles, used to force many tiles at small n), and 512-thread shapes of 1,
+// 2, 3 and 5 rows, which the planner picks so that one tile holds a whole
+// short segment.  fp32 sum also gets the shapes the tuning sweep visits.
 template <class T, class Op, int V>
 static LbLaunch pick_shape(int block, int rows) {
 #define SW64_SHAPE(B, R) \
@@ -122,7 +122,7 @@ static LbLaunch pick_shape(int block, int rows) {
     SW64_SHAPE(512, 3)
     SW64_SHAPE(512, 5)
     if constexpr (sizeof(T) == 4) {
-        SW64_SHAPE(512, 10)
+        SW64_SHAPE(768, 7)
     } else {
         SW64_SHAPE(512, 8)
     }
@@ -132,7 +132,9 @@ static LbLaunch pick_shape(int block, int rows) {
         SW64_SHAPE(256, 8)
         SW64_SHAPE(512, 4)
         SW64_SHAPE(512, 8)
+        SW64_SHAPE(512, 10)
         SW64_SHAPE(1024, 2)
+        SW64_SHAPE(768, 6)
     }
 #undef SW64_SHAPE
     return nullptr;

@@ -16,6 +16,10 @@
 //    without it the call claims tiles in order from a counter instead.
 //  * A control wave owns the descriptors and the look-back, and scanned
 //    tiles wait in LDS for their prefix (see CtrlPipeline's comment).
+//  * In the static order a workgroup knows the inclusive prefix of its own
+//    previous tile, so for grids of up to kGapGrid workgroups the look-back
+//    reads only the aggregates published since (GapRead in device.hpp):
+//    one round trip per tile and no chain of prefixes through a round.
 #pragma once
 
 #include "device.hpp"
@@ -46,10 +50,10 @@ struct PipeArgs {
 //    aggregates of the whole round have long been published, and the
 //    control wave's look-back for it completes in one round trip while the
 //    data waves stream the next tiles.
-//  * Descriptor reads are what the look-back costs: each poll reads one
-//    window of 64 predecessors (measured: four windows per round trip cost
-//    more HBM time than the extra round trips they save), and fp32 carries
-//    pack into one word per tile (DescTrunc).
+//  * Descriptor reads are what the look-back costs: one round trip per
+//    tile, issued a step before it is needed (GapRead); for larger grids and
+//    in dynamic mode, windows of 64 predecessors per poll.  fp32 carries pack
+//    into one word per tile (DescTrunc).
 //  * On gfx950 a wave's vector memory counter retires loads and stores in
 //    issue order: the control wave holds no tile traffic, so its polls are
 //    never counted behind a tile.
@@ -58,10 +62,13 @@ struct PipeArgs {
 //   data waves:    issue T(s+1)'s loads (the other register tile); scan T(s)
 //                  (barrier 1); barrier 2; emit T(s-2) from its LDS stash
 //                  with the prefix the control wave left; stash T(s).
-//   control wave:  look back for T(s-2), publish its inclusive prefix, leave
-//                  the exclusive prefix in LDS; barrier 1; combine T(s)'s
-//                  per-wave totals into its aggregate and publish it (A, or
-//                  P at a segment start); barrier 2.
+//   control wave:  complete T(s-2)'s look-back and leave its exclusive
+//                  prefix in LDS; barrier 1; combine T(s)'s per-wave totals
+//                  into its aggregate and publish it (A, or P at a segment
+//                  start); start T(s-1)'s look-back reads; barrier 2.  (With
+//                  the windowed look-back, for large grids, T(s-2)'s whole
+//                  look-back runs before barrier 1 and its inclusive prefix
+//                  is published.)
 // Every load a data wave issues is unconditional (a tile past the end loads
 // the array's first vector and discards it), and so is every store of the
 // scan policies (dropped past the end by the buffer resource), so the
@@ -90,6 +97,8 @@ struct CtrlPipeline {
     static constexpr int DATA = P::BLOCK;
     static constexpr int THREADS = DATA + kWave;
     static constexpr int kDepth = 1;  // look-back windows of 64 per round trip
+    static constexpr int kGapReads = 8;  // GapRead slots per lane
+    static constexpr uint32_t kGapGrid = kWave * kGapReads + 1;  // largest grid that uses GapRead
     static_assert(DATA % kWave == 0 && THREADS <= 1024, "whole waves");
 
     struct Smem {
@@ -129,6 +138,49 @@ struct CtrlPipeline {
         if (lane_id() == 0) {
             *prefix = pre;
             P::on_resolved(a, tile, pre, agg);
+        }
+    }
+
+    // Static-mode control wave with the aggregate-only look-back (GapRead):
+    // for grids of at most kGapGrid workgroups.  Step s: combine the gap
+    // reads issued one step earlier into T(s-2)'s exclusive prefix;
+    // barrier 1; publish T(s)'s aggregate; issue T(s-1)'s gap reads, whose
+    // aggregates were published a step or more before; barrier 2.  No
+    // inclusive prefix is published, so every word read holds an aggregate
+    // (a segment's first tile publishes its aggregate as P).
+    __device__ __forceinline__ static void ctrl_static_gap(const Args &a, Smem &sm, WsHeader *hdr, uint64_t *desc,
+                                                           uint32_t epoch, uint32_t K) {
+        const uint32_t w = blockIdx.x, G = gridDim.x, tps = a.pipe.tiles_per_seg;
+        const bool chained = tps > 1;
+        const C id = Op::template identity<C>();
+        C agg0 = id, agg1 = id;  // aggregates of T(s-2), T(s-1)
+        C carry = id;            // inclusive prefix of this workgroup's last resolved tile
+        bool use_carry = false;  // the gap being read continues from `carry`
+        GapRead<C, typename P::D, kGapReads> gap;
+        for (uint32_t s = 0; s < K + 2; s++) {
+            if (s >= 2) {
+                const uint32_t t = w + (s - 2) * G;
+                C pre = id;
+                if (chained) {
+                    pre = gap.template finish<Op>(desc, epoch, hdr, a.pipe.spin_limit);
+                    if (use_carry) pre = Op::apply(carry, pre);
+                }
+                carry = Op::apply(pre, agg0);
+                if (lane_id() == 0) {
+                    sm.prefix[s & 1] = pre;
+                    P::on_resolved(a, t, pre, agg0);
+                }
+            }
+            __syncthreads();
+            agg0 = agg1;
+            if (s < K) agg1 = ctrl_publish(a, w + s * G, sm, desc, epoch);
+            if (chained && s >= 1 && s <= K) {
+                const int64_t t = int64_t(w) + int64_t(s - 1) * G;
+                const int64_t first = t - int64_t(uint32_t(t) % tps);  // segment start
+                use_carry = t - int64_t(G) >= first;
+                gap.issue(desc, use_carry ? t - G + 1 : first, t);
+            }
+            __syncthreads();
         }
     }
 
@@ -172,7 +224,10 @@ struct CtrlPipeline {
             __syncthreads();
             const uint32_t epoch = chained ? sm.epoch : 0u;
             const uint32_t mode = chained ? sm.mode : kModeStatic;
-            if (mode == kModeStatic) {
+            if (mode == kModeStatic && G <= kGapGrid) {
+                ctrl_static_gap(a, sm, hdr, desc, epoch, K);
+                end_static(a, sm, hdr, desc, epoch);
+            } else if (mode == kModeStatic) {
                 C agg0 = Op::template identity<C>(), agg1 = agg0;  // aggregates of T(s-2), T(s-1)
                 for (uint32_t s = 0; s < K + 2; s++) {
                     if (s >= 2) ctrl_resolve(a, w + (s - 2) * G, agg0, &sm.prefix[s & 1], hdr, desc, epoch);

@@ -61,6 +61,24 @@ def test_wide_inner_misaligned_and_ragged():
     _check(z, 1)
 
 
+@pytest.mark.parametrize("grid", [64, 300, 0])
+def test_rows_many_tiles_per_row(grid):
+    # rows of 131 one-row tiles: a workgroup's consecutive tiles cross row
+    # (segment) boundaries; grids of 64 and 300 use the aggregate-only
+    # look-back, the resident grid of one-row tiles (above 513) the windowed one
+    rng = np.random.default_rng(93)
+    tuning = {"block_size": 256, "items_per_thread": 4, "grid_blocks": grid}
+    for dt in (np.float32, np.int32):
+        x = rng.integers(-9, 10, (7, 100_000)).astype(dt) if dt == np.int32 else \
+            (2 * rng.random((7, 100_000)) - 1).astype(dt)
+        xd = to_dev(x)
+        for excl in (False, True):
+            r = sw.scan_dim(xd, 1, op="sum", exclusive=excl, tuning=tuning)
+            torch.cuda.synchronize()
+            assert_scan_matches(x.ravel(), to_host(r).ravel(), "sum", excl, dims=(7, 100_000, 1),
+                                what=f"grid={grid} {np.dtype(dt).name} excl={excl}")
+
+
 def test_configs_2d_full_size():
     square, tall, wide = inputs.dims_arrays(seed=3)
     _check(square, 1)   # 4096 x 4096 along rows

@@ -81,6 +81,23 @@ def test_parity_small_persistent_grid(dt, grid):
 
 
 @pytest.mark.parametrize("dt", DTYPES, ids=lambda d: np.dtype(d).name)
+@pytest.mark.parametrize("grid", [513, 514, 0])
+def test_parity_lookback_either_side_of_gap_grid(dt, grid):
+    # grids of up to 513 workgroups use the aggregate-only look-back (each
+    # workgroup reads the G - 1 aggregates since its own previous tile);
+    # larger ones (514, or the resident count of one-row tiles) the windowed
+    # look-back over published prefixes; 1501 tiles either way
+    vec = 16 // np.dtype(dt).itemsize
+    tuning = {"block_size": 256, "items_per_thread": vec, "grid_blocks": grid}
+    n = 192 * vec * 1500 + 3 * vec
+    assert sw.plan("scan", TORCH[np.dtype(dt)], "sum", 1, n, tuning=tuning)["num_tiles"] == 1501
+    for op, seed in (("sum", 11), ("max", 12)):
+        x = _input(dt, n, seed, op)
+        for excl in (False, True):
+            assert_scan_matches(x, _run(x, op, excl, tuning), op, excl, what=f"grid={grid} {op} excl={excl}")
+
+
+@pytest.mark.parametrize("dt", DTYPES, ids=lambda d: np.dtype(d).name)
 def test_parity_misaligned_elementwise(dt):
     for n in (1, 5, 3001, 100_001):
         x = _input(dt, n, 7, "sum")
