@@ -217,7 +217,10 @@ int pack_offsets(const int32_t *counts, int64_t n, int32_t *offsets, void *ws,
 
 /* Count-scan-emit, step 3 (synthetic records): object i writes its
  * offsets[i+1]-offsets[i] records at out[offsets[i] ...]; its j-th record is
- * (i + 1 + j) mod n.  out must hold offsets[n] entries. */
+ * (i + 1 + j) mod n.  offsets must be non-decreasing from offsets[0] >= 0
+ * (as pack_offsets writes them); out must hold offsets[n] entries and needs
+ * only int32 alignment.  Nothing outside out[offsets[0] .. offsets[n]) is
+ * written. */
 int pack_emit_neighbors(const int32_t *offsets, int64_t n, int32_t *out, void *stream);
 
 /* Measurement aid: copy `bytes` (multiple of 16, 16-byte aligned pointers)

@@ -88,6 +88,31 @@ def test_pack_config_1e7_offsets_and_emit():
     assert np.array_equal(to_host(rec)[:total], oracle.pack_emit(ref_off))
 
 
+def test_emit_windows_wrap_and_alignment():
+    # records staged through LDS windows of 4096: one object far longer than
+    # a window, workgroups whose 1024 objects need several windows, counts
+    # that wrap the record value past 2n, object counts that are not a
+    # multiple of 1024; and outputs starting 1..3 elements past 16-byte
+    # alignment, with guard values on both sides that must survive
+    rng = np.random.default_rng(44)
+    cases = [np.array([0, 10_000, 3, 0, 7], np.int32),
+             np.full(3000, 20, np.int32),
+             np.array([5, 7, 2], np.int32),
+             rng.integers(0, 9, 1025).astype(np.int32),
+             rng.integers(0, 40, 5000).astype(np.int32)]
+    for counts in cases:
+        ref_off, total = oracle.pack_offsets(counts)
+        want = oracle.pack_emit(ref_off)
+        off = to_dev(ref_off.astype(np.int32))
+        for shift in (0, 1, 2, 3):
+            buf = torch.full((total + 8,), -5, dtype=torch.int32, device=DEV)
+            sw.pack_emit_neighbors(off, total, out=buf[shift:shift + total])
+            torch.cuda.synchronize()
+            got = to_host(buf)
+            assert np.array_equal(got[shift:shift + total], want), (counts.size, shift)
+            assert (got[:shift] == -5).all() and (got[shift + total:] == -5).all(), (counts.size, shift)
+
+
 def test_pack_edges():
     cases = [np.zeros(1000, np.int32), np.ones(4097, np.int32), np.array([0, 0, 1000, 0], np.int32),
              np.array([5], np.int32), np.array([3, 2, 0, 1, 2], np.int32),
