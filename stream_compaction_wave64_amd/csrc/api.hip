@@ -403,14 +403,15 @@ int scan_common(const void *in, void *out, int64_t outer, int64_t len, int64_t i
     return find_lookback(dt, op, p.block, p.rows, p.vec)(a, grid_cap, stream);
 }
 
-// LDS of the element kernels (ElemTile::lds_bytes in element.hip): the tile
-// in the owner layout, each thread's slots padded to an odd number of
-// accesses, then one slot per wave (up to 8) and component.
+// LDS of the element kernels (ElemTile::lds_bytes_rescan in element.hip):
+// the tile in the owner layout, each thread's slots padded to an odd number
+// of accesses, then one slot per wave (up to 8) and component, then the
+// rescan's W running carries.
 int64_t element_lds_bytes(scan_dtype_t dt, scan_op_t op, const TilePlan &p) {
     const int64_t s = dtype_bytes(dt), lv = p.vec;  // values per access
     const int64_t vpt = int64_t(p.rows) * p.width, upt = vpt / lv;
     const int64_t stride = vpt + (upt % 2 == 0 ? lv : 0);
-    return int64_t(p.block) * stride * s + 8 * int64_t(p.width) * carry_bytes(dt, op);
+    return int64_t(p.block) * stride * s + (8 + 1) * int64_t(p.width) * carry_bytes(dt, op);
 }
 
 void fill_plan(const TilePlan &p, scan_dtype_t dt, scan_op_t op, scan_plan_t *plan) {

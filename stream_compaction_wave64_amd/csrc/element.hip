@@ -45,9 +45,11 @@ struct ElemTile {
     static constexpr int UPT = VPT / LV;    // accesses per thread per tile
     static constexpr int STRIDE = VPT + (UPT % 2 == 0 ? LV : 0);  // LDS values per thread
 
+    // tile + per-wave totals (reduce: in C, rescan: in T) + W carries (rescan)
     static constexpr size_t lds_bytes(int threads) {
         return size_t(threads) * STRIDE * S + size_t(kElemMaxWaves) * W * sizeof(C);
     }
+    static constexpr size_t lds_bytes_rescan(int threads) { return lds_bytes(threads) + W * sizeof(C); }
 
     using Acc = Vec<T, LV>;  // one global access
 
@@ -172,70 +174,79 @@ struct ElemTile {
         }
     }
 
-    // Pass 3: scan each tile of the chunk from the chunk's prefix.
+    // Pass 3: scan each tile of the chunk from the chunk's prefix.  The
+    // tile's values stay in LDS, read twice by their owner thread: once for
+    // its W component totals, once to replace them by their results; only
+    // the W running offsets live in registers, and the chunk's W carries in
+    // LDS, so the pass keeps the occupancy that hides its memory latency.
     __device__ static void rescan(const ElemArgs &a) {
         extern __shared__ __align__(16) char smem[];
         T *lds = reinterpret_cast<T *>(smem);
         T *wt = reinterpret_cast<T *>(smem + size_t(blockDim.x) * STRIDE * S);
+        C *carry = reinterpret_cast<C *>(smem + lds_bytes(int(blockDim.x)));  // W running prefixes
         const uint32_t seg = blockIdx.x / a.chunks, chunk = blockIdx.x % a.chunks;
         const int lane = lane_id(), wave = threadIdx.x / kWave, waves = blockDim.x / kWave;
         const T id = Op::template identity<T>();
         C *part = reinterpret_cast<C *>(a.partials) + (int64_t(seg) * a.chunks + chunk) * W;
-        C carry[W];
-#pragma unroll
-        for (int c = 0; c < W; c++) carry[c] = part[c];
-        __syncthreads();  // every thread has read the prefix
-        if (threadIdx.x < W) part[threadIdx.x] = C{};  // leave the workspace zeroed
+        if (threadIdx.x < W) {
+            carry[threadIdx.x] = part[threadIdx.x];
+            part[threadIdx.x] = C{};  // leave the workspace zeroed
+        }
         int64_t j0;
         const uint32_t nt = tiles_of(a, chunk, j0);
+        T *own = lds + threadIdx.x * STRIDE;
         for (uint32_t k = 0; k < nt; k++) {
             const Geo gi = geo(a, a.in, seg, j0 + k);
-            if (k > 0) __syncthreads();  // previous tile's stores have read LDS
+            __syncthreads();  // carry written; previous tile's stores have read LDS
             load_tile(gi, lds);
             __syncthreads();
-            T v[VPT];
-            read_own(gi, lds, v);
-            // thread-serial inclusive scans of the E elements, per component
-            T run[W];
+            // this thread's component totals (elements past the range: identity)
+            T off[W];
 #pragma unroll
-            for (int c = 0; c < W; c++) run[c] = id;
+            for (int c = 0; c < W; c++) off[c] = id;
 #pragma unroll
-            for (int e = 0; e < E; e++) {
+            for (int q = 0; q < UPT; q++) {
+                const Acc x = *reinterpret_cast<const Acc *>(own + q * LV);
 #pragma unroll
-                for (int c = 0; c < W; c++) {
-                    run[c] = Op::apply(run[c], v[e * W + c]);
-                    v[e * W + c] = run[c];
+                for (int i = 0; i < LV; i++) {
+                    const int idx = q * LV + i, e = idx / W, c = idx % W;
+                    if (int64_t(threadIdx.x) * E + e < gi.valid) off[c] = Op::apply(off[c], x.v[i]);
                 }
             }
-            // wave scans of the thread totals; run[c] becomes the thread's
-            // exclusive offset within its wave
+            // wave scans of the totals: off[c] becomes the thread's exclusive
+            // offset within its wave
 #pragma unroll
             for (int c = 0; c < W; c++) {
-                const T inc = wave_scan_incl<Op>(run[c]);
+                const T inc = wave_scan_incl<Op>(off[c]);
                 if (lane == kWave - 1) wt[wave * W + c] = inc;
-                run[c] = wave_shr1(id, inc);
+                off[c] = wave_shr1(id, inc);
             }
             __syncthreads();
 #pragma unroll
             for (int c = 0; c < W; c++) {
-                T base = id, tot = id;
-                for (int w = 0; w < waves; w++) {
-                    const T t = wt[w * W + c];
-                    if (w < wave) base = Op::apply(base, t);
-                    tot = Op::apply(tot, t);
-                }
-                const T off = Op::apply(base, run[c]);
-                T prev = off;
-#pragma unroll
-                for (int e = 0; e < E; e++) {
-                    const T inc = Op::apply(off, v[e * W + c]);
-                    v[e * W + c] = T(Op::apply(carry[c], C(a.exclusive ? prev : inc)));
-                    prev = inc;
-                }
-                carry[c] = Op::apply(carry[c], C(tot));
+                T base = id;
+                for (int w = 0; w < wave; w++) base = Op::apply(base, wt[w * W + c]);
+                off[c] = Op::apply(base, off[c]);
             }
-            write_own(lds, v);
-            __syncthreads();
+            // results in place: carry (+) inclusive (or exclusive) tile-local value
+#pragma unroll
+            for (int q = 0; q < UPT; q++) {
+                Acc x = *reinterpret_cast<const Acc *>(own + q * LV);
+#pragma unroll
+                for (int i = 0; i < LV; i++) {
+                    const int c = (q * LV + i) % W;
+                    const T inc = Op::apply(off[c], x.v[i]);
+                    x.v[i] = T(Op::apply(carry[c], C(a.exclusive ? off[c] : inc)));
+                    off[c] = inc;
+                }
+                *reinterpret_cast<Acc *>(own + q * LV) = x;
+            }
+            __syncthreads();  // every thread has read the carry and written its results
+            if (threadIdx.x < W) {
+                T tot = id;
+                for (int w = 0; w < waves; w++) tot = Op::apply(tot, wt[w * W + threadIdx.x]);
+                carry[threadIdx.x] = Op::apply(carry[threadIdx.x], C(tot));
+            }
             store_tile(geo(a, a.out, seg, j0 + k), lds);
         }
     }
@@ -287,19 +298,19 @@ static int launch_elem_impl(const ElemArgs &a, int threads, hipStream_t s) {
     using K = ElemTile<T, Op, W, E, LG>;
     if (threads < kWave || threads > kElemMaxThreads || threads % kWave) return SCAN_ERR_UNSUPPORTED;
     const uint32_t blocks = a.outer * a.chunks;
-    const size_t lds = K::lds_bytes(threads);
-    if (lds > 65536) {  // above the default dynamic LDS limit (gfx950 has 160 KiB per workgroup)
+    const size_t lds = K::lds_bytes(threads), lds_r = K::lds_bytes_rescan(threads);
+    if (lds_r > 65536) {  // above the default dynamic LDS limit (gfx950 has 160 KiB per workgroup)
         if (hipFuncSetAttribute(reinterpret_cast<const void *>(&k_elem_reduce<K>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, int(lds)) != hipSuccess ||
             hipFuncSetAttribute(reinterpret_cast<const void *>(&k_elem_rescan<K>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, int(lds)) != hipSuccess)
+                                hipFuncAttributeMaxDynamicSharedMemorySize, int(lds_r)) != hipSuccess)
             return SCAN_ERR_HIP;
     }
     hipLaunchKernelGGL((k_elem_reduce<K>), dim3(blocks), dim3(threads), lds, s, a);
     if (hipGetLastError() != hipSuccess) return SCAN_ERR_HIP;
     hipLaunchKernelGGL((k_elem_partials<T, Op, W>), dim3(a.outer * W), dim3(256), 0, s, a);
     if (hipGetLastError() != hipSuccess) return SCAN_ERR_HIP;
-    hipLaunchKernelGGL((k_elem_rescan<K>), dim3(blocks), dim3(threads), lds, s, a);
+    hipLaunchKernelGGL((k_elem_rescan<K>), dim3(blocks), dim3(threads), lds_r, s, a);
     return hipGetLastError() == hipSuccess ? SCAN_OK : SCAN_ERR_HIP;
 }
 
