@@ -83,7 +83,7 @@ constexpr int kDefaultBlock = 512;  // threads per workgroup of the tiled kernel
 constexpr int kDefaultRtsBlocks = 1024;               // C of reduce-then-scan
 constexpr int64_t kDefaultLocalMem = 64 * 1024;       // LDS budget of the large-element rule
 constexpr int kElemDefaultBlock = 256;                // large elements: start of the rule
-constexpr int64_t kElemChunks = 2048;                 // large elements: workgroups per launch
+constexpr int64_t kElemChunks = 2048;  // large elements: workgroups per launch (<= 2048, the partials pass)
 
 // AcceleratedKernels.jl PR #208, first bullet: an explicit block size is kept
 // as given; an unset one starts at the default and is lowered to the largest

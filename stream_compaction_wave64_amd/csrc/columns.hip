@@ -88,9 +88,18 @@ __global__ __launch_bounds__(kColThreads) void k_col_partials(ColArgs a) {
     const int nch = int(a.chunks);
     const C id = Op::template identity<C>();
     C *part = reinterpret_cast<C *>(a.partials) + int64_t(o) * a.chunks * a.inner + col0;
-    for (int i = threadIdx.x; i < nch * kColGroup; i += kColThreads) {
-        const int c = i / kColGroup, k = i % kColGroup;
-        blk[c][k] = k < ncol ? part[int64_t(c) * a.inner + k] : id;
+    // every load of the block issued before any is used (one round trip)
+    constexpr int kPer = kColMaxChunks * kColGroup / kColThreads;
+    C x[kPer];
+#pragma unroll
+    for (int it = 0; it < kPer; it++) {
+        const int i = it * kColThreads + threadIdx.x, c = i / kColGroup, k = i % kColGroup;
+        x[it] = (c < nch && k < ncol) ? part[int64_t(c) * a.inner + k] : id;
+    }
+#pragma unroll
+    for (int it = 0; it < kPer; it++) {
+        const int i = it * kColThreads + threadIdx.x;
+        if (i < nch * kColGroup) blk[i / kColGroup][i % kColGroup] = x[it];
     }
     __syncthreads();
     const int k = threadIdx.x % kColGroup, sgi = threadIdx.x / kColGroup;

@@ -263,20 +263,28 @@ __global__ __launch_bounds__(kElemMaxThreads) void k_elem_rescan(ElemArgs a) {
 }
 
 // Pass 2: one workgroup per (segment, component) scans the chunk partials
-// into exclusive prefixes: each thread folds a run of consecutive chunks,
-// then a workgroup scan of the runs.
+// into exclusive prefixes: each thread loads a run of up to kElemPartPer
+// consecutive chunks at once (one round trip), folds it, then a workgroup
+// scan of the runs, and writes the run's prefixes back from registers.
+constexpr int kElemPartThreads = 256, kElemPartPer = 8;
+constexpr int kElemMaxChunks = kElemPartThreads * kElemPartPer;
+
 template <class T, class Op, int W>
-__global__ __launch_bounds__(256) void k_elem_partials(ElemArgs a) {
+__global__ __launch_bounds__(kElemPartThreads) void k_elem_partials(ElemArgs a) {
     using C = typename Carry<T, Op>::type;
-    __shared__ C tot[256 / kWave];
+    __shared__ C tot[kElemPartThreads / kWave];
     const uint32_t seg = blockIdx.x / W, comp = blockIdx.x % W;
     C *part = reinterpret_cast<C *>(a.partials) + int64_t(seg) * a.chunks * W + comp;
     const C id = Op::template identity<C>();
-    const uint32_t per = (a.chunks + 255u) / 256u;
+    const uint32_t per = (a.chunks + kElemPartThreads - 1) / kElemPartThreads;  // <= kElemPartPer
     const uint32_t c0 = threadIdx.x * per;
+    C x[kElemPartPer];
+#pragma unroll
+    for (int i = 0; i < kElemPartPer; i++)
+        x[i] = (uint32_t(i) < per && c0 + i < a.chunks) ? part[int64_t(c0 + i) * W] : id;
     C run = id;
-    for (uint32_t i = 0; i < per; i++)
-        if (c0 + i < a.chunks) run = Op::apply(run, part[int64_t(c0 + i) * W]);
+#pragma unroll
+    for (int i = 0; i < kElemPartPer; i++) run = Op::apply(run, x[i]);
     const int wave = threadIdx.x / kWave;
     const C inc = wave_scan_incl<Op>(run);
     if (lane_id() == kWave - 1) tot[wave] = inc;
@@ -284,11 +292,11 @@ __global__ __launch_bounds__(256) void k_elem_partials(ElemArgs a) {
     C base = id;
     for (int w = 0; w < wave; w++) base = Op::apply(base, tot[w]);
     C ex = Op::apply(base, wave_shr1(id, inc));
-    for (uint32_t i = 0; i < per; i++) {
-        if (c0 + i < a.chunks) {
-            const C x = part[int64_t(c0 + i) * W];
+#pragma unroll
+    for (int i = 0; i < kElemPartPer; i++) {
+        if (uint32_t(i) < per && c0 + i < a.chunks) {
             part[int64_t(c0 + i) * W] = ex;
-            ex = Op::apply(ex, x);
+            ex = Op::apply(ex, x[i]);
         }
     }
 }
@@ -297,6 +305,7 @@ template <class T, class Op, int W, int E, int LG>
 static int launch_elem_impl(const ElemArgs &a, int threads, hipStream_t s) {
     using K = ElemTile<T, Op, W, E, LG>;
     if (threads < kWave || threads > kElemMaxThreads || threads % kWave) return SCAN_ERR_UNSUPPORTED;
+    if (a.chunks > uint32_t(kElemMaxChunks)) return SCAN_ERR_UNSUPPORTED;
     const uint32_t blocks = a.outer * a.chunks;
     const size_t lds = K::lds_bytes(threads), lds_r = K::lds_bytes_rescan(threads);
     if (lds_r > 65536) {  // above the default dynamic LDS limit (gfx950 has 160 KiB per workgroup)
@@ -308,7 +317,7 @@ static int launch_elem_impl(const ElemArgs &a, int threads, hipStream_t s) {
     }
     hipLaunchKernelGGL((k_elem_reduce<K>), dim3(blocks), dim3(threads), lds, s, a);
     if (hipGetLastError() != hipSuccess) return SCAN_ERR_HIP;
-    hipLaunchKernelGGL((k_elem_partials<T, Op, W>), dim3(a.outer * W), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_elem_partials<T, Op, W>), dim3(a.outer * W), dim3(kElemPartThreads), 0, s, a);
     if (hipGetLastError() != hipSuccess) return SCAN_ERR_HIP;
     hipLaunchKernelGGL((k_elem_rescan<K>), dim3(blocks), dim3(threads), lds_r, s, a);
     return hipGetLastError() == hipSuccess ? SCAN_OK : SCAN_ERR_HIP;
