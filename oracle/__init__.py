@@ -23,7 +23,7 @@ _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
 OPS = {"sum": 0, "prod": 1, "max": 2, "min": 3}
-CMPS = {"gt": 0, "ge": 1, "lt": 2, "le": 3, "eq": 4, "ne": 5}
+CMPS = {"gt": 0, "ge": 1, "lt": 2, "le": 3, "eq": 4, "ne": 5, "bit_clear": 6, "bit_set": 7}
 
 _lib = None
 
@@ -58,6 +58,13 @@ def _load():
         lib.oracle_compact_f32.restype = i64
         lib.oracle_compact_i32.argtypes = [vp, i64, i32, ctypes.c_int32, vp]
         lib.oracle_compact_i32.restype = i64
+        lib.oracle_compact_u32.argtypes = [vp, i64, i32, ctypes.c_uint32, vp]
+        lib.oracle_compact_u32.restype = i64
+        lib.oracle_partition_f32.argtypes = [vp, i64, i32, ctypes.c_float, vp, vp]
+        lib.oracle_partition_i32.argtypes = [vp, i64, i32, ctypes.c_int32, vp, vp]
+        lib.oracle_partition_u32.argtypes = [vp, i64, i32, ctypes.c_uint32, vp, vp]
+        for name in ("oracle_partition_f32", "oracle_partition_i32", "oracle_partition_u32"):
+            getattr(lib, name).restype = i64
         lib.oracle_pack_offsets.argtypes = [vp, i64, vp]
         lib.oracle_pack_offsets.restype = i64
         lib.oracle_pack_emit.argtypes = [vp, i64, vp]
@@ -120,18 +127,42 @@ def abs_prefix(x: np.ndarray, exclusive: bool = False, dims=None) -> np.ndarray:
     return p.reshape(x.shape)
 
 
+def _threshold(x: np.ndarray, cmp: str, threshold):
+    if cmp.startswith("bit_"):
+        if x.dtype == np.float32:
+            raise TypeError("bit predicates take integer keys")
+        return int(threshold) & 31
+    return float(np.float32(threshold)) if x.dtype == np.float32 else int(threshold)
+
+
 def compact(x: np.ndarray, cmp: str = "gt", threshold=0.5) -> np.ndarray:
-    """Ascending int32 indices i with x[i] <cmp> threshold (in x's precision)."""
+    """Ascending int32 indices i with x[i] <cmp> threshold (in x's precision;
+    bit_clear / bit_set test bit `threshold` of an integer key)."""
     lib = _load()
     x = np.ascontiguousarray(x)
     idx = np.empty(max(x.size, 1), dtype=np.int32)
-    if x.dtype == np.float32:
-        cnt = lib.oracle_compact_f32(_ptr(x), x.size, CMPS[cmp], float(np.float32(threshold)), _ptr(idx))
-    elif x.dtype == np.int32:
-        cnt = lib.oracle_compact_i32(_ptr(x), x.size, CMPS[cmp], int(threshold), _ptr(idx))
-    else:
+    fn = {np.dtype(np.float32): lib.oracle_compact_f32, np.dtype(np.int32): lib.oracle_compact_i32,
+          np.dtype(np.uint32): lib.oracle_compact_u32}.get(x.dtype)
+    if fn is None:
         raise TypeError(x.dtype)
+    cnt = fn(_ptr(x), x.size, CMPS[cmp], _threshold(x, cmp, threshold), _ptr(idx))
     return idx[:cnt].copy()
+
+
+def partition(x: np.ndarray, cmp: str = "gt", threshold=0.5):
+    """Stable partition: (vals, idx, k) with the k elements that satisfy the
+    predicate first, then the others, each part in input order; idx holds
+    each output's source index (int32)."""
+    lib = _load()
+    x = np.ascontiguousarray(x)
+    fn = {np.dtype(np.float32): lib.oracle_partition_f32, np.dtype(np.int32): lib.oracle_partition_i32,
+          np.dtype(np.uint32): lib.oracle_partition_u32}.get(x.dtype)
+    if fn is None:
+        raise TypeError(x.dtype)
+    vals = np.empty(max(x.size, 1), dtype=x.dtype)
+    idx = np.empty(max(x.size, 1), dtype=np.int32)
+    k = fn(_ptr(x), x.size, CMPS[cmp], _threshold(x, cmp, threshold), _ptr(vals), _ptr(idx))
+    return vals[: x.size].copy(), idx[: x.size].copy(), int(k)
 
 
 def pack_offsets(counts: np.ndarray):

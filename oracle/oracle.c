@@ -44,7 +44,7 @@
 #include <string.h>
 
 enum { O_SUM = 0, O_PROD = 1, O_MAX = 2, O_MIN = 3 };
-enum { O_GT = 0, O_GE = 1, O_LT = 2, O_LE = 3, O_EQ = 4, O_NE = 5 };
+enum { O_GT = 0, O_GE = 1, O_LT = 2, O_LE = 3, O_EQ = 4, O_NE = 5, O_BIT_CLEAR = 6, O_BIT_SET = 7 };
 
 /* ---------------------------------------------------------------- int32 -- */
 
@@ -323,6 +323,8 @@ static int keep_f32(int cmp, float v, float t) {
     }
 }
 
+/* Integer keys also take the bit predicates: bit t (0..31) of the key's
+ * 32-bit pattern clear / set -- the one-bit digit of a radix sort pass. */
 static int keep_i32(int cmp, int32_t v, int32_t t) {
     switch (cmp) {
     case O_GT: return v > t;
@@ -330,6 +332,21 @@ static int keep_i32(int cmp, int32_t v, int32_t t) {
     case O_LT: return v < t;
     case O_LE: return v <= t;
     case O_EQ: return v == t;
+    case O_BIT_CLEAR: return (((uint32_t)v >> (t & 31)) & 1u) == 0u;
+    case O_BIT_SET: return (((uint32_t)v >> (t & 31)) & 1u) == 1u;
+    default: return v != t;
+    }
+}
+
+static int keep_u32(int cmp, uint32_t v, uint32_t t) {
+    switch (cmp) {
+    case O_GT: return v > t;
+    case O_GE: return v >= t;
+    case O_LT: return v < t;
+    case O_LE: return v <= t;
+    case O_EQ: return v == t;
+    case O_BIT_CLEAR: return ((v >> (t & 31u)) & 1u) == 0u;
+    case O_BIT_SET: return ((v >> (t & 31u)) & 1u) == 1u;
     default: return v != t;
     }
 }
@@ -347,6 +364,36 @@ int64_t oracle_compact_i32(const int32_t *x, int64_t n, int cmp, int32_t t, int3
         if (keep_i32(cmp, x[i], t)) idx[count++] = (int32_t)i;
     return count;
 }
+
+int64_t oracle_compact_u32(const uint32_t *x, int64_t n, int cmp, uint32_t t, int32_t *idx) {
+    int64_t count = 0;
+    for (int64_t i = 0; i < n; i++)
+        if (keep_u32(cmp, x[i], t)) idx[count++] = (int32_t)i;
+    return count;
+}
+
+/* ------------------------------------------------------------ partition --
+ * Merry, "Prefix sums on GPUs", slide "Other Applications": partitioning
+ * places the objects that satisfy a predicate before the others, and radix
+ * sort is repeated partitioning -- which needs each part to keep the input
+ * order (a stable partition).  Written out: every satisfying element in
+ * increasing index order, then every other element in increasing index
+ * order; vals gets the 32-bit element, idx its source index.  Returns the
+ * number of satisfying elements. */
+#define PARTITION(NAME, T, KEEP)                                                     \
+    int64_t NAME(const T *x, int64_t n, int cmp, T t, T *vals, int32_t *idx) {       \
+        int64_t k = 0;                                                               \
+        for (int64_t i = 0; i < n; i++)                                              \
+            if (KEEP(cmp, x[i], t)) { vals[k] = x[i]; idx[k] = (int32_t)i; k++; }    \
+        int64_t at = k;                                                              \
+        for (int64_t i = 0; i < n; i++)                                              \
+            if (!KEEP(cmp, x[i], t)) { vals[at] = x[i]; idx[at] = (int32_t)i; at++; } \
+        return k;                                                                    \
+    }
+PARTITION(oracle_partition_f32, float, keep_f32)
+PARTITION(oracle_partition_i32, int32_t, keep_i32)
+PARTITION(oracle_partition_u32, uint32_t, keep_u32)
+#undef PARTITION
 
 /* --------------------------------------------------------------- packing --
  * offsets[0] = 0, offsets[i+1] = offsets[i] + counts[i]; returns the total

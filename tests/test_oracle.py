@@ -363,6 +363,81 @@ def test_compaction_closed_forms(oracle_lib):
     assert list(oracle_lib.compact(xi, "gt", 0)) == list(range(6, 11))
 
 
+def test_compaction_bit_predicates(oracle_lib):
+    keys = np.arange(64, dtype=np.uint32)
+    for b in range(6):
+        assert np.array_equal(oracle_lib.compact(keys, "bit_set", b), np.flatnonzero((keys >> b) & 1))
+        assert np.array_equal(oracle_lib.compact(keys, "bit_clear", b), np.flatnonzero(((keys >> b) & 1) == 0))
+    neg = np.array([-1, 0, 5, -8], np.int32)  # bit 31 is the sign bit
+    assert list(oracle_lib.compact(neg, "bit_set", 31)) == [0, 3]
+
+
+# ------------------------------------------------------------- partition
+
+
+def _check_partition(x, pred, vals, idx, k):
+    """Stable partition by the boolean mask `pred` (True first)."""
+    n = x.size
+    assert k == int(pred.sum())
+    assert np.array_equal(np.sort(idx), np.arange(n))           # a permutation
+    assert np.array_equal(vals, x[idx])                           # values follow indices
+    assert pred[idx[:k]].all() and not pred[idx[k:]].any()        # the split
+    assert np.all(np.diff(idx[:k]) > 0) and np.all(np.diff(idx[k:]) > 0)  # each part in order
+
+
+def test_partition_invariants(oracle_lib):
+    x, _ = inputs.compaction_inputs(50_000, seed=6)
+    for cmp, fn in (("gt", np.greater), ("le", np.less_equal), ("eq", np.equal)):
+        vals, idx, k = oracle_lib.partition(x, cmp, 0.5)
+        _check_partition(x, fn(x, np.float32(0.5)), vals, idx, k)
+    rng = np.random.default_rng(7)
+    xi = rng.integers(-1000, 1000, 30_000).astype(np.int32)
+    vals, idx, k = oracle_lib.partition(xi, "lt", 17)
+    _check_partition(xi, xi < 17, vals, idx, k)
+    keys = rng.integers(0, 2 ** 32, 30_000, dtype=np.uint64).astype(np.uint32)
+    for b in (0, 13, 31):
+        vals, idx, k = oracle_lib.partition(keys, "bit_clear", b)
+        _check_partition(keys, ((keys >> np.uint32(b)) & 1) == 0, vals, idx, k)
+    # small: brute force
+    small = x[:200]
+    vals, idx, k = oracle_lib.partition(small, "gt", 0.5)
+    want = [i for i in range(200) if small[i] > 0.5] + [i for i in range(200) if not small[i] > 0.5]
+    assert list(idx) == want and k == sum(1 for v in small if v > 0.5)
+
+
+def test_partition_closed_forms(oracle_lib):
+    n = 1001
+    for x, k_want in ((np.ones(n, np.float32), n), (np.zeros(n, np.float32), 0)):
+        vals, idx, k = oracle_lib.partition(x, "gt", 0.5)
+        assert k == k_want and np.array_equal(idx, np.arange(n)) and np.array_equal(vals, x)
+    alt = np.tile(np.array([0.0, 1.0], np.float32), n)
+    vals, idx, k = oracle_lib.partition(alt, "gt", 0.5)
+    assert k == n
+    assert np.array_equal(idx, np.concatenate([2 * np.arange(n) + 1, 2 * np.arange(n)]))
+    assert np.array_equal(vals, np.concatenate([np.ones(n, np.float32), np.zeros(n, np.float32)]))
+
+
+def test_radix_sort_from_stable_bit_partitions(oracle_lib):
+    # LSD radix sort is repeated stable partitioning by one-bit digits: the
+    # composed permutation must be numpy's stable argsort
+    rng = np.random.default_rng(8)
+    keys = rng.integers(0, 2 ** 32, 5000, dtype=np.uint64).astype(np.uint32)
+    keys[::7] = keys[3]                                           # many equal keys
+    cur, perm = keys.copy(), np.arange(keys.size)
+    for b in range(32):
+        cur, idx, _ = oracle_lib.partition(cur, "bit_clear", b)
+        perm = perm[idx]
+    assert np.array_equal(cur, np.sort(keys))
+    assert np.array_equal(perm, np.argsort(keys, kind="stable"))
+    # signed keys: the sign bit's pass puts set bits (negatives) first
+    sk = rng.integers(-2 ** 31, 2 ** 31, 5000, dtype=np.int64).astype(np.int32)
+    cur, perm = sk.copy(), np.arange(sk.size)
+    for b in range(32):
+        cur, idx, _ = oracle_lib.partition(cur, "bit_set" if b == 31 else "bit_clear", b)
+        perm = perm[idx]
+    assert np.array_equal(cur, np.sort(sk)) and np.array_equal(perm, np.argsort(sk, kind="stable"))
+
+
 # ---------------------------------------------------------------- packing
 
 

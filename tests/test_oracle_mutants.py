@@ -33,6 +33,13 @@ MUTANTS = {
         "if (!exclusive) { p[at] = acc; acc += fabs((double)x[at]); }"),
     "compaction off by one": ("idx[count++] = (int32_t)i;", "idx[count++] = (int32_t)(i + 1);"),
     "compaction > taken as >=": ("case O_GT: return v > t;", "case O_GT: return v >= t;"),
+    "partition rejected part not offset by k": (
+        "int64_t at = k;                                                              \\",
+        "int64_t at = 0;                                                              \\"),
+    "partition keeps the rejected part's order reversed": (
+        "for (int64_t i = 0; i < n; i++)                                              \\\n            if (!KEEP",
+        "for (int64_t i = n - 1; i >= 0; i--)                                         \\\n            if (!KEEP"),
+    "bit predicate tests the next bit": ("return ((v >> (t & 31u)) & 1u) == 0u;", "return ((v >> ((t + 1) & 31u)) & 1u) == 0u;"),
     "pack offsets shifted": ("offsets[i + 1] = (int32_t)run;", "offsets[i] = (int32_t)run;"),
     "emit record drops the +1": ("(int32_t)((i + 1 + j) % n)", "(int32_t)((i + j) % n)"),
     "block rule without the per-thread totals": ("2 * b * esize > budget", "b * esize > budget"),
@@ -56,6 +63,10 @@ PINS = [
     lambda o: T.test_compaction_brute_and_numpy(o),
     lambda o: T.test_compaction_closed_forms(o),
     lambda o: T.test_pack_offsets_and_emit(o),
+    lambda o: T.test_compaction_bit_predicates(o),
+    lambda o: T.test_partition_invariants(o),
+    lambda o: T.test_partition_closed_forms(o),
+    lambda o: T.test_radix_sort_from_stable_bit_partitions(o),
 ]
 
 
