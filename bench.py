@@ -188,6 +188,20 @@ def _rows(dev, lib, binding, inputs):
     rows.append(_Row("compact_fp32_gt_half_1e7", "compaction of 1e7 fp32 uniform [0,1) with x > 0.5, seed 4",
                      n, 4 * n + 4 * kept + 4, 4 * n + 4 * kept, make_compact))
 
+    ws_q = ws_for("partition", torch.float32, "sum", 1, n, 1)
+
+    def make_partition(k):
+        x = x0 if k == 0 else x0.clone()
+        vals = torch.empty(n, dtype=torch.float32, device=dev)
+        idx = torch.empty(n, dtype=torch.int32, device=dev)
+        cnt = torch.empty(1, dtype=torch.int32, device=dev)
+        return (lambda s: lib.partition_if(vp(x), n, 3, 0, 0.5, vp(vals), vp(idx), vp(cnt), vp(ws_q), ws_q.numel(),
+                                           null, s)), [vals, idx, cnt]
+    # algorithmic bytes: one read of x, the values and their source indices
+    # written once (the count pass's second read of x is not counted)
+    rows.append(_Row("partition_fp32_gt_half_1e7", "stable partition of 1e7 fp32 uniform [0,1) by x > 0.5: "
+                     "values and source indices (2 launches), seed 4", n, 12 * n + 4, 12 * n, make_partition))
+
     c0 = torch.from_numpy(counts).to(dev)
     total = int(counts.sum(dtype=np.int64))
     ws_p = ws_for("pack", torch.int32, "sum", 1, n, 1)

@@ -14,7 +14,8 @@
  *  - scans along one dimension and of large element types, with the block
  *    size lowered to fit a local-memory budget: AcceleratedKernels.jl PR
  *    #208 ("Fit the scans' tiles in local memory for large element types");
- *  - stream compaction and count-scan-emit packing: Merry's slides "Output
+ *  - stream compaction, stable partitioning (one pass of a radix sort by a
+ *    one-bit digit) and count-scan-emit packing: Merry's slides "Output
  *    Format", "Solution" and "Other Applications".
  *
  * Conventions for every entry point:
@@ -91,7 +92,9 @@ typedef enum {
     SCAN_CMP_LT = 2,
     SCAN_CMP_LE = 3,
     SCAN_CMP_EQ = 4,
-    SCAN_CMP_NE = 5
+    SCAN_CMP_NE = 5,
+    SCAN_CMP_BIT_CLEAR = 6,  /* integer keys: bit `threshold` (0..31) of the 32-bit pattern is 0 */
+    SCAN_CMP_BIT_SET = 7     /* integer keys: that bit is 1 */
 } scan_cmp_t;
 
 enum {
@@ -133,7 +136,8 @@ typedef enum {
     SCAN_KERNEL_ELEMENT = 3,    /* element = `inner` components, staged through LDS */
     SCAN_KERNEL_COLUMNS = 4,    /* wide inner extent: column strips, chunked rows */
     SCAN_KERNEL_COMPACT = 5,    /* fused predicate + scan + scatter */
-    SCAN_KERNEL_PACK = 6        /* exclusive int32 scan + total */
+    SCAN_KERNEL_PACK = 6,       /* exclusive int32 scan + total */
+    SCAN_KERNEL_PARTITION = 7   /* count pass, then fused predicate + scan + two-sided scatter */
 } scan_kernel_t;
 
 typedef struct {
@@ -154,7 +158,8 @@ typedef struct {
 typedef enum {
     SCAN_CALL_SCAN = 0,        /* scan_inclusive / scan_exclusive / scan_dim */
     SCAN_CALL_COMPACT = 1,     /* compact_if (dtype = x dtype) */
-    SCAN_CALL_PACK = 2         /* pack_offsets (dtype must be SCAN_I32) */
+    SCAN_CALL_PACK = 2,        /* pack_offsets (dtype must be SCAN_I32) */
+    SCAN_CALL_PARTITION = 3    /* partition_if (dtype = x dtype) */
 } scan_call_t;
 
 /* Host only: the launch a call with these arguments would enqueue. */
@@ -200,13 +205,31 @@ int scan_dim(const void *in, void *out, int64_t outer, int64_t len, int64_t inne
 
 /* Stream compaction: writes, in increasing order, every 0-based index i with
  * x[i] <cmp> threshold to out_idx, and the number written to *d_count (a
- * device int32).  x_dtype is SCAN_F32 or SCAN_I32; the threshold is
- * converted to x's type once and compared in that precision.  out_idx must
- * hold n entries (the worst case).  n > INT32_MAX -> SCAN_ERR_OVERFLOW.
- * n == 0 writes *d_count = 0. */
+ * device int32).  x_dtype is SCAN_F32, SCAN_I32 or SCAN_U32; the threshold
+ * is converted to x's type once (fp32 rounded, integers clamped to the
+ * type's range and truncated) and compared in that precision.  The bit
+ * predicates take integer keys and a threshold that is a bit index 0..31
+ * (else SCAN_ERR_INVALID_ARG).  out_idx must hold n entries (the worst
+ * case).  n > INT32_MAX -> SCAN_ERR_OVERFLOW.  n == 0 writes *d_count = 0. */
 int compact_if(const void *x, int64_t n, scan_dtype_t x_dtype, scan_cmp_t cmp,
                double threshold, int32_t *out_idx, int32_t *d_count, void *ws,
                size_t ws_bytes, const scan_tuning_t *tuning, void *stream);
+
+/* Stable partition (Merry, "Prefix sums on GPUs", slide "Other
+ * Applications": partitioning puts the objects that satisfy a predicate
+ * before the others; radix sort is repeated partitioning, which needs each
+ * part in input order).  Writes the k elements with x[i] <cmp> threshold to
+ * out_vals[0..k) and the others to out_vals[k..n), each part in increasing
+ * i; out_idx (may be NULL) gets each output's source index i; *d_count = k.
+ * x, out_vals: n 32-bit values of x_dtype (SCAN_F32, SCAN_I32, SCAN_U32);
+ * predicates and threshold as for compact_if.  With SCAN_CMP_BIT_CLEAR and
+ * bit b this is one pass of an LSD radix sort by a one-bit digit.  Two
+ * launches (a count pass, then the scan-and-scatter pass); x must not
+ * overlap the outputs.  n > INT32_MAX -> SCAN_ERR_OVERFLOW; n == 0 writes
+ * *d_count = 0. */
+int partition_if(const void *x, int64_t n, scan_dtype_t x_dtype, scan_cmp_t cmp,
+                 double threshold, void *out_vals, int32_t *out_idx, int32_t *d_count,
+                 void *ws, size_t ws_bytes, const scan_tuning_t *tuning, void *stream);
 
 /* Count-scan-emit, step 2: offsets[i] = counts[0] + ... + counts[i-1] for
  * i <= n (offsets has n + 1 entries; offsets[n] is the total).  Counts must

@@ -20,10 +20,10 @@ LIB_PATH = os.path.join(_HERE, "libscan_wave64.so")
 DTYPES = {torch.int32: 0, torch.uint32: 1, torch.int64: 2, torch.float32: 3, torch.float64: 4}
 OPS = {"sum": 0, "prod": 1, "max": 2, "min": 3}
 ALGOS = {"auto": 0, "lookback": 1, "reduce_then_scan": 2, "rts": 2}
-CMPS = {"gt": 0, "ge": 1, "lt": 2, "le": 3, "eq": 4, "ne": 5}
-CALLS = {"scan": 0, "compact": 1, "pack": 2}
+CMPS = {"gt": 0, "ge": 1, "lt": 2, "le": 3, "eq": 4, "ne": 5, "bit_clear": 6, "bit_set": 7}
+CALLS = {"scan": 0, "compact": 1, "pack": 2, "partition": 3}
 KERNELS = {0: "none", 1: "lookback", 2: "reduce_then_scan", 3: "element", 4: "columns", 5: "compact",
-           6: "pack"}
+           6: "pack", 7: "partition"}
 
 
 class ScanError(RuntimeError):
@@ -48,7 +48,7 @@ class Plan(ctypes.Structure):
 
 
 EXPORTS = ["scan_plan", "scan_workspace_bytes", "scan_workspace_init", "scan_workspace_error", "scan_inclusive",
-           "scan_exclusive", "scan_dim", "compact_if", "pack_offsets", "pack_emit_neighbors",
+           "scan_exclusive", "scan_dim", "compact_if", "partition_if", "pack_offsets", "pack_emit_neighbors",
            "scan_copy", "scan_status_string", "scan_version"]
 
 _lib = None
@@ -78,6 +78,7 @@ def load_library(path: str = LIB_PATH):
             "scan_exclusive": ([vp, vp, i64, i32, i32, i32, vp, sz, tp, vp], i32),
             "scan_dim": ([vp, vp, i64, i64, i64, i32, i32, i32, vp, sz, tp, vp], i32),
             "compact_if": ([vp, i64, i32, i32, ctypes.c_double, vp, vp, vp, sz, tp, vp], i32),
+            "partition_if": ([vp, i64, i32, i32, ctypes.c_double, vp, vp, vp, vp, sz, tp, vp], i32),
             "pack_offsets": ([vp, i64, vp, vp, sz, tp, vp], i32),
             "pack_emit_neighbors": ([vp, i64, vp, vp], i32),
             "scan_copy": ([vp, vp, sz, vp], i32),
@@ -243,6 +244,37 @@ def compact_if(x: torch.Tensor, cmp: str = "gt", threshold: float = 0.5, out=Non
     _check("compact_if", lib.compact_if(x.data_ptr(), n, _dtype(x), CMPS[cmp], float(threshold), out.data_ptr(),
                                         count.data_ptr(), ws.data_ptr(), wsb, _tuning(tuning), _stream(x.device)))
     return out, count
+
+
+def partition_if(x: torch.Tensor, cmp: str = "gt", threshold: float = 0.5, out=None, out_idx=None,
+                 with_idx: bool = True, count=None, tuning=None):
+    """Stable partition of x: the elements with x[i] <cmp> threshold first,
+    then the others, each part in input order.  Returns (out, out_idx,
+    count): out_idx holds each output's source index (None when with_idx is
+    False and no out_idx is given); count is a 1-element int32 device tensor
+    (no synchronisation here).  bit_clear / bit_set test bit `threshold` of
+    an integer key (one pass of an LSD radix sort)."""
+    lib = load_library()
+    _need_cuda(x)
+    n = x.numel()
+    if out is None:
+        out = torch.empty(max(n, 1), dtype=x.dtype, device=x.device)
+    if out_idx is None and with_idx:
+        out_idx = torch.empty(max(n, 1), dtype=torch.int32, device=x.device)
+    if count is None:
+        count = torch.empty(1, dtype=torch.int32, device=x.device)
+    _need_cuda(out, count)
+    if out.dtype != x.dtype or out.numel() < n:
+        raise ValueError("out must match x in dtype and hold n values")
+    if out_idx is not None:
+        _need_cuda(out_idx)
+        if out_idx.dtype != torch.int32 or out_idx.numel() < n:
+            raise ValueError("out_idx must be int32 with n entries")
+    ws, wsb = _workspace_for("partition", x, "sum", 1, n, 1, tuning)
+    _check("partition_if", lib.partition_if(x.data_ptr(), n, _dtype(x), CMPS[cmp], float(threshold), out.data_ptr(),
+                                            out_idx.data_ptr() if out_idx is not None else None, count.data_ptr(),
+                                            ws.data_ptr(), wsb, _tuning(tuning), _stream(x.device)))
+    return out, out_idx, count
 
 
 def pack_offsets(counts: torch.Tensor, out=None, tuning=None) -> torch.Tensor:

@@ -98,7 +98,8 @@ int64_t element_block(int64_t esize, int64_t budget, int64_t explicit_b, int64_t
 
 bool valid_dtype(int dt) { return dt >= SCAN_I32 && dt <= SCAN_F64; }
 bool valid_op(int op) { return op >= SCAN_OP_SUM && op <= SCAN_OP_MIN; }
-bool valid_cmp(int c) { return c >= SCAN_CMP_GT && c <= SCAN_CMP_NE; }
+bool valid_cmp(int c) { return c >= SCAN_CMP_GT && c <= SCAN_CMP_BIT_SET; }
+bool bit_cmp(int c) { return c == SCAN_CMP_BIT_CLEAR || c == SCAN_CMP_BIT_SET; }
 
 int dtype_bytes(scan_dtype_t dt) { return (dt == SCAN_I64 || dt == SCAN_F64) ? 8 : 4; }
 
@@ -306,6 +307,58 @@ int plan_compact(scan_dtype_t dt, int64_t n, bool aligned, const scan_tuning_t &
     return SCAN_OK;
 }
 
+// A bit predicate takes an integer key and a bit index 0..31.
+bool threshold_ok(scan_dtype_t dt, scan_cmp_t cmp, double t) {
+    if (!bit_cmp(cmp)) return true;
+    return dt != SCAN_F32 && t >= 0.0 && t <= 31.0 && t == double(int(t));
+}
+
+// The threshold converted once to x's type (its bit pattern): fp32 rounded,
+// integers clamped to the type's range then truncated; the bit index for
+// the bit predicates.
+uint32_t threshold_bits(scan_dtype_t dt, scan_cmp_t cmp, double threshold) {
+    uint32_t bits = 0;
+    if (bit_cmp(cmp)) {
+        bits = uint32_t(threshold);
+    } else if (dt == SCAN_F32) {
+        const float t = float(threshold);
+        memcpy(&bits, &t, 4);
+    } else if (dt == SCAN_I32) {
+        const double c = threshold < double(INT32_MIN) ? double(INT32_MIN)
+                         : threshold > double(INT32_MAX) ? double(INT32_MAX) : threshold;
+        const int32_t t = int32_t(c);
+        memcpy(&bits, &t, 4);
+    } else {
+        const double c = threshold < 0.0 ? 0.0 : threshold > double(UINT32_MAX) ? double(UINT32_MAX) : threshold;
+        bits = uint32_t(c);
+    }
+    return bits;
+}
+
+// Stable partition: the compaction's tiles, plus a count pass of at most
+// 1024 workgroups whose counts follow the tile descriptors.
+int plan_partition(scan_dtype_t dt, scan_cmp_t cmp, int64_t n, bool aligned, const scan_tuning_t &tu, TilePlan &p,
+                   int64_t &count_wgs, int64_t &count_chunk) {
+    const int rc = plan_shape(
+        4, aligned && n % 4 == 0, tu, p,
+        [&](int b, int r, int v) { return find_partition(dt, cmp, b, r, v) != nullptr; }, true, 8,
+        kDefaultBlock);
+    if (rc != SCAN_OK) return rc;
+    p.kernel = SCAN_KERNEL_PARTITION;
+    p.tiles_per_seg = p.num_tiles = (n + p.tile - 1) / p.tile;
+    p.carry_words = 1;
+    p.rts_blocks = p.rts_chunk = 0;
+    // about 16 Ki elements per count workgroup, at most 1024 of them, chunks
+    // on vector boundaries
+    count_wgs = (n + 16383) / 16384;
+    if (count_wgs > 1024) count_wgs = 1024;
+    count_chunk = round_up(size_t((n + count_wgs - 1) / count_wgs), size_t(p.vec));
+    count_wgs = (n + count_chunk - 1) / count_chunk;
+    p.ws_bytes = kHeader + round_up(size_t(p.num_tiles + count_wgs) * 8, 256);
+    p.launches = 2;
+    return SCAN_OK;
+}
+
 bool aligned16(const void *a, const void *b) {
     return ((reinterpret_cast<uintptr_t>(a) | reinterpret_cast<uintptr_t>(b)) & 15u) == 0;
 }
@@ -458,11 +511,20 @@ int scan_plan(scan_call_t call, scan_dtype_t dtype, scan_op_t op, int64_t outer,
         }
         break;
     case SCAN_CALL_COMPACT:
-        if (dtype != SCAN_F32 && dtype != SCAN_I32) return SCAN_ERR_UNSUPPORTED;
+        if (dtype != SCAN_F32 && dtype != SCAN_I32 && dtype != SCAN_U32) return SCAN_ERR_UNSUPPORTED;
         if (outer * len * inner > int64_t(INT32_MAX)) return SCAN_ERR_OVERFLOW;
         if (outer * len * inner == 0) return SCAN_OK;
         rc = plan_compact(dtype, outer * len * inner, true, tu, p);
         break;
+    case SCAN_CALL_PARTITION: {
+        // the predicate does not change the plan; GT stands for any
+        if (dtype != SCAN_F32 && dtype != SCAN_I32 && dtype != SCAN_U32) return SCAN_ERR_UNSUPPORTED;
+        if (outer * len * inner > int64_t(INT32_MAX)) return SCAN_ERR_OVERFLOW;
+        if (outer * len * inner == 0) return SCAN_OK;
+        int64_t cw = 0, cc = 0;
+        rc = plan_partition(dtype, SCAN_CMP_GT, outer * len * inner, true, tu, p, cw, cc);
+        break;
+    }
     case SCAN_CALL_PACK: {
         if (dtype != SCAN_I32 || outer != 1 || inner != 1) return SCAN_ERR_INVALID_ARG;
         if (len > int64_t(INT32_MAX)) return SCAN_ERR_OVERFLOW;
@@ -529,7 +591,8 @@ int compact_if(const void *x, int64_t n, scan_dtype_t x_dtype, scan_cmp_t cmp, d
                int32_t *d_count, void *ws, size_t ws_bytes, const scan_tuning_t *tuning, void *stream) {
     if (n < 0 || !valid_cmp(cmp) || d_count == nullptr) return SCAN_ERR_INVALID_ARG;
     if (!valid_dtype(x_dtype)) return SCAN_ERR_INVALID_ARG;
-    if (x_dtype != SCAN_F32 && x_dtype != SCAN_I32) return SCAN_ERR_UNSUPPORTED;
+    if (x_dtype != SCAN_F32 && x_dtype != SCAN_I32 && x_dtype != SCAN_U32) return SCAN_ERR_UNSUPPORTED;
+    if (!threshold_ok(x_dtype, cmp, threshold)) return SCAN_ERR_INVALID_ARG;
     if (n > int64_t(INT32_MAX)) return SCAN_ERR_OVERFLOW;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if (n == 0) return launch_fill_i32(d_count, 1, 0, s);
@@ -544,20 +607,45 @@ int compact_if(const void *x, int64_t n, scan_dtype_t x_dtype, scan_cmp_t cmp, d
     a.pipe = pipe_args(p, ws, ws_bytes, tu);
     a.x = x;
     a.n = n;
-    if (x_dtype == SCAN_F32) {
-        const float t = float(threshold);
-        memcpy(&a.threshold, &t, 4);
-    } else {
-        // clamp to the int32 range, then compare in int32
-        const double c = threshold < double(INT32_MIN) ? double(INT32_MIN)
-                         : threshold > double(INT32_MAX) ? double(INT32_MAX) : threshold;
-        const int32_t t = int32_t(c);
-        memcpy(&a.threshold, &t, 4);
-    }
+    a.threshold = threshold_bits(x_dtype, cmp, threshold);
     a.out_idx = out_idx;
     a.count = d_count;
     const uint32_t grid_cap = tu.grid_blocks > 0 ? uint32_t(tu.grid_blocks) : 0u;
     return find_compact(x_dtype, cmp, p.block, p.rows, p.vec)(a, grid_cap, s);
+}
+
+int partition_if(const void *x, int64_t n, scan_dtype_t x_dtype, scan_cmp_t cmp, double threshold, void *out_vals,
+                 int32_t *out_idx, int32_t *d_count, void *ws, size_t ws_bytes, const scan_tuning_t *tuning,
+                 void *stream) {
+    if (n < 0 || !valid_cmp(cmp) || d_count == nullptr) return SCAN_ERR_INVALID_ARG;
+    if (!valid_dtype(x_dtype)) return SCAN_ERR_INVALID_ARG;
+    if (x_dtype != SCAN_F32 && x_dtype != SCAN_I32 && x_dtype != SCAN_U32) return SCAN_ERR_UNSUPPORTED;
+    if (!threshold_ok(x_dtype, cmp, threshold)) return SCAN_ERR_INVALID_ARG;
+    if (n > int64_t(INT32_MAX)) return SCAN_ERR_OVERFLOW;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (n == 0) return launch_fill_i32(d_count, 1, 0, s);
+    if (x == nullptr || out_vals == nullptr) return SCAN_ERR_INVALID_ARG;
+    const scan_tuning_t tu = tuning_or_default(tuning);
+    TilePlan p;
+    int64_t count_wgs = 0, count_chunk = 0;
+    int rc = plan_partition(x_dtype, cmp, n, aligned16(x, x), tu, p, count_wgs, count_chunk);
+    if (rc != SCAN_OK) return rc;
+    rc = check_ws(ws, ws_bytes, p.ws_bytes);
+    if (rc != SCAN_OK) return rc;
+    PartitionArgs a;
+    a.pipe = pipe_args(p, ws, ws_bytes, tu);
+    a.pipe.words_used = uint64_t(p.num_tiles + count_wgs);  // tile descriptors, then the counts
+    a.x = x;
+    a.n = n;
+    a.threshold = threshold_bits(x_dtype, cmp, threshold);
+    a.out_vals = out_vals;
+    a.out_idx = out_idx;
+    a.count = d_count;
+    a.count_base = uint32_t(p.num_tiles);
+    a.count_wgs = uint32_t(count_wgs);
+    a.count_chunk = count_chunk;
+    const uint32_t grid_cap = tu.grid_blocks > 0 ? uint32_t(tu.grid_blocks) : 0u;
+    return find_partition(x_dtype, cmp, p.block, p.rows, p.vec)(a, grid_cap, s);
 }
 
 int pack_offsets(const int32_t *counts, int64_t n, int32_t *offsets, void *ws, size_t ws_bytes,

@@ -18,6 +18,8 @@
 
 namespace sw64 {
 
+// The predicate.  For integer keys the bit predicates test bit t (0..31) of
+// the key's 32-bit pattern: a one-bit radix digit.
 template <class X, int CMP>
 __device__ __forceinline__ bool keep(X v, X t) {
     if constexpr (CMP == SCAN_CMP_GT) return v > t;
@@ -25,7 +27,12 @@ __device__ __forceinline__ bool keep(X v, X t) {
     else if constexpr (CMP == SCAN_CMP_LT) return v < t;
     else if constexpr (CMP == SCAN_CMP_LE) return v <= t;
     else if constexpr (CMP == SCAN_CMP_EQ) return v == t;
-    else return v != t;
+    else if constexpr (CMP == SCAN_CMP_NE) return v != t;
+    else {
+        static_assert(!std::is_floating_point_v<X>, "bit predicates take integer keys");
+        const uint32_t bit = (uint32_t(v) >> (uint32_t(t) & 31u)) & 1u;
+        return CMP == SCAN_CMP_BIT_SET ? bit != 0u : bit == 0u;
+    }
 }
 
 template <class X, int CMP, int BLOCK_, int ROWS, int VEC>
@@ -51,7 +58,11 @@ struct CompactPolicy {
     };
 
     // Each selected element's index at its position.
-    __device__ __forceinline__ static void emit(const Stash &st, const Args &a, uint32_t tile, C pre, bool valid) {
+    static constexpr bool kSetup = false;
+    __device__ __forceinline__ static C setup(const Args &, const uint64_t *, uint32_t, WsHeader *) { return C{}; }
+
+    __device__ __forceinline__ static void emit(const Stash &st, const Args &a, uint32_t tile, C pre, bool valid,
+                                                C) {
         if (!valid) return;
         const int64_t start = int64_t(tile) * TS::TILE;
         const uint32_t bits = st.bits[threadIdx.x];
@@ -161,6 +172,13 @@ static CompactLaunch pick_compact_cmp(scan_cmp_t cmp, int block, int rows, int v
     case SCAN_CMP_LE: return pick_compact_shape<X, SCAN_CMP_LE>(block, rows, vec);
     case SCAN_CMP_EQ: return pick_compact_shape<X, SCAN_CMP_EQ>(block, rows, vec);
     case SCAN_CMP_NE: return pick_compact_shape<X, SCAN_CMP_NE>(block, rows, vec);
+    case SCAN_CMP_BIT_CLEAR:
+    case SCAN_CMP_BIT_SET:
+        if constexpr (!std::is_floating_point_v<X>) {
+            if (cmp == SCAN_CMP_BIT_CLEAR) return pick_compact_shape<X, SCAN_CMP_BIT_CLEAR>(block, rows, vec);
+            return pick_compact_shape<X, SCAN_CMP_BIT_SET>(block, rows, vec);
+        }
+        return nullptr;
     }
     return nullptr;
 }
@@ -168,6 +186,221 @@ static CompactLaunch pick_compact_cmp(scan_cmp_t cmp, int block, int rows, int v
 CompactLaunch find_compact(scan_dtype_t dt, scan_cmp_t cmp, int block, int rows, int vec) {
     if (dt == SCAN_F32) return pick_compact_cmp<float>(cmp, block, rows, vec);
     if (dt == SCAN_I32) return pick_compact_cmp<int32_t>(cmp, block, rows, vec);
+    if (dt == SCAN_U32) return pick_compact_cmp<uint32_t>(cmp, block, rows, vec);
+    return nullptr;
+}
+
+// -------------------------------------------------------------- partition
+// Stable partition (Merry, "Prefix sums on GPUs", slide "Other
+// Applications": partitioning places the objects that satisfy a predicate
+// before the others; radix sort is repeated partitioning, so each part keeps
+// the input order).  Element i with s_i selected elements before it goes to
+// s_i when selected, else to k + (i - s_i), k being the total selected.
+// s_i comes from the compaction's fused scan on the look-back pipeline; k
+// must be known before the first rejected element is written, so a count
+// pass runs first and publishes one count per workgroup as descriptor
+// words of this call (state A, the call's epoch) just above the scan's own
+// tile descriptors; the scan's control wave adds them up in its setup step.
+// Traffic: x read twice, the values (and indices) written once.
+
+// Count pass: workgroup w counts the selected elements of its contiguous
+// chunk of x and publishes the count.
+constexpr int kPartCountThreads = 256, kPartCountMax = 1024;  // at most this many count words
+
+template <class X, int CMP, int VEC>
+__global__ __launch_bounds__(kPartCountThreads) void k_part_count(PartitionArgs a) {
+    __shared__ int32_t wsum[kPartCountThreads / kWave];
+    const WsHeader *hdr = reinterpret_cast<const WsHeader *>(a.pipe.ws);
+    uint64_t *desc = reinterpret_cast<uint64_t *>(reinterpret_cast<char *>(a.pipe.ws) + kWsHeaderBytes);
+    const int64_t b = int64_t(blockIdx.x) * a.count_chunk;
+    const int64_t e = b + a.count_chunk < a.n ? b + a.count_chunk : a.n;
+    const X t = __builtin_bit_cast(X, a.threshold);
+    const X *x = reinterpret_cast<const X *>(a.x);
+    int32_t cnt = 0;
+    constexpr int64_t kStep = int64_t(kPartCountThreads) * VEC;
+#pragma unroll 4
+    for (int64_t i = b + int64_t(threadIdx.x) * VEC; i < e; i += kStep) {
+        // chunks start on VEC boundaries and n is a multiple of VEC here
+        const Vec<X, VEC> v = load_vec<X, VEC>(x + i);
+#pragma unroll
+        for (int c = 0; c < VEC; c++) cnt += keep<X, CMP>(v.v[c], t) ? 1 : 0;
+    }
+    cnt = wave_reduce<OpSum>(cnt);
+    if (lane_id() == 0) wsum[threadIdx.x / kWave] = cnt;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int32_t tot = 0;
+        for (int w = 0; w < kPartCountThreads / kWave; w++) tot += wsum[w];
+        Desc<int32_t>::publish(desc + a.count_base + blockIdx.x, ld(&hdr->epoch), kStateA, tot);
+    }
+}
+
+template <class X, int CMP, int BLOCK_, int ROWS, int VEC>
+struct PartitionPolicy {
+    using T = int32_t;
+    using Op = OpSum;
+    using C = int32_t;
+    using D = Desc<C>;
+    static constexpr int kDescWords = D::kWords;
+    static constexpr int BLOCK = BLOCK_;
+    using TS = TileScan<int32_t, OpSum, BLOCK, ROWS, VEC>;
+    using Args = PartitionArgs;
+    using Shared = typename TS::Shared;
+    using V = Vec<uint32_t, VEC>;
+    static_assert(ROWS * VEC <= 32, "selection bits fit one word");
+
+    __device__ __forceinline__ static C aggregate(const Shared &sh) { return TS::template aggregate_from<C>(sh); }
+
+    // The total selected: the count pass's words, one round trip.
+    static constexpr bool kSetup = true;
+    __device__ __forceinline__ static C setup(const Args &a, const uint64_t *desc, uint32_t epoch, WsHeader *hdr) {
+        GapRead<C, D, kPartCountMax / kWave> counts;
+        counts.issue(desc, int64_t(a.count_base), int64_t(a.count_base) + a.count_wgs);
+        return counts.template finish<Op>(desc, epoch, hdr, a.pipe.spin_limit);
+    }
+
+    // A scanned tile waiting for its prefix: row offsets, selection bits and
+    // the raw values.
+    struct Stash {
+        int32_t off[ROWS][BLOCK];
+        uint32_t bits[BLOCK];
+        V val[ROWS][BLOCK];
+    };
+
+    __device__ __forceinline__ static void emit(const Stash &st, const Args &a, uint32_t tile, C pre, bool valid,
+                                                C total) {
+        if (!valid) return;
+        const int64_t start = int64_t(tile) * TS::TILE;
+        const uint32_t bits = st.bits[threadIdx.x];
+        uint32_t *vals = reinterpret_cast<uint32_t *>(a.out_vals);
+#pragma unroll
+        for (int r = 0; r < ROWS; r++) {
+            const int64_t e = start + TS::elem(r);
+            if (e >= a.n) break;  // rows past the end (n is a multiple of VEC)
+            int32_t sel = pre + st.off[r][threadIdx.x];  // selected elements before this vector's next one
+            const V v = st.val[r][threadIdx.x];
+#pragma unroll
+            for (int c = 0; c < VEC; c++) {
+                const int64_t i = e + c;
+                const bool k = (bits >> (r * VEC + c)) & 1u;
+                const int64_t pos = k ? int64_t(sel) : int64_t(total) + (i - sel);
+                // in [0, n) whenever the count pass and the scan agree; a
+                // failed wait (flagged in the workspace) must not write outside
+                if (pos >= 0 && pos < a.n) {
+                    vals[pos] = v.v[c];
+                    if (a.out_idx != nullptr) a.out_idx[pos] = int32_t(i);
+                }
+                sel += k ? 1 : 0;
+            }
+        }
+    }
+
+    __device__ __forceinline__ static void on_resolved(const Args &a, uint32_t tile, C pre, C agg) {
+        if (tile == a.pipe.num_tiles - 1) *a.count = pre + agg;
+    }
+
+    struct Tile {
+        TS ts;          // raw element bits after load, 0/1 counts after scan
+        V raw[ROWS];    // the loaded values, kept for emission
+        uint32_t bits;  // bit r*VEC + c: element c of this thread's vector in row r is selected
+        uint32_t thr;
+        int64_t rem;
+
+        __device__ __forceinline__ void load(const Args &a, uint32_t tile) {
+            const bool valid = tile < a.pipe.num_tiles;
+            const int64_t start = valid ? int64_t(tile) * TS::TILE : 0;
+            rem = valid ? uniform(a.n - start) : 0;
+            thr = a.threshold;
+            const int32_t *x = reinterpret_cast<const int32_t *>(a.x) + uniform(start);
+#pragma unroll
+            for (int r = 0; r < ROWS; r++) {
+                const int64_t e = TS::elem(r);
+                ts.v[r] = load_vec<int32_t, VEC>(x + (e < rem ? e : 0));
+            }
+        }
+
+        __device__ __forceinline__ void scan(Shared &sh) {
+            const X t = __builtin_bit_cast(X, thr);
+            bits = 0;
+#pragma unroll
+            for (int r = 0; r < ROWS; r++) {
+                const int64_t e = TS::elem(r);
+                raw[r] = __builtin_bit_cast(V, ts.v[r]);
+#pragma unroll
+                for (int c = 0; c < VEC; c++) {
+                    const bool k = (e + c < rem) && keep<X, CMP>(__builtin_bit_cast(X, ts.v[r].v[c]), t);
+                    ts.v[r].v[c] = k ? 1 : 0;
+                    bits |= uint32_t(k) << (r * VEC + c);
+                }
+            }
+            ts.rem = TS::TILE;
+            ts.scan(sh);
+        }
+
+        __device__ __forceinline__ void stash(Stash &st, const Args &) const {
+#pragma unroll
+            for (int r = 0; r < ROWS; r++) {
+                st.off[r][threadIdx.x] = ts.off[r];
+                st.val[r][threadIdx.x] = raw[r];
+            }
+            st.bits[threadIdx.x] = bits;
+        }
+    };
+};
+
+template <class P>
+__global__ __launch_bounds__(CtrlPipeline<P>::THREADS) void k_partition(typename P::Args a) {
+    CtrlPipeline<P>::run(a);
+}
+
+template <class X, int CMP, int B, int R, int V>
+static int launch_partition_impl(const PartitionArgs &a, uint32_t grid_cap, hipStream_t s) {
+    using P = PartitionPolicy<X, CMP, B - kWave, R, V>;
+    if (a.count_wgs < 1 || a.count_wgs > uint32_t(kPartCountMax)) return SCAN_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL((k_part_count<X, CMP, V>), dim3(a.count_wgs), dim3(kPartCountThreads), 0, s, a);
+    if (hipGetLastError() != hipSuccess) return SCAN_ERR_HIP;
+    const int g = pipeline_grid(reinterpret_cast<const void *>(&k_partition<P>), B, a.pipe.num_tiles, grid_cap);
+    if (g <= 0) return SCAN_ERR_HIP;
+    hipLaunchKernelGGL((k_partition<P>), dim3(g), dim3(B), 0, s, a);
+    return hipGetLastError() == hipSuccess ? SCAN_OK : SCAN_ERR_HIP;
+}
+
+template <class X, int CMP>
+static PartitionLaunch pick_partition_shape(int block, int rows, int vec) {
+    if (vec == 4) {
+        if (block == 512 && rows == 8) return &launch_partition_impl<X, CMP, 512, 8, 4>;
+        if (block == 256 && rows == 1) return &launch_partition_impl<X, CMP, 256, 1, 4>;
+    } else if (vec == 1) {
+        if (block == 512 && rows == 8) return &launch_partition_impl<X, CMP, 512, 8, 1>;
+        if (block == 256 && rows == 1) return &launch_partition_impl<X, CMP, 256, 1, 1>;
+    }
+    return nullptr;
+}
+
+template <class X>
+static PartitionLaunch pick_partition_cmp(scan_cmp_t cmp, int block, int rows, int vec) {
+    switch (cmp) {
+    case SCAN_CMP_GT: return pick_partition_shape<X, SCAN_CMP_GT>(block, rows, vec);
+    case SCAN_CMP_GE: return pick_partition_shape<X, SCAN_CMP_GE>(block, rows, vec);
+    case SCAN_CMP_LT: return pick_partition_shape<X, SCAN_CMP_LT>(block, rows, vec);
+    case SCAN_CMP_LE: return pick_partition_shape<X, SCAN_CMP_LE>(block, rows, vec);
+    case SCAN_CMP_EQ: return pick_partition_shape<X, SCAN_CMP_EQ>(block, rows, vec);
+    case SCAN_CMP_NE: return pick_partition_shape<X, SCAN_CMP_NE>(block, rows, vec);
+    case SCAN_CMP_BIT_CLEAR:
+    case SCAN_CMP_BIT_SET:
+        if constexpr (!std::is_floating_point_v<X>) {
+            if (cmp == SCAN_CMP_BIT_CLEAR) return pick_partition_shape<X, SCAN_CMP_BIT_CLEAR>(block, rows, vec);
+            return pick_partition_shape<X, SCAN_CMP_BIT_SET>(block, rows, vec);
+        }
+        return nullptr;
+    }
+    return nullptr;
+}
+
+PartitionLaunch find_partition(scan_dtype_t dt, scan_cmp_t cmp, int block, int rows, int vec) {
+    if (dt == SCAN_F32) return pick_partition_cmp<float>(cmp, block, rows, vec);
+    if (dt == SCAN_I32) return pick_partition_cmp<int32_t>(cmp, block, rows, vec);
+    if (dt == SCAN_U32) return pick_partition_cmp<uint32_t>(cmp, block, rows, vec);
     return nullptr;
 }
 

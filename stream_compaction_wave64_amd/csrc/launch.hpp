@@ -63,6 +63,23 @@ using CompactLaunch = int (*)(const CompactArgs &, uint32_t grid_cap, hipStream_
 CompactLaunch find_compact(scan_dtype_t x_dt, scan_cmp_t cmp, int block, int rows, int vec);
 int launch_emit_neighbors(const int32_t *offsets, int64_t n, int32_t *out, hipStream_t s);
 
+// Stable partition: a count pass, then the compaction's fused scan writing
+// every element (compact.hip).
+struct PartitionArgs {
+    PipeArgs pipe;
+    const void *x;
+    int64_t n;
+    uint32_t threshold;       // bit pattern of the threshold (bit index for the bit predicates)
+    void *out_vals;           // n 32-bit values
+    int32_t *out_idx;         // n source indices, or null
+    int32_t *count;
+    uint32_t count_base;      // descriptor word of the count pass's first count (after the tiles')
+    uint32_t count_wgs;       // count-pass workgroups (<= 1024)
+    int64_t count_chunk;      // elements per count-pass workgroup (a multiple of the vector width)
+};
+using PartitionLaunch = int (*)(const PartitionArgs &, uint32_t grid_cap, hipStream_t);
+PartitionLaunch find_partition(scan_dtype_t x_dt, scan_cmp_t cmp, int block, int rows, int vec);
+
 // ---------------------------------------------------------- large elements
 // Elements of W components scanned component-wise along the middle axis of
 // an (outer, len, W) array by reduce-then-scan over chunks of tiles; a tile

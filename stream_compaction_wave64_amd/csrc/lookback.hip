@@ -46,7 +46,11 @@ struct ScanPolicy {
     // Store the stashed tile with its prefix.  An invalid call stores
     // nothing (its buffer resource has no range) but issues the same
     // instructions.
-    __device__ __forceinline__ static void emit(const Stash &st, const Args &a, uint32_t tile, C pre, bool valid) {
+    static constexpr bool kSetup = false;
+    __device__ __forceinline__ static C setup(const Args &, const uint64_t *, uint32_t, WsHeader *) { return C{}; }
+
+    __device__ __forceinline__ static void emit(const Stash &st, const Args &a, uint32_t tile, C pre, bool valid,
+                                                C) {
         int64_t start, remaining;
         uint32_t seg, j;
         geom(a, tile, start, remaining, seg, j);

@@ -79,8 +79,17 @@ struct PipeArgs {
 //   using T, C, Op, Args, Shared, Stash;  static constexpr int BLOCK, kDescWords
 //   static C aggregate(const Shared&)     control wave, between the scan's
 //                                         barrier and the next
-//   static void emit(const Stash&, const Args&, uint32_t tile, C pre, bool valid)
-//                                         data threads; !valid: no effect
+//   static void emit(const Stash&, const Args&, uint32_t tile, C pre, bool valid, C total)
+//                                         data threads; !valid: no effect;
+//                                         total: what setup() returned
+//   static constexpr bool kSetup          true: the control wave calls
+//   static C setup(const Args&, const uint64_t *desc, uint32_t epoch, WsHeader*)
+//                                         once, before the first barrier, and
+//                                         the call always runs the workspace
+//                                         protocol (epoch, end-of-call reset),
+//                                         even with one tile, so setup() can
+//                                         read words an earlier launch of the
+//                                         same call tagged with the epoch
 //   static void on_resolved(const Args&, uint32_t tile, C pre, C agg)
 //                                         control lane 0, after the prefix
 //   struct Tile {
@@ -105,9 +114,14 @@ struct CtrlPipeline {
         typename P::Stash stash[2];  // scanned tiles waiting for their prefix
         typename P::Shared ps;
         C prefix[2];  // exclusive prefix of the tile emitted in this step
+        C total;      // setup()'s result
         uint32_t epoch, mode, ticket;
         uint64_t clear_end;
     };
+
+    // Whether a call runs the workspace protocol: every chained scan, and
+    // every call of a policy with a setup step.
+    __device__ __forceinline__ static bool protocol(const Args &a) { return a.pipe.tiles_per_seg > 1 || P::kSetup; }
 
     __device__ __forceinline__ static uint64_t *desc_of(uint64_t *desc, uint32_t tile) {
         return desc + uint64_t(tile) * P::kDescWords;
@@ -196,7 +210,7 @@ struct CtrlPipeline {
             __syncthreads();
         __syncthreads();
         const bool emit = s >= 2;
-        P::emit(sm.stash[s & 1], a, emit ? w + (s - 2) * G : a.pipe.num_tiles, sm.prefix[s & 1], emit);
+        P::emit(sm.stash[s & 1], a, emit ? w + (s - 2) * G : a.pipe.num_tiles, sm.prefix[s & 1], emit, sm.total);
         if (s < K) cur.stash(sm.stash[s & 1], a);
         return s + 1 < K + 2;
     }
@@ -212,14 +226,20 @@ struct CtrlPipeline {
         uint64_t *desc = reinterpret_cast<uint64_t *>(reinterpret_cast<char *>(a.pipe.ws) + kWsHeaderBytes);
         const uint32_t n = a.pipe.num_tiles, G = gridDim.x, w = blockIdx.x;
         const uint32_t K = (n - w + G - 1) / G;  // tiles of this workgroup (>= 1)
-        const bool chained = a.pipe.tiles_per_seg > 1;
+        const bool chained = protocol(a);
         // Wave-uniform role (a scalar branch: no wave ever runs both sides).
         const bool ctrl = uniform(uint32_t(threadIdx.x)) >= uint32_t(DATA);
 
         if (ctrl) {
+            uint32_t e = 0;
             if (chained && lane_id() == 0) {
-                sm.epoch = begin_call(hdr);
+                e = begin_call(hdr);
+                sm.epoch = e;
                 sm.mode = decide_mode(hdr, G, a.pipe.mode_limit);
+            }
+            if constexpr (P::kSetup) {
+                const C t = P::setup(a, desc, uniform(e), hdr);  // uniform(): lane 0's epoch
+                if (lane_id() == 0) sm.total = t;
             }
             __syncthreads();
             const uint32_t epoch = chained ? sm.epoch : 0u;
@@ -270,7 +290,7 @@ struct CtrlPipeline {
             b0.stash(sm.stash[0], a);
             __syncthreads();
             __syncthreads();
-            P::emit(sm.stash[0], a, tk, sm.prefix[0], true);
+            P::emit(sm.stash[0], a, tk, sm.prefix[0], true, sm.total);
         }
     }
 
@@ -279,7 +299,7 @@ struct CtrlPipeline {
     __device__ __forceinline__ static void end_static(const Args &a, Smem &sm, WsHeader *hdr, uint64_t *desc,
                                                       uint32_t epoch) {
         const uint32_t n = a.pipe.num_tiles, G = gridDim.x;
-        if (a.pipe.tiles_per_seg > 1 && blockIdx.x == (n - 1) % G)
+        if (protocol(a) && blockIdx.x == (n - 1) % G)
             end_call_static(hdr, G, epoch, a.pipe.words_used, a.pipe.ws_words, desc, a.pipe.spin_limit,
                             sm.clear_end);
     }

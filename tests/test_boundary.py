@@ -115,6 +115,32 @@ def test_argument_errors_before_launch(lib):
     assert lib.pack_offsets(fake, -1, fake, ws, 1 << 20, None, None) == -1
     assert lib.pack_offsets(fake, 1 << 31, fake, ws, 1 << 20, None, None) == -5     # int32 overflow
     assert lib.scan_copy(fake, fake, 17, None) == -1
+    d = ctypes.c_double
+    for fn in ("compact_if", "partition_if"):
+        extra = (fake,) if fn == "partition_if" else ()
+        call = lambda dt, cmp, t, n=10: getattr(lib, fn)(fake, n, dt, cmp, d(t), fake, *extra, fake, ws, 1 << 20,
+                                                         None, None)
+        assert call(3, 9, 0.5) == -1          # bad predicate
+        assert call(3, 6, 3) == -1            # bit predicate on fp32 keys
+        assert call(0, 6, 32) == -1           # bit index past 31
+        assert call(1, 7, 2.5) == -1          # fractional bit index
+        assert call(2, 0, 0.5) == -2          # int64 keys are not built
+        assert call(1, 0, 0.5, n=1 << 31) == -5
+    assert lib.partition_if(fake, 10, 3, 0, d(0.5), None, None, fake, ws, 1 << 20, None, None) == -1  # NULL out
+
+
+def test_plan_partition():
+    from stream_compaction_wave64_amd import binding
+    import torch
+    for dt in (torch.float32, torch.int32, torch.uint32):
+        for n in (1, 1000, 10 ** 7, 2 ** 31 - 1):
+            p = binding.plan("partition", dt, "sum", 1, n)
+            assert p["kernel"] == "partition" and p["launches"] == 2
+            # tile descriptors, then at most 1024 count words
+            tiles = -(-n // p["tile_elems"])
+            assert p["num_tiles"] == tiles
+            assert 4096 + (tiles + 1) * 8 <= p["workspace_bytes"] <= 4096 + (tiles + 1024) * 8 + 256
+            assert p["workspace_bytes"] <= binding.scan_workspace_bytes(dt, n)
 
 
 def test_workspace_bound_covers_plans():

@@ -56,6 +56,17 @@ def test_compaction_all_comparisons(cmp, dt):
     _check_compact(x, cmp, t, tuning={"block_size": 256, "items_per_thread": 4})
 
 
+@pytest.mark.parametrize("dt", [np.int32, np.uint32])
+def test_compaction_integer_keys_and_bit_predicates(dt):
+    rng = np.random.default_rng(41)
+    keys = rng.integers(0, 2 ** 32, 300_001, dtype=np.uint64).astype(np.uint32).view(dt)
+    for b in (0, 9, 31):
+        _check_compact(keys, "bit_clear", b)
+        _check_compact(keys, "bit_set", b)
+    _check_compact(keys, "gt", 2 ** 31 if dt == np.uint32 else 0)
+    _check_compact(keys, "le", 12345, tuning={"block_size": 256, "items_per_thread": 4})
+
+
 def test_compaction_closed_forms_and_edges():
     for n in (1, 3, 4, 5, 1000, 16384, 16385, 100_003):
         _check_compact(np.ones(n, np.float32))                      # all selected -> iota

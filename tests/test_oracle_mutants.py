@@ -1,9 +1,13 @@
 """Plant plausible mistakes in a copy of the oracle (CPU only) and check that the
 pins in test_oracle.py catch each one.  This shows the pins are sensitive to a
 dropped term, a wrong index, a swapped comparison or an off-by-one anywhere in
-the oracle, rather than merely agreeing with it."""
+the oracle, rather than merely agreeing with it.
+
+Each mutant runs in a child process: a planted index mistake writes outside
+the oracle's output arrays, and that must not corrupt the test process."""
 import os
 import subprocess
+import sys
 
 import numpy as np
 import pytest
@@ -101,7 +105,15 @@ def test_pins_catch_mutant(tmp_path, name):
     src.write_text(text)
     lib = tmp_path / "libmut.so"
     subprocess.check_call(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-w", "-o", str(lib), str(src), "-lm"])
-    assert _caught(str(lib)), f"no pin caught the mutant: {name}"
+    here = os.path.dirname(os.path.abspath(__file__))
+    code = ("import sys; sys.path[:0] = [sys.argv[1], sys.argv[2]]\n"
+            "import test_oracle_mutants as M\n"
+            "print('CAUGHT' if M._caught(sys.argv[3]) else 'MISSED', flush=True)\n")
+    r = subprocess.run([sys.executable, "-c", code, here, os.path.dirname(here), str(lib)],
+                       capture_output=True, text=True, timeout=300)
+    # a child killed by a signal ran into the mutant's own memory error
+    caught = "CAUGHT" in r.stdout or r.returncode < 0
+    assert caught and "MISSED" not in r.stdout, f"no pin caught the mutant: {name}\n{r.stdout}\n{r.stderr[-2000:]}"
 
 
 def test_unmutated_oracle_passes_all_pins(oracle_lib):
