@@ -65,6 +65,11 @@ def _load():
         lib.oracle_partition_u32.argtypes = [vp, i64, i32, ctypes.c_uint32, vp, vp]
         for name in ("oracle_partition_f32", "oracle_partition_i32", "oracle_partition_u32"):
             getattr(lib, name).restype = i64
+        for name in ("oracle_segscan_i32", "oracle_segscan_u32", "oracle_segscan_i64",
+                     "oracle_segscan_f32", "oracle_segscan_f64"):
+            f = getattr(lib, name)
+            f.argtypes = [vp, vp, vp, i64, i32, i32]
+            f.restype = i32
         lib.oracle_pack_offsets.argtypes = [vp, i64, vp]
         lib.oracle_pack_offsets.restype = i64
         lib.oracle_pack_emit.argtypes = [vp, i64, vp]
@@ -112,6 +117,38 @@ def scan(x: np.ndarray, op: str = "sum", exclusive: bool = False, dims=None) -> 
         if rc != 0:
             raise ValueError("oracle scan rejected its arguments")
     return y.reshape(x.shape)
+
+
+def scan_segmented(x: np.ndarray, offsets: np.ndarray, op: str = "sum", exclusive: bool = False) -> np.ndarray:
+    """Each ragged segment x[offsets[s] .. offsets[s+1]) scanned on its own
+    (offsets: int32, non-decreasing, offsets[0] = 0, offsets[-1] = x.size).
+    Result types as for scan()."""
+    lib = _load()
+    x = np.ascontiguousarray(x)
+    off = np.ascontiguousarray(offsets, dtype=np.int32)
+    if off.size < 1 or off[0] != 0 or off[-1] != x.size or np.any(np.diff(off.astype(np.int64)) < 0):
+        raise ValueError("offsets must be non-decreasing from 0 to x.size")
+    name, out_t = _SCAN[x.dtype]
+    y = np.empty(x.size, dtype=out_t)
+    if x.size:
+        rc = getattr(lib, name.replace("oracle_scan_", "oracle_segscan_"))(
+            _ptr(x), _ptr(y), _ptr(off), off.size - 1, OPS[op], int(exclusive))
+        if rc != 0:
+            raise ValueError("oracle segmented scan rejected its arguments")
+    return y
+
+
+def segment_abs_prefix(x: np.ndarray, offsets: np.ndarray, exclusive: bool = False) -> np.ndarray:
+    """P_i of a segmented scan, in fp64: the sum of |x_j| over the inputs
+    output i depends on (a tolerance weight, from one running sum less its
+    value before the segment's start)."""
+    a = np.abs(np.ascontiguousarray(x).astype(np.float64))
+    off = np.asarray(offsets, dtype=np.int64)
+    run = np.cumsum(a)
+    start = np.repeat(off[:-1], np.diff(off))            # segment start of every element
+    before = np.where(start > 0, run[np.maximum(start - 1, 0)], 0.0)
+    p = run - before
+    return p - a if exclusive else p
 
 
 def abs_prefix(x: np.ndarray, exclusive: bool = False, dims=None) -> np.ndarray:

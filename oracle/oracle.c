@@ -395,6 +395,32 @@ PARTITION(oracle_partition_i32, int32_t, keep_i32)
 PARTITION(oracle_partition_u32, uint32_t, keep_u32)
 #undef PARTITION
 
+/* ------------------------------------------------------ segmented scan --
+ * Ragged segments (the packed lists of Merry's "Output Format" and
+ * "Solution" slides, AcceleratedKernels.jl PR #208's SliceScan generalised
+ * to segments of any length): segment s is x[off[s] .. off[s+1]) and is
+ * scanned on its own with the plain scan above, so an exclusive result
+ * starts every segment at the identity.  Empty segments are allowed.
+ * Returns -1 if the offsets decrease. */
+#define SEGSCAN(NAME, SCAN, TX, TY)                                                     \
+    int NAME(const TX *x, TY *y, const int32_t *off, int64_t nseg, int op, int exclusive) { \
+        for (int64_t s = 0; s < nseg; s++) {                                            \
+            const int64_t b = off[s], e = off[s + 1];                                   \
+            if (e < b) return -1;                                                       \
+            if (e > b) {                                                                \
+                const int rc = SCAN(x + b, y + b, 1, e - b, 1, op, exclusive);          \
+                if (rc != 0) return rc;                                                 \
+            }                                                                           \
+        }                                                                               \
+        return 0;                                                                       \
+    }
+SEGSCAN(oracle_segscan_i32, oracle_scan_i32, int32_t, int32_t)
+SEGSCAN(oracle_segscan_u32, oracle_scan_u32, uint32_t, uint32_t)
+SEGSCAN(oracle_segscan_i64, oracle_scan_i64, int64_t, int64_t)
+SEGSCAN(oracle_segscan_f32, oracle_scan_f32, float, double)
+SEGSCAN(oracle_segscan_f64, oracle_scan_f64, double, double)
+#undef SEGSCAN
+
 /* --------------------------------------------------------------- packing --
  * offsets[0] = 0, offsets[i+1] = offsets[i] + counts[i]; returns the total
  * (offsets[n]) computed in 64 bits, so a caller can see int32 overflow. */

@@ -438,6 +438,69 @@ def test_radix_sort_from_stable_bit_partitions(oracle_lib):
     assert np.array_equal(cur, np.sort(sk)) and np.array_equal(perm, np.argsort(sk, kind="stable"))
 
 
+# ------------------------------------------------------- segmented scan
+
+
+def test_segmented_packing_example(oracle_lib):
+    g = read_golden("segmented_scan_packing_example.txt")
+    off = np.array(g["offsets"], np.int32)
+    for dt in (np.int32, np.int64, np.float32, np.float64):
+        x = np.array(g["values"], dt)
+        assert list(oracle_lib.scan_segmented(x, off, "sum")) == g["incl_sum"]
+        assert list(oracle_lib.scan_segmented(x, off, "sum", exclusive=True)) == g["excl_sum"]
+        assert list(oracle_lib.scan_segmented(x, off, "max")) == g["incl_max"]
+        assert list(oracle_lib.scan_segmented(x, off, "prod")) == g["incl_prod"]
+
+
+def _random_offsets(rng, n, mean):
+    lens = rng.poisson(mean, n)                          # includes empty segments
+    off = np.concatenate([[0], np.cumsum(lens)])
+    off = off[off <= n]
+    return np.concatenate([off, [n]]).astype(np.int32)
+
+
+def test_segmented_brute_force(oracle_lib):
+    rng = np.random.default_rng(60)
+    for n, mean in ((1, 1.0), (37, 2.0), (200, 5.0), (300, 0.7)):
+        x = rng.integers(-9, 10, n).astype(np.int64)
+        off = _random_offsets(rng, n, mean)
+        seg = np.repeat(np.arange(off.size - 1), np.diff(off))
+        for op, f, ident in (("sum", lambda a, b: a + b, 0), ("max", max, np.iinfo(np.int64).min)):
+            incl = oracle_lib.scan_segmented(x, off, op)
+            excl = oracle_lib.scan_segmented(x, off, op, exclusive=True)
+            for i in range(n):
+                acc = ident
+                for j in range(off[seg[i]], i):
+                    acc = f(acc, x[j])
+                assert excl[i] == acc
+                assert incl[i] == f(acc, x[i])
+
+
+def test_segmented_closed_forms_and_invariants(oracle_lib):
+    rng = np.random.default_rng(61)
+    n = 50_000
+    off = _random_offsets(rng, n, 6.0)
+    start = np.repeat(off[:-1], np.diff(off))
+    ones = np.ones(n, np.int32)
+    assert np.array_equal(oracle_lib.scan_segmented(ones, off, "sum"), np.arange(n) - start + 1)
+    assert np.array_equal(oracle_lib.scan_segmented(ones, off, "sum", exclusive=True), np.arange(n) - start)
+    x = rng.random(n, dtype=np.float32)
+    # one segment is the plain scan; one-element segments return x (identity when exclusive)
+    assert np.array_equal(oracle_lib.scan_segmented(x, np.array([0, n], np.int32), "sum"), oracle_lib.scan(x))
+    each = np.arange(n + 1, dtype=np.int32)
+    assert np.array_equal(oracle_lib.scan_segmented(x, each, "sum"), x.astype(np.float64))
+    assert not oracle_lib.scan_segmented(x, each, "sum", exclusive=True).any()
+    # empty segments change nothing
+    dup = np.sort(np.concatenate([off, off[::3], off[::7]])).astype(np.int32)
+    assert np.array_equal(oracle_lib.scan_segmented(x, dup, "max"), oracle_lib.scan_segmented(x, off, "max"))
+    # the last output of each non-empty segment is the segment total
+    incl = oracle_lib.scan_segmented(x, off, "sum")
+    ends = off[1:][np.diff(off) > 0] - 1
+    starts = off[:-1][np.diff(off) > 0]
+    totals = np.add.reduceat(x.astype(np.float64), starts)
+    assert np.allclose(incl[ends], totals, rtol=1e-12)
+
+
 # ---------------------------------------------------------------- packing
 
 

@@ -44,6 +44,12 @@ MUTANTS = {
         "for (int64_t i = 0; i < n; i++)                                              \\\n            if (!KEEP",
         "for (int64_t i = n - 1; i >= 0; i--)                                         \\\n            if (!KEEP"),
     "bit predicate tests the next bit": ("return ((v >> (t & 31u)) & 1u) == 0u;", "return ((v >> ((t + 1) & 31u)) & 1u) == 0u;"),
+    "segmented scan drops each segment's last element": (
+        "const int rc = SCAN(x + b, y + b, 1, e - b, 1, op, exclusive);",
+        "const int rc = SCAN(x + b, y + b, 1, e - b - 1, 1, op, exclusive);"),
+    "segmented scan skips the last segment": (
+        "for (int64_t s = 0; s < nseg; s++) {                                            \\",
+        "for (int64_t s = 0; s + 1 < nseg; s++) {                                        \\"),
     "pack offsets shifted": ("offsets[i + 1] = (int32_t)run;", "offsets[i] = (int32_t)run;"),
     "emit record drops the +1": ("(int32_t)((i + 1 + j) % n)", "(int32_t)((i + j) % n)"),
     "block rule without the per-thread totals": ("2 * b * esize > budget", "b * esize > budget"),
@@ -71,6 +77,9 @@ PINS = [
     lambda o: T.test_partition_invariants(o),
     lambda o: T.test_partition_closed_forms(o),
     lambda o: T.test_radix_sort_from_stable_bit_partitions(o),
+    lambda o: T.test_segmented_packing_example(o),
+    lambda o: T.test_segmented_brute_force(o),
+    lambda o: T.test_segmented_closed_forms_and_invariants(o),
 ]
 
 
