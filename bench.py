@@ -220,6 +220,30 @@ def _rows(dev, lib, binding, inputs):
                      4 * n + 8 * (n + 1) + 4 * total, make_pack))
     del xc, counts
 
+    # segmented scan over the count-scan-emit layout: the 1e7 Poisson(3)
+    # counts as segment lengths (offsets from the library's pack_offsets,
+    # set-up only), one fp32 value per record
+    counts_s, vals_s = inputs.segmented_inputs(10 ** 7, 4)
+    nseg, nv = counts_s.size, vals_s.size
+    c_dev = torch.from_numpy(counts_s).to(dev)
+    off_s = torch.empty(nseg + 1, dtype=torch.int32, device=dev)
+    ws_o = ws_for("pack", torch.int32, "sum", 1, nseg, 1)
+    assert lib.pack_offsets(vp(c_dev), nseg, vp(off_s), vp(ws_o), ws_o.numel(), null,
+                            torch.cuda.current_stream(dev).cuda_stream) == 0
+    v0 = torch.from_numpy(vals_s).to(dev)
+    ws_s = ws_for("segmented", torch.float32, "sum", nseg, nv, 1)
+
+    def make_seg(k):
+        v = v0 if k == 0 else v0.clone()
+        o = off_s if k == 0 else off_s.clone()
+        y = torch.empty_like(v)
+        return (lambda s: lib.scan_segmented(vp(v), vp(y), nv, vp(o), nseg, 3, 0, 0, vp(ws_s), ws_s.numel(), null,
+                                             s)), [y]
+    rows.append(_Row("segscan_fp32_poisson3_1e7", "segmented inclusive sum of ~3e7 fp32 uniform [0,1) records in "
+                     "1e7 Poisson(3)-length segments (offsets from pack_offsets), seed 4", nv,
+                     8 * nv + 4 * (nseg + 1), 8 * nv + 4 * (nseg + 1), make_seg))
+    del counts_s, vals_s
+
     s64, s32 = inputs.struct_inputs(10 ** 6, 5)
     scan_row("struct136_fp64x17_1e6", "1e6 elements of 17 fp64 (136 B), elementwise sum, seed 5", s64.reshape(-1),
              width=17)

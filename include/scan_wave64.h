@@ -137,7 +137,8 @@ typedef enum {
     SCAN_KERNEL_COLUMNS = 4,    /* wide inner extent: column strips, chunked rows */
     SCAN_KERNEL_COMPACT = 5,    /* fused predicate + scan + scatter */
     SCAN_KERNEL_PACK = 6,       /* exclusive int32 scan + total */
-    SCAN_KERNEL_PARTITION = 7   /* count pass, then fused predicate + scan + two-sided scatter */
+    SCAN_KERNEL_PARTITION = 7,  /* count pass, then fused predicate + scan + two-sided scatter */
+    SCAN_KERNEL_SEGMENTED = 8   /* ragged segments: tile map, then reduce-then-scan of (head, value) pairs */
 } scan_kernel_t;
 
 typedef struct {
@@ -159,7 +160,8 @@ typedef enum {
     SCAN_CALL_SCAN = 0,        /* scan_inclusive / scan_exclusive / scan_dim */
     SCAN_CALL_COMPACT = 1,     /* compact_if (dtype = x dtype) */
     SCAN_CALL_PACK = 2,        /* pack_offsets (dtype must be SCAN_I32) */
-    SCAN_CALL_PARTITION = 3    /* partition_if (dtype = x dtype) */
+    SCAN_CALL_PARTITION = 3,   /* partition_if (dtype = x dtype) */
+    SCAN_CALL_SEGMENTED = 4    /* scan_segmented (outer = segments, len = elements, inner = 1) */
 } scan_call_t;
 
 /* Host only: the launch a call with these arguments would enqueue. */
@@ -202,6 +204,22 @@ int scan_exclusive(const void *in, void *out, int64_t n, scan_dtype_t dtype,
 int scan_dim(const void *in, void *out, int64_t outer, int64_t len, int64_t inner,
              scan_dtype_t dtype, scan_op_t op, int exclusive, void *ws,
              size_t ws_bytes, const scan_tuning_t *tuning, void *stream);
+
+/* Scan of ragged segments: segment s is in[offsets[s] .. offsets[s+1]) and
+ * is scanned on its own, so an inclusive result restarts at every segment's
+ * first element and an exclusive one puts the identity there (Merry,
+ * "Prefix sums on GPUs", slides "Output Format" and "Solution": the packed
+ * lists whose offsets pack_offsets writes; AcceleratedKernels.jl PR #208's
+ * SliceScan with segments of any length).  offsets: nseg + 1 device int32,
+ * non-decreasing, offsets[0] = 0, offsets[nseg] = n; empty segments are
+ * allowed.  Offsets that break this give unspecified results (no access
+ * outside in, out, offsets or the workspace).  out may equal in.  Four
+ * launches (tile map, reduce, partials, rescan; reduce-then-scan of
+ * (head flag, value) pairs).  n > INT32_MAX -> SCAN_ERR_OVERFLOW; n == 0 is a
+ * no-op; n > 0 with nseg == 0 -> SCAN_ERR_INVALID_ARG. */
+int scan_segmented(const void *in, void *out, int64_t n, const int32_t *offsets,
+                   int64_t nseg, scan_dtype_t dtype, scan_op_t op, int exclusive,
+                   void *ws, size_t ws_bytes, const scan_tuning_t *tuning, void *stream);
 
 /* Stream compaction: writes, in increasing order, every 0-based index i with
  * x[i] <cmp> threshold to out_idx, and the number written to *d_count (a

@@ -140,15 +140,9 @@ def scan_segmented(x: np.ndarray, offsets: np.ndarray, op: str = "sum", exclusiv
 
 def segment_abs_prefix(x: np.ndarray, offsets: np.ndarray, exclusive: bool = False) -> np.ndarray:
     """P_i of a segmented scan, in fp64: the sum of |x_j| over the inputs
-    output i depends on (a tolerance weight, from one running sum less its
-    value before the segment's start)."""
-    a = np.abs(np.ascontiguousarray(x).astype(np.float64))
-    off = np.asarray(offsets, dtype=np.int64)
-    run = np.cumsum(a)
-    start = np.repeat(off[:-1], np.diff(off))            # segment start of every element
-    before = np.where(start > 0, run[np.maximum(start - 1, 0)], 0.0)
-    p = run - before
-    return p - a if exclusive else p
+    output i depends on (the segmented scan of |x| itself, so each segment's
+    sum starts from zero with no cancellation)."""
+    return scan_segmented(np.abs(np.ascontiguousarray(x)), offsets, "sum", exclusive)
 
 
 def abs_prefix(x: np.ndarray, exclusive: bool = False, dims=None) -> np.ndarray:

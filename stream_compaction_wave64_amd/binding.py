@@ -21,9 +21,9 @@ DTYPES = {torch.int32: 0, torch.uint32: 1, torch.int64: 2, torch.float32: 3, tor
 OPS = {"sum": 0, "prod": 1, "max": 2, "min": 3}
 ALGOS = {"auto": 0, "lookback": 1, "reduce_then_scan": 2, "rts": 2}
 CMPS = {"gt": 0, "ge": 1, "lt": 2, "le": 3, "eq": 4, "ne": 5, "bit_clear": 6, "bit_set": 7}
-CALLS = {"scan": 0, "compact": 1, "pack": 2, "partition": 3}
+CALLS = {"scan": 0, "compact": 1, "pack": 2, "partition": 3, "segmented": 4}
 KERNELS = {0: "none", 1: "lookback", 2: "reduce_then_scan", 3: "element", 4: "columns", 5: "compact",
-           6: "pack", 7: "partition"}
+           6: "pack", 7: "partition", 8: "segmented"}
 
 
 class ScanError(RuntimeError):
@@ -48,7 +48,7 @@ class Plan(ctypes.Structure):
 
 
 EXPORTS = ["scan_plan", "scan_workspace_bytes", "scan_workspace_init", "scan_workspace_error", "scan_inclusive",
-           "scan_exclusive", "scan_dim", "compact_if", "partition_if", "pack_offsets", "pack_emit_neighbors",
+           "scan_exclusive", "scan_dim", "scan_segmented", "compact_if", "partition_if", "pack_offsets", "pack_emit_neighbors",
            "scan_copy", "scan_status_string", "scan_version"]
 
 _lib = None
@@ -78,6 +78,7 @@ def load_library(path: str = LIB_PATH):
             "scan_exclusive": ([vp, vp, i64, i32, i32, i32, vp, sz, tp, vp], i32),
             "scan_dim": ([vp, vp, i64, i64, i64, i32, i32, i32, vp, sz, tp, vp], i32),
             "compact_if": ([vp, i64, i32, i32, ctypes.c_double, vp, vp, vp, sz, tp, vp], i32),
+            "scan_segmented": ([vp, vp, i64, vp, i64, i32, i32, i32, vp, sz, tp, vp], i32),
             "partition_if": ([vp, i64, i32, i32, ctypes.c_double, vp, vp, vp, vp, sz, tp, vp], i32),
             "pack_offsets": ([vp, i64, vp, vp, sz, tp, vp], i32),
             "pack_emit_neighbors": ([vp, i64, vp, vp], i32),
@@ -225,6 +226,28 @@ def scan_dim(x: torch.Tensor, dim: int, op: str = "sum", exclusive: bool = False
     ws, wsb = _workspace_for("scan", x, op, outer, length, inner, tuning)
     _check("scan_dim", lib.scan_dim(x.data_ptr(), out.data_ptr(), outer, length, inner, _dtype(x), OPS[op],
                                     int(exclusive), ws.data_ptr(), wsb, _tuning(tuning), _stream(x.device)))
+    return out
+
+
+def scan_segmented(x: torch.Tensor, offsets: torch.Tensor, op: str = "sum", exclusive: bool = False, out=None,
+                   tuning=None) -> torch.Tensor:
+    """Each ragged segment x[offsets[s] .. offsets[s+1]) scanned on its own
+    (offsets: int32 device tensor of nseg + 1 non-decreasing values from 0 to
+    x.numel(), as pack_offsets writes them)."""
+    lib = load_library()
+    _need_cuda(x, offsets)
+    if offsets.dtype != torch.int32 or offsets.dim() != 1 or offsets.numel() < 1:
+        raise ValueError("offsets must be a 1-D int32 tensor of nseg + 1 entries")
+    if out is None:
+        out = torch.empty_like(x)
+    _need_cuda(out)
+    if out.dtype != x.dtype or out.numel() != x.numel():
+        raise ValueError("out must match x in dtype and size")
+    n, nseg = x.numel(), offsets.numel() - 1
+    ws, wsb = _workspace_for("segmented", x, op, nseg, n, 1, tuning)
+    _check("scan_segmented", lib.scan_segmented(x.data_ptr(), out.data_ptr(), n, offsets.data_ptr(), nseg, _dtype(x),
+                                                OPS[op], int(exclusive), ws.data_ptr(), wsb, _tuning(tuning),
+                                                _stream(x.device)))
     return out
 
 

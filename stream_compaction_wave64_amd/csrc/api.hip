@@ -17,6 +17,7 @@ namespace sw64 {
     ret name##_f64(scan_op_t, int, int, int);
 SW64_DECLARE_PER_TYPE(find_lookback, LbLaunch)
 SW64_DECLARE_PER_TYPE(find_rts, RtsLaunch)
+SW64_DECLARE_PER_TYPE(find_seg, SegLaunch)
 #undef SW64_DECLARE_PER_TYPE
 ElemLaunch find_element_i32(scan_op_t, int, int, bool);
 ElemLaunch find_element_u32(scan_op_t, int, int, bool);
@@ -59,6 +60,17 @@ LbLaunch find_lookback(scan_dtype_t dt, scan_op_t op, int block, int rows, int v
     case SCAN_I64: return find_lookback_i64(op, block, rows, vec);
     case SCAN_F32: return find_lookback_f32(op, block, rows, vec);
     case SCAN_F64: return find_lookback_f64(op, block, rows, vec);
+    }
+    return nullptr;
+}
+
+SegLaunch find_seg(scan_dtype_t dt, scan_op_t op, int block, int rows, int vec) {
+    switch (dt) {
+    case SCAN_I32: return find_seg_i32(op, block, rows, vec);
+    case SCAN_U32: return find_seg_u32(op, block, rows, vec);
+    case SCAN_I64: return find_seg_i64(op, block, rows, vec);
+    case SCAN_F32: return find_seg_f32(op, block, rows, vec);
+    case SCAN_F64: return find_seg_f64(op, block, rows, vec);
     }
     return nullptr;
 }
@@ -335,6 +347,30 @@ uint32_t threshold_bits(scan_dtype_t dt, scan_cmp_t cmp, double threshold) {
     return bits;
 }
 
+// Ragged segmented scan: the reduce-then-scan tile shapes, about
+// kDefaultRtsBlocks chunks (at most 2048, the partials pass), the tile map
+// (one word per tile) and the chunk partials (16 bytes each) in the workspace.
+int plan_segmented(scan_dtype_t dt, scan_op_t op, int64_t n, bool aligned, const scan_tuning_t &tu, TilePlan &p) {
+    const int esize = dtype_bytes(dt);
+    const bool vec_ok = aligned;  // the last tile is accessed element-wise, so any n
+    const int rc = plan_shape(
+        esize, vec_ok, tu, p, [&](int b, int r, int v) { return find_seg(dt, op, b, r, v) != nullptr; }, false,
+        esize == 8 ? 4 : 8, kDefaultBlock);
+    if (rc != SCAN_OK) return rc;
+    p.kernel = SCAN_KERNEL_SEGMENTED;
+    p.tiles_per_seg = p.num_tiles = (n + p.tile - 1) / p.tile;
+    if (p.num_tiles > int64_t(UINT32_MAX)) return SCAN_ERR_OVERFLOW;
+    int64_t chunks = tu.rts_blocks > 0 ? tu.rts_blocks : kDefaultRtsBlocks;
+    if (chunks > 2048) chunks = 2048;
+    if (chunks > p.num_tiles) chunks = p.num_tiles;
+    p.rts_chunk = (p.num_tiles + chunks - 1) / chunks;
+    p.rts_blocks = (p.num_tiles + p.rts_chunk - 1) / p.rts_chunk;
+    p.carry_words = carry_bytes(dt, op) / 4;
+    p.ws_bytes = kHeader + round_up(size_t(p.num_tiles) * 8, 16) + round_up(size_t(p.rts_blocks) * 16, 256);
+    p.launches = 4;
+    return SCAN_OK;
+}
+
 // Stable partition: the compaction's tiles, plus a count pass of at most
 // 1024 workgroups whose counts follow the tile descriptors.
 int plan_partition(scan_dtype_t dt, scan_cmp_t cmp, int64_t n, bool aligned, const scan_tuning_t &tu, TilePlan &p,
@@ -516,6 +552,13 @@ int scan_plan(scan_call_t call, scan_dtype_t dtype, scan_op_t op, int64_t outer,
         if (outer * len * inner == 0) return SCAN_OK;
         rc = plan_compact(dtype, outer * len * inner, true, tu, p);
         break;
+    case SCAN_CALL_SEGMENTED:
+        // outer = number of segments, len = elements
+        if (inner != 1) return SCAN_ERR_INVALID_ARG;
+        if (len > int64_t(INT32_MAX) || outer > int64_t(INT32_MAX)) return SCAN_ERR_OVERFLOW;
+        if (len == 0) return SCAN_OK;
+        rc = plan_segmented(dtype, op, len, true, tu, p);
+        break;
     case SCAN_CALL_PARTITION: {
         // the predicate does not change the plan; GT stands for any
         if (dtype != SCAN_F32 && dtype != SCAN_I32 && dtype != SCAN_U32) return SCAN_ERR_UNSUPPORTED;
@@ -646,6 +689,38 @@ int partition_if(const void *x, int64_t n, scan_dtype_t x_dtype, scan_cmp_t cmp,
     a.count_chunk = count_chunk;
     const uint32_t grid_cap = tu.grid_blocks > 0 ? uint32_t(tu.grid_blocks) : 0u;
     return find_partition(x_dtype, cmp, p.block, p.rows, p.vec)(a, grid_cap, s);
+}
+
+int scan_segmented(const void *in, void *out, int64_t n, const int32_t *offsets, int64_t nseg,
+                   scan_dtype_t dtype, scan_op_t op, int exclusive, void *ws, size_t ws_bytes,
+                   const scan_tuning_t *tuning, void *stream) {
+    if (n < 0 || nseg < 0 || !valid_dtype(dtype) || !valid_op(op)) return SCAN_ERR_INVALID_ARG;
+    if (n > int64_t(INT32_MAX) || nseg > int64_t(INT32_MAX)) return SCAN_ERR_OVERFLOW;
+    if (n == 0) return SCAN_OK;
+    if (nseg == 0 || in == nullptr || out == nullptr || offsets == nullptr) return SCAN_ERR_INVALID_ARG;
+    const scan_tuning_t tu = tuning_or_default(tuning);
+    TilePlan p;
+    int rc = plan_segmented(dtype, op, n, aligned16(in, out), tu, p);
+    if (rc != SCAN_OK) return rc;
+    rc = check_ws(ws, ws_bytes, p.ws_bytes);
+    if (rc != SCAN_OK) return rc;
+    SegArgs a;
+    a.in = in;
+    a.out = out;
+    a.n = n;
+    a.off = offsets;
+    a.nseg = nseg;
+    a.map = reinterpret_cast<uint64_t *>(reinterpret_cast<char *>(ws) + kHeader);
+    a.partials = reinterpret_cast<char *>(ws) + kHeader + round_up(size_t(p.num_tiles) * 8, 16);
+    a.tile = p.tile;
+    a.tile_log2 = 0;
+    while ((int64_t(1) << a.tile_log2) < p.tile) a.tile_log2++;
+    if ((int64_t(1) << a.tile_log2) != p.tile) return SCAN_ERR_UNSUPPORTED;  // tiles are powers of two
+    a.num_tiles = uint32_t(p.num_tiles);
+    a.chunk_tiles = uint32_t(p.rts_chunk);
+    a.blocks = uint32_t(p.rts_blocks);
+    a.exclusive = exclusive ? 1 : 0;
+    return find_seg(dtype, op, p.block, p.rows, p.vec)(a, reinterpret_cast<hipStream_t>(stream));
 }
 
 int pack_offsets(const int32_t *counts, int64_t n, int32_t *offsets, void *ws, size_t ws_bytes,

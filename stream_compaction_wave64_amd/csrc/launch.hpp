@@ -50,6 +50,27 @@ struct RtsArgs {
 using RtsLaunch = int (*)(const RtsArgs &, hipStream_t);
 RtsLaunch find_rts(scan_dtype_t dt, scan_op_t op, int block, int rows, int vec);
 
+// ----------------------------------------------------------- segmented scan
+// Ragged segments given by int32 offsets, reduce-then-scan over chunks of
+// tiles with (head flag, value) pairs (segmented.hip).
+struct SegArgs {
+    const void *in;
+    void *out;
+    int64_t n;
+    const int32_t *off;       // nseg + 1 offsets
+    int64_t nseg;
+    uint64_t *map;            // per tile: the segment holding its first element (workspace)
+    void *partials;           // per chunk: (carry value, head flag) (workspace)
+    int64_t tile;             // elements per tile (a power of two)
+    int32_t tile_log2;
+    uint32_t num_tiles;
+    uint32_t chunk_tiles;
+    uint32_t blocks;          // chunks (<= 2048)
+    int32_t exclusive;
+};
+using SegLaunch = int (*)(const SegArgs &, hipStream_t);
+SegLaunch find_seg(scan_dtype_t dt, scan_op_t op, int block, int rows, int vec);
+
 // ---------------------------------------------------------------- compaction
 struct CompactArgs {
     PipeArgs pipe;

@@ -1,0 +1,447 @@
+// segmented.hip -- scans of ragged segments: segment s is in[off[s] ..
+// off[s+1]) and is scanned on its own (the packed lists of Merry, "Prefix
+// sums on GPUs", slides "Output Format" and "Solution", whose offsets
+// pack_offsets produces; AcceleratedKernels.jl PR #208's SliceScan with
+// segments of any length).
+//
+// A segmented scan is a plain scan of (head flag, value) pairs under the
+// operator that restarts at a head:
+//   (fa, a) . (fb, b) = (fa | fb, fb ? b : a (+) b)        (a earlier)
+// which is associative but not commutative, so every combination below keeps
+// sequence order (the earlier operand on the left).  The structure is
+// reduce-then-scan (The CUDA Handbook ch. 13 section 13.3.3), four launches:
+//   1. map: one thread per segment writes, for every tile whose first
+//      element lies in the segment, the segment's index;
+//   2. reduce: each workgroup folds its chunk of tiles into one (flag,
+//      value) partial;
+//   3. partials: one workgroup scans the partials in order into each chunk's
+//      exclusive prefix;
+//   4. rescan: each workgroup scans its chunk again, tile by tile, carrying
+//      the prefix into the elements before the first head it meets.
+// A tile learns its heads from the offsets: from the map it reads the
+// segments that can start inside it and marks their starts in an LDS byte
+// map, so no per-element flag array is ever materialised in HBM.  Traffic: two
+// reads of the data and one write, plus two reads of the offsets.
+//
+// Workspace: the map (one 64-bit word per tile, the index as a value below
+// 2^32: a look-back descriptor reader sees such a word as unpublished, so it
+// may stay) and the chunk partials (zeroed by the rescan, as the other
+// reduce-then-scan kernels leave theirs).
+//
+// Compiled once per element type (SW64_DT).
+#include "launch.hpp"
+#include "tile.hpp"
+
+namespace sw64 {
+
+template <class V>
+struct SegVal {
+    V v;
+    uint32_t f;  // a segment head lies in the combined range
+};
+
+template <class Op, class V>
+__device__ __forceinline__ SegVal<V> seg_combine(const SegVal<V> &a, const SegVal<V> &b) {
+    return {b.f ? b.v : Op::apply(a.v, b.v), a.f | b.f};
+}
+
+template <class Op, class V>
+__device__ __forceinline__ SegVal<V> seg_identity() {
+    return {Op::template identity<V>(), 0u};
+}
+
+// Inclusive segmented scan across the 64 lanes in lane order (Kogge-Stone).
+template <class Op, class V>
+__device__ __forceinline__ SegVal<V> wave_seg_scan_incl(SegVal<V> x) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const V pv = __shfl_up(x.v, d, kWave);
+        const uint32_t pf = __shfl_up(x.f, d, kWave);
+        if (lane >= d) x = seg_combine<Op, V>(SegVal<V>{pv, pf}, x);
+    }
+    return x;
+}
+
+// The lane before's inclusive value (the identity in lane 0).
+template <class Op, class V>
+__device__ __forceinline__ SegVal<V> wave_seg_shr1(const SegVal<V> &inc) {
+    const V pv = __shfl_up(inc.v, 1, kWave);
+    const uint32_t pf = __shfl_up(inc.f, 1, kWave);
+    return lane_id() == 0 ? seg_identity<Op, V>() : SegVal<V>{pv, pf};
+}
+
+// A tile of ROWS rows of B * VEC elements, laid out as TileScan's: thread t
+// holds vector (r * B + t) of row r.
+template <class T, class Op, int B, int ROWS, int VEC>
+struct SegTile {
+    using C = typename Carry<T, Op>::type;
+    static constexpr int W = B / kWave;
+    static constexpr int64_t TILE = int64_t(B) * ROWS * VEC;
+    static_assert(TILE % 16 == 0 && ROWS * VEC <= 32, "16-byte clears of the head map, per-thread head bits");
+
+    struct Shared {
+        alignas(16) uint8_t heads[TILE];  // nonzero: element e of the tile starts a segment
+        T tv[ROWS][W];                    // per row and wave: inclusive segmented total
+        uint32_t tf[ROWS][W];
+    };
+
+    Vec<T, VEC> v[ROWS];
+    uint32_t head;    // bit r*VEC+c: this thread's element starts a segment
+    int64_t rem;      // elements of the tile in range
+    SegVal<T> agg;    // tile aggregate
+
+    __device__ __forceinline__ static int64_t elem(int r) { return (int64_t(r) * B + threadIdx.x) * VEC; }
+
+    // Whole tiles load whole vectors; the last, partial tile loads element
+    // by element (any n works with vector access; the identity fills the
+    // rest).
+    __device__ __forceinline__ void load(const T *src, int64_t remaining) {
+        rem = remaining;
+        const T id = Op::template identity<T>();
+        if (remaining >= TILE) {
+#pragma unroll
+            for (int r = 0; r < ROWS; r++) v[r] = load_vec<T, VEC>(src + elem(r));
+            return;
+        }
+#pragma unroll
+        for (int r = 0; r < ROWS; r++) {
+            const int64_t e = elem(r);
+#pragma unroll
+            for (int c = 0; c < VEC; c++) v[r].v[c] = e + c < remaining ? src[e + c] : id;
+        }
+    }
+
+    // Mark the heads of tile t (elements [t0, t0 + TILE)) in LDS and read
+    // this thread's.  The segments that can start in the tile are s0 (the
+    // one holding t0) up to s1 (the one holding the next tile's first
+    // element; nseg for the last tile), both clamped to nseg by the caller,
+    // so invalid offsets give wrong results, never an access out of bounds.
+    // A head is one byte in LDS written with a plain store (empty segments
+    // write the same byte again), so no atomics: consecutive segment starts
+    // a few elements apart would otherwise contend for the same word.  Each
+    // thread issues its offset loads kMarkBatch at a time.  Contains two
+    // barriers.
+    static constexpr int kMarkBatch = 16;
+    __device__ __forceinline__ void mark(Shared &sh, const SegArgs &a, uint32_t t, uint64_t s0, uint64_t s1) {
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+        for (int i = threadIdx.x; i < int(TILE / 16); i += B)
+            reinterpret_cast<u32x4 *>(sh.heads)[i] = u32x4{0u, 0u, 0u, 0u};
+        __syncthreads();
+        const int64_t t0 = int64_t(t) * TILE;
+        for (uint64_t base = s0 + threadIdx.x; base <= s1; base += uint64_t(kMarkBatch) * B) {
+            int64_t o[kMarkBatch];
+#pragma unroll
+            for (int u = 0; u < kMarkBatch; u++) {
+                const uint64_t s = base + uint64_t(u) * B;
+                o[u] = s <= s1 ? int64_t(a.off[s]) - t0 : -1;
+            }
+#pragma unroll
+            for (int u = 0; u < kMarkBatch; u++)
+                if (o[u] >= 0 && o[u] < TILE && o[u] < rem) sh.heads[o[u]] = 1;
+        }
+        __syncthreads();
+        head = 0;
+#pragma unroll
+        for (int r = 0; r < ROWS; r++) {
+            const int64_t e = elem(r);
+#pragma unroll
+            for (int c = 0; c < VEC; c++) head |= uint32_t(sh.heads[e + c] != 0) << (r * VEC + c);
+        }
+    }
+
+    // Scan the tile within itself; afterwards v holds, per element, the
+    // segmented inclusive value (or exclusive with `exclusive`) counted from
+    // the tile's start, `cov` the elements with a head at or before them in
+    // the tile (they ignore any carry), and agg the tile's aggregate.
+    // Contains one barrier; the caller separates reuses of sh.
+    __device__ __forceinline__ void scan(Shared &sh, bool exclusive, uint32_t &cov) {
+        const int wave = threadIdx.x / kWave;
+        SegVal<T> tot[ROWS], ex[ROWS];
+#pragma unroll
+        for (int r = 0; r < ROWS; r++) {
+            SegVal<T> run = seg_identity<Op, T>();
+#pragma unroll
+            for (int c = 0; c < VEC; c++)
+                run = seg_combine<Op, T>(run, SegVal<T>{v[r].v[c], (head >> (r * VEC + c)) & 1u});
+            tot[r] = run;
+        }
+#pragma unroll
+        for (int r = 0; r < ROWS; r++) {
+            const SegVal<T> inc = wave_seg_scan_incl<Op, T>(tot[r]);
+            if (lane_id() == kWave - 1) {
+                sh.tv[r][wave] = inc.v;
+                sh.tf[r][wave] = inc.f;
+            }
+            ex[r] = wave_seg_shr1<Op, T>(inc);
+        }
+        __syncthreads();
+        SegVal<T> run = seg_identity<Op, T>();
+        cov = 0;
+#pragma unroll
+        for (int r = 0; r < ROWS; r++) {
+            SegVal<T> base = run;  // everything before this row, then before this wave
+            for (int w = 0; w < W; w++) {
+                const SegVal<T> x{sh.tv[r][w], sh.tf[r][w]};
+                if (w < wave) base = seg_combine<Op, T>(base, x);
+                run = seg_combine<Op, T>(run, x);
+            }
+            SegVal<T> prev = seg_combine<Op, T>(base, ex[r]);  // before this thread's vector
+#pragma unroll
+            for (int c = 0; c < VEC; c++) {
+                const SegVal<T> x{v[r].v[c], (head >> (r * VEC + c)) & 1u};
+                const SegVal<T> inc = seg_combine<Op, T>(prev, x);
+                const SegVal<T> out = exclusive ? (x.f ? SegVal<T>{Op::template identity<T>(), 1u} : prev) : inc;
+                v[r].v[c] = out.v;
+                cov |= out.f << (r * VEC + c);
+                prev = inc;
+            }
+        }
+        agg = run;
+    }
+
+    // Only the aggregate (the reduce pass).  Contains one barrier.
+    __device__ __forceinline__ void reduce(Shared &sh) {
+        const int wave = threadIdx.x / kWave;
+#pragma unroll
+        for (int r = 0; r < ROWS; r++) {
+            SegVal<T> run = seg_identity<Op, T>();
+#pragma unroll
+            for (int c = 0; c < VEC; c++)
+                run = seg_combine<Op, T>(run, SegVal<T>{v[r].v[c], (head >> (r * VEC + c)) & 1u});
+            const SegVal<T> inc = wave_seg_scan_incl<Op, T>(run);
+            if (lane_id() == kWave - 1) {
+                sh.tv[r][wave] = inc.v;
+                sh.tf[r][wave] = inc.f;
+            }
+        }
+        __syncthreads();
+        SegVal<T> run = seg_identity<Op, T>();
+        for (int r = 0; r < ROWS; r++)
+            for (int w = 0; w < W; w++) run = seg_combine<Op, T>(run, SegVal<T>{sh.tv[r][w], sh.tf[r][w]});
+        agg = run;
+    }
+
+    // Store: elements without a head at or before them in the tile get the
+    // carry in front (in the carry type, rounded once).
+    // (Whole vectors for whole tiles, element by element in the last one.)
+    __device__ __forceinline__ void store(T *dst, int64_t remaining, C carry, uint32_t cov) const {
+        const BufRsrc rs = make_rsrc(dst, remaining < TILE ? (remaining > 0 ? remaining : 0) : TILE);
+#pragma unroll
+        for (int r = 0; r < ROWS; r++) {
+            Vec<T, VEC> o;
+#pragma unroll
+            for (int c = 0; c < VEC; c++) {
+                const bool own = (cov >> (r * VEC + c)) & 1u;
+                o.v[c] = own ? v[r].v[c] : T(Op::apply(carry, C(v[r].v[c])));
+            }
+            if (remaining >= TILE) {
+                store_vec_bounded<T, VEC>(rs, uint32_t(elem(r) * int64_t(sizeof(T))), o);
+            } else {
+#pragma unroll
+                for (int c = 0; c < VEC; c++)
+                    store_vec_bounded<T, 1>(rs, uint32_t((elem(r) + c) * int64_t(sizeof(T))), Vec<T, 1>{{o.v[c]}});
+            }
+        }
+    }
+};
+
+// Pass 1: the tile -> segment map (a template only so that each element
+// type's unit has its own instance).
+template <class T>
+__global__ __launch_bounds__(256) void k_seg_map(SegArgs a) {
+    for (int64_t s = int64_t(blockIdx.x) * 256 + threadIdx.x; s < a.nseg; s += int64_t(gridDim.x) * 256) {
+        const int64_t b = a.off[s], e = a.off[s + 1];
+        if (e <= b || b < 0) continue;
+        // tiles are a power of two long: the first tile starting at or after b
+        const int64_t t0 = (b + a.tile - 1) >> a.tile_log2;
+        for (int64_t t = t0; (t << a.tile_log2) < e && t < int64_t(a.num_tiles); t++) a.map[t] = uint64_t(s);
+    }
+}
+
+// The map entries a chunk's tiles need (its tiles and the next one), read
+// once into LDS when they fit, each clamped to nseg.
+constexpr int kSegMapCache = 64;
+
+struct SegChunkMap {
+    uint64_t m[kSegMapCache + 1];
+
+    __device__ __forceinline__ void load(const SegArgs &a, uint64_t t0, uint64_t t1) {
+        if (t1 - t0 <= uint64_t(kSegMapCache)) {
+            for (uint64_t i = threadIdx.x; i <= t1 - t0; i += blockDim.x) {
+                const uint64_t t = t0 + i;
+                const uint64_t v = t < a.num_tiles ? a.map[t] : uint64_t(a.nseg);
+                m[i] = v < uint64_t(a.nseg) ? v : uint64_t(a.nseg);
+            }
+        }
+        __syncthreads();
+    }
+    __device__ __forceinline__ uint64_t get(const SegArgs &a, uint64_t t0, uint64_t t1, uint64_t t) const {
+        if (t1 - t0 <= uint64_t(kSegMapCache)) return m[t - t0];
+        const uint64_t v = t < a.num_tiles ? a.map[t] : uint64_t(a.nseg);
+        return v < uint64_t(a.nseg) ? v : uint64_t(a.nseg);
+    }
+};
+
+template <class T, class Op>
+struct SegPartial {
+    typename Carry<T, Op>::type v;
+    uint32_t f, pad;
+};
+
+template <class T, class Op, int B, int R, int V>
+__global__ __launch_bounds__(B) void k_seg_reduce(SegArgs a) {
+    using ST = SegTile<T, Op, B, R, V>;
+    using C = typename ST::C;
+    __shared__ typename ST::Shared sh;
+    __shared__ SegChunkMap cm;
+    const uint64_t t0 = uint64_t(blockIdx.x) * a.chunk_tiles;
+    const uint64_t t1 = t0 + a.chunk_tiles < a.num_tiles ? t0 + a.chunk_tiles : a.num_tiles;
+    cm.load(a, t0, t1);
+    SegVal<C> acc = seg_identity<Op, C>();
+    ST st;
+    for (uint64_t t = t0; t < t1; t++) {
+        const int64_t start = int64_t(t) * ST::TILE;
+        st.load(reinterpret_cast<const T *>(a.in) + start, a.n - start);
+        st.mark(sh, a, uint32_t(t), cm.get(a, t0, t1, t), cm.get(a, t0, t1, t + 1));
+        st.reduce(sh);
+        acc = seg_combine<Op, C>(acc, SegVal<C>{C(st.agg.v), st.agg.f});
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        SegPartial<T, Op> *p = reinterpret_cast<SegPartial<T, Op> *>(a.partials);
+        p[blockIdx.x].v = acc.v;
+        p[blockIdx.x].f = acc.f;
+    }
+}
+
+// Pass 3: one workgroup of 256 threads scans the chunk partials in order;
+// thread k owns a run of up to kSegPartPer consecutive chunks.
+constexpr int kSegPartThreads = 256, kSegPartPer = 8;
+
+template <class T, class Op>
+__global__ __launch_bounds__(kSegPartThreads) void k_seg_partials(SegArgs a) {
+    using C = typename Carry<T, Op>::type;
+    __shared__ C wv[kSegPartThreads / kWave];
+    __shared__ uint32_t wf[kSegPartThreads / kWave];
+    SegPartial<T, Op> *p = reinterpret_cast<SegPartial<T, Op> *>(a.partials);
+    const uint32_t per = (a.blocks + kSegPartThreads - 1) / kSegPartThreads;  // <= kSegPartPer
+    const uint32_t c0 = threadIdx.x * per;
+    SegVal<C> x[kSegPartPer];
+    SegVal<C> run = seg_identity<Op, C>();
+#pragma unroll
+    for (int i = 0; i < kSegPartPer; i++) {
+        x[i] = seg_identity<Op, C>();
+        if (uint32_t(i) < per && c0 + i < a.blocks) x[i] = SegVal<C>{p[c0 + i].v, p[c0 + i].f};
+        run = seg_combine<Op, C>(run, x[i]);
+    }
+    const int wave = threadIdx.x / kWave;
+    const SegVal<C> inc = wave_seg_scan_incl<Op, C>(run);
+    if (lane_id() == kWave - 1) {
+        wv[wave] = inc.v;
+        wf[wave] = inc.f;
+    }
+    __syncthreads();
+    SegVal<C> pre = seg_identity<Op, C>();
+    for (int w = 0; w < wave; w++) pre = seg_combine<Op, C>(pre, SegVal<C>{wv[w], wf[w]});
+    pre = seg_combine<Op, C>(pre, wave_seg_shr1<Op, C>(inc));
+#pragma unroll
+    for (int i = 0; i < kSegPartPer; i++) {
+        if (uint32_t(i) < per && c0 + i < a.blocks) {
+            p[c0 + i].v = pre.v;  // the value carried into the chunk
+            p[c0 + i].f = pre.f;
+            pre = seg_combine<Op, C>(pre, x[i]);
+        }
+    }
+}
+
+template <class T, class Op, int B, int R, int V>
+__global__ __launch_bounds__(B) void k_seg_rescan(SegArgs a) {
+    using ST = SegTile<T, Op, B, R, V>;
+    using C = typename ST::C;
+    __shared__ typename ST::Shared sh;
+    __shared__ C s_carry;
+    SegPartial<T, Op> *p = reinterpret_cast<SegPartial<T, Op> *>(a.partials);
+    if (threadIdx.x == 0) s_carry = p[blockIdx.x].v;
+    __syncthreads();
+    C carry = s_carry;
+    if (threadIdx.x == 0) p[blockIdx.x] = SegPartial<T, Op>{};  // leave the workspace zeroed
+    const uint64_t t0 = uint64_t(blockIdx.x) * a.chunk_tiles;
+    const uint64_t t1 = t0 + a.chunk_tiles < a.num_tiles ? t0 + a.chunk_tiles : a.num_tiles;
+    __shared__ SegChunkMap cm;
+    cm.load(a, t0, t1);
+    ST st;
+    for (uint64_t t = t0; t < t1; t++) {
+        const int64_t start = int64_t(t) * ST::TILE;
+        st.load(reinterpret_cast<const T *>(a.in) + start, a.n - start);
+        st.mark(sh, a, uint32_t(t), cm.get(a, t0, t1, t), cm.get(a, t0, t1, t + 1));
+        uint32_t cov;
+        st.scan(sh, a.exclusive != 0, cov);
+        st.store(reinterpret_cast<T *>(a.out) + start, a.n - start, carry, cov);
+        carry = st.agg.f ? C(st.agg.v) : Op::apply(carry, C(st.agg.v));
+        __syncthreads();
+    }
+}
+
+template <class T, class Op, int B, int R, int V>
+static int launch_seg_impl(const SegArgs &a, hipStream_t s) {
+    if (a.blocks < 1 || a.blocks > uint32_t(kSegPartThreads * kSegPartPer)) return SCAN_ERR_UNSUPPORTED;
+    if (a.tile != SegTile<T, Op, B, R, V>::TILE || (int64_t(1) << a.tile_log2) != a.tile) return SCAN_ERR_UNSUPPORTED;
+    const int64_t mg = (a.nseg + 255) / 256;
+    hipLaunchKernelGGL(k_seg_map<T>, dim3(unsigned(mg < 4096 ? (mg > 0 ? mg : 1) : 4096)), dim3(256), 0, s, a);
+    if (hipGetLastError() != hipSuccess) return SCAN_ERR_HIP;
+    hipLaunchKernelGGL((k_seg_reduce<T, Op, B, R, V>), dim3(a.blocks), dim3(B), 0, s, a);
+    if (hipGetLastError() != hipSuccess) return SCAN_ERR_HIP;
+    hipLaunchKernelGGL((k_seg_partials<T, Op>), dim3(1), dim3(kSegPartThreads), 0, s, a);
+    if (hipGetLastError() != hipSuccess) return SCAN_ERR_HIP;
+    hipLaunchKernelGGL((k_seg_rescan<T, Op, B, R, V>), dim3(a.blocks), dim3(B), 0, s, a);
+    return hipGetLastError() == hipSuccess ? SCAN_OK : SCAN_ERR_HIP;
+}
+
+// Shapes: 512 threads x 8 rows of 4-byte vectors (4 rows for 8-byte
+// elements), and 256 x 1 (small tiles for tests); element-wide variants.
+template <class T, class Op, int V>
+static SegLaunch pick_seg_shape(int block, int rows) {
+    if (block == 256 && rows == 1) return &launch_seg_impl<T, Op, 256, 1, V>;
+    if constexpr (sizeof(T) == 4) {
+        if (block == 512 && rows == 8) return &launch_seg_impl<T, Op, 512, 8, V>;
+    } else {
+        if (block == 512 && rows == 4) return &launch_seg_impl<T, Op, 512, 4, V>;
+    }
+    return nullptr;
+}
+
+template <class T, class Op>
+static SegLaunch pick_seg_vec(int block, int rows, int vec) {
+    constexpr int VMAX = 16 / int(sizeof(T));
+    if (vec == VMAX) return pick_seg_shape<T, Op, VMAX>(block, rows);
+    if (vec == 1) return pick_seg_shape<T, Op, 1>(block, rows);
+    return nullptr;
+}
+
+template <class T>
+static SegLaunch pick_seg_op(scan_op_t op, int block, int rows, int vec) {
+    switch (op) {
+    case SCAN_OP_SUM: return pick_seg_vec<T, OpSum>(block, rows, vec);
+    case SCAN_OP_PROD: return pick_seg_vec<T, OpProd>(block, rows, vec);
+    case SCAN_OP_MAX: return pick_seg_vec<T, OpMax>(block, rows, vec);
+    case SCAN_OP_MIN: return pick_seg_vec<T, OpMin>(block, rows, vec);
+    }
+    return nullptr;
+}
+
+#if SW64_DT == 0
+SegLaunch find_seg_i32(scan_op_t op, int b, int r, int v) { return pick_seg_op<int32_t>(op, b, r, v); }
+#elif SW64_DT == 1
+SegLaunch find_seg_u32(scan_op_t op, int b, int r, int v) { return pick_seg_op<uint32_t>(op, b, r, v); }
+#elif SW64_DT == 2
+SegLaunch find_seg_i64(scan_op_t op, int b, int r, int v) { return pick_seg_op<int64_t>(op, b, r, v); }
+#elif SW64_DT == 3
+SegLaunch find_seg_f32(scan_op_t op, int b, int r, int v) { return pick_seg_op<float>(op, b, r, v); }
+#elif SW64_DT == 4
+SegLaunch find_seg_f64(scan_op_t op, int b, int r, int v) { return pick_seg_op<double>(op, b, r, v); }
+#else
+#error "SW64_DT must select an element type (0..4)"
+#endif
+
+}  // namespace sw64

@@ -14,6 +14,8 @@ time (synthetic arrays only; no dataset is involved):
                 of 1e7, seed 4
   structs       uniform [-1, 1) 17 x fp64 per element, then 24 x fp32 per
                 element as 2*u - 1 (exact, multiples of 2^-23), seed 5
+  segments      the compaction draw's Poisson(3) counts as segment lengths,
+                then one uniform [0, 1) float32 value per record, seed 4
 
 Each generator takes the element count so the tests can draw smaller arrays
 of the same distribution.
@@ -86,3 +88,14 @@ def generic(dtype, n: int, seed: int, kind: str = "default") -> np.ndarray:
             return 0.999 + 0.002 * rng.random(n)
         return rng.uniform(-1.0, 1.0, n)
     raise TypeError(dt)
+
+
+def segmented_inputs(nseg: int = 10 ** 7, seed: int = 4, lam: float = 3.0):
+    """(counts int32, values float32): the Poisson(lam) counts of
+    compaction_inputs(nseg, seed) as segment lengths, then one uniform [0, 1)
+    value per record, drawn next from the same generator."""
+    rng = np.random.default_rng(seed)
+    rng.random(nseg, dtype=np.float32)  # the compaction draw comes first
+    counts = rng.poisson(lam, nseg).astype(np.int32)
+    values = rng.random(int(counts.sum(dtype=np.int64)), dtype=np.float32)
+    return counts, values

@@ -68,3 +68,31 @@ def assert_scan_matches(x: np.ndarray, got: np.ndarray, op: str, exclusive: bool
     bad = np.flatnonzero(~(err <= tol))
     assert bad.size == 0, (f"{what}: {bad.size} outside tolerance, worst at "
                            f"{int(np.argmax(err - tol))}: err {err.max():.3e}")
+
+
+def assert_segscan_matches(x: np.ndarray, off: np.ndarray, got: np.ndarray, op: str, exclusive: bool, what=""):
+    """A device segmented scan against the oracle, under the same rules as a
+    plain scan with P_i and the product's rounding counted within each
+    segment."""
+    ref = oracle.scan_segmented(x, off, op, exclusive=exclusive)
+    got = np.asarray(got).ravel()
+    if np.issubdtype(x.dtype, np.integer) or op in ("max", "min"):
+        if np.issubdtype(x.dtype, np.floating):
+            ref = ref.astype(x.dtype)
+        bad = np.flatnonzero(got != ref)
+        assert bad.size == 0, (f"{what}: {bad.size} mismatches, first at {bad[0]}: "
+                               f"got {got[bad[0]]} want {ref[bad[0]]}")
+        return
+    g = got.astype(np.float64)
+    if op == "sum":
+        p = oracle.segment_abs_prefix(x, off, exclusive=exclusive)
+        tol = F32_REL * p + F32_ABS if x.dtype == np.float32 else F64_REL * p
+    else:  # prod: one rounding per factor within the segment
+        start = np.repeat(off[:-1].astype(np.int64), np.diff(off.astype(np.int64)))
+        factors = np.arange(x.size) - start + (0 if exclusive else 1)
+        tol = 1.01 * factors * UNIT_ROUNDOFF[x.dtype.type] * np.abs(ref) + \
+            (1e-37 if x.dtype == np.float32 else 1e-300)
+    err = np.abs(g - ref)
+    bad = np.flatnonzero(~(err <= tol))
+    assert bad.size == 0, (f"{what}: {bad.size} outside tolerance, worst at "
+                           f"{int(np.argmax(err - tol))}: err {err.max():.3e}")

@@ -129,6 +129,29 @@ def test_argument_errors_before_launch(lib):
     assert lib.partition_if(fake, 10, 3, 0, d(0.5), None, None, fake, ws, 1 << 20, None, None) == -1  # NULL out
 
 
+def test_segmented_argument_errors_and_plan(lib):
+    from stream_compaction_wave64_amd import binding
+    import torch
+    fake = ctypes.c_void_p(1 << 20)
+    ws = ctypes.c_void_p(1 << 24)
+    seg = lambda n, nseg, off=fake, dt=3, op=0: lib.scan_segmented(fake, fake, n, off, nseg, dt, op, 0, ws, 1 << 20,
+                                                                   None, None)
+    assert seg(0, 0) == 0            # empty: no-op
+    assert seg(-1, 1) == -1
+    assert seg(10, -1) == -1
+    assert seg(10, 0) == -1          # elements but no segment
+    assert seg(10, 2, off=None) == -1
+    assert seg(10, 2, dt=9) == -1
+    assert seg(10, 2, op=7) == -1
+    assert seg(1 << 31, 2) == -5
+    for dt in (torch.int32, torch.float32, torch.float64, torch.int64):
+        for n in (1, 1000, 10 ** 7, 3 * 10 ** 7):
+            p = binding.plan("segmented", dt, "sum", n // 3 + 1, n)
+            assert p["kernel"] == "segmented" and p["launches"] == 4
+            assert p["num_tiles"] == -(-n // p["tile_elems"])
+            assert 4096 + p["num_tiles"] * 8 <= p["workspace_bytes"] <= binding.scan_workspace_bytes(dt, n)
+
+
 def test_plan_partition():
     from stream_compaction_wave64_amd import binding
     import torch
