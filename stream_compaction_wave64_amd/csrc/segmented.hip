@@ -122,19 +122,19 @@ struct SegTile {
     // a few elements apart would otherwise contend for the same word.  Each
     // thread issues its offset loads kMarkBatch at a time.  Contains two
     // barriers.
-    static constexpr int kMarkBatch = 16;
+    static constexpr int kMarkBatch = 8;
     __device__ __forceinline__ void mark(Shared &sh, const SegArgs &a, uint32_t t, uint64_t s0, uint64_t s1) {
         typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
         for (int i = threadIdx.x; i < int(TILE / 16); i += B)
             reinterpret_cast<u32x4 *>(sh.heads)[i] = u32x4{0u, 0u, 0u, 0u};
         __syncthreads();
-        const int64_t t0 = int64_t(t) * TILE;
+        const int32_t t0 = int32_t(int64_t(t) * TILE);  // n <= INT32_MAX
         for (uint64_t base = s0 + threadIdx.x; base <= s1; base += uint64_t(kMarkBatch) * B) {
-            int64_t o[kMarkBatch];
+            int32_t o[kMarkBatch];  // offsets and tile starts are in [0, 2^31): the difference fits
 #pragma unroll
             for (int u = 0; u < kMarkBatch; u++) {
                 const uint64_t s = base + uint64_t(u) * B;
-                o[u] = s <= s1 ? int64_t(a.off[s]) - t0 : -1;
+                o[u] = s <= s1 ? a.off[s] - t0 : -1;
             }
 #pragma unroll
             for (int u = 0; u < kMarkBatch; u++)
@@ -145,8 +145,12 @@ struct SegTile {
 #pragma unroll
         for (int r = 0; r < ROWS; r++) {
             const int64_t e = elem(r);
+            uint32_t bytes;  // this thread's VEC head bytes of row r, one LDS read
+            if constexpr (VEC == 4) bytes = *reinterpret_cast<const uint32_t *>(sh.heads + e);
+            else if constexpr (VEC == 2) bytes = *reinterpret_cast<const uint16_t *>(sh.heads + e);
+            else bytes = sh.heads[e];
 #pragma unroll
-            for (int c = 0; c < VEC; c++) head |= uint32_t(sh.heads[e + c] != 0) << (r * VEC + c);
+            for (int c = 0; c < VEC; c++) head |= uint32_t(((bytes >> (8 * c)) & 0xffu) != 0u) << (r * VEC + c);
         }
     }
 
@@ -157,18 +161,14 @@ struct SegTile {
     // Contains one barrier; the caller separates reuses of sh.
     __device__ __forceinline__ void scan(Shared &sh, bool exclusive, uint32_t &cov) {
         const int wave = threadIdx.x / kWave;
-        SegVal<T> tot[ROWS], ex[ROWS];
+        SegVal<T> ex[ROWS];  // per row: the segmented value before this thread's vector, within its wave
 #pragma unroll
         for (int r = 0; r < ROWS; r++) {
             SegVal<T> run = seg_identity<Op, T>();
 #pragma unroll
             for (int c = 0; c < VEC; c++)
                 run = seg_combine<Op, T>(run, SegVal<T>{v[r].v[c], (head >> (r * VEC + c)) & 1u});
-            tot[r] = run;
-        }
-#pragma unroll
-        for (int r = 0; r < ROWS; r++) {
-            const SegVal<T> inc = wave_seg_scan_incl<Op, T>(tot[r]);
+            const SegVal<T> inc = wave_seg_scan_incl<Op, T>(run);
             if (lane_id() == kWave - 1) {
                 sh.tv[r][wave] = inc.v;
                 sh.tf[r][wave] = inc.f;
@@ -181,6 +181,7 @@ struct SegTile {
 #pragma unroll
         for (int r = 0; r < ROWS; r++) {
             SegVal<T> base = run;  // everything before this row, then before this wave
+#pragma unroll 1
             for (int w = 0; w < W; w++) {
                 const SegVal<T> x{sh.tv[r][w], sh.tf[r][w]};
                 if (w < wave) base = seg_combine<Op, T>(base, x);
