@@ -65,7 +65,7 @@ struct SegArgs {
     int32_t tile_log2;
     uint32_t num_tiles;
     uint32_t chunk_tiles;
-    uint32_t blocks;          // chunks (<= 2048)
+    uint32_t blocks;          // chunks (<= 8192)
     int32_t exclusive;
 };
 using SegLaunch = int (*)(const SegArgs &, hipStream_t);

@@ -316,9 +316,9 @@ __global__ __launch_bounds__(B) void k_seg_reduce(SegArgs a) {
     }
 }
 
-// Pass 3: one workgroup of 256 threads scans the chunk partials in order;
+// Pass 3: one workgroup of 1024 threads scans the chunk partials in order;
 // thread k owns a run of up to kSegPartPer consecutive chunks.
-constexpr int kSegPartThreads = 256, kSegPartPer = 8;
+constexpr int kSegPartThreads = 1024, kSegPartPer = 8;
 
 template <class T, class Op>
 __global__ __launch_bounds__(kSegPartThreads) void k_seg_partials(SegArgs a) {
@@ -399,13 +399,20 @@ static int launch_seg_impl(const SegArgs &a, hipStream_t s) {
     return hipGetLastError() == hipSuccess ? SCAN_OK : SCAN_ERR_HIP;
 }
 
-// Shapes: 512 threads x 8 rows of 4-byte vectors (4 rows for 8-byte
-// elements), and 256 x 1 (small tiles for tests); element-wide variants.
+// Shapes: the default 256 threads x 2 rows, the ones the tuning sweep
+// visits, and 256 x 1 (the smallest tiles, for tests); element-wide
+// variants of each.
 template <class T, class Op, int V>
 static SegLaunch pick_seg_shape(int block, int rows) {
     if (block == 256 && rows == 1) return &launch_seg_impl<T, Op, 256, 1, V>;
+    if (block == 256 && rows == 2) return &launch_seg_impl<T, Op, 256, 2, V>;
+    if (block == 256 && rows == 4) return &launch_seg_impl<T, Op, 256, 4, V>;
+    if (block == 512 && rows == 1) return &launch_seg_impl<T, Op, 512, 1, V>;
+    if (block == 512 && rows == 2) return &launch_seg_impl<T, Op, 512, 2, V>;
+    if (block == 128 && rows == 2) return &launch_seg_impl<T, Op, 128, 2, V>;
     if constexpr (sizeof(T) == 4) {
         if (block == 512 && rows == 8) return &launch_seg_impl<T, Op, 512, 8, V>;
+        if (block == 512 && rows == 4) return &launch_seg_impl<T, Op, 512, 4, V>;
     } else {
         if (block == 512 && rows == 4) return &launch_seg_impl<T, Op, 512, 4, V>;
     }
