@@ -95,7 +95,7 @@ constexpr int kDefaultBlock = 512;  // threads per workgroup of the tiled kernel
 constexpr int kDefaultRtsBlocks = 1024;               // C of reduce-then-scan
 constexpr int64_t kDefaultLocalMem = 64 * 1024;       // LDS budget of the large-element rule
 constexpr int kElemDefaultBlock = 256;                // large elements: start of the rule
-constexpr int64_t kElemChunks = 2048;  // large elements: workgroups per launch (<= 2048, the partials pass)
+constexpr int64_t kElemChunks = 2048;  // large elements: workgroups per launch (<= 8192, the partials pass)
 
 // AcceleratedKernels.jl PR #208, first bullet: an explicit block size is kept
 // as given; an unset one starts at the default and is lowered to the largest
@@ -256,7 +256,8 @@ int plan_element(scan_dtype_t dt, scan_op_t op, int64_t outer, int64_t len, int6
     p.tiles_per_seg = (len + p.tile - 1) / p.tile;
     p.num_tiles = outer * p.tiles_per_seg;
     if (p.num_tiles > int64_t(INT32_MAX)) return SCAN_ERR_OVERFLOW;
-    int64_t chunks = (kElemChunks + outer - 1) / outer;
+    const int64_t want = tu.rts_blocks > 0 ? (tu.rts_blocks < 8192 ? tu.rts_blocks : 8192) : kElemChunks;
+    int64_t chunks = (want + outer - 1) / outer;
     if (chunks > p.tiles_per_seg) chunks = p.tiles_per_seg;
     if (chunks < 1) chunks = 1;
     p.rts_chunk = (p.tiles_per_seg + chunks - 1) / chunks;      // tiles per chunk

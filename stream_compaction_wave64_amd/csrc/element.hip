@@ -266,7 +266,7 @@ __global__ __launch_bounds__(kElemMaxThreads) void k_elem_rescan(ElemArgs a) {
 // into exclusive prefixes: each thread loads a run of up to kElemPartPer
 // consecutive chunks at once (one round trip), folds it, then a workgroup
 // scan of the runs, and writes the run's prefixes back from registers.
-constexpr int kElemPartThreads = 256, kElemPartPer = 8;
+constexpr int kElemPartThreads = 1024, kElemPartPer = 8;
 constexpr int kElemMaxChunks = kElemPartThreads * kElemPartPer;
 
 template <class T, class Op, int W>

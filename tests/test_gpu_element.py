@@ -47,6 +47,25 @@ def test_struct_scan_other_ops(op, w):
         assert_scan_matches(x.ravel(), to_host(r).ravel(), op, False, dims=(1, x.shape[0], w), what=f"{dt} {op}")
 
 
+@pytest.mark.parametrize("w,dt,n", [(24, np.float32, 600_001), (17, np.float64, 300_001), (8, np.int32, 300_001)])
+def test_struct_scan_many_chunks(w, dt, n):
+    # more than 2048 chunks: the partials pass runs several chunks per thread
+    # of its 1024; and a single chunk holding every tile
+    x = _struct_input(dt, n, w, 90 + w, "sum")
+    for tuning in ({"rts_blocks": 8192, "block_size": 64}, {"rts_blocks": 1, "block_size": 64}):
+        for excl in (False, True):
+            fn = sw.scan_exclusive if excl else sw.scan_inclusive
+            r = fn(to_dev(x), width=w, tuning=tuning)
+            torch.cuda.synchronize()
+            assert_scan_matches(x.ravel(), to_host(r).ravel(), "sum", excl, dims=(1, n, w),
+                                what=f"w={w} {tuning} excl={excl}")
+    # segments (outer > 1) each get their own run of chunks
+    xs = x[: (n // 3) * 3].reshape(3, n // 3, w)
+    r = sw.scan_dim(to_dev(xs), 1, tuning={"rts_blocks": 8192, "block_size": 64})
+    torch.cuda.synchronize()
+    assert_scan_matches(xs.ravel(), to_host(r).ravel(), "sum", False, dims=xs.shape, what="3 segments")
+
+
 def test_dim_small_inner_segments():
     # (outer, len, inner) with outer > 1: each outer slice scanned independently
     rng = np.random.default_rng(81)
