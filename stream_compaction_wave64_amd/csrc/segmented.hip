@@ -50,25 +50,32 @@ __device__ __forceinline__ SegVal<V> seg_identity() {
     return {Op::template identity<V>(), 0u};
 }
 
-// Inclusive segmented scan across the 64 lanes in lane order (Kogge-Stone).
+// Inclusive segmented scan across the 64 lanes in lane order: the DPP
+// Kogge-Stone rounds of wave_scan_incl (shift 1, 2, 4, 8 inside each
+// 16-lane row, then lane 15 and lane 31 broadcasts), moving the value and the
+// flag.  A lane whose source lies outside its row receives the identity pair
+// (identity, no head), which combines as a no-op, as in the plain scan.
+template <int CTRL, int ROW_MASK, class Op, class V>
+__device__ __forceinline__ SegVal<V> seg_dpp_round(const SegVal<V> &x) {
+    const SegVal<V> p{dpp_mov<CTRL, ROW_MASK>(Op::template identity<V>(), x.v), dpp_mov<CTRL, ROW_MASK>(0u, x.f)};
+    return seg_combine<Op, V>(p, x);
+}
+
 template <class Op, class V>
 __device__ __forceinline__ SegVal<V> wave_seg_scan_incl(SegVal<V> x) {
-    const int lane = lane_id();
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        const V pv = __shfl_up(x.v, d, kWave);
-        const uint32_t pf = __shfl_up(x.f, d, kWave);
-        if (lane >= d) x = seg_combine<Op, V>(SegVal<V>{pv, pf}, x);
-    }
+    x = seg_dpp_round<kRowShr1, 0xf, Op>(x);
+    x = seg_dpp_round<kRowShr2, 0xf, Op>(x);
+    x = seg_dpp_round<kRowShr4, 0xf, Op>(x);
+    x = seg_dpp_round<kRowShr8, 0xf, Op>(x);
+    x = seg_dpp_round<kRowBcast15, 0xa, Op>(x);
+    x = seg_dpp_round<kRowBcast31, 0xc, Op>(x);
     return x;
 }
 
-// The lane before's inclusive value (the identity in lane 0).
+// The lane before's inclusive value (the identity pair in lane 0).
 template <class Op, class V>
 __device__ __forceinline__ SegVal<V> wave_seg_shr1(const SegVal<V> &inc) {
-    const V pv = __shfl_up(inc.v, 1, kWave);
-    const uint32_t pf = __shfl_up(inc.f, 1, kWave);
-    return lane_id() == 0 ? seg_identity<Op, V>() : SegVal<V>{pv, pf};
+    return SegVal<V>{wave_shr1(Op::template identity<V>(), inc.v), wave_shr1(0u, inc.f)};
 }
 
 // A tile of ROWS rows of B * VEC elements, laid out as TileScan's: thread t
