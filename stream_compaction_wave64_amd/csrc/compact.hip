@@ -434,12 +434,15 @@ __global__ __launch_bounds__(kEmitThreads) void k_emit_neighbors(const int32_t *
         for (int j = threadIdx.x; j < cnt; j += kEmitThreads) {
             const int64_t b = off[j], e = off[j + 1];
             const int64_t lo = b > w0 ? b : w0, hi = e < w1 ? e : w1;
-            int64_t r = i0 + j + 1 + (lo - b);  // record value, (i + 1 + j) mod n
-            if (r >= n) r -= n;
-            if (r >= n) r %= n;
-            for (int64_t k = lo; k < hi; k++) {
-                win[k - w0] = int32_t(r);
-                r = r + 1 == n ? 0 : r + 1;
+            int64_t r0 = i0 + j + 1 + (lo - b);  // first record value, (i + 1 + j) mod n
+            if (r0 >= n) r0 -= n;
+            if (r0 >= n) r0 %= n;
+            // within the window everything fits 32 bits (n <= INT32_MAX)
+            const int32_t n32 = int32_t(n), k1 = int32_t(hi - w0);
+            int32_t r = int32_t(r0);
+            for (int32_t k = int32_t(lo - w0); k < k1; k++) {
+                win[k] = r;
+                r = r + 1 == n32 ? 0 : r + 1;
             }
         }
         __syncthreads();
