@@ -420,11 +420,21 @@ constexpr int kEmitThreads = 256, kEmitObjects = 1024, kEmitWindow = 4096;
 
 __global__ __launch_bounds__(kEmitThreads) void k_emit_neighbors(const int32_t *offsets, int64_t n, int32_t *out) {
     typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
-    __shared__ int32_t off[kEmitObjects + 1];
+    static_assert(kEmitObjects == 4 * kEmitThreads, "one 16-byte offsets load per thread");
+    __shared__ __attribute__((aligned(16))) int32_t off[kEmitObjects + 4];
     __shared__ __attribute__((aligned(16))) int32_t win[kEmitWindow + 4];
     const int64_t i0 = int64_t(blockIdx.x) * kEmitObjects;
     const int cnt = int(n - i0 < kEmitObjects ? n - i0 : kEmitObjects);
-    for (int t = threadIdx.x; t <= cnt; t += kEmitThreads) off[t] = offsets[i0 + t];
+    const int32_t *src = offsets + i0;
+    if (cnt == kEmitObjects && (reinterpret_cast<uintptr_t>(src) & 15u) == 0) {
+        // all of the workgroup's offset loads in flight at once
+        const i32x4 v = *reinterpret_cast<const i32x4 *>(src + 4 * threadIdx.x);
+        const int32_t last = threadIdx.x == 0 ? src[kEmitObjects] : 0;
+        *reinterpret_cast<i32x4 *>(off + 4 * threadIdx.x) = v;
+        if (threadIdx.x == 0) off[kEmitObjects] = last;
+    } else {
+        for (int t = threadIdx.x; t <= cnt; t += kEmitThreads) off[t] = src[t];
+    }
     __syncthreads();
     const int64_t ob = off[0], oe = off[cnt];
     // windows start where out + k is 16-byte aligned
