@@ -416,7 +416,7 @@ PartitionLaunch find_partition(scan_dtype_t dt, scan_cmp_t cmp, int block, int r
 // gives 4-byte stores scattered by the counts, which measured 2.4x slower.
 // A range longer than the window is done in several windows, so any counts
 // work; Poisson(3) counts fill one window per workgroup.
-constexpr int kEmitThreads = 256, kEmitObjects = 1024, kEmitWindow = 4096;
+constexpr int kEmitThreads = 256, kEmitObjects = 1024, kEmitWindow = 3968;
 
 __global__ __launch_bounds__(kEmitThreads) void k_emit_neighbors(const int32_t *offsets, int64_t n, int32_t *out) {
     typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
