@@ -26,7 +26,7 @@
 
 namespace sw64 {
 
-constexpr int kColThreads = 256;
+constexpr int kColThreads = 256, kColBatch = 16;
 
 // Workgroup index -> (outer slice, row chunk, column strip).
 __device__ __forceinline__ static void col_decode(const ColArgs &a, uint32_t wg, uint32_t &o, uint32_t &c,
@@ -50,17 +50,24 @@ __global__ __launch_bounds__(kColThreads) void k_col_reduce(ColArgs a) {
 #pragma unroll
     for (int v = 0; v < V; v++) acc[v] = Op::template identity<C>();
     // V > 1 only when inner is a multiple of V with 16-byte aligned rows, so
-    // a thread's V columns are one aligned 128-bit access per row.
-#pragma unroll 8
-    for (int64_t r = r0; r < r1; r++) {
-        const T *p = src + r * a.inner;
-        if constexpr (V > 1) {
-            const Vec<T, V> x = *reinterpret_cast<const Vec<T, V> *>(p);
+    // a thread's V columns are one aligned 128-bit access per row.  Rows go
+    // in batches of kColBatch whose loads are all issued before the first is
+    // folded: the grid is about one workgroup wave, so nothing else hides
+    // the round trips.
+    int64_t r = r0;
+    for (; r + kColBatch <= r1; r += kColBatch) {
+        Vec<T, V> x[kColBatch];
 #pragma unroll
-            for (int v = 0; v < V; v++) acc[v] = Op::apply(acc[v], C(x.v[v]));
-        } else {
-            acc[0] = Op::apply(acc[0], C(p[0]));
-        }
+        for (int i = 0; i < kColBatch; i++) x[i] = *reinterpret_cast<const Vec<T, V> *>(src + (r + i) * a.inner);
+#pragma unroll
+        for (int i = 0; i < kColBatch; i++)
+#pragma unroll
+            for (int v = 0; v < V; v++) acc[v] = Op::apply(acc[v], C(x[i].v[v]));
+    }
+    for (; r < r1; r++) {
+        const Vec<T, V> x = *reinterpret_cast<const Vec<T, V> *>(src + r * a.inner);
+#pragma unroll
+        for (int v = 0; v < V; v++) acc[v] = Op::apply(acc[v], C(x.v[v]));
     }
     C *part = reinterpret_cast<C *>(a.partials) + (int64_t(o) * a.chunks + c) * a.inner + col;
 #pragma unroll
@@ -154,10 +161,10 @@ __global__ __launch_bounds__(kColThreads) void k_col_rescan(ColArgs a) {
                 y.v[v] = T(a.exclusive ? run[v] : next);
                 run[v] = next;
             }
-            *reinterpret_cast<Vec<T, V> *>(q) = y;
+            store_vec<T, V>(q, y);
         } else {
             const C next = Op::apply(run[0], C(p[0]));
-            q[0] = T(a.exclusive ? run[0] : next);
+            store_vec<T, 1>(q, Vec<T, 1>{{T(a.exclusive ? run[0] : next)}});
             run[0] = next;
         }
     }
