@@ -35,6 +35,35 @@ __device__ __forceinline__ bool keep(X v, X t) {
     }
 }
 
+// Writes dst[g0 + i] = f(i) for i in [0, len), skipping positions outside
+// [0, lim).  The range is cut at dst's 16-byte boundaries: whole quads go
+// out as one nontemporal 16-byte store, the partial quads at its two ends
+// element by element.  The BLOCK data threads take quads in turn.
+template <int BLOCK, class F>
+__device__ __forceinline__ void write_range(int32_t *dst, int64_t g0, int32_t len, int64_t lim, F f) {
+    typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+    if (len <= 0) return;
+    const int32_t lead = int32_t(((reinterpret_cast<uintptr_t>(dst) >> 2) + uint64_t(g0)) & 3u);
+    const int64_t a0 = g0 - lead;  // dst + a0 is 16-byte aligned
+    const int32_t nq = (lead + len + 3) >> 2;
+    const bool inside = g0 >= 0 && g0 + len <= lim;
+    for (int32_t q = threadIdx.x; q < nq; q += BLOCK) {
+        const int32_t i0 = 4 * q - lead;  // range index of the quad's first element
+        int32_t *d = dst + a0 + 4 * q;
+        if (inside && i0 >= 0 && i0 + 4 <= len) {
+            const i32x4 x = {f(i0), f(i0 + 1), f(i0 + 2), f(i0 + 3)};
+            __builtin_nontemporal_store(x, reinterpret_cast<i32x4 *>(d));
+        } else {
+#pragma unroll
+            for (int c = 0; c < 4; c++) {
+                const int32_t i = i0 + c;
+                const int64_t g = a0 + 4 * q + c;
+                if (i >= 0 && i < len && g >= 0 && g < lim) d[c] = f(i);
+            }
+        }
+    }
+}
+
 template <class X, int CMP, int BLOCK_, int ROWS, int VEC>
 struct CompactPolicy {
     using T = int32_t;
@@ -50,12 +79,16 @@ struct CompactPolicy {
 
     __device__ __forceinline__ static C aggregate(const Shared &sh) { return TS::template aggregate_from<C>(sh); }
 
-    // A scanned tile waiting for its prefix: every thread's row offsets and
-    // selection bits.
+    // A scanned tile waiting for its prefix: the tile-local indices of its
+    // selected elements in output order, and how many there are.  The emit
+    // then writes one contiguous range with whole 16-byte stores instead of
+    // 4-byte stores scattered by the selection.
+    static_assert(TS::TILE <= 65536, "tile-local indices fit 16 bits");
     struct Stash {
-        int32_t off[ROWS][BLOCK];
-        uint32_t bits[BLOCK];
+        uint16_t lidx[TS::TILE];
+        int32_t nsel;
     };
+    static constexpr bool kStagedEmit = true;  // emit reads other threads' slots
 
     // Each selected element's index at its position.
     static constexpr bool kSetup = false;
@@ -64,20 +97,9 @@ struct CompactPolicy {
     __device__ __forceinline__ static void emit(const Stash &st, const Args &a, uint32_t tile, C pre, bool valid,
                                                 C) {
         if (!valid) return;
-        const int64_t start = int64_t(tile) * TS::TILE;
-        const uint32_t bits = st.bits[threadIdx.x];
-#pragma unroll
-        for (int r = 0; r < ROWS; r++) {
-            const int64_t e = TS::elem(r);
-            int32_t pos = pre + st.off[r][threadIdx.x];
-#pragma unroll
-            for (int c = 0; c < VEC; c++) {
-                if (bits & (1u << (r * VEC + c))) {
-                    a.out_idx[pos] = int32_t(start + e + c);
-                    pos++;
-                }
-            }
-        }
+        const int32_t start = int32_t(int64_t(tile) * TS::TILE);  // n <= INT32_MAX
+        write_range<BLOCK>(a.out_idx, int64_t(pre), st.nsel, a.n,
+                           [&](int32_t i) { return start + int32_t(st.lidx[i]); });
     }
 
     // The count after the last tile.
@@ -128,8 +150,17 @@ struct CompactPolicy {
 
         __device__ __forceinline__ void stash(Stash &st, const Args &) const {
 #pragma unroll
-            for (int r = 0; r < ROWS; r++) st.off[r][threadIdx.x] = ts.off[r];
-            st.bits[threadIdx.x] = bits;
+            for (int r = 0; r < ROWS; r++) {
+                int32_t pos = ts.off[r];
+#pragma unroll
+                for (int c = 0; c < VEC; c++) {
+                    if (bits & (1u << (r * VEC + c))) {
+                        st.lidx[pos] = uint16_t(TS::elem(r) + c);
+                        pos++;
+                    }
+                }
+            }
+            if (threadIdx.x == 0) st.nsel = ts.agg;
         }
     };
 };
@@ -259,39 +290,35 @@ struct PartitionPolicy {
         return counts.template finish<Op>(desc, epoch, hdr, a.pipe.spin_limit);
     }
 
-    // A scanned tile waiting for its prefix: row offsets, selection bits and
-    // the raw values.
+    // A scanned tile waiting for its prefix, already in output order: the
+    // selected elements (values and tile-local indices), then the rejected
+    // ones, and the selected count.  Each part then goes out as one
+    // contiguous range of whole 16-byte stores.
+    static_assert(TS::TILE <= 65536, "tile-local indices fit 16 bits");
     struct Stash {
-        int32_t off[ROWS][BLOCK];
-        uint32_t bits[BLOCK];
-        V val[ROWS][BLOCK];
+        uint32_t val[TS::TILE];
+        uint16_t lidx[TS::TILE];
+        int32_t nsel;
     };
+    static constexpr bool kStagedEmit = true;  // emit reads other threads' slots
 
     __device__ __forceinline__ static void emit(const Stash &st, const Args &a, uint32_t tile, C pre, bool valid,
                                                 C total) {
         if (!valid) return;
         const int64_t start = int64_t(tile) * TS::TILE;
-        const uint32_t bits = st.bits[threadIdx.x];
-        uint32_t *vals = reinterpret_cast<uint32_t *>(a.out_vals);
-#pragma unroll
-        for (int r = 0; r < ROWS; r++) {
-            const int64_t e = start + TS::elem(r);
-            if (e >= a.n) break;  // rows past the end (n is a multiple of VEC)
-            int32_t sel = pre + st.off[r][threadIdx.x];  // selected elements before this vector's next one
-            const V v = st.val[r][threadIdx.x];
-#pragma unroll
-            for (int c = 0; c < VEC; c++) {
-                const int64_t i = e + c;
-                const bool k = (bits >> (r * VEC + c)) & 1u;
-                const int64_t pos = k ? int64_t(sel) : int64_t(total) + (i - sel);
-                // in [0, n) whenever the count pass and the scan agree; a
-                // failed wait (flagged in the workspace) must not write outside
-                if (pos >= 0 && pos < a.n) {
-                    vals[pos] = v.v[c];
-                    if (a.out_idx != nullptr) a.out_idx[pos] = int32_t(i);
-                }
-                sel += k ? 1 : 0;
-            }
+        const int32_t cnt = int32_t(a.n - start < TS::TILE ? a.n - start : TS::TILE);
+        const int32_t nsel = st.nsel, s32 = int32_t(start);  // n <= INT32_MAX
+        int32_t *vals = reinterpret_cast<int32_t *>(a.out_vals);
+        // selected: from position pre; rejected: after all k selected, from
+        // k + (elements before the tile) - pre.  A failed wait (flagged in
+        // the workspace) must not write outside [0, n).
+        const int64_t g_sel = int64_t(pre), g_rej = int64_t(total) + (start - int64_t(pre));
+        write_range<BLOCK>(vals, g_sel, nsel, a.n, [&](int32_t i) { return int32_t(st.val[i]); });
+        write_range<BLOCK>(vals, g_rej, cnt - nsel, a.n, [&](int32_t i) { return int32_t(st.val[nsel + i]); });
+        if (a.out_idx != nullptr) {
+            write_range<BLOCK>(a.out_idx, g_sel, nsel, a.n, [&](int32_t i) { return s32 + int32_t(st.lidx[i]); });
+            write_range<BLOCK>(a.out_idx, g_rej, cnt - nsel, a.n,
+                               [&](int32_t i) { return s32 + int32_t(st.lidx[nsel + i]); });
         }
     }
 
@@ -337,13 +364,26 @@ struct PartitionPolicy {
             ts.scan(sh);
         }
 
+        // Element i of the tile with s selected before it goes to s when
+        // selected, else to nsel + (i - s).
         __device__ __forceinline__ void stash(Stash &st, const Args &) const {
+            const int32_t nsel = ts.agg;
 #pragma unroll
             for (int r = 0; r < ROWS; r++) {
-                st.off[r][threadIdx.x] = ts.off[r];
-                st.val[r][threadIdx.x] = raw[r];
+                const int32_t e = int32_t(TS::elem(r));
+                int32_t sel = ts.off[r];
+#pragma unroll
+                for (int c = 0; c < VEC; c++) {
+                    const bool k = (bits >> (r * VEC + c)) & 1u;
+                    const int32_t p = k ? sel : nsel + (e + c - sel);
+                    if (e + c < rem) {
+                        st.val[p] = raw[r].v[c];
+                        st.lidx[p] = uint16_t(e + c);
+                    }
+                    sel += k ? 1 : 0;
+                }
             }
-            st.bits[threadIdx.x] = bits;
+            if (threadIdx.x == 0) st.nsel = nsel;
         }
     };
 };
@@ -368,10 +408,10 @@ static int launch_partition_impl(const PartitionArgs &a, uint32_t grid_cap, hipS
 template <class X, int CMP>
 static PartitionLaunch pick_partition_shape(int block, int rows, int vec) {
     if (vec == 4) {
-        if (block == 512 && rows == 8) return &launch_partition_impl<X, CMP, 512, 8, 4>;
+        if (block == 512 && rows == 6) return &launch_partition_impl<X, CMP, 512, 6, 4>;
         if (block == 256 && rows == 1) return &launch_partition_impl<X, CMP, 256, 1, 4>;
     } else if (vec == 1) {
-        if (block == 512 && rows == 8) return &launch_partition_impl<X, CMP, 512, 8, 1>;
+        if (block == 512 && rows == 6) return &launch_partition_impl<X, CMP, 512, 6, 1>;
         if (block == 256 && rows == 1) return &launch_partition_impl<X, CMP, 256, 1, 1>;
     }
     return nullptr;

@@ -92,6 +92,11 @@ struct PipeArgs {
 //                                         same call tagged with the epoch
 //   static void on_resolved(const Args&, uint32_t tile, C pre, C agg)
 //                                         control lane 0, after the prefix
+//   static constexpr bool kStagedEmit     optional; true: emit() reads stash
+//                                         slots other threads wrote, so each
+//                                         static-mode step has a third
+//                                         barrier (both roles) between the
+//                                         emit and the next stash
 //   struct Tile {
 //     void load(const Args&, uint32_t tile);   tile >= num_tiles: dummy loads
 //     void scan(Shared&);                      exactly one __syncthreads()
@@ -109,6 +114,10 @@ struct CtrlPipeline {
     static constexpr int kGapReads = 8;  // GapRead slots per lane
     static constexpr uint32_t kGapGrid = kWave * kGapReads + 1;  // largest grid that uses GapRead
     static_assert(DATA % kWave == 0 && THREADS <= 1024, "whole waves");
+    static constexpr bool kStaged = [] {
+        if constexpr (requires { P::kStagedEmit; }) return bool(P::kStagedEmit);
+        else return false;
+    }();
 
     struct Smem {
         typename P::Stash stash[2];  // scanned tiles waiting for their prefix
@@ -195,6 +204,7 @@ struct CtrlPipeline {
                 gap.issue(desc, use_carry ? t - G + 1 : first, t);
             }
             __syncthreads();
+            if constexpr (kStaged) __syncthreads();
         }
     }
 
@@ -211,6 +221,7 @@ struct CtrlPipeline {
         __syncthreads();
         const bool emit = s >= 2;
         P::emit(sm.stash[s & 1], a, emit ? w + (s - 2) * G : a.pipe.num_tiles, sm.prefix[s & 1], emit, sm.total);
+        if constexpr (kStaged) __syncthreads();
         if (s < K) cur.stash(sm.stash[s & 1], a);
         return s + 1 < K + 2;
     }
@@ -255,6 +266,7 @@ struct CtrlPipeline {
                     agg0 = agg1;
                     if (s < K) agg1 = ctrl_publish(a, w + s * G, sm, desc, epoch);
                     __syncthreads();
+                    if constexpr (kStaged) __syncthreads();
                 }
                 end_static(a, sm, hdr, desc, epoch);
             } else {
