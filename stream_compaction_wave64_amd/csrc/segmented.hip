@@ -255,15 +255,38 @@ struct SegTile {
 };
 
 // Pass 1: the tile -> segment map (a template only so that each element
-// type's unit has its own instance).
+// type's unit has its own instance).  Each thread takes kMapSegs
+// consecutive segments, whose kMapSegs + 1 offsets it loads at once (one
+// 16-byte load when aligned), so a thread waits for one round trip.
+constexpr int kMapSegs = 4;
+
 template <class T>
 __global__ __launch_bounds__(256) void k_seg_map(SegArgs a) {
-    for (int64_t s = int64_t(blockIdx.x) * 256 + threadIdx.x; s < a.nseg; s += int64_t(gridDim.x) * 256) {
-        const int64_t b = a.off[s], e = a.off[s + 1];
-        if (e <= b || b < 0) continue;
-        // tiles are a power of two long: the first tile starting at or after b
-        const int64_t t0 = (b + a.tile - 1) >> a.tile_log2;
-        for (int64_t t = t0; (t << a.tile_log2) < e && t < int64_t(a.num_tiles); t++) a.map[t] = uint64_t(s);
+    typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+    static_assert(kMapSegs == 4, "one 16-byte load of offsets");
+    const bool vec = (reinterpret_cast<uintptr_t>(a.off) & 15u) == 0;
+    for (int64_t s0 = (int64_t(blockIdx.x) * 256 + threadIdx.x) * kMapSegs; s0 < a.nseg;
+         s0 += int64_t(gridDim.x) * 256 * kMapSegs) {
+        int32_t o[kMapSegs + 1];
+        if (vec && s0 + kMapSegs <= a.nseg) {
+            const i32x4 v = *reinterpret_cast<const i32x4 *>(a.off + s0);
+            o[0] = v.x;
+            o[1] = v.y;
+            o[2] = v.z;
+            o[3] = v.w;
+            o[4] = a.off[s0 + kMapSegs];
+        } else {
+#pragma unroll
+            for (int i = 0; i <= kMapSegs; i++) o[i] = s0 + i <= a.nseg ? a.off[s0 + i] : 0;
+        }
+#pragma unroll
+        for (int i = 0; i < kMapSegs; i++) {
+            const int64_t b = o[i], e = o[i + 1];
+            if (s0 + i >= a.nseg || e <= b || b < 0) continue;
+            // tiles are a power of two long: the first tile starting at or after b
+            const int64_t t0 = (b + a.tile - 1) >> a.tile_log2;
+            for (int64_t t = t0; (t << a.tile_log2) < e && t < int64_t(a.num_tiles); t++) a.map[t] = uint64_t(s0 + i);
+        }
     }
 }
 
@@ -395,8 +418,8 @@ template <class T, class Op, int B, int R, int V>
 static int launch_seg_impl(const SegArgs &a, hipStream_t s) {
     if (a.blocks < 1 || a.blocks > uint32_t(kSegPartThreads * kSegPartPer)) return SCAN_ERR_UNSUPPORTED;
     if (a.tile != SegTile<T, Op, B, R, V>::TILE || (int64_t(1) << a.tile_log2) != a.tile) return SCAN_ERR_UNSUPPORTED;
-    const int64_t mg = (a.nseg + 255) / 256;
-    hipLaunchKernelGGL(k_seg_map<T>, dim3(unsigned(mg < 4096 ? (mg > 0 ? mg : 1) : 4096)), dim3(256), 0, s, a);
+    const int64_t mg = (a.nseg + 256 * kMapSegs - 1) / (256 * kMapSegs);
+    hipLaunchKernelGGL(k_seg_map<T>, dim3(unsigned(mg < 16384 ? (mg > 0 ? mg : 1) : 16384)), dim3(256), 0, s, a);
     if (hipGetLastError() != hipSuccess) return SCAN_ERR_HIP;
     hipLaunchKernelGGL((k_seg_reduce<T, Op, B, R, V>), dim3(a.blocks), dim3(B), 0, s, a);
     if (hipGetLastError() != hipSuccess) return SCAN_ERR_HIP;
