@@ -177,10 +177,10 @@ size_t scan_workspace_bytes(scan_dtype_t dtype, int64_t count);
 int scan_workspace_init(void *ws, size_t ws_bytes, void *stream);
 
 /* Diagnostic (synchronizes `stream`): copy the workspace's error word to
- * *error.  Bits 0 and 1 mean a wait gave up after spin_limit polls (a
- * look-back window, or the end-of-call count of started workgroups), e.g.
- * because the workspace was not zeroed or was used by overlapping calls: the
- * results of that call are invalid and the workspace must be re-initialised.
+ * *error.  Bit 0 means a wait gave up after spin_limit polls (a look-back
+ * window), e.g. because the workspace was not zeroed or was used by
+ * overlapping calls: the results of that call are invalid and the workspace
+ * must be re-initialised.  Bit 1 is not used.
  * Bit 2 means a call could not confirm that all of its workgroups were
  * resident and claimed tiles one by one instead (results valid, slower).
  * None is set in normal operation; the word stays set until re-init. */

@@ -281,7 +281,7 @@ struct WsHeader {
     uint32_t epoch;       // tag of the running call's descriptors
     uint32_t error;       // kErr* bits (see flag_error)
     uint64_t high_water;  // descriptor words the last call left tagged
-    uint32_t mode;        // 0 undecided, kModeStatic or kModeDynamic (running call)
+    uint32_t mode;        // (epoch << 2) | kModeStatic or kModeDynamic: the call that decided it
     uint32_t claim;       // next tile ticket in dynamic mode
     uint32_t pad0[26];
     struct {
@@ -291,7 +291,7 @@ struct WsHeader {
 };
 constexpr size_t kWsHeaderBytes = 4096;
 static_assert(sizeof(WsHeader) <= kWsHeaderBytes, "header fits its reserved bytes");
-constexpr uint32_t kErrSpin = 1u, kErrStart = 2u, kErrFallback = 4u;
+constexpr uint32_t kErrSpin = 1u, kErrFallback = 4u;  // bit 1 is no longer used
 constexpr uint32_t kModeStatic = 1u, kModeDynamic = 2u;
 
 __device__ __forceinline__ void flag_error(WsHeader *hdr, uint32_t code) {
@@ -307,13 +307,16 @@ __device__ __forceinline__ void st(U *p, U v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Start of a call that publishes descriptors (thread 0 only): read the epoch,
-// then count this workgroup with a fire-and-forget atomic whose operand
-// depends on the loaded epoch, so the read has returned before the count is
-// made.  Whoever later sees every workgroup counted knows that none will
-// read the epoch again.
-__device__ __forceinline__ uint32_t begin_call(WsHeader *hdr) {
+// Start of a call that publishes descriptors (thread 0 only): read the epoch
+// and the high-water mark (one round trip), then count this workgroup with
+// a fire-and-forget atomic whose operand depends on the loaded epoch, so the
+// read has returned before the count is made.  Whoever later sees every
+// workgroup counted knows that none will read the epoch again.  The
+// high-water mark changes only at a call's end, after every workgroup is
+// counted, so the value read here is the one end_call needs.
+__device__ __forceinline__ uint32_t begin_call(WsHeader *hdr, uint64_t &high_water) {
     const uint32_t e = ld(&hdr->epoch);
+    high_water = ld(&hdr->high_water);
     __hip_atomic_fetch_add(&hdr->started[blockIdx.x & 15].count, 1u + (e >> 30), __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
     return e;
@@ -336,67 +339,55 @@ __device__ __forceinline__ uint32_t started_sum(const WsHeader *hdr) {
 // dynamic mode, where tiles are claimed in order from a counter -- slower
 // (one same-address atomic per tile), but deadlock-free with any number of
 // resident workgroups.  No descriptor is published before the decision.
-__device__ __forceinline__ uint32_t decide_mode(WsHeader *hdr, uint32_t G, uint32_t limit) {
+// Each poll reads the mode word and the counters in one round trip; the
+// compare-and-swap returns the decided mode whether or not it won.  The
+// mode word carries the epoch it was decided in ((epoch << 2) | mode) and
+// is never reset: a word from another call reads as undecided, and a
+// workgroup still polling after this call's end (which resets the counters)
+// still finds this call's decision.
+__device__ __forceinline__ uint32_t decide_mode(WsHeader *hdr, uint32_t epoch, uint32_t G, uint32_t limit) {
+    const uint32_t tag = (epoch & kEpochMask) << 2;
+    auto decided = [&](uint32_t m) { return (m & ~3u) == tag && (m & 3u) != 0u; };
     uint32_t m = ld(&hdr->mode);
-    for (uint32_t polls = 0; m == 0u; polls++) {
-        uint32_t want = 0u;
-        if (started_sum(hdr) >= G) {
-            want = kModeStatic;
-        } else if (polls >= limit) {
-            want = kModeDynamic;
-        }
+    for (uint32_t polls = 0;; polls++) {
+        const uint32_t started = started_sum(hdr);
+        if (decided(m)) return m & 3u;
+        const uint32_t want = started >= G ? kModeStatic : (polls >= limit ? kModeDynamic : 0u);
         if (want != 0u) {
-            uint32_t expected = 0u;
-            __hip_atomic_compare_exchange_strong(&hdr->mode, &expected, want, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
-            if (want == kModeDynamic && expected == 0u) flag_error(hdr, kErrFallback);
-        } else {
-            __builtin_amdgcn_s_sleep(2);
+            uint32_t expected = m;
+            if (__hip_atomic_compare_exchange_strong(&hdr->mode, &expected, tag | want, __ATOMIC_RELAXED,
+                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+                if (want == kModeDynamic) flag_error(hdr, kErrFallback);
+                return want;
+            }
+            if (decided(expected)) return expected & 3u;  // another workgroup's decision
+            m = expected;
+            continue;
         }
+        __builtin_amdgcn_s_sleep(2);
         m = ld(&hdr->mode);
     }
-    return m;
 }
 
 // End of a call, run by one workgroup once every workgroup is known to have
 // read the epoch: reset the per-call words, advance the epoch for the next
 // call on this workspace, and clear the descriptor words above this call's
-// up to the previous high-water mark (within the workspace): words below
-// `words_used` were all rewritten by this call, so afterwards every word
-// carries this call's tag or none.  Whole workgroup; one barrier.
-__device__ __forceinline__ void end_call(WsHeader *hdr, uint32_t epoch, uint64_t words_used, uint64_t ws_words,
-                                         uint64_t *desc, uint64_t &s_clear_end) {
+// up to the previous high-water mark `hw` (begin_call's, within the
+// workspace): words below `words_used` were all rewritten by this call, so
+// afterwards every word carries this call's tag or none.  In static mode
+// every workgroup was counted before the mode was decided; in dynamic mode
+// the caller holds the last claim.  Whole workgroup (no barrier).
+__device__ __forceinline__ void end_call(WsHeader *hdr, uint32_t epoch, uint64_t hw, uint64_t words_used,
+                                         uint64_t ws_words, uint64_t *desc) {
     if (threadIdx.x == 0) {
-        const uint64_t hw = ld(&hdr->high_water);
         st(&hdr->high_water, words_used);
 #pragma unroll
         for (int i = 0; i < 16; i++) st(&hdr->started[i].count, 0u);
         st(&hdr->claim, 0u);
-        st(&hdr->mode, 0u);
         st(&hdr->epoch, (epoch + 1u) & kEpochMask);
-        s_clear_end = hw < ws_words ? hw : ws_words;
     }
-    __syncthreads();
-    const uint64_t clear_end = s_clear_end;
+    const uint64_t clear_end = hw < ws_words ? hw : ws_words;
     for (uint64_t i = words_used + threadIdx.x; i < clear_end; i += blockDim.x) st(desc + i, uint64_t(0));
-}
-
-// Static mode's end: the workgroup that finished the last tile waits
-// (bounded) until all G workgroups are counted -- already true when static
-// mode was chosen -- then ends the call.
-__device__ __forceinline__ void end_call_static(WsHeader *hdr, uint32_t G, uint32_t epoch, uint64_t words_used,
-                                                uint64_t ws_words, uint64_t *desc, uint32_t spin_limit,
-                                                uint64_t &s_clear_end) {
-    if (threadIdx.x == 0) {
-        for (uint32_t polls = 0; started_sum(hdr) < G; polls++) {
-            if (polls >= spin_limit) {
-                flag_error(hdr, kErrStart);
-                break;
-            }
-            __builtin_amdgcn_s_sleep(2);
-        }
-    }
-    end_call(hdr, epoch, words_used, ws_words, desc, s_clear_end);
 }
 
 // Decoupled look-back by one wave (The CUDA Handbook ch. 13, Figure 13-11),

@@ -125,7 +125,7 @@ struct CtrlPipeline {
         C prefix[2];  // exclusive prefix of the tile emitted in this step
         C total;      // setup()'s result
         uint32_t epoch, mode, ticket;
-        uint64_t clear_end;
+        uint64_t high_water;  // begin_call's, for end_call
     };
 
     // Whether a call runs the workspace protocol: every chained scan, and
@@ -244,9 +244,11 @@ struct CtrlPipeline {
         if (ctrl) {
             uint32_t e = 0;
             if (chained && lane_id() == 0) {
-                e = begin_call(hdr);
+                uint64_t hw = 0;
+                e = begin_call(hdr, hw);
                 sm.epoch = e;
-                sm.mode = decide_mode(hdr, G, a.pipe.mode_limit);
+                sm.high_water = hw;
+                sm.mode = decide_mode(hdr, e, G, a.pipe.mode_limit);
             }
             if constexpr (P::kSetup) {
                 const C t = P::setup(a, desc, uniform(e), hdr);  // uniform(): lane 0's epoch
@@ -294,7 +296,7 @@ struct CtrlPipeline {
             __syncthreads();
             const uint32_t tk = sm.ticket;
             if (tk >= n) {
-                if (tk == n + G - 1) end_call(hdr, epoch, a.pipe.words_used, a.pipe.ws_words, desc, sm.clear_end);
+                if (tk == n + G - 1) end_call(hdr, epoch, sm.high_water, a.pipe.words_used, a.pipe.ws_words, desc);
                 break;
             }
             b0.load(a, tk);
@@ -312,8 +314,7 @@ struct CtrlPipeline {
                                                       uint32_t epoch) {
         const uint32_t n = a.pipe.num_tiles, G = gridDim.x;
         if (protocol(a) && blockIdx.x == (n - 1) % G)
-            end_call_static(hdr, G, epoch, a.pipe.words_used, a.pipe.ws_words, desc, a.pipe.spin_limit,
-                            sm.clear_end);
+            end_call(hdr, epoch, sm.high_water, a.pipe.words_used, a.pipe.ws_words, desc);
     }
 
     // Dynamic mode (control wave): claim a tile, then resolve it.  Every
@@ -329,7 +330,7 @@ struct CtrlPipeline {
             __syncthreads();
             const uint32_t tk = sm.ticket;
             if (tk >= n) {
-                if (tk == n + G - 1) end_call(hdr, epoch, a.pipe.words_used, a.pipe.ws_words, desc, sm.clear_end);
+                if (tk == n + G - 1) end_call(hdr, epoch, sm.high_water, a.pipe.words_used, a.pipe.ws_words, desc);
                 break;
             }
             __syncthreads();
