@@ -39,8 +39,8 @@ N = 10 ** 8
 # the scan kernel, each scaled by what the counter reads for the copy kernel of
 # known size (profiles/lookback_scan_fp32_1e8_hbm_counters.md).  Valid only for
 # the kernel sources that were measured: reported as null once they change.
-TRAFFIC_BYTES = 8.011e8
-TRAFFIC_SOURCES_SHA = "36dee93245e42451"
+TRAFFIC_BYTES = 8.012e8
+TRAFFIC_SOURCES_SHA = "5cfd3aba4cc2c513"
 
 
 def _kernel_sources_sha():
