@@ -263,6 +263,8 @@ def compact_if(x: torch.Tensor, cmp: str = "gt", threshold: float = 0.5, out=Non
     if count is None:
         count = torch.empty(1, dtype=torch.int32, device=x.device)
     _need_cuda(out, count)
+    if out.dtype != torch.int32 or out.numel() < n:
+        raise ValueError("out must be int32 with n entries")
     ws, wsb = _workspace_for("compact", x, "sum", 1, n, 1, tuning)
     _check("compact_if", lib.compact_if(x.data_ptr(), n, _dtype(x), CMPS[cmp], float(threshold), out.data_ptr(),
                                         count.data_ptr(), ws.data_ptr(), wsb, _tuning(tuning), _stream(x.device)))

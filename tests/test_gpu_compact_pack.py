@@ -141,3 +141,24 @@ def test_pack_edges():
     off = sw.pack_offsets(torch.empty(0, dtype=torch.int32, device=DEV))
     torch.cuda.synchronize()
     assert to_host(off).tolist() == [0]
+
+
+@pytest.mark.parametrize("shift", [1, 2, 3])
+def test_compaction_misaligned_output(shift):
+    # The emit writes each tile's selected indices as one contiguous range cut
+    # at the output's 16-byte boundaries: an output starting 1-3 elements past
+    # a boundary exercises the partial quads at both ends of every range.
+    # Sentinels around the output must stay untouched.
+    x, _ = inputs.compaction_inputs(300_007, seed=44)
+    ref = oracle.compact(x, "gt", 0.5)
+    n = x.size
+    for tuning in (None, {"block_size": 256, "items_per_thread": 4}):
+        buf = torch.full((n + 8,), -7, dtype=torch.int32, device=DEV)
+        out = buf[shift:shift + n]
+        _, count = sw.compact_if(to_dev(x), "gt", 0.5, out=out, tuning=tuning)
+        torch.cuda.synchronize()
+        c = int(count.item())
+        got = to_host(buf)
+        assert c == ref.size
+        assert np.array_equal(got[shift:shift + c], ref)
+        assert (got[:shift] == -7).all() and (got[shift + n:] == -7).all()

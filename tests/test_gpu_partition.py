@@ -111,3 +111,26 @@ def test_partition_shares_workspace_with_scans():
         assert abs(float(to_host(big)[-1]) - float(x.astype(np.float64).sum())) < 1e-3 * x.size
     ws = sw.workspaces.get(DEV, 1)
     assert sw.scan_workspace_error(ws) == 0
+
+
+@pytest.mark.parametrize("shifts", [(1, 2), (3, 1), (2, 0)])
+def test_partition_misaligned_outputs(shifts):
+    # Values and indices go out as contiguous ranges cut at each output's own
+    # 16-byte boundaries; outputs 1-3 elements off a boundary (and off each
+    # other) exercise the partial quads.  Sentinels around both stay intact.
+    sv, si = shifts
+    x, _ = inputs.compaction_inputs(300_007, seed=53)
+    vals, idx, k = oracle.partition(x, "gt", 0.5)
+    n = x.size
+    for tuning in (None, {"block_size": 256, "items_per_thread": 4}):
+        vbuf = torch.full((n + 8,), -1.0, dtype=torch.float32, device=DEV)
+        ibuf = torch.full((n + 8,), -7, dtype=torch.int32, device=DEV)
+        _, _, count = sw.partition_if(to_dev(x), "gt", 0.5, out=vbuf[sv:sv + n], out_idx=ibuf[si:si + n],
+                                      tuning=tuning)
+        torch.cuda.synchronize()
+        assert int(count.item()) == k
+        gv, gi = to_host(vbuf), to_host(ibuf)
+        assert np.array_equal(gv[sv:sv + n].view(np.uint32), vals.view(np.uint32))
+        assert np.array_equal(gi[si:si + n], idx)
+        assert (gv[:sv] == -1.0).all() and (gv[sv + n:] == -1.0).all()
+        assert (gi[:si] == -7).all() and (gi[si + n:] == -7).all()
