@@ -373,7 +373,9 @@ int plan_segmented(scan_dtype_t dt, scan_op_t op, int64_t n, bool aligned, const
     p.rts_chunk = (p.num_tiles + chunks - 1) / chunks;
     p.rts_blocks = (p.num_tiles + p.rts_chunk - 1) / p.rts_chunk;
     p.carry_words = carry_bytes(dt, op) / 4;
-    p.ws_bytes = kHeader + round_up(size_t(p.num_tiles) * 8, 16) + round_up(size_t(p.rts_blocks) * 16, 256);
+    // map words, head planes (a quarter byte per element), chunk partials
+    p.ws_bytes = kHeader + round_up(size_t(p.num_tiles) * 8, 16) + round_up(size_t(p.num_tiles) * (p.tile / 4), 16) +
+                 round_up(size_t(p.rts_blocks) * 16, 256);
     p.launches = 4;
     return SCAN_OK;
 }
@@ -717,8 +719,12 @@ int scan_segmented(const void *in, void *out, int64_t n, const int32_t *offsets,
     a.n = n;
     a.off = offsets;
     a.nseg = nseg;
-    a.map = reinterpret_cast<uint64_t *>(reinterpret_cast<char *>(ws) + kHeader);
-    a.partials = reinterpret_cast<char *>(ws) + kHeader + round_up(size_t(p.num_tiles) * 8, 16);
+    char *w = reinterpret_cast<char *>(ws) + kHeader;
+    a.map = reinterpret_cast<uint64_t *>(w);
+    w += round_up(size_t(p.num_tiles) * 8, 16);
+    a.heads = reinterpret_cast<uint64_t *>(w);
+    w += round_up(size_t(p.num_tiles) * (p.tile / 4), 16);
+    a.partials = w;
     a.tile = p.tile;
     a.tile_log2 = 0;
     while ((int64_t(1) << a.tile_log2) < p.tile) a.tile_log2++;

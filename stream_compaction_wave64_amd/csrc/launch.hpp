@@ -60,6 +60,7 @@ struct SegArgs {
     const int32_t *off;       // nseg + 1 offsets
     int64_t nseg;
     uint64_t *map;            // per tile: the segment holding its first element (workspace)
+    uint64_t *heads;          // per tile: its head bits as planes, TILE / 4 bytes (workspace)
     void *partials;           // per chunk: (carry value, head flag) (workspace)
     int64_t tile;             // elements per tile (a power of two)
     int32_t tile_log2;

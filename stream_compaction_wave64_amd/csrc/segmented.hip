@@ -10,23 +10,26 @@
 // which is associative but not commutative, so every combination below keeps
 // sequence order (the earlier operand on the left).  The structure is
 // reduce-then-scan (The CUDA Handbook ch. 13 section 13.3.3), four launches:
-//   1. map: one thread per segment writes, for every tile whose first
-//      element lies in the segment, the segment's index;
+//   1. map: for every tile whose first element lies in a segment, that
+//      segment's index;
 //   2. reduce: each workgroup folds its chunk of tiles into one (flag,
-//      value) partial;
+//      value) partial, and saves each tile's head bits;
 //   3. partials: one workgroup scans the partials in order into each chunk's
 //      exclusive prefix;
 //   4. rescan: each workgroup scans its chunk again, tile by tile, carrying
 //      the prefix into the elements before the first head it meets.
-// A tile learns its heads from the offsets: from the map it reads the
-// segments that can start inside it and marks their starts in an LDS byte
-// map, so no per-element flag array is ever materialised in HBM.  Traffic: two
-// reads of the data and one write, plus two reads of the offsets.
+// The reduce pass learns a tile's heads from the offsets: from the map it
+// reads the segments that can start inside the tile and marks their starts
+// in an LDS byte map, then saves them as bit planes (one bit per element)
+// that the rescan loads with the tile, so no per-element flag array is ever
+// materialised in HBM and the offsets are read once.  Traffic: two reads of
+// the data and one write, one read of the offsets, and the planes (an
+// eighth of a byte per element each way, stored in 32-bit halves).
 //
 // Workspace: the map (one 64-bit word per tile, the index as a value below
 // 2^32: a look-back descriptor reader sees such a word as unpublished, so it
-// may stay) and the chunk partials (zeroed by the rescan, as the other
-// reduce-then-scan kernels leave theirs).
+// may stay), the head planes (likewise below 2^32) and the chunk partials
+// (zeroed by the rescan, as the other reduce-then-scan kernels leave theirs).
 //
 // Compiled once per element type (SW64_DT).
 #include "launch.hpp"
@@ -138,11 +141,15 @@ struct SegTile {
         const int32_t t0 = int32_t(int64_t(t) * TILE);  // n <= INT32_MAX
         for (uint64_t base = s0 + threadIdx.x; base <= s1; base += uint64_t(kMarkBatch) * B) {
             int32_t o[kMarkBatch];  // offsets and tile starts are in [0, 2^31): the difference fits
+            // unconditional loads (indices clamped to s1, a valid offset), so
+            // the batch is in flight at once rather than one branch per load
 #pragma unroll
             for (int u = 0; u < kMarkBatch; u++) {
                 const uint64_t s = base + uint64_t(u) * B;
-                o[u] = s <= s1 ? a.off[s] - t0 : -1;
+                o[u] = a.off[s <= s1 ? s : s1];
             }
+#pragma unroll
+            for (int u = 0; u < kMarkBatch; u++) o[u] = base + uint64_t(u) * B <= s1 ? o[u] - t0 : -1;
 #pragma unroll
             for (int u = 0; u < kMarkBatch; u++)
                 if (o[u] >= 0 && o[u] < TILE && o[u] < rem) sh.heads[o[u]] = 1;
@@ -159,6 +166,43 @@ struct SegTile {
 #pragma unroll
             for (int c = 0; c < VEC; c++) head |= uint32_t(((bytes >> (8 * c)) & 0xffu) != 0u) << (r * VEC + c);
         }
+    }
+
+    // The tile's head bits for the rescan, as bit planes: plane j of wave w
+    // holds bit j (row j / VEC, element j % VEC) of each lane's head mask, a
+    // 64-lane ballot stored as two words holding 32 lanes each; a wave's
+    // planes are contiguous, written by one store instruction.  Every word
+    // stays below 2^32, which a look-back reader of a later call on this
+    // workspace sees as unpublished, so the planes may stay.  TILE / 4 bytes
+    // per tile.
+    static constexpr int kPlanes = ROWS * VEC;
+    static constexpr int64_t kPlaneWords = int64_t(kPlanes) * W * 2;
+    __device__ __forceinline__ void save_heads(uint64_t *planes) const {
+        const int wave = threadIdx.x / kWave, lane = lane_id();
+        // one ballot per plane, stored at once by lane 0 (so the ballots do
+        // not all stay live in scalar registers)
+        uint64_t *dst = planes + int64_t(wave) * 2 * kPlanes;
+#pragma unroll
+        for (int j = 0; j < kPlanes; j++) {
+            const uint64_t m = __ballot((head >> j) & 1u);
+            if (lane == 0) {
+                __builtin_nontemporal_store(m & 0xffffffffu, dst + 2 * j);
+                __builtin_nontemporal_store(m >> 32, dst + 2 * j + 1);
+            }
+        }
+    }
+
+    // This thread's head mask from the planes save_heads() wrote (the
+    // addresses are uniform across the wave).
+    __device__ __forceinline__ void load_heads(const uint64_t *planes) {
+        const uint32_t wave = uniform(uint32_t(threadIdx.x / kWave));
+        const int lane = lane_id();
+        uint64_t w[kPlanes];
+#pragma unroll
+        for (int j = 0; j < kPlanes; j++) w[j] = planes[(int64_t(wave) * kPlanes + j) * 2 + (lane >> 5)];
+        head = 0;
+#pragma unroll
+        for (int j = 0; j < kPlanes; j++) head |= uint32_t((w[j] >> (lane & 31)) & 1u) << j;
     }
 
     // Scan the tile within itself; afterwards v holds, per element, the
@@ -336,6 +380,7 @@ __global__ __launch_bounds__(B) void k_seg_reduce(SegArgs a) {
         st.load(reinterpret_cast<const T *>(a.in) + start, a.n - start);
         st.mark(sh, a, uint32_t(t), cm.get(a, t0, t1, t), cm.get(a, t0, t1, t + 1));
         st.reduce(sh);
+        st.save_heads(a.heads + int64_t(t) * ST::kPlaneWords);
         acc = seg_combine<Op, C>(acc, SegVal<C>{C(st.agg.v), st.agg.f});
         __syncthreads();
     }
@@ -399,13 +444,11 @@ __global__ __launch_bounds__(B) void k_seg_rescan(SegArgs a) {
     if (threadIdx.x == 0) p[blockIdx.x] = SegPartial<T, Op>{};  // leave the workspace zeroed
     const uint64_t t0 = uint64_t(blockIdx.x) * a.chunk_tiles;
     const uint64_t t1 = t0 + a.chunk_tiles < a.num_tiles ? t0 + a.chunk_tiles : a.num_tiles;
-    __shared__ SegChunkMap cm;
-    cm.load(a, t0, t1);
     ST st;
     for (uint64_t t = t0; t < t1; t++) {
         const int64_t start = int64_t(t) * ST::TILE;
         st.load(reinterpret_cast<const T *>(a.in) + start, a.n - start);
-        st.mark(sh, a, uint32_t(t), cm.get(a, t0, t1, t), cm.get(a, t0, t1, t + 1));
+        st.load_heads(a.heads + int64_t(t) * ST::kPlaneWords);  // the reduce pass's marks
         uint32_t cov;
         st.scan(sh, a.exclusive != 0, cov);
         st.store(reinterpret_cast<T *>(a.out) + start, a.n - start, carry, cov);
