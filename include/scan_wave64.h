@@ -81,7 +81,7 @@ typedef enum {
 } scan_op_t;
 
 typedef enum {
-    SCAN_ALGO_AUTO = 0,             /* the single-pass look-back */
+    SCAN_ALGO_AUTO = 0,             /* the single-pass look-back (segmented: reduce-then-scan) */
     SCAN_ALGO_LOOKBACK = 1,         /* single-pass decoupled look-back */
     SCAN_ALGO_REDUCE_THEN_SCAN = 2  /* three launches, 3n traffic (comparison path) */
 } scan_algo_t;
@@ -213,10 +213,13 @@ int scan_dim(const void *in, void *out, int64_t outer, int64_t len, int64_t inne
  * SliceScan with segments of any length).  offsets: nseg + 1 device int32,
  * non-decreasing, offsets[0] = 0, offsets[nseg] = n; empty segments are
  * allowed.  Offsets that break this give unspecified results (no access
- * outside in, out, offsets or the workspace).  out may equal in.  Four
- * launches (tile map, reduce, partials, rescan; reduce-then-scan of
- * (head flag, value) pairs).  n > INT32_MAX -> SCAN_ERR_OVERFLOW; n == 0 is a
- * no-op; n > 0 with nseg == 0 -> SCAN_ERR_INVALID_ARG. */
+ * outside in, out, offsets or the workspace).  out may equal in.  Default
+ * (algo AUTO or REDUCE_THEN_SCAN): four launches (tile map, reduce,
+ * partials, rescan; reduce-then-scan of (head flag, value) pairs).  algo
+ * LOOKBACK: three launches (tile map, heads, then one pass on the look-back
+ * pipeline whose tiles combine (flag, value) carries in tile order).
+ * n > INT32_MAX -> SCAN_ERR_OVERFLOW; n == 0 is a no-op; n > 0 with
+ * nseg == 0 -> SCAN_ERR_INVALID_ARG. */
 int scan_segmented(const void *in, void *out, int64_t n, const int32_t *offsets,
                    int64_t nseg, scan_dtype_t dtype, scan_op_t op, int exclusive,
                    void *ws, size_t ws_bytes, const scan_tuning_t *tuning, void *stream);

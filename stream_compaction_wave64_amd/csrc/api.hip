@@ -18,6 +18,7 @@ namespace sw64 {
 SW64_DECLARE_PER_TYPE(find_lookback, LbLaunch)
 SW64_DECLARE_PER_TYPE(find_rts, RtsLaunch)
 SW64_DECLARE_PER_TYPE(find_seg, SegLaunch)
+SW64_DECLARE_PER_TYPE(find_seg_pipe, SegLaunch)
 #undef SW64_DECLARE_PER_TYPE
 ElemLaunch find_element_i32(scan_op_t, int, int, bool);
 ElemLaunch find_element_u32(scan_op_t, int, int, bool);
@@ -71,6 +72,17 @@ SegLaunch find_seg(scan_dtype_t dt, scan_op_t op, int block, int rows, int vec) 
     case SCAN_I64: return find_seg_i64(op, block, rows, vec);
     case SCAN_F32: return find_seg_f32(op, block, rows, vec);
     case SCAN_F64: return find_seg_f64(op, block, rows, vec);
+    }
+    return nullptr;
+}
+
+SegLaunch find_seg_pipe(scan_dtype_t dt, scan_op_t op, int block, int rows, int vec) {
+    switch (dt) {
+    case SCAN_I32: return find_seg_pipe_i32(op, block, rows, vec);
+    case SCAN_U32: return find_seg_pipe_u32(op, block, rows, vec);
+    case SCAN_I64: return find_seg_pipe_i64(op, block, rows, vec);
+    case SCAN_F32: return find_seg_pipe_f32(op, block, rows, vec);
+    case SCAN_F64: return find_seg_pipe_f64(op, block, rows, vec);
     }
     return nullptr;
 }
@@ -348,35 +360,52 @@ uint32_t threshold_bits(scan_dtype_t dt, scan_cmp_t cmp, double threshold) {
     return bits;
 }
 
-// Ragged segmented scan: small tiles (256 threads x 2 rows of 128-bit
-// vectors) in about 4096 chunks (at most 8192, the partials pass): its
-// per-tile chain of loads, head marking and barriers is hidden by many
-// resident workgroups, measured 1.9x faster than 512 x 8-row tiles in 1024
-// chunks.  The tile map (one word per tile) and the chunk partials (16 bytes
-// each) go in the workspace.
-constexpr int kSegBlock = 256, kSegRows = 2;
+// Ragged segmented scan.  Default: reduce-then-scan with small tiles (256
+// threads x 2 rows of 128-bit vectors) in about kSegChunks chunks (at most
+// 8192, the partials pass), whose per-tile chain of loads, head marking and
+// barriers is hidden by many resident workgroups (1.9x faster than 512 x
+// 8-row tiles in 1024 chunks).  Workspace: the tile map (one word per
+// tile), the head planes (a quarter byte per element), then the chunk
+// partials (16 bytes each).  algo = look-back: the single pass on the
+// look-back pipeline (512 threads, 448 of them data, x 4 rows), after a map
+// pass and a heads pass; the (flag, value) descriptors come first in the
+// workspace, then the map and the planes.  Every map and plane word stays
+// below 2^32, so a look-back reads it as unpublished.  The single pass
+// measured slower on 3e7 elements (see segmented.hip).
+constexpr int kSegBlock = 256, kSegRows = 2, kSegPipeRows = 4;
 constexpr int64_t kSegChunks = 4096;
 
 int plan_segmented(scan_dtype_t dt, scan_op_t op, int64_t n, bool aligned, const scan_tuning_t &tu, TilePlan &p) {
     const int esize = dtype_bytes(dt);
     const bool vec_ok = aligned;  // the last tile is accessed element-wise, so any n
-    const int rc = plan_shape(
-        esize, vec_ok, tu, p, [&](int b, int r, int v) { return find_seg(dt, op, b, r, v) != nullptr; }, false,
-        kSegRows, kSegBlock);
+    const bool rts = tu.algo != SCAN_ALGO_LOOKBACK;
+    const int rc =
+        rts ? plan_shape(
+                  esize, vec_ok, tu, p, [&](int b, int r, int v) { return find_seg(dt, op, b, r, v) != nullptr; },
+                  false, kSegRows, kSegBlock)
+            : plan_shape(
+                  esize, vec_ok, tu, p,
+                  [&](int b, int r, int v) { return find_seg_pipe(dt, op, b, r, v) != nullptr; }, true,
+                  kSegPipeRows, kDefaultBlock);
     if (rc != SCAN_OK) return rc;
     p.kernel = SCAN_KERNEL_SEGMENTED;
     p.tiles_per_seg = p.num_tiles = (n + p.tile - 1) / p.tile;
-    if (p.num_tiles > int64_t(UINT32_MAX)) return SCAN_ERR_OVERFLOW;
+    if (p.num_tiles > int64_t(INT32_MAX)) return SCAN_ERR_OVERFLOW;
     int64_t chunks = tu.rts_blocks > 0 ? tu.rts_blocks : kSegChunks;
     if (chunks > 8192) chunks = 8192;
     if (chunks > p.num_tiles) chunks = p.num_tiles;
     p.rts_chunk = (p.num_tiles + chunks - 1) / chunks;
     p.rts_blocks = (p.num_tiles + p.rts_chunk - 1) / p.rts_chunk;
-    p.carry_words = carry_bytes(dt, op) / 4;
-    // map words, head planes (a quarter byte per element), chunk partials
-    p.ws_bytes = kHeader + round_up(size_t(p.num_tiles) * 8, 16) + round_up(size_t(p.num_tiles) * (p.tile / 4), 16) +
-                 round_up(size_t(p.rts_blocks) * 16, 256);
-    p.launches = 4;
+    const size_t maps = round_up(size_t(p.num_tiles) * 8, 16) + round_up(size_t(p.num_tiles) * (p.tile / 4), 16);
+    if (rts) {
+        p.carry_words = carry_bytes(dt, op) / 4;
+        p.ws_bytes = kHeader + maps + round_up(size_t(p.rts_blocks) * 16, 256);
+        p.launches = 4;
+    } else {
+        p.carry_words = carry_bytes(dt, op) / 4;  // (flag, value) descriptors: the value's chunks
+        p.ws_bytes = kHeader + round_up(size_t(p.num_tiles) * p.carry_words * 8, 256) + round_up(maps, 256);
+        p.launches = 3;
+    }
     return SCAN_OK;
 }
 
@@ -719,21 +748,28 @@ int scan_segmented(const void *in, void *out, int64_t n, const int32_t *offsets,
     a.n = n;
     a.off = offsets;
     a.nseg = nseg;
+    a.tile = p.tile;
+    a.tile_log2 = -1;
+    for (int l = 0; l < 31; l++)
+        if ((int64_t(1) << l) == p.tile) a.tile_log2 = l;
+    a.num_tiles = uint32_t(p.num_tiles);
+    a.chunk_tiles = uint32_t(p.rts_chunk);
+    a.blocks = uint32_t(p.rts_blocks);
+    a.exclusive = exclusive ? 1 : 0;
+    a.grid_cap = tu.grid_blocks > 0 ? uint32_t(tu.grid_blocks) : 0u;
     char *w = reinterpret_cast<char *>(ws) + kHeader;
+    const bool rts = tu.algo != SCAN_ALGO_LOOKBACK;
+    if (!rts) {
+        a.pipe = pipe_args(p, ws, ws_bytes, tu);  // descriptors right after the header
+        w += round_up(size_t(p.num_tiles) * p.carry_words * 8, 256);
+    }
     a.map = reinterpret_cast<uint64_t *>(w);
     w += round_up(size_t(p.num_tiles) * 8, 16);
     a.heads = reinterpret_cast<uint64_t *>(w);
     w += round_up(size_t(p.num_tiles) * (p.tile / 4), 16);
     a.partials = w;
-    a.tile = p.tile;
-    a.tile_log2 = 0;
-    while ((int64_t(1) << a.tile_log2) < p.tile) a.tile_log2++;
-    if ((int64_t(1) << a.tile_log2) != p.tile) return SCAN_ERR_UNSUPPORTED;  // tiles are powers of two
-    a.num_tiles = uint32_t(p.num_tiles);
-    a.chunk_tiles = uint32_t(p.rts_chunk);
-    a.blocks = uint32_t(p.rts_blocks);
-    a.exclusive = exclusive ? 1 : 0;
-    return find_seg(dtype, op, p.block, p.rows, p.vec)(a, reinterpret_cast<hipStream_t>(stream));
+    if (rts) return find_seg(dtype, op, p.block, p.rows, p.vec)(a, reinterpret_cast<hipStream_t>(stream));
+    return find_seg_pipe(dtype, op, p.block, p.rows, p.vec)(a, reinterpret_cast<hipStream_t>(stream));
 }
 
 int pack_offsets(const int32_t *counts, int64_t n, int32_t *offsets, void *ws, size_t ws_bytes,

@@ -168,6 +168,24 @@ __device__ __forceinline__ int64_t uniform(int64_t x) {
     return int64_t((hi << 32) | lo);
 }
 
+// Operators that are associative but not commutative (the segmented scan's
+// (head flag, value) operator) declare kOrdered; every combination of
+// look-back values then keeps tile order, earlier tiles on the left.
+template <class Op>
+inline constexpr bool kOrderedOp = requires { Op::kOrdered; };
+
+// Lane l receives lane 63 - l's value (one cross-lane read per 32-bit word).
+template <class T>
+__device__ __forceinline__ T wave_reverse(T x) {
+    static_assert(sizeof(T) % 4 == 0, "cross-lane reads move 32-bit words");
+    struct W { int w[sizeof(T) / 4]; };
+    W s = __builtin_bit_cast(W, x), r;
+    const int addr = (kWave - 1 - lane_id()) * 4;
+#pragma unroll
+    for (int i = 0; i < int(sizeof(T) / 4); i++) r.w[i] = __builtin_amdgcn_ds_bpermute(addr, s.w[i]);
+    return __builtin_bit_cast(T, r);
+}
+
 // --------------------------------------------------------- tile descriptors --
 //
 // A tile publishes its aggregate (state A) and later its inclusive prefix
@@ -404,8 +422,8 @@ __device__ __forceinline__ void end_call(WsHeader *hdr, uint32_t epoch, uint64_t
 // combined; with no P in the window, all of them are combined and the
 // window moves 64*DEPTH tiles back.  Tiles before `first` (the start of the
 // segment) count as P with the identity.  Returns the exclusive prefix of
-// `tile`, the same in every lane.  Operators must be commutative: the window
-// is combined in lane order, not tile order.
+// `tile`, the same in every lane.  A commutative operator combines the
+// window in lane order; an ordered one (kOrderedOp) in tile order.
 //
 // Every wait is bounded: after `spin_limit` polls of one window the wave
 // flags kErrSpin in the header and takes the unpublished slots as P with the
@@ -455,12 +473,24 @@ __device__ __forceinline__ C lookback(const uint64_t *desc, uint32_t epoch, int6
             }
             __builtin_amdgcn_s_sleep(1);
         }
-        C contrib = id;
+        if constexpr (kOrderedOp<Op>) {
+            // tile order is distance order reversed: per block of 64 slots,
+            // reverse the lanes and reduce; older blocks on the left
+            C win = id;
 #pragma unroll
-        for (int k = 0; k < DEPTH; k++) {
-            if (lane + kWave * k <= near_p) contrib = Op::apply(v[k], contrib);
+            for (int k = DEPTH - 1; k >= 0; k--) {
+                const C x = lane + kWave * k <= near_p ? v[k] : id;
+                win = Op::apply(win, wave_reduce<Op>(wave_reverse(x)));
+            }
+            excl = Op::apply(win, excl);
+        } else {
+            C contrib = id;
+#pragma unroll
+            for (int k = 0; k < DEPTH; k++) {
+                if (lane + kWave * k <= near_p) contrib = Op::apply(v[k], contrib);
+            }
+            excl = Op::apply(wave_reduce<Op>(contrib), excl);
         }
-        excl = Op::apply(wave_reduce<Op>(contrib), excl);
         if (near_p < kSpan) break;
         frontier -= kSpan;
     }
@@ -482,7 +512,8 @@ __device__ __forceinline__ C lookback(const uint64_t *desc, uint32_t epoch, int6
 // Slot (lane, k) reads tile lo + lane + 64k for tiles in [lo, hi).  A slot
 // still X at finish() is re-read until published; after `spin_limit` polls
 // the wave flags kErrSpin and counts it as the identity, so the wait always
-// ends.  Operators must be commutative (slots combine in lane order).
+// ends.  Commutative operators combine slots as they arrive; ordered ones
+// (kOrderedOp) keep tile order.
 template <class C, class D, int NR>
 struct GapRead {
     uint64_t w[NR][D::kWords];
@@ -501,6 +532,7 @@ struct GapRead {
     // The combination of the aggregates of [lo, hi), the same in every lane.
     template <class Op>
     __device__ __forceinline__ C finish(const uint64_t *desc, uint32_t epoch, WsHeader *hdr, uint32_t spin_limit) {
+        if constexpr (kOrderedOp<Op>) return finish_ordered<Op>(desc, epoch, hdr, spin_limit);
         const C id = Op::template identity<C>();
         C acc = id;
         uint32_t pending = 0;  // bit k: slot k not yet published
@@ -535,6 +567,50 @@ struct GapRead {
             }
         }
         return wave_reduce<Op>(acc);
+    }
+
+    // The same for an ordered operator: every slot's value is kept until all
+    // are published, then block k (tiles lo + 64k .. lo + 64k + 63, in lane
+    // order) is reduced across the wave and the blocks combined in order.
+    template <class Op>
+    __device__ __forceinline__ C finish_ordered(const uint64_t *desc, uint32_t epoch, WsHeader *hdr,
+                                                uint32_t spin_limit) {
+        const C id = Op::template identity<C>();
+        C v[NR];
+        uint32_t pending = 0;  // bit k: slot k not yet published
+#pragma unroll
+        for (int k = 0; k < NR; k++) {
+            const int64_t p = lo + lane_id() + int64_t(kWave) * k;
+            v[k] = id;
+            if (p < hi && D::decode(w[k], epoch, v[k]) == 0u) {
+                v[k] = id;
+                pending |= 1u << k;
+            }
+        }
+        for (uint32_t polls = 0; __ballot(pending != 0u) != 0ull; polls++) {
+            if (polls >= spin_limit) {
+                if (lane_id() == 0) flag_error(hdr, kErrSpin);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+            for (int k = 0; k < NR; k++) {
+                if (pending & (1u << k)) {
+                    const int64_t p = lo + lane_id() + int64_t(kWave) * k;
+                    D::fetch(desc + p * D::kWords, w[k]);
+                    if (D::decode(w[k], epoch, v[k]) != 0u)
+                        pending &= ~(1u << k);
+                    else
+                        v[k] = id;
+                }
+            }
+        }
+        C acc = id;
+#pragma unroll
+        for (int k = 0; k < NR; k++) {
+            if (lo + int64_t(kWave) * k < hi) acc = Op::apply(acc, wave_reduce<Op>(v[k]));
+        }
+        return acc;
     }
 };
 

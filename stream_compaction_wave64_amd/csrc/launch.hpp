@@ -54,6 +54,7 @@ RtsLaunch find_rts(scan_dtype_t dt, scan_op_t op, int block, int rows, int vec);
 // Ragged segments given by int32 offsets, reduce-then-scan over chunks of
 // tiles with (head flag, value) pairs (segmented.hip).
 struct SegArgs {
+    PipeArgs pipe;            // single-pass path: the look-back pipeline (descriptors first in the workspace)
     const void *in;
     void *out;
     int64_t n;
@@ -61,16 +62,19 @@ struct SegArgs {
     int64_t nseg;
     uint64_t *map;            // per tile: the segment holding its first element (workspace)
     uint64_t *heads;          // per tile: its head bits as planes, TILE / 4 bytes (workspace)
-    void *partials;           // per chunk: (carry value, head flag) (workspace)
-    int64_t tile;             // elements per tile (a power of two)
-    int32_t tile_log2;
+    void *partials;           // reduce-then-scan path: per chunk (carry value, head flag) (workspace)
+    int64_t tile;             // elements per tile
+    int32_t tile_log2;        // log2(tile) for a power of two, else -1
     uint32_t num_tiles;
     uint32_t chunk_tiles;
     uint32_t blocks;          // chunks (<= 8192)
     int32_t exclusive;
+    uint32_t grid_cap;        // single-pass path: cap on the persistent grid (0: none)
 };
 using SegLaunch = int (*)(const SegArgs &, hipStream_t);
+// reduce-then-scan (four launches) and single-pass (map, heads, look-back scan)
 SegLaunch find_seg(scan_dtype_t dt, scan_op_t op, int block, int rows, int vec);
+SegLaunch find_seg_pipe(scan_dtype_t dt, scan_op_t op, int block, int rows, int vec);
 
 // ---------------------------------------------------------------- compaction
 struct CompactArgs {

@@ -39,6 +39,7 @@ namespace sw64 {
 
 template <class V>
 struct SegVal {
+    using value_type = V;
     V v;
     uint32_t f;  // a segment head lies in the combined range
 };
@@ -83,7 +84,11 @@ __device__ __forceinline__ SegVal<V> wave_seg_shr1(const SegVal<V> &inc) {
 
 // A tile of ROWS rows of B * VEC elements, laid out as TileScan's: thread t
 // holds vector (r * B + t) of row r.
-template <class T, class Op, int B, int ROWS, int VEC>
+// PRELOAD: the scan reads a row's per-wave totals from LDS all at once
+// before folding them (the single pass, where one workgroup per compute
+// unit leaves the dependent reads exposed); otherwise one at a time (fewer
+// registers, for the many-workgroup rescan).
+template <class T, class Op, int B, int ROWS, int VEC, bool PRELOAD = false>
 struct SegTile {
     using C = typename Carry<T, Op>::type;
     static constexpr int W = B / kWave;
@@ -91,9 +96,11 @@ struct SegTile {
     static_assert(TILE % 16 == 0 && ROWS * VEC <= 32, "16-byte clears of the head map, per-thread head bits");
 
     struct Shared {
-        alignas(16) uint8_t heads[TILE];  // nonzero: element e of the tile starts a segment
-        T tv[ROWS][W];                    // per row and wave: inclusive segmented total
+        T tv[ROWS][W];  // per row and wave: inclusive segmented total
         uint32_t tf[ROWS][W];
+    };
+    struct Marks {
+        alignas(16) uint8_t heads[TILE];  // nonzero: element e of the tile starts a segment
     };
 
     Vec<T, VEC> v[ROWS];
@@ -133,7 +140,7 @@ struct SegTile {
     // thread issues its offset loads kMarkBatch at a time.  Contains two
     // barriers.
     static constexpr int kMarkBatch = 8;
-    __device__ __forceinline__ void mark(Shared &sh, const SegArgs &a, uint32_t t, uint64_t s0, uint64_t s1) {
+    __device__ __forceinline__ void mark(Marks &sh, const SegArgs &a, uint32_t t, uint64_t s0, uint64_t s1) {
         typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
         for (int i = threadIdx.x; i < int(TILE / 16); i += B)
             reinterpret_cast<u32x4 *>(sh.heads)[i] = u32x4{0u, 0u, 0u, 0u};
@@ -192,6 +199,22 @@ struct SegTile {
         }
     }
 
+    // The plane words holding this lane's bits, loaded only (for a pipeline
+    // that prefetches the next tile: computing the mask at once would wait
+    // for the loads), and the mask from them.
+    __device__ __forceinline__ static void issue_heads(const uint64_t *planes, uint32_t (&pw)[kPlanes]) {
+        const uint32_t *p32 = reinterpret_cast<const uint32_t *>(planes);
+        const int wave = threadIdx.x / kWave, lane = lane_id();
+#pragma unroll
+        for (int j = 0; j < kPlanes; j++) pw[j] = p32[((int64_t(wave) * kPlanes + j) * 2 + (lane >> 5)) * 2];
+    }
+    __device__ __forceinline__ void heads_from(const uint32_t (&pw)[kPlanes]) {
+        const int lane = lane_id();
+        head = 0;
+#pragma unroll
+        for (int j = 0; j < kPlanes; j++) head |= ((pw[j] >> (lane & 31)) & 1u) << j;
+    }
+
     // This thread's head mask from the planes save_heads() wrote (the
     // addresses are uniform across the wave).
     __device__ __forceinline__ void load_heads(const uint64_t *planes) {
@@ -232,11 +255,22 @@ struct SegTile {
 #pragma unroll
         for (int r = 0; r < ROWS; r++) {
             SegVal<T> base = run;  // everything before this row, then before this wave
+            if constexpr (PRELOAD) {
+                SegVal<T> x[W];
+#pragma unroll
+                for (int w = 0; w < W; w++) x[w] = SegVal<T>{sh.tv[r][w], sh.tf[r][w]};
+#pragma unroll
+                for (int w = 0; w < W; w++) {
+                    if (w < wave) base = seg_combine<Op, T>(base, x[w]);
+                    run = seg_combine<Op, T>(run, x[w]);
+                }
+            } else {
 #pragma unroll 1
-            for (int w = 0; w < W; w++) {
-                const SegVal<T> x{sh.tv[r][w], sh.tf[r][w]};
-                if (w < wave) base = seg_combine<Op, T>(base, x);
-                run = seg_combine<Op, T>(run, x);
+                for (int w = 0; w < W; w++) {
+                    const SegVal<T> x{sh.tv[r][w], sh.tf[r][w]};
+                    if (w < wave) base = seg_combine<Op, T>(base, x);
+                    run = seg_combine<Op, T>(run, x);
+                }
             }
             SegVal<T> prev = seg_combine<Op, T>(base, ex[r]);  // before this thread's vector
 #pragma unroll
@@ -327,9 +361,13 @@ __global__ __launch_bounds__(256) void k_seg_map(SegArgs a) {
         for (int i = 0; i < kMapSegs; i++) {
             const int64_t b = o[i], e = o[i + 1];
             if (s0 + i >= a.nseg || e <= b || b < 0) continue;
-            // tiles are a power of two long: the first tile starting at or after b
-            const int64_t t0 = (b + a.tile - 1) >> a.tile_log2;
-            for (int64_t t = t0; (t << a.tile_log2) < e && t < int64_t(a.num_tiles); t++) a.map[t] = uint64_t(s0 + i);
+            // the first tile starting at or after b, and on while tiles start
+            // before e (a shift for power-of-two tiles, else a 32-bit
+            // division: offsets and the tile size are below 2^31)
+            const uint32_t tile = uint32_t(a.tile);
+            const int64_t t0 = a.tile_log2 >= 0 ? int64_t((uint32_t(b) + tile - 1u) >> a.tile_log2)
+                                                : int64_t((uint32_t(b) + tile - 1u) / tile);
+            for (int64_t t = t0; t * a.tile < e && t < int64_t(a.num_tiles); t++) a.map[t] = uint64_t(s0 + i);
         }
     }
 }
@@ -369,6 +407,7 @@ __global__ __launch_bounds__(B) void k_seg_reduce(SegArgs a) {
     using ST = SegTile<T, Op, B, R, V>;
     using C = typename ST::C;
     __shared__ typename ST::Shared sh;
+    __shared__ typename ST::Marks mk;
     __shared__ SegChunkMap cm;
     const uint64_t t0 = uint64_t(blockIdx.x) * a.chunk_tiles;
     const uint64_t t1 = t0 + a.chunk_tiles < a.num_tiles ? t0 + a.chunk_tiles : a.num_tiles;
@@ -378,7 +417,7 @@ __global__ __launch_bounds__(B) void k_seg_reduce(SegArgs a) {
     for (uint64_t t = t0; t < t1; t++) {
         const int64_t start = int64_t(t) * ST::TILE;
         st.load(reinterpret_cast<const T *>(a.in) + start, a.n - start);
-        st.mark(sh, a, uint32_t(t), cm.get(a, t0, t1, t), cm.get(a, t0, t1, t + 1));
+        st.mark(mk, a, uint32_t(t), cm.get(a, t0, t1, t), cm.get(a, t0, t1, t + 1));
         st.reduce(sh);
         st.save_heads(a.heads + int64_t(t) * ST::kPlaneWords);
         acc = seg_combine<Op, C>(acc, SegVal<C>{C(st.agg.v), st.agg.f});
@@ -457,10 +496,199 @@ __global__ __launch_bounds__(B) void k_seg_rescan(SegArgs a) {
     }
 }
 
+// ------------------------------------------------------------ single pass
+// The same scan on the persistent look-back pipeline (pipeline.hpp): one
+// read and one write of the data.  The carry between tiles is a (head flag,
+// value) pair under the restarting operator, which the look-back combines in
+// tile order (kOrderedOp).  Heads come from a heads pass (the reduce pass's
+// marking without the data) as the same bit planes, laid out for the
+// pipeline's data threads; the map pass runs first as before.
+
+template <class BaseOp>
+struct SegOp {
+    static constexpr bool kOrdered = true;
+    template <class X>
+    __device__ __forceinline__ static X identity() {
+        return X{BaseOp::template identity<typename X::value_type>(), 0u};
+    }
+    template <class X>
+    __device__ __forceinline__ static X apply(const X &a, const X &b) {
+        return seg_combine<BaseOp, typename X::value_type>(a, b);
+    }
+};
+
+// A (flag, value) descriptor: the value in 32-bit chunks, one per word as
+// Desc<C> does, and the flag in bit 32 of the first word (the payload has 54
+// bits); accepted only when every word carries the same tag.
+template <class V>
+struct SegDesc {
+    static constexpr int kWords = int(sizeof(V) / 4);
+    struct Chunks { uint32_t w[kWords]; };
+
+    __device__ __forceinline__ static void publish(uint64_t *d, uint32_t epoch, uint32_t state, SegVal<V> x) {
+        const Chunks c = __builtin_bit_cast(Chunks, x.v);
+        const uint64_t tag = desc_tag(epoch, state);
+#pragma unroll
+        for (int i = 0; i < kWords; i++) {
+            const uint64_t flag = i == 0 ? uint64_t(x.f & 1u) << 32 : 0;
+            __hip_atomic_store(d + i, tag | flag | c.w[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+    __device__ __forceinline__ static void fetch(const uint64_t *d, uint64_t (&w)[kWords]) {
+#pragma unroll
+        for (int i = 0; i < kWords; i++) w[i] = __hip_atomic_load(d + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __device__ __forceinline__ static uint32_t decode(const uint64_t (&w)[kWords], uint32_t epoch, SegVal<V> &x) {
+        const uint32_t state = desc_state(w[0], epoch);
+        bool ok = state != 0u;
+        Chunks c;
+#pragma unroll
+        for (int i = 0; i < kWords; i++) {
+            ok = ok && (w[i] >> kTagShift) == (w[0] >> kTagShift);
+            c.w[i] = uint32_t(w[i]);
+        }
+        x.v = __builtin_bit_cast(V, c);
+        x.f = uint32_t(w[0] >> 32) & 1u;
+        return ok ? state : 0u;
+    }
+    __device__ __forceinline__ static uint32_t read(const uint64_t *d, uint32_t epoch, SegVal<V> &x) {
+        uint64_t w[kWords];
+        fetch(d, w);
+        return decode(w, epoch, x);
+    }
+};
+
+template <class T, class BaseOp, int BLOCK_, int ROWS, int VEC>
+struct SegScanPolicy {
+    using ST = SegTile<T, BaseOp, BLOCK_, ROWS, VEC, true>;
+    using V = typename ST::C;  // carry value type
+    using C = SegVal<V>;
+    using Op = SegOp<BaseOp>;
+    using D = SegDesc<V>;
+    using Args = SegArgs;
+    using Shared = typename ST::Shared;
+    static constexpr int kDescWords = D::kWords;
+    static constexpr int BLOCK = BLOCK_;
+
+    // The tile's (flag, value) aggregate: rows, then waves, in order.
+    __device__ __forceinline__ static C aggregate(const Shared &sh) {
+        SegVal<T> run = seg_identity<BaseOp, T>();
+        for (int r = 0; r < ROWS; r++)
+            for (int w = 0; w < ST::W; w++) run = seg_combine<BaseOp, T>(run, SegVal<T>{sh.tv[r][w], sh.tf[r][w]});
+        return C{V(run.v), run.f};
+    }
+
+    // A scanned tile waiting for its prefix: the tile-local results and
+    // which of them have a head at or before them (own slots only).
+    struct Stash {
+        Vec<T, VEC> v[ROWS][BLOCK];
+        uint32_t cov[BLOCK];
+    };
+
+    static constexpr bool kSetup = false;
+    __device__ __forceinline__ static C setup(const Args &, const uint64_t *, uint32_t, WsHeader *) { return C{}; }
+
+    // Elements with no head at or before them in the tile take the carry in
+    // front (in the carry type, rounded once).
+    __device__ __forceinline__ static void emit(const Stash &st, const Args &a, uint32_t tile, C pre, bool valid,
+                                                C) {
+        if (!valid) return;
+        const int64_t start = int64_t(tile) * ST::TILE, remaining = a.n - start;
+        T *dst = reinterpret_cast<T *>(a.out) + start;
+        const BufRsrc rs = make_rsrc(dst, remaining < ST::TILE ? remaining : ST::TILE);
+        const uint32_t cov = st.cov[threadIdx.x];
+#pragma unroll
+        for (int r = 0; r < ROWS; r++) {
+            Vec<T, VEC> o = st.v[r][threadIdx.x];
+#pragma unroll
+            for (int c = 0; c < VEC; c++) {
+                if (!((cov >> (r * VEC + c)) & 1u)) o.v[c] = T(BaseOp::apply(pre.v, V(o.v[c])));
+            }
+            if (remaining >= ST::TILE) {
+                store_vec_bounded<T, VEC>(rs, uint32_t(ST::elem(r) * int64_t(sizeof(T))), o);
+            } else {
+#pragma unroll
+                for (int c = 0; c < VEC; c++)
+                    store_vec_bounded<T, 1>(rs, uint32_t((ST::elem(r) + c) * int64_t(sizeof(T))), Vec<T, 1>{{o.v[c]}});
+            }
+        }
+    }
+
+    __device__ __forceinline__ static void on_resolved(const Args &, uint32_t, C, C) {}
+
+    struct Tile {
+        ST st;
+        uint32_t pw[ST::kPlanes];  // this lane's plane words, loaded with the data
+        uint32_t cov;
+        bool excl;
+
+        // A tile past the end (the pipeline's prefetch) loads tile 0's data
+        // and planes and is never scanned.  Loads are only issued here; the
+        // head mask is formed in scan(), once the tile is due.
+        __device__ __forceinline__ void load(const Args &a, uint32_t tile) {
+            const bool valid = tile < a.pipe.num_tiles;
+            const uint32_t t = valid ? tile : 0u;
+            const int64_t start = int64_t(t) * ST::TILE;
+            excl = a.exclusive != 0;
+            st.load(reinterpret_cast<const T *>(a.in) + start, a.n - start);
+            ST::issue_heads(a.heads + int64_t(t) * ST::kPlaneWords, pw);
+        }
+        __device__ __forceinline__ void scan(Shared &sh) {
+            st.heads_from(pw);
+            st.scan(sh, excl, cov);
+        }
+        __device__ __forceinline__ void stash(Stash &s, const Args &) const {
+#pragma unroll
+            for (int r = 0; r < ROWS; r++) s.v[r][threadIdx.x] = st.v[r];
+            s.cov[threadIdx.x] = cov;
+        }
+    };
+};
+
+template <class P>
+__global__ __launch_bounds__(CtrlPipeline<P>::THREADS) void k_seg_scan(typename P::Args a) {
+    CtrlPipeline<P>::run(a);
+}
+
+// The heads pass: the reduce pass's marking and plane stores, without the
+// data, for tiles of B threads (the pipeline's data threads).
+template <class T, class Op, int B, int R, int V>
+__global__ __launch_bounds__(B) void k_seg_heads(SegArgs a) {
+    using ST = SegTile<T, Op, B, R, V>;
+    __shared__ typename ST::Marks mk;
+    __shared__ SegChunkMap cm;
+    const uint64_t t0 = uint64_t(blockIdx.x) * a.chunk_tiles;
+    const uint64_t t1 = t0 + a.chunk_tiles < a.num_tiles ? t0 + a.chunk_tiles : a.num_tiles;
+    cm.load(a, t0, t1);
+    ST st;
+    for (uint64_t t = t0; t < t1; t++) {
+        st.rem = a.n - int64_t(t) * ST::TILE;
+        st.mark(mk, a, uint32_t(t), cm.get(a, t0, t1, t), cm.get(a, t0, t1, t + 1));
+        st.save_heads(a.heads + int64_t(t) * ST::kPlaneWords);
+        __syncthreads();  // the marks are rewritten by the next tile
+    }
+}
+
+// B threads per workgroup: B - 64 data threads and the control wave.
+template <class T, class Op, int B, int R, int V>
+static int launch_seg_pipe_impl(const SegArgs &a, hipStream_t s) {
+    using P = SegScanPolicy<T, Op, B - kWave, R, V>;
+    if (a.tile != P::ST::TILE || a.blocks < 1) return SCAN_ERR_UNSUPPORTED;
+    const int64_t mg = (a.nseg + 256 * kMapSegs - 1) / (256 * kMapSegs);
+    hipLaunchKernelGGL(k_seg_map<T>, dim3(unsigned(mg < 16384 ? (mg > 0 ? mg : 1) : 16384)), dim3(256), 0, s, a);
+    if (hipGetLastError() != hipSuccess) return SCAN_ERR_HIP;
+    hipLaunchKernelGGL((k_seg_heads<T, Op, B - kWave, R, V>), dim3(a.blocks), dim3(B - kWave), 0, s, a);
+    if (hipGetLastError() != hipSuccess) return SCAN_ERR_HIP;
+    const int g = pipeline_grid(reinterpret_cast<const void *>(&k_seg_scan<P>), B, a.pipe.num_tiles, a.grid_cap);
+    if (g <= 0) return SCAN_ERR_HIP;
+    hipLaunchKernelGGL((k_seg_scan<P>), dim3(g), dim3(B), 0, s, a);
+    return hipGetLastError() == hipSuccess ? SCAN_OK : SCAN_ERR_HIP;
+}
+
 template <class T, class Op, int B, int R, int V>
 static int launch_seg_impl(const SegArgs &a, hipStream_t s) {
     if (a.blocks < 1 || a.blocks > uint32_t(kSegPartThreads * kSegPartPer)) return SCAN_ERR_UNSUPPORTED;
-    if (a.tile != SegTile<T, Op, B, R, V>::TILE || (int64_t(1) << a.tile_log2) != a.tile) return SCAN_ERR_UNSUPPORTED;
+    if (a.tile != SegTile<T, Op, B, R, V>::TILE) return SCAN_ERR_UNSUPPORTED;
     const int64_t mg = (a.nseg + 256 * kMapSegs - 1) / (256 * kMapSegs);
     hipLaunchKernelGGL(k_seg_map<T>, dim3(unsigned(mg < 16384 ? (mg > 0 ? mg : 1) : 16384)), dim3(256), 0, s, a);
     if (hipGetLastError() != hipSuccess) return SCAN_ERR_HIP;
@@ -475,6 +703,17 @@ static int launch_seg_impl(const SegArgs &a, hipStream_t s) {
 // Shapes: the default 256 threads x 2 rows, the ones the tuning sweep
 // visits, and 256 x 1 (the smallest tiles, for tests); element-wide
 // variants of each.
+// Single-pass shapes: 512 threads (448 data) x 8 rows, and 256 x 1 (small
+// tiles for tests); element-wide variants of each.
+template <class T, class Op, int V>
+static SegLaunch pick_seg_pipe_shape(int block, int rows) {
+    if (block == 512 && rows == 4) return &launch_seg_pipe_impl<T, Op, 512, 4, V>;
+    if (block == 512 && rows == 2) return &launch_seg_pipe_impl<T, Op, 512, 2, V>;
+    if (block == 768 && rows == 2) return &launch_seg_pipe_impl<T, Op, 768, 2, V>;
+    if (block == 256 && rows == 1) return &launch_seg_pipe_impl<T, Op, 256, 1, V>;
+    return nullptr;
+}
+
 template <class T, class Op, int V>
 static SegLaunch pick_seg_shape(int block, int rows) {
     if (block == 256 && rows == 1) return &launch_seg_impl<T, Op, 256, 1, V>;
@@ -492,35 +731,45 @@ static SegLaunch pick_seg_shape(int block, int rows) {
     return nullptr;
 }
 
-template <class T, class Op>
+template <class T, class Op, bool PIPE>
 static SegLaunch pick_seg_vec(int block, int rows, int vec) {
     constexpr int VMAX = 16 / int(sizeof(T));
-    if (vec == VMAX) return pick_seg_shape<T, Op, VMAX>(block, rows);
-    if (vec == 1) return pick_seg_shape<T, Op, 1>(block, rows);
+    if constexpr (PIPE) {
+        if (vec == VMAX) return pick_seg_pipe_shape<T, Op, VMAX>(block, rows);
+        if (vec == 1) return pick_seg_pipe_shape<T, Op, 1>(block, rows);
+    } else {
+        if (vec == VMAX) return pick_seg_shape<T, Op, VMAX>(block, rows);
+        if (vec == 1) return pick_seg_shape<T, Op, 1>(block, rows);
+    }
     return nullptr;
 }
 
-template <class T>
+template <class T, bool PIPE>
 static SegLaunch pick_seg_op(scan_op_t op, int block, int rows, int vec) {
     switch (op) {
-    case SCAN_OP_SUM: return pick_seg_vec<T, OpSum>(block, rows, vec);
-    case SCAN_OP_PROD: return pick_seg_vec<T, OpProd>(block, rows, vec);
-    case SCAN_OP_MAX: return pick_seg_vec<T, OpMax>(block, rows, vec);
-    case SCAN_OP_MIN: return pick_seg_vec<T, OpMin>(block, rows, vec);
+    case SCAN_OP_SUM: return pick_seg_vec<T, OpSum, PIPE>(block, rows, vec);
+    case SCAN_OP_PROD: return pick_seg_vec<T, OpProd, PIPE>(block, rows, vec);
+    case SCAN_OP_MAX: return pick_seg_vec<T, OpMax, PIPE>(block, rows, vec);
+    case SCAN_OP_MIN: return pick_seg_vec<T, OpMin, PIPE>(block, rows, vec);
     }
     return nullptr;
 }
 
 #if SW64_DT == 0
-SegLaunch find_seg_i32(scan_op_t op, int b, int r, int v) { return pick_seg_op<int32_t>(op, b, r, v); }
+SegLaunch find_seg_i32(scan_op_t op, int b, int r, int v) { return pick_seg_op<int32_t, false>(op, b, r, v); }
+SegLaunch find_seg_pipe_i32(scan_op_t op, int b, int r, int v) { return pick_seg_op<int32_t, true>(op, b, r, v); }
 #elif SW64_DT == 1
-SegLaunch find_seg_u32(scan_op_t op, int b, int r, int v) { return pick_seg_op<uint32_t>(op, b, r, v); }
+SegLaunch find_seg_u32(scan_op_t op, int b, int r, int v) { return pick_seg_op<uint32_t, false>(op, b, r, v); }
+SegLaunch find_seg_pipe_u32(scan_op_t op, int b, int r, int v) { return pick_seg_op<uint32_t, true>(op, b, r, v); }
 #elif SW64_DT == 2
-SegLaunch find_seg_i64(scan_op_t op, int b, int r, int v) { return pick_seg_op<int64_t>(op, b, r, v); }
+SegLaunch find_seg_i64(scan_op_t op, int b, int r, int v) { return pick_seg_op<int64_t, false>(op, b, r, v); }
+SegLaunch find_seg_pipe_i64(scan_op_t op, int b, int r, int v) { return pick_seg_op<int64_t, true>(op, b, r, v); }
 #elif SW64_DT == 3
-SegLaunch find_seg_f32(scan_op_t op, int b, int r, int v) { return pick_seg_op<float>(op, b, r, v); }
+SegLaunch find_seg_f32(scan_op_t op, int b, int r, int v) { return pick_seg_op<float, false>(op, b, r, v); }
+SegLaunch find_seg_pipe_f32(scan_op_t op, int b, int r, int v) { return pick_seg_op<float, true>(op, b, r, v); }
 #elif SW64_DT == 4
-SegLaunch find_seg_f64(scan_op_t op, int b, int r, int v) { return pick_seg_op<double>(op, b, r, v); }
+SegLaunch find_seg_f64(scan_op_t op, int b, int r, int v) { return pick_seg_op<double, false>(op, b, r, v); }
+SegLaunch find_seg_pipe_f64(scan_op_t op, int b, int r, int v) { return pick_seg_op<double, true>(op, b, r, v); }
 #else
 #error "SW64_DT must select an element type (0..4)"
 #endif

@@ -146,10 +146,15 @@ def test_segmented_argument_errors_and_plan(lib):
     assert seg(1 << 31, 2) == -5
     for dt in (torch.int32, torch.float32, torch.float64, torch.int64):
         for n in (1, 1000, 10 ** 7, 3 * 10 ** 7):
-            p = binding.plan("segmented", dt, "sum", n // 3 + 1, n)
-            assert p["kernel"] == "segmented" and p["launches"] == 4
-            assert p["num_tiles"] == -(-n // p["tile_elems"])
-            assert 4096 + p["num_tiles"] * 8 <= p["workspace_bytes"] <= binding.scan_workspace_bytes(dt, n)
+            # reduce-then-scan by default; single pass (map, heads, look-back scan) on request
+            for algo, launches in ((None, 4), ("reduce_then_scan", 4), ("lookback", 3)):
+                tu = {"algo": algo} if algo else None
+                p = binding.plan("segmented", dt, "sum", n // 3 + 1, n, tuning=tu)
+                assert p["kernel"] == "segmented" and p["launches"] == launches
+                assert p["num_tiles"] == -(-n // p["tile_elems"])
+                # map words and head planes at least (descriptors too in one pass)
+                assert 4096 + p["num_tiles"] * 8 + n // 4 <= p["workspace_bytes"]
+                assert p["workspace_bytes"] <= binding.scan_workspace_bytes(dt, n)
 
 
 def test_plan_partition():

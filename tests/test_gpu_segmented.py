@@ -71,7 +71,9 @@ def test_segmentations(dt, op):
     x = _values(dt, n, 7, op)
     for name, off in cases.items():
         for excl in (False, True):
-            _check(x, off, op, excl, what=f"{name} excl={excl}")
+            for algo in (None, "lookback"):  # reduce-then-scan (default), single pass
+                tu = {"algo": algo} if algo else None
+                _check(x, off, op, excl, tuning=tu, what=f"{name} excl={excl} algo={algo}")
 
 
 @pytest.mark.parametrize("dt", [np.int32, np.float32, np.float64], ids=lambda d: np.dtype(d).name)
@@ -82,7 +84,10 @@ def test_small_tiles_few_chunks_misaligned_in_place(dt):
     vec = 16 // np.dtype(dt).itemsize
     for tuning in ({"block_size": 256, "items_per_thread": vec},
                    {"block_size": 256, "items_per_thread": vec, "rts_blocks": 3},
-                   {"rts_blocks": 1}):
+                   {"rts_blocks": 1},
+                   {"algo": "lookback", "block_size": 256, "items_per_thread": vec, "grid_blocks": 3},
+                   {"algo": "lookback", "grid_blocks": 1},
+                   {"algo": "lookback", "rts_blocks": 3}):
         for excl in (False, True):
             _check(x, off, "sum", excl, tuning=tuning, what=f"{tuning} excl={excl}")
     _check(x, off, "sum", False, offset=1, what="element-wise")
@@ -113,3 +118,35 @@ def test_count_scan_emit_shape_full_size():
     assert np.all(np.abs(got.astype(np.float64) - ref) <= 1e-5 * p + 1e-6)
     got = _run(vals, off, "max", True)
     assert np.array_equal(got, oracle.scan_segmented(vals, off, "max", exclusive=True).astype(np.float32))
+
+
+@pytest.mark.parametrize("dt", [np.int32, np.float32, np.float64], ids=lambda d: np.dtype(d).name)
+def test_single_pass_dynamic_claiming(dt):
+    # A start count that wraps past the grid size never confirms that all
+    # workgroups are resident, so the single pass (algo look-back) claims
+    # tiles one by one and
+    # resolves prefixes with the windowed look-back, whose (flag, value)
+    # pairs must combine in tile order.  Long segments carry across many
+    # tiles; short ones restart inside tiles.
+    from stream_compaction_wave64_amd import binding
+    n = 600_011
+    x = _values(dt, n, 9, "sum")
+    vec = 16 // np.dtype(dt).itemsize
+    key = (torch.device(DEV).index, binding._stream(torch.device(DEV)))
+    saved = binding.workspaces._ws.get(key)
+    try:
+        for off in (_poisson(n, 30_000.0, 6), _poisson(n, 3.0, 7), np.array([0, n], np.int32)):
+            for tuning in ({"algo": "lookback", "mode_limit": 8},
+                           {"algo": "lookback", "mode_limit": 8, "block_size": 256, "items_per_thread": vec}):
+                ws = torch.zeros(1 << 24, dtype=torch.uint8, device=DEV)
+                ws[128:132].view(torch.int32)[0] = -1  # first started-count slot
+                binding.workspaces._ws[key] = ws
+                for excl in (False, True):
+                    _check(x, off, "sum", excl, tuning=tuning, what=f"{tuning} excl={excl}")
+                    assert sw.scan_workspace_error(ws) == 4, tuning  # the dynamic path ran, no wait gave up
+                    ws[128:132].view(torch.int32)[0] = -1  # the call reset it; force the fallback again
+    finally:
+        if saved is None:
+            binding.workspaces._ws.pop(key, None)
+        else:
+            binding.workspaces._ws[key] = saved
