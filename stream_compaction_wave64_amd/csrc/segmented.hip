@@ -332,13 +332,14 @@ struct SegTile {
     }
 };
 
-// Pass 1: the tile -> segment map (a template only so that each element
-// type's unit has its own instance).  Each thread takes kMapSegs
-// consecutive segments, whose kMapSegs + 1 offsets it loads at once (one
-// 16-byte load when aligned), so a thread waits for one round trip.
+// Pass 1: the tile -> segment map (templated on T only so that each element
+// type's unit has its own instance; POW2: tiles are a power of two long).
+// Each thread takes kMapSegs consecutive segments, whose kMapSegs + 1
+// offsets it loads at once (one 16-byte load when aligned), so a thread
+// waits for one round trip.
 constexpr int kMapSegs = 4;
 
-template <class T>
+template <class T, bool POW2>
 __global__ __launch_bounds__(256) void k_seg_map(SegArgs a) {
     typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
     static_assert(kMapSegs == 4, "one 16-byte load of offsets");
@@ -365,8 +366,11 @@ __global__ __launch_bounds__(256) void k_seg_map(SegArgs a) {
             // before e (a shift for power-of-two tiles, else a 32-bit
             // division: offsets and the tile size are below 2^31)
             const uint32_t tile = uint32_t(a.tile);
-            const int64_t t0 = a.tile_log2 >= 0 ? int64_t((uint32_t(b) + tile - 1u) >> a.tile_log2)
-                                                : int64_t((uint32_t(b) + tile - 1u) / tile);
+            int64_t t0;
+            if constexpr (POW2)
+                t0 = int64_t((uint32_t(b) + tile - 1u) >> a.tile_log2);
+            else
+                t0 = int64_t((uint32_t(b) + tile - 1u) / tile);
             for (int64_t t = t0; t * a.tile < e && t < int64_t(a.num_tiles); t++) a.map[t] = uint64_t(s0 + i);
         }
     }
@@ -675,7 +679,11 @@ static int launch_seg_pipe_impl(const SegArgs &a, hipStream_t s) {
     using P = SegScanPolicy<T, Op, B - kWave, R, V>;
     if (a.tile != P::ST::TILE || a.blocks < 1) return SCAN_ERR_UNSUPPORTED;
     const int64_t mg = (a.nseg + 256 * kMapSegs - 1) / (256 * kMapSegs);
-    hipLaunchKernelGGL(k_seg_map<T>, dim3(unsigned(mg < 16384 ? (mg > 0 ? mg : 1) : 16384)), dim3(256), 0, s, a);
+    const dim3 mgrid(unsigned(mg < 16384 ? (mg > 0 ? mg : 1) : 16384));
+    if (a.tile_log2 >= 0)
+        hipLaunchKernelGGL((k_seg_map<T, true>), mgrid, dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL((k_seg_map<T, false>), mgrid, dim3(256), 0, s, a);
     if (hipGetLastError() != hipSuccess) return SCAN_ERR_HIP;
     hipLaunchKernelGGL((k_seg_heads<T, Op, B - kWave, R, V>), dim3(a.blocks), dim3(B - kWave), 0, s, a);
     if (hipGetLastError() != hipSuccess) return SCAN_ERR_HIP;
@@ -690,7 +698,11 @@ static int launch_seg_impl(const SegArgs &a, hipStream_t s) {
     if (a.blocks < 1 || a.blocks > uint32_t(kSegPartThreads * kSegPartPer)) return SCAN_ERR_UNSUPPORTED;
     if (a.tile != SegTile<T, Op, B, R, V>::TILE) return SCAN_ERR_UNSUPPORTED;
     const int64_t mg = (a.nseg + 256 * kMapSegs - 1) / (256 * kMapSegs);
-    hipLaunchKernelGGL(k_seg_map<T>, dim3(unsigned(mg < 16384 ? (mg > 0 ? mg : 1) : 16384)), dim3(256), 0, s, a);
+    const dim3 mgrid(unsigned(mg < 16384 ? (mg > 0 ? mg : 1) : 16384));
+    if (a.tile_log2 >= 0)
+        hipLaunchKernelGGL((k_seg_map<T, true>), mgrid, dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL((k_seg_map<T, false>), mgrid, dim3(256), 0, s, a);
     if (hipGetLastError() != hipSuccess) return SCAN_ERR_HIP;
     hipLaunchKernelGGL((k_seg_reduce<T, Op, B, R, V>), dim3(a.blocks), dim3(B), 0, s, a);
     if (hipGetLastError() != hipSuccess) return SCAN_ERR_HIP;
