@@ -162,3 +162,15 @@ def test_compaction_misaligned_output(shift):
         assert c == ref.size
         assert np.array_equal(got[shift:shift + c], ref)
         assert (got[:shift] == -7).all() and (got[shift + n:] == -7).all()
+
+
+@pytest.mark.parametrize("cmp", CMPS)
+def test_compaction_special_floats(cmp):
+    # IEEE comparisons: a NaN satisfies only "ne"; -0.0 equals 0.0; the
+    # infinities order as usual.  Both sides compare in fp32.
+    rng = np.random.default_rng(45)
+    x = rng.random(70_001, dtype=np.float32) - np.float32(0.5)
+    specials = np.array([np.nan, -np.nan, np.inf, -np.inf, 0.0, -0.0, 0.5, -0.5], np.float32)
+    x[rng.integers(0, x.size, 5000)] = specials[rng.integers(0, specials.size, 5000)]
+    for t in (0.0, 0.5, float("inf")):
+        _check_compact(x, cmp, t)

@@ -134,3 +134,15 @@ def test_partition_misaligned_outputs(shifts):
         assert np.array_equal(gi[si:si + n], idx)
         assert (gv[:sv] == -1.0).all() and (gv[sv + n:] == -1.0).all()
         assert (gi[:si] == -7).all() and (gi[si + n:] == -7).all()
+
+
+@pytest.mark.parametrize("cmp", ["gt", "eq", "ne"])
+def test_partition_special_floats(cmp):
+    # NaNs (with their bit patterns), signed zeros and infinities move as raw
+    # 32-bit values; the predicate follows IEEE comparisons in fp32.
+    rng = np.random.default_rng(54)
+    x = rng.random(70_001, dtype=np.float32) - np.float32(0.5)
+    specials = np.array([np.nan, -np.nan, np.inf, -np.inf, 0.0, -0.0], np.float32)
+    x[rng.integers(0, x.size, 5000)] = specials[rng.integers(0, specials.size, 5000)]
+    for t in (0.0, float("-inf")):
+        _check(x, cmp, t)

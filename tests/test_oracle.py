@@ -363,6 +363,22 @@ def test_compaction_closed_forms(oracle_lib):
     assert list(oracle_lib.compact(xi, "gt", 0)) == list(range(6, 11))
 
 
+def test_compaction_special_floats(oracle_lib):
+    # IEEE 754 comparisons: an unordered operand (NaN) makes every relation
+    # false except "not equal"; -0.0 == +0.0; infinities are ordered.
+    x = np.array([np.nan, -0.0, 0.0, np.inf, -np.inf, 0.5, np.nan], np.float32)
+    assert list(oracle_lib.compact(x, "gt", 0.0)) == [3, 5]
+    assert list(oracle_lib.compact(x, "ge", 0.0)) == [1, 2, 3, 5]
+    assert list(oracle_lib.compact(x, "lt", 0.0)) == [4]
+    assert list(oracle_lib.compact(x, "le", 0.0)) == [1, 2, 4]
+    assert list(oracle_lib.compact(x, "eq", 0.0)) == [1, 2]
+    assert list(oracle_lib.compact(x, "ne", 0.0)) == [0, 3, 4, 5, 6]
+    assert list(oracle_lib.compact(x, "lt", np.inf)) == [1, 2, 4, 5]
+    vals, idx, k = oracle_lib.partition(x, "ne", 0.0)
+    assert k == 5 and list(idx) == [0, 3, 4, 5, 6, 1, 2]
+    assert np.array_equal(vals.view(np.uint32), x[idx].view(np.uint32))  # raw bits move, NaNs included
+
+
 def test_compaction_bit_predicates(oracle_lib):
     keys = np.arange(64, dtype=np.uint32)
     for b in range(6):
