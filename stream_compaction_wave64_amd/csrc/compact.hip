@@ -251,8 +251,10 @@ __global__ __launch_bounds__(kPartCountThreads) void k_part_count(PartitionArgs 
     constexpr int64_t kStep = int64_t(kPartCountThreads) * VEC;
 #pragma unroll 4
     for (int64_t i = b + int64_t(threadIdx.x) * VEC; i < e; i += kStep) {
-        // chunks start on VEC boundaries and n is a multiple of VEC here
-        const Vec<X, VEC> v = load_vec<X, VEC>(x + i);
+        // chunks start on VEC boundaries and n is a multiple of VEC here.
+        // Plain (temporal) loads: the partition pass reads x again right
+        // after, and may then find it in the caches.
+        const Vec<X, VEC> v = *reinterpret_cast<const Vec<X, VEC> *>(x + i);
 #pragma unroll
         for (int c = 0; c < VEC; c++) cnt += keep<X, CMP>(v.v[c], t) ? 1 : 0;
     }
