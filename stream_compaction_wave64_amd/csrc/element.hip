@@ -73,17 +73,20 @@ struct ElemTile {
 
     // Global -> LDS in the owner layout: access u of the tile (value u * LV)
     // belongs to thread u / UPT at its slot (u % UPT) * LV.
+    // AUX: the loads' cache policy (2: nontemporal; 0: the reduce pass, whose
+    // data the rescan reads again soon after and may find in the caches).
+    template <int AUX = 2>
     __device__ __forceinline__ static void load_tile(const Geo &g, T *lds) {
 #pragma unroll
         for (int r = 0; r < UPT; r++) {
             const uint32_t u = uint32_t(r) * blockDim.x + threadIdx.x;
             Acc x;
             if constexpr (LG == 16)
-                x = __builtin_bit_cast(Acc, __builtin_amdgcn_raw_buffer_load_b128(g.rs, u * 16u, 0, 2));
+                x = __builtin_bit_cast(Acc, __builtin_amdgcn_raw_buffer_load_b128(g.rs, u * 16u, 0, AUX));
             else if constexpr (LG == 8)
-                x = __builtin_bit_cast(Acc, __builtin_amdgcn_raw_buffer_load_b64(g.rs, u * 8u, 0, 2));
+                x = __builtin_bit_cast(Acc, __builtin_amdgcn_raw_buffer_load_b64(g.rs, u * 8u, 0, AUX));
             else
-                x = __builtin_bit_cast(Acc, __builtin_amdgcn_raw_buffer_load_b32(g.rs, u * 4u, 0, 2));
+                x = __builtin_bit_cast(Acc, __builtin_amdgcn_raw_buffer_load_b32(g.rs, u * 4u, 0, AUX));
             *reinterpret_cast<Acc *>(lds + (u / UPT) * STRIDE + (u % UPT) * LV) = x;
         }
     }
@@ -150,7 +153,7 @@ struct ElemTile {
         for (uint32_t k = 0; k < nt; k++) {
             const Geo g = geo(a, a.in, seg, j0 + k);
             if (k > 0) __syncthreads();  // previous tile's reads are done
-            load_tile(g, lds);
+            load_tile<0>(g, lds);
             __syncthreads();
             T v[VPT];
             read_own(g, lds, v);
