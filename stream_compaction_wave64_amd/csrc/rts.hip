@@ -27,7 +27,15 @@ __global__ __launch_bounds__(B) void k_rts_reduce(RtsArgs a) {
     TS ts;
     for (uint64_t t = t0; t < t1; t++) {
         const int64_t start = int64_t(t) * TS::TILE;
-        ts.load(reinterpret_cast<const T *>(a.in) + start, a.n - start);
+        // plain (temporal) loads, unlike TileScan::load: the rescan reads the
+        // chunk again and may find part of it in the caches
+        const T *src = reinterpret_cast<const T *>(a.in) + start;
+        ts.rem = a.n - start;
+#pragma unroll
+        for (int r = 0; r < R; r++) {
+            const int64_t e = TS::elem(r);
+            ts.v[r] = *reinterpret_cast<const Vec<T, V> *>(src + (e < ts.rem ? e : 0));
+        }
         ts.reduce(sh);
         acc = Op::apply(acc, C(ts.agg));
         __syncthreads();
@@ -67,11 +75,14 @@ __global__ __launch_bounds__(B) void k_rts_rescan(RtsArgs a) {
     __shared__ typename TS::Shared sh;
     __shared__ C s_base;
     C *partials = reinterpret_cast<C *>(a.partials);
-    if (threadIdx.x == 0) s_base = partials[blockIdx.x];
+    // chunks in reverse: workgroups start in index order, so the first ones
+    // take the chunks the reduce pass read last, the likeliest still cached
+    const uint32_t chunk = a.blocks - 1u - blockIdx.x;
+    if (threadIdx.x == 0) s_base = partials[chunk];
     __syncthreads();
     C base = s_base;
-    if (threadIdx.x == 0) partials[blockIdx.x] = C{};  // leave the workspace zeroed
-    const uint64_t t0 = uint64_t(blockIdx.x) * a.chunk_tiles;
+    if (threadIdx.x == 0) partials[chunk] = C{};  // leave the workspace zeroed
+    const uint64_t t0 = uint64_t(chunk) * a.chunk_tiles;
     const uint64_t t1 = t0 + a.chunk_tiles < a.num_tiles ? t0 + a.chunk_tiles : a.num_tiles;
     TS ts;
     for (uint64_t t = t0; t < t1; t++) {
