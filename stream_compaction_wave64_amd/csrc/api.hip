@@ -516,6 +516,8 @@ int scan_common(const void *in, void *out, int64_t outer, int64_t len, int64_t i
         r.chunk_tiles = uint32_t(p.rts_chunk);
         r.blocks = uint32_t(p.rts_blocks);
         r.exclusive = exclusive ? 1 : 0;
+        // larger than the 256 MB Infinity Cache can keep between the passes
+        r.reverse = len * dtype_bytes(dt) > (int64_t(192) << 20) ? 1 : 0;
         r.partials = reinterpret_cast<char *>(ws) + kHeader;
         return find_rts(dt, op, p.block, p.rows, p.vec)(r, stream);
     }

@@ -45,6 +45,7 @@ struct RtsArgs {
     uint32_t chunk_tiles;
     uint32_t blocks;
     int32_t exclusive;
+    int32_t reverse;          // rescan the chunks in reverse (arrays larger than the caches)
     void *partials;
 };
 using RtsLaunch = int (*)(const RtsArgs &, hipStream_t);

@@ -75,13 +75,15 @@ __global__ __launch_bounds__(B) void k_rts_rescan(RtsArgs a) {
     __shared__ typename TS::Shared sh;
     __shared__ C s_base;
     C *partials = reinterpret_cast<C *>(a.partials);
-    // chunks in reverse: workgroups start in index order, so the first ones
-    // take the chunks the reduce pass read last, the likeliest still cached.
-    // Workgroup b runs on XCD b mod 8 (round-robin dispatch), so the
-    // reversal keeps b mod 8: each chunk is rescanned on the XCD whose L2
-    // read it.  The last G mod 8 workgroups keep their own chunks.
+    // For arrays larger than the caches, chunks in reverse: workgroups start
+    // in index order, so the first ones take the chunks the reduce pass read
+    // last, the likeliest still cached.  Workgroup b runs on XCD b mod 8
+    // (round-robin dispatch), so the reversal keeps b mod 8: each chunk is
+    // rescanned on the XCD whose L2 read it.  The last G mod 8 workgroups
+    // keep their own chunks.  (Arrays that fit measured fastest in the
+    // reduce pass's own order.)
     const uint32_t b = blockIdx.x, full = a.blocks & ~7u;
-    const uint32_t chunk = b < full ? full - 8u - (b & ~7u) + (b & 7u) : b;
+    const uint32_t chunk = a.reverse && b < full ? full - 8u - (b & ~7u) + (b & 7u) : b;
     if (threadIdx.x == 0) s_base = partials[chunk];
     __syncthreads();
     C base = s_base;
