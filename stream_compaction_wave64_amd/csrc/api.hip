@@ -473,7 +473,7 @@ int scan_common(const void *in, void *out, int64_t outer, int64_t len, int64_t i
             if (rc != SCAN_OK) return rc;
             rc = check_ws(ws, ws_bytes, p.ws_bytes);
             if (rc != SCAN_OK) return rc;
-            ColArgs c;
+            ColArgs c{};
             c.in = in;
             c.out = out;
             c.outer = uint32_t(outer);
@@ -489,7 +489,7 @@ int scan_common(const void *in, void *out, int64_t outer, int64_t len, int64_t i
         if (rc != SCAN_OK) return rc;
         rc = check_ws(ws, ws_bytes, p.ws_bytes);
         if (rc != SCAN_OK) return rc;
-        ElemArgs a;
+        ElemArgs a{};
         a.in = in;
         a.out = out;
         a.outer = uint32_t(outer);
@@ -508,7 +508,7 @@ int scan_common(const void *in, void *out, int64_t outer, int64_t len, int64_t i
     if (rc != SCAN_OK) return rc;
     if (p.kernel == SCAN_KERNEL_RTS) {
         if (total_out != nullptr) return SCAN_ERR_UNSUPPORTED;
-        RtsArgs r;
+        RtsArgs r{};
         r.in = in;
         r.out = out;
         r.n = len;
@@ -521,7 +521,7 @@ int scan_common(const void *in, void *out, int64_t outer, int64_t len, int64_t i
         r.partials = reinterpret_cast<char *>(ws) + kHeader;
         return find_rts(dt, op, p.block, p.rows, p.vec)(r, stream);
     }
-    ScanArgs a;
+    ScanArgs a{};
     a.pipe = pipe_args(p, ws, ws_bytes, tu);
     a.in = in;
     a.out = out;
@@ -686,7 +686,7 @@ int compact_if(const void *x, int64_t n, scan_dtype_t x_dtype, scan_cmp_t cmp, d
     if (rc != SCAN_OK) return rc;
     rc = check_ws(ws, ws_bytes, p.ws_bytes);
     if (rc != SCAN_OK) return rc;
-    CompactArgs a;
+    CompactArgs a{};
     a.pipe = pipe_args(p, ws, ws_bytes, tu);
     a.x = x;
     a.n = n;
@@ -715,7 +715,7 @@ int partition_if(const void *x, int64_t n, scan_dtype_t x_dtype, scan_cmp_t cmp,
     if (rc != SCAN_OK) return rc;
     rc = check_ws(ws, ws_bytes, p.ws_bytes);
     if (rc != SCAN_OK) return rc;
-    PartitionArgs a;
+    PartitionArgs a{};
     a.pipe = pipe_args(p, ws, ws_bytes, tu);
     a.pipe.words_used = uint64_t(p.num_tiles + count_wgs);  // tile descriptors, then the counts
     a.x = x;
@@ -744,7 +744,7 @@ int scan_segmented(const void *in, void *out, int64_t n, const int32_t *offsets,
     if (rc != SCAN_OK) return rc;
     rc = check_ws(ws, ws_bytes, p.ws_bytes);
     if (rc != SCAN_OK) return rc;
-    SegArgs a;
+    SegArgs a{};
     a.in = in;
     a.out = out;
     a.n = n;
