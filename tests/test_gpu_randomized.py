@@ -1,0 +1,152 @@
+"""Seeded randomized parity sweep over every entry point: array lengths drawn
+around tile and vector boundaries (and at random), every dtype and operator,
+inclusive and exclusive, aligned and misaligned data, and tunings that change
+the tile shape, the grid, the algorithm and the chunk count.  Each case is
+compared with the oracle under the usual rules (bit-exact for integers,
+max/min, indices and moved values; the stated tolerance for fp sums and
+products).  The draw is fixed by the seed, so a failure names a reproducible
+case."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import stream_compaction_wave64_amd as sw
+from stream_compaction_wave64_amd import inputs
+from gpu_util import DEV, assert_scan_matches, assert_segscan_matches, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+DTYPES = [np.int32, np.uint32, np.int64, np.float32, np.float64]
+OPS = ["sum", "prod", "max", "min"]
+CASES = 150
+
+
+def _length(rng, tile):
+    kind = rng.integers(0, 4)
+    if kind == 0:  # just around a multiple of the tile
+        return int(max(1, tile * rng.integers(1, 9) + rng.integers(-5, 6)))
+    if kind == 1:  # tiny
+        return int(rng.integers(1, 200))
+    if kind == 2:  # a few vectors off a vector boundary
+        return int(4 * rng.integers(1, 20000) + rng.integers(0, 4))
+    return int(rng.integers(1, 600_000))
+
+
+def _values(dt, n, seed, op):
+    kind = "near1" if op == "prod" and np.issubdtype(dt, np.floating) else "wide"
+    if op == "sum" and np.issubdtype(dt, np.floating):
+        kind = "default"
+    return inputs.generic(dt, n, seed, kind)
+
+
+def _device(x, offset):
+    if not offset:
+        return to_dev(x), None
+    buf = to_dev(np.concatenate([np.zeros(offset, x.dtype), x]))
+    out = torch.empty(x.size + offset, dtype=buf.dtype, device=DEV)
+    return buf[offset:], out[offset:]
+
+
+def _tuning(rng, vec):
+    choices = [None,
+               {"block_size": 256, "items_per_thread": vec},
+               {"grid_blocks": int(rng.integers(1, 40))},
+               {"algo": "reduce_then_scan"},
+               {"algo": "reduce_then_scan", "rts_blocks": int(rng.integers(1, 300))}]
+    return choices[int(rng.integers(0, len(choices)))]
+
+
+def test_random_scans():
+    rng = np.random.default_rng(2026)
+    for case in range(CASES):
+        dt = DTYPES[int(rng.integers(0, len(DTYPES)))]
+        op = OPS[int(rng.integers(0, len(OPS)))]
+        excl = bool(rng.integers(0, 2))
+        vec = 16 // np.dtype(dt).itemsize
+        tile = sw.plan("scan", torch.float64 if vec == 2 else torch.float32, "sum", 1, 1 << 20)["tile_elems"]
+        n = _length(rng, tile)
+        offset = int(rng.integers(0, vec)) if rng.integers(0, 4) == 0 else 0
+        tuning = _tuning(rng, vec)
+        x = _values(dt, n, 100 + case, op)
+        xd, out = _device(x, offset)
+        fn = sw.scan_exclusive if excl else sw.scan_inclusive
+        r = fn(xd, op=op, out=out, tuning=tuning)
+        torch.cuda.synchronize()
+        assert_scan_matches(x, to_host(r), op, excl,
+                            what=f"case {case}: {np.dtype(dt).name} {op} excl={excl} n={n} off={offset} {tuning}")
+
+
+def test_random_scan_dims():
+    rng = np.random.default_rng(2027)
+    for case in range(CASES // 2):
+        dt = DTYPES[int(rng.integers(0, len(DTYPES)))]
+        op = OPS[int(rng.integers(0, len(OPS)))]
+        excl = bool(rng.integers(0, 2))
+        rows, cols = int(rng.integers(1, 700)), int(rng.integers(1, 700))
+        dim = int(rng.integers(0, 2))
+        x = _values(dt, rows * cols, 200 + case, op).reshape(rows, cols)
+        r = sw.scan_dim(to_dev(x), dim, op=op, exclusive=excl)
+        torch.cuda.synchronize()
+        dims = (1, rows, cols) if dim == 0 else (rows, cols, 1)  # (outer, len, inner)
+        assert_scan_matches(x.ravel(), to_host(r).ravel(), op, excl, dims=dims,
+                            what=f"case {case}: {np.dtype(dt).name} {op} excl={excl} {rows}x{cols} dim={dim}")
+
+
+def test_random_compaction_and_partition():
+    rng = np.random.default_rng(2028)
+    cmps = ["gt", "ge", "lt", "le", "eq", "ne"]
+    for case in range(CASES):
+        n = _length(rng, 14336)
+        dt = [np.float32, np.int32, np.uint32][int(rng.integers(0, 3))]
+        cmp = cmps[int(rng.integers(0, len(cmps)))]
+        if dt == np.float32:
+            x = rng.random(n, dtype=np.float32)
+            t = float(rng.choice([0.0, 0.25, 0.5, 0.99]))
+            x[rng.integers(0, n, max(1, n // 50))] = np.float32(t)  # ties
+        else:
+            x = rng.integers(0, 64, n).astype(dt)
+            t = int(rng.integers(0, 64))
+        tuning = [None, {"block_size": 256, "items_per_thread": 4}, {"grid_blocks": int(rng.integers(1, 30))}][
+            int(rng.integers(0, 3))]
+        what = f"case {case}: {np.dtype(dt).name} {cmp} {t} n={n} {tuning}"
+        idx, count = sw.compact_if(to_dev(x), cmp, t, tuning=tuning)
+        torch.cuda.synchronize()
+        ref = oracle.compact(x, cmp, t)
+        c = int(count.item())
+        assert c == ref.size, what
+        assert np.array_equal(to_host(idx)[:c], ref), what
+        vals, vidx, k = oracle.partition(x, cmp, t)
+        out, oidx, count = sw.partition_if(to_dev(x), cmp, t, tuning=tuning)
+        torch.cuda.synchronize()
+        assert int(count.item()) == k, what
+        assert np.array_equal(to_host(out)[:n].view(np.uint32), vals.view(np.uint32)), what
+        assert np.array_equal(to_host(oidx)[:n], vidx), what
+
+
+def test_random_packing_and_segments():
+    rng = np.random.default_rng(2029)
+    for case in range(CASES // 2):
+        nobj = int(rng.integers(1, 300_000))
+        mean = float(rng.choice([0.2, 1.0, 3.0, 17.0]))
+        counts = rng.poisson(mean, nobj).astype(np.int32)
+        ref_off, ref_total = oracle.pack_offsets(counts)
+        off = sw.pack_offsets(to_dev(counts))
+        torch.cuda.synchronize()
+        got_off = to_host(off)
+        assert np.array_equal(got_off, ref_off), f"case {case}: offsets nobj={nobj} mean={mean}"
+        total = int(ref_total)
+        if total > 0:
+            rec = sw.pack_emit_neighbors(off, total)
+            torch.cuda.synchronize()
+            assert np.array_equal(to_host(rec), oracle.pack_emit(ref_off)), f"case {case}: records"
+            dt = DTYPES[int(rng.integers(0, len(DTYPES)))]
+            op = OPS[int(rng.integers(0, len(OPS)))]
+            excl = bool(rng.integers(0, 2))
+            x = _values(dt, total, 300 + case, op)
+            tuning = [None, {"algo": "lookback"}, {"block_size": 256, "items_per_thread": 16 // np.dtype(dt).itemsize},
+                      {"algo": "lookback", "grid_blocks": int(rng.integers(1, 20))}][int(rng.integers(0, 4))]
+            r = sw.scan_segmented(to_dev(x), off, op, excl, tuning=tuning)
+            torch.cuda.synchronize()
+            assert_segscan_matches(x, ref_off, to_host(r), op, excl,
+                                   what=f"case {case}: {np.dtype(dt).name} {op} excl={excl} nobj={nobj} {tuning}")
