@@ -529,6 +529,8 @@ int scan_common(const void *in, void *out, int64_t outer, int64_t len, int64_t i
     a.exclusive = exclusive ? 1 : 0;
     a.total_out = total_out;
     const uint32_t grid_cap = tu.grid_blocks > 0 ? uint32_t(tu.grid_blocks) : 0u;
+    if (total_out != nullptr && dt == SCAN_I32 && op == SCAN_OP_SUM)  // count-scan-emit's offsets
+        return find_pack_lookback(p.block, p.rows, p.vec)(a, grid_cap, stream);
     return find_lookback(dt, op, p.block, p.rows, p.vec)(a, grid_cap, stream);
 }
 

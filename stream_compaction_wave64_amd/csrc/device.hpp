@@ -655,11 +655,13 @@ __device__ __forceinline__ BufRsrc make_rsrc(const T *base, int64_t count) {
 
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 
-// Nontemporal (streaming) store of one vector through a buffer resource.
-template <class T, int V>
+// Store of one vector through a buffer resource; AUX is the cache policy
+// (2: nontemporal, streaming, the default; 0: the default policy, for an
+// output the next kernel reads right away).
+template <class T, int V, int AUX = 2>
 __device__ __forceinline__ void store_vec_bounded(BufRsrc rs, uint32_t byte_off, const Vec<T, V> &x) {
     constexpr int B = int(sizeof(T)) * V;
-    constexpr int kNT = 2;  // cache policy: nontemporal
+    constexpr int kNT = AUX;
     if constexpr (B == 16) {
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, x), rs, byte_off, 0, kNT);
     } else if constexpr (B == 8) {

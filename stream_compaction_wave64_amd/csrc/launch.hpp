@@ -29,6 +29,7 @@ struct ScanArgs {
 };
 using LbLaunch = int (*)(const ScanArgs &, uint32_t grid_cap, hipStream_t);
 LbLaunch find_lookback(scan_dtype_t dt, scan_op_t op, int block, int rows, int vec);
+LbLaunch find_pack_lookback(int block, int rows, int vec);  // int32 sum, offsets kept cacheable
 
 // ---------------------------------------------------------- reduce-then-scan
 // Three launches over `blocks` workgroups, each owning `chunk_tiles`

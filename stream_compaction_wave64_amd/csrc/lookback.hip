@@ -16,7 +16,10 @@
 
 namespace sw64 {
 
-template <class T_, class Op_, int BLOCK_, int ROWS, int VEC>
+// OUT_AUX: the output stores' cache policy: nontemporal (2) for scans;
+// the default (0) for count-scan-emit's offsets, which the emit kernel reads
+// next and may then find in the caches.
+template <class T_, class Op_, int BLOCK_, int ROWS, int VEC, int OUT_AUX = 2>
 struct ScanPolicy {
     using T = T_;
     using Op = Op_;
@@ -57,7 +60,8 @@ struct ScanPolicy {
         Vec<T, VEC> w[ROWS];
 #pragma unroll
         for (int r = 0; r < ROWS; r++) w[r] = st.v[r][threadIdx.x];
-        TS::store_folded(w, reinterpret_cast<T *>(a.out) + (valid ? start : 0), valid ? remaining : 0, pre);
+        TS::template store_folded<OUT_AUX>(w, reinterpret_cast<T *>(a.out) + (valid ? start : 0),
+                                           valid ? remaining : 0, pre);
     }
 
     // The segment total after its last tile (count-scan-emit's offsets[n]).
@@ -98,9 +102,9 @@ __global__ __launch_bounds__(CtrlPipeline<P>::THREADS) void k_lookback(typename 
 }
 
 // B threads per workgroup: B - 64 data threads and the control wave.
-template <class T, class Op, int B, int R, int V>
+template <class T, class Op, int B, int R, int V, int OUT_AUX = 2>
 static int launch_lookback_impl(const ScanArgs &a, uint32_t grid_cap, hipStream_t s) {
-    using P = ScanPolicy<T, Op, B - kWave, R, V>;
+    using P = ScanPolicy<T, Op, B - kWave, R, V, OUT_AUX>;
     static_assert(CtrlPipeline<P>::THREADS == B, "launch size");
     const int g = pipeline_grid(reinterpret_cast<const void *>(&k_lookback<P>), B, a.pipe.num_tiles, grid_cap);
     if (g <= 0) return SCAN_ERR_HIP;
@@ -165,6 +169,12 @@ static LbLaunch pick_op(scan_op_t op, int block, int rows, int vec) {
 
 #if SW64_DT == 0
 LbLaunch find_lookback_i32(scan_op_t op, int b, int r, int v) { return pick_op<int32_t>(op, b, r, v); }
+// count-scan-emit's offsets (int32 sums) in the default shape, stored with
+// the default cache policy; other shapes use the scan's launchers
+LbLaunch find_pack_lookback(int b, int r, int v) {
+    if (b == 768 && r == 7 && v == 4) return &launch_lookback_impl<int32_t, OpSum, 768, 7, 4, 0>;
+    return pick_op<int32_t>(SCAN_OP_SUM, b, r, v);
+}
 #elif SW64_DT == 1
 LbLaunch find_lookback_u32(scan_op_t op, int b, int r, int v) { return pick_op<uint32_t>(op, b, r, v); }
 #elif SW64_DT == 2

@@ -162,6 +162,7 @@ struct TileScan {
 
     // Store fold()ed values with the tile's prefix `pre` applied (in the
     // carry type, rounded once).  Rows at or past `remaining` are dropped.
+    template <int AUX = 2>  // the stores' cache policy (see store_vec_bounded)
     __device__ __forceinline__ static void store_folded(const Vec<T, VEC> (&w)[ROWS], T *dst, int64_t remaining,
                                                         C pre) {
         const BufRsrc rs = make_rsrc(dst, remaining < TILE ? (remaining > 0 ? remaining : 0) : TILE);
@@ -170,7 +171,7 @@ struct TileScan {
             Vec<T, VEC> o;
 #pragma unroll
             for (int c = 0; c < VEC; c++) o.v[c] = T(Op::apply(pre, C(w[r].v[c])));
-            store_vec_bounded<T, VEC>(rs, uint32_t(elem(r) * int64_t(sizeof(T))), o);
+            store_vec_bounded<T, VEC, AUX>(rs, uint32_t(elem(r) * int64_t(sizeof(T))), o);
         }
     }
 
