@@ -40,7 +40,7 @@ N = 10 ** 8
 # known size (profiles/lookback_scan_fp32_1e8_hbm_counters.md).  Valid only for
 # the kernel sources that were measured: reported as null once they change.
 TRAFFIC_BYTES = 8.012e8
-TRAFFIC_SOURCES_SHA = "faf59983a8e804da"
+TRAFFIC_SOURCES_SHA = "b5de5569d903c33b"
 
 
 def _kernel_sources_sha():
