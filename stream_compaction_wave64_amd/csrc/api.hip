@@ -320,8 +320,7 @@ int plan_compact(scan_dtype_t dt, int64_t n, bool aligned, const scan_tuning_t &
     // 128-bit loads need 16-byte aligned x and whole vectors up to n
     const int rc = plan_shape(
         4, aligned && n % 4 == 0, tu, p,
-        [&](int b, int r, int v) { return find_compact(dt, SCAN_CMP_GT, b, r, v) != nullptr; }, true, 8,
-        kDefaultBlock);
+        [&](int b, int r, int v) { return find_compact(dt, SCAN_CMP_GT, b, r, v) != nullptr; }, true, 5, 768);
     if (rc != SCAN_OK) return rc;
     p.kernel = SCAN_KERNEL_COMPACT;
     p.tiles_per_seg = p.num_tiles = (n + p.tile - 1) / p.tile;

@@ -68,7 +68,7 @@ def test_compaction_integer_keys_and_bit_predicates(dt):
 
 
 def test_compaction_closed_forms_and_edges():
-    for n in (1, 3, 4, 5, 1000, 16384, 16385, 100_003):
+    for n in (1, 3, 4, 5, 1000, 14080, 14081, 16384, 16385, 100_003):
         _check_compact(np.ones(n, np.float32))                      # all selected -> iota
         _check_compact(np.zeros(n, np.float32))                     # none selected
         _check_compact(np.tile(np.array([0, 1], np.float32), n)[:n])  # alternating -> 2k+1
