@@ -414,8 +414,7 @@ int plan_partition(scan_dtype_t dt, scan_cmp_t cmp, int64_t n, bool aligned, con
                    int64_t &count_wgs, int64_t &count_chunk) {
     const int rc = plan_shape(
         4, aligned && n % 4 == 0, tu, p,
-        [&](int b, int r, int v) { return find_partition(dt, cmp, b, r, v) != nullptr; }, true, 6,
-        kDefaultBlock);
+        [&](int b, int r, int v) { return find_partition(dt, cmp, b, r, v) != nullptr; }, true, 3, 768);
     if (rc != SCAN_OK) return rc;
     p.kernel = SCAN_KERNEL_PARTITION;
     p.tiles_per_seg = p.num_tiles = (n + p.tile - 1) / p.tile;

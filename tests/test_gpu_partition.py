@@ -64,7 +64,7 @@ def test_partition_bit_digits(dt):
 
 
 def test_partition_edges_and_shapes():
-    for n in (1, 3, 4, 5, 1000, 14336, 14337, 100_003):
+    for n in (1, 3, 4, 5, 1000, 8448, 8449, 14336, 14337, 100_003):
         _check(np.ones(n, np.float32))                               # all selected: identity
         _check(np.zeros(n, np.float32))                              # none selected: identity
         _check(np.tile(np.array([0, 1], np.float32), n)[:n])         # odd indices first
