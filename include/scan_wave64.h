@@ -115,7 +115,8 @@ typedef struct {
     int32_t items_per_thread;  /* elements per thread per tile (a multiple of
                                   the 128-bit vector width; the element-wide
                                   fallback snaps it to its nearest built shape) */
-    int64_t local_mem_bytes;   /* LDS budget per workgroup for large elements */
+    int64_t local_mem_bytes;   /* LDS budget per workgroup for large elements
+                                  (default 32 KiB, the PR's) */
     int32_t algo;              /* scan_algo_t */
     int32_t rts_blocks;        /* workgroup count C of reduce-then-scan */
     int32_t spin_limit;        /* polls of one look-back window before a tile

@@ -105,7 +105,8 @@ constexpr uint32_t kDefaultSpinLimit = 1u << 22;
 constexpr uint32_t kDefaultModeLimit = 512;
 constexpr int kDefaultBlock = 512;  // threads per workgroup of the tiled kernels
 constexpr int kDefaultRtsBlocks = 1024;               // C of reduce-then-scan
-constexpr int64_t kDefaultLocalMem = 64 * 1024;       // LDS budget of the large-element rule
+constexpr int64_t kDefaultLocalMem = 32 * 1024;       // LDS budget of the large-element rule (AcceleratedKernels.jl PR #208)
+constexpr int64_t kElemTileLocalMem = 64 * 1024;      // default bound on an element tile's E (default dynamic LDS limit)
 constexpr int kElemDefaultBlock = 256;                // large elements: start of the rule
 constexpr int64_t kElemChunks = 2048;  // large elements: workgroups per launch (<= 8192, the partials pass)
 
@@ -245,7 +246,10 @@ int plan_scan(scan_dtype_t dt, scan_op_t op, int64_t outer, int64_t len, bool al
 
 // Large elements (inner > 1): `block` threads per workgroup from the PR's
 // rule, each owning E elements of a tile: E = elem_e_max(inner) when that
-// tile still fits the rule's budget (2 * block * E * esize bytes), else 1.
+// tile still fits (2 * block * E * esize bytes within the caller's budget,
+// else within kElemTileLocalMem), else 1.  The rule's own budget only sizes
+// the block: E is this kernel's blocking, not the PR's, and narrow elements
+// (1e6 x 8 fp32: 256 threads x 4) lose a third of their rate at E = 1.
 // Chunks of tiles give about kElemChunks workgroups per launch.
 int plan_element(scan_dtype_t dt, scan_op_t op, int64_t outer, int64_t len, int64_t inner, bool aligned,
                  const scan_tuning_t &tu, TilePlan &p) {
@@ -257,7 +261,8 @@ int plan_element(scan_dtype_t dt, scan_op_t op, int64_t outer, int64_t len, int6
     if (b < 64 || b > 512 || b % 64 != 0) return SCAN_ERR_UNSUPPORTED;
     const bool vec = aligned && (inner * esize) % 16 == 0;
     int e = elem_e_max(int(inner));
-    if (e > 1 && 2 * b * e * inner * esize > budget) e = 1;
+    const int64_t e_budget = tu.local_mem_bytes > 0 ? tu.local_mem_bytes : kElemTileLocalMem;
+    if (e > 1 && 2 * b * e * inner * esize > e_budget) e = 1;
     if (!find_element(dt, op, int(inner), e, vec)) return SCAN_ERR_UNSUPPORTED;
     p.kernel = SCAN_KERNEL_ELEMENT;
     p.block = int(b);

@@ -193,7 +193,7 @@ def test_element_block_rule_matches_oracle():
         for w in (2, 3, 4, 8, 16, 17, 24):
             for budget in (0, 32768, 65536, 49152):
                 tun = {"local_mem_bytes": budget} if budget else None
-                expect = oracle.block_size(w * esz, budget or 65536, 0, 256)
+                expect = oracle.block_size(w * esz, budget or 32768, 0, 256)
                 if expect < 64:
                     continue
                 p = binding.plan("scan", dt, "sum", 1, 10 ** 6, w, tuning=tun)
@@ -201,8 +201,11 @@ def test_element_block_rule_matches_oracle():
     # explicit block size is kept
     p = binding.plan("scan", torch.float64, "sum", 1, 10 ** 6, 17, tuning={"block_size": 64})
     assert p["block_size"] == 64
-    # the two struct configs: 136-byte duals and 96-byte structs at the 64 KiB default
-    assert binding.plan("scan", torch.float64, "sum", 1, 10 ** 6, 17)["block_size"] == 128
-    assert binding.plan("scan", torch.float32, "sum", 1, 10 ** 6, 24)["block_size"] == 256
+    # the two struct configs: 136-byte duals and 96-byte structs at the PR's 32 KiB default
+    assert binding.plan("scan", torch.float64, "sum", 1, 10 ** 6, 17)["block_size"] == 64
+    assert binding.plan("scan", torch.float32, "sum", 1, 10 ** 6, 24)["block_size"] == 128
+    # a budget below one wave's tile (2 * 64 * 192 B) falls through to the column kernel
+    p = binding.plan("scan", torch.float64, "sum", 1, 10 ** 5, 24, tuning={"local_mem_bytes": 16384})
+    assert p["kernel"] == "columns", p
     assert binding.plan("scan", torch.float64, "sum", 1, 10 ** 6, 17)["carry_words"] == 34
     assert binding.plan("scan", torch.float32, "sum", 1, 10 ** 6, 24)["carry_words"] == 48
