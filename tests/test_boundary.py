@@ -92,6 +92,32 @@ def test_plan_segments_and_types():
         binding.plan("scan", torch.float32, "sum", 1, 1000, tuning={"block_size": 192, "items_per_thread": 4})
 
 
+def test_plan_small_arrays_take_short_tiles():
+    # Whole arrays that 448 x 5-row tiles cover in at most 256 tiles (one per
+    # CU) take those tiles; larger ones, rows of a 2-D array, explicit shapes
+    # and the reduce-then-scan path keep their own (arrays within one default
+    # tile follow the short-segment rule instead).
+    from stream_compaction_wave64_amd import binding
+    import torch
+    for dt, vec, big_ipt in ((torch.int32, 4, 28), (torch.float32, 4, 28), (torch.float64, 2, 16)):
+        small_tile = 448 * 5 * vec
+        big_tile = 448 * big_ipt if vec == 2 else 704 * big_ipt
+        for n in (2 * big_tile, 128 * small_tile, 256 * small_tile):
+            p = binding.plan("scan", dt, "sum", 1, n)
+            assert (p["block_size"], p["items_per_thread"]) == (512, 5 * vec), (dt, n, p)
+            assert p["num_tiles"] <= 256
+        p = binding.plan("scan", dt, "sum", 1, 256 * small_tile + vec)
+        assert p["items_per_thread"] == big_ipt, (dt, p)
+        p = binding.plan("scan", dt, "sum", 1, 64 * small_tile + 1)  # element-wide path: unchanged
+        assert p["vec"] == 1 and p["items_per_thread"] == big_ipt // vec, (dt, p)
+        p = binding.plan("scan", dt, "sum", 1, 64 * small_tile, tuning={"block_size": 512, "items_per_thread": 3 * vec})
+        assert p["items_per_thread"] == 3 * vec
+        p = binding.plan("scan", dt, "sum", 2, 64 * small_tile)
+        assert p["items_per_thread"] == big_ipt, (dt, p)
+    p = binding.plan("scan", torch.float32, "sum", 1, 1 << 20, tuning={"algo": "reduce_then_scan"})
+    assert p["kernel"] == "reduce_then_scan" and p["items_per_thread"] == 32
+
+
 def _call_scan(lib, fn, inp, out, n, dt=3, op=0, width=1, ws=None, wsb=0):
     return getattr(lib, fn)(inp, out, n, dt, op, width, ws, wsb, None, None)
 
