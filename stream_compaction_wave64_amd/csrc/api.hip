@@ -26,6 +26,27 @@ ElemLaunch find_element_i64(scan_op_t, int, int, bool);
 ElemLaunch find_element_f32(scan_op_t, int, int, bool);
 ElemLaunch find_element_f64(scan_op_t, int, int, bool);
 
+CompactLaunch find_compact_i32(scan_cmp_t, int, int, int);
+CompactLaunch find_compact_u32(scan_cmp_t, int, int, int);
+CompactLaunch find_compact_f32(scan_cmp_t, int, int, int);
+PartitionLaunch find_partition_i32(scan_cmp_t, int, int, int);
+PartitionLaunch find_partition_u32(scan_cmp_t, int, int, int);
+PartitionLaunch find_partition_f32(scan_cmp_t, int, int, int);
+
+CompactLaunch find_compact(scan_dtype_t dt, scan_cmp_t cmp, int block, int rows, int vec) {
+    if (dt == SCAN_F32) return find_compact_f32(cmp, block, rows, vec);
+    if (dt == SCAN_I32) return find_compact_i32(cmp, block, rows, vec);
+    if (dt == SCAN_U32) return find_compact_u32(cmp, block, rows, vec);
+    return nullptr;
+}
+
+PartitionLaunch find_partition(scan_dtype_t dt, scan_cmp_t cmp, int block, int rows, int vec) {
+    if (dt == SCAN_F32) return find_partition_f32(cmp, block, rows, vec);
+    if (dt == SCAN_I32) return find_partition_i32(cmp, block, rows, vec);
+    if (dt == SCAN_U32) return find_partition_u32(cmp, block, rows, vec);
+    return nullptr;
+}
+
 ColLaunch find_columns_i32(scan_op_t, int);
 ColLaunch find_columns_u32(scan_op_t, int);
 ColLaunch find_columns_i64(scan_op_t, int);

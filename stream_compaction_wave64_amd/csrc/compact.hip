@@ -13,6 +13,10 @@
 // pack_emit_neighbors (same slides, "Solution" step 3): each object writes
 // its records from its start offset; record j of object i is (i + 1 + j)
 // mod n, a reading of the deliberately open record content.
+//
+// This file is compiled once per key type (SW64_DT: 0 int32, 1 uint32, 3
+// fp32) and per entry point (SW64_PART: 0 compaction and the emit kernel,
+// 1 partition), so the instantiations build in parallel.
 #include "launch.hpp"
 #include "tile.hpp"
 
@@ -218,12 +222,15 @@ static CompactLaunch pick_compact_cmp(scan_cmp_t cmp, int block, int rows, int v
     return nullptr;
 }
 
-CompactLaunch find_compact(scan_dtype_t dt, scan_cmp_t cmp, int block, int rows, int vec) {
-    if (dt == SCAN_F32) return pick_compact_cmp<float>(cmp, block, rows, vec);
-    if (dt == SCAN_I32) return pick_compact_cmp<int32_t>(cmp, block, rows, vec);
-    if (dt == SCAN_U32) return pick_compact_cmp<uint32_t>(cmp, block, rows, vec);
-    return nullptr;
-}
+#if SW64_PART == 0
+#if SW64_DT == 0
+CompactLaunch find_compact_i32(scan_cmp_t cmp, int b, int r, int v) { return pick_compact_cmp<int32_t>(cmp, b, r, v); }
+#elif SW64_DT == 1
+CompactLaunch find_compact_u32(scan_cmp_t cmp, int b, int r, int v) { return pick_compact_cmp<uint32_t>(cmp, b, r, v); }
+#elif SW64_DT == 3
+CompactLaunch find_compact_f32(scan_cmp_t cmp, int b, int r, int v) { return pick_compact_cmp<float>(cmp, b, r, v); }
+#endif
+#endif
 
 // -------------------------------------------------------------- partition
 // Stable partition (Merry, "Prefix sums on GPUs", slide "Other
@@ -449,13 +456,17 @@ static PartitionLaunch pick_partition_cmp(scan_cmp_t cmp, int block, int rows, i
     return nullptr;
 }
 
-PartitionLaunch find_partition(scan_dtype_t dt, scan_cmp_t cmp, int block, int rows, int vec) {
-    if (dt == SCAN_F32) return pick_partition_cmp<float>(cmp, block, rows, vec);
-    if (dt == SCAN_I32) return pick_partition_cmp<int32_t>(cmp, block, rows, vec);
-    if (dt == SCAN_U32) return pick_partition_cmp<uint32_t>(cmp, block, rows, vec);
-    return nullptr;
-}
+#if SW64_PART == 1
+#if SW64_DT == 0
+PartitionLaunch find_partition_i32(scan_cmp_t cmp, int b, int r, int v) { return pick_partition_cmp<int32_t>(cmp, b, r, v); }
+#elif SW64_DT == 1
+PartitionLaunch find_partition_u32(scan_cmp_t cmp, int b, int r, int v) { return pick_partition_cmp<uint32_t>(cmp, b, r, v); }
+#elif SW64_DT == 3
+PartitionLaunch find_partition_f32(scan_cmp_t cmp, int b, int r, int v) { return pick_partition_cmp<float>(cmp, b, r, v); }
+#endif
+#endif
 
+#if SW64_PART == 0 && SW64_DT == 0
 // ------------------------------------------------------------------- emit
 // One thread per object; the record value starts at (i + 1) mod n and wraps
 // at n without a division per record.
@@ -530,4 +541,10 @@ int launch_emit_neighbors(const int32_t *offsets, int64_t n, int32_t *out, hipSt
     return hipGetLastError() == hipSuccess ? SCAN_OK : SCAN_ERR_HIP;
 }
 
+#endif
+
 }  // namespace sw64
+
+#if !defined(SW64_PART) || !defined(SW64_DT) || (SW64_DT != 0 && SW64_DT != 1 && SW64_DT != 3)
+#error "SW64_PART (0, 1) and SW64_DT (0, 1, 3) select the unit"
+#endif
