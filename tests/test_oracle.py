@@ -280,6 +280,54 @@ def test_scan_invariants_float(oracle_lib):
     assert np.all(np.diff(m) >= 0) and np.all(m >= x)
 
 
+# ------------------------------------------- tolerance weights, signed inputs
+# P_i = sum of |x_j| over the inputs output i depends on scales every fp
+# tolerance, so it is pinned on signed data, where a dropped absolute value
+# or a swapped inclusive/exclusive form changes the result.
+
+
+@pytest.mark.parametrize("dt", [np.float32, np.float64])
+def test_abs_prefix_alternating_signs_closed_form(oracle_lib, dt):
+    # +1, -1, +1, ...: the prefix alternates 1, 0, 1, ... while P_i = i + 1
+    # (inclusive) and i (exclusive), exactly.
+    n = 1001
+    x = np.where(np.arange(n) % 2 == 0, 1.0, -1.0).astype(dt)
+    i = np.arange(n, dtype=np.float64)
+    assert np.array_equal(oracle_lib.abs_prefix(x), i + 1)
+    assert np.array_equal(oracle_lib.abs_prefix(x, exclusive=True), i)
+    # the scan itself cancels: the weight is what keeps the tolerance honest
+    assert np.array_equal(oracle_lib.scan(x, "sum"), (i % 2 == 0).astype(np.float64))
+
+
+@pytest.mark.parametrize("dt,q", [(np.float32, 23), (np.float64, 30)])
+@pytest.mark.parametrize("exclusive", [False, True])
+def test_abs_prefix_signed_integer_shadow(oracle_lib, dt, q, exclusive):
+    # signed values on the 2^-q grid: |x_j| * 2^q are integers whose int64
+    # prefix is exact, and every partial sum stays below 2^53, so the
+    # oracle's fp64 accumulation must reproduce it bit for bit
+    rng = np.random.default_rng(7)
+    k = rng.integers(-(2 ** q), 2 ** q, 50_000, dtype=np.int64)
+    x = (k.astype(np.float64) * 2.0 ** -q).astype(dt)
+    assert np.array_equal(x.astype(np.float64) * 2.0 ** q, k.astype(np.float64))
+    a = np.abs(k)
+    shadow = np.cumsum(a) - (a if exclusive else 0)
+    assert np.array_equal(oracle_lib.abs_prefix(x, exclusive=exclusive), shadow.astype(np.float64) * 2.0 ** -q)
+
+
+@pytest.mark.parametrize("dt,q", [(np.float32, 23), (np.float64, 30)])
+@pytest.mark.parametrize("exclusive", [False, True])
+def test_abs_prefix_signed_dims(oracle_lib, dt, q, exclusive):
+    # (outer, len, inner) = (3, 257, 5): each of the 15 columns along the
+    # middle axis gets its own weight, exact on the grid
+    rng = np.random.default_rng(8)
+    k = rng.integers(-(2 ** q), 2 ** q, (3, 257, 5), dtype=np.int64)
+    x = (k.astype(np.float64) * 2.0 ** -q).astype(dt)
+    a = np.abs(k)
+    shadow = np.cumsum(a, axis=1) - (a if exclusive else 0)
+    got = oracle_lib.abs_prefix(x, exclusive=exclusive, dims=(3, 257, 5))
+    assert np.array_equal(got, shadow.astype(np.float64) * 2.0 ** -q)
+
+
 # ------------------------------------------------------- exact integer shadow
 
 

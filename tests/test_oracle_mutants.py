@@ -35,6 +35,11 @@ MUTANTS = {
     "abs prefix exclusive/inclusive swapped": (
         "if (exclusive) { p[at] = acc; acc += fabs((double)x[at]); }",
         "if (!exclusive) { p[at] = acc; acc += fabs((double)x[at]); }"),
+    "abs prefix f64 exclusive/inclusive swapped": (
+        "if (exclusive) { p[at] = acc; acc += fabs(x[at]); }",
+        "if (!exclusive) { p[at] = acc; acc += fabs(x[at]); }"),
+    "abs prefix f32 drops the absolute value": ("fabs((double)x[at])", "((double)x[at])"),
+    "abs prefix f64 drops the absolute value": ("fabs(x[at])", "(x[at])"),
     "compaction off by one": ("idx[count++] = (int32_t)i;", "idx[count++] = (int32_t)(i + 1);"),
     "compaction > taken as >=": ("case O_GT: return v > t;", "case O_GT: return v >= t;"),
     "partition rejected part not offset by k": (
@@ -68,6 +73,11 @@ PINS = [
     lambda o: [T.test_brute_force_small(o, dt, op, 65) for dt in T.ALL_TYPES for op in T.OPS],
     lambda o: T.test_matches_numpy_accumulate_u32_i64(o),
     lambda o: T.test_scan_invariants_float(o),
+    lambda o: [T.test_abs_prefix_alternating_signs_closed_form(o, dt) for dt in (np.float32, np.float64)],
+    lambda o: [T.test_abs_prefix_signed_integer_shadow(o, dt, q, e)
+               for dt, q in ((np.float32, 23), (np.float64, 30)) for e in (False, True)],
+    lambda o: [T.test_abs_prefix_signed_dims(o, dt, q, e)
+               for dt, q in ((np.float32, 23), (np.float64, 30)) for e in (False, True)],
     lambda o: T.test_fp64_exact_integer_shadow(o),
     lambda o: [T.test_dims_layouts_agree(o, dt) for dt in (np.int32, np.float32)],
     lambda o: T.test_compaction_brute_and_numpy(o),
