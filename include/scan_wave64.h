@@ -41,16 +41,24 @@
  * Workspace: a caller-owned, 256-byte aligned device buffer of at least the
  * size returned by scan_plan (per call) or scan_workspace_bytes (an upper bound for any call
  * on arrays of up to `count` values).  Before its first use it must be zeroed
- * once (scan_workspace_init or any zero fill).  After that it is self-
+ * once, preferably with scan_workspace_init.  After that it is self-
  * resetting: the look-back kernels tag their tile descriptors with a per-
  * workspace epoch held in the workspace header, advance it at the end of
  * each call and clear the descriptor words a previous, larger call left
- * above their own, so no clearing launch is needed between calls.  Calls that may
+ * above their own, so no clearing launch is needed between calls.
+ * scan_workspace_init records the buffer's size in the header: later calls
+ * may then pass any ws_bytes (e.g. each call's own scan_plan size) on the
+ * same buffer, and a call may write anywhere in the buffer so initialised
+ * until it is initialised again.  A buffer zeroed by other means has no
+ * recorded size; calls on it should pass the whole buffer each time (words a
+ * larger call tagged beyond a smaller call's ws_bytes are then cleared only
+ * by the next call that passes enough bytes to reach them).  Calls that may
  * overlap in time (different streams) need distinct workspaces.  Layout
  * (informative): bytes [0, 4096) header { uint32 epoch, uint32 error word,
- * uint64 descriptor high-water mark, uint32 mode, uint32 claim counter, and
- * sixteen counters of started workgroups, one per 128-byte line from byte
- * 128 }, then 64-bit descriptor words.
+ * uint64 descriptor high-water mark, uint32 mode, uint32 claim counter,
+ * uint64 recorded capacity in descriptor words (byte 24), and sixteen
+ * counters of started workgroups, one per 128-byte line from byte 128 },
+ * then 64-bit descriptor words.
  */
 #ifndef SCAN_WAVE64_H
 #define SCAN_WAVE64_H
@@ -174,7 +182,8 @@ int scan_plan(scan_call_t call, scan_dtype_t dtype, scan_op_t op, int64_t outer,
  * `count` values (components) of `dtype`, with any op and tuning. */
 size_t scan_workspace_bytes(scan_dtype_t dtype, int64_t count);
 
-/* Zero a workspace (one fill kernel). Required once before first use. */
+/* Zero a workspace and record its size in its header (one fill kernel).
+ * Required once before first use (see the workspace notes above). */
 int scan_workspace_init(void *ws, size_t ws_bytes, void *stream);
 
 /* Diagnostic (synchronizes `stream`): copy the workspace's error word to

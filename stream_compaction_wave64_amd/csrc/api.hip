@@ -677,7 +677,12 @@ size_t scan_workspace_bytes(scan_dtype_t dtype, int64_t count) {
 int scan_workspace_init(void *ws, size_t ws_bytes, void *stream) {
     if (ws_bytes == 0) return SCAN_OK;
     if (ws == nullptr || (reinterpret_cast<uintptr_t>(ws) & 7u)) return SCAN_ERR_INVALID_ARG;
-    return launch_fill_u64(ws, ws_bytes / 8, 0, reinterpret_cast<hipStream_t>(stream));
+    // zero everything; the header's capacity word records the descriptor
+    // words of this buffer, so that a later call passing a smaller size still
+    // clears what a larger one left tagged (end_call in device.hpp)
+    const uint64_t cap = ws_bytes > kHeader ? uint64_t(ws_bytes - kHeader) / 8 : 0;
+    return launch_fill_u64(ws, ws_bytes / 8, 0, reinterpret_cast<hipStream_t>(stream),
+                           offsetof(WsHeader, capacity) / 8, cap);
 }
 
 int scan_workspace_error(const void *ws, int32_t *error, void *stream) {

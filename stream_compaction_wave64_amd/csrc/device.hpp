@@ -13,6 +13,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <stddef.h>
 #include <stdint.h>
 
 #include <type_traits>
@@ -301,7 +302,8 @@ struct WsHeader {
     uint64_t high_water;  // descriptor words the last call left tagged
     uint32_t mode;        // (epoch << 2) | kModeStatic or kModeDynamic: the call that decided it
     uint32_t claim;       // next tile ticket in dynamic mode
-    uint32_t pad0[26];
+    uint64_t capacity;    // descriptor words of the buffer scan_workspace_init zeroed (0: not recorded)
+    uint32_t pad0[24];
     struct {
         uint32_t count;   // workgroups of the running call counted in this slot
         uint32_t pad[31];
@@ -309,6 +311,7 @@ struct WsHeader {
 };
 constexpr size_t kWsHeaderBytes = 4096;
 static_assert(sizeof(WsHeader) <= kWsHeaderBytes, "header fits its reserved bytes");
+static_assert(offsetof(WsHeader, capacity) == 24 && offsetof(WsHeader, started) == 128, "header layout");
 constexpr uint32_t kErrSpin = 1u, kErrFallback = 4u;  // bit 1 is no longer used
 constexpr uint32_t kModeStatic = 1u, kModeDynamic = 2u;
 
@@ -325,16 +328,17 @@ __device__ __forceinline__ void st(U *p, U v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Start of a call that publishes descriptors (thread 0 only): read the epoch
-// and the high-water mark (one round trip), then count this workgroup with
-// a fire-and-forget atomic whose operand depends on the loaded epoch, so the
-// read has returned before the count is made.  Whoever later sees every
-// workgroup counted knows that none will read the epoch again.  The
-// high-water mark changes only at a call's end, after every workgroup is
-// counted, so the value read here is the one end_call needs.
-__device__ __forceinline__ uint32_t begin_call(WsHeader *hdr, uint64_t &high_water) {
+// Start of a call that publishes descriptors (thread 0 only): read the epoch,
+// the high-water mark and the recorded capacity (one round trip), then count
+// this workgroup with a fire-and-forget atomic whose operand depends on the
+// loaded epoch, so the read has returned before the count is made.  Whoever
+// later sees every workgroup counted knows that none will read the epoch
+// again.  The high-water mark changes only at a call's end, after every
+// workgroup is counted, so the value read here is the one end_call needs.
+__device__ __forceinline__ uint32_t begin_call(WsHeader *hdr, uint64_t &high_water, uint64_t &capacity) {
     const uint32_t e = ld(&hdr->epoch);
     high_water = ld(&hdr->high_water);
+    capacity = ld(&hdr->capacity);
     __hip_atomic_fetch_add(&hdr->started[blockIdx.x & 15].count, 1u + (e >> 30), __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
     return e;
@@ -390,21 +394,27 @@ __device__ __forceinline__ uint32_t decide_mode(WsHeader *hdr, uint32_t epoch, u
 // End of a call, run by one workgroup once every workgroup is known to have
 // read the epoch: reset the per-call words, advance the epoch for the next
 // call on this workspace, and clear the descriptor words above this call's
-// up to the previous high-water mark `hw` (begin_call's, within the
-// workspace): words below `words_used` were all rewritten by this call, so
-// afterwards every word carries this call's tag or none.  In static mode
-// every workgroup was counted before the mode was decided; in dynamic mode
-// the caller holds the last claim.  Whole workgroup (no barrier).
-__device__ __forceinline__ void end_call(WsHeader *hdr, uint32_t epoch, uint64_t hw, uint64_t words_used,
-                                         uint64_t ws_words, uint64_t *desc) {
+// up to the previous high-water mark `hw` (begin_call's): words below
+// `words_used` were all rewritten by this call, so afterwards every word
+// carries this call's tag or none.  The clearing reaches as far as the buffer
+// goes: the call's own `ws_words`, or the capacity scan_workspace_init
+// recorded when the caller passes a smaller size on the same buffer.  Words
+// beyond both (a buffer zeroed by other means, then passed with shrinking
+// sizes) keep the high-water mark up, so the next call that sees them clears
+// them.  In static mode every workgroup was counted before the mode was
+// decided; in dynamic mode the caller holds the last claim.  Whole workgroup
+// (no barrier).
+__device__ __forceinline__ void end_call(WsHeader *hdr, uint32_t epoch, uint64_t hw, uint64_t capacity,
+                                         uint64_t words_used, uint64_t ws_words, uint64_t *desc) {
+    const uint64_t room = ws_words > capacity ? ws_words : capacity;
+    const uint64_t clear_end = hw < room ? hw : room;
     if (threadIdx.x == 0) {
-        st(&hdr->high_water, words_used);
+        st(&hdr->high_water, clear_end < hw ? hw : words_used);
 #pragma unroll
         for (int i = 0; i < 16; i++) st(&hdr->started[i].count, 0u);
         st(&hdr->claim, 0u);
         st(&hdr->epoch, (epoch + 1u) & kEpochMask);
     }
-    const uint64_t clear_end = hw < ws_words ? hw : ws_words;
     for (uint64_t i = words_used + threadIdx.x; i < clear_end; i += blockDim.x) st(desc + i, uint64_t(0));
 }
 

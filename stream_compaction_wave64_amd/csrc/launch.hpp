@@ -149,7 +149,9 @@ using ColLaunch = int (*)(const ColArgs &, hipStream_t);
 ColLaunch find_columns(scan_dtype_t dt, scan_op_t op, int vec);
 
 // -------------------------------------------------------------- utilities
-int launch_fill_u64(void *p, uint64_t words, uint64_t value, hipStream_t s);
+// fill `words` 64-bit words with `value`; word `at` (when in range) gets `at_value`
+int launch_fill_u64(void *p, uint64_t words, uint64_t value, hipStream_t s, uint64_t at = ~uint64_t(0),
+                    uint64_t at_value = 0);
 int launch_fill_i32(int32_t *p, int64_t count, int32_t value, hipStream_t s);
 int launch_copy(const void *in, void *out, size_t bytes, hipStream_t s);
 

@@ -169,10 +169,12 @@ static LbLaunch pick_op(scan_op_t op, int block, int rows, int vec) {
 
 #if SW64_DT == 0
 LbLaunch find_lookback_i32(scan_op_t op, int b, int r, int v) { return pick_op<int32_t>(op, b, r, v); }
-// count-scan-emit's offsets (int32 sums) in the default shape, stored with
-// the default cache policy; other shapes use the scan's launchers
+// count-scan-emit's offsets (int32 sums) in the default and small-array
+// shapes, stored with the default cache policy so that the emit kernel finds
+// them in the caches; other shapes use the scan's launchers
 LbLaunch find_pack_lookback(int b, int r, int v) {
     if (b == 768 && r == 7 && v == 4) return &launch_lookback_impl<int32_t, OpSum, 768, 7, 4, 0>;
+    if (b == 512 && r == 5 && v == 4) return &launch_lookback_impl<int32_t, OpSum, 512, 5, 4, 0>;
     return pick_op<int32_t>(SCAN_OP_SUM, b, r, v);
 }
 #elif SW64_DT == 1

@@ -125,7 +125,7 @@ struct CtrlPipeline {
         C prefix[2];  // exclusive prefix of the tile emitted in this step
         C total;      // setup()'s result
         uint32_t epoch, mode, ticket;
-        uint64_t high_water;  // begin_call's, for end_call
+        uint64_t high_water, capacity;  // begin_call's, for end_call
     };
 
     // Whether a call runs the workspace protocol: every chained scan, and
@@ -244,10 +244,11 @@ struct CtrlPipeline {
         if (ctrl) {
             uint32_t e = 0;
             if (chained && lane_id() == 0) {
-                uint64_t hw = 0;
-                e = begin_call(hdr, hw);
+                uint64_t hw = 0, cap = 0;
+                e = begin_call(hdr, hw, cap);
                 sm.epoch = e;
                 sm.high_water = hw;
+                sm.capacity = cap;
                 sm.mode = decide_mode(hdr, e, G, a.pipe.mode_limit);
             }
             if constexpr (P::kSetup) {
@@ -296,7 +297,7 @@ struct CtrlPipeline {
             __syncthreads();
             const uint32_t tk = sm.ticket;
             if (tk >= n) {
-                if (tk == n + G - 1) end_call(hdr, epoch, sm.high_water, a.pipe.words_used, a.pipe.ws_words, desc);
+                if (tk == n + G - 1) end_call(hdr, epoch, sm.high_water, sm.capacity, a.pipe.words_used, a.pipe.ws_words, desc);
                 break;
             }
             b0.load(a, tk);
@@ -314,7 +315,7 @@ struct CtrlPipeline {
                                                       uint32_t epoch) {
         const uint32_t n = a.pipe.num_tiles, G = gridDim.x;
         if (protocol(a) && blockIdx.x == (n - 1) % G)
-            end_call(hdr, epoch, sm.high_water, a.pipe.words_used, a.pipe.ws_words, desc);
+            end_call(hdr, epoch, sm.high_water, sm.capacity, a.pipe.words_used, a.pipe.ws_words, desc);
     }
 
     // Dynamic mode (control wave): claim a tile, then resolve it.  Every
@@ -330,7 +331,7 @@ struct CtrlPipeline {
             __syncthreads();
             const uint32_t tk = sm.ticket;
             if (tk >= n) {
-                if (tk == n + G - 1) end_call(hdr, epoch, sm.high_water, a.pipe.words_used, a.pipe.ws_words, desc);
+                if (tk == n + G - 1) end_call(hdr, epoch, sm.high_water, sm.capacity, a.pipe.words_used, a.pipe.ws_words, desc);
                 break;
             }
             __syncthreads();

@@ -32,9 +32,12 @@ int resident_blocks(const void *kernel, int waves_per_block) {
     return v;
 }
 
-__global__ __launch_bounds__(256) void k_fill_u64(uint64_t *p, uint64_t words, uint64_t value) {
+// Fill `words` 64-bit words with `value`, except word `at` (if < words),
+// which gets `at_value`.
+__global__ __launch_bounds__(256) void k_fill_u64(uint64_t *p, uint64_t words, uint64_t value, uint64_t at,
+                                                   uint64_t at_value) {
     for (uint64_t i = uint64_t(blockIdx.x) * 256 + threadIdx.x; i < words; i += uint64_t(gridDim.x) * 256)
-        p[i] = value;
+        p[i] = i == at ? at_value : value;
 }
 
 __global__ __launch_bounds__(256) void k_fill_i32(int32_t *p, int64_t count, int32_t value) {
@@ -42,11 +45,11 @@ __global__ __launch_bounds__(256) void k_fill_i32(int32_t *p, int64_t count, int
         p[i] = value;
 }
 
-int launch_fill_u64(void *p, uint64_t words, uint64_t value, hipStream_t s) {
+int launch_fill_u64(void *p, uint64_t words, uint64_t value, hipStream_t s, uint64_t at, uint64_t at_value) {
     if (words == 0) return SCAN_OK;
     const uint64_t blocks = (words + 255) / 256;
     hipLaunchKernelGGL(k_fill_u64, dim3(unsigned(blocks < 4096 ? blocks : 4096)), dim3(256), 0, s,
-                       reinterpret_cast<uint64_t *>(p), words, value);
+                       reinterpret_cast<uint64_t *>(p), words, value, at, at_value);
     return hipGetLastError() == hipSuccess ? SCAN_OK : SCAN_ERR_HIP;
 }
 

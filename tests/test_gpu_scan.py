@@ -55,6 +55,40 @@ def test_parity_default_tiles(dt, op, exclusive):
 
 @pytest.mark.parametrize("dt", DTYPES, ids=lambda d: np.dtype(d).name)
 @pytest.mark.parametrize("op", OPS)
+@pytest.mark.parametrize("exclusive", [False, True], ids=["incl", "excl"])
+def test_parity_whole_array_default_shape(dt, op, exclusive):
+    # the shape large whole arrays get (the planner's choice at 1e7, beyond
+    # the small-array rule), pinned through the tuning so that sizes of a few
+    # tiles run it too
+    p = sw.plan("scan", TORCH[np.dtype(dt)], op, 1, 10 ** 7)
+    tuning = {"block_size": p["block_size"], "items_per_thread": p["items_per_thread"]}
+    tile = p["tile_elems"]
+    assert sw.plan("scan", TORCH[np.dtype(dt)], op, 1, 1000, tuning=tuning)["tile_elems"] == tile
+    for i, n in enumerate([5, tile - 4, tile + 4, 3 * tile + 12, 300 * tile - 4]):
+        x = _input(dt, n, 300 + i, op)
+        assert_scan_matches(x, _run(x, op, exclusive, tuning), op, exclusive, what=f"n={n}")
+
+
+@pytest.mark.parametrize("dt", DTYPES, ids=lambda d: np.dtype(d).name)
+@pytest.mark.parametrize("op", OPS)
+def test_parity_across_small_array_switch(dt, op):
+    # whole arrays of up to 256 small-array tiles take that shape, longer
+    # ones the default: both sides of the switch, planner's choice
+    big = sw.plan("scan", TORCH[np.dtype(dt)], op, 1, 10 ** 7)
+    vec = 16 // np.dtype(dt).itemsize
+    edge = 256 * 448 * 5 * vec  # 256 tiles of 448 data threads x 5 rows
+    below = sw.plan("scan", TORCH[np.dtype(dt)], op, 1, edge)
+    above = sw.plan("scan", TORCH[np.dtype(dt)], op, 1, edge + vec)
+    assert below["tile_elems"] == 448 * 5 * vec and below["num_tiles"] == 256
+    assert above["tile_elems"] == big["tile_elems"] != below["tile_elems"]
+    for i, n in enumerate([edge, edge + vec]):
+        x = _input(dt, n, 400 + i, op)
+        for excl in (False, True):
+            assert_scan_matches(x, _run(x, op, excl), op, excl, what=f"n={n} excl={excl}")
+
+
+@pytest.mark.parametrize("dt", DTYPES, ids=lambda d: np.dtype(d).name)
+@pytest.mark.parametrize("op", OPS)
 def test_parity_many_small_tiles(dt, op):
     # one row per tile: tile = 192 x vec elements (256 threads less the
     # look-back wave), so 1e5 elements make
@@ -227,6 +261,51 @@ def test_shrinking_call_clears_stale_descriptors():
             binding.workspaces._ws.pop(key, None)
         else:
             binding.workspaces._ws[key] = saved
+
+
+def test_shrinking_ws_bytes_on_one_buffer():
+    # A buffer initialised with scan_workspace_init records its size, so calls
+    # that pass only their own plan's ws_bytes on it still clear what a larger
+    # call left tagged beyond their range.  A large call, then 300 small calls
+    # (more than the 256 epochs after which a tag repeats) each passing its
+    # own smaller size, then a large call again: every result exact, no error.
+    import ctypes
+    from stream_compaction_wave64_amd import binding
+    lib = binding.load_library()
+    nbytes = 1 << 22
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    sw.scan_workspace_init(ws)
+    stream = binding._stream(torch.device(DEV))
+    big1 = inputs.generic(np.int32, 2_000_003, 17, "wide")
+    big2 = inputs.generic(np.int32, 2_000_003, 18, "wide")
+    small = inputs.generic(np.int32, 60_000, 19, "wide")
+    p_big = sw.plan("scan", torch.int32, "sum", 1, big1.size)
+    p_small = sw.plan("scan", torch.int32, "sum", 1, small.size)
+    assert p_small["num_tiles"] > 1 and p_big["num_tiles"] > 2 * p_small["num_tiles"]
+    assert p_big["workspace_bytes"] <= nbytes
+
+    def run(x, ws_bytes):
+        xd, out = to_dev(x), torch.empty(x.size, dtype=torch.int32, device=DEV)
+        rc = lib.scan_inclusive(xd.data_ptr(), out.data_ptr(), x.size, 0, 0, 1, ws.data_ptr(), ws_bytes, None,
+                                stream)
+        assert rc == 0, rc
+        return out
+
+    r = run(big1, p_big["workspace_bytes"])
+    torch.cuda.synchronize()
+    assert_scan_matches(big1, to_host(r), "sum", False, what="first large call")
+    xs = to_dev(small)
+    outs = torch.empty(small.size, dtype=torch.int32, device=DEV)
+    for k in range(300):
+        rc = lib.scan_inclusive(xs.data_ptr(), outs.data_ptr(), small.size, 0, 0, 1, ws.data_ptr(),
+                                p_small["workspace_bytes"], None, stream)
+        assert rc == 0, rc
+    torch.cuda.synchronize()
+    assert_scan_matches(small, to_host(outs), "sum", False, what="small calls")
+    r = run(big2, p_big["workspace_bytes"])
+    torch.cuda.synchronize()
+    assert_scan_matches(big2, to_host(r), "sum", False, what="large call after 300 small ones")
+    assert sw.scan_workspace_error(ws) == 0
 
 
 def test_empty_and_degenerate():
