@@ -278,7 +278,9 @@ int pack_offsets(const int32_t *counts, int64_t n, int32_t *offsets, void *ws,
 int pack_emit_neighbors(const int32_t *offsets, int64_t n, int32_t *out, void *stream);
 
 /* Measurement aid: copy `bytes` (multiple of 16, 16-byte aligned pointers)
- * with the same 128-bit access pattern and tile shape as the fp32 scan. */
+ * with the fastest plain copy measured on MI355X (one 128-bit nontemporal
+ * load and store per thread, 4 KiB per workgroup): the attainable read+write
+ * bandwidth that a one-read, one-write scan is compared with. */
 int scan_copy(const void *in, void *out, size_t bytes, void *stream);
 
 /* Static description of a status code. */
