@@ -203,6 +203,25 @@ int scan_inclusive(const void *in, void *out, int64_t n, scan_dtype_t dtype,
                    scan_op_t op, int32_t width, void *ws, size_t ws_bytes,
                    const scan_tuning_t *tuning, void *stream);
 
+/* For callers that cannot allocate (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): scan_inclusive without a
+ * workspace argument.  The call allocates nothing.  Its workspace is a
+ * device array inside the library, SCAN_NOALLOC_SCRATCH_BYTES (1 MiB) on each
+ * GPU, held from that GPU's first call until the process ends.  The first
+ * call on a GPU zeroes the array with one extra fill kernel on `stream`.
+ * A call whose plan (scan_plan) needs a larger workspace returns
+ * SCAN_ERR_WORKSPACE before anything is enqueued: e.g. fp32 sums of up to
+ * about 2.5e9 elements fit, fp64 sums of up to about 4.6e8.  Every call on
+ * one GPU shares that GPU's array, which keeps the last call's contents:
+ * calls that may overlap in time on one GPU (different streams, or several
+ * host threads without ordering) race and give wrong results; order them on
+ * one stream.  A call that reports a timed-out wait (see
+ * scan_workspace_error) leaves the array unusable until the process ends. */
+#define SCAN_NOALLOC_SCRATCH_BYTES (1u << 20)
+int scan_inclusive_noalloc(const void *in, void *out, int64_t n, scan_dtype_t dtype,
+                           scan_op_t op, int32_t width, const scan_tuning_t *tuning,
+                           void *stream);
+
 /* Exclusive scan: out[0] = identity, out[i] = in[0] (+) ... (+) in[i-1]. */
 int scan_exclusive(const void *in, void *out, int64_t n, scan_dtype_t dtype,
                    scan_op_t op, int32_t width, void *ws, size_t ws_bytes,

@@ -9,7 +9,7 @@ GPU stack; any binding call raises if the HIP library is missing.
 """
 
 _BINDING_NAMES = {
-    "scan_inclusive", "scan_exclusive", "scan_dim", "scan_segmented", "compact_if", "partition_if", "pack_offsets",
+    "scan_inclusive", "scan_inclusive_noalloc", "scan_exclusive", "scan_dim", "scan_segmented", "compact_if", "partition_if", "pack_offsets",
     "pack_emit_neighbors", "scan_copy", "scan_workspace_init", "scan_workspace_bytes", "scan_workspace_error",
     "plan", "version", "load_library", "workspaces", "ScanError", "Tuning",
 }

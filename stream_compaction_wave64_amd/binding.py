@@ -48,6 +48,7 @@ class Plan(ctypes.Structure):
 
 
 EXPORTS = ["scan_plan", "scan_workspace_bytes", "scan_workspace_init", "scan_workspace_error", "scan_inclusive",
+           "scan_inclusive_noalloc",
            "scan_exclusive", "scan_dim", "scan_segmented", "compact_if", "partition_if", "pack_offsets", "pack_emit_neighbors",
            "scan_copy", "scan_status_string", "scan_version"]
 
@@ -75,6 +76,7 @@ def load_library(path: str = LIB_PATH):
             "scan_workspace_init": ([vp, sz, vp], i32),
             "scan_workspace_error": ([vp, ctypes.POINTER(ctypes.c_int32), vp], i32),
             "scan_inclusive": ([vp, vp, i64, i32, i32, i32, vp, sz, tp, vp], i32),
+            "scan_inclusive_noalloc": ([vp, vp, i64, i32, i32, i32, tp, vp], i32),
             "scan_exclusive": ([vp, vp, i64, i32, i32, i32, vp, sz, tp, vp], i32),
             "scan_dim": ([vp, vp, i64, i64, i64, i32, i32, i32, vp, sz, tp, vp], i32),
             "compact_if": ([vp, i64, i32, i32, ctypes.c_double, vp, vp, vp, sz, tp, vp], i32),
@@ -199,6 +201,22 @@ def scan_inclusive(x: torch.Tensor, op: str = "sum", out=None, width: int = 1, t
     """out[i] = x[0] (+) ... (+) x[i] over the flattened tensor (structs of
     `width` components scanned component-wise)."""
     return _scan("scan_inclusive", x, op, out, width, tuning)
+
+
+def scan_inclusive_noalloc(x: torch.Tensor, out: torch.Tensor, op: str = "sum", width: int = 1,
+                           tuning=None) -> torch.Tensor:
+    """scan_inclusive on the library's own per-GPU workspace: no allocation,
+    so `out` must be given.  Calls that may overlap on one GPU race."""
+    lib = load_library()
+    _need_cuda(x, out)
+    if out.dtype != x.dtype or out.numel() != x.numel():
+        raise ValueError("out must match x in dtype and size")
+    if width < 1 or x.numel() % width:
+        raise ValueError("width must divide the element count")
+    n = x.numel() // width
+    _check("scan_inclusive_noalloc", lib.scan_inclusive_noalloc(x.data_ptr(), out.data_ptr(), n, _dtype(x), OPS[op],
+                                                                width, _tuning(tuning), _stream(x.device)))
+    return out
 
 
 def scan_exclusive(x: torch.Tensor, op: str = "sum", out=None, width: int = 1, tuning=None) -> torch.Tensor:

@@ -1,8 +1,11 @@
 // api.hip -- the C ABI (include/scan_wave64.h): argument checks, the tile
 // planner and kernel selection.  Everything here runs on the host; every
 // arithmetic step of a scan runs in the kernels.
+#include <stddef.h>
 #include <stdint.h>
 #include <string.h>
+
+#include <mutex>
 
 #include "launch.hpp"
 #include "scan_wave64.h"
@@ -602,6 +605,48 @@ void fill_plan(const TilePlan &p, scan_dtype_t dt, scan_op_t op, scan_plan_t *pl
 }  // namespace
 }  // namespace sw64
 
+namespace sw64 {
+
+// ------------------------------------------------- the no-allocation entry point
+// The workspace of scan_inclusive_noalloc: a device array of the library's own,
+// one copy per GPU (each device holds its own, at its own address, from the
+// first call until the process ends).  Host code never passes `scratch`
+// itself to a kernel or a copy -- on the host that name is only a stand-in --
+// but the device address hipGetSymbolAddress returns for the current device.
+constexpr size_t kStaticScratchBytes = SCAN_NOALLOC_SCRATCH_BYTES;
+static_assert(kStaticScratchBytes % 256 == 0 && kStaticScratchBytes > kWsHeaderBytes, "scratch size");
+static __device__ __align__(256) uint64_t scratch[kStaticScratchBytes / 8];
+
+constexpr int kMaxDevices = 64;
+
+// The current device's scratch address.  On a device's first call: look the
+// address up (with that device current) and zero the array with a fill
+// kernel on `stream`, recording its capacity in the workspace header the way
+// scan_workspace_init does, so the call that follows on the same stream finds
+// a fresh workspace.  A fill kernel, not a memset node: the first call may be
+// under graph capture.
+int noalloc_scratch(hipStream_t stream, void **out) {
+    static std::mutex mu;
+    static void *ptr[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return SCAN_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return SCAN_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(mu);
+    if (ptr[dev] == nullptr) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return SCAN_ERR_HIP;
+        if (reinterpret_cast<uintptr_t>(p) & 255u) return SCAN_ERR_HIP;
+        const uint64_t cap = (kStaticScratchBytes - kWsHeaderBytes) / 8;
+        const int rc = launch_fill_u64(p, kStaticScratchBytes / 8, 0, stream, offsetof(WsHeader, capacity) / 8, cap);
+        if (rc != SCAN_OK) return rc;
+        ptr[dev] = p;
+    }
+    *out = ptr[dev];
+    return SCAN_OK;
+}
+
+}  // namespace sw64
+
 using namespace sw64;
 
 extern "C" {
@@ -699,6 +744,23 @@ int scan_inclusive(const void *in, void *out, int64_t n, scan_dtype_t dtype, sca
     if (width < 1 || n < 0) return SCAN_ERR_INVALID_ARG;
     return scan_common(in, out, 1, n, width, dtype, op, 0, nullptr, ws, ws_bytes, tuning,
                        reinterpret_cast<hipStream_t>(stream));
+}
+
+int scan_inclusive_noalloc(const void *in, void *out, int64_t n, scan_dtype_t dtype, scan_op_t op, int32_t width,
+                           const scan_tuning_t *tuning, void *stream) {
+    if (width < 1 || n < 0 || !valid_dtype(dtype) || !valid_op(op)) return SCAN_ERR_INVALID_ARG;
+    if (n == 0) return SCAN_OK;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    // the plan's workspace must fit the array; larger calls are rejected
+    // before anything is enqueued
+    scan_plan_t p;
+    const int prc = scan_plan(SCAN_CALL_SCAN, dtype, op, 1, n, width, tuning, &p);
+    if (prc != SCAN_OK) return prc;
+    if (size_t(p.workspace_bytes) > kStaticScratchBytes) return SCAN_ERR_WORKSPACE;
+    void *ws = nullptr;
+    const int rc = noalloc_scratch(s, &ws);
+    if (rc != SCAN_OK) return rc;
+    return scan_common(in, out, 1, n, width, dtype, op, 0, nullptr, ws, kStaticScratchBytes, tuning, s);
 }
 
 int scan_exclusive(const void *in, void *out, int64_t n, scan_dtype_t dtype, scan_op_t op, int32_t width,

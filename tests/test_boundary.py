@@ -235,3 +235,15 @@ def test_element_block_rule_matches_oracle():
     assert p["kernel"] == "columns", p
     assert binding.plan("scan", torch.float64, "sum", 1, 10 ** 6, 17)["carry_words"] == 34
     assert binding.plan("scan", torch.float32, "sum", 1, 10 ** 6, 24)["carry_words"] == 48
+
+
+def test_noalloc_rejects_before_any_device_work(lib):
+    # Checked on the host before the library's array is touched: a plan
+    # whose workspace exceeds the array, bad arguments, and the n == 0 no-op.
+    # fp64 sums take two descriptor words per 7168-element tile, so 6e8
+    # elements need more than 1 MiB.  The pointers are never dereferenced.
+    assert lib.scan_inclusive_noalloc(16, 32, 600_000_000, 4, 0, 1, None, None) == -3  # SCAN_ERR_WORKSPACE
+    assert lib.scan_inclusive_noalloc(None, None, 0, 4, 0, 1, None, None) == 0
+    assert lib.scan_inclusive_noalloc(16, 32, 10, 4, 0, 0, None, None) == -1  # width 0
+    assert lib.scan_inclusive_noalloc(16, 32, 10, 9, 0, 1, None, None) == -1  # unknown dtype
+    assert lib.scan_inclusive_noalloc(16, 32, -1, 4, 0, 1, None, None) == -1
