@@ -50,6 +50,11 @@ def _load():
             f = getattr(lib, name)
             f.argtypes = [vp, vp, i64, i64, i64, i32, i32]
             f.restype = i32
+        for name in ("oracle_scan_noid_i32", "oracle_scan_noid_u32", "oracle_scan_noid_i64",
+                     "oracle_scan_noid_f32", "oracle_scan_noid_f64"):
+            f = getattr(lib, name)
+            f.argtypes = [vp, vp, i64, i64, i64, i32]
+            f.restype = i32
         for name in ("oracle_abs_prefix_f32", "oracle_abs_prefix_f64"):
             f = getattr(lib, name)
             f.argtypes = [vp, vp, i64, i64, i64, i32]
@@ -114,6 +119,24 @@ def scan(x: np.ndarray, op: str = "sum", exclusive: bool = False, dims=None) -> 
     y = np.empty(x.size, dtype=out_t)
     if x.size:
         rc = getattr(lib, name)(_ptr(x), _ptr(y), outer, length, inner, OPS[op], int(exclusive))
+        if rc != 0:
+            raise ValueError("oracle scan rejected its arguments")
+    return y.reshape(x.shape)
+
+
+def scan_noid(x: np.ndarray, op: str = "sum", dims=None) -> np.ndarray:
+    """Inclusive scan that never uses the operator's identity: each column
+    starts from its first element (AcceleratedKernels.jl PR #208's Optional
+    partials for operators without a neutral element).  Result types as for
+    scan()."""
+    lib = _load()
+    x = np.ascontiguousarray(x)
+    name, out_t = _SCAN[x.dtype]
+    outer, length, inner = _dims(x, dims)
+    y = np.empty(x.size, dtype=out_t)
+    if x.size:
+        rc = getattr(lib, name.replace("oracle_scan_", "oracle_scan_noid_"))(_ptr(x), _ptr(y), outer, length,
+                                                                              inner, OPS[op])
         if rc != 0:
             raise ValueError("oracle scan rejected its arguments")
     return y.reshape(x.shape)

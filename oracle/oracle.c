@@ -222,6 +222,11 @@ typedef struct { double hi, lo; } dd_t;
 
 static dd_t dd_renorm(double s, double e) {         /* Fast2Sum, |s| >= |e| */
     dd_t r;
+    if (e == 0.0) {          /* exact: s + 0.0 would turn a -0.0 into +0.0 */
+        r.hi = s;
+        r.lo = 0.0;
+        return r;
+    }
     r.hi = s + e;
     r.lo = e - (r.hi - s);
     return r;
@@ -277,6 +282,51 @@ int oracle_scan_f64(const double *x, double *y, int64_t outer, int64_t len,
     }
     return 0;
 }
+
+/* ---------------------------- inclusive scans without a neutral element --
+ * AcceleratedKernels.jl PR #208, description, first bullet: the partial
+ * results may be "Optional" when the operator has no neutral element.  The
+ * inclusive scan needs none: element 0 of each scanned column is x[0] itself
+ * and element i is element i-1 combined with x[i].  These loops start from
+ * the first input and never form an identity, so for sums a -0.0 input keeps
+ * its sign (an identity 0.0 would turn 0.0 + -0.0 into +0.0).  Exclusive
+ * scans have no value at i = 0 without an identity and are not defined. */
+#define NOID_SCAN(NAME, T, ACC_T, LOAD, COMBINE, STORE)                            \
+    int NAME(const T *x, void *yv, int64_t outer, int64_t len, int64_t inner,   \
+             int op) {                                                          \
+        if (op < O_SUM || op > O_MIN) return -1;                                \
+        for (int64_t o = 0; o < outer; o++) {                                   \
+            for (int64_t k = 0; k < inner; k++) {                               \
+                ACC_T acc;                                                      \
+                for (int64_t i = 0; i < len; i++) {                             \
+                    int64_t at = (o * len + i) * inner + k;                     \
+                    if (i == 0) acc = LOAD(x[at]);                              \
+                    else acc = COMBINE(op, acc, x[at]);                         \
+                    STORE(yv, at, acc);                                         \
+                }                                                               \
+            }                                                                   \
+        }                                                                       \
+        return 0;                                                               \
+    }
+
+#define LD_U32(v) ((uint32_t)(v))
+#define LD_U64(v) ((uint64_t)(v))
+#define LD_F64(v) ((double)(v))
+static dd_t dd_from(double v) { dd_t r; r.hi = v; r.lo = 0.0; return r; }
+#define ST_I32(y, at, acc) (((int32_t *)(y))[at] = (int32_t)(acc))
+#define ST_U32(y, at, acc) (((uint32_t *)(y))[at] = (acc))
+#define ST_I64(y, at, acc) (((int64_t *)(y))[at] = (int64_t)(acc))
+#define ST_F64(y, at, acc) (((double *)(y))[at] = (acc))
+#define ST_DD(y, at, acc) (((double *)(y))[at] = (acc).hi)
+#define CB_I32(op, acc, v) i32_combine(op, acc, (uint32_t)(v))
+#define CB_I64(op, acc, v) i64_combine(op, acc, (uint64_t)(v))
+#define CB_F64(op, acc, v) f64_combine(op, acc, (double)(v))
+
+NOID_SCAN(oracle_scan_noid_i32, int32_t, uint32_t, LD_U32, CB_I32, ST_I32)
+NOID_SCAN(oracle_scan_noid_u32, uint32_t, uint32_t, LD_U32, u32_combine, ST_U32)
+NOID_SCAN(oracle_scan_noid_i64, int64_t, uint64_t, LD_U64, CB_I64, ST_I64)
+NOID_SCAN(oracle_scan_noid_f32, float, double, LD_F64, CB_F64, ST_F64)   /* fp64 accumulator */
+NOID_SCAN(oracle_scan_noid_f64, double, dd_t, dd_from, dd_combine, ST_DD) /* double-double */
 
 /* ------------------------------------------- tolerance weight P_i (fp64) --
  * P_i = sum of |x_j| over the elements the i-th output depends on (j <= i

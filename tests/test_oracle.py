@@ -219,6 +219,73 @@ def test_brute_force_small(oracle_lib, dt, op, n):
                 assert abs(g - e) <= rel * n * abs(e) + 1e-300
 
 
+# ------------------------------------- inclusive scans without a neutral element
+# AcceleratedKernels.jl PR #208, description, first bullet: operators with no
+# neutral element keep Optional partials.  The oracle's scan_noid starts each
+# column from its first element and never forms an identity.
+
+
+@pytest.mark.parametrize("dt", ALL_TYPES, ids=lambda d: np.dtype(d).name)
+@pytest.mark.parametrize("op", OPS)
+@pytest.mark.parametrize("n", [1, 2, 3, 17, 64])
+def test_noid_brute_force_small(oracle_lib, dt, op, n):
+    rng = np.random.default_rng(2000 + n)
+    if np.issubdtype(dt, np.integer):
+        info = np.iinfo(dt)
+        x = rng.integers(max(info.min, -2 ** 62), min(info.max, 2 ** 62), n, dtype=np.int64)
+        x = x.astype(dt) if dt != np.uint32 else (x % (1 << 32)).astype(np.uint32)
+    else:
+        x = (rng.integers(-64, 65, n) / 16.0).astype(dt)
+        if op == "prod":
+            x = (1.0 + rng.integers(-8, 9, n) / 1024.0).astype(dt)
+    got = oracle_lib.scan_noid(x, op)
+    exp = _brute(x, op, False, dt)  # inclusive: every term is an input, no identity involved
+    if np.issubdtype(dt, np.integer) or op != "prod":
+        assert list(got) == exp
+    else:
+        rel = 2.0 ** -50 if dt == np.float32 else 2.0 ** -100
+        for g, e in zip(got, exp):
+            assert abs(g - e) <= rel * n * abs(e)
+
+
+@pytest.mark.parametrize("dt", ALL_TYPES, ids=lambda d: np.dtype(d).name)
+@pytest.mark.parametrize("op", OPS)
+def test_noid_equals_identity_scan_inclusive(oracle_lib, dt, op):
+    # with no signed zero in the data, combining the identity first changes
+    # nothing: both scans must agree bit for bit, 1-D and along a middle axis
+    kind = "near1" if op == "prod" and np.issubdtype(dt, np.floating) else "wide"
+    x = inputs.generic(dt, 3 * 257 * 5, 31, kind)
+    if np.issubdtype(dt, np.floating):
+        x[x == 0] = 1
+    a, b = oracle_lib.scan_noid(x, op), oracle_lib.scan(x, op)
+    assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+    d = (3, 257, 5)
+    a, b = oracle_lib.scan_noid(x, op, dims=d), oracle_lib.scan(x, op, dims=d)
+    assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+
+
+@pytest.mark.parametrize("dt", [np.float32, np.float64])
+def test_noid_keeps_negative_zero(oracle_lib, dt):
+    # IEEE addition: -0.0 + -0.0 = -0.0, but 0.0 + -0.0 = +0.0.  A scan of
+    # negative zeros that never uses the identity stays -0.0 everywhere; one
+    # that starts from the identity 0.0 is +0.0 everywhere.
+    z = np.full(100, -0.0, dtype=dt)
+    got = oracle_lib.scan_noid(z, "sum")
+    assert np.all(got == 0) and np.all(np.signbit(got))
+    ident = oracle_lib.scan(z, "sum")
+    assert np.all(ident == 0) and not np.any(np.signbit(ident))
+    x = np.array([-0.0, 1.5, -1.5, 2.0], dtype=dt)
+    got = oracle_lib.scan_noid(x, "sum")
+    assert np.signbit(got[0]) and list(got) == [0.0, 1.5, 0.0, 2.0]
+    # products: -0.0 * 2 = -0.0 and 1 * -0.0 = -0.0, with or without the identity
+    p = np.array([-0.0, 2.0, 3.0], dtype=dt)
+    for r in (oracle_lib.scan_noid(p, "prod"), oracle_lib.scan(p, "prod")):
+        assert np.all(r == 0) and np.all(np.signbit(r))
+    # along the middle axis: each of the 6 columns starts from its own -0.0
+    got = oracle_lib.scan_noid(np.full((2, 50, 3), -0.0, dtype=dt), "sum", dims=(2, 50, 3))
+    assert np.all(np.signbit(got))
+
+
 # ----------------------------------------------------- independent routines
 
 

@@ -40,6 +40,13 @@ MUTANTS = {
         "if (!exclusive) { p[at] = acc; acc += fabs(x[at]); }"),
     "abs prefix f32 drops the absolute value": ("fabs((double)x[at])", "((double)x[at])"),
     "abs prefix f64 drops the absolute value": ("fabs(x[at])", "(x[at])"),
+    "no-identity scan seeded with zero": (
+        "if (i == 0) acc = LOAD(x[at]);                              \\",
+        "if (i == 0) acc = COMBINE(op, LOAD(0), x[at]);              \\"),
+    "no-identity scan drops x[0] from the fold": (
+        "if (i == 0) acc = LOAD(x[at]);", "if (i <= 1) acc = LOAD(x[at]);"),
+    "double-double turns -0.0 into +0.0": (
+        "    if (e == 0.0) {          /* exact: s + 0.0 would turn a -0.0 into +0.0 */", "    if (0) {"),
     "compaction off by one": ("idx[count++] = (int32_t)i;", "idx[count++] = (int32_t)(i + 1);"),
     "compaction > taken as >=": ("case O_GT: return v > t;", "case O_GT: return v >= t;"),
     "partition rejected part not offset by k": (
@@ -78,6 +85,9 @@ PINS = [
                for dt, q in ((np.float32, 23), (np.float64, 30)) for e in (False, True)],
     lambda o: [T.test_abs_prefix_signed_dims(o, dt, q, e)
                for dt, q in ((np.float32, 23), (np.float64, 30)) for e in (False, True)],
+    lambda o: [T.test_noid_brute_force_small(o, dt, op, n) for dt in T.ALL_TYPES for op in T.OPS for n in (3, 17)],
+    lambda o: [T.test_noid_equals_identity_scan_inclusive(o, dt, op) for dt in T.ALL_TYPES for op in T.OPS],
+    lambda o: [T.test_noid_keeps_negative_zero(o, dt) for dt in (np.float32, np.float64)],
     lambda o: T.test_fp64_exact_integer_shadow(o),
     lambda o: [T.test_dims_layouts_agree(o, dt) for dt in (np.int32, np.float32)],
     lambda o: T.test_compaction_brute_and_numpy(o),
