@@ -12,15 +12,20 @@ over the measured average launch duration, against 8 TB/s HBM), the copy
 ceiling measured the same way, and the CPU oracle timed on this host.
 
 Beside the headline figure, "rows" times every other workload of the path
-once each: int32 2^20 inclusive and exclusive, fp64 1e7, the reduce-then-scan
+once each: int32 2^20 inclusive and exclusive, fp64 1e7, fp32 1e7 with and
+without the operator's identity (the pages' "no neutral" row), the reduce-then-scan
 comparison on the fp32 1e8 array, the four 2-D scans (4096 x 4096 along rows
 and along columns, 1e6 x 8 along its long axis, 2 x 1e7 along rows),
-compaction of 1e7 fp32 with x > 0.5, count-scan-emit packing of 1e7 Poisson(3)
-counts, and the 136-byte and 96-byte struct scans of 1e6 elements.  Each row
+compaction of 1e7 fp32 with x > 0.5, its stable partition, count-scan-emit
+packing of 1e7 Poisson(3) counts, the segmented scan over those segments, and
+the 136-byte and 96-byte struct scans of 1e6 elements.  Each row
 rotates over enough copies of its buffers (> 512 MB in all) that no call
 finds its data in the 256 MB Infinity Cache, replays the calls from a HIP
 graph (so small launches are not timed against the Python host), and reports
-the algorithmic bytes of one call over its average duration.
+the algorithmic bytes of one call over its average duration.  Each row is
+also timed the way AcceleratedKernels.jl PR #208 times its table (timing
+paragraph): the device time of one call, best of 20, as the median (and
+range) of 3 runs interleaved across the rows.
 """
 from __future__ import annotations
 
@@ -98,7 +103,19 @@ def cpu_baseline(x: np.ndarray):
         runs += 1
     return {"value": round(x.size / best / 1e9, 4), "unit": "GElem/s", "cores": 1, "kind": "oracle",
             "sample": f"full {x.size:.0e}-element fp32 array, sequential fp64 accumulation, best of {runs} runs",
-            "host_cpus": os.cpu_count()}, ref
+            "host_cpus": os.cpu_count(), "cpu_model": _cpu_model()}, ref
+
+
+def _cpu_model():
+    """The host CPU's model name from /proc/cpuinfo."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 # ------------------------------------------------------------------ rows
@@ -125,10 +142,10 @@ def _rows(dev, lib, binding, inputs):
         p = binding.plan(call, dtype, op, outer, length, inner, tuning)
         return torch.zeros(max(int(p["workspace_bytes"]), 1 << 16), dtype=torch.uint8, device=dev)
 
-    def scan_row(name, workload, host, width=1, excl=False, algo=None, elems=None):
+    def scan_row(name, workload, host, width=1, excl=False, algo=None, elems=None, tuning=None):
         x0 = torch.from_numpy(host).to(dev)
         n = x0.numel() // width
-        tun = {"algo": algo} if algo else None
+        tun = dict(tuning or {}, **({"algo": algo} if algo else {})) or None
         ws = ws_for("scan", x0.dtype, "sum", 1, n, width, tun)
         fn = lib.scan_exclusive if excl else lib.scan_inclusive
         t = binding._tuning(tun)
@@ -164,6 +181,11 @@ def _rows(dev, lib, binding, inputs):
              inputs.int32_uniform_0_100(2 ** 20, 0), excl=True)
     scan_row("fp64_incl_1e7", "fp64 inclusive sum scan, n=1e7, uniform [-1,1), seed 1",
              inputs.f64_uniform_pm1(10 ** 7, 1))
+    f7 = inputs.f32_uniform_01(10 ** 7, 1)
+    scan_row("fp32_incl_1e7", "fp32 inclusive sum scan, n=1e7, uniform [0,1), seed 1", f7)
+    scan_row("fp32_incl_1e7_no_neutral", "fp32 inclusive sum scan, n=1e7, uniform [0,1), seed 1, computed "
+             "without the operator's identity (Optional partials)", f7, tuning={"no_identity": 1})
+    del f7
     scan_row("fp32_incl_1e8_reduce_then_scan", "fp32 inclusive sum scan, n=1e8, reduce-then-scan (3 launches)",
              inputs.f32_uniform_01(N, 1), algo="reduce_then_scan")
     sq, tall, wide = inputs.dims_arrays(3)
@@ -252,14 +274,35 @@ def _rows(dev, lib, binding, inputs):
     return rows
 
 
-def time_row(row, lib, steps, warmup, use_graph=True):
-    """Average duration of one call of the row, cycling through its buffer sets."""
-    import torch
+def prepare_row(row):
+    """The row's calls and outputs, one per buffer set."""
     calls, outs = [], []
     for k in range(row.sets):
         c, o = row.make(k)
         calls.append(c)
         outs.append(o)
+    return calls, outs
+
+
+def best_single_call_us(row, calls, lib, count=20):
+    """Best device time of `count` single calls (HIP events around each call
+    on its stream), cycling through the buffer sets."""
+    import torch
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(count)]
+    for i in range(count):
+        ev[i][0].record(stream)
+        st = calls[i % len(calls)](stream.cuda_stream)
+        ev[i][1].record(stream)
+        if st != 0:
+            raise RuntimeError(f"{row.name}: {lib.scan_status_string(st).decode()} (status {st})")
+    torch.cuda.synchronize()
+    return min(a.elapsed_time(b) * 1e3 for a, b in ev)
+
+
+def time_row(row, calls, outs, lib, steps, warmup, use_graph=True):
+    """Average duration of one call of the row, cycling through its buffer sets."""
+    import torch
     stream = torch.cuda.current_stream()
 
     def run_all(s):
@@ -378,9 +421,24 @@ def main():
         from stream_compaction_wave64_amd import binding
         lib = binding.load_library()
         rows = {}
+        prepared = []
         for row in _rows(dev, lib, binding, inputs):
-            rows[row.name] = time_row(row, lib, args.row_steps, 2)
-            torch.cuda.empty_cache()
+            calls, outs = prepare_row(row)
+            rows[row.name] = time_row(row, calls, outs, lib, args.row_steps, 2)
+            prepared.append((row, calls))
+        # AcceleratedKernels.jl PR #208's method: best of 20 single calls,
+        # median of 3 runs interleaved across the rows
+        best = {row.name: [] for row, _ in prepared}
+        for _ in range(3):
+            for row, calls in prepared:
+                best[row.name].append(best_single_call_us(row, calls, lib))
+        for row, _ in prepared:
+            b = sorted(best[row.name])
+            rows[row.name]["best_of_20_us"] = round(b[1], 3)
+            rows[row.name]["best_of_20_range_us"] = [round(b[0], 3), round(b[2], 3)]
+            rows[row.name]["best_of_20_frac"] = round(row.alg_bytes / (b[1] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+        del prepared
+        torch.cuda.empty_cache()
         result["rows"] = rows
 
     ref = None

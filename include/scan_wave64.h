@@ -135,6 +135,23 @@ typedef struct {
     int32_t mode_limit;        /* polls a call waits for all of its workgroups
                                   to start before it claims tiles dynamically
                                   instead (default 512); tests force tiny values */
+    int32_t no_identity;       /* nonzero: compute without the operator's
+                                  identity, as for an operator that has none
+                                  (AcceleratedKernels.jl PR #208, description,
+                                  first bullet: "Optional" partials): partial
+                                  results carry a presence flag instead, so
+                                  e.g. a sum of -0.0 values stays -0.0.
+                                  Inclusive scans of whole arrays and of rows
+                                  (scan_inclusive, scan_dim with inner == 1,
+                                  look-back algorithm); anything else returns
+                                  SCAN_ERR_UNSUPPORTED, exclusive scans
+                                  included (no value for element 0) */
+    int32_t delay_stride;      /* test aid for the look-back's waits: with
+                                  delay_stride > 0, every tile t with
+                                  t % delay_stride == delay_stride - 1 waits
+                                  delay_sleeps periods of about 1.7 us before
+                                  publishing its aggregate (0: off) */
+    int32_t delay_sleeps;
 } scan_tuning_t;
 
 /* Kernel family a call runs (reported by scan_plan). */

@@ -36,7 +36,9 @@ class Tuning(ctypes.Structure):
     _fields_ = [("block_size", ctypes.c_int32), ("items_per_thread", ctypes.c_int32),
                 ("local_mem_bytes", ctypes.c_int64), ("algo", ctypes.c_int32),
                 ("rts_blocks", ctypes.c_int32), ("spin_limit", ctypes.c_int32),
-                ("grid_blocks", ctypes.c_int32), ("mode_limit", ctypes.c_int32)]
+                ("grid_blocks", ctypes.c_int32), ("mode_limit", ctypes.c_int32),
+                ("no_identity", ctypes.c_int32), ("delay_stride", ctypes.c_int32),
+                ("delay_sleeps", ctypes.c_int32)]
 
 
 class Plan(ctypes.Structure):

@@ -19,6 +19,7 @@ namespace sw64 {
     ret name##_f32(scan_op_t, int, int, int);       \
     ret name##_f64(scan_op_t, int, int, int);
 SW64_DECLARE_PER_TYPE(find_lookback, LbLaunch)
+SW64_DECLARE_PER_TYPE(find_noid, LbLaunch)
 SW64_DECLARE_PER_TYPE(find_rts, RtsLaunch)
 SW64_DECLARE_PER_TYPE(find_seg, SegLaunch)
 SW64_DECLARE_PER_TYPE(find_seg_pipe, SegLaunch)
@@ -85,6 +86,18 @@ LbLaunch find_lookback(scan_dtype_t dt, scan_op_t op, int block, int rows, int v
     case SCAN_I64: return find_lookback_i64(op, block, rows, vec);
     case SCAN_F32: return find_lookback_f32(op, block, rows, vec);
     case SCAN_F64: return find_lookback_f64(op, block, rows, vec);
+    }
+    return nullptr;
+}
+
+// the look-back scan that never uses the operator's identity (noid.hip)
+LbLaunch find_noid(scan_dtype_t dt, scan_op_t op, int block, int rows, int vec) {
+    switch (dt) {
+    case SCAN_I32: return find_noid_i32(op, block, rows, vec);
+    case SCAN_U32: return find_noid_u32(op, block, rows, vec);
+    case SCAN_I64: return find_noid_i64(op, block, rows, vec);
+    case SCAN_F32: return find_noid_f32(op, block, rows, vec);
+    case SCAN_F64: return find_noid_f64(op, block, rows, vec);
     }
     return nullptr;
 }
@@ -221,7 +234,12 @@ int plan_scan(scan_dtype_t dt, scan_op_t op, int64_t outer, int64_t len, bool al
     const int esize = dtype_bytes(dt);
     const bool rts = tu.algo == SCAN_ALGO_REDUCE_THEN_SCAN;
     if (rts && outer != 1) return SCAN_ERR_UNSUPPORTED;  // reduce-then-scan: whole arrays only
+    if (rts && tu.no_identity) return SCAN_ERR_UNSUPPORTED;  // without an identity: the look-back only
     const bool vec_ok = aligned && len % (16 / esize) == 0;
+    // the look-back kernels of this call: with or without the identity
+    auto find_lb = [&](int b, int r, int v) {
+        return tu.no_identity ? find_noid(dt, op, b, r, v) : find_lookback(dt, op, b, r, v);
+    };
     // default shapes: reduce-then-scan 512 threads x 8 rows (4 for 8-byte
     // elements); look-back 768 x 7 (512 x 8 for 8-byte elements), its tiles
     // bounded by the two LDS stashes of the pipeline
@@ -231,7 +249,7 @@ int plan_scan(scan_dtype_t dt, scan_op_t op, int64_t outer, int64_t len, bool al
                        esize == 8 ? 4 : 8, kDefaultBlock)
                  : plan_shape(
                        esize, vec_ok, tu, p,
-                       [&](int b, int r, int v) { return find_lookback(dt, op, b, r, v) != nullptr; }, true,
+                       [&](int b, int r, int v) { return find_lb(b, r, v) != nullptr; }, true,
                        esize == 8 ? 8 : 7, esize == 8 ? kDefaultBlock : 768);
     if (rc != SCAN_OK) return rc;
     const bool shape_free = !rts && tu.block_size <= 0 && tu.items_per_thread <= 0;
@@ -241,7 +259,7 @@ int plan_scan(scan_dtype_t dt, scan_op_t op, int64_t outer, int64_t len, bool al
         // little of it idle.
         for (int r : {1, 2, 3, 5}) {
             const int64_t t = int64_t(kDefaultBlock - 64) * r * p.vec;
-            if (t < p.tile && t >= len && find_lookback(dt, op, kDefaultBlock, r, p.vec) != nullptr) {
+            if (t < p.tile && t >= len && find_lb(kDefaultBlock, r, p.vec) != nullptr) {
                 p.block = kDefaultBlock;
                 p.rows = r;
                 p.tile = t;
@@ -254,7 +272,7 @@ int plan_scan(scan_dtype_t dt, scan_op_t op, int64_t outer, int64_t len, bool al
         // shorter tile: int32 2^20 took 8.9 us against 11.2, fp64 2^20 12.1
         // against 12.8); past that the default's longer tiles win.
         const int64_t t = int64_t(kDefaultBlock - 64) * 5 * p.vec;
-        if ((len + t - 1) / t <= kSmallArrayTiles && find_lookback(dt, op, kDefaultBlock, 5, p.vec) != nullptr) {
+        if ((len + t - 1) / t <= kSmallArrayTiles && find_lb(kDefaultBlock, 5, p.vec) != nullptr) {
             p.block = kDefaultBlock;
             p.rows = 5;
             p.tile = t;
@@ -492,6 +510,8 @@ PipeArgs pipe_args(const TilePlan &p, void *ws, size_t ws_bytes, const scan_tuni
     a.tiles_per_seg = uint32_t(p.tiles_per_seg);
     a.spin_limit = tu.spin_limit > 0 ? uint32_t(tu.spin_limit) : kDefaultSpinLimit;
     a.mode_limit = tu.mode_limit > 0 ? uint32_t(tu.mode_limit) : kDefaultModeLimit;
+    a.delay_stride = tu.delay_stride > 0 ? uint32_t(tu.delay_stride) : 0u;
+    a.delay_sleeps = tu.delay_sleeps > 0 ? uint32_t(tu.delay_sleeps) : 0u;
     return a;
 }
 
@@ -504,6 +524,8 @@ int scan_common(const void *in, void *out, int64_t outer, int64_t len, int64_t i
     if (in == nullptr || out == nullptr) return SCAN_ERR_INVALID_ARG;
     const scan_tuning_t tu = tuning_or_default(tuning);
     if (tu.algo < SCAN_ALGO_AUTO || tu.algo > SCAN_ALGO_REDUCE_THEN_SCAN) return SCAN_ERR_INVALID_ARG;
+    // without an identity: inclusive look-back scans of scalar elements only
+    if (tu.no_identity && (exclusive || inner != 1 || total_out != nullptr)) return SCAN_ERR_UNSUPPORTED;
     if (inner != 1) {
         if (total_out != nullptr) return SCAN_ERR_UNSUPPORTED;
         TilePlan p;
@@ -571,6 +593,7 @@ int scan_common(const void *in, void *out, int64_t outer, int64_t len, int64_t i
     const uint32_t grid_cap = tu.grid_blocks > 0 ? uint32_t(tu.grid_blocks) : 0u;
     if (total_out != nullptr && dt == SCAN_I32 && op == SCAN_OP_SUM)  // count-scan-emit's offsets
         return find_pack_lookback(p.block, p.rows, p.vec)(a, grid_cap, stream);
+    if (tu.no_identity) return find_noid(dt, op, p.block, p.rows, p.vec)(a, grid_cap, stream);
     return find_lookback(dt, op, p.block, p.rows, p.vec)(a, grid_cap, stream);
 }
 
@@ -658,6 +681,7 @@ int scan_plan(scan_call_t call, scan_dtype_t dtype, scan_op_t op, int64_t outer,
     if (!valid_dtype(dtype) || !valid_op(op)) return SCAN_ERR_INVALID_ARG;
     if (outer < 0 || len < 0 || inner < 1) return SCAN_ERR_INVALID_ARG;
     const scan_tuning_t tu = tuning_or_default(tuning);
+    if (tu.no_identity && (call != SCAN_CALL_SCAN || inner != 1)) return SCAN_ERR_UNSUPPORTED;
     TilePlan p;
     int rc;
     switch (call) {
@@ -787,6 +811,7 @@ int compact_if(const void *x, int64_t n, scan_dtype_t x_dtype, scan_cmp_t cmp, d
     if (n == 0) return launch_fill_i32(d_count, 1, 0, s);
     if (x == nullptr || out_idx == nullptr) return SCAN_ERR_INVALID_ARG;
     const scan_tuning_t tu = tuning_or_default(tuning);
+    if (tu.no_identity) return SCAN_ERR_UNSUPPORTED;  // inclusive scans only
     TilePlan p;
     int rc = plan_compact(x_dtype, n, aligned16(x, x), tu, p);
     if (rc != SCAN_OK) return rc;
@@ -815,6 +840,7 @@ int partition_if(const void *x, int64_t n, scan_dtype_t x_dtype, scan_cmp_t cmp,
     if (n == 0) return launch_fill_i32(d_count, 1, 0, s);
     if (x == nullptr || out_vals == nullptr) return SCAN_ERR_INVALID_ARG;
     const scan_tuning_t tu = tuning_or_default(tuning);
+    if (tu.no_identity) return SCAN_ERR_UNSUPPORTED;  // inclusive scans only
     TilePlan p;
     int64_t count_wgs = 0, count_chunk = 0;
     int rc = plan_partition(x_dtype, cmp, n, aligned16(x, x), tu, p, count_wgs, count_chunk);
@@ -845,6 +871,7 @@ int scan_segmented(const void *in, void *out, int64_t n, const int32_t *offsets,
     if (n == 0) return SCAN_OK;
     if (nseg == 0 || in == nullptr || out == nullptr || offsets == nullptr) return SCAN_ERR_INVALID_ARG;
     const scan_tuning_t tu = tuning_or_default(tuning);
+    if (tu.no_identity) return SCAN_ERR_UNSUPPORTED;  // inclusive scans only
     TilePlan p;
     int rc = plan_segmented(dtype, op, n, aligned16(in, out), tu, p);
     if (rc != SCAN_OK) return rc;
@@ -888,6 +915,7 @@ int pack_offsets(const int32_t *counts, int64_t n, int32_t *offsets, void *ws, s
     if (n == 0) return launch_fill_i32(offsets, 1, 0, s);
     if (counts == nullptr) return SCAN_ERR_INVALID_ARG;
     scan_tuning_t tu = tuning_or_default(tuning);
+    if (tu.no_identity) return SCAN_ERR_UNSUPPORTED;  // offsets are an exclusive scan
     tu.algo = SCAN_ALGO_LOOKBACK;  // the total comes from the look-back's last tile
     return scan_common(counts, offsets, 1, n, 1, SCAN_I32, SCAN_OP_SUM, 1, offsets + n, ws, ws_bytes, &tu, s);
 }

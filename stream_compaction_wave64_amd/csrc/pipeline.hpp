@@ -34,6 +34,8 @@ struct PipeArgs {
     uint32_t tiles_per_seg;   // tiles per segment (>= 1)
     uint32_t spin_limit;      // polls of one look-back window before giving up
     uint32_t mode_limit;      // polls before a call falls back to dynamic claiming
+    uint32_t delay_stride;    // test aid: tiles t with t % stride == stride - 1 publish late (0: off)
+    uint32_t delay_sleeps;    // periods of s_sleep(64) those tiles wait before publishing
 };
 
 // The pipeline with a control wave and deferred emission, for policies whose
@@ -141,6 +143,10 @@ struct CtrlPipeline {
     __device__ __forceinline__ static C ctrl_publish(const Args &a, uint32_t tile, const Smem &sm, uint64_t *desc,
                                                      uint32_t epoch) {
         const C agg = P::aggregate(sm.ps);
+        if (a.pipe.delay_stride > 0 && tile % a.pipe.delay_stride == a.pipe.delay_stride - 1) {
+            // a late publisher, so tests reach the look-back's re-polls
+            for (uint32_t i = 0; i < a.pipe.delay_sleeps; i++) __builtin_amdgcn_s_sleep(64);
+        }
         if (a.pipe.tiles_per_seg > 1 && lane_id() == 0) {
             const uint32_t state = (tile % a.pipe.tiles_per_seg == 0) ? kStateP : kStateA;
             P::D::publish(desc_of(desc, tile), epoch, state, agg);

@@ -38,9 +38,14 @@ def to_host(t: torch.Tensor) -> np.ndarray:
     return t.cpu().numpy()
 
 
-def assert_scan_matches(x: np.ndarray, got: np.ndarray, op: str, exclusive: bool, dims=None, what=""):
-    """Compare a device result with the oracle under the rules above."""
-    ref = oracle.scan(x, op, exclusive=exclusive, dims=dims)
+def assert_scan_matches(x: np.ndarray, got: np.ndarray, op: str, exclusive: bool, dims=None, what="", noid=False):
+    """Compare a device result with the oracle under the rules above (noid:
+    against the oracle's inclusive scan that never uses the identity)."""
+    if noid:
+        assert not exclusive
+        ref = oracle.scan_noid(x, op, dims=dims)
+    else:
+        ref = oracle.scan(x, op, exclusive=exclusive, dims=dims)
     got = np.asarray(got).reshape(ref.shape)
     if np.issubdtype(x.dtype, np.integer) or op in ("max", "min"):
         if np.issubdtype(x.dtype, np.floating):

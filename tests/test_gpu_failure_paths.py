@@ -84,3 +84,56 @@ def test_errors_never_set_in_normal_operation():
     torch.cuda.synchronize()
     for ws in binding.workspaces._ws.values():
         assert sw.scan_workspace_error(ws) == 0
+
+
+# Late publishers: tiles picked by a stride wait (s_sleep periods of about
+# 1.7 us) before publishing their aggregate, so the look-back reaches its
+# re-polls deterministically: the gap read of the static order re-reads the
+# slots still unpublished, the windowed look-back of large grids and of
+# dynamic claiming spins on a window with no P (The CUDA Handbook ch. 13,
+# decoupled look-back section, Figure 13-11).  Results must stay exact and
+# no wait may give up (default spin limit).
+DELAYS = [(7, 1), (3, 8), (1, 2), (64, 30)]
+
+
+@pytest.mark.parametrize("stride,sleeps", DELAYS)
+def test_late_publishers_gap_read_and_windowed(stride, sleeps):
+    delay = {"delay_stride": stride, "delay_sleeps": sleeps}
+    ws = torch.zeros(1 << 22, dtype=torch.uint8, device=DEV)
+    cases = [
+        (np.float32, 30_000_001, {}),                                            # gap read, 256 workgroups
+        (np.int32, 1_000_003, {"block_size": 256, "items_per_thread": 4}),       # windowed: > 513 workgroups
+        (np.int64, 500_001, {"block_size": 256, "items_per_thread": 2, "grid_blocks": 5}),
+        (np.float64, 2_000_003, {}),
+    ]
+    with _Installed(ws):
+        for dt, n, tuning in cases:
+            x = inputs.generic(dt, n, 40 + stride, "wide" if np.issubdtype(dt, np.integer) else "default")
+            xd = to_dev(x)
+            for excl in (False, True):
+                fn = sw.scan_exclusive if excl else sw.scan_inclusive
+                r = fn(xd, tuning=dict(tuning, **delay))
+                torch.cuda.synchronize()
+                assert_scan_matches(x, to_host(r), "sum", excl, what=f"{np.dtype(dt).name} {tuning} {delay}")
+            assert sw.scan_workspace_error(ws) == 0, (tuning, delay)
+
+
+@pytest.mark.parametrize("stride,sleeps", DELAYS[:2])
+def test_late_publishers_dynamic_claiming_and_no_identity(stride, sleeps):
+    delay = {"delay_stride": stride, "delay_sleeps": sleeps}
+    x = inputs.generic(np.int32, 1_000_003, 50 + stride, "wide")
+    xd = to_dev(x)
+    ws = torch.zeros(1 << 22, dtype=torch.uint8, device=DEV)
+    with _Installed(ws):
+        ws[128:132].view(torch.int32)[0] = -1  # never confirms residency: dynamic claiming
+        r = sw.scan_inclusive(xd, tuning=dict(delay, mode_limit=8, block_size=256, items_per_thread=4))
+        torch.cuda.synchronize()
+        assert sw.scan_workspace_error(ws) == 4
+        assert_scan_matches(x, to_host(r), "sum", False, what="dynamic")
+        sw.scan_workspace_init(ws)
+        f = inputs.generic(np.float32, 3_000_001, 60 + stride)
+        for tuning in ({}, {"block_size": 256, "items_per_thread": 4}):
+            r = sw.scan_inclusive(to_dev(f), tuning=dict(tuning, no_identity=1, **delay))
+            torch.cuda.synchronize()
+            assert_scan_matches(f, to_host(r), "sum", False, what=f"no identity {tuning}", noid=True)
+        assert sw.scan_workspace_error(ws) == 0
