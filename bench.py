@@ -70,6 +70,7 @@ def parse():
     ap.add_argument("--no-verify", action="store_true")
     ap.add_argument("--no-rows", action="store_true", help="time only the headline fp32 1e8 scan")
     ap.add_argument("--row-steps", type=int, default=20, help="calls timed per row")
+    ap.add_argument("--rows", default="", help="comma-separated row names to time (default: every row)")
     return ap.parse_args()
 
 
@@ -422,7 +423,10 @@ def main():
         lib = binding.load_library()
         rows = {}
         prepared = []
+        wanted = set(filter(None, args.rows.split(",")))
         for row in _rows(dev, lib, binding, inputs):
+            if wanted and row.name not in wanted:
+                continue
             calls, outs = prepare_row(row)
             rows[row.name] = time_row(row, calls, outs, lib, args.row_steps, 2)
             prepared.append((row, calls))
