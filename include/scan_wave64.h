@@ -164,7 +164,9 @@ typedef enum {
     SCAN_KERNEL_COMPACT = 5,    /* fused predicate + scan + scatter */
     SCAN_KERNEL_PACK = 6,       /* exclusive int32 scan + total */
     SCAN_KERNEL_PARTITION = 7,  /* count pass, then fused predicate + scan + two-sided scatter */
-    SCAN_KERNEL_SEGMENTED = 8   /* ragged segments: tile map, then reduce-then-scan of (head, value) pairs */
+    SCAN_KERNEL_SEGMENTED = 8,  /* ragged segments: tile map, then reduce-then-scan of (head, value) pairs */
+    SCAN_KERNEL_COLUMNS_LOOKBACK = 9  /* wide inner extent in one pass: register tiles of 256 rows, each adding
+                                         the column aggregates of the tiles above it */
 } scan_kernel_t;
 
 typedef struct {

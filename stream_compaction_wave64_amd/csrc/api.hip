@@ -57,6 +57,23 @@ ColLaunch find_columns_i64(scan_op_t, int);
 ColLaunch find_columns_f32(scan_op_t, int);
 ColLaunch find_columns_f64(scan_op_t, int);
 
+ColSingleLaunch find_columns_single_i32(scan_op_t);
+ColSingleLaunch find_columns_single_u32(scan_op_t);
+ColSingleLaunch find_columns_single_i64(scan_op_t);
+ColSingleLaunch find_columns_single_f32(scan_op_t);
+ColSingleLaunch find_columns_single_f64(scan_op_t);
+
+ColSingleLaunch find_columns_single(scan_dtype_t dt, scan_op_t op) {
+    switch (dt) {
+    case SCAN_I32: return find_columns_single_i32(op);
+    case SCAN_U32: return find_columns_single_u32(op);
+    case SCAN_I64: return find_columns_single_i64(op);
+    case SCAN_F32: return find_columns_single_f32(op);
+    case SCAN_F64: return find_columns_single_f64(op);
+    }
+    return nullptr;
+}
+
 ColLaunch find_columns(scan_dtype_t dt, scan_op_t op, int vec) {
     switch (dt) {
     case SCAN_I32: return find_columns_i32(op, vec);
@@ -341,14 +358,41 @@ int plan_element(scan_dtype_t dt, scan_op_t op, int64_t outer, int64_t len, int6
     return SCAN_OK;
 }
 
-// Wide inner extents: reduce-then-scan over row chunks.  About 2048
-// workgroups over (outer, chunk, strip), at least 16 rows per chunk (so the
-// partials stay within 0.5 byte per value) and at most 1024 chunks (one
-// workgroup scans a column's partials).
+// Wide inner extents.  In one pass (k_col_single) when the rows allow
+// 128-bit accesses, the strips are at least half full, the array makes at
+// most kColSingleMaxTiles register tiles (one per compute unit) of at most
+// kColSingleMaxRowBlocks per strip, and reduce-then-scan is not asked for.
+// Otherwise reduce-then-scan over row chunks: about 512 workgroups over
+// (outer, chunk, strip), at least 16 rows per chunk (so the partials stay
+// within 0.5 byte per value) and at most 256 chunks (the partials kernel's
+// LDS block).
 int plan_columns(scan_dtype_t dt, scan_op_t op, int64_t outer, int64_t len, int64_t inner, bool aligned,
-                 TilePlan &p) {
+                 const scan_tuning_t &tu, TilePlan &p) {
     const int esize = dtype_bytes(dt);
     const int vmax = 16 / esize;
+    const int64_t tc = int64_t(kWave) * vmax;  // columns per strip of the single pass
+    if (tu.algo != SCAN_ALGO_REDUCE_THEN_SCAN && aligned && inner % vmax == 0 && 2 * inner >= tc &&
+        find_columns_single(dt, op) != nullptr) {
+        const int64_t strips = (inner + tc - 1) / tc, rblocks = (len + kColTileRows - 1) / kColTileRows;
+        if (outer * strips * rblocks <= kColSingleMaxTiles && rblocks <= kColSingleMaxRowBlocks) {
+            p.kernel = SCAN_KERNEL_COLUMNS_LOOKBACK;
+            p.block = kColTileWaves * kWave;
+            p.rows = kColTileRowsPerThread;
+            p.vec = vmax;
+            p.width = 1;
+            p.col_strips = strips;
+            p.col_chunks = rblocks;
+            p.col_rows = kColTileRows;
+            p.num_tiles = outer * strips * rblocks;
+            p.tiles_per_seg = rblocks;
+            p.tile = kColTileRows * tc;
+            p.carry_words = desc_words(dt, op);  // per column
+            p.rts_blocks = p.rts_chunk = 0;
+            p.ws_bytes = kHeader + round_up(size_t(p.num_tiles * tc) * p.carry_words * 8, 256);
+            p.launches = 1;
+            return SCAN_OK;
+        }
+    }
     p.kernel = SCAN_KERNEL_COLUMNS;
     p.vec = (aligned && inner % vmax == 0) ? vmax : 1;
     if (!find_columns(dt, op, p.vec)) return SCAN_ERR_UNSUPPORTED;
@@ -531,10 +575,24 @@ int scan_common(const void *in, void *out, int64_t outer, int64_t len, int64_t i
         TilePlan p;
         int rc = plan_element(dt, op, outer, len, inner, aligned16(in, out), tu, p);
         if (rc == SCAN_ERR_UNSUPPORTED) {
-            rc = plan_columns(dt, op, outer, len, inner, aligned16(in, out), p);
+            rc = plan_columns(dt, op, outer, len, inner, aligned16(in, out), tu, p);
             if (rc != SCAN_OK) return rc;
             rc = check_ws(ws, ws_bytes, p.ws_bytes);
             if (rc != SCAN_OK) return rc;
+            if (p.kernel == SCAN_KERNEL_COLUMNS_LOOKBACK) {
+                ColSingleArgs c{};
+                c.pipe = pipe_args(p, ws, ws_bytes, tu);
+                c.pipe.words_used = uint64_t(p.num_tiles) * (int64_t(kWave) * p.vec) * p.carry_words;
+                c.in = in;
+                c.out = out;
+                c.outer = uint32_t(outer);
+                c.len = len;
+                c.inner = inner;
+                c.strips = uint32_t(p.col_strips);
+                c.rblocks = uint32_t(p.col_chunks);
+                c.exclusive = exclusive ? 1 : 0;
+                return find_columns_single(dt, op)(c, stream);
+            }
             ColArgs c{};
             c.in = in;
             c.out = out;
@@ -618,6 +676,8 @@ void fill_plan(const TilePlan &p, scan_dtype_t dt, scan_op_t op, scan_plan_t *pl
     if (p.kernel == SCAN_KERNEL_ELEMENT) plan->num_tiles = p.num_tiles / p.tiles_per_seg * p.rts_blocks;
     if (p.kernel == SCAN_KERNEL_ELEMENT)
         plan->lds_bytes = element_lds_bytes(dt, op, p);
+    else if (p.kernel == SCAN_KERNEL_COLUMNS_LOOKBACK)
+        plan->lds_bytes = 2 * int64_t(kColTileWaves) * kWave * p.vec * carry_bytes(dt, op) + 32;
     else
         plan->lds_bytes = int64_t(p.rows) * (p.block / 64) * dtype_bytes(dt) + carry_bytes(dt, op) + 32;
     plan->workspace_bytes = int64_t(p.ws_bytes);
@@ -691,7 +751,7 @@ int scan_plan(scan_call_t call, scan_dtype_t dtype, scan_op_t op, int64_t outer,
             rc = plan_scan(dtype, op, outer, len, true, tu, p);
         } else {
             rc = plan_element(dtype, op, outer, len, inner, true, tu, p);
-            if (rc == SCAN_ERR_UNSUPPORTED) rc = plan_columns(dtype, op, outer, len, inner, true, p);
+            if (rc == SCAN_ERR_UNSUPPORTED) rc = plan_columns(dtype, op, outer, len, inner, true, tu, p);
         }
         break;
     case SCAN_CALL_COMPACT:

@@ -539,6 +539,17 @@ struct GapRead {
         }
     }
 
+    // Every still-unpublished slot read again, all loads issued before any
+    // is decoded: one memory round trip per poll however many slots wait
+    // (a load and its decode per slot made one round trip per slot).
+    __device__ __forceinline__ void refetch(const uint64_t *desc, uint32_t pending) {
+#pragma unroll
+        for (int k = 0; k < NR; k++) {
+            const int64_t p = lo + lane_id() + int64_t(kWave) * k;
+            if (pending & (1u << k)) D::fetch(desc + p * D::kWords, w[k]);
+        }
+    }
+
     // The combination of the aggregates of [lo, hi), the same in every lane.
     template <class Op>
     __device__ __forceinline__ C finish(const uint64_t *desc, uint32_t epoch, WsHeader *hdr, uint32_t spin_limit) {
@@ -563,16 +574,13 @@ struct GapRead {
                 break;
             }
             __builtin_amdgcn_s_sleep(1);
+            refetch(desc, pending);
 #pragma unroll
             for (int k = 0; k < NR; k++) {
-                if (pending & (1u << k)) {
-                    const int64_t p = lo + lane_id() + int64_t(kWave) * k;
-                    C v;
-                    D::fetch(desc + p * D::kWords, w[k]);
-                    if (D::decode(w[k], epoch, v) != 0u) {
-                        acc = Op::apply(v, acc);
-                        pending &= ~(1u << k);
-                    }
+                C v;
+                if ((pending & (1u << k)) && D::decode(w[k], epoch, v) != 0u) {
+                    acc = Op::apply(v, acc);
+                    pending &= ~(1u << k);
                 }
             }
         }
@@ -603,11 +611,10 @@ struct GapRead {
                 break;
             }
             __builtin_amdgcn_s_sleep(1);
+            refetch(desc, pending);
 #pragma unroll
             for (int k = 0; k < NR; k++) {
                 if (pending & (1u << k)) {
-                    const int64_t p = lo + lane_id() + int64_t(kWave) * k;
-                    D::fetch(desc + p * D::kWords, w[k]);
                     if (D::decode(w[k], epoch, v[k]) != 0u)
                         pending &= ~(1u << k);
                     else

@@ -148,6 +148,28 @@ struct ColArgs {
 using ColLaunch = int (*)(const ColArgs &, hipStream_t);
 ColLaunch find_columns(scan_dtype_t dt, scan_op_t op, int vec);
 
+// The single pass for wide inner extents (128-bit rows only): one register
+// tile of kColTileRows rows x (64 x vec) columns per 1024-thread workgroup,
+// grid = tiles; each tile publishes its column aggregates and adds those of
+// the tiles above it in its strip (columns.hip).
+constexpr int kColTileWaves = 16, kColTileRowsPerThread = 16;
+constexpr int kColTileRows = kColTileWaves * kColTileRowsPerThread;
+constexpr int64_t kColSingleMaxTiles = 256;     // one tile per compute unit on MI355X
+constexpr int64_t kColSingleMaxRowBlocks = 64;  // tiles above a tile: at most 63 reads per column
+struct ColSingleArgs {
+    PipeArgs pipe;            // workspace protocol (num_tiles = tiles, the grid)
+    const void *in;
+    void *out;
+    uint32_t outer;
+    int64_t len;
+    int64_t inner;
+    uint32_t strips;          // column strips of 64 x vec columns
+    uint32_t rblocks;         // row blocks of kColTileRows rows per strip
+    int32_t exclusive;
+};
+using ColSingleLaunch = int (*)(const ColSingleArgs &, hipStream_t);
+ColSingleLaunch find_columns_single(scan_dtype_t dt, scan_op_t op);
+
 // -------------------------------------------------------------- utilities
 // fill `words` 64-bit words with `value`; word `at` (when in range) gets `at_value`
 int launch_fill_u64(void *p, uint64_t words, uint64_t value, hipStream_t s, uint64_t at = ~uint64_t(0),

@@ -118,6 +118,32 @@ def test_plan_small_arrays_take_short_tiles():
     assert p["kernel"] == "reduce_then_scan" and p["items_per_thread"] == 32
 
 
+def test_plan_columns_single_pass():
+    # Wide inner extents take the one-pass column kernel when the array makes
+    # at most 256 register tiles of 256 rows x (64 x vec) columns (one per
+    # compute unit) and at most 64 row blocks per strip; its workspace holds
+    # one descriptor word per column of every tile (two for 64-bit carries).
+    from stream_compaction_wave64_amd import binding
+    import torch
+    p = binding.plan("scan", torch.float32, "sum", 1, 4096, 4096)
+    assert (p["kernel"], p["launches"], p["block_size"], p["vec"]) == ("columns_lookback", 1, 1024, 4)
+    assert p["num_tiles"] == 16 * 16 and p["tile_elems"] == 256 * 256
+    assert p["workspace_bytes"] == 4096 + 256 * 256 * 8
+    p = binding.plan("scan", torch.float64, "sum", 1, 4096, 4096)  # 512 tiles of 128 columns
+    assert (p["kernel"], p["launches"]) == ("columns", 3)
+    p = binding.plan("scan", torch.float64, "max", 2, 1024, 1024)   # 2 x 4 x 8 tiles
+    assert (p["kernel"], p["num_tiles"], p["carry_words"]) == ("columns_lookback", 64, 2)
+    assert p["workspace_bytes"] == 4096 + 64 * 128 * 2 * 8
+    p = binding.plan("scan", torch.int32, "sum", 1, 16384, 256)      # 64 row blocks: the most
+    assert p["kernel"] == "columns_lookback"
+    p = binding.plan("scan", torch.int32, "sum", 1, 16385, 256)      # 65 row blocks
+    assert p["kernel"] == "columns"
+    p = binding.plan("scan", torch.float32, "sum", 1, 4096, 4096, tuning={"algo": "reduce_then_scan"})
+    assert (p["kernel"], p["launches"]) == ("columns", 3)
+    p = binding.plan("scan", torch.float32, "sum", 1, 4096, 100)      # strips less than half full
+    assert p["kernel"] != "columns_lookback"
+
+
 def _call_scan(lib, fn, inp, out, n, dt=3, op=0, width=1, ws=None, wsb=0):
     return getattr(lib, fn)(inp, out, n, dt, op, width, ws, wsb, None, None)
 

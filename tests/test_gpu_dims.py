@@ -85,3 +85,83 @@ def test_configs_2d_full_size():
     _check(square, 0)   # 4096 x 4096 along columns
     _check(wide, 1)     # 2 x 1e7 along rows
     _check(tall, 0)     # 1e6 x 8 along the long axis
+
+
+# The single pass for wide inner extents: register tiles of 256 rows x
+# (64 x vec) columns, one per workgroup, each adding the column aggregates of
+# the tiles above it.  Shapes: several row blocks and strips, ragged rows, a
+# partial last strip, outer slices, the most row blocks per strip (64), and a
+# strip just half full.
+SINGLE_SHAPES = [(1, 4096, 4096), (1, 300, 1024), (3, 257, 520), (1, 16384, 256), (1, 1, 4096), (2, 513, 128)]
+TORCH_DT = {np.float32: torch.float32, np.float64: torch.float64, np.int32: torch.int32, np.int64: torch.int64,
+            np.uint32: torch.uint32}
+
+
+def _single_input(dt, shape, seed, op):
+    rng = np.random.default_rng(seed)
+    if np.issubdtype(dt, np.integer):
+        return rng.integers(-1000, 1000, shape).astype(dt) if dt != np.uint32 else \
+            rng.integers(0, 2000, shape).astype(dt)
+    if op == "prod":
+        return (1 + (rng.random(shape) - 0.5) * 0.002).astype(dt)
+    return (2 * rng.random(shape) - 1).astype(dt)
+
+
+@pytest.mark.parametrize("dt", [np.float32, np.float64, np.int32, np.uint32, np.int64], ids=lambda d: np.dtype(d).name)
+@pytest.mark.parametrize("op", ["sum", "prod", "max", "min"])
+def test_columns_single_pass(dt, op):
+    vec = 16 // np.dtype(dt).itemsize
+    for i, (outer, length, inner) in enumerate(SINGLE_SHAPES):
+        if 2 * inner < 64 * vec:
+            continue
+        if op != "sum" and length * inner > 2 ** 22:
+            continue
+        p = sw.plan("scan", TORCH_DT[dt], op, outer, length, inner)
+        tiles = outer * -(-inner // (64 * vec)) * -(-length // 256)
+        # more tiles than compute units: the three-launch path
+        want = ("columns_lookback", 1) if tiles <= 256 else ("columns", 3)
+        assert (p["kernel"], p["launches"]) == want, (outer, length, inner, p)
+        x = _single_input(dt, (outer, length, inner), 95 + i, op)
+        for excl in (False, True):
+            _check(x, 1, op, excl)
+
+
+def test_columns_single_pass_dynamic_claiming():
+    # a start count that never confirms residency: tiles are claimed in order
+    # (error word bit 2), results still exact
+    from stream_compaction_wave64_amd import binding
+    x = _single_input(np.int32, (1, 4096, 4096), 99, "sum")
+    xd = to_dev(x)
+    ws = torch.zeros(1 << 22, dtype=torch.uint8, device=DEV)
+    key = (torch.device(DEV).index, binding._stream(torch.device(DEV)))
+    saved = binding.workspaces._ws.get(key)
+    binding.workspaces._ws[key] = ws
+    try:
+        for excl in (False, True):
+            ws[128:132].view(torch.int32)[0] = -1
+            r = sw.scan_dim(xd, 1, exclusive=excl, tuning={"mode_limit": 8})
+            torch.cuda.synchronize()
+            assert sw.scan_workspace_error(ws) == 4
+            assert_scan_matches(x.ravel(), to_host(r).ravel(), "sum", excl, dims=(1, 4096, 4096),
+                                what=f"dynamic excl={excl}")
+            sw.scan_workspace_init(ws)
+        r = sw.scan_dim(xd, 1)
+        torch.cuda.synchronize()
+        assert sw.scan_workspace_error(ws) == 0
+        assert_scan_matches(x.ravel(), to_host(r).ravel(), "sum", False, dims=(1, 4096, 4096))
+    finally:
+        if saved is None:
+            binding.workspaces._ws.pop(key, None)
+        else:
+            binding.workspaces._ws[key] = saved
+
+
+def test_columns_reduce_then_scan_on_request():
+    # the three-launch path stays available (algo reduce-then-scan) for the
+    # shapes the single pass takes
+    x = _single_input(np.float32, (1, 4096, 4096), 98, "sum")
+    p = sw.plan("scan", torch.float32, "sum", 1, 4096, 4096, tuning={"algo": "reduce_then_scan"})
+    assert p["kernel"] == "columns" and p["launches"] == 3
+    r = sw.scan_dim(to_dev(x), 1, tuning={"algo": "reduce_then_scan"})
+    torch.cuda.synchronize()
+    assert_scan_matches(x.ravel(), to_host(r).ravel(), "sum", False, dims=(1, 4096, 4096))
