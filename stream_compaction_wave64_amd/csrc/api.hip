@@ -57,6 +57,23 @@ ColLaunch find_columns_i64(scan_op_t, int);
 ColLaunch find_columns_f32(scan_op_t, int);
 ColLaunch find_columns_f64(scan_op_t, int);
 
+ResLaunch find_resident_i32(scan_op_t);
+ResLaunch find_resident_u32(scan_op_t);
+ResLaunch find_resident_i64(scan_op_t);
+ResLaunch find_resident_f32(scan_op_t);
+ResLaunch find_resident_f64(scan_op_t);
+
+ResLaunch find_resident(scan_dtype_t dt, scan_op_t op) {
+    switch (dt) {
+    case SCAN_I32: return find_resident_i32(op);
+    case SCAN_U32: return find_resident_u32(op);
+    case SCAN_I64: return find_resident_i64(op);
+    case SCAN_F32: return find_resident_f32(op);
+    case SCAN_F64: return find_resident_f64(op);
+    }
+    return nullptr;
+}
+
 ColSingleLaunch find_columns_single_i32(scan_op_t);
 ColSingleLaunch find_columns_single_u32(scan_op_t);
 ColSingleLaunch find_columns_single_i64(scan_op_t);
@@ -161,6 +178,11 @@ constexpr int kDefaultBlock = 512;  // threads per workgroup of the tiled kernel
 constexpr int kDefaultRtsBlocks = 1024;               // C of reduce-then-scan
 constexpr int64_t kDefaultLocalMem = 32 * 1024;       // LDS budget of the large-element rule (AcceleratedKernels.jl PR #208)
 constexpr int64_t kSmallArrayTiles = 256;             // one tile per CU: the small-array shape rule
+// the resident single pass from this many bytes up: below it the small
+// array tiles won (back-to-back calls, int32 2^20: 9.1 against 9.9 us), from
+// it the resident pass (int32 2^21: 10.6 against 11.3, fp64 2^20: 11.1
+// against 12.3)
+constexpr int64_t kResMinBytes = int64_t(8) << 20;
 constexpr int64_t kElemTileLocalMem = 64 * 1024;      // default bound on an element tile's E (default dynamic LDS limit)
 constexpr int kElemDefaultBlock = 256;                // large elements: start of the rule
 constexpr int64_t kElemChunks = 2048;  // large elements: workgroups per launch (<= 8192, the partials pass)
@@ -299,6 +321,31 @@ int plan_scan(scan_dtype_t dt, scan_op_t op, int64_t outer, int64_t len, bool al
     p.num_tiles = outer * p.tiles_per_seg;
     if (p.num_tiles > int64_t(INT32_MAX)) return SCAN_ERR_OVERFLOW;  // grid x limit
     p.carry_words = rts ? carry_bytes(dt, op) / 4 : desc_words(dt, op);
+    // Arrays that fit one register tile per compute unit: the resident single
+    // pass, with the fewest rows per tile that keep the tiles within
+    // kResMaxTiles (the most compute units reading).  Only for the default
+    // shape, without a grid cap, identity scans of 128-bit rows.
+    if (shape_free && tu.grid_blocks <= 0 && !tu.no_identity && vec_ok && outer * len * esize >= kResMinBytes &&
+        find_resident(dt, op) != nullptr) {
+        const int64_t re = int64_t(kResWaves - 1) * kWave * (16 / esize);  // the data waves
+        const int maxr = esize == 8 ? kResMaxRows8 : kResMaxRows4;
+        for (int r = 1; r <= maxr; r++) {
+            const int64_t tps = (len + r * re - 1) / (r * re);
+            if (outer * tps <= kResMaxTiles) {
+                p.kernel = SCAN_KERNEL_RESIDENT;
+                p.block = kResWaves * kWave;
+                p.rows = r;
+                p.vec = 16 / esize;
+                p.tile = r * re;
+                p.tiles_per_seg = tps;
+                p.num_tiles = outer * tps;
+                p.rts_blocks = p.rts_chunk = 0;
+                p.ws_bytes = kHeader + round_up(size_t(p.num_tiles) * p.carry_words * 8, 256);
+                p.launches = 1;
+                return SCAN_OK;
+            }
+        }
+    }
     if (rts) {
         p.kernel = SCAN_KERNEL_RTS;
         int64_t c = tu.rts_blocks > 0 ? tu.rts_blocks : kDefaultRtsBlocks;
@@ -648,6 +695,11 @@ int scan_common(const void *in, void *out, int64_t outer, int64_t len, int64_t i
     a.seg_len = len;
     a.exclusive = exclusive ? 1 : 0;
     a.total_out = total_out;
+    if (p.kernel == SCAN_KERNEL_RESIDENT) {
+        if (total_out != nullptr && dt == SCAN_I32 && op == SCAN_OP_SUM)  // count-scan-emit's offsets
+            return find_pack_resident()(a, p.rows, stream);
+        return find_resident(dt, op)(a, p.rows, stream);
+    }
     const uint32_t grid_cap = tu.grid_blocks > 0 ? uint32_t(tu.grid_blocks) : 0u;
     if (total_out != nullptr && dt == SCAN_I32 && op == SCAN_OP_SUM)  // count-scan-emit's offsets
         return find_pack_lookback(p.block, p.rows, p.vec)(a, grid_cap, stream);
@@ -677,7 +729,10 @@ void fill_plan(const TilePlan &p, scan_dtype_t dt, scan_op_t op, scan_plan_t *pl
     if (p.kernel == SCAN_KERNEL_ELEMENT)
         plan->lds_bytes = element_lds_bytes(dt, op, p);
     else if (p.kernel == SCAN_KERNEL_COLUMNS_LOOKBACK)
-        plan->lds_bytes = 2 * int64_t(kColTileWaves) * kWave * p.vec * carry_bytes(dt, op) + 32;
+        plan->lds_bytes = int64_t(kColTileWaves + 1) * kWave * p.vec * carry_bytes(dt, op) + 32;
+    else if (p.kernel == SCAN_KERNEL_RESIDENT)
+        plan->lds_bytes = int64_t(dtype_bytes(dt)) * (kResWaves - 1) * (dt == SCAN_I64 || dt == SCAN_F64 ? kResMaxRows8 : kResMaxRows4) +
+                          carry_bytes(dt, op) + 32;
     else
         plan->lds_bytes = int64_t(p.rows) * (p.block / 64) * dtype_bytes(dt) + carry_bytes(dt, op) + 32;
     plan->workspace_bytes = int64_t(p.ws_bytes);

@@ -31,6 +31,16 @@ using LbLaunch = int (*)(const ScanArgs &, uint32_t grid_cap, hipStream_t);
 LbLaunch find_lookback(scan_dtype_t dt, scan_op_t op, int block, int rows, int vec);
 LbLaunch find_pack_lookback(int block, int rows, int vec);  // int32 sum, offsets kept cacheable
 
+// The resident single pass (resident.hip): one 1024-thread workgroup (15
+// data waves and a control wave) per tile of `rows` x 960 x vec elements
+// (vec = 16 / element size), at most kResMaxTiles tiles, grid = tiles.
+constexpr int kResWaves = 16;
+constexpr int kResMaxRows4 = 17, kResMaxRows8 = 21;  // 68 and 84 data registers per thread
+constexpr int64_t kResMaxTiles = 256;                // one per compute unit on MI355X
+using ResLaunch = int (*)(const ScanArgs &, int rows, hipStream_t);
+ResLaunch find_resident(scan_dtype_t dt, scan_op_t op);
+ResLaunch find_pack_resident();  // int32 sum, offsets kept cacheable
+
 // ---------------------------------------------------------- reduce-then-scan
 // Three launches over `blocks` workgroups, each owning `chunk_tiles`
 // consecutive tiles of block*rows*vec elements: reduce each chunk into a

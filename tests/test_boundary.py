@@ -93,29 +93,62 @@ def test_plan_segments_and_types():
 
 
 def test_plan_small_arrays_take_short_tiles():
-    # Whole arrays that 448 x 5-row tiles cover in at most 256 tiles (one per
-    # CU) take those tiles; larger ones, rows of a 2-D array, explicit shapes
-    # and the reduce-then-scan path keep their own (arrays within one default
-    # tile follow the short-segment rule instead).
+    # Whole arrays under 8 MiB that 448 x 5-row tiles cover in at most 256
+    # tiles (one per CU) take those tiles; from 8 MiB the resident pass takes
+    # arrays of 128-bit rows; rows of a 2-D array, explicit shapes, the
+    # element-wide path and reduce-then-scan keep their own (arrays within
+    # one default tile follow the short-segment rule instead).
     from stream_compaction_wave64_amd import binding
     import torch
     for dt, vec, big_ipt in ((torch.int32, 4, 28), (torch.float32, 4, 28), (torch.float64, 2, 16)):
         small_tile = 448 * 5 * vec
         big_tile = 448 * big_ipt if vec == 2 else 704 * big_ipt
-        for n in (2 * big_tile, 128 * small_tile, 256 * small_tile):
+        below = (8 << 20) // (16 // vec) - vec  # the largest array under 8 MiB
+        for n in (2 * big_tile, 128 * small_tile, below):
             p = binding.plan("scan", dt, "sum", 1, n)
-            assert (p["block_size"], p["items_per_thread"]) == (512, 5 * vec), (dt, n, p)
+            assert (p["kernel"], p["block_size"], p["items_per_thread"]) == ("lookback", 512, 5 * vec), (dt, n, p)
             assert p["num_tiles"] <= 256
-        p = binding.plan("scan", dt, "sum", 1, 256 * small_tile + vec)
-        assert p["items_per_thread"] == big_ipt, (dt, p)
+        for n in (below + vec, 256 * small_tile, 256 * small_tile + vec):
+            p = binding.plan("scan", dt, "sum", 1, n)
+            assert p["kernel"] == "resident" and p["num_tiles"] <= 256, (dt, n, p)
         p = binding.plan("scan", dt, "sum", 1, 64 * small_tile + 1)  # element-wide path: unchanged
         assert p["vec"] == 1 and p["items_per_thread"] == big_ipt // vec, (dt, p)
+        p = binding.plan("scan", dt, "sum", 1, 1024 * small_tile + 1)  # element-wide, 8 MiB and more
+        assert p["kernel"] == "lookback" and p["vec"] == 1, (dt, p)
         p = binding.plan("scan", dt, "sum", 1, 64 * small_tile, tuning={"block_size": 512, "items_per_thread": 3 * vec})
         assert p["items_per_thread"] == 3 * vec
         p = binding.plan("scan", dt, "sum", 2, 64 * small_tile)
         assert p["items_per_thread"] == big_ipt, (dt, p)
     p = binding.plan("scan", torch.float32, "sum", 1, 1 << 20, tuning={"algo": "reduce_then_scan"})
     assert p["kernel"] == "reduce_then_scan" and p["items_per_thread"] == 32
+
+
+def test_plan_resident():
+    # The resident pass: one 1024-thread workgroup (15 data waves and a
+    # control wave) per tile of rows x 960 x vec elements, the fewest rows
+    # that keep the tiles within 256, up to 17 rows (4-byte elements) or 21
+    # (8-byte); one descriptor word per tile (two for 64-bit carries); not
+    # with a grid cap, an explicit shape or without an identity; segments
+    # (rows of a 2-D array) when all fit.
+    from stream_compaction_wave64_amd import binding
+    import torch
+    p = binding.plan("scan", torch.float32, "sum", 1, 10 ** 7)   # 11 rows of 3840: 237 tiles
+    assert (p["kernel"], p["block_size"], p["items_per_thread"], p["num_tiles"]) == ("resident", 1024, 44, 237)
+    assert p["workspace_bytes"] == 4096 + 2048 and p["launches"] == 1  # 237 words, in 256-byte units
+    p = binding.plan("scan", torch.float64, "sum", 1, 10 ** 7)   # 21 rows of 1920: 249 tiles
+    assert (p["kernel"], p["items_per_thread"], p["num_tiles"], p["carry_words"]) == ("resident", 42, 249, 2)
+    cap4, cap8 = 256 * 17 * 3840, 256 * 21 * 1920
+    p = binding.plan("scan", torch.int32, "sum", 1, cap4)
+    assert (p["kernel"], p["items_per_thread"], p["num_tiles"]) == ("resident", 68, 256)
+    assert binding.plan("scan", torch.int32, "sum", 1, cap4 + 4)["kernel"] == "lookback"
+    assert binding.plan("scan", torch.int64, "max", 1, cap8)["kernel"] == "resident"
+    assert binding.plan("scan", torch.int64, "max", 1, cap8 + 2)["kernel"] == "lookback"
+    p = binding.plan("scan", torch.float32, "sum", 4, 1 << 20)    # segments: 4 x 55 tiles of 5 rows
+    assert (p["kernel"], p["num_tiles"], p["items_per_thread"]) == ("resident", 220, 20)
+    for tu in ({"grid_blocks": 8}, {"block_size": 768, "items_per_thread": 28}, {"no_identity": 1},
+               {"algo": "reduce_then_scan"}):
+        assert binding.plan("scan", torch.float32, "sum", 1, 10 ** 7, tuning=tu)["kernel"] != "resident", tu
+    assert binding.plan("pack", torch.int32, "sum", 1, 10 ** 7)["kernel"] == "pack"
 
 
 def test_plan_columns_single_pass():

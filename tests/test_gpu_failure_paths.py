@@ -137,3 +137,38 @@ def test_late_publishers_dynamic_claiming_and_no_identity(stride, sleeps):
             torch.cuda.synchronize()
             assert_scan_matches(f, to_host(r), "sum", False, what=f"no identity {tuning}", noid=True)
         assert sw.scan_workspace_error(ws) == 0
+
+
+def test_resident_pass_failure_paths():
+    # The resident single pass (arrays of 8 MiB and more that fit one register
+    # tile per compute unit) under the same forced conditions: a residency
+    # check that never confirms (dynamic claiming, flag bit 2, exact
+    # results), late publishers (the gap read's re-polls, exact results, no
+    # flag) and a garbage epoch (the waits give up: flag bit 0).
+    x = inputs.generic(np.int32, 3_000_000, 70, "wide")
+    xd = to_dev(x)
+    assert sw.plan("scan", torch.int32, "sum", 1, x.size)["kernel"] == "resident"
+    ws = torch.zeros(1 << 22, dtype=torch.uint8, device=DEV)
+    with _Installed(ws):
+        for excl in (False, True):
+            ws[128:132].view(torch.int32)[0] = -1
+            fn = sw.scan_exclusive if excl else sw.scan_inclusive
+            r = fn(xd, tuning={"mode_limit": 8})
+            torch.cuda.synchronize()
+            assert sw.scan_workspace_error(ws) == 4
+            assert_scan_matches(x, to_host(r), "sum", excl, what=f"dynamic excl={excl}")
+        sw.scan_workspace_init(ws)
+        f = inputs.generic(np.float32, 3_000_000, 71)
+        fd = to_dev(f)
+        for stride, sleeps in DELAYS:
+            for excl in (False, True):
+                fn = sw.scan_exclusive if excl else sw.scan_inclusive
+                r = fn(fd, tuning={"delay_stride": stride, "delay_sleeps": sleeps})
+                torch.cuda.synchronize()
+                assert_scan_matches(f, to_host(r), "sum", excl, what=f"late publishers {stride} {sleeps}")
+        assert sw.scan_workspace_error(ws) == 0
+        ws[:16].view(torch.int32)[0] = 1 << 30
+        sw.scan_inclusive(xd, tuning={"spin_limit": 32})
+        torch.cuda.synchronize()
+        assert sw.scan_workspace_error(ws) & 1
+        _recovers(ws, x, xd)

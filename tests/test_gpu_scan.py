@@ -57,10 +57,11 @@ def test_parity_default_tiles(dt, op, exclusive):
 @pytest.mark.parametrize("op", OPS)
 @pytest.mark.parametrize("exclusive", [False, True], ids=["incl", "excl"])
 def test_parity_whole_array_default_shape(dt, op, exclusive):
-    # the shape large whole arrays get (the planner's choice at 1e7, beyond
-    # the small-array rule), pinned through the tuning so that sizes of a few
-    # tiles run it too
-    p = sw.plan("scan", TORCH[np.dtype(dt)], op, 1, 10 ** 7)
+    # the shape large whole arrays get (the planner's choice at 1e8, beyond
+    # the small-array rule and the resident pass), pinned through the tuning
+    # so that sizes of a few tiles run it too
+    p = sw.plan("scan", TORCH[np.dtype(dt)], op, 1, 10 ** 8)
+    assert p["kernel"] == "lookback"
     tuning = {"block_size": p["block_size"], "items_per_thread": p["items_per_thread"]}
     tile = p["tile_elems"]
     assert sw.plan("scan", TORCH[np.dtype(dt)], op, 1, 1000, tuning=tuning)["tile_elems"] == tile
@@ -71,20 +72,51 @@ def test_parity_whole_array_default_shape(dt, op, exclusive):
 
 @pytest.mark.parametrize("dt", DTYPES, ids=lambda d: np.dtype(d).name)
 @pytest.mark.parametrize("op", OPS)
-def test_parity_across_small_array_switch(dt, op):
-    # whole arrays of up to 256 small-array tiles take that shape, longer
-    # ones the default: both sides of the switch, planner's choice
-    big = sw.plan("scan", TORCH[np.dtype(dt)], op, 1, 10 ** 7)
-    vec = 16 // np.dtype(dt).itemsize
-    edge = 256 * 448 * 5 * vec  # 256 tiles of 448 data threads x 5 rows
-    below = sw.plan("scan", TORCH[np.dtype(dt)], op, 1, edge)
-    above = sw.plan("scan", TORCH[np.dtype(dt)], op, 1, edge + vec)
-    assert below["tile_elems"] == 448 * 5 * vec and below["num_tiles"] == 256
-    assert above["tile_elems"] == big["tile_elems"] != below["tile_elems"]
-    for i, n in enumerate([edge, edge + vec]):
+def test_parity_across_shape_switches(dt, op):
+    # Whole arrays of 128-bit rows: below 8 MiB the small-array tiles (448 x 5
+    # rows, at most 256 of them); from 8 MiB the resident single pass (one
+    # register tile of 960 data threads x rows per compute unit, at most 256
+    # tiles, 17 rows for 4-byte and 21 for 8-byte elements); past its
+    # capacity the default look-back shape.  Both sides of each switch.
+    es = np.dtype(dt).itemsize
+    vec = 16 // es
+    big = sw.plan("scan", TORCH[np.dtype(dt)], op, 1, 10 ** 8)
+    res_min = (8 << 20) // es
+    cap = 256 * (17 if es == 4 else 21) * 960 * vec
+    cases = [(res_min - vec, "lookback", 448 * 5 * vec), (res_min, "resident", None), (cap, "resident", None),
+             (cap + vec, "lookback", big["tile_elems"])]
+    for i, (n, kernel, tile) in enumerate(cases):
+        p = sw.plan("scan", TORCH[np.dtype(dt)], op, 1, n)
+        assert p["kernel"] == kernel, (n, p)
+        if tile is not None:
+            assert p["tile_elems"] == tile, (n, p)
+        else:
+            assert p["num_tiles"] <= 256 and p["block_size"] == 1024, (n, p)
+        if op not in ("sum", "max") and n > res_min:
+            continue  # the two largest sizes: sum and max only (time)
         x = _input(dt, n, 400 + i, op)
         for excl in (False, True):
             assert_scan_matches(x, _run(x, op, excl), op, excl, what=f"n={n} excl={excl}")
+
+
+@pytest.mark.parametrize("dt", DTYPES, ids=lambda d: np.dtype(d).name)
+@pytest.mark.parametrize("op", OPS)
+def test_parity_resident(dt, op):
+    # the resident pass at row counts 3 and 7 with a ragged last tile (a
+    # partial row, then a partial vector row), and a tile count that leaves
+    # compute units idle
+    es = np.dtype(dt).itemsize
+    vec = 16 // es
+    re = 960 * vec  # elements per tile row
+    for i, (rows, n) in enumerate([(3, 3 * re * 200 + 5 * vec), (7, 7 * re * 255 + re + 3 * vec),
+                                   (3, 3 * re * 181)]):
+        if n * es < (8 << 20):
+            n = -(-(8 << 20) // (es * rows * re)) * rows * re + vec  # at least the switch
+        p = sw.plan("scan", TORCH[np.dtype(dt)], op, 1, n)
+        assert p["kernel"] == "resident", (n, p)
+        x = _input(dt, n, 500 + i, op)
+        for excl in (False, True):
+            assert_scan_matches(x, _run(x, op, excl), op, excl, what=f"n={n} rows={p['items_per_thread'] // vec}")
 
 
 @pytest.mark.parametrize("dt", DTYPES, ids=lambda d: np.dtype(d).name)
