@@ -167,8 +167,10 @@ typedef enum {
     SCAN_KERNEL_SEGMENTED = 8,  /* ragged segments: tile map, then reduce-then-scan of (head, value) pairs */
     SCAN_KERNEL_COLUMNS_LOOKBACK = 9, /* wide inner extent in one pass: register tiles of 256 rows, each adding
                                          the column aggregates of the tiles above it */
-    SCAN_KERNEL_RESIDENT = 10         /* arrays of at most 256 register tiles (one per compute unit): each tile
+    SCAN_KERNEL_RESIDENT = 10,        /* arrays of at most 256 register tiles (one per compute unit): each tile
                                          loaded once, every earlier tile's aggregate read in one round trip */
+    SCAN_KERNEL_COMPACT_RESIDENT = 11 /* compaction of such arrays in the same way: counts by ballots, selected
+                                         indices staged in LDS, one contiguous range written per tile */
 } scan_kernel_t;
 
 typedef struct {

@@ -222,6 +222,214 @@ static CompactLaunch pick_compact_cmp(scan_cmp_t cmp, int block, int rows, int v
     return nullptr;
 }
 
+// ------------------------------------------------- resident compaction
+// Arrays that fit one tile per compute unit, in one step (the resident scan
+// pass of resident.hip, applied to the selection counts): a control wave
+// (wave 0) runs the call protocol while 15 data waves load their rows of x
+// and, row by row as the data arrives, evaluate the predicate and count the
+// selected elements before each lane in the row with four ballots (no wave
+// scan).  After a barrier the control wave scans the (row, wave) counts in
+// tile order and publishes the tile's count; after a second, each data
+// thread places the tile-local index of each of its selected elements at its
+// slot of an LDS stash while the control wave reads the counts of every
+// earlier tile (one gap read); after a third, all 16 waves write the tile's
+// contiguous output range with whole 16-byte stores.  Traffic: x read once,
+// the selected indices written once.
+template <class X, int CMP, int MAXR>
+__global__ __launch_bounds__(kResWaves *kWave) void k_compact_resident(CompactArgs a, uint32_t rows) {
+    using D = Desc<int32_t>;
+    constexpr int V = 4;
+    constexpr int NDW = kResWaves - 1;                    // data waves
+    constexpr int RE = NDW * kWave * V;                   // elements per tile row
+    constexpr int KE = (MAXR * NDW + kWave - 1) / kWave;  // (row, wave) counts per lane of the control wave
+    static_assert(MAXR * RE <= 65536, "tile-local indices fit 16 bits");
+    __shared__ uint16_t lidx[MAXR * RE];  // selected elements' tile-local indices, in output order
+    __shared__ int32_t ent[MAXR * NDW];   // (row, wave) counts, then their exclusive prefixes in the tile
+    __shared__ int32_t s_pre, s_nsel;
+    __shared__ uint32_t s_epoch, s_tile;
+    __shared__ uint64_t s_hw, s_cap;
+    WsHeader *hdr = reinterpret_cast<WsHeader *>(a.pipe.ws);
+    uint64_t *desc = reinterpret_cast<uint64_t *>(reinterpret_cast<char *>(a.pipe.ws) + kWsHeaderBytes);
+    const int lane = lane_id();
+    const uint32_t wr = uniform(uint32_t(threadIdx.x / kWave));
+    const bool ctrl = wr == 0;
+    const uint32_t dw = wr - 1;                         // data wave index (data waves only)
+    const uint32_t dt = uint32_t(threadIdx.x) - kWave;  // data thread index
+    const uint32_t nt = a.pipe.num_tiles;
+    rows = uniform(rows);
+    const int64_t tile_elems = int64_t(rows) * RE;
+    const X thr = __builtin_bit_cast(X, a.threshold);
+    const int32_t *xs = reinterpret_cast<const int32_t *>(a.x);
+
+    Vec<int32_t, V> x[MAXR];
+    uint32_t pk[MAXR];  // per row: selection bits (4) | selected elements in lower lanes << 4
+    const uint32_t voff = dt * V * 4u;
+    constexpr uint32_t kRowBytes = uint32_t(RE) * 4u;
+    auto load = [&](uint32_t t) {
+        const int64_t start = int64_t(t) * tile_elems, rem = a.n - start;
+        const BufRsrc rs = make_rsrc(xs + start, rem < tile_elems ? rem : tile_elems);
+#pragma unroll
+        for (int r = 0; r < MAXR; r++) {
+            if (r < int(rows))
+                x[r] = __builtin_bit_cast(Vec<int32_t, V>, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, r * kRowBytes, 2));
+        }
+    };
+    auto select_rows = [&](uint32_t t) {
+        const int64_t rem = uniform(a.n - int64_t(t) * tile_elems);
+#pragma unroll
+        for (int r = 0; r < MAXR; r++) {
+            if (r < int(rows)) {
+                const int64_t e0 = int64_t(r) * RE + int64_t(dt) * V;
+                uint32_t b = 0;
+#pragma unroll
+                for (int c = 0; c < V; c++)
+                    b |= uint32_t(e0 + c < rem && keep<X, CMP>(__builtin_bit_cast(X, x[r].v[c]), thr)) << c;
+                uint32_t below = 0, total = 0;
+#pragma unroll
+                for (int c = 0; c < V; c++) {
+                    const uint64_t m = __ballot((b >> c) & 1u);
+                    below += __builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u));
+                    total += uint32_t(__builtin_popcountll(m));
+                }
+                pk[r] = b | (below << 4);
+                if (lane == 0) ent[r * NDW + dw] = int32_t(total);
+            }
+        }
+    };
+    uint32_t tile = blockIdx.x;
+    if (ctrl) {
+        uint32_t tk = 0;
+        if (lane == 0) {
+            uint64_t hw = 0, cap = 0;
+            const uint32_t e = begin_call(hdr, hw, cap);
+            s_epoch = e;
+            s_hw = hw;
+            s_cap = cap;
+            const uint32_t m = decide_mode(hdr, e, gridDim.x, a.pipe.mode_limit);
+            tk = m == kModeStatic
+                     ? uint32_t(blockIdx.x)
+                     : __hip_atomic_fetch_add(&hdr->claim, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            s_tile = tk;
+        }
+        tile = uint32_t(__builtin_amdgcn_readlane(int(tk), 0));
+    } else {
+        load(tile);
+        select_rows(tile);
+    }
+    __syncthreads();
+    if (s_tile != blockIdx.x) {
+        // dynamic mode gave the workgroup another tile (every wave sees the
+        // same s_tile, so all or none take this branch and its barrier)
+        tile = s_tile;
+        if (!ctrl) {
+            load(tile);
+            select_rows(tile);
+        }
+        __syncthreads();
+    }
+    const uint32_t epoch = s_epoch;
+    const int64_t start = int64_t(tile) * tile_elems;
+    if (ctrl) {
+        const uint32_t ne = rows * NDW;
+        int32_t e[KE];
+        int32_t acc = 0;
+#pragma unroll
+        for (int k = 0; k < KE; k++) {
+            const uint32_t i = uint32_t(lane) * KE + k;
+            e[k] = i < ne ? ent[i] : 0;
+            acc += e[k];
+        }
+        const int32_t linc = wave_scan_incl<OpSum>(acc);
+        int32_t run = linc - acc;
+#pragma unroll
+        for (int k = 0; k < KE; k++) {
+            const uint32_t i = uint32_t(lane) * KE + k;
+            if (i < ne) ent[i] = run;
+            run += e[k];
+        }
+        const int32_t nsel = wave_read(linc, kWave - 1);
+        if (lane == 0) {
+            s_nsel = nsel;
+            if (nt > 1) {
+                if (a.pipe.delay_stride > 0 && tile % a.pipe.delay_stride == a.pipe.delay_stride - 1) {
+                    // a late publisher, so tests reach the look-back's re-polls
+                    for (uint32_t i = 0; i < a.pipe.delay_sleeps; i++) __builtin_amdgcn_s_sleep(64);
+                }
+                D::publish(desc + uint64_t(tile) * D::kWords, epoch, kStateA, nsel);
+            }
+        }
+    }
+    __syncthreads();
+    if (ctrl) {
+        int32_t pre = 0;
+        if (tile > 0) {
+            GapRead<int32_t, D, kResMaxTiles / kWave> g;
+            g.issue(desc, 0, int64_t(tile));
+            pre = g.template finish<OpSum>(desc, epoch, hdr, a.pipe.spin_limit);
+        }
+        if (lane == 0) {
+            s_pre = pre;
+            if (tile == nt - 1) *a.count = pre + s_nsel;
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < MAXR; r++) {
+            if (r < int(rows)) {
+                int32_t pos = ent[r * NDW + dw] + int32_t(pk[r] >> 4);
+#pragma unroll
+                for (int c = 0; c < V; c++) {
+                    if ((pk[r] >> c) & 1u) lidx[pos++] = uint16_t(r * RE + int32_t(dt) * V + c);
+                }
+            }
+        }
+    }
+    __syncthreads();
+    const int32_t s0 = int32_t(start);  // n <= INT32_MAX
+    write_range<kResWaves * kWave>(a.out_idx, int64_t(s_pre), s_nsel, a.n,
+                                   [&](int32_t i) { return s0 + int32_t(lidx[i]); });
+    // end of the call: in static mode every workgroup was counted before the
+    // decision; in dynamic mode the holder of the last ticket claimed last
+    if (tile == nt - 1) end_call(hdr, epoch, s_hw, s_cap, a.pipe.words_used, a.pipe.ws_words, desc);
+}
+
+template <class X, int CMP>
+static int launch_compact_resident_impl(const CompactArgs &a, int rows, hipStream_t s) {
+    if (rows < 1 || rows > kResCompactMaxRows || a.pipe.num_tiles > uint32_t(kResMaxTiles)) return SCAN_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL((k_compact_resident<X, CMP, kResCompactMaxRows>), dim3(a.pipe.num_tiles),
+                       dim3(kResWaves * kWave), 0, s, a, uint32_t(rows));
+    return hipGetLastError() == hipSuccess ? SCAN_OK : SCAN_ERR_HIP;
+}
+
+template <class X>
+static ResCompactLaunch pick_compact_resident(scan_cmp_t cmp) {
+    switch (cmp) {
+    case SCAN_CMP_GT: return &launch_compact_resident_impl<X, SCAN_CMP_GT>;
+    case SCAN_CMP_GE: return &launch_compact_resident_impl<X, SCAN_CMP_GE>;
+    case SCAN_CMP_LT: return &launch_compact_resident_impl<X, SCAN_CMP_LT>;
+    case SCAN_CMP_LE: return &launch_compact_resident_impl<X, SCAN_CMP_LE>;
+    case SCAN_CMP_EQ: return &launch_compact_resident_impl<X, SCAN_CMP_EQ>;
+    case SCAN_CMP_NE: return &launch_compact_resident_impl<X, SCAN_CMP_NE>;
+    case SCAN_CMP_BIT_CLEAR:
+    case SCAN_CMP_BIT_SET:
+        if constexpr (!std::is_floating_point_v<X>) {
+            if (cmp == SCAN_CMP_BIT_CLEAR) return &launch_compact_resident_impl<X, SCAN_CMP_BIT_CLEAR>;
+            return &launch_compact_resident_impl<X, SCAN_CMP_BIT_SET>;
+        }
+        return nullptr;
+    }
+    return nullptr;
+}
+
+#if SW64_PART == 0
+#if SW64_DT == 0
+ResCompactLaunch find_compact_resident_i32(scan_cmp_t cmp) { return pick_compact_resident<int32_t>(cmp); }
+#elif SW64_DT == 1
+ResCompactLaunch find_compact_resident_u32(scan_cmp_t cmp) { return pick_compact_resident<uint32_t>(cmp); }
+#elif SW64_DT == 3
+ResCompactLaunch find_compact_resident_f32(scan_cmp_t cmp) { return pick_compact_resident<float>(cmp); }
+#endif
+#endif
+
 #if SW64_PART == 0
 #if SW64_DT == 0
 CompactLaunch find_compact_i32(scan_cmp_t cmp, int b, int r, int v) { return pick_compact_cmp<int32_t>(cmp, b, r, v); }

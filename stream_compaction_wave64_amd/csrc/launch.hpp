@@ -99,6 +99,11 @@ struct CompactArgs {
 };
 using CompactLaunch = int (*)(const CompactArgs &, uint32_t grid_cap, hipStream_t);
 CompactLaunch find_compact(scan_dtype_t x_dt, scan_cmp_t cmp, int block, int rows, int vec);
+// Resident compaction (compact.hip): the resident pass's tiles of rows x 960 x
+// 4 elements, at most kResCompactMaxRows rows (tile-local indices in 16 bits).
+constexpr int kResCompactMaxRows = 17;
+using ResCompactLaunch = int (*)(const CompactArgs &, int rows, hipStream_t);
+ResCompactLaunch find_compact_resident(scan_dtype_t x_dt, scan_cmp_t cmp);
 int launch_emit_neighbors(const int32_t *offsets, int64_t n, int32_t *out, hipStream_t s);
 
 // Stable partition: a count pass, then the compaction's fused scan writing

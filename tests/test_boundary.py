@@ -149,6 +149,15 @@ def test_plan_resident():
                {"algo": "reduce_then_scan"}):
         assert binding.plan("scan", torch.float32, "sum", 1, 10 ** 7, tuning=tu)["kernel"] != "resident", tu
     assert binding.plan("pack", torch.int32, "sum", 1, 10 ** 7)["kernel"] == "pack"
+    # compaction: the same tiles (rows of 960 x 4 keys, at most 17 rows so the
+    # tile-local indices fit 16 bits), at any size of whole 128-bit vectors
+    p = binding.plan("compact", torch.float32, "sum", 1, 10 ** 7)
+    assert (p["kernel"], p["num_tiles"], p["items_per_thread"], p["launches"]) == ("compact_resident", 237, 44, 1)
+    assert binding.plan("compact", torch.int32, "sum", 1, 256 * 17 * 3840)["kernel"] == "compact_resident"
+    assert binding.plan("compact", torch.int32, "sum", 1, 256 * 17 * 3840 + 4)["kernel"] == "compact"
+    assert binding.plan("compact", torch.int32, "sum", 1, 4096)["kernel"] == "compact_resident"
+    assert binding.plan("compact", torch.int32, "sum", 1, 4097)["kernel"] == "compact"  # element-wide
+    assert binding.plan("compact", torch.float32, "sum", 1, 10 ** 7, tuning={"grid_blocks": 4})["kernel"] == "compact"
 
 
 def test_plan_columns_single_pass():

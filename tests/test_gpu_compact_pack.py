@@ -174,3 +174,42 @@ def test_compaction_special_floats(cmp):
     x[rng.integers(0, x.size, 5000)] = specials[rng.integers(0, specials.size, 5000)]
     for t in (0.0, 0.5, float("inf")):
         _check_compact(x, cmp, t)
+
+
+def test_compaction_resident():
+    # x of whole 128-bit vectors that fits one register tile per compute unit
+    # (at most 256 tiles of rows x 960 x 4 elements, rows <= 17) takes the
+    # resident compaction: both sides of its capacity, one-row and ragged
+    # last tiles, every comparison, the bit predicates, closed forms and a
+    # misaligned output.
+    lo, cap = (8 << 20) // 4, 256 * 17 * 3840
+    assert sw.plan("compact", torch.float32, "sum", 1, 4096)["kernel"] == "compact_resident"
+    assert sw.plan("compact", torch.float32, "sum", 1, cap)["kernel"] == "compact_resident"
+    assert sw.plan("compact", torch.float32, "sum", 1, cap + 4)["kernel"] == "compact"
+    for n in (4096, 256 * 3840, 256 * 3840 + 4, cap, cap + 4):
+        x, _ = inputs.compaction_inputs(n, seed=46)
+        _check_compact(x)
+    rng = np.random.default_rng(47)
+    n = 3 * 3840 * 200 + 44  # 3 rows, 201 tiles, 44 elements in the last
+    x = rng.random(n, dtype=np.float32)
+    x[::97] = np.float32(0.5)  # exact ties
+    for cmp in CMPS:
+        _check_compact(x, cmp, 0.5)
+    n = 7 * 3840 * 255 + 3840 + 12  # 7 rows, 256 tiles, the last with a row and 12 elements
+    for dt in (np.int32, np.uint32):
+        keys = rng.integers(0, 2 ** 32, n, dtype=np.uint64).astype(np.uint32).view(dt)
+        for b in (0, 31):
+            _check_compact(keys, "bit_set", b)
+        _check_compact(keys, "le", 12345)
+    for f in (np.ones(lo, np.float32), np.zeros(lo, np.float32), np.tile(np.array([0, 1], np.float32), lo // 2)):
+        _check_compact(f)
+    x, _ = inputs.compaction_inputs(lo + 4, seed=48)
+    ref = oracle.compact(x, "gt", 0.5)
+    buf = torch.full((x.size + 8,), -7, dtype=torch.int32, device=DEV)
+    out = buf[3:3 + x.size]
+    _, count = sw.compact_if(to_dev(x), "gt", 0.5, out=out)
+    torch.cuda.synchronize()
+    got = to_host(buf)
+    assert int(count.item()) == ref.size
+    assert np.array_equal(got[3:3 + ref.size], ref)
+    assert (got[:3] == -7).all() and (got[3 + x.size:] == -7).all()

@@ -172,3 +172,38 @@ def test_resident_pass_failure_paths():
         torch.cuda.synchronize()
         assert sw.scan_workspace_error(ws) & 1
         _recovers(ws, x, xd)
+
+
+def test_resident_compaction_failure_paths():
+    # The resident compaction under the same forced conditions: dynamic
+    # claiming (flag bit 2), late publishers, a garbage epoch (flag bit 0).
+    import oracle
+    x, _ = inputs.compaction_inputs(3_000_000, seed=72)
+    xd = to_dev(x)
+    ref = oracle.compact(x, "gt", 0.5)
+    assert sw.plan("compact", torch.float32, "sum", 1, x.size)["kernel"] == "compact_resident"
+
+    def run(tuning):
+        out, count = sw.compact_if(xd, "gt", 0.5, tuning=tuning)
+        torch.cuda.synchronize()
+        c = int(count.item())
+        return c, to_host(out[:c])
+
+    ws = torch.zeros(1 << 22, dtype=torch.uint8, device=DEV)
+    with _Installed(ws):
+        ws[128:132].view(torch.int32)[0] = -1
+        c, got = run({"mode_limit": 8})
+        assert sw.scan_workspace_error(ws) == 4
+        assert c == ref.size and np.array_equal(got, ref)
+        sw.scan_workspace_init(ws)
+        for stride, sleeps in DELAYS:
+            c, got = run({"delay_stride": stride, "delay_sleeps": sleeps})
+            assert c == ref.size and np.array_equal(got, ref), (stride, sleeps)
+        assert sw.scan_workspace_error(ws) == 0
+        ws[:16].view(torch.int32)[0] = 1 << 30
+        run({"spin_limit": 32})
+        assert sw.scan_workspace_error(ws) & 1
+        sw.scan_workspace_init(ws)
+        c, got = run(None)
+        assert sw.scan_workspace_error(ws) == 0
+        assert c == ref.size and np.array_equal(got, ref)
