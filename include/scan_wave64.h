@@ -169,8 +169,10 @@ typedef enum {
                                          the column aggregates of the tiles above it */
     SCAN_KERNEL_RESIDENT = 10,        /* arrays of at most 256 register tiles (one per compute unit): each tile
                                          loaded once, every earlier tile's aggregate read in one round trip */
-    SCAN_KERNEL_COMPACT_RESIDENT = 11 /* compaction of such arrays in the same way: counts by ballots, selected
-                                         indices staged in LDS, one contiguous range written per tile */
+    SCAN_KERNEL_COMPACT_RESIDENT = 11, /* compaction of such arrays in the same way: counts by ballots, selected
+                                          indices staged in LDS, one contiguous range written per tile */
+    SCAN_KERNEL_PARTITION_RESIDENT = 12 /* stable partition of such arrays in one launch: every tile reads all
+                                           tiles' counts, each element goes straight to its slot */
 } scan_kernel_t;
 
 typedef struct {

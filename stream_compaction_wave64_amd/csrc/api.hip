@@ -68,6 +68,17 @@ ResCompactLaunch find_compact_resident(scan_dtype_t dt, scan_cmp_t cmp) {
     return nullptr;
 }
 
+ResPartitionLaunch find_partition_resident_i32(scan_cmp_t);
+ResPartitionLaunch find_partition_resident_u32(scan_cmp_t);
+ResPartitionLaunch find_partition_resident_f32(scan_cmp_t);
+
+ResPartitionLaunch find_partition_resident(scan_dtype_t dt, scan_cmp_t cmp) {
+    if (dt == SCAN_F32) return find_partition_resident_f32(cmp);
+    if (dt == SCAN_I32) return find_partition_resident_i32(cmp);
+    if (dt == SCAN_U32) return find_partition_resident_u32(cmp);
+    return nullptr;
+}
+
 ResLaunch find_resident_i32(scan_op_t);
 ResLaunch find_resident_u32(scan_op_t);
 ResLaunch find_resident_i64(scan_op_t);
@@ -600,6 +611,30 @@ int plan_segmented(scan_dtype_t dt, scan_op_t op, int64_t n, bool aligned, const
 // 1024 workgroups whose counts follow the tile descriptors.
 int plan_partition(scan_dtype_t dt, scan_cmp_t cmp, int64_t n, bool aligned, const scan_tuning_t &tu, TilePlan &p,
                    int64_t &count_wgs, int64_t &count_chunk) {
+    // Arrays that fit one register tile per compute unit: the resident pass,
+    // one launch, x read once (the tiles read every tile's count instead of
+    // a count pass); the default shape without a grid cap.
+    const bool shape_free = tu.block_size <= 0 && tu.items_per_thread <= 0;
+    if (shape_free && tu.grid_blocks <= 0 && aligned && n % 4 == 0 && find_partition_resident(dt, cmp) != nullptr) {
+        const int64_t re = int64_t(kResWaves - 1) * kWave * 4;
+        for (int r = 1; r <= kResCompactMaxRows; r++) {
+            const int64_t tiles = (n + r * re - 1) / (r * re);
+            if (tiles <= kResMaxTiles) {
+                p.kernel = SCAN_KERNEL_PARTITION_RESIDENT;
+                p.block = kResWaves * kWave;
+                p.rows = r;
+                p.vec = 4;
+                p.tile = r * re;
+                p.tiles_per_seg = p.num_tiles = tiles;
+                p.carry_words = 1;
+                p.rts_blocks = p.rts_chunk = 0;
+                p.ws_bytes = kHeader + round_up(size_t(p.num_tiles) * 8, 256);
+                p.launches = 1;
+                count_wgs = count_chunk = 0;
+                return SCAN_OK;
+            }
+        }
+    }
     const int rc = plan_shape(
         4, aligned && n % 4 == 0, tu, p,
         [&](int b, int r, int v) { return find_partition(dt, cmp, b, r, v) != nullptr; }, true, 3, 768);
@@ -767,6 +802,9 @@ void fill_plan(const TilePlan &p, scan_dtype_t dt, scan_op_t op, scan_plan_t *pl
         plan->lds_bytes = element_lds_bytes(dt, op, p);
     else if (p.kernel == SCAN_KERNEL_COLUMNS_LOOKBACK)
         plan->lds_bytes = int64_t(kColTileWaves + 1) * kWave * p.vec * carry_bytes(dt, op) + 32;
+    else if (p.kernel == SCAN_KERNEL_PARTITION_RESIDENT)
+        plan->lds_bytes = int64_t(kResPartChunkRows) * (kResWaves - 1) * kWave * 4 * 6 +
+                          int64_t(kResCompactMaxRows) * (kResWaves - 1) * 4 + 32;
     else if (p.kernel == SCAN_KERNEL_COMPACT_RESIDENT)
         plan->lds_bytes = int64_t(kResCompactMaxRows) * (kResWaves - 1) * kWave * 4 * 2 +
                           int64_t(kResCompactMaxRows) * (kResWaves - 1) * 4 + 32;
@@ -1005,7 +1043,8 @@ int partition_if(const void *x, int64_t n, scan_dtype_t x_dtype, scan_cmp_t cmp,
     if (rc != SCAN_OK) return rc;
     PartitionArgs a{};
     a.pipe = pipe_args(p, ws, ws_bytes, tu);
-    a.pipe.words_used = uint64_t(p.num_tiles + count_wgs);  // tile descriptors, then the counts
+    if (p.kernel == SCAN_KERNEL_PARTITION)
+        a.pipe.words_used = uint64_t(p.num_tiles + count_wgs);  // tile descriptors, then the counts
     a.x = x;
     a.n = n;
     a.threshold = threshold_bits(x_dtype, cmp, threshold);
@@ -1015,6 +1054,7 @@ int partition_if(const void *x, int64_t n, scan_dtype_t x_dtype, scan_cmp_t cmp,
     a.count_base = uint32_t(p.num_tiles);
     a.count_wgs = uint32_t(count_wgs);
     a.count_chunk = count_chunk;
+    if (p.kernel == SCAN_KERNEL_PARTITION_RESIDENT) return find_partition_resident(x_dtype, cmp)(a, p.rows, s);
     const uint32_t grid_cap = tu.grid_blocks > 0 ? uint32_t(tu.grid_blocks) : 0u;
     return find_partition(x_dtype, cmp, p.block, p.rows, p.vec)(a, grid_cap, s);
 }

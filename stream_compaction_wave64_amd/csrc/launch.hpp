@@ -122,6 +122,11 @@ struct PartitionArgs {
 };
 using PartitionLaunch = int (*)(const PartitionArgs &, uint32_t grid_cap, hipStream_t);
 PartitionLaunch find_partition(scan_dtype_t x_dt, scan_cmp_t cmp, int block, int rows, int vec);
+// Resident partition (compact.hip): the resident compaction's tiles; the
+// count_* fields are unused.
+constexpr int kResPartChunkRows = 6;  // rows staged in LDS at a time (values and 16-bit indices: 135 KiB)
+using ResPartitionLaunch = int (*)(const PartitionArgs &, int rows, hipStream_t);
+ResPartitionLaunch find_partition_resident(scan_dtype_t x_dt, scan_cmp_t cmp);
 
 // ---------------------------------------------------------- large elements
 // Elements of W components scanned component-wise along the middle axis of

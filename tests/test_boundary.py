@@ -158,6 +158,10 @@ def test_plan_resident():
     assert binding.plan("compact", torch.int32, "sum", 1, 4096)["kernel"] == "compact_resident"
     assert binding.plan("compact", torch.int32, "sum", 1, 4097)["kernel"] == "compact"  # element-wide
     assert binding.plan("compact", torch.float32, "sum", 1, 10 ** 7, tuning={"grid_blocks": 4})["kernel"] == "compact"
+    p = binding.plan("partition", torch.float32, "sum", 1, 10 ** 7)  # one launch, no count pass
+    assert (p["kernel"], p["num_tiles"], p["launches"]) == ("partition_resident", 237, 1)
+    p = binding.plan("partition", torch.float32, "sum", 1, 10 ** 7, tuning={"grid_blocks": 4})
+    assert (p["kernel"], p["launches"]) == ("partition", 2)
 
 
 def test_plan_columns_single_pass():
@@ -255,7 +259,11 @@ def test_plan_partition():
     from stream_compaction_wave64_amd import binding
     import torch
     for dt in (torch.float32, torch.int32, torch.uint32):
-        for n in (1, 1000, 10 ** 7, 2 ** 31 - 1):
+        for n in (1000, 10 ** 7):  # whole vectors within 256 register tiles: one launch, no count words
+            p = binding.plan("partition", dt, "sum", 1, n)
+            assert p["kernel"] == "partition_resident" and p["launches"] == 1
+            assert p["workspace_bytes"] == 4096 + -(-p["num_tiles"] * 8 // 256) * 256
+        for n in (1, 1001, 10 ** 8, 2 ** 31 - 1):
             p = binding.plan("partition", dt, "sum", 1, n)
             assert p["kernel"] == "partition" and p["launches"] == 2
             # tile descriptors, then at most 1024 count words

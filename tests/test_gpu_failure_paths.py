@@ -207,3 +207,38 @@ def test_resident_compaction_failure_paths():
         c, got = run(None)
         assert sw.scan_workspace_error(ws) == 0
         assert c == ref.size and np.array_equal(got, ref)
+
+
+def test_resident_partition_failure_paths():
+    # The resident partition under the same forced conditions: dynamic
+    # claiming (flag bit 2), late publishers, a garbage epoch (flag bit 0).
+    import oracle
+    x, _ = inputs.compaction_inputs(3_000_000, seed=73)
+    xd = to_dev(x)
+    vals, idx, k = oracle.partition(x, "gt", 0.5)
+    assert sw.plan("partition", torch.float32, "sum", 1, x.size)["kernel"] == "partition_resident"
+
+    def run(tuning):
+        out, oi, count = sw.partition_if(xd, "gt", 0.5, tuning=tuning)
+        torch.cuda.synchronize()
+        return int(count.item()), to_host(out).view(np.uint32), to_host(oi)
+
+    def ok(res):
+        c, v, i = res
+        return c == k and np.array_equal(v, vals.view(np.uint32)) and np.array_equal(i, idx)
+
+    ws = torch.zeros(1 << 22, dtype=torch.uint8, device=DEV)
+    with _Installed(ws):
+        ws[128:132].view(torch.int32)[0] = -1
+        assert ok(run({"mode_limit": 8}))
+        assert sw.scan_workspace_error(ws) == 4
+        sw.scan_workspace_init(ws)
+        for stride, sleeps in DELAYS:
+            assert ok(run({"delay_stride": stride, "delay_sleeps": sleeps})), (stride, sleeps)
+        assert sw.scan_workspace_error(ws) == 0
+        ws[:16].view(torch.int32)[0] = 1 << 30
+        run({"spin_limit": 32})
+        assert sw.scan_workspace_error(ws) & 1
+        sw.scan_workspace_init(ws)
+        assert ok(run(None))
+        assert sw.scan_workspace_error(ws) == 0

@@ -146,3 +146,45 @@ def test_partition_special_floats(cmp):
     x[rng.integers(0, x.size, 5000)] = specials[rng.integers(0, specials.size, 5000)]
     for t in (0.0, float("-inf")):
         _check(x, cmp, t)
+
+
+def test_partition_resident():
+    # x of whole 128-bit vectors that fits one register tile per compute unit
+    # (at most 256 tiles of rows x 960 x 4 elements, rows <= 17) is
+    # partitioned in one launch: both sides of the capacity, single-row and
+    # ragged last tiles, comparisons, bit digits, closed forms, no index
+    # output, misaligned outputs.
+    cap = 256 * 17 * 3840
+    assert sw.plan("partition", torch.float32, "sum", 1, 4096)["kernel"] == "partition_resident"
+    assert sw.plan("partition", torch.float32, "sum", 1, cap)["kernel"] == "partition_resident"
+    assert sw.plan("partition", torch.float32, "sum", 1, cap + 4)["kernel"] == "partition"
+    assert sw.plan("partition", torch.float32, "sum", 1, 4097)["kernel"] == "partition"
+    for n in (4096, 256 * 3840, 256 * 3840 + 4, cap, cap + 4):
+        x, _ = inputs.compaction_inputs(n, seed=54)
+        _check(x)
+    rng = np.random.default_rng(55)
+    n = 3 * 3840 * 200 + 44
+    x = rng.random(n, dtype=np.float32)
+    x[::97] = np.float32(0.5)
+    for cmp in ("gt", "le", "eq", "ne"):
+        _check(x, cmp, 0.5)
+    _check(x, with_idx=False)
+    keys = rng.integers(0, 2 ** 32, 7 * 3840 * 255 + 3840 + 12, dtype=np.uint64).astype(np.uint32)
+    for dt in (np.int32, np.uint32):
+        for b in (0, 31):
+            _check(keys.view(dt), "bit_clear", b)
+    for f in (np.ones(8192, np.float32), np.zeros(8192, np.float32), np.tile(np.array([0, 1], np.float32), 4096)):
+        _check(f)
+    x, _ = inputs.compaction_inputs(1_000_000, seed=56)
+    vals, idx, k = oracle.partition(x, "gt", 0.5)
+    vbuf = torch.full((x.size + 8,), -7, dtype=torch.int32, device=DEV)
+    ibuf = torch.full((x.size + 8,), -7, dtype=torch.int32, device=DEV)
+    _, _, count = sw.partition_if(to_dev(x), "gt", 0.5, out=vbuf[1:1 + x.size].view(torch.float32),
+                                  out_idx=ibuf[3:3 + x.size])
+    torch.cuda.synchronize()
+    gv, gi = to_host(vbuf), to_host(ibuf)
+    assert int(count.item()) == k
+    assert np.array_equal(gv[1:1 + x.size].view(np.uint32), vals.view(np.uint32))
+    assert np.array_equal(gi[3:3 + x.size], idx)
+    assert (gv[:1] == -7).all() and (gv[1 + x.size:] == -7).all()
+    assert (gi[:3] == -7).all() and (gi[3 + x.size:] == -7).all()
