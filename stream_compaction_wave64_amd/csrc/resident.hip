@@ -30,8 +30,8 @@
 // the protocol its rows arrived about 3 us late; with the control wave last
 // in the workgroup its requests queued behind every data wave's loads (the
 // mode was known after 16 us instead of 11); with the row scans after the
-// barrier (which waits for every load) 21 rows of wave scans, about 3.5 us,
-// followed the loads instead of overlapping them.
+// barrier that waits for the protocol, 21 rows of wave scans (about 3.5 us)
+// started only once the protocol was done instead of overlapping it.
 //
 // This file is compiled once per element type (SW64_DT selects it).
 #include "launch.hpp"
