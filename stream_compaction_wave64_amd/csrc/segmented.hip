@@ -12,24 +12,25 @@
 // reduce-then-scan (The CUDA Handbook ch. 13 section 13.3.3), four launches:
 //   1. map: for every tile whose first element lies in a segment, that
 //      segment's index;
-//   2. reduce: each workgroup folds its chunk of tiles into one (flag,
-//      value) partial, and saves each tile's head bits;
+//   2. reduce: each workgroup finds its chunk's last head from the offsets
+//      and folds only the elements from there to the chunk's end into one
+//      (flag, value) partial (everything before a head is discarded);
 //   3. partials: one workgroup scans the partials in order into each chunk's
 //      exclusive prefix;
-//   4. rescan: each workgroup scans its chunk again, tile by tile, carrying
-//      the prefix into the elements before the first head it meets.
-// The reduce pass learns a tile's heads from the offsets: from the map it
-// reads the segments that can start inside the tile and marks their starts
-// in an LDS byte map, then saves them as bit planes (one bit per element)
-// that the rescan loads with the tile, so no per-element flag array is ever
-// materialised in HBM and the offsets are read once.  Traffic: two reads of
-// the data and one write, one read of the offsets, and the planes (an
-// eighth of a byte per element each way, stored in 32-bit halves).
+//   4. rescan: each workgroup scans its chunk, tile by tile, carrying the
+//      prefix into the elements before the first head it meets.
+// The rescan learns a tile's heads from the offsets: from the map it reads
+// the segments that can start inside the tile and marks their starts in an
+// LDS byte map, so no per-element flag array is ever materialised in HBM and
+// the offsets are read once.  Traffic: one read of the data (plus the
+// elements after each chunk's last head) and one write, one read of the
+// offsets.
 //
 // Workspace: the map (one 64-bit word per tile, the index as a value below
 // 2^32: a look-back descriptor reader sees such a word as unpublished, so it
-// may stay), the head planes (likewise below 2^32) and the chunk partials
-// (zeroed by the rescan, as the other reduce-then-scan kernels leave theirs).
+// may stay), the head planes of the single pass (likewise below 2^32) and
+// the chunk partials (zeroed by the rescan, as the other reduce-then-scan
+// kernels leave theirs).
 //
 // Compiled once per element type (SW64_DT).
 #include "launch.hpp"
@@ -170,6 +171,22 @@ struct SegTile {
             if constexpr (VEC == 4) bytes = *reinterpret_cast<const uint32_t *>(sh.heads + e);
             else if constexpr (VEC == 2) bytes = *reinterpret_cast<const uint16_t *>(sh.heads + e);
             else bytes = sh.heads[e];
+#pragma unroll
+            for (int c = 0; c < VEC; c++) head |= uint32_t(((bytes >> (8 * c)) & 0xffu) != 0u) << (r * VEC + c);
+        }
+    }
+
+    // This thread's head bits from an LDS byte map of the tile's elements
+    // (nonzero: the element starts a segment).
+    __device__ __forceinline__ void heads_from_map(const uint8_t *hm) {
+        head = 0;
+#pragma unroll
+        for (int r = 0; r < ROWS; r++) {
+            const int64_t e = elem(r);
+            uint32_t bytes;  // this thread's VEC head bytes of row r, one LDS read
+            if constexpr (VEC == 4) bytes = *reinterpret_cast<const uint32_t *>(hm + e);
+            else if constexpr (VEC == 2) bytes = *reinterpret_cast<const uint16_t *>(hm + e);
+            else bytes = hm[e];
 #pragma unroll
             for (int c = 0; c < VEC; c++) head |= uint32_t(((bytes >> (8 * c)) & 0xffu) != 0u) << (r * VEC + c);
         }
@@ -406,31 +423,61 @@ struct SegPartial {
     uint32_t f, pad;
 };
 
+// Pass 2.  A chunk's partial depends only on its elements from its last
+// head on: under the segmented operator a head discards everything before
+// it, so the partial is (1, the fold of the elements from the last head to
+// the chunk's end), or (0, the fold of the whole chunk) when no segment
+// starts in it.  The last head is the start of the last segment starting at
+// or before the chunk's last element; the offsets being non-decreasing, it
+// is found among the segments the map gives for the chunk's last tile (the
+// one holding its first element up to the one holding the next tile's), all
+// read at once.  Then only the elements from that head on are read: with
+// short segments a few per chunk instead of the whole chunk (Poisson(3)
+// segments of 3e7 fp32: the pass that folded every tile read all 120 MB at
+// 3.3 TB/s, 37.6 us).  The heads themselves are marked by the rescan.
 template <class T, class Op, int B, int R, int V>
 __global__ __launch_bounds__(B) void k_seg_reduce(SegArgs a) {
     using ST = SegTile<T, Op, B, R, V>;
     using C = typename ST::C;
-    __shared__ typename ST::Shared sh;
-    __shared__ typename ST::Marks mk;
-    __shared__ SegChunkMap cm;
+    __shared__ int64_t s_last;  // index of the last segment starting at or before the chunk's end, or -1
+    __shared__ C s_part[B / kWave];
     const uint64_t t0 = uint64_t(blockIdx.x) * a.chunk_tiles;
     const uint64_t t1 = t0 + a.chunk_tiles < a.num_tiles ? t0 + a.chunk_tiles : a.num_tiles;
-    cm.load(a, t0, t1);
-    SegVal<C> acc = seg_identity<Op, C>();
-    ST st;
-    for (uint64_t t = t0; t < t1; t++) {
-        const int64_t start = int64_t(t) * ST::TILE;
-        st.load(reinterpret_cast<const T *>(a.in) + start, a.n - start);
-        st.mark(mk, a, uint32_t(t), cm.get(a, t0, t1, t), cm.get(a, t0, t1, t + 1));
-        st.reduce(sh);
-        st.save_heads(a.heads + int64_t(t) * ST::kPlaneWords);
-        acc = seg_combine<Op, C>(acc, SegVal<C>{C(st.agg.v), st.agg.f});
-        __syncthreads();
+    const int64_t e0 = int64_t(t0) * ST::TILE;                                          // the chunk's start
+    const int64_t e1 = int64_t(t1) * ST::TILE < a.n ? int64_t(t1) * ST::TILE : a.n;  // and end
+    auto seg_at = [&](uint64_t t) -> int64_t {  // the map: segment holding tile t's first element (clamped)
+        const uint64_t v = t < a.num_tiles ? a.map[t] : uint64_t(a.nseg);
+        return int64_t(v < uint64_t(a.nseg) ? v : uint64_t(a.nseg));
+    };
+    if (threadIdx.x == 0) s_last = -1;
+    __syncthreads();
+    {
+        const int64_t lo = seg_at(t1 - 1), hi = seg_at(t1);  // candidates [lo, hi], within [0, nseg]
+        int64_t best = -1;
+        for (int64_t sidx = lo + threadIdx.x; sidx <= hi && sidx < a.nseg; sidx += B) {
+            if (int64_t(a.off[sidx]) <= e1 - 1) best = sidx;  // non-decreasing: the last such is the largest
+        }
+        const int64_t wb = wave_reduce<OpMax>(best);
+        if (lane_id() == 0 && wb >= 0) __hip_atomic_fetch_max(&s_last, wb, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
+    __syncthreads();
+    const int64_t sl = s_last;
+    const int64_t h = sl >= 0 ? int64_t(a.off[sl]) : -1;  // the last head at or before the chunk's end
+    const bool has = h >= e0 && h < e1;
+    const int64_t from = has ? h : e0;
+    const T *in = reinterpret_cast<const T *>(a.in);
+    C acc = Op::template identity<C>();
+#pragma unroll 4
+    for (int64_t i = from + threadIdx.x; i < e1; i += B) acc = Op::apply(acc, C(in[i]));
+    acc = wave_reduce<Op>(acc);
+    if (lane_id() == 0) s_part[threadIdx.x / kWave] = acc;
+    __syncthreads();
     if (threadIdx.x == 0) {
+        C v = Op::template identity<C>();
+        for (int w = 0; w < B / kWave; w++) v = Op::apply(v, s_part[w]);
         SegPartial<T, Op> *p = reinterpret_cast<SegPartial<T, Op> *>(a.partials);
-        p[blockIdx.x].v = acc.v;
-        p[blockIdx.x].f = acc.f;
+        p[blockIdx.x].v = v;
+        p[blockIdx.x].f = has ? 1u : 0u;
     }
 }
 
@@ -474,11 +521,20 @@ __global__ __launch_bounds__(kSegPartThreads) void k_seg_partials(SegArgs a) {
     }
 }
 
+// Pass 4.  The heads of up to kSegMarkTiles tiles are marked at once (one
+// batch of offset loads per group: marking tile by tile put a dependent round
+// trip and two barriers before every tile's scan), then each tile is scanned
+// with the carry and stored.
+constexpr int kSegMarkTiles = 8;
+
 template <class T, class Op, int B, int R, int V>
 __global__ __launch_bounds__(B) void k_seg_rescan(SegArgs a) {
     using ST = SegTile<T, Op, B, R, V>;
     using C = typename ST::C;
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
     __shared__ typename ST::Shared sh;
+    __shared__ alignas(16) uint8_t hm[kSegMarkTiles * ST::TILE];  // the group's heads, one byte per element
+    __shared__ SegChunkMap cm;
     __shared__ C s_carry;
     SegPartial<T, Op> *p = reinterpret_cast<SegPartial<T, Op> *>(a.partials);
     if (threadIdx.x == 0) s_carry = p[blockIdx.x].v;
@@ -487,16 +543,45 @@ __global__ __launch_bounds__(B) void k_seg_rescan(SegArgs a) {
     if (threadIdx.x == 0) p[blockIdx.x] = SegPartial<T, Op>{};  // leave the workspace zeroed
     const uint64_t t0 = uint64_t(blockIdx.x) * a.chunk_tiles;
     const uint64_t t1 = t0 + a.chunk_tiles < a.num_tiles ? t0 + a.chunk_tiles : a.num_tiles;
+    cm.load(a, t0, t1);
     ST st;
-    for (uint64_t t = t0; t < t1; t++) {
-        const int64_t start = int64_t(t) * ST::TILE;
-        st.load(reinterpret_cast<const T *>(a.in) + start, a.n - start);
-        st.load_heads(a.heads + int64_t(t) * ST::kPlaneWords);  // the reduce pass's marks
-        uint32_t cov;
-        st.scan(sh, a.exclusive != 0, cov);
-        st.store(reinterpret_cast<T *>(a.out) + start, a.n - start, carry, cov);
-        carry = st.agg.f ? C(st.agg.v) : Op::apply(carry, C(st.agg.v));
+    for (uint64_t g0 = t0; g0 < t1; g0 += kSegMarkTiles) {
+        const uint64_t g1 = g0 + kSegMarkTiles < t1 ? g0 + kSegMarkTiles : t1;
+        const int64_t eg0 = int64_t(g0) * ST::TILE;
+        const int64_t span = (int64_t(g1) * ST::TILE < a.n ? int64_t(g1) * ST::TILE : a.n) - eg0;  // elements in range
+        for (int i = threadIdx.x; i < int((g1 - g0) * ST::TILE / 16); i += B)
+            reinterpret_cast<u32x4 *>(hm)[i] = u32x4{0u, 0u, 0u, 0u};
         __syncthreads();
+        // the segments that can start in the group: the one holding its first
+        // element up to the one holding the next group's (clamped to nseg by
+        // the map), so invalid offsets give wrong results, never an access
+        // out of bounds
+        const uint64_t s0 = cm.get(a, t0, t1, g0), s1 = cm.get(a, t0, t1, g1);
+        const int32_t eg0_32 = int32_t(eg0);  // n <= INT32_MAX: offsets and group starts fit, so does their difference
+        for (uint64_t base = s0 + threadIdx.x; base <= s1; base += uint64_t(ST::kMarkBatch) * B) {
+            int32_t o[ST::kMarkBatch];
+#pragma unroll
+            for (int u = 0; u < ST::kMarkBatch; u++) {
+                const uint64_t sidx = base + uint64_t(u) * B;
+                o[u] = a.off[sidx <= s1 ? sidx : s1];
+            }
+#pragma unroll
+            for (int u = 0; u < ST::kMarkBatch; u++) {
+                const int32_t d = base + uint64_t(u) * B <= s1 ? o[u] - eg0_32 : -1;
+                if (d >= 0 && d < span) hm[d] = 1;
+            }
+        }
+        __syncthreads();
+        for (uint64_t t = g0; t < g1; t++) {
+            const int64_t start = int64_t(t) * ST::TILE;
+            st.load(reinterpret_cast<const T *>(a.in) + start, a.n - start);
+            st.heads_from_map(hm + (t - g0) * ST::TILE);
+            uint32_t cov;
+            st.scan(sh, a.exclusive != 0, cov);
+            st.store(reinterpret_cast<T *>(a.out) + start, a.n - start, carry, cov);
+            carry = st.agg.f ? C(st.agg.v) : Op::apply(carry, C(st.agg.v));
+            __syncthreads();
+        }
     }
 }
 
@@ -504,8 +589,8 @@ __global__ __launch_bounds__(B) void k_seg_rescan(SegArgs a) {
 // The same scan on the persistent look-back pipeline (pipeline.hpp): one
 // read and one write of the data.  The carry between tiles is a (head flag,
 // value) pair under the restarting operator, which the look-back combines in
-// tile order (kOrderedOp).  Heads come from a heads pass (the reduce pass's
-// marking without the data) as the same bit planes, laid out for the
+// tile order (kOrderedOp).  Heads come from a heads pass (the marking of the
+// reduce-then-scan rescan, without the data) as bit planes, laid out for the
 // pipeline's data threads; the map pass runs first as before.
 
 template <class BaseOp>
