@@ -19,6 +19,8 @@ pytestmark = pytest.mark.gpu
 
 DTYPES = [np.int32, np.uint32, np.int64, np.float32, np.float64]
 OPS = ["sum", "prod", "max", "min"]
+TORCH_OF = {np.int32: torch.int32, np.uint32: torch.uint32, np.int64: torch.int64, np.float32: torch.float32,
+            np.float64: torch.float64}
 CASES = 150
 
 
@@ -150,3 +152,53 @@ def test_random_packing_and_segments():
             torch.cuda.synchronize()
             assert_segscan_matches(x, ref_off, to_host(r), op, excl,
                                    what=f"case {case}: {np.dtype(dt).name} {op} excl={excl} nobj={nobj} {tuning}")
+
+
+def test_random_single_pass_paths():
+    # The one-step paths at random sizes: whole arrays and rows of 8 MiB up to
+    # the resident pass's capacity (most with whole 128-bit vectors, some
+    # not: those fall back to the pipeline), and column scans whose register
+    # tiles fit one per compute unit.  Every case against the oracle; the
+    # planner's choice is recorded so that the sweep keeps reaching them.
+    rng = np.random.default_rng(2030)
+    kernels = {}
+    for case in range(24):
+        dt = DTYPES[int(rng.integers(0, len(DTYPES)))]
+        op = OPS[int(rng.integers(0, len(OPS)))]
+        excl = bool(rng.integers(0, 2))
+        es = np.dtype(dt).itemsize
+        vec = 16 // es
+        cap = 256 * (17 if es == 4 else 21) * 960 * vec
+        outer = int(rng.integers(1, 4)) if rng.integers(0, 3) == 0 else 1
+        lo = -(-(8 << 20) // (es * outer))
+        length = int(rng.integers(lo, cap // outer + 1))
+        if rng.integers(0, 4):
+            length -= length % vec  # whole vectors (the resident pass)
+        kind = sw.plan("scan", TORCH_OF[dt], op, outer, length)["kernel"]
+        kernels[kind] = kernels.get(kind, 0) + 1
+        x = _values(dt, outer * length, 300 + case, op)
+        if outer == 1:
+            fn = sw.scan_exclusive if excl else sw.scan_inclusive
+            r = fn(to_dev(x), op=op)
+        else:
+            r = sw.scan_dim(to_dev(x.reshape(outer, length)), 1, op=op, exclusive=excl)
+        torch.cuda.synchronize()
+        assert_scan_matches(x, to_host(r).ravel(), op, excl, dims=(outer, length, 1),
+                            what=f"case {case}: {np.dtype(dt).name} {op} excl={excl} {outer}x{length} ({kind})")
+    for case in range(12):
+        dt = DTYPES[int(rng.integers(0, len(DTYPES)))]
+        op = OPS[int(rng.integers(0, len(OPS)))]
+        excl = bool(rng.integers(0, 2))
+        vec = 16 // np.dtype(dt).itemsize
+        tc = 64 * vec  # columns per strip
+        cols = vec * int(rng.integers(tc // (2 * vec), 4096 // vec + 1))
+        strips = -(-cols // tc)
+        rows = int(rng.integers(1, min(4096, 256 * 64 // strips) + 1))
+        kind = sw.plan("scan", TORCH_OF[dt], op, 1, rows, cols)["kernel"]
+        kernels[kind] = kernels.get(kind, 0) + 1
+        x = _values(dt, rows * cols, 400 + case, op).reshape(rows, cols)
+        r = sw.scan_dim(to_dev(x), 0, op=op, exclusive=excl)
+        torch.cuda.synchronize()
+        assert_scan_matches(x.ravel(), to_host(r).ravel(), op, excl, dims=(1, rows, cols),
+                            what=f"case {case}: {np.dtype(dt).name} {op} excl={excl} {rows}x{cols} dim 0 ({kind})")
+    assert kernels.get("resident", 0) >= 10 and kernels.get("columns_lookback", 0) >= 6, kernels
