@@ -71,23 +71,31 @@ struct ElemTile {
         return g;
     }
 
-    // Global -> LDS in the owner layout: access u of the tile (value u * LV)
-    // belongs to thread u / UPT at its slot (u % UPT) * LV.
+    // Global -> registers: access u = r * threads + thread of the tile
+    // (value u * LV), r < UPT; accesses past the range read zero.
     // AUX: the loads' cache policy (2: nontemporal; 0: the reduce pass, whose
     // data the rescan reads again soon after and may find in the caches).
     template <int AUX = 2>
-    __device__ __forceinline__ static void load_tile(const Geo &g, T *lds) {
+    __device__ __forceinline__ static void load_regs(const Geo &g, Acc (&x)[UPT]) {
 #pragma unroll
         for (int r = 0; r < UPT; r++) {
             const uint32_t u = uint32_t(r) * blockDim.x + threadIdx.x;
-            Acc x;
             if constexpr (LG == 16)
-                x = __builtin_bit_cast(Acc, __builtin_amdgcn_raw_buffer_load_b128(g.rs, u * 16u, 0, AUX));
+                x[r] = __builtin_bit_cast(Acc, __builtin_amdgcn_raw_buffer_load_b128(g.rs, u * 16u, 0, AUX));
             else if constexpr (LG == 8)
-                x = __builtin_bit_cast(Acc, __builtin_amdgcn_raw_buffer_load_b64(g.rs, u * 8u, 0, AUX));
+                x[r] = __builtin_bit_cast(Acc, __builtin_amdgcn_raw_buffer_load_b64(g.rs, u * 8u, 0, AUX));
             else
-                x = __builtin_bit_cast(Acc, __builtin_amdgcn_raw_buffer_load_b32(g.rs, u * 4u, 0, AUX));
-            *reinterpret_cast<Acc *>(lds + (u / UPT) * STRIDE + (u % UPT) * LV) = x;
+                x[r] = __builtin_bit_cast(Acc, __builtin_amdgcn_raw_buffer_load_b32(g.rs, u * 4u, 0, AUX));
+        }
+    }
+
+    // Registers -> LDS in the owner layout: access u belongs to thread
+    // u / UPT at its slot (u % UPT) * LV.
+    __device__ __forceinline__ static void regs_to_lds(const Acc (&x)[UPT], T *lds) {
+#pragma unroll
+        for (int r = 0; r < UPT; r++) {
+            const uint32_t u = uint32_t(r) * blockDim.x + threadIdx.x;
+            *reinterpret_cast<Acc *>(lds + (u / UPT) * STRIDE + (u % UPT) * LV) = x[r];
         }
     }
 
@@ -150,10 +158,14 @@ struct ElemTile {
         for (int c = 0; c < W; c++) acc[c] = cid;
         int64_t j0;
         const uint32_t nt = tiles_of(a, chunk, j0);
+        // the next tile's loads are in flight while this one is folded
+        Acc nx[UPT];
+        if (nt > 0) load_regs<0>(geo(a, a.in, seg, j0), nx);
         for (uint32_t k = 0; k < nt; k++) {
             const Geo g = geo(a, a.in, seg, j0 + k);
             if (k > 0) __syncthreads();  // previous tile's reads are done
-            load_tile<0>(g, lds);
+            regs_to_lds(nx, lds);
+            if (k + 1 < nt) load_regs<0>(geo(a, a.in, seg, j0 + k + 1), nx);
             __syncthreads();
             T v[VPT];
             read_own(g, lds, v);
@@ -179,9 +191,11 @@ struct ElemTile {
 
     // Pass 3: scan each tile of the chunk from the chunk's prefix.  The
     // tile's values stay in LDS, read twice by their owner thread: once for
-    // its W component totals, once to replace them by their results; only
-    // the W running offsets live in registers, and the chunk's W carries in
-    // LDS, so the pass keeps the occupancy that hides its memory latency.
+    // its W component totals, once to replace them by their results; the
+    // registers hold the W running offsets and the next tile's loads (issued
+    // as soon as this tile is in LDS, so a workgroup's tiles do not each wait
+    // a full load latency: 1e6 elements of 24 fp32, 65.9 -> 61.8 us per
+    // call), and the chunk's W carries sit in LDS.
     __device__ static void rescan(const ElemArgs &a) {
         extern __shared__ __align__(16) char smem[];
         T *lds = reinterpret_cast<T *>(smem);
@@ -198,10 +212,15 @@ struct ElemTile {
         int64_t j0;
         const uint32_t nt = tiles_of(a, chunk, j0);
         T *own = lds + threadIdx.x * STRIDE;
+        // the next tile's loads are in flight while this one is scanned and
+        // stored
+        Acc nx[UPT];
+        if (nt > 0) load_regs(geo(a, a.in, seg, j0), nx);
         for (uint32_t k = 0; k < nt; k++) {
             const Geo gi = geo(a, a.in, seg, j0 + k);
             __syncthreads();  // carry written; previous tile's stores have read LDS
-            load_tile(gi, lds);
+            regs_to_lds(nx, lds);
+            if (k + 1 < nt) load_regs(geo(a, a.in, seg, j0 + k + 1), nx);
             __syncthreads();
             // this thread's component totals (elements past the range: identity)
             T off[W];
