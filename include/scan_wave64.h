@@ -142,8 +142,10 @@ typedef struct {
                                   results carry a presence flag instead, so
                                   e.g. a sum of -0.0 values stays -0.0.
                                   Inclusive scans of whole arrays and of rows
-                                  (scan_inclusive, scan_dim with inner == 1,
-                                  look-back algorithm); anything else returns
+                                  (scan_inclusive, scan_dim with inner == 1;
+                                  single pass: the look-back pipeline, or the
+                                  resident pass where the plain scan takes
+                                  it); anything else returns
                                   SCAN_ERR_UNSUPPORTED, exclusive scans
                                   included (no value for element 0) */
     int32_t delay_stride;      /* test aid for the look-back's waits: with

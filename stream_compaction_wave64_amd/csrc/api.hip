@@ -96,6 +96,23 @@ ResLaunch find_resident(scan_dtype_t dt, scan_op_t op) {
     return nullptr;
 }
 
+ResLaunch find_resident_noid_i32(scan_op_t);
+ResLaunch find_resident_noid_u32(scan_op_t);
+ResLaunch find_resident_noid_i64(scan_op_t);
+ResLaunch find_resident_noid_f32(scan_op_t);
+ResLaunch find_resident_noid_f64(scan_op_t);
+
+ResLaunch find_resident_noid(scan_dtype_t dt, scan_op_t op) {
+    switch (dt) {
+    case SCAN_I32: return find_resident_noid_i32(op);
+    case SCAN_U32: return find_resident_noid_u32(op);
+    case SCAN_I64: return find_resident_noid_i64(op);
+    case SCAN_F32: return find_resident_noid_f32(op);
+    case SCAN_F64: return find_resident_noid_f64(op);
+    }
+    return nullptr;
+}
+
 ColSingleLaunch find_columns_single_i32(scan_op_t);
 ColSingleLaunch find_columns_single_u32(scan_op_t);
 ColSingleLaunch find_columns_single_i64(scan_op_t);
@@ -346,9 +363,10 @@ int plan_scan(scan_dtype_t dt, scan_op_t op, int64_t outer, int64_t len, bool al
     // Arrays that fit one register tile per compute unit: the resident single
     // pass, with the fewest rows per tile that keep the tiles within
     // kResMaxTiles (the most compute units reading).  Only for the default
-    // shape, without a grid cap, identity scans of 128-bit rows.
-    if (shape_free && tu.grid_blocks <= 0 && !tu.no_identity && vec_ok && outer * len * esize >= kResMinBytes &&
-        find_resident(dt, op) != nullptr) {
+    // shape, without a grid cap, scans of 128-bit rows (without an identity
+    // too: inclusive, as everywhere).
+    if (shape_free && tu.grid_blocks <= 0 && vec_ok && outer * len * esize >= kResMinBytes &&
+        (tu.no_identity ? find_resident_noid(dt, op) : find_resident(dt, op)) != nullptr) {
         const int64_t re = int64_t(kResWaves - 1) * kWave * (16 / esize);  // the data waves
         const int maxr = esize == 8 ? kResMaxRows8 : kResMaxRows4;
         for (int r = 1; r <= maxr; r++) {
@@ -770,7 +788,7 @@ int scan_common(const void *in, void *out, int64_t outer, int64_t len, int64_t i
     if (p.kernel == SCAN_KERNEL_RESIDENT) {
         if (total_out != nullptr && dt == SCAN_I32 && op == SCAN_OP_SUM)  // count-scan-emit's offsets
             return find_pack_resident()(a, p.rows, stream);
-        return find_resident(dt, op)(a, p.rows, stream);
+        return (tu.no_identity ? find_resident_noid(dt, op) : find_resident(dt, op))(a, p.rows, stream);
     }
     const uint32_t grid_cap = tu.grid_blocks > 0 ? uint32_t(tu.grid_blocks) : 0u;
     if (total_out != nullptr && dt == SCAN_I32 && op == SCAN_OP_SUM)  // count-scan-emit's offsets

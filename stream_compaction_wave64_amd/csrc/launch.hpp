@@ -39,6 +39,7 @@ constexpr int kResMaxRows4 = 17, kResMaxRows8 = 21;  // 68 and 84 data registers
 constexpr int64_t kResMaxTiles = 256;                // one per compute unit on MI355X
 using ResLaunch = int (*)(const ScanArgs &, int rows, hipStream_t);
 ResLaunch find_resident(scan_dtype_t dt, scan_op_t op);
+ResLaunch find_resident_noid(scan_dtype_t dt, scan_op_t op);  // inclusive, no identity, no total
 ResLaunch find_pack_resident();  // int32 sum, offsets kept cacheable
 
 // ---------------------------------------------------------- reduce-then-scan

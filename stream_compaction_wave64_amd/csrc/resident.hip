@@ -35,19 +35,28 @@
 //
 // This file is compiled once per element type (SW64_DT selects it).
 #include "launch.hpp"
+#include "noid.hpp"
 
 namespace sw64 {
 
-template <class T, class Op, int V, int MAXR, int OUT_AUX>
+// NOID: an inclusive scan that never uses the operator's identity (Op is
+// then wrapped in NoId, which has none): elements past the segment's end
+// are scanned as loaded (they reach only results past the end, which the
+// bounded stores drop, and the last tile's aggregate, which no tile
+// reads); a lane, a (row, wave) entry or a tile with nothing before it
+// skips the combination instead of taking an identity; the look-back
+// combines optional carries (Opt, "absent" being their only identity).
+template <class T, class Op0, int V, int MAXR, int OUT_AUX, bool NOID = false>
 __global__ __launch_bounds__(kResWaves *kWave) void k_resident(ScanArgs a, uint32_t rows) {
-    using C = typename Carry<T, Op>::type;
+    using Op = std::conditional_t<NOID, NoId<Op0>, Op0>;
+    using C = typename Carry<T, Op0>::type;
     using D = DescFor<T, C>;
     constexpr int NDW = kResWaves - 1;                       // data waves
     constexpr int RE = NDW * kWave * V;                      // elements per tile row
     constexpr int KE = (MAXR * NDW + kWave - 1) / kWave;     // (row, wave) totals per lane of the control wave
     static_assert(V * sizeof(T) == 16, "128-bit rows");
     __shared__ T ent[MAXR * NDW];        // (row, wave) totals, then their exclusive prefixes in the tile
-    __shared__ C s_pre;                  // the tile's exclusive prefix
+    __shared__ C s_pre;                  // the tile's exclusive prefix (NOID: none for a segment's first tile)
     __shared__ uint32_t s_epoch, s_tile;
     __shared__ uint64_t s_hw, s_cap;
     WsHeader *hdr = reinterpret_cast<WsHeader *>(a.pipe.ws);
@@ -58,7 +67,6 @@ __global__ __launch_bounds__(kResWaves *kWave) void k_resident(ScanArgs a, uint3
     const uint32_t dw = wr - 1;                                  // data wave index (data waves only)
     const uint32_t dt = uint32_t(threadIdx.x) - kWave;           // data thread index
     const uint32_t n = a.pipe.num_tiles, tps = a.pipe.tiles_per_seg;
-    const T id = Op::template identity<T>();
     rows = uniform(rows);
     const int64_t tile_elems = int64_t(rows) * RE;
     const T *in = reinterpret_cast<const T *>(a.in);
@@ -105,19 +113,31 @@ __global__ __launch_bounds__(kResWaves *kWave) void k_resident(ScanArgs a, uint3
             if (r < int(rows)) {
                 const int64_t e0 = int64_t(r) * RE + e_thread;
                 T inc[V];
-                T acc = id;
+                T acc = x[r].v[0];
 #pragma unroll
                 for (int c = 0; c < V; c++) {
-                    const T val = e0 + c < rem_ ? x[r].v[c] : id;
+                    T val = x[r].v[c];
+                    if constexpr (!NOID) val = e0 + c < rem_ ? val : Op::template identity<T>();
                     acc = c == 0 ? val : Op::apply(acc, val);
                     inc[c] = acc;
                 }
-                const T winc = wave_scan_incl<Op>(acc);
-                const T wex = wave_shr1(id, winc);
+                if constexpr (NOID) {
+                    // inclusive only; lane 0 has no lane before it
+                    const T winc = wave_scan_incl_noid<Op>(acc);
+                    const T wex = dpp_mov<kWaveShr1>(winc, winc);
 #pragma unroll
-                for (int c = 0; c < V; c++)
-                    x[r].v[c] = a.exclusive ? (c == 0 ? wex : Op::apply(wex, inc[c - 1])) : Op::apply(wex, inc[c]);
-                if (lane == kWave - 1) ent[r * NDW + dw] = winc;
+                    for (int c = 0; c < V; c++) x[r].v[c] = lane > 0 ? Op::apply(wex, inc[c]) : inc[c];
+                    if (lane == kWave - 1) ent[r * NDW + dw] = winc;
+                } else {
+                    const T id = Op::template identity<T>();
+                    const T winc = wave_scan_incl<Op>(acc);
+                    const T wex = wave_shr1(id, winc);
+#pragma unroll
+                    for (int c = 0; c < V; c++)
+                        x[r].v[c] =
+                            a.exclusive ? (c == 0 ? wex : Op::apply(wex, inc[c - 1])) : Op::apply(wex, inc[c]);
+                    if (lane == kWave - 1) ent[r * NDW + dw] = winc;
+                }
             }
         }
     };
@@ -169,23 +189,53 @@ __global__ __launch_bounds__(kResWaves *kWave) void k_resident(ScanArgs a, uint3
     if (ctrl) {
         const uint32_t ne = rows * NDW;
         T e[KE];
-        T acc = id;
+        T linc;
+        C agg;
+        if constexpr (NOID) {
+            // lanes past the last entry hold whatever they read; they sit
+            // above every lane with entries, so the inclusive scan carries
+            // nothing from them down, and the aggregate is the last such
+            // lane's result.  Entry 0 has nothing before it: its slot is left
+            // as it is (the data waves do not read it).
+            T acc = ent[uint32_t(lane) * KE < ne ? uint32_t(lane) * KE : 0u];
 #pragma unroll
-        for (int k = 0; k < KE; k++) {
-            const uint32_t i = uint32_t(lane) * KE + k;
-            e[k] = i < ne ? ent[i] : id;
-            acc = Op::apply(acc, e[k]);
-        }
-        const T linc = wave_scan_incl<Op>(acc);
-        T run = wave_shr1(id, linc);
+            for (int k = 0; k < KE; k++) {
+                const uint32_t i = uint32_t(lane) * KE + k;
+                e[k] = ent[i < ne ? i : 0u];
+                if (k > 0 && i < ne) acc = Op::apply(acc, e[k]);
+            }
+            linc = wave_scan_incl_noid<Op>(acc);
+            T run = dpp_mov<kWaveShr1>(linc, linc);
 #pragma unroll
-        for (int k = 0; k < KE; k++) {
-            const uint32_t i = uint32_t(lane) * KE + k;
-            if (i < ne) ent[i] = run;
-            run = Op::apply(run, e[k]);
+            for (int k = 0; k < KE; k++) {
+                const uint32_t i = uint32_t(lane) * KE + k;
+                if (i < ne) {
+                    if (i > 0) ent[i] = run;
+                    run = i > 0 ? Op::apply(run, e[k]) : e[k];
+                }
+            }
+            agg = C(wave_read(linc, int((ne - 1) / KE)));
+        } else {
+            const T id = Op::template identity<T>();
+            T acc = id;
+#pragma unroll
+            for (int k = 0; k < KE; k++) {
+                const uint32_t i = uint32_t(lane) * KE + k;
+                e[k] = i < ne ? ent[i] : id;
+                acc = Op::apply(acc, e[k]);
+            }
+            linc = wave_scan_incl<Op>(acc);
+            T run = wave_shr1(id, linc);
+#pragma unroll
+            for (int k = 0; k < KE; k++) {
+                const uint32_t i = uint32_t(lane) * KE + k;
+                if (i < ne) ent[i] = run;
+                run = Op::apply(run, e[k]);
+            }
+            agg = C(wave_read(linc, kWave - 1));
         }
-        const C agg = C(wave_read(linc, kWave - 1));
-        C pre = Op::template identity<C>();
+        C pre{};
+        if constexpr (!NOID) pre = Op::template identity<C>();
         if (tps > 1) {
             if (a.pipe.delay_stride > 0 && tile % a.pipe.delay_stride == a.pipe.delay_stride - 1) {
                 // a late publisher, so tests reach the look-back's re-polls
@@ -193,14 +243,24 @@ __global__ __launch_bounds__(kResWaves *kWave) void k_resident(ScanArgs a, uint3
             }
             if (lane == 0) D::publish(desc + uint64_t(tile) * D::kWords, epoch, kStateA, agg);
             if (j > 0) {
-                GapRead<C, D, kResMaxTiles / kWave> g;
-                g.issue(desc, int64_t(tile) - j, int64_t(tile));
-                pre = g.template finish<Op>(desc, epoch, hdr, a.pipe.spin_limit);
+                if constexpr (NOID) {
+                    // j > 0 earlier tiles, all published with a value
+                    GapRead<Opt<C>, OptDesc<D>, kResMaxTiles / kWave> g;
+                    g.issue(desc, int64_t(tile) - j, int64_t(tile));
+                    pre = g.template finish<OptOp<Op0>>(desc, epoch, hdr, a.pipe.spin_limit).v;
+                } else {
+                    GapRead<C, D, kResMaxTiles / kWave> g;
+                    g.issue(desc, int64_t(tile) - j, int64_t(tile));
+                    pre = g.template finish<Op>(desc, epoch, hdr, a.pipe.spin_limit);
+                }
             }
         }
         if (lane == 0) {
             s_pre = pre;
-            if (a.total_out != nullptr && j == tps - 1) reinterpret_cast<T *>(a.total_out)[seg] = T(Op::apply(pre, agg));
+            if constexpr (!NOID) {
+                if (a.total_out != nullptr && j == tps - 1)
+                    reinterpret_cast<T *>(a.total_out)[seg] = T(Op::apply(pre, agg));
+            }
         }
     }
     __syncthreads();
@@ -210,8 +270,19 @@ __global__ __launch_bounds__(kResWaves *kWave) void k_resident(ScanArgs a, uint3
         if (!ctrl && r < int(rows)) {
             const T eb = ent[r * NDW + dw];
             Vec<T, V> y;
+            if constexpr (NOID) {
+                // entry (0, 0) has nothing before it in the tile, and a
+                // segment's first tile has nothing before it
+                const bool has_eb = r > 0 || dw > 0;
 #pragma unroll
-            for (int c = 0; c < V; c++) y.v[c] = T(Op::apply(pre, C(Op::apply(eb, x[r].v[c]))));
+                for (int c = 0; c < V; c++) {
+                    const T t = has_eb ? Op::apply(eb, x[r].v[c]) : x[r].v[c];
+                    y.v[c] = j > 0 ? T(Op::apply(pre, C(t))) : t;
+                }
+            } else {
+#pragma unroll
+                for (int c = 0; c < V; c++) y.v[c] = T(Op::apply(pre, C(Op::apply(eb, x[r].v[c]))));
+            }
             // the row step in the vector offset, the scalar offset a constant
             // 0 (see the column single pass: 128-bit buffer stores with a
             // scalar-register offset lost their data registers)
@@ -225,40 +296,46 @@ __global__ __launch_bounds__(kResWaves *kWave) void k_resident(ScanArgs a, uint3
     if (tile == n - 1) end_call(hdr, epoch, s_hw, s_cap, a.pipe.words_used, a.pipe.ws_words, desc);
 }
 
-template <class T, class Op, int OUT_AUX>
+template <class T, class Op, int OUT_AUX, bool NOID = false>
 static int launch_resident_impl(const ScanArgs &a, int rows, hipStream_t s) {
     constexpr int V = 16 / int(sizeof(T));
     constexpr int MAXR = sizeof(T) == 8 ? kResMaxRows8 : kResMaxRows4;
     if (rows < 1 || rows > MAXR || a.pipe.num_tiles > uint32_t(kResMaxTiles)) return SCAN_ERR_UNSUPPORTED;
-    hipLaunchKernelGGL((k_resident<T, Op, V, MAXR, OUT_AUX>), dim3(a.pipe.num_tiles), dim3(kResWaves * kWave), 0, s,
-                       a, uint32_t(rows));
+    if (NOID && (a.exclusive || a.total_out != nullptr)) return SCAN_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL((k_resident<T, Op, V, MAXR, OUT_AUX, NOID>), dim3(a.pipe.num_tiles), dim3(kResWaves * kWave), 0,
+                       s, a, uint32_t(rows));
     return hipGetLastError() == hipSuccess ? SCAN_OK : SCAN_ERR_HIP;
 }
 
-template <class T>
+template <class T, bool NOID = false>
 static ResLaunch pick_resident(scan_op_t op) {
     switch (op) {
-    case SCAN_OP_SUM: return &launch_resident_impl<T, OpSum, 2>;
-    case SCAN_OP_PROD: return &launch_resident_impl<T, OpProd, 2>;
-    case SCAN_OP_MAX: return &launch_resident_impl<T, OpMax, 2>;
-    case SCAN_OP_MIN: return &launch_resident_impl<T, OpMin, 2>;
+    case SCAN_OP_SUM: return &launch_resident_impl<T, OpSum, 2, NOID>;
+    case SCAN_OP_PROD: return &launch_resident_impl<T, OpProd, 2, NOID>;
+    case SCAN_OP_MAX: return &launch_resident_impl<T, OpMax, 2, NOID>;
+    case SCAN_OP_MIN: return &launch_resident_impl<T, OpMin, 2, NOID>;
     }
     return nullptr;
 }
 
 #if SW64_DT == 0
 ResLaunch find_resident_i32(scan_op_t op) { return pick_resident<int32_t>(op); }
+ResLaunch find_resident_noid_i32(scan_op_t op) { return pick_resident<int32_t, true>(op); }
 // count-scan-emit's offsets: stores with the default cache policy, since the
 // emit kernel reads them next
 ResLaunch find_pack_resident() { return &launch_resident_impl<int32_t, OpSum, 0>; }
 #elif SW64_DT == 1
 ResLaunch find_resident_u32(scan_op_t op) { return pick_resident<uint32_t>(op); }
+ResLaunch find_resident_noid_u32(scan_op_t op) { return pick_resident<uint32_t, true>(op); }
 #elif SW64_DT == 2
 ResLaunch find_resident_i64(scan_op_t op) { return pick_resident<int64_t>(op); }
+ResLaunch find_resident_noid_i64(scan_op_t op) { return pick_resident<int64_t, true>(op); }
 #elif SW64_DT == 3
 ResLaunch find_resident_f32(scan_op_t op) { return pick_resident<float>(op); }
+ResLaunch find_resident_noid_f32(scan_op_t op) { return pick_resident<float, true>(op); }
 #elif SW64_DT == 4
 ResLaunch find_resident_f64(scan_op_t op) { return pick_resident<double>(op); }
+ResLaunch find_resident_noid_f64(scan_op_t op) { return pick_resident<double, true>(op); }
 #else
 #error "SW64_DT must select an element type (0..4)"
 #endif

@@ -145,9 +145,13 @@ def test_plan_resident():
     assert binding.plan("scan", torch.int64, "max", 1, cap8 + 2)["kernel"] == "lookback"
     p = binding.plan("scan", torch.float32, "sum", 4, 1 << 20)    # segments: 4 x 55 tiles of 5 rows
     assert (p["kernel"], p["num_tiles"], p["items_per_thread"]) == ("resident", 220, 20)
-    for tu in ({"grid_blocks": 8}, {"block_size": 768, "items_per_thread": 28}, {"no_identity": 1},
-               {"algo": "reduce_then_scan"}):
+    for tu in ({"grid_blocks": 8}, {"block_size": 768, "items_per_thread": 28}, {"algo": "reduce_then_scan"}):
         assert binding.plan("scan", torch.float32, "sum", 1, 10 ** 7, tuning=tu)["kernel"] != "resident", tu
+    # inclusive scans without an identity take it too (Optional partials)
+    p = binding.plan("scan", torch.float32, "sum", 1, 10 ** 7, tuning={"no_identity": 1})
+    assert (p["kernel"], p["num_tiles"], p["items_per_thread"]) == ("resident", 237, 44)
+    assert binding.plan("scan", torch.float32, "sum", 1, 10 ** 7,
+                        tuning={"no_identity": 1, "grid_blocks": 8})["kernel"] == "lookback"
     assert binding.plan("pack", torch.int32, "sum", 1, 10 ** 7)["kernel"] == "pack"
     # compaction: the same tiles (rows of 960 x 4 keys, at most 17 rows so the
     # tile-local indices fit 16 bits), at any size of whole 128-bit vectors

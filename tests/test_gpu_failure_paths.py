@@ -166,7 +166,20 @@ def test_resident_pass_failure_paths():
                 r = fn(fd, tuning={"delay_stride": stride, "delay_sleeps": sleeps})
                 torch.cuda.synchronize()
                 assert_scan_matches(f, to_host(r), "sum", excl, what=f"late publishers {stride} {sleeps}")
+            # without an identity: the look-back's optional carries re-polled
+            r = sw.scan_inclusive(fd, tuning={"delay_stride": stride, "delay_sleeps": sleeps, "no_identity": 1})
+            torch.cuda.synchronize()
+            assert_scan_matches(f, to_host(r), "sum", False, what=f"no identity, late {stride} {sleeps}", noid=True)
         assert sw.scan_workspace_error(ws) == 0
+        # without an identity under dynamic claiming (each workgroup scans the
+        # tile it claims, which need not be its own)
+        assert sw.plan("scan", torch.int32, "max", 1, x.size, tuning={"no_identity": 1})["kernel"] == "resident"
+        ws[128:132].view(torch.int32)[0] = -1
+        r = sw.scan_inclusive(xd, op="max", tuning={"mode_limit": 8, "no_identity": 1})
+        torch.cuda.synchronize()
+        assert sw.scan_workspace_error(ws) == 4
+        assert_scan_matches(x, to_host(r), "max", False, what="no identity, dynamic", noid=True)
+        sw.scan_workspace_init(ws)
         ws[:16].view(torch.int32)[0] = 1 << 30
         sw.scan_inclusive(xd, tuning={"spin_limit": 32})
         torch.cuda.synchronize()

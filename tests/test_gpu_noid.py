@@ -5,8 +5,10 @@ cumsum row), against the oracle's scan_noid.
 
 Sizes span one partial tile, tile boundaries, several tiles with a ragged
 tail and many tiles; every dtype x op; the default, small-array, short-row
-and one-row tile shapes; misaligned (element-wide) data; rows of 2-D arrays;
-small persistent grids; the fp32 1e7 config.  Negative zeros tell the two
+and one-row tile shapes of the look-back pipeline, and the resident single
+pass (arrays of 8 MiB and more that fit one register tile per compute unit,
+the fp32 1e7 config among them); misaligned (element-wide) data; rows of 2-D
+arrays; small persistent grids.  Negative zeros tell the two
 paths apart: -0.0 + -0.0 = -0.0 but 0.0 + -0.0 = +0.0, so a sum of negative
 zeros stays -0.0 everywhere only if no identity enters any partial result
 (thread, wave, workgroup, look-back carry)."""
@@ -61,7 +63,9 @@ def test_noid_parity_planner_shapes(dt, op):
 @pytest.mark.parametrize("dt", DTYPES, ids=lambda d: np.dtype(d).name)
 @pytest.mark.parametrize("op", OPS)
 def test_noid_parity_default_shape_and_small_tiles(dt, op):
-    big = sw.plan("scan", TORCH[np.dtype(dt)], op, 1, 10 ** 7, tuning=NOID)
+    # the pipeline's default shape (1e8 elements exceed the resident pass)
+    big = sw.plan("scan", TORCH[np.dtype(dt)], op, 1, 10 ** 8, tuning=NOID)
+    assert big["kernel"] == "lookback"
     default = {"block_size": big["block_size"], "items_per_thread": big["items_per_thread"]}
     tile = big["tile_elems"]
     for i, n in enumerate([tile - 4, tile + 4, 40 * tile + 8]):
@@ -137,9 +141,41 @@ def test_noid_rows(dt):
 
 def test_noid_fp32_1e7_config():
     # the pages' "cumsum F32 1e7, no neutral" row, on the seeded uniform [0,1)
+    assert sw.plan("scan", torch.float32, "sum", 1, 10 ** 7, tuning=NOID)["kernel"] == "resident"
     x = inputs.f32_uniform_01(10 ** 7, seed=1)
     got = _run(x, "sum")
     assert_scan_matches(x, got, "sum", False, what="fp32 1e7 no neutral", noid=True)
+
+
+@pytest.mark.parametrize("dt", DTYPES, ids=lambda d: np.dtype(d).name)
+@pytest.mark.parametrize("op", OPS)
+def test_noid_resident_pass(dt, op):
+    # The resident single pass without an identity: from its smallest array
+    # (8 MiB) to its capacity (256 tiles of 17 rows of 960 x 4 elements, or
+    # 21 rows of 960 x 2), tile ends ragged inside a row; rows of 2-D arrays,
+    # several tiles per row and one tile per row (no row has a prefix).
+    isz = np.dtype(dt).itemsize
+    vec = 16 // isz
+    cap = 256 * (17 if vec == 4 else 21) * 960 * vec
+    sizes = [(8 << 20) // isz, 3_000_000 + 4 * vec]
+    if op == "sum":
+        sizes += [cap - 7 * vec, cap]
+    for i, n in enumerate(sizes):
+        assert sw.plan("scan", TORCH[np.dtype(dt)], op, 1, n, tuning=NOID)["kernel"] == "resident", n
+        x = _input(dt, n, 1100 + i, op)
+        assert_scan_matches(x, _run(x, op), op, False, what=f"n={n}", noid=True)
+    for shape in ((3, 1_000_000 + 4 * vec), (200, 10_500 * 4 // vec)):
+        assert sw.plan("scan", TORCH[np.dtype(dt)], op, shape[0], shape[1], tuning=NOID)["kernel"] == "resident"
+        x = _input(dt, shape[0] * shape[1], sum(shape), op).reshape(shape)
+        res = sw.scan_dim(to_dev(x), dim=1, op=op, tuning=NOID)
+        torch.cuda.synchronize()
+        assert_scan_matches(x, to_host(res), op, False, dims=(shape[0], shape[1], 1), what=f"{shape}", noid=True)
+    if op == "sum" and np.issubdtype(dt, np.floating):
+        # no identity enters any partial result: -0.0 everywhere stays -0.0
+        for shape in ((1, 3_000_000 + 4 * vec), (200, 10_500 * 4 // vec)):
+            z = np.full(shape, -0.0, dtype=dt)
+            res = to_host(sw.scan_dim(to_dev(z), dim=1, tuning=NOID))
+            assert np.all(res == 0) and np.all(np.signbit(res)), f"{shape}: a +0.0 appeared"
 
 
 def test_noid_unsupported_forms():
