@@ -173,8 +173,10 @@ typedef enum {
                                          loaded once, every earlier tile's aggregate read in one round trip */
     SCAN_KERNEL_COMPACT_RESIDENT = 11, /* compaction of such arrays in the same way: counts by ballots, selected
                                           indices staged in LDS, one contiguous range written per tile */
-    SCAN_KERNEL_PARTITION_RESIDENT = 12 /* stable partition of such arrays in one launch: every tile reads all
-                                           tiles' counts, each element goes straight to its slot */
+    SCAN_KERNEL_PARTITION_RESIDENT = 12, /* stable partition of such arrays in one launch: every tile reads all
+                                            tiles' counts, each element goes straight to its slot */
+    SCAN_KERNEL_ROWS = 13                /* many rows that each fit one tile: one workgroup per row, no
+                                            workspace traffic (scan_dim along the contiguous axis) */
 } scan_kernel_t;
 
 typedef struct {

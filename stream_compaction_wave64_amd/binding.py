@@ -24,7 +24,7 @@ CMPS = {"gt": 0, "ge": 1, "lt": 2, "le": 3, "eq": 4, "ne": 5, "bit_clear": 6, "b
 CALLS = {"scan": 0, "compact": 1, "pack": 2, "partition": 3, "segmented": 4}
 KERNELS = {0: "none", 1: "lookback", 2: "reduce_then_scan", 3: "element", 4: "columns", 5: "compact",
            6: "pack", 7: "partition", 8: "segmented", 9: "columns_lookback", 10: "resident",
-           11: "compact_resident", 12: "partition_resident"}
+           11: "compact_resident", 12: "partition_resident", 13: "rows"}
 
 
 class ScanError(RuntimeError):

@@ -96,6 +96,23 @@ ResLaunch find_resident(scan_dtype_t dt, scan_op_t op) {
     return nullptr;
 }
 
+RowsLaunch find_rows_i32(scan_op_t, int);
+RowsLaunch find_rows_u32(scan_op_t, int);
+RowsLaunch find_rows_i64(scan_op_t, int);
+RowsLaunch find_rows_f32(scan_op_t, int);
+RowsLaunch find_rows_f64(scan_op_t, int);
+
+RowsLaunch find_rows(scan_dtype_t dt, scan_op_t op, int rows) {
+    switch (dt) {
+    case SCAN_I32: return find_rows_i32(op, rows);
+    case SCAN_U32: return find_rows_u32(op, rows);
+    case SCAN_I64: return find_rows_i64(op, rows);
+    case SCAN_F32: return find_rows_f32(op, rows);
+    case SCAN_F64: return find_rows_f64(op, rows);
+    }
+    return nullptr;
+}
+
 ResLaunch find_resident_noid_i32(scan_op_t);
 ResLaunch find_resident_noid_u32(scan_op_t);
 ResLaunch find_resident_noid_i64(scan_op_t);
@@ -381,6 +398,31 @@ int plan_scan(scan_dtype_t dt, scan_op_t op, int64_t outer, int64_t len, bool al
                 p.num_tiles = outer * tps;
                 p.rts_blocks = p.rts_chunk = 0;
                 p.ws_bytes = kHeader + round_up(size_t(p.num_tiles) * p.carry_words * 8, 256);
+                p.launches = 1;
+                return SCAN_OK;
+            }
+        }
+    }
+    // Many rows that each fit one tile of the rows kernel (256 threads x 1,
+    // 2, 4 or 8 rows of 128-bit vectors, the fewest that hold a row; rows of
+    // at least one wave's vectors): one workgroup per row and no look-back.
+    // Identity scans of the default shape without a grid cap; two rows or
+    // more, so that count-scan-emit's single array keeps its total.
+    if (shape_free && tu.grid_blocks <= 0 && !tu.no_identity && vec_ok && outer >= 2 &&
+        len >= int64_t(kWave) * (16 / esize)) {
+        for (int r : {1, 2, 4, 8}) {
+            const int64_t t = int64_t(kRowsBlock) * r * (16 / esize);
+            if (len <= t && find_rows(dt, op, r) != nullptr) {
+                p.kernel = SCAN_KERNEL_ROWS;
+                p.block = kRowsBlock;
+                p.rows = r;
+                p.vec = 16 / esize;
+                p.tile = t;
+                p.tiles_per_seg = 1;
+                p.num_tiles = outer;
+                p.carry_words = 0;
+                p.rts_blocks = p.rts_chunk = 0;
+                p.ws_bytes = 0;  // no workspace
                 p.launches = 1;
                 return SCAN_OK;
             }
@@ -761,6 +803,16 @@ int scan_common(const void *in, void *out, int64_t outer, int64_t len, int64_t i
     TilePlan p;
     int rc = plan_scan(dt, op, outer, len, aligned16(in, out), tu, p);
     if (rc != SCAN_OK) return rc;
+    if (p.kernel == SCAN_KERNEL_ROWS) {  // no workspace
+        if (total_out != nullptr) return SCAN_ERR_UNSUPPORTED;
+        RowsArgs r{};
+        r.in = in;
+        r.out = out;
+        r.len = len;
+        r.rows = uint64_t(outer);
+        r.exclusive = exclusive ? 1 : 0;
+        return find_rows(dt, op, p.rows)(r, stream);
+    }
     rc = check_ws(ws, ws_bytes, p.ws_bytes);
     if (rc != SCAN_OK) return rc;
     if (p.kernel == SCAN_KERNEL_RTS) {

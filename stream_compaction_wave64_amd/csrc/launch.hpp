@@ -42,6 +42,20 @@ ResLaunch find_resident(scan_dtype_t dt, scan_op_t op);
 ResLaunch find_resident_noid(scan_dtype_t dt, scan_op_t op);  // inclusive, no identity, no total
 ResLaunch find_pack_resident();  // int32 sum, offsets kept cacheable
 
+// Many rows that each fit one tile (rows.hip): one workgroup of kRowsBlock
+// threads per row, ROWS (1, 2, 4 or 8) tile rows of kRowsBlock x vec
+// elements; rows of whole 128-bit vectors.
+constexpr int kRowsBlock = 256;
+struct RowsArgs {
+    const void *in;
+    void *out;
+    int64_t len;        // elements per row (a multiple of the vector width)
+    uint64_t rows;      // rows (one workgroup each)
+    int32_t exclusive;  // 0 inclusive, 1 exclusive
+};
+using RowsLaunch = int (*)(const RowsArgs &, hipStream_t);
+RowsLaunch find_rows(scan_dtype_t dt, scan_op_t op, int rows);
+
 // ---------------------------------------------------------- reduce-then-scan
 // Three launches over `blocks` workgroups, each owning `chunk_tiles`
 // consecutive tiles of block*rows*vec elements: reduce each chunk into a

@@ -76,8 +76,8 @@ def test_plan_fp32_metric_shape():
 def test_plan_segments_and_types():
     from stream_compaction_wave64_amd import binding
     import torch
-    p = binding.plan("scan", torch.int32, "sum", 4096, 4096)
-    assert p["num_tiles"] == 4096 * -(-4096 // p["tile_elems"])
+    p = binding.plan("scan", torch.int32, "sum", 64, 20_000)
+    assert p["kernel"] == "lookback" and p["num_tiles"] == 64 * -(-20_000 // p["tile_elems"])
     assert p["carry_words"] == 1
     p = binding.plan("scan", torch.float64, "max", 1, 10 ** 7)
     assert p["carry_words"] == 2 and p["vec"] == 2
@@ -90,6 +90,35 @@ def test_plan_segments_and_types():
     assert p["tile_elems"] == 256 * 4
     with pytest.raises(binding.ScanError):
         binding.plan("scan", torch.float32, "sum", 1, 1000, tuning={"block_size": 192, "items_per_thread": 4})
+
+
+def test_plan_rows_that_fit_one_tile():
+    # Two or more rows of whole 128-bit vectors, each at least one wave's
+    # vectors and at most 256 threads x 8 rows of them: one workgroup per row
+    # (the fewest tile rows that hold it), no workspace, one launch.
+    from stream_compaction_wave64_amd import binding
+    import torch
+    p = binding.plan("scan", torch.float32, "sum", 4096, 4096)
+    assert (p["kernel"], p["block_size"], p["items_per_thread"], p["num_tiles"], p["workspace_bytes"],
+            p["launches"]) == ("rows", 256, 16, 4096, 0, 1)
+    for dt, vec in ((torch.float32, 4), (torch.int32, 4), (torch.float64, 2), (torch.int64, 2)):
+        for r in (1, 2, 4, 8):
+            for length in (256 * (r // 2) * vec + vec, 256 * r * vec):
+                if length < 64 * vec:
+                    continue
+                p = binding.plan("scan", dt, "max", 3, length)
+                assert (p["kernel"], p["items_per_thread"]) == ("rows", r * vec), (dt, r, length)
+        assert binding.plan("scan", dt, "sum", 3, 2048 * vec + vec)["kernel"] == "lookback"  # longer than 8 rows
+        assert binding.plan("scan", dt, "sum", 3, 64 * vec - vec)["kernel"] == "lookback"   # under one wave
+        assert binding.plan("scan", dt, "sum", 3, 4096 + 1)["kernel"] == "lookback"         # not whole vectors
+    assert binding.plan("scan", torch.float32, "sum", 1, 4096)["kernel"] == "lookback"        # one array
+    for tu in ({"grid_blocks": 8}, {"block_size": 512, "items_per_thread": 8}, {"no_identity": 1},
+               {"algo": "reduce_then_scan"}):
+        if tu.get("algo"):
+            with pytest.raises(binding.ScanError):  # reduce-then-scan: whole arrays only
+                binding.plan("scan", torch.float32, "sum", 4096, 4096, tuning=tu)
+            continue
+        assert binding.plan("scan", torch.float32, "sum", 4096, 4096, tuning=tu)["kernel"] == "lookback", tu
 
 
 def test_plan_small_arrays_take_short_tiles():

@@ -7,7 +7,7 @@ import torch
 
 import stream_compaction_wave64_amd as sw
 from stream_compaction_wave64_amd import inputs
-from gpu_util import DEV, assert_scan_matches, to_dev, to_host
+from gpu_util import DEV, TORCH, assert_scan_matches, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -165,3 +165,41 @@ def test_columns_reduce_then_scan_on_request():
     r = sw.scan_dim(to_dev(x), 1, tuning={"algo": "reduce_then_scan"})
     torch.cuda.synchronize()
     assert_scan_matches(x.ravel(), to_host(r).ravel(), "sum", False, dims=(1, 4096, 4096))
+
+
+@pytest.mark.parametrize("dt", [np.float32, np.float64, np.int32, np.uint32, np.int64], ids=lambda d: np.dtype(d).name)
+@pytest.mark.parametrize("op", ["sum", "prod", "max", "min"])
+def test_rows_kernel_one_workgroup_per_row(dt, op):
+    # Rows that each fit one tile of the rows kernel (256 threads x 1, 2, 4 or
+    # 8 rows of 128-bit vectors): every tile-row count at a full tile and just
+    # past the previous one (a ragged end inside a tile row), the shortest row
+    # it takes (one wave's vectors), inclusive and exclusive, in place, and a
+    # 3-D array scanned along its last axis.
+    vec = 16 // np.dtype(dt).itemsize
+    rng = np.random.default_rng(91)
+    lengths = [64 * vec, 256 * vec - vec, 256 * vec, 256 * vec + vec, 512 * vec, 1024 * vec - vec, 1024 * vec,
+               1024 * vec + vec, 2048 * vec]
+    for i, length in enumerate(lengths):
+        rows = 37 if length > 1024 * vec else 301
+        assert sw.plan("scan", TORCH[np.dtype(dt)], op, rows, length)["kernel"] == "rows"
+        if op == "prod" and np.issubdtype(dt, np.floating):
+            x = (1.0 + (rng.random((rows, length)) - 0.5) * 0.002).astype(dt)
+        elif np.issubdtype(dt, np.floating):
+            x = (2 * rng.random((rows, length)) - 1).astype(dt)
+        else:
+            x = rng.integers(-9 if dt != np.uint32 else 0, 10, (rows, length)).astype(dt)
+        for excl in (False, True):
+            _check(x, 1, op, excl)
+    # in place: each row is read whole before any of it is written
+    x = inputs.generic(dt, 129 * 1024, 92, "wide" if np.issubdtype(dt, np.integer) else "default")
+    x = x.reshape(129, 1024)
+    xd = to_dev(x)
+    sw.scan_dim(xd, 1, op=op, out=xd)
+    torch.cuda.synchronize()
+    assert_scan_matches(x.ravel(), to_host(xd).ravel(), op, False, dims=(129, 1024, 1), what="in place")
+    x3 = x.reshape(3, 43, 1024)
+    _check(x3, 2, op, False)
+    # thousands of workgroups
+    x = inputs.generic(dt, 2049 * 64 * vec, 93, "wide" if np.issubdtype(dt, np.integer) else "default")
+    _check(x.reshape(2049, 64 * vec), 1, op, op == "max")
+

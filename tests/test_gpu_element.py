@@ -103,3 +103,32 @@ def test_misaligned_struct_rows_use_element_wide_access():
     r = sw.scan_inclusive(xd, width=8)
     torch.cuda.synchronize()
     assert_scan_matches(x.ravel(), to_host(r).ravel(), "sum", False, dims=(1, 10_001, 8))
+
+
+def test_element_calls_leave_workspace_untagged():
+    # The element partials share the workspace's descriptor area: after
+    # element scans of every carry width and operator (and exclusive scans,
+    # and segments), a look-back scan on the same workspace must see no
+    # leftover word that reads as published.
+    follow = inputs.generic(np.int32, 2_000_003, 83, "wide")
+    fd = to_dev(follow)
+    cases = [(np.float32, 8, 1_000_003, "sum", False), (np.float64, 4, 700_001, "sum", True),
+             (np.int64, 4, 300_007, "max", True), (np.int32, 8, 500_001, "min", False),
+             (np.float32, 8, 500_003, "prod", False), (np.float32, 3, 400_009, "sum", True),
+             (np.float64, 17, 100_003, "sum", False)]
+    for dt, w, n, op, excl in cases:
+        x = _struct_input(dt, n, w, 84 + w, op)
+        fn = sw.scan_exclusive if excl else sw.scan_inclusive
+        r = fn(to_dev(x), op=op, width=w)
+        torch.cuda.synchronize()
+        assert_scan_matches(x.ravel(), to_host(r).ravel(), op, excl, dims=(1, n, w), what=f"{dt} w={w} n={n} {op}")
+        f = sw.scan_inclusive(fd)
+        torch.cuda.synchronize()
+        assert_scan_matches(follow, to_host(f), "sum", False, what=f"look-back after {dt} w={w} n={n}")
+    xs = _struct_input(np.float32, 4 * 250_000, 4, 85, "sum").reshape(4, 250_000, 4)
+    r = sw.scan_dim(to_dev(xs), 1)
+    torch.cuda.synchronize()
+    assert_scan_matches(xs.ravel(), to_host(r).ravel(), "sum", False, dims=xs.shape, what="4 segments")
+    f = sw.scan_inclusive(fd)
+    torch.cuda.synchronize()
+    assert_scan_matches(follow, to_host(f), "sum", False, what="look-back after segments")
