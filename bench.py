@@ -365,7 +365,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(this build has no multi-GPU path)", file=sys.stderr)
+              "(the library has no multi-GPU path)", file=sys.stderr)
         return 2
     import torch
     import stream_compaction_wave64_amd as sw

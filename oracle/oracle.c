@@ -23,7 +23,7 @@
  *    large element types"), description, first bullet and first commit
  *    message: the block-size rule for large element types.
  *
- * Readings of points the pages leave open (each is listed in the design doc):
+ * Readings of points the pages leave open:
  *  - integer arithmetic wraps modulo 2^w (two's complement), done here in
  *    unsigned arithmetic of the same width;
  *  - fp32 inputs are accumulated in fp64 and the fp64 prefix is returned;
