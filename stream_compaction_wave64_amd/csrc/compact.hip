@@ -378,6 +378,40 @@ __global__ __launch_bounds__(kResWaves *kWave) void k_compact_resident(A a, uint
     }
     __syncthreads();
     if constexpr (PART) {
+        const int64_t rem = a.n - start;
+        const int32_t nsel = s_nsel;
+        // chunk [c0, c1) of the tile's rows: selected before it (in the tile),
+        // selected and rejected in it, rejected before it
+        auto chunk = [&](int c0, int &c1, int32_t &sel0, int32_t &nsc, int32_t &nrc, int32_t &rej_b) {
+            c1 = c0 + CH < int(rows) ? c0 + CH : int(rows);
+            sel0 = ent[c0 * NDW];
+            const int32_t sel1 = c1 < int(rows) ? ent[c1 * NDW] : nsel;
+            const int64_t end = int64_t(c1) * RE < rem ? int64_t(c1) * RE : rem;
+            nsc = sel1 - sel0;
+            nrc = int32_t(end - int64_t(c0) * RE) - nsc;
+            rej_b = c0 * RE - sel0;
+        };
+        // the chunk's values and tile-local indices into LDS in output order
+        // (tile-local: no prefix needed)
+        auto stage = [&](int c0, int c1, int32_t sel0, int32_t nsc, int32_t rej_b) {
+#pragma unroll
+            for (int r = 0; r < MAXR; r++) {
+                if (r >= c0 && r < c1) {
+                    int32_t sb = ent[r * NDW + dw] + int32_t(pk[r] >> 4);  // selected before, in the tile
+#pragma unroll
+                    for (int c = 0; c < V; c++) {
+                        const int32_t li = r * RE + int32_t(dt) * V + c;
+                        if (li < rem) {
+                            const bool sel = (pk[r] >> c) & 1u;
+                            const int32_t slot = sel ? sb - sel0 : nsc + (li - sb) - rej_b;
+                            sval[slot] = x[r].v[c];
+                            lidx[slot] = uint16_t(li);
+                            sb += int32_t(sel);
+                        }
+                    }
+                }
+            }
+        };
         if (ctrl) {
             // every tile's count: the total, and the sum over the earlier ones
             int32_t total = s_nsel, pre = 0;
@@ -399,43 +433,27 @@ __global__ __launch_bounds__(kResWaves *kWave) void k_compact_resident(A a, uint
                 s_total = total;
                 if (tile == nt - 1) *a.count = total;
             }
+        } else {
+            // the first chunk is staged while the control wave reads the counts
+            int c1;
+            int32_t sel0, nsc, nrc, rej_b;
+            chunk(0, c1, sel0, nsc, nrc, rej_b);
+            stage(0, c1, sel0, nsc, rej_b);
         }
         __syncthreads();
-        const int64_t rem = a.n - start;
         const int64_t pre = s_pre, rej0 = int64_t(s_total) + (start - pre);  // first rejected slot of the tile
-        const int32_t nsel = s_nsel;
         const int32_t s0 = int32_t(start);  // n <= INT32_MAX
         int32_t *vals = reinterpret_cast<int32_t *>(a.out_vals);
 #pragma unroll
         for (int c0 = 0; c0 < MAXR; c0 += CH) {
             if (c0 >= int(rows)) break;
-            const int c1 = c0 + CH < int(rows) ? c0 + CH : int(rows);
-            const int32_t sel0 = ent[c0 * NDW];                       // selected before the chunk, in the tile
-            const int32_t sel1 = c1 < int(rows) ? ent[c1 * NDW] : nsel;
-            const int64_t end = int64_t(c1) * RE < rem ? int64_t(c1) * RE : rem;
-            const int32_t nsc = sel1 - sel0;                          // selected in the chunk
-            const int32_t nrc = int32_t(end - int64_t(c0) * RE) - nsc;  // rejected in the chunk
-            const int32_t rej_b = c0 * RE - sel0;                     // rejected before the chunk, in the tile
-            if (!ctrl) {
-#pragma unroll
-                for (int r = 0; r < MAXR; r++) {
-                    if (r >= c0 && r < c1) {
-                        int32_t sb = ent[r * NDW + dw] + int32_t(pk[r] >> 4);  // selected before, in the tile
-#pragma unroll
-                        for (int c = 0; c < V; c++) {
-                            const int32_t li = r * RE + int32_t(dt) * V + c;
-                            if (li < rem) {
-                                const bool sel = (pk[r] >> c) & 1u;
-                                const int32_t slot = sel ? sb - sel0 : nsc + (li - sb) - rej_b;
-                                sval[slot] = x[r].v[c];
-                                lidx[slot] = uint16_t(li);
-                                sb += int32_t(sel);
-                            }
-                        }
-                    }
-                }
+            int c1;
+            int32_t sel0, nsc, nrc, rej_b;
+            chunk(c0, c1, sel0, nsc, nrc, rej_b);
+            if (c0 > 0) {
+                if (!ctrl) stage(c0, c1, sel0, nsc, rej_b);
+                __syncthreads();
             }
-            __syncthreads();
             write_range<kResWaves * kWave>(vals, pre + sel0, nsc, a.n, [&](int32_t i) { return sval[i]; });
             write_range<kResWaves * kWave>(vals, rej0 + rej_b, nrc, a.n, [&](int32_t i) { return sval[nsc + i]; });
             if (a.out_idx != nullptr) {
