@@ -524,7 +524,10 @@ __global__ __launch_bounds__(kSegPartThreads) void k_seg_partials(SegArgs a) {
 // Pass 4.  The heads of up to kSegMarkTiles tiles are marked at once (one
 // batch of offset loads per group: marking tile by tile put a dependent round
 // trip and two barriers before every tile's scan), then each tile is scanned
-// with the carry and stored.
+// with the carry and stored.  The next tile's values are loaded while the
+// current one is marked, scanned and stored (unconditional buffer loads, a
+// range of zero when there is no next tile), so the tiles of a chunk do not
+// each wait a full load latency.
 constexpr int kSegMarkTiles = 8;
 
 template <class T, class Op, int B, int R, int V>
@@ -545,6 +548,27 @@ __global__ __launch_bounds__(B) void k_seg_rescan(SegArgs a) {
     const uint64_t t1 = t0 + a.chunk_tiles < a.num_tiles ? t0 + a.chunk_tiles : a.num_tiles;
     cm.load(a, t0, t1);
     ST st;
+    constexpr int VB = V * int(sizeof(T));  // bytes per vector
+    static_assert(VB == 4 || VB == 8 || VB == 16, "vector access of 4, 8 or 16 bytes");
+    Vec<T, V> nv[R];  // the next tile's values
+    auto fetch = [&](uint64_t t) {
+        const bool valid = t < t1;
+        const int64_t start = valid ? int64_t(t) * ST::TILE : 0;
+        const int64_t left = a.n - start;
+        const BufRsrc rs =
+            make_rsrc(reinterpret_cast<const T *>(a.in) + start, valid ? (left < ST::TILE ? left : ST::TILE) : 0);
+#pragma unroll
+        for (int r = 0; r < R; r++) {
+            const uint32_t off = uint32_t(ST::elem(r) * int64_t(sizeof(T)));
+            if constexpr (VB == 16)
+                nv[r] = __builtin_bit_cast(Vec<T, V>, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 2));
+            else if constexpr (VB == 8)
+                nv[r] = __builtin_bit_cast(Vec<T, V>, __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 2));
+            else
+                nv[r] = __builtin_bit_cast(Vec<T, V>, __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 2));
+        }
+    };
+    fetch(t0);
     for (uint64_t g0 = t0; g0 < t1; g0 += kSegMarkTiles) {
         const uint64_t g1 = g0 + kSegMarkTiles < t1 ? g0 + kSegMarkTiles : t1;
         const int64_t eg0 = int64_t(g0) * ST::TILE;
@@ -574,7 +598,17 @@ __global__ __launch_bounds__(B) void k_seg_rescan(SegArgs a) {
         __syncthreads();
         for (uint64_t t = g0; t < g1; t++) {
             const int64_t start = int64_t(t) * ST::TILE;
-            st.load(reinterpret_cast<const T *>(a.in) + start, a.n - start);
+            // a whole tile takes the prefetched values; the array's last,
+            // partial tile (a vector may cross its end) is loaded element by
+            // element as before
+            if (a.n - start >= ST::TILE) {
+                st.rem = a.n - start;
+#pragma unroll
+                for (int r = 0; r < R; r++) st.v[r] = nv[r];
+            } else {
+                st.load(reinterpret_cast<const T *>(a.in) + start, a.n - start);
+            }
+            fetch(t + 1);
             st.heads_from_map(hm + (t - g0) * ST::TILE);
             uint32_t cov;
             st.scan(sh, a.exclusive != 0, cov);
