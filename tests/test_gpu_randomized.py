@@ -202,3 +202,81 @@ def test_random_single_pass_paths():
         assert_scan_matches(x.ravel(), to_host(r).ravel(), op, excl, dims=(1, rows, cols),
                             what=f"case {case}: {np.dtype(dt).name} {op} excl={excl} {rows}x{cols} dim 0 ({kind})")
     assert kernels.get("resident", 0) >= 10 and kernels.get("columns_lookback", 0) >= 6, kernels
+
+
+def test_random_no_identity():
+    # Inclusive scans without the operator's identity at random sizes, from
+    # tiny arrays to the resident pass's range, whole arrays and rows, against
+    # the oracle's scan that never uses the identity.
+    rng = np.random.default_rng(2031)
+    kernels = {}
+    for case in range(CASES // 3):
+        dt = DTYPES[int(rng.integers(0, len(DTYPES)))]
+        op = OPS[int(rng.integers(0, len(OPS)))]
+        es = np.dtype(dt).itemsize
+        vec = 16 // es
+        if rng.integers(0, 3) == 0:  # the resident pass's range
+            cap = 256 * (17 if es == 4 else 21) * 960 * vec
+            n = int(rng.integers(-(-(8 << 20) // es), cap + 1))
+            n -= n % vec
+        else:
+            n = _length(rng, 19712)
+        outer = 1 if rng.integers(0, 3) else int(rng.integers(2, 5))
+        n = max(outer, n - n % outer)
+        length = n // outer
+        tuning = [{"no_identity": 1}, {"no_identity": 1, "block_size": 256, "items_per_thread": vec},
+                  {"no_identity": 1, "grid_blocks": int(rng.integers(1, 40))}][int(rng.integers(0, 3))]
+        kind = sw.plan("scan", TORCH_OF[dt], op, outer, length, tuning=tuning)["kernel"]
+        kernels[kind] = kernels.get(kind, 0) + 1
+        x = _values(dt, n, 500 + case, op)
+        if outer == 1:
+            r = sw.scan_inclusive(to_dev(x), op=op, tuning=tuning)
+        else:
+            r = sw.scan_dim(to_dev(x.reshape(outer, length)), 1, op=op, tuning=tuning)
+        torch.cuda.synchronize()
+        assert_scan_matches(x, to_host(r).ravel(), op, False, dims=(outer, length, 1), noid=True,
+                            what=f"case {case}: {np.dtype(dt).name} {op} {outer}x{length} {tuning} ({kind})")
+    assert kernels.get("resident", 0) > 0 and kernels.get("lookback", 0) > 0, kernels
+
+
+def test_random_rows_kernel():
+    # Many rows that each fit one tile of the rows kernel (one workgroup per
+    # row), at random row lengths and counts, against the oracle.
+    rng = np.random.default_rng(2032)
+    kernels = {}
+    for case in range(CASES // 3):
+        dt = DTYPES[int(rng.integers(0, len(DTYPES)))]
+        op = OPS[int(rng.integers(0, len(OPS)))]
+        excl = bool(rng.integers(0, 2))
+        vec = 16 // np.dtype(dt).itemsize
+        cols = vec * int(rng.integers(64, 2048 + 1))
+        rows = int(rng.integers(2, max(3, min(3000, 4_000_000 // cols))))
+        kind = sw.plan("scan", TORCH_OF[dt], op, rows, cols)["kernel"]
+        kernels[kind] = kernels.get(kind, 0) + 1
+        x = _values(dt, rows * cols, 600 + case, op).reshape(rows, cols)
+        r = sw.scan_dim(to_dev(x), 1, op=op, exclusive=excl)
+        torch.cuda.synchronize()
+        assert_scan_matches(x.ravel(), to_host(r).ravel(), op, excl, dims=(rows, cols, 1),
+                            what=f"case {case}: {np.dtype(dt).name} {op} excl={excl} {rows}x{cols} ({kind})")
+    assert kernels.get("rows", 0) > 0, kernels
+
+
+def test_random_element_scans():
+    # Scans of elements of W components (every built width) at random sizes,
+    # shapes and chunk counts, against the oracle's (outer, len, W) scan.
+    rng = np.random.default_rng(2033)
+    widths = [2, 3, 4, 8, 16, 17, 24]
+    for case in range(CASES // 3):
+        dt = [np.float32, np.float64, np.int32, np.int64][int(rng.integers(0, 4))]
+        op = OPS[int(rng.integers(0, len(OPS)))]
+        excl = bool(rng.integers(0, 2))
+        w = widths[int(rng.integers(0, len(widths)))]
+        n = int(rng.integers(1, 200_000 // w + 2))
+        tuning = [None, {"block_size": 64}, {"rts_blocks": int(rng.integers(1, 3000))},
+                  {"block_size": 128, "rts_blocks": int(rng.integers(1, 3000))}][int(rng.integers(0, 4))]
+        x = _values(dt, n * w, 700 + case, op)
+        fn = sw.scan_exclusive if excl else sw.scan_inclusive
+        r = fn(to_dev(x), op=op, width=w, tuning=tuning)
+        torch.cuda.synchronize()
+        assert_scan_matches(x, to_host(r), op, excl, dims=(1, n, w),
+                            what=f"case {case}: {np.dtype(dt).name} {op} excl={excl} n={n} w={w} {tuning}")
