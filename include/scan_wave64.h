@@ -154,6 +154,12 @@ typedef struct {
                                   delay_sleeps periods of about 1.7 us before
                                   publishing its aggregate (0: off) */
     int32_t delay_sleeps;
+    int32_t resident_sweeps;   /* resident single pass over a whole array:
+                                  1 holds one tile per workgroup (the look-back
+                                  between all loads and all stores), 2 two
+                                  where they fit (the second tile's loads and
+                                  the first's stores overlapping the
+                                  look-backs); 0: two from 32 MiB up */
 } scan_tuning_t;
 
 /* Kernel family a call runs (reported by scan_plan). */
@@ -185,12 +191,15 @@ typedef struct {
     int32_t items_per_thread;  /* elements (or components) per thread per tile */
     int32_t vec;               /* elements per vector access (1 = element-wide) */
     int64_t tile_elems;        /* elements per tile */
-    int64_t num_tiles;         /* tiles (= workgroups) of the main launch */
+    int64_t num_tiles;         /* tiles of the main launch */
     int64_t lds_bytes;         /* LDS per workgroup of the main launch */
     int64_t workspace_bytes;   /* workspace this call needs */
     int32_t launches;          /* kernel launches the call enqueues */
     int32_t carry_words;       /* 64-bit descriptor words per tile (look-back kernels; carry
                                   values per partial for reduce-then-scan) */
+    int32_t tiles_per_block;   /* resident pass: tiles each workgroup holds (1, or 2
+                                  for a whole array, see resident_sweeps); 0 for
+                                  the other kernels */
 } scan_plan_t;
 
 /* Which call scan_plan describes. */

@@ -39,7 +39,7 @@ class Tuning(ctypes.Structure):
                 ("rts_blocks", ctypes.c_int32), ("spin_limit", ctypes.c_int32),
                 ("grid_blocks", ctypes.c_int32), ("mode_limit", ctypes.c_int32),
                 ("no_identity", ctypes.c_int32), ("delay_stride", ctypes.c_int32),
-                ("delay_sleeps", ctypes.c_int32)]
+                ("delay_sleeps", ctypes.c_int32), ("resident_sweeps", ctypes.c_int32)]
 
 
 class Plan(ctypes.Structure):
@@ -47,7 +47,8 @@ class Plan(ctypes.Structure):
                 ("items_per_thread", ctypes.c_int32), ("vec", ctypes.c_int32),
                 ("tile_elems", ctypes.c_int64), ("num_tiles", ctypes.c_int64),
                 ("lds_bytes", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64),
-                ("launches", ctypes.c_int32), ("carry_words", ctypes.c_int32)]
+                ("launches", ctypes.c_int32), ("carry_words", ctypes.c_int32),
+                ("tiles_per_block", ctypes.c_int32)]
 
 
 EXPORTS = ["scan_plan", "scan_workspace_bytes", "scan_workspace_init", "scan_workspace_error", "scan_inclusive",

@@ -239,6 +239,7 @@ constexpr int64_t kSmallArrayTiles = 256;             // one tile per CU: the sm
 // it the resident pass (int32 2^21: 10.6 against 11.3, fp64 2^20: 11.1
 // against 12.3)
 constexpr int64_t kResMinBytes = int64_t(8) << 20;
+constexpr int64_t kResTwoTileBytes = int64_t(32) << 20;  // whole arrays: two tiles per workgroup from here
 constexpr int64_t kElemTileLocalMem = 64 * 1024;      // default bound on an element tile's E (default dynamic LDS limit)
 constexpr int kElemDefaultBlock = 256;                // large elements: start of the rule
 constexpr int64_t kElemChunks = 2048;  // large elements: workgroups per launch (<= 8192, the partials pass)
@@ -289,6 +290,7 @@ scan_tuning_t tuning_or_default(const scan_tuning_t *t) {
 struct TilePlan {
     int kernel;               // scan_kernel_t
     int block, rows, vec;
+    int sweeps = 1;           // resident pass: tiles per workgroup
     int64_t tile;
     int64_t tiles_per_seg, num_tiles;
     int carry_words;
@@ -382,24 +384,35 @@ int plan_scan(scan_dtype_t dt, scan_op_t op, int64_t outer, int64_t len, bool al
     // kResMaxTiles (the most compute units reading).  Only for the default
     // shape, without a grid cap, scans of 128-bit rows (without an identity
     // too: inclusive, as everywhere).
+    // A whole array of 32 MiB or more takes two tiles per workgroup where
+    // they fit (the second tile's loads and the first's stores overlap the
+    // look-backs: fp32 1e7 20.3 -> 19.4 us, fp64 1e7 35.1 -> 34.3, int32
+    // 2^23 17.5 -> 17.0); below that the fewer, longer workgroups lost
+    // (int32 2^22 10.7 -> 11.7 us).  The tuning can ask for either.
     if (shape_free && tu.grid_blocks <= 0 && vec_ok && outer * len * esize >= kResMinBytes &&
         (tu.no_identity ? find_resident_noid(dt, op) : find_resident(dt, op)) != nullptr) {
         const int64_t re = int64_t(kResWaves - 1) * kWave * (16 / esize);  // the data waves
-        const int maxr = esize == 8 ? kResMaxRows8 : kResMaxRows4;
-        for (int r = 1; r <= maxr; r++) {
-            const int64_t tps = (len + r * re - 1) / (r * re);
-            if (outer * tps <= kResMaxTiles) {
-                p.kernel = SCAN_KERNEL_RESIDENT;
-                p.block = kResWaves * kWave;
-                p.rows = r;
-                p.vec = 16 / esize;
-                p.tile = r * re;
-                p.tiles_per_seg = tps;
-                p.num_tiles = outer * tps;
-                p.rts_blocks = p.rts_chunk = 0;
-                p.ws_bytes = kHeader + round_up(size_t(p.num_tiles) * p.carry_words * 8, 256);
-                p.launches = 1;
-                return SCAN_OK;
+        const bool two = outer == 1 && (tu.resident_sweeps == 2 ||
+                                        (tu.resident_sweeps != 1 && len * esize >= kResTwoTileBytes));
+        for (int sw = two ? 2 : 1; sw >= 1; sw--) {
+            const int maxr = sw == 2 ? (esize == 8 ? kResMaxRows2x8 : kResMaxRows2x4)
+                                     : (esize == 8 ? kResMaxRows8 : kResMaxRows4);
+            for (int r = 1; r <= maxr; r++) {
+                const int64_t tps = (len + r * re - 1) / (r * re);
+                if ((outer * tps + sw - 1) / sw <= kResMaxTiles) {
+                    p.kernel = SCAN_KERNEL_RESIDENT;
+                    p.block = kResWaves * kWave;
+                    p.rows = r;
+                    p.sweeps = sw;
+                    p.vec = 16 / esize;
+                    p.tile = r * re;
+                    p.tiles_per_seg = tps;
+                    p.num_tiles = outer * tps;
+                    p.rts_blocks = p.rts_chunk = 0;
+                    p.ws_bytes = kHeader + round_up(size_t(p.num_tiles) * p.carry_words * 8, 256);
+                    p.launches = 1;
+                    return SCAN_OK;
+                }
             }
         }
     }
@@ -839,8 +852,8 @@ int scan_common(const void *in, void *out, int64_t outer, int64_t len, int64_t i
     a.total_out = total_out;
     if (p.kernel == SCAN_KERNEL_RESIDENT) {
         if (total_out != nullptr && dt == SCAN_I32 && op == SCAN_OP_SUM)  // count-scan-emit's offsets
-            return find_pack_resident()(a, p.rows, stream);
-        return (tu.no_identity ? find_resident_noid(dt, op) : find_resident(dt, op))(a, p.rows, stream);
+            return find_pack_resident()(a, p.rows, p.sweeps, stream);
+        return (tu.no_identity ? find_resident_noid(dt, op) : find_resident(dt, op))(a, p.rows, p.sweeps, stream);
     }
     const uint32_t grid_cap = tu.grid_blocks > 0 ? uint32_t(tu.grid_blocks) : 0u;
     if (total_out != nullptr && dt == SCAN_I32 && op == SCAN_OP_SUM)  // count-scan-emit's offsets
@@ -878,14 +891,17 @@ void fill_plan(const TilePlan &p, scan_dtype_t dt, scan_op_t op, scan_plan_t *pl
     else if (p.kernel == SCAN_KERNEL_COMPACT_RESIDENT)
         plan->lds_bytes = int64_t(kResCompactMaxRows) * (kResWaves - 1) * kWave * 4 * 2 +
                           int64_t(kResCompactMaxRows) * (kResWaves - 1) * 4 + 32;
-    else if (p.kernel == SCAN_KERNEL_RESIDENT)
-        plan->lds_bytes = int64_t(dtype_bytes(dt)) * (kResWaves - 1) * (dt == SCAN_I64 || dt == SCAN_F64 ? kResMaxRows8 : kResMaxRows4) +
-                          carry_bytes(dt, op) + 32;
+    else if (p.kernel == SCAN_KERNEL_RESIDENT) {
+        const bool wide = dt == SCAN_I64 || dt == SCAN_F64;
+        const int maxr = p.sweeps == 2 ? 2 * (wide ? kResMaxRows2x8 : kResMaxRows2x4) : (wide ? kResMaxRows8 : kResMaxRows4);
+        plan->lds_bytes = int64_t(dtype_bytes(dt)) * (kResWaves - 1) * maxr + p.sweeps * carry_bytes(dt, op) + 32;
+    }
     else
         plan->lds_bytes = int64_t(p.rows) * (p.block / 64) * dtype_bytes(dt) + carry_bytes(dt, op) + 32;
     plan->workspace_bytes = int64_t(p.ws_bytes);
     plan->launches = p.launches;
     plan->carry_words = p.carry_words;
+    plan->tiles_per_block = p.kernel == SCAN_KERNEL_RESIDENT ? p.sweeps : 0;
 }
 
 }  // namespace

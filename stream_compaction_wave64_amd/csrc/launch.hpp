@@ -32,12 +32,14 @@ LbLaunch find_lookback(scan_dtype_t dt, scan_op_t op, int block, int rows, int v
 LbLaunch find_pack_lookback(int block, int rows, int vec);  // int32 sum, offsets kept cacheable
 
 // The resident single pass (resident.hip): one 1024-thread workgroup (15
-// data waves and a control wave) per tile of `rows` x 960 x vec elements
-// (vec = 16 / element size), at most kResMaxTiles tiles, grid = tiles.
+// data waves and a control wave) per `sweeps` tiles (1, or 2 for a whole
+// array) of `rows` x 960 x vec elements (vec = 16 / element size), at most
+// kResMaxTiles workgroups.
 constexpr int kResWaves = 16;
 constexpr int kResMaxRows4 = 17, kResMaxRows8 = 21;  // 68 and 84 data registers per thread
+constexpr int kResMaxRows2x4 = 8, kResMaxRows2x8 = 11;  // rows per tile with two tiles: 64 and 88 registers
 constexpr int64_t kResMaxTiles = 256;                // one per compute unit on MI355X
-using ResLaunch = int (*)(const ScanArgs &, int rows, hipStream_t);
+using ResLaunch = int (*)(const ScanArgs &, int rows, int sweeps, hipStream_t);
 ResLaunch find_resident(scan_dtype_t dt, scan_op_t op);
 ResLaunch find_resident_noid(scan_dtype_t dt, scan_op_t op);  // inclusive, no identity, no total
 ResLaunch find_pack_resident();  // int32 sum, offsets kept cacheable

@@ -46,18 +46,31 @@ namespace sw64 {
 // reads); a lane, a (row, wave) entry or a tile with nothing before it
 // skips the combination instead of taking an identity; the look-back
 // combines optional carries (Opt, "absent" being their only identity).
-template <class T, class Op0, int V, int MAXR, int OUT_AUX, bool NOID = false>
+//
+// SW = 2 (whole arrays only): each workgroup holds two tiles of `rows`
+// rows, w and w + G in the static order (G workgroups), both loaded at
+// once.  The first tile is scanned, published and looked back while the
+// second one's loads land; the second is published and looked back while
+// the first one's results are stored.  Its look-back is the pipeline's
+// aggregate-only form: the workgroup's own first tile's inclusive prefix
+// and the G - 1 aggregates between the two.  With one tile per workgroup
+// the whole look-back sits between the loads and the stores, with HBM idle.
+// Dynamic mode (tiles claimed in order) gives claim k the tiles 2k and
+// 2k + 1, so every tile a look-back reads belongs to an earlier claim.
+template <class T, class Op0, int V, int MAXR, int OUT_AUX, bool NOID = false, int SW = 1>
 __global__ __launch_bounds__(kResWaves *kWave) void k_resident(ScanArgs a, uint32_t rows) {
+    static_assert(SW == 1 || SW == 2, "one or two tiles per workgroup");
     using Op = std::conditional_t<NOID, NoId<Op0>, Op0>;
     using C = typename Carry<T, Op0>::type;
     using D = DescFor<T, C>;
-    constexpr int NDW = kResWaves - 1;                       // data waves
-    constexpr int RE = NDW * kWave * V;                      // elements per tile row
-    constexpr int KE = (MAXR * NDW + kWave - 1) / kWave;     // (row, wave) totals per lane of the control wave
+    constexpr int NDW = kResWaves - 1;                          // data waves
+    constexpr int RE = NDW * kWave * V;                         // elements per tile row
+    constexpr int KE = ((MAXR / SW) * NDW + kWave - 1) / kWave;  // (row, wave) totals per lane of the control wave
+    constexpr int NRW = int(kResMaxTiles / kWave);              // look-back windows of 64 tiles
     static_assert(V * sizeof(T) == 16, "128-bit rows");
     __shared__ T ent[MAXR * NDW];        // (row, wave) totals, then their exclusive prefixes in the tile
-    __shared__ C s_pre;                  // the tile's exclusive prefix (NOID: none for a segment's first tile)
-    __shared__ uint32_t s_epoch, s_tile;
+    __shared__ C s_pre[SW];              // each tile's exclusive prefix (NOID: none for a segment's first tile)
+    __shared__ uint32_t s_epoch, s_claim, s_dyn;
     __shared__ uint64_t s_hw, s_cap;
     WsHeader *hdr = reinterpret_cast<WsHeader *>(a.pipe.ws);
     uint64_t *desc = reinterpret_cast<uint64_t *>(reinterpret_cast<char *>(a.pipe.ws) + kWsHeaderBytes);
@@ -80,38 +93,42 @@ __global__ __launch_bounds__(kResWaves *kWave) void k_resident(ScanArgs a, uint3
     };
     // Buffer accesses from the tile's first element, bounded by the segment:
     // rows and vectors past its end read 0 (replaced by the identity below)
-    // and drop their stores.
+    // and drop their stores.  Tile s of the workgroup holds rows
+    // s * rows .. s * rows + rows - 1 of x.
     Vec<T, V> x[MAXR];
     const uint32_t voff = dt * V * uint32_t(sizeof(T));
     constexpr uint32_t kRowBytes = uint32_t(RE) * sizeof(T);
-    BufRsrc rs_in, rs_out;
-    auto load = [&](uint32_t t) {
+    BufRsrc rs_in[SW], rs_out[SW];
+    auto load = [&](uint32_t t, int s) {
         int64_t start, rem;
         uint32_t seg, j;
         geom(t, start, rem, seg, j);
-        const int64_t cnt = rem < tile_elems ? rem : tile_elems;
-        rs_in = make_rsrc(in + start, cnt);
-        rs_out = make_rsrc(out + start, cnt);
+        int64_t cnt = rem < tile_elems ? rem : tile_elems;
+        if (t >= n) cnt = 0;  // no such tile (an odd tile count's last workgroup): nothing in range
+        rs_in[s] = make_rsrc(in + start, cnt);
+        rs_out[s] = make_rsrc(out + start, cnt);
+        const uint32_t r0 = uint32_t(s) * rows;
 #pragma unroll
         for (int r = 0; r < MAXR; r++) {
-            if (r < int(rows))
-                x[r] = __builtin_bit_cast(Vec<T, V>,
-                                          __builtin_amdgcn_raw_buffer_load_b128(rs_in, voff, r * kRowBytes, 2));
+            if (uint32_t(r) >= r0 && uint32_t(r) < r0 + rows)
+                x[r] = __builtin_bit_cast(
+                    Vec<T, V>, __builtin_amdgcn_raw_buffer_load_b128(rs_in[s], voff, (uint32_t(r) - r0) * kRowBytes, 2));
         }
     };
     // Each row of the tile: this thread's vector scanned, then across the
     // wave; every value becomes its result within the wave's 64 x V run
     // (inclusive, or exclusive with the identity first), and the wave's row
     // total goes to LDS.  Elements past the segment's end take the identity.
-    auto scan_rows = [&](uint32_t t) {
+    auto scan_rows = [&](uint32_t t, int s) {
         int64_t start_, rem_;
         uint32_t seg_, j_;
         geom(t, start_, rem_, seg_, j_);
         const int64_t e_thread = int64_t(dt) * V;
+        const uint32_t r0 = uint32_t(s) * rows;
 #pragma unroll
         for (int r = 0; r < MAXR; r++) {
-            if (r < int(rows)) {
-                const int64_t e0 = int64_t(r) * RE + e_thread;
+            if (uint32_t(r) >= r0 && uint32_t(r) < r0 + rows) {
+                const int64_t e0 = int64_t(uint32_t(r) - r0) * RE + e_thread;
                 T inc[V];
                 T acc = x[r].v[0];
 #pragma unroll
@@ -141,13 +158,122 @@ __global__ __launch_bounds__(kResWaves *kWave) void k_resident(ScanArgs a, uint3
             }
         }
     };
+    // Control wave: tile s's (row, wave) totals in tile order (lane l: KE
+    // consecutive ones) scanned into their exclusive prefixes; returns the
+    // tile's aggregate.
+    auto scan_entries = [&](int s) -> C {
+        const uint32_t ne = rows * NDW, b0 = uint32_t(s) * ne;
+        T e[KE];
+        if constexpr (NOID) {
+            // lanes past the last entry hold whatever they read; they sit
+            // above every lane with entries, so the inclusive scan carries
+            // nothing from them down, and the aggregate is the last such
+            // lane's result.  Entry 0 has nothing before it: its slot is left
+            // as it is (the data waves do not read it).
+            T acc = ent[b0 + (uint32_t(lane) * KE < ne ? uint32_t(lane) * KE : 0u)];
+#pragma unroll
+            for (int k = 0; k < KE; k++) {
+                const uint32_t i = uint32_t(lane) * KE + k;
+                e[k] = ent[b0 + (i < ne ? i : 0u)];
+                if (k > 0 && i < ne) acc = Op::apply(acc, e[k]);
+            }
+            const T linc = wave_scan_incl_noid<Op>(acc);
+            T run = dpp_mov<kWaveShr1>(linc, linc);
+#pragma unroll
+            for (int k = 0; k < KE; k++) {
+                const uint32_t i = uint32_t(lane) * KE + k;
+                if (i < ne) {
+                    if (i > 0) ent[b0 + i] = run;
+                    run = i > 0 ? Op::apply(run, e[k]) : e[k];
+                }
+            }
+            return C(wave_read(linc, int((ne - 1) / KE)));
+        } else {
+            const T id = Op::template identity<T>();
+            T acc = id;
+#pragma unroll
+            for (int k = 0; k < KE; k++) {
+                const uint32_t i = uint32_t(lane) * KE + k;
+                e[k] = i < ne ? ent[b0 + i] : id;
+                acc = Op::apply(acc, e[k]);
+            }
+            const T linc = wave_scan_incl<Op>(acc);
+            T run = wave_shr1(id, linc);
+#pragma unroll
+            for (int k = 0; k < KE; k++) {
+                const uint32_t i = uint32_t(lane) * KE + k;
+                if (i < ne) ent[b0 + i] = run;
+                run = Op::apply(run, e[k]);
+            }
+            return C(wave_read(linc, kWave - 1));
+        }
+    };
+    auto publish = [&](uint32_t t, const C &agg) {
+        if (a.pipe.delay_stride > 0 && t % a.pipe.delay_stride == a.pipe.delay_stride - 1) {
+            // a late publisher, so tests reach the look-back's re-polls
+            for (uint32_t i = 0; i < a.pipe.delay_sleeps; i++) __builtin_amdgcn_s_sleep(64);
+        }
+        if (lane == 0) D::publish(desc + uint64_t(t) * D::kWords, s_epoch, kStateA, agg);
+    };
+    // The combination of the aggregates of tiles [lo, hi) (non-empty, all
+    // published with a value), read kResMaxTiles at a time: one round trip
+    // except for dynamic mode's first tiles of SW = 2 (up to twice as many).
+    auto gap = [&](uint32_t lo, uint32_t hi) -> C {
+        C acc{};
+        for (uint32_t b = lo; b < hi; b += uint32_t(kResMaxTiles)) {
+            const uint32_t e = hi - b > uint32_t(kResMaxTiles) ? b + uint32_t(kResMaxTiles) : hi;
+            C part;
+            if constexpr (NOID) {
+                GapRead<Opt<C>, OptDesc<D>, NRW> g;
+                g.issue(desc, int64_t(b), int64_t(e));
+                part = g.template finish<OptOp<Op0>>(desc, s_epoch, hdr, a.pipe.spin_limit).v;
+            } else {
+                GapRead<C, D, NRW> g;
+                g.issue(desc, int64_t(b), int64_t(e));
+                part = g.template finish<Op>(desc, s_epoch, hdr, a.pipe.spin_limit);
+            }
+            acc = b == lo ? part : C(Op::apply(acc, part));
+        }
+        return acc;
+    };
+    // Tile s's results: (row, wave) prefix, then the tile's prefix (carry
+    // type, one rounding); has_pre false for a segment's first tile.
+    auto store = [&](int s, const C &pre, bool has_pre) {
+        const uint32_t r0 = uint32_t(s) * rows;
+#pragma unroll
+        for (int r = 0; r < MAXR; r++) {
+            if (uint32_t(r) >= r0 && uint32_t(r) < r0 + rows) {
+                const T eb = ent[r * NDW + dw];
+                Vec<T, V> y;
+                if constexpr (NOID) {
+                    // entry (0, 0) has nothing before it in the tile, and a
+                    // segment's first tile has nothing before it
+                    const bool has_eb = uint32_t(r) > r0 || dw > 0;
+#pragma unroll
+                    for (int c = 0; c < V; c++) {
+                        const T t = has_eb ? Op::apply(eb, x[r].v[c]) : x[r].v[c];
+                        y.v[c] = has_pre ? T(Op::apply(pre, C(t))) : t;
+                    }
+                } else {
+#pragma unroll
+                    for (int c = 0; c < V; c++) y.v[c] = T(Op::apply(pre, C(Op::apply(eb, x[r].v[c]))));
+                }
+                // the row step in the vector offset, the scalar offset a
+                // constant 0 (see the column single pass: 128-bit buffer
+                // stores with a scalar-register offset lost their data
+                // registers)
+                uint32_t vo = voff + (uint32_t(r) - r0) * kRowBytes;
+                asm volatile("" : "+v"(vo));
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, y), rs_out[s], vo, 0, OUT_AUX);
+            }
+        }
+    };
+
     // The control wave runs the workspace protocol; the data waves load the
-    // static tile and scan it meanwhile (each row as it arrives), and load and
-    // scan again after the barrier if a dynamic-mode claim gave the workgroup
-    // another tile.
-    uint32_t tile = blockIdx.x;
+    // static tiles and scan the first meanwhile (each row as it arrives),
+    // and load and scan again after the barrier if dynamic mode gave the
+    // workgroup other tiles.
     if (ctrl) {
-        uint32_t tk = 0;
         if (lane == 0) {
             uint64_t hw = 0, cap = 0;
             const uint32_t e = begin_call(hdr, hw, cap);
@@ -155,155 +281,112 @@ __global__ __launch_bounds__(kResWaves *kWave) void k_resident(ScanArgs a, uint3
             s_hw = hw;
             s_cap = cap;
             const uint32_t m = decide_mode(hdr, e, gridDim.x, a.pipe.mode_limit);
-            tk = m == kModeStatic
-                     ? uint32_t(blockIdx.x)
-                     : __hip_atomic_fetch_add(&hdr->claim, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            s_tile = tk;
+            s_dyn = m == kModeStatic ? 0u : 1u;
+            s_claim = m == kModeStatic
+                          ? uint32_t(blockIdx.x)
+                          : __hip_atomic_fetch_add(&hdr->claim, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-        tile = uint32_t(__builtin_amdgcn_readlane(int(tk), 0));
-    }
-    if (!ctrl) {
-        tile = blockIdx.x;
-        load(tile);
-        scan_rows(tile);
+    } else {
+        load(blockIdx.x, 0);
+        if constexpr (SW == 2) load(blockIdx.x + gridDim.x, 1);
+        scan_rows(blockIdx.x, 0);
     }
     __syncthreads();
-    if (s_tile != blockIdx.x) {
-        // dynamic mode gave the workgroup another tile (every wave sees the
-        // same s_tile, so all or none take this branch and its barrier)
-        tile = s_tile;
+    // this workgroup's tiles: static, w (and w + G); dynamic, claim k's
+    // SW * k (and SW * k + 1)
+    const bool dyn = s_dyn != 0u;
+    const uint32_t claim = s_claim;
+    uint32_t tl[SW];
+    tl[0] = dyn ? uint32_t(SW) * claim : claim;
+    if constexpr (SW == 2) tl[1] = dyn ? 2u * claim + 1u : claim + gridDim.x;
+    if (SW == 2 ? dyn : claim != blockIdx.x) {
+        // every wave sees the same words, so all or none take this branch
+        // and its barrier
         if (!ctrl) {
-            load(tile);
-            scan_rows(tile);
+            load(tl[0], 0);
+            if constexpr (SW == 2) load(tl[1], 1);
+            scan_rows(tl[0], 0);
         }
         __syncthreads();
     }
-    const uint32_t epoch = s_epoch;
-    int64_t start, rem;
-    uint32_t seg, j;
-    geom(tile, start, rem, seg, j);
-    // Control wave: the (row, wave) totals in tile order (lane l: KE
-    // consecutive ones) scanned into their exclusive prefixes; the tile
-    // aggregate published; the aggregates of the segment's earlier tiles
-    // combined.
+    int64_t start0, rem0;
+    uint32_t seg0, j0;
+    geom(tl[0], start0, rem0, seg0, j0);
+    // First tile: its aggregate published and the aggregates of the
+    // segment's earlier tiles combined.
+    C inc0{};  // its inclusive prefix (SW = 2)
     if (ctrl) {
-        const uint32_t ne = rows * NDW;
-        T e[KE];
-        T linc;
-        C agg;
-        if constexpr (NOID) {
-            // lanes past the last entry hold whatever they read; they sit
-            // above every lane with entries, so the inclusive scan carries
-            // nothing from them down, and the aggregate is the last such
-            // lane's result.  Entry 0 has nothing before it: its slot is left
-            // as it is (the data waves do not read it).
-            T acc = ent[uint32_t(lane) * KE < ne ? uint32_t(lane) * KE : 0u];
-#pragma unroll
-            for (int k = 0; k < KE; k++) {
-                const uint32_t i = uint32_t(lane) * KE + k;
-                e[k] = ent[i < ne ? i : 0u];
-                if (k > 0 && i < ne) acc = Op::apply(acc, e[k]);
-            }
-            linc = wave_scan_incl_noid<Op>(acc);
-            T run = dpp_mov<kWaveShr1>(linc, linc);
-#pragma unroll
-            for (int k = 0; k < KE; k++) {
-                const uint32_t i = uint32_t(lane) * KE + k;
-                if (i < ne) {
-                    if (i > 0) ent[i] = run;
-                    run = i > 0 ? Op::apply(run, e[k]) : e[k];
-                }
-            }
-            agg = C(wave_read(linc, int((ne - 1) / KE)));
-        } else {
-            const T id = Op::template identity<T>();
-            T acc = id;
-#pragma unroll
-            for (int k = 0; k < KE; k++) {
-                const uint32_t i = uint32_t(lane) * KE + k;
-                e[k] = i < ne ? ent[i] : id;
-                acc = Op::apply(acc, e[k]);
-            }
-            linc = wave_scan_incl<Op>(acc);
-            T run = wave_shr1(id, linc);
-#pragma unroll
-            for (int k = 0; k < KE; k++) {
-                const uint32_t i = uint32_t(lane) * KE + k;
-                if (i < ne) ent[i] = run;
-                run = Op::apply(run, e[k]);
-            }
-            agg = C(wave_read(linc, kWave - 1));
-        }
+        const C agg = scan_entries(0);
         C pre{};
         if constexpr (!NOID) pre = Op::template identity<C>();
         if (tps > 1) {
-            if (a.pipe.delay_stride > 0 && tile % a.pipe.delay_stride == a.pipe.delay_stride - 1) {
-                // a late publisher, so tests reach the look-back's re-polls
-                for (uint32_t i = 0; i < a.pipe.delay_sleeps; i++) __builtin_amdgcn_s_sleep(64);
-            }
-            if (lane == 0) D::publish(desc + uint64_t(tile) * D::kWords, epoch, kStateA, agg);
-            if (j > 0) {
-                if constexpr (NOID) {
-                    // j > 0 earlier tiles, all published with a value
-                    GapRead<Opt<C>, OptDesc<D>, kResMaxTiles / kWave> g;
-                    g.issue(desc, int64_t(tile) - j, int64_t(tile));
-                    pre = g.template finish<OptOp<Op0>>(desc, epoch, hdr, a.pipe.spin_limit).v;
-                } else {
-                    GapRead<C, D, kResMaxTiles / kWave> g;
-                    g.issue(desc, int64_t(tile) - j, int64_t(tile));
-                    pre = g.template finish<Op>(desc, epoch, hdr, a.pipe.spin_limit);
-                }
-            }
+            publish(tl[0], agg);
+            if (j0 > 0) pre = gap(tl[0] - j0, tl[0]);
         }
+        inc0 = j0 > 0 ? C(Op::apply(pre, agg)) : agg;
         if (lane == 0) {
-            s_pre = pre;
+            s_pre[0] = pre;
             if constexpr (!NOID) {
-                if (a.total_out != nullptr && j == tps - 1)
-                    reinterpret_cast<T *>(a.total_out)[seg] = T(Op::apply(pre, agg));
+                if (a.total_out != nullptr && j0 == tps - 1) reinterpret_cast<T *>(a.total_out)[seg0] = T(inc0);
             }
         }
     }
-    __syncthreads();
-    const C pre = s_pre;
-#pragma unroll
-    for (int r = 0; r < MAXR; r++) {
-        if (!ctrl && r < int(rows)) {
-            const T eb = ent[r * NDW + dw];
-            Vec<T, V> y;
-            if constexpr (NOID) {
-                // entry (0, 0) has nothing before it in the tile, and a
-                // segment's first tile has nothing before it
-                const bool has_eb = r > 0 || dw > 0;
-#pragma unroll
-                for (int c = 0; c < V; c++) {
-                    const T t = has_eb ? Op::apply(eb, x[r].v[c]) : x[r].v[c];
-                    y.v[c] = j > 0 ? T(Op::apply(pre, C(t))) : t;
+    if constexpr (SW == 2) {
+        // Second tile (same segment: whole arrays only): the first tile's
+        // inclusive prefix and the aggregates of the tiles between the two.
+        // The first tile's stores wait for the second tile's scan: issued
+        // earlier, beside the second tile's loads, they slowed those loads,
+        // which lead to the last look-back (fp32 1e7: 19.4 -> 22.0 us).
+        if (!ctrl) scan_rows(tl[1], 1);
+        __syncthreads();
+        if (ctrl) {
+            if (tl[1] < n) {
+                const C agg = scan_entries(1);
+                publish(tl[1], agg);
+                C pre = inc0;
+                if (tl[1] > tl[0] + 1) pre = C(Op::apply(inc0, gap(tl[0] + 1, tl[1])));
+                if (lane == 0) {
+                    s_pre[1] = pre;
+                    if constexpr (!NOID) {
+                        if (a.total_out != nullptr && tl[1] == n - 1)
+                            reinterpret_cast<T *>(a.total_out)[0] = T(Op::apply(pre, agg));
+                    }
                 }
-            } else {
-#pragma unroll
-                for (int c = 0; c < V; c++) y.v[c] = T(Op::apply(pre, C(Op::apply(eb, x[r].v[c]))));
             }
-            // the row step in the vector offset, the scalar offset a constant
-            // 0 (see the column single pass: 128-bit buffer stores with a
-            // scalar-register offset lost their data registers)
-            uint32_t vo = voff + uint32_t(r) * kRowBytes;
-            asm volatile("" : "+v"(vo));
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, y), rs_out, vo, 0, OUT_AUX);
+        } else {
+            store(0, s_pre[0], j0 > 0);
         }
+        __syncthreads();
+        if (!ctrl) store(1, s_pre[1], true);
+    } else {
+        __syncthreads();
+        if (!ctrl) store(0, s_pre[0], j0 > 0);
     }
     // end of the call: in static mode every workgroup was counted before the
-    // decision; in dynamic mode the holder of the last ticket claimed last
-    if (tile == n - 1) end_call(hdr, epoch, s_hw, s_cap, a.pipe.words_used, a.pipe.ws_words, desc);
+    // decision; in dynamic mode the holder of the last tile claimed last
+    bool last = tl[0] == n - 1;
+    if constexpr (SW == 2) last = last || tl[1] == n - 1;
+    if (last) end_call(hdr, s_epoch, s_hw, s_cap, a.pipe.words_used, a.pipe.ws_words, desc);
 }
 
 template <class T, class Op, int OUT_AUX, bool NOID = false>
-static int launch_resident_impl(const ScanArgs &a, int rows, hipStream_t s) {
+static int launch_resident_impl(const ScanArgs &a, int rows, int sweeps, hipStream_t s) {
     constexpr int V = 16 / int(sizeof(T));
     constexpr int MAXR = sizeof(T) == 8 ? kResMaxRows8 : kResMaxRows4;
-    if (rows < 1 || rows > MAXR || a.pipe.num_tiles > uint32_t(kResMaxTiles)) return SCAN_ERR_UNSUPPORTED;
+    constexpr int MAXR2 = sizeof(T) == 8 ? kResMaxRows2x8 : kResMaxRows2x4;  // per tile, two tiles
+    const uint32_t n = a.pipe.num_tiles;
+    if (rows < 1 || sweeps < 1 || sweeps > 2 || rows > (sweeps == 2 ? MAXR2 : MAXR) || n < 1)
+        return SCAN_ERR_UNSUPPORTED;
+    const uint32_t grid = (n + uint32_t(sweeps) - 1) / uint32_t(sweeps);
+    if (grid > uint32_t(kResMaxTiles)) return SCAN_ERR_UNSUPPORTED;
+    if (sweeps == 2 && a.pipe.tiles_per_seg != n) return SCAN_ERR_UNSUPPORTED;  // whole arrays only
     if (NOID && (a.exclusive || a.total_out != nullptr)) return SCAN_ERR_UNSUPPORTED;
-    hipLaunchKernelGGL((k_resident<T, Op, V, MAXR, OUT_AUX, NOID>), dim3(a.pipe.num_tiles), dim3(kResWaves * kWave), 0,
-                       s, a, uint32_t(rows));
+    if (sweeps == 2)
+        hipLaunchKernelGGL((k_resident<T, Op, V, 2 * MAXR2, OUT_AUX, NOID, 2>), dim3(grid), dim3(kResWaves * kWave), 0,
+                           s, a, uint32_t(rows));
+    else
+        hipLaunchKernelGGL((k_resident<T, Op, V, MAXR, OUT_AUX, NOID, 1>), dim3(grid), dim3(kResWaves * kWave), 0, s,
+                           a, uint32_t(rows));
     return hipGetLastError() == hipSuccess ? SCAN_OK : SCAN_ERR_HIP;
 }
 

@@ -154,30 +154,52 @@ def test_plan_small_arrays_take_short_tiles():
 
 def test_plan_resident():
     # The resident pass: one 1024-thread workgroup (15 data waves and a
-    # control wave) per tile of rows x 960 x vec elements, the fewest rows
-    # that keep the tiles within 256, up to 17 rows (4-byte elements) or 21
-    # (8-byte); one descriptor word per tile (two for 64-bit carries); not
-    # with a grid cap, an explicit shape or without an identity; segments
-    # (rows of a 2-D array) when all fit.
+    # control wave) per tile of rows x 960 x vec elements, or per two tiles
+    # for a whole array of 32 MiB or more; the fewest rows that keep the
+    # workgroups within 256, up to 17 rows (4-byte elements) or 21 (8-byte)
+    # with one tile, 8 or 11 per tile with two; one descriptor word per tile
+    # (two for 64-bit carries); not with a grid cap or an explicit shape;
+    # segments (rows of a 2-D array) when all fit, one tile per workgroup.
     from stream_compaction_wave64_amd import binding
     import torch
-    p = binding.plan("scan", torch.float32, "sum", 1, 10 ** 7)   # 11 rows of 3840: 237 tiles
+    one = {"resident_sweeps": 1}
+    p = binding.plan("scan", torch.float32, "sum", 1, 10 ** 7, tuning=one)   # 11 rows of 3840: 237 tiles
     assert (p["kernel"], p["block_size"], p["items_per_thread"], p["num_tiles"]) == ("resident", 1024, 44, 237)
     assert p["workspace_bytes"] == 4096 + 2048 and p["launches"] == 1  # 237 words, in 256-byte units
-    p = binding.plan("scan", torch.float64, "sum", 1, 10 ** 7)   # 21 rows of 1920: 249 tiles
+    assert p["tiles_per_block"] == 1
+    p = binding.plan("scan", torch.float32, "sum", 1, 10 ** 7)   # 6 rows of 3840: 435 tiles, 218 workgroups
+    assert (p["kernel"], p["items_per_thread"], p["num_tiles"], p["tiles_per_block"]) == ("resident", 24, 435, 2)
+    assert p["workspace_bytes"] == 4096 + 3584
+    p = binding.plan("scan", torch.float64, "sum", 1, 10 ** 7, tuning=one)   # 21 rows of 1920: 249 tiles
     assert (p["kernel"], p["items_per_thread"], p["num_tiles"], p["carry_words"]) == ("resident", 42, 249, 2)
-    cap4, cap8 = 256 * 17 * 3840, 256 * 21 * 1920
+    p = binding.plan("scan", torch.float64, "sum", 1, 10 ** 7)   # 11 rows of 1920: 474 tiles, 237 workgroups
+    assert (p["kernel"], p["items_per_thread"], p["num_tiles"], p["tiles_per_block"]) == ("resident", 22, 474, 2)
+    # two tiles from 32 MiB, one below; a forced two below the threshold
+    below = (32 << 20) // 4 - 4
+    assert binding.plan("scan", torch.int32, "sum", 1, below)["tiles_per_block"] == 1
+    assert binding.plan("scan", torch.int32, "sum", 1, below + 4)["tiles_per_block"] == 2
+    assert binding.plan("scan", torch.int32, "sum", 1, 1 << 21, tuning={"resident_sweeps": 2})["tiles_per_block"] == 2
+    # capacities: 256 x 17 rows of 3840 with one tile (two tiles hold 512 x 8
+    # rows, fewer); 512 x 11 rows of 1920 with two (one tile: 256 x 21)
+    cap4, cap8 = 256 * 17 * 3840, 512 * 11 * 1920
     p = binding.plan("scan", torch.int32, "sum", 1, cap4)
-    assert (p["kernel"], p["items_per_thread"], p["num_tiles"]) == ("resident", 68, 256)
+    assert (p["kernel"], p["items_per_thread"], p["num_tiles"], p["tiles_per_block"]) == ("resident", 68, 256, 1)
     assert binding.plan("scan", torch.int32, "sum", 1, cap4 + 4)["kernel"] == "lookback"
-    assert binding.plan("scan", torch.int64, "max", 1, cap8)["kernel"] == "resident"
+    p = binding.plan("scan", torch.int64, "max", 1, cap8)
+    assert (p["kernel"], p["items_per_thread"], p["num_tiles"], p["tiles_per_block"]) == ("resident", 22, 512, 2)
     assert binding.plan("scan", torch.int64, "max", 1, cap8 + 2)["kernel"] == "lookback"
+    assert binding.plan("scan", torch.int64, "max", 1, 256 * 21 * 1920 + 2, tuning=one)["kernel"] == "lookback"
     p = binding.plan("scan", torch.float32, "sum", 4, 1 << 20)    # segments: 4 x 55 tiles of 5 rows
     assert (p["kernel"], p["num_tiles"], p["items_per_thread"]) == ("resident", 220, 20)
+    p = binding.plan("scan", torch.float32, "sum", 4, 3 << 20)    # 48 MiB of segments: one tile per workgroup
+    assert (p["kernel"], p["tiles_per_block"]) == ("resident", 1), p
     for tu in ({"grid_blocks": 8}, {"block_size": 768, "items_per_thread": 28}, {"algo": "reduce_then_scan"}):
         assert binding.plan("scan", torch.float32, "sum", 1, 10 ** 7, tuning=tu)["kernel"] != "resident", tu
+        assert binding.plan("scan", torch.float32, "sum", 1, 10 ** 7, tuning=tu)["tiles_per_block"] == 0, tu
     # inclusive scans without an identity take it too (Optional partials)
     p = binding.plan("scan", torch.float32, "sum", 1, 10 ** 7, tuning={"no_identity": 1})
+    assert (p["kernel"], p["num_tiles"], p["items_per_thread"]) == ("resident", 435, 24)
+    p = binding.plan("scan", torch.float32, "sum", 1, 10 ** 7, tuning={"no_identity": 1, "resident_sweeps": 1})
     assert (p["kernel"], p["num_tiles"], p["items_per_thread"]) == ("resident", 237, 44)
     assert binding.plan("scan", torch.float32, "sum", 1, 10 ** 7,
                         tuning={"no_identity": 1, "grid_blocks": 8})["kernel"] == "lookback"

@@ -187,6 +187,51 @@ def test_resident_pass_failure_paths():
         _recovers(ws, x, xd)
 
 
+def test_resident_two_tile_failure_paths():
+    # The resident pass with two tiles per workgroup under the same forced
+    # conditions: dynamic claiming (claim k takes tiles 2k and 2k + 1 and
+    # reloads them; its first tile reads up to 510 aggregates, two gap reads),
+    # late publishers on both tiles' aggregates (with and without an
+    # identity), and a garbage epoch whose waits give up.
+    x = inputs.generic(np.int32, 10_000_004, 72, "wide")
+    xd = to_dev(x)
+    p = sw.plan("scan", torch.int32, "sum", 1, x.size)
+    assert (p["kernel"], p["tiles_per_block"], p["num_tiles"] % 2) == ("resident", 2, 1), p
+    ws = torch.zeros(1 << 22, dtype=torch.uint8, device=DEV)
+    with _Installed(ws):
+        for excl in (False, True):
+            ws[128:132].view(torch.int32)[0] = -1
+            fn = sw.scan_exclusive if excl else sw.scan_inclusive
+            r = fn(xd, tuning={"mode_limit": 8})
+            torch.cuda.synchronize()
+            assert sw.scan_workspace_error(ws) == 4
+            assert_scan_matches(x, to_host(r), "sum", excl, what=f"dynamic excl={excl}")
+        ws[128:132].view(torch.int32)[0] = -1
+        r = sw.scan_inclusive(xd, op="max", tuning={"mode_limit": 8, "no_identity": 1})
+        torch.cuda.synchronize()
+        assert sw.scan_workspace_error(ws) == 4
+        assert_scan_matches(x, to_host(r), "max", False, what="no identity, dynamic", noid=True)
+        sw.scan_workspace_init(ws)
+        f = inputs.generic(np.float32, 10_000_012, 73)
+        fd = to_dev(f)
+        assert sw.plan("scan", torch.float32, "sum", 1, f.size)["tiles_per_block"] == 2
+        for stride, sleeps in DELAYS:
+            for excl in (False, True):
+                fn = sw.scan_exclusive if excl else sw.scan_inclusive
+                r = fn(fd, tuning={"delay_stride": stride, "delay_sleeps": sleeps})
+                torch.cuda.synchronize()
+                assert_scan_matches(f, to_host(r), "sum", excl, what=f"late publishers {stride} {sleeps}")
+            r = sw.scan_inclusive(fd, tuning={"delay_stride": stride, "delay_sleeps": sleeps, "no_identity": 1})
+            torch.cuda.synchronize()
+            assert_scan_matches(f, to_host(r), "sum", False, what=f"no identity, late {stride} {sleeps}", noid=True)
+        assert sw.scan_workspace_error(ws) == 0
+        ws[:16].view(torch.int32)[0] = 1 << 30
+        sw.scan_inclusive(xd, tuning={"spin_limit": 32})
+        torch.cuda.synchronize()
+        assert sw.scan_workspace_error(ws) & 1
+        _recovers(ws, x, xd)
+
+
 def test_resident_compaction_failure_paths():
     # The resident compaction under the same forced conditions: dynamic
     # claiming (flag bit 2), late publishers, a garbage epoch (flag bit 0).

@@ -82,7 +82,9 @@ def test_parity_across_shape_switches(dt, op):
     vec = 16 // es
     big = sw.plan("scan", TORCH[np.dtype(dt)], op, 1, 10 ** 8)
     res_min = (8 << 20) // es
-    cap = 256 * (17 if es == 4 else 21) * 960 * vec
+    # capacity: 256 tiles of 17 rows (4-byte), 512 tiles of 11 rows two per
+    # workgroup (8-byte)
+    cap = 256 * 17 * 960 * vec if es == 4 else 512 * 11 * 960 * vec
     cases = [(res_min - vec, "lookback", 448 * 5 * vec), (res_min, "resident", None), (cap, "resident", None),
              (cap + vec, "lookback", big["tile_elems"])]
     for i, (n, kernel, tile) in enumerate(cases):
@@ -91,7 +93,8 @@ def test_parity_across_shape_switches(dt, op):
         if tile is not None:
             assert p["tile_elems"] == tile, (n, p)
         else:
-            assert p["num_tiles"] <= 256 and p["block_size"] == 1024, (n, p)
+            blocks = -(-p["num_tiles"] // p["tiles_per_block"])
+            assert blocks <= 256 and p["block_size"] == 1024, (n, p)
         if op not in ("sum", "max") and n > res_min:
             continue  # the two largest sizes: sum and max only (time)
         x = _input(dt, n, 400 + i, op)
@@ -117,6 +120,36 @@ def test_parity_resident(dt, op):
         x = _input(dt, n, 500 + i, op)
         for excl in (False, True):
             assert_scan_matches(x, _run(x, op, excl), op, excl, what=f"n={n} rows={p['items_per_thread'] // vec}")
+
+
+@pytest.mark.parametrize("dt", DTYPES, ids=lambda d: np.dtype(d).name)
+@pytest.mark.parametrize("op", OPS)
+def test_parity_resident_two_tiles(dt, op):
+    # The resident pass with two tiles per workgroup (whole arrays from 32
+    # MiB; workgroup w holds tiles w and w + G): an odd tile count (the last
+    # workgroup has no second tile) with a ragged last tile, an even count
+    # ending in a partial vector row, the form's capacity (512 full tiles),
+    # and a forced two-tile plan below the threshold (two rows per tile).
+    es = np.dtype(dt).itemsize
+    vec = 16 // es
+    re = 960 * vec
+    rows = 8 if es == 4 else 11
+    even = 436 * 6 * re - 3 * vec if es == 4 else 10 ** 7
+    sizes = [((32 << 20) // es + 3 * vec, None), (even, None), (512 * rows * re, None),
+             ((8 << 20) // es, {"resident_sweeps": 2})]
+    if op not in ("sum", "max"):
+        sizes = sizes[:1] + sizes[3:]  # time: the other operators at the small sizes
+    counts = set()
+    for i, (n, tuning) in enumerate(sizes):
+        p = sw.plan("scan", TORCH[np.dtype(dt)], op, 1, n, tuning=tuning)
+        assert p["kernel"] == "resident" and p["tiles_per_block"] == 2, (n, p)
+        assert -(-p["num_tiles"] // 2) <= 256, (n, p)
+        counts.add(p["num_tiles"] % 2)
+        x = _input(dt, n, 520 + i, op)
+        for excl in (False, True):
+            assert_scan_matches(x, _run(x, op, excl, tuning), op, excl,
+                                what=f"n={n} tiles={p['num_tiles']} rows={p['items_per_thread'] // vec}")
+    assert counts == {0, 1}, "odd and even tile counts"
 
 
 @pytest.mark.parametrize("dt", DTYPES, ids=lambda d: np.dtype(d).name)
