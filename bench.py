@@ -5,6 +5,9 @@ A step is one scan_inclusive call (one kernel launch of the single-pass
 look-back scan) over the resident 1e8-element fp32 array (uniform [0,1),
 seed 1).  W untimed warmup steps, then K timed steps bracketed by device
 synchronisation, timed with HIP events on the stream the kernels run on.
+The K timed calls are captured into one HIP graph and replayed once, so the
+time between launches is the device's, not the Python host's (--eager
+launches them one by one).
 
 Prints one JSON line with the throughput (GElem/s), the roofline of the scan
 kernel (algorithmic bytes = one read + one write of n fp32 values per launch,
@@ -61,30 +64,67 @@ def _kernel_sources_sha():
 def parse():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--algo", default="lookback", choices=["lookback", "reduce_then_scan"])
     ap.add_argument("--block", type=int, default=0, help="tuning: threads per workgroup")
     ap.add_argument("--ipt", type=int, default=0, help="tuning: items per thread")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle leg (profiling runs)")
     ap.add_argument("--no-verify", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch the timed headline steps one by one instead of from one HIP graph")
     ap.add_argument("--no-rows", action="store_true", help="time only the headline fp32 1e8 scan")
     ap.add_argument("--row-steps", type=int, default=20, help="calls timed per row")
     ap.add_argument("--rows", default="", help="comma-separated row names to time (default: every row)")
     return ap.parse_args()
 
 
-def timed(fn, steps, warmup, stream):
+def _upload_graph(g, stream):
+    """Upload the instantiated graph to the device before it is timed, so that
+    the timed replay does not include the one-time upload (no kernel runs)."""
+    import ctypes
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        hip.hipGraphUpload.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        rc = hip.hipGraphUpload(ctypes.c_void_p(g.raw_cuda_graph_exec()), ctypes.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            print(f"# hipGraphUpload returned {rc}; the timed replay includes the upload", file=sys.stderr)
+    except (OSError, AttributeError, RuntimeError, TypeError) as e:
+        print(f"# graph upload skipped ({e}); the timed replay includes the upload", file=sys.stderr)
+
+
+def timed(fn, steps, warmup, graph=True):
+    """ms per step: `warmup` eager calls, then the `steps` calls, launched
+    from one HIP graph holding all of them (default) or one by one.  All on
+    one side stream, whose workspace the warmup allocates (at least one
+    warmup call with a graph, so nothing is allocated during capture)."""
     import torch
-    for _ in range(warmup):
-        fn()
-    torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for _ in range(steps):
-        fn()
-    end.record(stream)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(max(warmup, 1) if graph else warmup):
+            fn()
+        torch.cuda.synchronize()
+        g = None
+        if graph:
+            g = torch.cuda.CUDAGraph()
+            g.capture_begin()
+            try:
+                for _ in range(steps):
+                    fn()
+            finally:
+                g.capture_end()
+            _upload_graph(g, side)
+            torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record(side)
+        if g is not None:
+            g.replay()
+        else:
+            for _ in range(steps):
+                fn()
+        end.record(side)
     torch.cuda.synchronize()
     return start.elapsed_time(end) / steps  # ms per step
 
@@ -373,7 +413,6 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    stream = torch.cuda.current_stream(dev)
     x_host = inputs.f32_uniform_01(N, seed=1)
     x = torch.from_numpy(x_host).to(dev)
     out = torch.empty_like(x)
@@ -384,9 +423,10 @@ def main():
         tuning["items_per_thread"] = args.ipt
     plan = sw.plan("scan", torch.float32, "sum", 1, N, tuning=tuning)
 
-    ms = timed(lambda: sw.scan_inclusive(x, out=out, tuning=tuning), args.steps, args.warmup, stream)
+    graph = not args.eager
+    ms = timed(lambda: sw.scan_inclusive(x, out=out, tuning=tuning), args.steps, args.warmup, graph)
     copy_out = torch.empty_like(x)
-    ms_copy = timed(lambda: sw.scan_copy(x, copy_out), args.steps, args.warmup, stream)
+    ms_copy = timed(lambda: sw.scan_copy(x, copy_out), args.steps, args.warmup, graph)
 
     alg_bytes = 2 * N * 4
     achieved = alg_bytes / (ms * 1e-3) / 1e9
@@ -408,7 +448,8 @@ def main():
                    "n": N, "op": "sum", "algo": args.algo, "kernel": plan["kernel"],
                    "launches_per_step": plan["launches"], "block": plan["block_size"],
                    "items_per_thread": plan["items_per_thread"], "tile_elems": plan["tile_elems"],
-                   "num_tiles": plan["num_tiles"]},
+                   "num_tiles": plan["num_tiles"],
+                   "launch": "one HIP graph of the timed steps" if graph else "one call per step"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": TRAFFIC_BYTES if (_kernel_sources_sha() == TRAFFIC_SOURCES_SHA
