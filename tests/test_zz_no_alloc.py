@@ -88,3 +88,18 @@ def test_noalloc_struct_elements():
         assert_scan_matches(x.reshape(n, 17), got.reshape(n, 17), "sum", False, dims=(1, n, 17),
                             what=f"struct n={n}")
         _same_result(x, got, _with_workspace(x, "sum", width=17), "sum", dims=(1, n, 17), what=f"struct n={n}")
+
+
+@pytest.mark.parametrize("dt,op", [(np.int32, "sum"), (np.float64, "sum"), (np.float32, "max")])
+def test_noalloc_two_tile_resident_then_smaller(dt, op):
+    # whole arrays of 32 MiB or more take the resident pass with two tiles per
+    # workgroup; then a one-tile resident call on the same scratch array
+    es = np.dtype(dt).itemsize
+    kind = "default" if np.issubdtype(dt, np.floating) and op == "sum" else "wide"
+    big = (40 << 20) // es + 16 // es
+    assert sw.plan("scan", torch.int32 if es == 4 else torch.float64, "sum", 1, big)["tiles_per_block"] == 2
+    for i, n in enumerate([big, (12 << 20) // es]):
+        x = inputs.generic(dt, n, 520 + i, kind)
+        got = _noalloc(x, op)
+        assert_scan_matches(x, got, op, False, what=f"noalloc n={n}")
+        _same_result(x, got, _with_workspace(x, op), op, what=f"n={n}")
