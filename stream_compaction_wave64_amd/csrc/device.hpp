@@ -360,7 +360,11 @@ __device__ __forceinline__ uint32_t started_sum(const WsHeader *hdr) {
 // static mode; one that waits `limit` polls without seeing them selects
 // dynamic mode, where tiles are claimed in order from a counter -- slower
 // (one same-address atomic per tile), but deadlock-free with any number of
-// resident workgroups.  No descriptor is published before the decision.
+// resident workgroups.  No tile waits on another before the decision; the
+// resident passes publish their static first tile's aggregate before it,
+// which is safe because a tile's aggregate depends only on its data, so the
+// workgroup that processes the tile in either mode publishes the same words
+// (aggregates only: a word never changes state within a call).
 // Each poll reads the mode word and the counters in one round trip; the
 // compare-and-swap returns the decided mode whether or not it won.  The
 // mode word carries the epoch it was decided in ((epoch << 2) | mode) and

@@ -269,100 +269,116 @@ __global__ __launch_bounds__(kResWaves *kWave) void k_resident(ScanArgs a, uint3
         }
     };
 
-    // The control wave runs the workspace protocol; the data waves load the
-    // static tiles and scan the first meanwhile (each row as it arrives),
-    // and load and scan again after the barrier if dynamic mode gave the
-    // workgroup other tiles.
+    // The control wave and the data waves run separate programs (the branch
+    // is uniform within each wave) that meet at the same barriers, so the
+    // control wave's code is not compiled around the data waves' tile
+    // registers.  Barriers: B1 (the static first tile scanned), Bm (the
+    // mode decided), in dynamic mode Bd (the claimed tiles loaded and their
+    // first scanned), B2 (the first tile's prefix known; with two tiles,
+    // the second scanned), and with two tiles B3 (the second's prefix).
+    //
+    // The static first tile's aggregate is published before the residency
+    // decision, which waits for every workgroup to start (about 2 us of
+    // each call when it came first), so the look-backs that follow it find
+    // their predecessors published.  A tile's aggregate depends only on its
+    // data, so whoever processes the tile in either mode publishes the same
+    // words; only waiting on predecessors needs the decision.
+    uint32_t tl[SW];  // this workgroup's tiles: static, w (and w + G); dynamic, claim k's SW * k (and SW * k + 1)
+    tl[0] = blockIdx.x;
+    if constexpr (SW == 2) tl[1] = blockIdx.x + gridDim.x;
+    int64_t start0, rem0;
+    uint32_t seg0, j0;
     if (ctrl) {
         if (lane == 0) {
             uint64_t hw = 0, cap = 0;
-            const uint32_t e = begin_call(hdr, hw, cap);
-            s_epoch = e;
+            s_epoch = begin_call(hdr, hw, cap);
             s_hw = hw;
             s_cap = cap;
-            const uint32_t m = decide_mode(hdr, e, gridDim.x, a.pipe.mode_limit);
-            s_dyn = m == kModeStatic ? 0u : 1u;
-            s_claim = m == kModeStatic
-                          ? uint32_t(blockIdx.x)
-                          : __hip_atomic_fetch_add(&hdr->claim, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-    } else {
-        load(blockIdx.x, 0);
-        if constexpr (SW == 2) load(blockIdx.x + gridDim.x, 1);
-        scan_rows(blockIdx.x, 0);
-    }
-    __syncthreads();
-    // this workgroup's tiles: static, w (and w + G); dynamic, claim k's
-    // SW * k (and SW * k + 1)
-    const bool dyn = s_dyn != 0u;
-    const uint32_t claim = s_claim;
-    uint32_t tl[SW];
-    tl[0] = dyn ? uint32_t(SW) * claim : claim;
-    if constexpr (SW == 2) tl[1] = dyn ? 2u * claim + 1u : claim + gridDim.x;
-    if (SW == 2 ? dyn : claim != blockIdx.x) {
-        // every wave sees the same words, so all or none take this branch
-        // and its barrier
-        if (!ctrl) {
-            load(tl[0], 0);
-            if constexpr (SW == 2) load(tl[1], 1);
-            scan_rows(tl[0], 0);
+        __syncthreads();  // B1
+        geom(tl[0], start0, rem0, seg0, j0);
+        C agg = scan_entries(0);
+        if (tps > 1) publish(tl[0], agg);
+        uint32_t dm = 0, ck = 0;
+        if (lane == 0) {
+            const uint32_t m = decide_mode(hdr, s_epoch, gridDim.x, a.pipe.mode_limit);
+            dm = m == kModeStatic ? 0u : 1u;
+            ck = m == kModeStatic ? uint32_t(blockIdx.x)
+                                  : __hip_atomic_fetch_add(&hdr->claim, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            s_dyn = dm;
+            s_claim = ck;
         }
-        __syncthreads();
-    }
-    int64_t start0, rem0;
-    uint32_t seg0, j0;
-    geom(tl[0], start0, rem0, seg0, j0);
-    // First tile: its aggregate published and the aggregates of the
-    // segment's earlier tiles combined.
-    C inc0{};  // its inclusive prefix (SW = 2)
-    if (ctrl) {
-        const C agg = scan_entries(0);
+        dm = uint32_t(__builtin_amdgcn_readlane(int(dm), 0));
+        ck = uint32_t(__builtin_amdgcn_readlane(int(ck), 0));
+        __syncthreads();  // Bm
+        if (dm != 0u) {
+            tl[0] = uint32_t(SW) * ck;
+            if constexpr (SW == 2) tl[1] = 2u * ck + 1u;
+            __syncthreads();  // Bd
+            geom(tl[0], start0, rem0, seg0, j0);
+            agg = scan_entries(0);
+            if (tps > 1) publish(tl[0], agg);
+        }
         C pre{};
         if constexpr (!NOID) pre = Op::template identity<C>();
-        if (tps > 1) {
-            publish(tl[0], agg);
-            if (j0 > 0) pre = gap(tl[0] - j0, tl[0]);
-        }
-        inc0 = j0 > 0 ? C(Op::apply(pre, agg)) : agg;
+        if (tps > 1 && j0 > 0) pre = gap(tl[0] - j0, tl[0]);
+        const C inc0 = j0 > 0 ? C(Op::apply(pre, agg)) : agg;
         if (lane == 0) {
             s_pre[0] = pre;
             if constexpr (!NOID) {
                 if (a.total_out != nullptr && j0 == tps - 1) reinterpret_cast<T *>(a.total_out)[seg0] = T(inc0);
             }
         }
-    }
-    if constexpr (SW == 2) {
-        // Second tile (same segment: whole arrays only): the first tile's
-        // inclusive prefix and the aggregates of the tiles between the two.
-        // The first tile's stores wait for the second tile's scan: issued
-        // earlier, beside the second tile's loads, they slowed those loads,
-        // which lead to the last look-back (fp32 1e7: 19.4 -> 22.0 us).
-        if (!ctrl) scan_rows(tl[1], 1);
-        __syncthreads();
-        if (ctrl) {
+        __syncthreads();  // B2
+        if constexpr (SW == 2) {
+            // Second tile (same segment: whole arrays only): the first
+            // tile's inclusive prefix and the aggregates of the tiles
+            // between the two, while the data waves store the first tile.
             if (tl[1] < n) {
-                const C agg = scan_entries(1);
-                publish(tl[1], agg);
-                C pre = inc0;
-                if (tl[1] > tl[0] + 1) pre = C(Op::apply(inc0, gap(tl[0] + 1, tl[1])));
+                const C agg1 = scan_entries(1);
+                publish(tl[1], agg1);
+                C pre1 = inc0;
+                if (tl[1] > tl[0] + 1) pre1 = C(Op::apply(inc0, gap(tl[0] + 1, tl[1])));
                 if (lane == 0) {
-                    s_pre[1] = pre;
+                    s_pre[1] = pre1;
                     if constexpr (!NOID) {
                         if (a.total_out != nullptr && tl[1] == n - 1)
-                            reinterpret_cast<T *>(a.total_out)[0] = T(Op::apply(pre, agg));
+                            reinterpret_cast<T *>(a.total_out)[0] = T(Op::apply(pre1, agg1));
                     }
                 }
             }
-        } else {
-            store(0, s_pre[0], j0 > 0);
+            __syncthreads();  // B3
         }
-        __syncthreads();
-        if (!ctrl) store(1, s_pre[1], true);
     } else {
-        __syncthreads();
-        if (!ctrl) store(0, s_pre[0], j0 > 0);
+        load(tl[0], 0);
+        if constexpr (SW == 2) load(tl[1], 1);
+        scan_rows(tl[0], 0);
+        __syncthreads();  // B1
+        if constexpr (SW == 2) scan_rows(tl[1], 1);
+        __syncthreads();  // Bm
+        if (s_dyn != 0u) {
+            const uint32_t ck = s_claim;
+            tl[0] = uint32_t(SW) * ck;
+            if constexpr (SW == 2) tl[1] = 2u * ck + 1u;
+            load(tl[0], 0);
+            if constexpr (SW == 2) load(tl[1], 1);
+            scan_rows(tl[0], 0);
+            __syncthreads();  // Bd
+            if constexpr (SW == 2) scan_rows(tl[1], 1);
+        }
+        geom(tl[0], start0, rem0, seg0, j0);
+        __syncthreads();  // B2
+        // The first tile's stores wait for the second tile's scan (above):
+        // issued earlier, beside the second tile's loads, they slowed those
+        // loads, which lead to the last look-back (fp32 1e7: 19.4 -> 22.0 us).
+        store(0, s_pre[0], j0 > 0);
+        if constexpr (SW == 2) {
+            __syncthreads();  // B3
+            store(1, s_pre[1], true);
+        }
     }
-    // end of the call: in static mode every workgroup was counted before the
+    // end of the call (every thread: the clearing is strided over the
+    // workgroup): in static mode every workgroup was counted before the
     // decision; in dynamic mode the holder of the last tile claimed last
     bool last = tl[0] == n - 1;
     if constexpr (SW == 2) last = last || tl[1] == n - 1;
