@@ -263,7 +263,7 @@ __global__ __launch_bounds__(kResWaves *kWave) void k_compact_resident(A a, uint
     __shared__ int32_t sval[PART ? CH * RE : 1];  // partition: the chunk's values in output order
     __shared__ int32_t ent[MAXR * NDW];   // (row, wave) counts, then their exclusive prefixes in the tile
     __shared__ int32_t s_pre, s_nsel, s_total;
-    __shared__ uint32_t s_epoch, s_tile;
+    __shared__ uint32_t s_epoch, s_dyn, s_claim;  // s_dyn: nonzero in dynamic mode
     __shared__ uint64_t s_hw, s_cap;
     WsHeader *hdr = reinterpret_cast<WsHeader *>(a.pipe.ws);
     uint64_t *desc = reinterpret_cast<uint64_t *>(reinterpret_cast<char *>(a.pipe.ws) + kWsHeaderBytes);
@@ -313,40 +313,9 @@ __global__ __launch_bounds__(kResWaves *kWave) void k_compact_resident(A a, uint
             }
         }
     };
-    uint32_t tile = blockIdx.x;
-    if (ctrl) {
-        uint32_t tk = 0;
-        if (lane == 0) {
-            uint64_t hw = 0, cap = 0;
-            const uint32_t e = begin_call(hdr, hw, cap);
-            s_epoch = e;
-            s_hw = hw;
-            s_cap = cap;
-            const uint32_t m = decide_mode(hdr, e, gridDim.x, a.pipe.mode_limit);
-            tk = m == kModeStatic
-                     ? uint32_t(blockIdx.x)
-                     : __hip_atomic_fetch_add(&hdr->claim, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            s_tile = tk;
-        }
-        tile = uint32_t(__builtin_amdgcn_readlane(int(tk), 0));
-    } else {
-        load(tile);
-        select_rows(tile);
-    }
-    __syncthreads();
-    if (s_tile != blockIdx.x) {
-        // dynamic mode gave the workgroup another tile (every wave sees the
-        // same s_tile, so all or none take this branch and its barrier)
-        tile = s_tile;
-        if (!ctrl) {
-            load(tile);
-            select_rows(tile);
-        }
-        __syncthreads();
-    }
-    const uint32_t epoch = s_epoch;
-    const int64_t start = int64_t(tile) * tile_elems;
-    if (ctrl) {
+    // The control wave: the tile's (row, wave) counts into their exclusive
+    // offsets in LDS, the tile's count published.
+    auto scan_counts = [&](uint32_t t) {
         const uint32_t ne = rows * NDW;
         int32_t e[KE];
         int32_t acc = 0;
@@ -368,15 +337,71 @@ __global__ __launch_bounds__(kResWaves *kWave) void k_compact_resident(A a, uint
         if (lane == 0) {
             s_nsel = nsel;
             if (nt > 1) {
-                if (a.pipe.delay_stride > 0 && tile % a.pipe.delay_stride == a.pipe.delay_stride - 1) {
+                if (a.pipe.delay_stride > 0 && t % a.pipe.delay_stride == a.pipe.delay_stride - 1) {
                     // a late publisher, so tests reach the look-back's re-polls
                     for (uint32_t i = 0; i < a.pipe.delay_sleeps; i++) __builtin_amdgcn_s_sleep(64);
                 }
-                D::publish(desc + uint64_t(tile) * D::kWords, epoch, kStateA, nsel);
+                D::publish(desc + uint64_t(t) * D::kWords, s_epoch, kStateA, nsel);
             }
         }
+    };
+    // As in the resident scan (resident.hip): the control wave starts the
+    // call and, for tiles of at most kResLateDecisionRows rows, publishes its
+    // static tile's count before the residency decision (the tile's claimer
+    // in dynamic mode publishes the same word); longer tiles decide while
+    // they load.  The two kinds of waves run separate programs that meet at
+    // the same barriers: B1 (the static tile's rows selected), Bm (the mode
+    // decided; in static mode the offsets ready), and in dynamic mode Bd
+    // (the claimed tile selected) and Bp (its offsets ready).
+    uint32_t tile = blockIdx.x;
+    if (ctrl) {
+        // short tiles decide after publishing, long ones while loading
+        const bool late = rows <= uint32_t(kResLateDecisionRows);
+        uint32_t dm = 0, ck = 0;
+        auto decide = [&]() {
+            const uint32_t m = decide_mode(hdr, s_epoch, gridDim.x, a.pipe.mode_limit);
+            dm = m == kModeStatic ? 0u : 1u;
+            ck = m == kModeStatic ? uint32_t(blockIdx.x)
+                                  : __hip_atomic_fetch_add(&hdr->claim, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        };
+        if (lane == 0) {
+            uint64_t hw = 0, cap = 0;
+            s_epoch = begin_call(hdr, hw, cap);
+            s_hw = hw;
+            s_cap = cap;
+            if (!late) decide();
+        }
+        __syncthreads();  // B1
+        scan_counts(tile);
+        if (lane == 0) {
+            if (late) decide();
+            s_dyn = dm;
+            s_claim = ck;
+        }
+        dm = uint32_t(__builtin_amdgcn_readlane(int(dm), 0));
+        ck = uint32_t(__builtin_amdgcn_readlane(int(ck), 0));
+        __syncthreads();  // Bm
+        if (dm != 0u) {
+            tile = ck;
+            __syncthreads();  // Bd
+            scan_counts(tile);
+            __syncthreads();  // Bp
+        }
+    } else {
+        load(tile);
+        select_rows(tile);
+        __syncthreads();  // B1
+        __syncthreads();  // Bm
+        if (s_dyn != 0u) {
+            tile = s_claim;
+            load(tile);
+            select_rows(tile);
+            __syncthreads();  // Bd
+            __syncthreads();  // Bp
+        }
     }
-    __syncthreads();
+    const uint32_t epoch = s_epoch;
+    const int64_t start = int64_t(tile) * tile_elems;
     if constexpr (PART) {
         const int64_t rem = a.n - start;
         const int32_t nsel = s_nsel;

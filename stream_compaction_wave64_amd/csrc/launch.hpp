@@ -38,6 +38,15 @@ LbLaunch find_pack_lookback(int block, int rows, int vec);  // int32 sum, offset
 constexpr int kResWaves = 16;
 constexpr int kResMaxRows4 = 17, kResMaxRows8 = 21;  // 68 and 84 data registers per thread
 constexpr int kResMaxRows2x4 = 8, kResMaxRows2x8 = 11;  // rows per tile with two tiles: 64 and 88 registers
+// Resident compactions, and resident scans with two tiles per workgroup,
+// whose first tile has at most this many rows decide the residency after
+// publishing it (their loads end before the decision would); longer tiles
+// decide while they load.  Measured: compaction of 1e7 keys in 11-row tiles
+// 18.1 us deciding early, 19.4 late; 2^21 keys in 3-row tiles 10.0 early,
+// 9.1 late; scan of 1e7 fp32 in two 6-row tiles 18.6 early, 17.4 late.  A
+// scan with one tile per workgroup decides early at any size (int32 2^22
+// in 5-row tiles: 10.6 us early, 11.4 late).
+constexpr int kResLateDecisionRows = 8;
 constexpr int64_t kResMaxTiles = 256;                // one per compute unit on MI355X
 using ResLaunch = int (*)(const ScanArgs &, int rows, int sweeps, hipStream_t);
 ResLaunch find_resident(scan_dtype_t dt, scan_op_t op);

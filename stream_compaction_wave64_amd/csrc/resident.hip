@@ -67,6 +67,7 @@ __global__ __launch_bounds__(kResWaves *kWave) void k_resident(ScanArgs a, uint3
     constexpr int RE = NDW * kWave * V;                         // elements per tile row
     constexpr int KE = ((MAXR / SW) * NDW + kWave - 1) / kWave;  // (row, wave) totals per lane of the control wave
     constexpr int NRW = int(kResMaxTiles / kWave);              // look-back windows of 64 tiles
+    constexpr int MS = MAXR / SW;                               // register rows (slots) per tile
     static_assert(V * sizeof(T) == 16, "128-bit rows");
     __shared__ T ent[MAXR * NDW];        // (row, wave) totals, then their exclusive prefixes in the tile
     __shared__ C s_pre[SW];              // each tile's exclusive prefix (NOID: none for a segment's first tile)
@@ -93,8 +94,9 @@ __global__ __launch_bounds__(kResWaves *kWave) void k_resident(ScanArgs a, uint3
     };
     // Buffer accesses from the tile's first element, bounded by the segment:
     // rows and vectors past its end read 0 (replaced by the identity below)
-    // and drop their stores.  Tile s of the workgroup holds rows
-    // s * rows .. s * rows + rows - 1 of x.
+    // and drop their stores.  Tile s of the workgroup holds its rows in the
+    // register slots x[s * MS ..], its (row, wave) totals in LDS from entry
+    // row s * rows.
     Vec<T, V> x[MAXR];
     const uint32_t voff = dt * V * uint32_t(sizeof(T));
     constexpr uint32_t kRowBytes = uint32_t(RE) * sizeof(T);
@@ -107,12 +109,18 @@ __global__ __launch_bounds__(kResWaves *kWave) void k_resident(ScanArgs a, uint3
         if (t >= n) cnt = 0;  // no such tile (an odd tile count's last workgroup): nothing in range
         rs_in[s] = make_rsrc(in + start, cnt);
         rs_out[s] = make_rsrc(out + start, cnt);
-        const uint32_t r0 = uint32_t(s) * rows;
+        // The first tile loads its rows only.  The second loads every slot,
+        // rows past `rows` from beyond the buffer's range (they read 0 and
+        // touch no memory): a fixed number of loads after the first tile's,
+        // so the first tile's scan waits for its own loads only.  (With the
+        // second tile's loads also counted at run time, the first tile's
+        // scan waited for every load; with every slot loaded in one-tile
+        // plans of few rows, the unused loads cost int32 2^22 10.9 -> 12.4 us.)
 #pragma unroll
-        for (int r = 0; r < MAXR; r++) {
-            if (uint32_t(r) >= r0 && uint32_t(r) < r0 + rows)
-                x[r] = __builtin_bit_cast(
-                    Vec<T, V>, __builtin_amdgcn_raw_buffer_load_b128(rs_in[s], voff, (uint32_t(r) - r0) * kRowBytes, 2));
+        for (int rr = 0; rr < MS; rr++) {
+            if (s == 1 || uint32_t(rr) < rows)
+                x[s * MS + rr] = __builtin_bit_cast(
+                    Vec<T, V>, __builtin_amdgcn_raw_buffer_load_b128(rs_in[s], voff, uint32_t(rr) * kRowBytes, 2));
         }
     };
     // Each row of the tile: this thread's vector scanned, then across the
@@ -124,11 +132,12 @@ __global__ __launch_bounds__(kResWaves *kWave) void k_resident(ScanArgs a, uint3
         uint32_t seg_, j_;
         geom(t, start_, rem_, seg_, j_);
         const int64_t e_thread = int64_t(dt) * V;
-        const uint32_t r0 = uint32_t(s) * rows;
 #pragma unroll
-        for (int r = 0; r < MAXR; r++) {
-            if (uint32_t(r) >= r0 && uint32_t(r) < r0 + rows) {
-                const int64_t e0 = int64_t(uint32_t(r) - r0) * RE + e_thread;
+        for (int rr = 0; rr < MS; rr++) {
+            const int r = s * MS + rr;                    // register slot
+            const uint32_t er = uint32_t(s) * rows + rr;  // (row, wave) entry row
+            if (uint32_t(rr) < rows) {
+                const int64_t e0 = int64_t(rr) * RE + e_thread;
                 T inc[V];
                 T acc = x[r].v[0];
 #pragma unroll
@@ -144,7 +153,7 @@ __global__ __launch_bounds__(kResWaves *kWave) void k_resident(ScanArgs a, uint3
                     const T wex = dpp_mov<kWaveShr1>(winc, winc);
 #pragma unroll
                     for (int c = 0; c < V; c++) x[r].v[c] = lane > 0 ? Op::apply(wex, inc[c]) : inc[c];
-                    if (lane == kWave - 1) ent[r * NDW + dw] = winc;
+                    if (lane == kWave - 1) ent[er * NDW + dw] = winc;
                 } else {
                     const T id = Op::template identity<T>();
                     const T winc = wave_scan_incl<Op>(acc);
@@ -153,7 +162,7 @@ __global__ __launch_bounds__(kResWaves *kWave) void k_resident(ScanArgs a, uint3
                     for (int c = 0; c < V; c++)
                         x[r].v[c] =
                             a.exclusive ? (c == 0 ? wex : Op::apply(wex, inc[c - 1])) : Op::apply(wex, inc[c]);
-                    if (lane == kWave - 1) ent[r * NDW + dw] = winc;
+                    if (lane == kWave - 1) ent[er * NDW + dw] = winc;
                 }
             }
         }
@@ -239,16 +248,16 @@ __global__ __launch_bounds__(kResWaves *kWave) void k_resident(ScanArgs a, uint3
     // Tile s's results: (row, wave) prefix, then the tile's prefix (carry
     // type, one rounding); has_pre false for a segment's first tile.
     auto store = [&](int s, const C &pre, bool has_pre) {
-        const uint32_t r0 = uint32_t(s) * rows;
 #pragma unroll
-        for (int r = 0; r < MAXR; r++) {
-            if (uint32_t(r) >= r0 && uint32_t(r) < r0 + rows) {
-                const T eb = ent[r * NDW + dw];
+        for (int rr = 0; rr < MS; rr++) {
+            const int r = s * MS + rr;
+            if (uint32_t(rr) < rows) {
+                const T eb = ent[(uint32_t(s) * rows + rr) * NDW + dw];
                 Vec<T, V> y;
                 if constexpr (NOID) {
                     // entry (0, 0) has nothing before it in the tile, and a
                     // segment's first tile has nothing before it
-                    const bool has_eb = uint32_t(r) > r0 || dw > 0;
+                    const bool has_eb = rr > 0 || dw > 0;
 #pragma unroll
                     for (int c = 0; c < V; c++) {
                         const T t = has_eb ? Op::apply(eb, x[r].v[c]) : x[r].v[c];
@@ -262,7 +271,7 @@ __global__ __launch_bounds__(kResWaves *kWave) void k_resident(ScanArgs a, uint3
                 // constant 0 (see the column single pass: 128-bit buffer
                 // stores with a scalar-register offset lost their data
                 // registers)
-                uint32_t vo = voff + (uint32_t(r) - r0) * kRowBytes;
+                uint32_t vo = voff + uint32_t(rr) * kRowBytes;
                 asm volatile("" : "+v"(vo));
                 __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, y), rs_out[s], vo, 0, OUT_AUX);
             }
@@ -275,36 +284,46 @@ __global__ __launch_bounds__(kResWaves *kWave) void k_resident(ScanArgs a, uint3
     // registers.  Barriers: B1 (the static first tile scanned), Bm (the
     // mode decided), in dynamic mode Bd (the claimed tiles loaded and their
     // first scanned), B2 (the first tile's prefix known; with two tiles,
-    // the second scanned), and with two tiles B3 (the second's prefix).
+    // the second scanned, after Bm so that its loads overlap the first
+    // look-back), and with two tiles B3 (the second's prefix).
     //
-    // The static first tile's aggregate is published before the residency
-    // decision, which waits for every workgroup to start (about 2 us of
-    // each call when it came first), so the look-backs that follow it find
-    // their predecessors published.  A tile's aggregate depends only on its
-    // data, so whoever processes the tile in either mode publishes the same
-    // words; only waiting on predecessors needs the decision.
+    // With two short tiles, the first one's aggregate is published before
+    // the residency decision, which waits for every workgroup to start
+    // (about 2 us of each call, longer than such a tile's loads), so the
+    // look-backs that follow find their predecessors published.  A tile's
+    // aggregate depends only on its data, so whoever processes the tile in
+    // either mode publishes the same words; only waiting on predecessors
+    // needs the decision.  Long first tiles, and single tiles of any
+    // length, decide while they load (measured faster).
     uint32_t tl[SW];  // this workgroup's tiles: static, w (and w + G); dynamic, claim k's SW * k (and SW * k + 1)
     tl[0] = blockIdx.x;
     if constexpr (SW == 2) tl[1] = blockIdx.x + gridDim.x;
     int64_t start0, rem0;
     uint32_t seg0, j0;
     if (ctrl) {
+        // short first tiles of two-tile workgroups decide after publishing;
+        // long ones, and one-tile workgroups, while loading
+        const bool late = SW == 2 && rows <= uint32_t(kResLateDecisionRows);
+        uint32_t dm = 0, ck = 0;
+        auto decide = [&]() {
+            const uint32_t m = decide_mode(hdr, s_epoch, gridDim.x, a.pipe.mode_limit);
+            dm = m == kModeStatic ? 0u : 1u;
+            ck = m == kModeStatic ? uint32_t(blockIdx.x)
+                                  : __hip_atomic_fetch_add(&hdr->claim, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        };
         if (lane == 0) {
             uint64_t hw = 0, cap = 0;
             s_epoch = begin_call(hdr, hw, cap);
             s_hw = hw;
             s_cap = cap;
+            if (!late) decide();
         }
         __syncthreads();  // B1
         geom(tl[0], start0, rem0, seg0, j0);
         C agg = scan_entries(0);
         if (tps > 1) publish(tl[0], agg);
-        uint32_t dm = 0, ck = 0;
         if (lane == 0) {
-            const uint32_t m = decide_mode(hdr, s_epoch, gridDim.x, a.pipe.mode_limit);
-            dm = m == kModeStatic ? 0u : 1u;
-            ck = m == kModeStatic ? uint32_t(blockIdx.x)
-                                  : __hip_atomic_fetch_add(&hdr->claim, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (late) decide();
             s_dyn = dm;
             s_claim = ck;
         }
@@ -354,7 +373,6 @@ __global__ __launch_bounds__(kResWaves *kWave) void k_resident(ScanArgs a, uint3
         if constexpr (SW == 2) load(tl[1], 1);
         scan_rows(tl[0], 0);
         __syncthreads();  // B1
-        if constexpr (SW == 2) scan_rows(tl[1], 1);
         __syncthreads();  // Bm
         if (s_dyn != 0u) {
             const uint32_t ck = s_claim;
@@ -364,8 +382,10 @@ __global__ __launch_bounds__(kResWaves *kWave) void k_resident(ScanArgs a, uint3
             if constexpr (SW == 2) load(tl[1], 1);
             scan_rows(tl[0], 0);
             __syncthreads();  // Bd
-            if constexpr (SW == 2) scan_rows(tl[1], 1);
         }
+        // the second tile is scanned while the control wave looks back for
+        // the first (its loads overlap that look-back)
+        if constexpr (SW == 2) scan_rows(tl[1], 1);
         geom(tl[0], start0, rem0, seg0, j0);
         __syncthreads();  // B2
         // The first tile's stores wait for the second tile's scan (above):
