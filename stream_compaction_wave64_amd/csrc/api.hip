@@ -234,10 +234,12 @@ constexpr int kDefaultBlock = 512;  // threads per workgroup of the tiled kernel
 constexpr int kDefaultRtsBlocks = 1024;               // C of reduce-then-scan
 constexpr int64_t kDefaultLocalMem = 32 * 1024;       // LDS budget of the large-element rule (AcceleratedKernels.jl PR #208)
 constexpr int64_t kSmallArrayTiles = 256;             // one tile per CU: the small-array shape rule
-// the resident single pass from this many bytes up: below it the small
-// array tiles won (back-to-back calls, int32 2^20: 9.1 against 9.9 us), from
-// it the resident pass (int32 2^21: 10.6 against 11.3, fp64 2^20: 11.1
-// against 12.3)
+// Rows of a 2-D array take the resident single pass from this many bytes
+// up (below it, when first measured, the small-array tiles won for whole
+// arrays too); whole arrays take it at every size (graph replays of
+// back-to-back calls, resident against small-array tiles, us: int32 2^14
+// 3.9 against 7.4, 2^18 6.1 against 7.4, 2^20 7.2 against 8.5; fp32 1e6 7.2
+// against 9.0; fp64 2^16 5.0 against 7.4, 2^19 6.9 against 9.5).
 constexpr int64_t kResMinBytes = int64_t(8) << 20;
 constexpr int64_t kResTwoTileBytes = int64_t(32) << 20;  // whole arrays: two tiles per workgroup from here
 constexpr int64_t kElemTileLocalMem = 64 * 1024;      // default bound on an element tile's E (default dynamic LDS limit)
@@ -389,7 +391,7 @@ int plan_scan(scan_dtype_t dt, scan_op_t op, int64_t outer, int64_t len, bool al
     // look-backs: fp32 1e7 20.3 -> 19.4 us, fp64 1e7 35.1 -> 34.3, int32
     // 2^23 17.5 -> 17.0); below that the fewer, longer workgroups lost
     // (int32 2^22 10.7 -> 11.7 us).  The tuning can ask for either.
-    if (shape_free && tu.grid_blocks <= 0 && vec_ok && outer * len * esize >= kResMinBytes &&
+    if (shape_free && tu.grid_blocks <= 0 && vec_ok && (outer == 1 || outer * len * esize >= kResMinBytes) &&
         (tu.no_identity ? find_resident_noid(dt, op) : find_resident(dt, op)) != nullptr) {
         const int64_t re = int64_t(kResWaves - 1) * kWave * (16 / esize);  // the data waves
         const bool two = outer == 1 && (tu.resident_sweeps == 2 ||

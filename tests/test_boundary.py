@@ -111,7 +111,7 @@ def test_plan_rows_that_fit_one_tile():
         assert binding.plan("scan", dt, "sum", 3, 2048 * vec + vec)["kernel"] == "lookback"  # longer than 8 rows
         assert binding.plan("scan", dt, "sum", 3, 64 * vec - vec)["kernel"] == "lookback"   # under one wave
         assert binding.plan("scan", dt, "sum", 3, 4096 + 1)["kernel"] == "lookback"         # not whole vectors
-    assert binding.plan("scan", torch.float32, "sum", 1, 4096)["kernel"] == "lookback"        # one array
+    assert binding.plan("scan", torch.float32, "sum", 1, 4096)["kernel"] == "resident"        # one array
     for tu in ({"grid_blocks": 8}, {"block_size": 512, "items_per_thread": 8}, {"no_identity": 1},
                {"algo": "reduce_then_scan"}):
         if tu.get("algo"):
@@ -122,34 +122,45 @@ def test_plan_rows_that_fit_one_tile():
 
 
 def test_plan_small_arrays_take_short_tiles():
-    # Whole arrays under 8 MiB that 448 x 5-row tiles cover in at most 256
-    # tiles (one per CU) take those tiles; from 8 MiB the resident pass takes
-    # arrays of 128-bit rows; rows of a 2-D array, explicit shapes, the
-    # element-wide path and reduce-then-scan keep their own (arrays within
-    # one default tile follow the short-segment rule instead).
+    # Whole arrays of 128-bit rows take the resident pass at every size up to
+    # its capacity, the smallest included.  With a grid cap (no resident
+    # pass) those that 448 x 5-row tiles cover in at most 256 tiles (one per
+    # CU) take those tiles; rows of a 2-D array take the resident pass from
+    # 8 MiB; explicit shapes, the element-wide path and reduce-then-scan keep
+    # their own (arrays within one default tile follow the short-segment rule
+    # instead).
     from stream_compaction_wave64_amd import binding
     import torch
+    cap = {"grid_blocks": 64}
     for dt, vec, big_ipt in ((torch.int32, 4, 28), (torch.float32, 4, 28), (torch.float64, 2, 16)):
         small_tile = 448 * 5 * vec
         big_tile = 448 * big_ipt if vec == 2 else 704 * big_ipt
         below = (8 << 20) // (16 // vec) - vec  # the largest array under 8 MiB
-        for n in (2 * big_tile, 128 * small_tile, below):
+        for n in (vec, 64 * vec, 2 * big_tile, 128 * small_tile, below, below + vec, 256 * small_tile + vec):
             p = binding.plan("scan", dt, "sum", 1, n)
+            assert p["kernel"] == "resident" and p["num_tiles"] <= 256 and p["block_size"] == 1024, (dt, n, p)
+        for n in (2 * big_tile, 128 * small_tile, below):
+            p = binding.plan("scan", dt, "sum", 1, n, tuning=cap)
             assert (p["kernel"], p["block_size"], p["items_per_thread"]) == ("lookback", 512, 5 * vec), (dt, n, p)
             assert p["num_tiles"] <= 256
-        for n in (below + vec, 256 * small_tile, 256 * small_tile + vec):
-            p = binding.plan("scan", dt, "sum", 1, n)
-            assert p["kernel"] == "resident" and p["num_tiles"] <= 256, (dt, n, p)
+        p = binding.plan("scan", dt, "sum", 1, 256 * small_tile + vec, tuning=cap)  # past 256 small tiles
+        assert (p["kernel"], p["items_per_thread"]) == ("lookback", big_ipt), (dt, p)
+        row8 = ((8 << 20) // (16 // vec) // 3 // vec + 1) * vec  # 3 rows of this many: just over 8 MiB
+        for n in (big_tile, row8 - 2 * vec):  # rows of a 2-D array under 8 MiB
+            assert binding.plan("scan", dt, "sum", 3, n)["kernel"] != "resident", (dt, n)
+        assert binding.plan("scan", dt, "sum", 3, row8)["kernel"] == "resident"
         p = binding.plan("scan", dt, "sum", 1, 64 * small_tile + 1)  # element-wide path: unchanged
         assert p["vec"] == 1 and p["items_per_thread"] == big_ipt // vec, (dt, p)
         p = binding.plan("scan", dt, "sum", 1, 1024 * small_tile + 1)  # element-wide, 8 MiB and more
         assert p["kernel"] == "lookback" and p["vec"] == 1, (dt, p)
         p = binding.plan("scan", dt, "sum", 1, 64 * small_tile, tuning={"block_size": 512, "items_per_thread": 3 * vec})
-        assert p["items_per_thread"] == 3 * vec
+        assert p["items_per_thread"] == 3 * vec and p["kernel"] == "lookback"
         p = binding.plan("scan", dt, "sum", 2, 64 * small_tile)
         assert p["items_per_thread"] == big_ipt, (dt, p)
     p = binding.plan("scan", torch.float32, "sum", 1, 1 << 20, tuning={"algo": "reduce_then_scan"})
     assert p["kernel"] == "reduce_then_scan" and p["items_per_thread"] == 32
+    # count-scan-emit's offsets follow the scan's plan
+    assert binding.plan("pack", torch.int32, "sum", 1, 4096)["launches"] == 1
 
 
 def test_plan_resident():

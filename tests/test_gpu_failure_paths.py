@@ -47,7 +47,9 @@ def test_garbage_epoch_times_out_lookback_and_reinit_recovers():
     ws = torch.zeros(1 << 20, dtype=torch.uint8, device=DEV)
     ws[:16].view(torch.int32)[0] = 1 << 30  # an epoch no descriptor tag can carry
     with _Installed(ws):
-        sw.scan_inclusive(xd, tuning={"spin_limit": 32})
+        # the look-back pipeline's small-array tiles (the resident pass has
+        # its own case below)
+        sw.scan_inclusive(xd, tuning={"spin_limit": 32, "block_size": 512, "items_per_thread": 20})
         torch.cuda.synchronize()
         assert sw.scan_workspace_error(ws) & 1
         _recovers(ws, x, xd)

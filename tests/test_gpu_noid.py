@@ -50,14 +50,20 @@ def _run(x, op, tuning=None, offset=0):
 @pytest.mark.parametrize("dt", DTYPES, ids=lambda d: np.dtype(d).name)
 @pytest.mark.parametrize("op", OPS)
 def test_noid_parity_planner_shapes(dt, op):
-    p = sw.plan("scan", TORCH[np.dtype(dt)], op, 1, 10 ** 6, tuning=NOID)
-    tile = p["tile_elems"]
+    # sizes around the small-array look-back tiles (448 x 5 rows), with the
+    # planner's choice and with that shape pinned (the pipeline)
     vec = 16 // np.dtype(dt).itemsize
-    edge = 256 * 448 * 5 * vec  # the small-array shape's last size
+    small = {"block_size": 512, "items_per_thread": 5 * vec}
+    p = sw.plan("scan", TORCH[np.dtype(dt)], op, 1, 10 ** 6, tuning=dict(NOID, **small))
+    assert p["kernel"] == "lookback"
+    tile = p["tile_elems"]
+    edge = 256 * tile  # the planner's last size for that shape under a grid cap
     for i, n in enumerate([1, 2, 3, 63, 64, 65, 1000, tile - 4, tile, tile + 4, 3 * tile + 12, 65 * tile + 4,
                            edge, edge + vec]):
         x = _input(dt, n, 700 + i, op)
         assert_scan_matches(x, _run(x, op), op, False, what=f"n={n}", noid=True)
+        if n <= edge:
+            assert_scan_matches(x, _run(x, op, small), op, False, what=f"n={n} small tiles", noid=True)
 
 
 @pytest.mark.parametrize("dt", DTYPES, ids=lambda d: np.dtype(d).name)
@@ -150,8 +156,8 @@ def test_noid_fp32_1e7_config():
 @pytest.mark.parametrize("dt", DTYPES, ids=lambda d: np.dtype(d).name)
 @pytest.mark.parametrize("op", OPS)
 def test_noid_resident_pass(dt, op):
-    # The resident single pass without an identity: from its smallest array
-    # (8 MiB) to its capacity (256 tiles of 17 rows of 960 x 4 elements, or
+    # The resident single pass without an identity: from 8 MiB to its
+    # capacity (256 tiles of 17 rows of 960 x 4 elements, or
     # 21 rows of 960 x 2), tile ends ragged inside a row; rows of 2-D arrays,
     # several tiles per row and one tile per row (no row has a prefix).
     isz = np.dtype(dt).itemsize

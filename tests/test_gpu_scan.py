@@ -45,12 +45,20 @@ def _run(x, op, exclusive, tuning=None, offset=0):
 @pytest.mark.parametrize("op", OPS)
 @pytest.mark.parametrize("exclusive", [False, True], ids=["incl", "excl"])
 def test_parity_default_tiles(dt, op, exclusive):
-    p = sw.plan("scan", TORCH[np.dtype(dt)], op, 1, 10 ** 6)
+    # Sizes around the small-array look-back tiles (448 x 5 rows of 128-bit
+    # vectors), each run with the planner's choice (the resident pass for
+    # whole vectors, the element-wide pipeline otherwise) and with that tile
+    # shape pinned through the tuning (the look-back pipeline).
+    vec = 16 // np.dtype(dt).itemsize
+    small = {"block_size": 512, "items_per_thread": 5 * vec}
+    p = sw.plan("scan", TORCH[np.dtype(dt)], op, 1, 10 ** 6, tuning=small)
+    assert p["kernel"] == "lookback"
     tile = p["tile_elems"]
     for i, n in enumerate([1, 2, 3, 63, 64, 65, 1000, tile - 4, tile, tile + 4, 3 * tile + 12,
                            64 * tile - 4, 65 * tile + 4, 200_003]):
         x = _input(dt, n, 100 + i, op)
         assert_scan_matches(x, _run(x, op, exclusive), op, exclusive, what=f"n={n}")
+        assert_scan_matches(x, _run(x, op, exclusive, small), op, exclusive, what=f"n={n} small tiles")
 
 
 @pytest.mark.parametrize("dt", DTYPES, ids=lambda d: np.dtype(d).name)
@@ -73,11 +81,11 @@ def test_parity_whole_array_default_shape(dt, op, exclusive):
 @pytest.mark.parametrize("dt", DTYPES, ids=lambda d: np.dtype(d).name)
 @pytest.mark.parametrize("op", OPS)
 def test_parity_across_shape_switches(dt, op):
-    # Whole arrays of 128-bit rows: below 8 MiB the small-array tiles (448 x 5
-    # rows, at most 256 of them); from 8 MiB the resident single pass (one
-    # register tile of 960 data threads x rows per compute unit, at most 256
-    # tiles, 17 rows for 4-byte and 21 for 8-byte elements); past its
-    # capacity the default look-back shape.  Both sides of each switch.
+    # Whole arrays of 128-bit rows: the resident single pass (one register
+    # tile of 960 data threads x rows per compute unit, at most 256 tiles, 17
+    # rows for 4-byte and 21 for 8-byte elements; two tiles per workgroup
+    # from 32 MiB) up to its capacity, the smallest arrays included; past it
+    # the default look-back shape.  Both sides of the switch.
     es = np.dtype(dt).itemsize
     vec = 16 // es
     big = sw.plan("scan", TORCH[np.dtype(dt)], op, 1, 10 ** 8)
@@ -85,7 +93,7 @@ def test_parity_across_shape_switches(dt, op):
     # capacity: 256 tiles of 17 rows (4-byte), 512 tiles of 11 rows two per
     # workgroup (8-byte)
     cap = 256 * 17 * 960 * vec if es == 4 else 512 * 11 * 960 * vec
-    cases = [(res_min - vec, "lookback", 448 * 5 * vec), (res_min, "resident", None), (cap, "resident", None),
+    cases = [(res_min - vec, "resident", None), (res_min, "resident", None), (cap, "resident", None),
              (cap + vec, "lookback", big["tile_elems"])]
     for i, (n, kernel, tile) in enumerate(cases):
         p = sw.plan("scan", TORCH[np.dtype(dt)], op, 1, n)
@@ -113,8 +121,6 @@ def test_parity_resident(dt, op):
     re = 960 * vec  # elements per tile row
     for i, (rows, n) in enumerate([(3, 3 * re * 200 + 5 * vec), (7, 7 * re * 255 + re + 3 * vec),
                                    (3, 3 * re * 181)]):
-        if n * es < (8 << 20):
-            n = -(-(8 << 20) // (es * rows * re)) * rows * re + vec  # at least the switch
         p = sw.plan("scan", TORCH[np.dtype(dt)], op, 1, n)
         assert p["kernel"] == "resident", (n, p)
         x = _input(dt, n, 500 + i, op)
