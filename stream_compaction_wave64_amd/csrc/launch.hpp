@@ -44,9 +44,15 @@ constexpr int kResMaxRows2x4 = 8, kResMaxRows2x8 = 11;  // rows per tile with tw
 // decide while they load.  Measured: compaction of 1e7 keys in 11-row tiles
 // 18.1 us deciding early, 19.4 late; 2^21 keys in 3-row tiles 10.0 early,
 // 9.1 late; scan of 1e7 fp32 in two 6-row tiles 18.6 early, 17.4 late.  A
-// scan with one tile per workgroup decides early at any size (int32 2^22
-// in 5-row tiles: 10.6 us early, 11.4 late).
+// scan with one tile per workgroup decides late only with tiles of at most
+// kResLateDecisionRows1 rows and at least kResLateDecisionTiles of them
+// (graph replays, us, early against late: int32 2^18 in 69 1-row tiles 6.0
+// against 5.3, 2^21 in 183 3-row tiles 9.0 against 8.3, fp32 1e6 in 131
+// 2-row tiles 7.0 against 6.6; but int32 2^22 in 219 5-row tiles 10.9
+// against 11.4, 2^14 in 5 tiles 4.1 against 4.6, fp64 2^16 in 35 tiles 4.7
+// against 5.0).
 constexpr int kResLateDecisionRows = 8;
+constexpr int kResLateDecisionRows1 = 3, kResLateDecisionTiles = 64;
 constexpr int64_t kResMaxTiles = 256;                // one per compute unit on MI355X
 using ResLaunch = int (*)(const ScanArgs &, int rows, int sweeps, hipStream_t);
 ResLaunch find_resident(scan_dtype_t dt, scan_op_t op);

@@ -287,23 +287,24 @@ __global__ __launch_bounds__(kResWaves *kWave) void k_resident(ScanArgs a, uint3
     // the second scanned, after Bm so that its loads overlap the first
     // look-back), and with two tiles B3 (the second's prefix).
     //
-    // With two short tiles, the first one's aggregate is published before
+    // With short tiles, the first one's aggregate is published before
     // the residency decision, which waits for every workgroup to start
     // (about 2 us of each call, longer than such a tile's loads), so the
     // look-backs that follow find their predecessors published.  A tile's
     // aggregate depends only on its data, so whoever processes the tile in
     // either mode publishes the same words; only waiting on predecessors
-    // needs the decision.  Long first tiles, and single tiles of any
-    // length, decide while they load (measured faster).
+    // needs the decision.  Long first tiles, and the tiles of one-tile grids
+    // of few workgroups, decide while they load (measured faster).
     uint32_t tl[SW];  // this workgroup's tiles: static, w (and w + G); dynamic, claim k's SW * k (and SW * k + 1)
     tl[0] = blockIdx.x;
     if constexpr (SW == 2) tl[1] = blockIdx.x + gridDim.x;
     int64_t start0, rem0;
     uint32_t seg0, j0;
     if (ctrl) {
-        // short first tiles of two-tile workgroups decide after publishing;
-        // long ones, and one-tile workgroups, while loading
-        const bool late = SW == 2 && rows <= uint32_t(kResLateDecisionRows);
+        // short first tiles decide after publishing, long ones (and one-tile
+        // grids of few workgroups) while loading
+        const bool late = SW == 2 ? rows <= uint32_t(kResLateDecisionRows)
+                                  : rows <= uint32_t(kResLateDecisionRows1) && n >= uint32_t(kResLateDecisionTiles);
         uint32_t dm = 0, ck = 0;
         auto decide = [&]() {
             const uint32_t m = decide_mode(hdr, s_epoch, gridDim.x, a.pipe.mode_limit);
