@@ -47,8 +47,8 @@ N = 10 ** 8
 # the scan kernel, each scaled by what the counter reads for the copy kernel of
 # known size (profiles/lookback_scan_fp32_1e8_hbm_counters.md).  Valid only for
 # the kernel sources that were measured: reported as null once they change.
-TRAFFIC_BYTES = 8.011e8
-TRAFFIC_SOURCES_SHA = "d281a1d5f869bcbe"
+TRAFFIC_BYTES = 8.010e8
+TRAFFIC_SOURCES_SHA = "fd4fba659611154b"
 
 
 def _kernel_sources_sha():
