@@ -141,15 +141,18 @@ def test_late_publishers_dynamic_claiming_and_no_identity(stride, sleeps):
         assert sw.scan_workspace_error(ws) == 0
 
 
-def test_resident_pass_failure_paths():
-    # The resident single pass (arrays of 8 MiB and more that fit one register
-    # tile per compute unit) under the same forced conditions: a residency
-    # check that never confirms (dynamic claiming, flag bit 2, exact
-    # results), late publishers (the gap read's re-polls, exact results, no
-    # flag) and a garbage epoch (the waits give up: flag bit 0).
-    x = inputs.generic(np.int32, 3_000_000, 70, "wide")
+@pytest.mark.parametrize("n,rows", [(3_000_000, 4), (1_000_000, 2)])
+def test_resident_pass_failure_paths(n, rows):
+    # The resident single pass (arrays that fit one register tile per compute
+    # unit) under the same forced conditions: a residency check that never
+    # confirms (dynamic claiming, flag bit 2, exact results), late publishers
+    # (the gap read's re-polls, exact results, no flag) and a garbage epoch
+    # (the waits give up: flag bit 0).  4-row tiles decide the residency
+    # while they load; 131 tiles of 2 rows publish their static tile first.
+    x = inputs.generic(np.int32, n, 70, "wide")
     xd = to_dev(x)
-    assert sw.plan("scan", torch.int32, "sum", 1, x.size)["kernel"] == "resident"
+    p = sw.plan("scan", torch.int32, "sum", 1, x.size)
+    assert (p["kernel"], p["items_per_thread"], p["tiles_per_block"]) == ("resident", 4 * rows, 1), p
     ws = torch.zeros(1 << 22, dtype=torch.uint8, device=DEV)
     with _Installed(ws):
         for excl in (False, True):
@@ -160,7 +163,7 @@ def test_resident_pass_failure_paths():
             assert sw.scan_workspace_error(ws) == 4
             assert_scan_matches(x, to_host(r), "sum", excl, what=f"dynamic excl={excl}")
         sw.scan_workspace_init(ws)
-        f = inputs.generic(np.float32, 3_000_000, 71)
+        f = inputs.generic(np.float32, n, 71)
         fd = to_dev(f)
         for stride, sleeps in DELAYS:
             for excl in (False, True):
@@ -234,14 +237,18 @@ def test_resident_two_tile_failure_paths():
         _recovers(ws, x, xd)
 
 
-def test_resident_compaction_failure_paths():
+@pytest.mark.parametrize("n,rows", [(3_000_000, 4), (10_000_000, 11)])
+def test_resident_compaction_failure_paths(n, rows):
     # The resident compaction under the same forced conditions: dynamic
     # claiming (flag bit 2), late publishers, a garbage epoch (flag bit 0).
+    # 4-row tiles publish their static tile's count before the residency
+    # decision; 11-row tiles decide while they load.
     import oracle
-    x, _ = inputs.compaction_inputs(3_000_000, seed=72)
+    x, _ = inputs.compaction_inputs(n, seed=72)
     xd = to_dev(x)
     ref = oracle.compact(x, "gt", 0.5)
-    assert sw.plan("compact", torch.float32, "sum", 1, x.size)["kernel"] == "compact_resident"
+    p = sw.plan("compact", torch.float32, "sum", 1, x.size)
+    assert (p["kernel"], p["items_per_thread"]) == ("compact_resident", 4 * rows), p
 
     def run(tuning):
         out, count = sw.compact_if(xd, "gt", 0.5, tuning=tuning)
@@ -269,14 +276,18 @@ def test_resident_compaction_failure_paths():
         assert c == ref.size and np.array_equal(got, ref)
 
 
-def test_resident_partition_failure_paths():
+@pytest.mark.parametrize("n,rows", [(3_000_000, 4), (10_000_000, 11)])
+def test_resident_partition_failure_paths(n, rows):
     # The resident partition under the same forced conditions: dynamic
-    # claiming (flag bit 2), late publishers, a garbage epoch (flag bit 0).
+    # claiming (flag bit 2), late publishers, a garbage epoch (flag bit 0),
+    # with the residency decided after (4 rows) and before (11 rows)
+    # the static tile's count is published.
     import oracle
-    x, _ = inputs.compaction_inputs(3_000_000, seed=73)
+    x, _ = inputs.compaction_inputs(n, seed=73)
     xd = to_dev(x)
     vals, idx, k = oracle.partition(x, "gt", 0.5)
-    assert sw.plan("partition", torch.float32, "sum", 1, x.size)["kernel"] == "partition_resident"
+    p = sw.plan("partition", torch.float32, "sum", 1, x.size)
+    assert (p["kernel"], p["items_per_thread"]) == ("partition_resident", 4 * rows), p
 
     def run(tuning):
         out, oi, count = sw.partition_if(xd, "gt", 0.5, tuning=tuning)
