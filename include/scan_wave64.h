@@ -159,7 +159,8 @@ typedef struct {
                                   between all loads and all stores), 2 two
                                   where they fit (the second tile's loads and
                                   the first's stores overlapping the
-                                  look-backs); 0: two from 32 MiB up */
+                                  look-backs); 0: two from 28 MiB up
+                                  for 4-byte elements, 40 MiB for 8-byte */
 } scan_tuning_t;
 
 /* Kernel family a call runs (reported by scan_plan). */

@@ -241,7 +241,11 @@ constexpr int64_t kSmallArrayTiles = 256;             // one tile per CU: the sm
 // 3.9 against 7.4, 2^18 6.1 against 7.4, 2^20 7.2 against 8.5; fp32 1e6 7.2
 // against 9.0; fp64 2^16 5.0 against 7.4, 2^19 6.9 against 9.5).
 constexpr int64_t kResMinBytes = int64_t(8) << 20;
-constexpr int64_t kResTwoTileBytes = int64_t(32) << 20;  // whole arrays: two tiles per workgroup from here
+// whole arrays: two tiles per workgroup from here (4-byte and 8-byte
+// elements; graph replays, us, one tile against two: int32 24 MiB 14.4
+// against 15.4, 28 MiB 15.7 against 14.7; fp64 32 MiB 17.9 against 19.1,
+// 36-40 MiB level, 48 MiB 24.3 against 23.3)
+constexpr int64_t kResTwoTileBytes4 = int64_t(28) << 20, kResTwoTileBytes8 = int64_t(40) << 20;
 constexpr int64_t kElemTileLocalMem = 64 * 1024;      // default bound on an element tile's E (default dynamic LDS limit)
 constexpr int kElemDefaultBlock = 256;                // large elements: start of the rule
 constexpr int64_t kElemChunks = 2048;  // large elements: workgroups per launch (<= 8192, the partials pass)
@@ -386,16 +390,18 @@ int plan_scan(scan_dtype_t dt, scan_op_t op, int64_t outer, int64_t len, bool al
     // kResMaxTiles (the most compute units reading).  Only for the default
     // shape, without a grid cap, scans of 128-bit rows (without an identity
     // too: inclusive, as everywhere).
-    // A whole array of 32 MiB or more takes two tiles per workgroup where
-    // they fit (the second tile's loads and the first's stores overlap the
-    // look-backs: fp32 1e7 20.3 -> 19.4 us, fp64 1e7 35.1 -> 34.3, int32
-    // 2^23 17.5 -> 17.0); below that the fewer, longer workgroups lost
-    // (int32 2^22 10.7 -> 11.7 us).  The tuning can ask for either.
+    // A whole array of 28 MiB or more (4-byte elements; 40 MiB, 8-byte)
+    // takes two tiles per workgroup where they fit (the second tile's loads
+    // and the first's stores overlap the look-backs: fp32 1e7 20.4 -> 16.8
+    // us, fp64 1e7 35.5 -> 34.0, int32 2^23 17.9 -> 16.2); below that the
+    // fewer, longer workgroups lose (int32 2^22 10.6 -> 13.3 us).  The
+    // tuning can ask for either.
     if (shape_free && tu.grid_blocks <= 0 && vec_ok && (outer == 1 || outer * len * esize >= kResMinBytes) &&
         (tu.no_identity ? find_resident_noid(dt, op) : find_resident(dt, op)) != nullptr) {
         const int64_t re = int64_t(kResWaves - 1) * kWave * (16 / esize);  // the data waves
         const bool two = outer == 1 && (tu.resident_sweeps == 2 ||
-                                        (tu.resident_sweeps != 1 && len * esize >= kResTwoTileBytes));
+                                        (tu.resident_sweeps != 1 &&
+                                         len * esize >= (esize == 8 ? kResTwoTileBytes8 : kResTwoTileBytes4)));
         for (int sw = two ? 2 : 1; sw >= 1; sw--) {
             const int maxr = sw == 2 ? (esize == 8 ? kResMaxRows2x8 : kResMaxRows2x4)
                                      : (esize == 8 ? kResMaxRows8 : kResMaxRows4);

@@ -166,7 +166,7 @@ def test_plan_small_arrays_take_short_tiles():
 def test_plan_resident():
     # The resident pass: one 1024-thread workgroup (15 data waves and a
     # control wave) per tile of rows x 960 x vec elements, or per two tiles
-    # for a whole array of 32 MiB or more; the fewest rows that keep the
+    # for a whole array of 28 MiB or more (40 MiB for 8-byte elements); the fewest rows that keep the
     # workgroups within 256, up to 17 rows (4-byte elements) or 21 (8-byte)
     # with one tile, 8 or 11 per tile with two; one descriptor word per tile
     # (two for 64-bit carries); not with a grid cap or an explicit shape;
@@ -185,10 +185,15 @@ def test_plan_resident():
     assert (p["kernel"], p["items_per_thread"], p["num_tiles"], p["carry_words"]) == ("resident", 42, 249, 2)
     p = binding.plan("scan", torch.float64, "sum", 1, 10 ** 7)   # 11 rows of 1920: 474 tiles, 237 workgroups
     assert (p["kernel"], p["items_per_thread"], p["num_tiles"], p["tiles_per_block"]) == ("resident", 22, 474, 2)
-    # two tiles from 32 MiB, one below; a forced two below the threshold
-    below = (32 << 20) // 4 - 4
+    # two tiles from 28 MiB (4-byte elements) or 40 MiB (8-byte), one below;
+    # a forced two below the threshold
+    below = (28 << 20) // 4 - 4
     assert binding.plan("scan", torch.int32, "sum", 1, below)["tiles_per_block"] == 1
     assert binding.plan("scan", torch.int32, "sum", 1, below + 4)["tiles_per_block"] == 2
+    below = (40 << 20) // 8 - 2
+    assert binding.plan("scan", torch.float64, "sum", 1, below)["tiles_per_block"] == 1
+    assert binding.plan("scan", torch.float64, "sum", 1, below + 2)["tiles_per_block"] == 2
+    assert binding.plan("scan", torch.int64, "max", 1, (32 << 20) // 8)["tiles_per_block"] == 1
     assert binding.plan("scan", torch.int32, "sum", 1, 1 << 21, tuning={"resident_sweeps": 2})["tiles_per_block"] == 2
     # capacities: 256 x 17 rows of 3840 with one tile (two tiles hold 512 x 8
     # rows, fewer); 512 x 11 rows of 1920 with two (one tile: 256 x 21)

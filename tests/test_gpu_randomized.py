@@ -157,9 +157,9 @@ def test_random_packing_and_segments():
 def test_random_single_pass_paths():
     # The one-step paths at random sizes: whole arrays and rows of 8 MiB up to
     # the resident pass's capacity (most with whole 128-bit vectors, some
-    # not: those fall back to the pipeline; whole arrays from 32 MiB with two
-    # tiles per workgroup), and column scans whose register tiles fit one per
-    # compute unit.  Every case against the oracle; the planner's choice is
+    # not: those fall back to the pipeline; whole arrays from 28 MiB, 40 MiB
+    # for 8-byte elements, with two tiles per workgroup), and column scans
+    # whose register tiles fit one per compute unit.  Every case against the oracle; the planner's choice is
     # recorded so that the sweep keeps reaching them.
     rng = np.random.default_rng(2030)
     kernels = {}

@@ -84,8 +84,9 @@ def test_parity_across_shape_switches(dt, op):
     # Whole arrays of 128-bit rows: the resident single pass (one register
     # tile of 960 data threads x rows per compute unit, at most 256 tiles, 17
     # rows for 4-byte and 21 for 8-byte elements; two tiles per workgroup
-    # from 32 MiB) up to its capacity, the smallest arrays included; past it
-    # the default look-back shape.  Both sides of the switch.
+    # from 28 MiB, 40 MiB for 8-byte elements) up to its capacity, the
+    # smallest arrays included; past it the default look-back shape.  Both
+    # sides of the switch.
     es = np.dtype(dt).itemsize
     vec = 16 // es
     big = sw.plan("scan", TORCH[np.dtype(dt)], op, 1, 10 ** 8)
@@ -131,8 +132,9 @@ def test_parity_resident(dt, op):
 @pytest.mark.parametrize("dt", DTYPES, ids=lambda d: np.dtype(d).name)
 @pytest.mark.parametrize("op", OPS)
 def test_parity_resident_two_tiles(dt, op):
-    # The resident pass with two tiles per workgroup (whole arrays from 32
-    # MiB; workgroup w holds tiles w and w + G): an odd tile count (the last
+    # The resident pass with two tiles per workgroup (whole arrays from 28
+    # MiB, 40 MiB for 8-byte elements; workgroup w holds tiles w and w + G):
+    # an odd tile count (the last
     # workgroup has no second tile) with a ragged last tile, an even count
     # ending in a partial vector row, the form's capacity (512 full tiles),
     # and a forced two-tile plan below the threshold (two rows per tile).
@@ -141,7 +143,12 @@ def test_parity_resident_two_tiles(dt, op):
     re = 960 * vec
     rows = 8 if es == 4 else 11
     even = 436 * 6 * re - 3 * vec if es == 4 else 10 ** 7
-    sizes = [((32 << 20) // es + 3 * vec, None), (even, None), (512 * rows * re, None),
+    # just past the planner's switch to two tiles, stepped until the tile
+    # count is odd, with a ragged last tile
+    odd = ((28 << 20) if es == 4 else (40 << 20)) // es + 3 * vec
+    while sw.plan("scan", TORCH[np.dtype(dt)], op, 1, odd)["num_tiles"] % 2 == 0:
+        odd += 997 * vec
+    sizes = [(odd, None), (even, None), (512 * rows * re, None),
              ((8 << 20) // es, {"resident_sweeps": 2})]
     if op not in ("sum", "max"):
         sizes = sizes[:1] + sizes[3:]  # time: the other operators at the small sizes

@@ -92,7 +92,7 @@ def test_noalloc_struct_elements():
 
 @pytest.mark.parametrize("dt,op", [(np.int32, "sum"), (np.float64, "sum"), (np.float32, "max")])
 def test_noalloc_two_tile_resident_then_smaller(dt, op):
-    # whole arrays of 32 MiB or more take the resident pass with two tiles per
+    # whole arrays of 40 MiB or more take the resident pass with two tiles per
     # workgroup; then a one-tile resident call on the same scratch array
     es = np.dtype(dt).itemsize
     kind = "default" if np.issubdtype(dt, np.floating) and op == "sum" else "wide"
