@@ -48,7 +48,7 @@ N = 10 ** 8
 # known size (profiles/lookback_scan_fp32_1e8_hbm_counters.md).  Valid only for
 # the kernel sources that were measured: reported as null once they change.
 TRAFFIC_BYTES = 8.010e8
-TRAFFIC_SOURCES_SHA = "fd4fba659611154b"
+TRAFFIC_SOURCES_SHA = "2ea649ecb2e64ddc"
 
 
 def _kernel_sources_sha():

@@ -350,8 +350,9 @@ struct CtrlPipeline {
 };
 
 // Workgroups of a kernel that can be resident at once on the current device,
-// cached per kernel.  The runtime's occupancy figure is trusted only up to 7
-// waves per SIMD (28 per compute unit): at the full 8 the grid it implies was
+// cached per kernel.  The runtime's occupancy figure is trusted only up to 6
+// waves per SIMD (24 per compute unit): grids at the bound a kernel's
+// resources set (8 waves, or 7 for the 64-bit kernels of 256 threads) were
 // measured not to fit at once.  The kernel verifies residency itself
 // (decide_mode), so this only keeps the fast path the common one.
 int resident_blocks(const void *kernel, int waves_per_block);

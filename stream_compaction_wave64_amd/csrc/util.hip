@@ -21,7 +21,14 @@ int resident_blocks(const void *kernel, int waves_per_block) {
     int per_cu = 0, cus = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, 0) != hipSuccess) return 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    if (per_cu * waves_per_block > 28) per_cu = 28 / waves_per_block > 0 ? 28 / waves_per_block : 1;
+    // At most 6 waves per SIMD (24 per compute unit).  A grid at the bound
+    // the kernel's resources set was measured not to start at once: 8 waves
+    // per SIMD for small 4-byte kernels, 7 for the 64-bit look-back kernels
+    // of 256 threads (102-104 scalar registers, 64-71 vector registers; every
+    // call fell back to dynamic claiming until the grid was capped here).
+    // Default shapes hold one large workgroup per compute unit and are not
+    // affected.
+    if (per_cu * waves_per_block > 24) per_cu = 24 / waves_per_block > 0 ? 24 / waves_per_block : 1;
     const int v = per_cu * cus;
     if (count < 512) {
         keys[count] = kernel;

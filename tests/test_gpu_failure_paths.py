@@ -79,10 +79,22 @@ def test_unconfirmed_residency_falls_back_to_dynamic_claiming(dt):
 
 
 def test_errors_never_set_in_normal_operation():
+    # No call falls back to dynamic claiming or times out on its own: the
+    # default shapes, and the persistent grids of 256-thread tiles whose
+    # occupancy the runtime overstates (64-bit elements, one 16-byte row or
+    # element-wide access).
+    for ws in binding.workspaces._ws.values():
+        sw.scan_workspace_init(ws)
     x = inputs.generic(np.float32, 3_000_000, 22)
     xd = to_dev(x)
     for _ in range(10):
         sw.scan_inclusive(xd)
+    for dt in (np.int64, np.float64, np.int32):
+        vec = 16 // np.dtype(dt).itemsize
+        for n in (300_000 * vec, 300_001):
+            y = to_dev(inputs.generic(dt, n, 24, "wide" if dt != np.float64 else "near1"))
+            for op in ("sum", "prod", "max"):
+                sw.scan_inclusive(y, op=op, tuning={"block_size": 256, "items_per_thread": vec})
     torch.cuda.synchronize()
     for ws in binding.workspaces._ws.values():
         assert sw.scan_workspace_error(ws) == 0
